@@ -1,0 +1,262 @@
+"""CPU oracle for the TTT-layer forward pass: the primal per-token recurrence, in float64.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or execute this
+module: only the test-suite, the smoke check and the CPU-baseline leg of the benchmark use
+it.  It shares no code, tables or helpers with the HIP library and imports nothing from it.
+
+What it computes (all citations are to the four web pages on test-time training that
+define the method; no line numbers are given on purpose):
+
+* Inner model f(k; W).  Linear: f(k; W) = W k with W stored [d_out][d_in]
+  (page "5.1 - Fast weights and TTT layers", section 1, which uses the column-vector
+  form; the blog page "TTT: Test-Time Training" uses row vectors, k W, which is the same
+  model transposed).  MLP: f(k; W1, W2) = W2 SiLU(W1 k), no bias, no layer norm, no
+  residual (ViT3 news page, section "2. inner model design", observation 4: a 2-layer
+  SiLU MLP whose hidden width is r times the input width).
+* Self-supervised loss: reconstruction, l(W; k, v) = 1/2 ||f(k; W) - v||^2 ("Fast weights"
+  page, opening formula).  The negative dot-product loss l = -v^T f(k; W) of the blog page
+  (section "TTT / 如何理解") is also provided; it is only used by the checks.
+* Update rule: online gradient descent W_t = W_{t-1} - eta * grad l_t(W_{t-1})
+  (blog page, section "TTT / 通用表示"), generalised to mini-batch GD as in the summary of
+  Sun et al. 2024 on the wmrh.cn page, section 1.2.2 ("mini-batch TTT"): inside a
+  mini-batch of b consecutive tokens every gradient is taken at the weights W_{t'} left by
+  the previous mini-batch (W_0 for the first one), and
+      W_t = W_{t'} - eta * sum_{s = t'+1..t} grad l_s(W_{t'})          (cumulative sum).
+  b = 1 is plain online GD, b = T is batch GD.
+* Output rule: z_t = f(q_t; W_t), i.e. the output is read after the token's own update
+  (blog page "TTT / 通用表示"; "Fast weights" page opening formula).
+* Non-causal variant (ViT3 news page, "1. inner training setup", observation 2): the keys
+  and values are used as a small data set to train the inner model (here: one pass of
+  mini-batch GD over all chunks), and every query then reads the final weights.
+
+The recurrence is written out literally: the gradient of each token is materialised, the
+per-token weights W_t are materialised, and there is no blocking, fusion or dual form.
+It is vectorised only over independent (batch, head) chains.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "silu",
+    "dsilu",
+    "linear_f",
+    "mlp_f",
+    "linear_loss",
+    "mlp_loss",
+    "linear_grad",
+    "mlp_grad",
+    "ttt_linear",
+    "ttt_mlp",
+    "delta_rule",
+]
+
+LOSSES = ("mse", "dot")
+
+
+# ----------------------------------------------------------------------------------------
+# Inner models, losses and their gradients (per chain, batched over a leading axis N)
+# ----------------------------------------------------------------------------------------
+
+def silu(u):
+    """SiLU(u) = u * sigma(u), the inner activation of the ViT3 inner MLP."""
+    return u / (1.0 + np.exp(-u))
+
+
+def dsilu(u):
+    """d/du SiLU(u) = sigma(u) * (1 + u * (1 - sigma(u)))."""
+    s = 1.0 / (1.0 + np.exp(-u))
+    return s * (1.0 + u * (1.0 - s))
+
+
+def linear_f(W, x):
+    """f(x; W) = W x.  W [N, d_out, d_in], x [N, d_in] -> [N, d_out]."""
+    return np.einsum("nij,nj->ni", W, x)
+
+
+def mlp_f(W1, W2, x):
+    """f(x; W1, W2) = W2 SiLU(W1 x).  W1 [N, h, d], W2 [N, d, h], x [N, d] -> [N, d]."""
+    return np.einsum("nih,nh->ni", W2, silu(np.einsum("nhj,nj->nh", W1, x)))
+
+
+def linear_loss(W, k, v, loss="mse"):
+    """Per-chain loss value: 1/2||W k - v||^2 (mse) or -v^T W k (dot).  -> [N]."""
+    y = linear_f(W, k)
+    if loss == "mse":
+        return 0.5 * np.sum((y - v) ** 2, axis=-1)
+    return -np.sum(v * y, axis=-1)
+
+
+def mlp_loss(W1, W2, k, v, loss="mse"):
+    """Per-chain loss value of the 2-layer SiLU inner MLP.  -> [N]."""
+    y = mlp_f(W1, W2, k)
+    if loss == "mse":
+        return 0.5 * np.sum((y - v) ** 2, axis=-1)
+    return -np.sum(v * y, axis=-1)
+
+
+def linear_grad(W, k, v, loss="mse"):
+    """Gradient of the loss with respect to W for f(k; W) = W k.
+
+    mse: (W k - v) k^T  ("Fast weights" page, section 1, gradient of the linear model).
+    dot: -v k^T         (blog page, "TTT / 如何理解", gradient of the negative dot product,
+                          written here in the column-vector form).
+    W [N, d, d], k, v [N, d] -> [N, d, d].
+    """
+    if loss == "mse":
+        r = linear_f(W, k) - v
+    elif loss == "dot":
+        r = -v
+    else:
+        raise ValueError(loss)
+    return np.einsum("ni,nj->nij", r, k)
+
+
+def mlp_grad(W1, W2, k, v, loss="mse"):
+    """Gradients (dW1, dW2) of the loss for f(k) = W2 SiLU(W1 k), by the chain rule.
+
+    u = W1 k, a = SiLU(u), y = W2 a, dl/dy = y - v (mse) or -v (dot),
+    dW2 = (dl/dy) a^T, dW1 = ((W2^T dl/dy) * SiLU'(u)) k^T.
+    """
+    u = np.einsum("nhj,nj->nh", W1, k)
+    a = silu(u)
+    y = np.einsum("nih,nh->ni", W2, a)
+    if loss == "mse":
+        r = y - v
+    elif loss == "dot":
+        r = -v
+    else:
+        raise ValueError(loss)
+    g2 = np.einsum("ni,nh->nih", r, a)
+    du = np.einsum("nih,ni->nh", W2, r) * dsilu(u)
+    g1 = np.einsum("nh,nj->nhj", du, k)
+    return g1, g2
+
+
+# ----------------------------------------------------------------------------------------
+# Shape helpers
+# ----------------------------------------------------------------------------------------
+
+def _flatten_tokens(x, dtype):
+    x = np.asarray(x)
+    if x.ndim < 2:
+        raise ValueError("token tensors need shape [..., T, d]")
+    lead = x.shape[:-2]
+    n = int(np.prod(lead)) if lead else 1
+    return np.ascontiguousarray(x.reshape((n,) + x.shape[-2:]).astype(dtype)), lead
+
+
+def _broadcast_state(w, lead, dtype):
+    """Broadcast an initial state [..., r, c] against the chains' leading dims."""
+    w = np.asarray(w).astype(dtype)
+    full = np.broadcast_to(w, tuple(lead) + w.shape[-2:])
+    n = int(np.prod(lead)) if lead else 1
+    return np.array(full.reshape((n,) + w.shape[-2:]), dtype=dtype, copy=True)
+
+
+def _check_chunk(T, chunk):
+    if not (isinstance(chunk, (int, np.integer)) and chunk >= 1):
+        raise ValueError("chunk must be a positive integer")
+    # A chunk longer than the sequence is one chunk of length T.
+    return int(min(chunk, T)) if T > 0 else int(chunk)
+
+
+# ----------------------------------------------------------------------------------------
+# The recurrences
+# ----------------------------------------------------------------------------------------
+
+def ttt_linear(q, k, v, w0, eta, chunk, causal=True, loss="mse", dtype=np.float64):
+    """TTT layer with the linear inner model, mini-batch GD of size `chunk`.
+
+    q, k, v: [..., T, d]; w0: [..., d, d] (broadcast over the leading dims, e.g. [H, d, d]
+    shared by every batch element).  Returns (z [..., T, d], w_final [..., d, d]).
+
+    The last chunk is shorter when T is not a multiple of `chunk`.  causal=False trains
+    over every chunk first and then applies the final weights to every query.
+    """
+    if loss not in LOSSES:
+        raise ValueError(loss)
+    q2, lead = _flatten_tokens(q, dtype)
+    k2, _ = _flatten_tokens(k, dtype)
+    v2, _ = _flatten_tokens(v, dtype)
+    N, T, d = q2.shape
+    W = _broadcast_state(w0, lead, dtype)
+    b = _check_chunk(T, chunk)
+    eta = dtype(eta)
+    z = np.zeros((N, T, d), dtype=dtype)
+    for c0 in range(0, T, b):
+        Wc = W.copy()                      # weights left by the previous mini-batch
+        G = np.zeros_like(Wc)              # running sum of this mini-batch's gradients
+        Wt = Wc
+        for t in range(c0, min(c0 + b, T)):
+            G = G + linear_grad(Wc, k2[:, t], v2[:, t], loss)
+            Wt = Wc - eta * G              # W_t, materialised
+            if causal:
+                z[:, t] = linear_f(Wt, q2[:, t])
+        W = Wt
+    if not causal:
+        for t in range(T):
+            z[:, t] = linear_f(W, q2[:, t])
+    return z.reshape(tuple(lead) + (T, d)), W.reshape(tuple(lead) + (d, d))
+
+
+def ttt_mlp(q, k, v, w1, w2, eta, chunk, causal=True, loss="mse", dtype=np.float64):
+    """TTT layer with the 2-layer SiLU MLP inner model, mini-batch GD of size `chunk`.
+
+    q, k, v: [..., T, d]; w1: [..., h, d]; w2: [..., d, h] (broadcast over the leading
+    dims).  Returns (z [..., T, d], w1_final [..., h, d], w2_final [..., d, h]).
+    """
+    if loss not in LOSSES:
+        raise ValueError(loss)
+    q2, lead = _flatten_tokens(q, dtype)
+    k2, _ = _flatten_tokens(k, dtype)
+    v2, _ = _flatten_tokens(v, dtype)
+    N, T, d = q2.shape
+    W1 = _broadcast_state(w1, lead, dtype)
+    W2 = _broadcast_state(w2, lead, dtype)
+    h = W1.shape[-2]
+    if W1.shape[-1] != d or W2.shape[-2:] != (d, h):
+        raise ValueError("w1 must be [..., h, d] and w2 [..., d, h]")
+    b = _check_chunk(T, chunk)
+    eta = dtype(eta)
+    z = np.zeros((N, T, d), dtype=dtype)
+    for c0 in range(0, T, b):
+        W1c, W2c = W1.copy(), W2.copy()
+        G1 = np.zeros_like(W1c)
+        G2 = np.zeros_like(W2c)
+        W1t, W2t = W1c, W2c
+        for t in range(c0, min(c0 + b, T)):
+            g1, g2 = mlp_grad(W1c, W2c, k2[:, t], v2[:, t], loss)
+            G1 = G1 + g1
+            G2 = G2 + g2
+            W1t = W1c - eta * G1
+            W2t = W2c - eta * G2
+            if causal:
+                z[:, t] = mlp_f(W1t, W2t, q2[:, t])
+        W1, W2 = W1t, W2t
+    if not causal:
+        for t in range(T):
+            z[:, t] = mlp_f(W1, W2, q2[:, t])
+    return (z.reshape(tuple(lead) + (T, d)), W1.reshape(tuple(lead) + (h, d)),
+            W2.reshape(tuple(lead) + (d, h)))
+
+
+def delta_rule(q, k, v, w0, eta, dtype=np.float64):
+    """The delta rule, written out as its closed-form update.
+
+    "Fast weights" page, section 1: W_t = W_{t-1} + eta (v_t - W_{t-1} k_t) k_t^T, and the
+    output z_t = W_t q_t.  Returns (z [..., T, d], w_final [..., d, d]).
+    """
+    q2, lead = _flatten_tokens(q, dtype)
+    k2, _ = _flatten_tokens(k, dtype)
+    v2, _ = _flatten_tokens(v, dtype)
+    N, T, d = q2.shape
+    W = _broadcast_state(w0, lead, dtype)
+    eta = dtype(eta)
+    z = np.zeros((N, T, d), dtype=dtype)
+    for t in range(T):
+        kt = k2[:, t]
+        err = v2[:, t] - np.einsum("nij,nj->ni", W, kt)      # prediction error
+        W = W + eta * np.einsum("ni,nj->nij", err, kt)
+        z[:, t] = np.einsum("nij,nj->ni", W, q2[:, t])
+    return z.reshape(tuple(lead) + (T, d)), W.reshape(tuple(lead) + (d, d))

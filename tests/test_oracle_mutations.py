@@ -1,0 +1,99 @@
+"""Plant plausible mistakes in a copy of the oracle (CPU only) and check the pins catch them.
+
+Each mutation edits the oracle's source text (a dropped term, a wrong sign, a transposed
+operand, the wrong weights for a gradient or an output) and loads the edited text as a
+throw-away module.  The pins of test_oracle_pins are then run against that module; at
+least one of them must fail for every mutation.  The real oracle is never modified.
+"""
+import inspect
+import types
+
+import pytest
+
+import oracle.ttt_oracle as real_oracle
+import tests.test_oracle_pins as pins
+
+MUTATIONS = {
+    "output_reads_chunk_start_weights": (
+        "z[:, t] = linear_f(Wt, q2[:, t])", "z[:, t] = linear_f(Wc, q2[:, t])"),
+    "gradient_at_current_not_chunk_start": (
+        "G = G + linear_grad(Wc, k2[:, t]", "G = G + linear_grad(Wt, k2[:, t]"),
+    "dropped_learning_rate": ("Wt = Wc - eta * G", "Wt = Wc - G"),
+    "wrong_update_sign": ("Wt = Wc - eta * G", "Wt = Wc + eta * G"),
+    "transposed_linear_gradient": (
+        'return np.einsum("ni,nj->nij", r, k)', 'return np.einsum("ni,nj->nij", k, r)'),
+    "transposed_linear_model": (
+        'return np.einsum("nij,nj->ni", W, x)', 'return np.einsum("nji,nj->ni", W, x)'),
+    "dot_loss_sign": ("        r = -v\n    else:\n        raise ValueError(loss)\n    return np.einsum",
+                      "        r = v\n    else:\n        raise ValueError(loss)\n    return np.einsum"),
+    "delta_rule_transposed_write": (
+        'W = W + eta * np.einsum("ni,nj->nij", err, kt)',
+        'W = W + eta * np.einsum("ni,nj->nij", kt, err)'),
+    "delta_rule_output_before_write": (
+        '        W = W + eta * np.einsum("ni,nj->nij", err, kt)\n'
+        '        z[:, t] = np.einsum("nij,nj->ni", W, q2[:, t])',
+        '        z[:, t] = np.einsum("nij,nj->ni", W, q2[:, t])\n'
+        '        W = W + eta * np.einsum("ni,nj->nij", err, kt)'),
+    "silu_derivative_missing_term": ("return s * (1.0 + u * (1.0 - s))", "return s"),
+    "silu_is_sigmoid": ("return u / (1.0 + np.exp(-u))", "return 1.0 / (1.0 + np.exp(-u))"),
+    "mlp_backward_skips_activation": (
+        'du = np.einsum("nih,ni->nh", W2, r) * dsilu(u)',
+        'du = np.einsum("nih,ni->nh", W2, r)'),
+    "mlp_second_layer_not_updated": ("W2t = W2c - eta * G2", "W2t = W2c"),
+    "mlp_gradient_at_current_weights": (
+        "g1, g2 = mlp_grad(W1c, W2c, k2[:, t]", "g1, g2 = mlp_grad(W1t, W2t, k2[:, t]"),
+    "last_token_of_chunk_dropped": (
+        "for t in range(c0, min(c0 + b, T)):\n            G = G + linear_grad",
+        "for t in range(c0, min(c0 + b, T) - 1):\n            G = G + linear_grad"),
+    "noncausal_reads_initial_weights": (
+        "    if not causal:\n        for t in range(T):\n            z[:, t] = linear_f(W, q2[:, t])",
+        "    if not causal:\n        W = _broadcast_state(w0, lead, dtype)\n"
+        "        for t in range(T):\n            z[:, t] = linear_f(W, q2[:, t])"),
+}
+
+
+def _pin_calls():
+    calls = []
+    for name, fn in inspect.getmembers(pins, inspect.isfunction):
+        if not name.startswith("test_"):
+            continue
+        marks = getattr(fn, "pytestmark", [])
+        params = [m for m in marks if m.name == "parametrize"]
+        if not params:
+            calls.append((name, fn, {}))
+            continue
+        m = params[0]
+        argnames = [a.strip() for a in m.args[0].split(",")]
+        for vals in m.args[1]:
+            if len(argnames) == 1:
+                vals = (vals,)
+            calls.append((f"{name}{vals}", fn, dict(zip(argnames, vals))))
+    return calls
+
+
+def _mutant(old, new):
+    src = inspect.getsource(real_oracle)
+    assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new, 1), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_mutation(name, monkeypatch):
+    old, new = MUTATIONS[name]
+    monkeypatch.setattr(pins, "O", _mutant(old, new))
+    caught = []
+    for pin_name, fn, kw in _pin_calls():
+        try:
+            fn(**kw)
+        except Exception:  # assertion or a shape error both count as caught
+            caught.append(pin_name)
+    assert caught, f"no pin caught mutation {name}"
+
+
+def test_unmutated_copy_passes_every_pin(monkeypatch):
+    """Control: the exec'd copy of the untouched source passes all pins."""
+    monkeypatch.setattr(pins, "O", _mutant("import numpy as np", "import numpy as np"))
+    for pin_name, fn, kw in _pin_calls():
+        fn(**kw)

@@ -1,0 +1,448 @@
+"""Pins of the CPU oracle to what the pages and mathematics fix (CPU only).
+
+Each test checks the oracle against something other than itself: hand-worked examples,
+closed forms (linear attention, the non-causal one-step solution, the delta-rule
+contraction), invariants (perfect write, orthonormal keys, zero tokens, state carry),
+central finite differences and torch.autograd.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import ttt_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_examples.json")
+TOL = 1e-12
+
+
+def _rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+def _rand_chains(rng, N, T, d, unit=False):
+    q = rng.standard_normal((N, T, d))
+    k = rng.standard_normal((N, T, d))
+    v = rng.standard_normal((N, T, d))
+    if unit:
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    return q, k, v
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _A(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+# ---------------------------------------------------------------- hand-worked examples
+
+def test_golden_delta_rule_by_hand():
+    g = _golden()["delta_rule_d2"]
+    for fn in ("delta", "linear_b1"):
+        if fn == "delta":
+            z, w = O.delta_rule(_A(g["q"]), _A(g["k"]), _A(g["v"]), _A(g["w0"]), g["eta"])
+        else:
+            z, w = O.ttt_linear(_A(g["q"]), _A(g["k"]), _A(g["v"]), _A(g["w0"]), g["eta"], 1)
+        np.testing.assert_allclose(z, _A(g["z"]), atol=TOL, rtol=0)
+        np.testing.assert_allclose(w, _A(g["w_final"]), atol=TOL, rtol=0)
+
+
+def test_golden_minibatch_by_hand():
+    g = _golden()["minibatch_scalar"]
+    args = (_A(g["q"]), _A(g["k"]), _A(g["v"]), _A(g["w0"]), g["eta"])
+    z, w = O.ttt_linear(*args, 1)
+    np.testing.assert_allclose(z, _A(g["z_b1"]), atol=TOL)
+    np.testing.assert_allclose(w, _A(g["w_final_b1"]), atol=TOL)
+    z, w = O.ttt_linear(*args, 2)
+    np.testing.assert_allclose(z, _A(g["z_b2"]), atol=TOL)
+    np.testing.assert_allclose(w, _A(g["w_final_b2"]), atol=TOL)
+    z, w = O.ttt_linear(*args, 2, causal=False)
+    np.testing.assert_allclose(z, _A(g["z_b2_noncausal"]), atol=TOL)
+
+
+def test_golden_mlp_by_hand():
+    g = _golden()["mlp_scalar"]
+    z, w1, w2 = O.ttt_mlp(_A(g["q"]), _A(g["k"]), _A(g["v"]), _A(g["w1"]), _A(g["w2"]),
+                          g["eta"], 1)
+    np.testing.assert_allclose(z, _A(g["z"]), atol=TOL)
+    np.testing.assert_allclose(w1, _A(g["w1_final"]), atol=TOL)
+    np.testing.assert_allclose(w2, _A(g["w2_final"]), atol=TOL)
+
+
+def test_golden_dot_loss_by_hand():
+    g = _golden()["dot_loss_linear_attention_scalar"]
+    for b in (1, 2):
+        z, _ = O.ttt_linear(_A(g["q"]), _A(g["k"]), _A(g["v"]), _A(g["w0"]), g["eta"], b,
+                            loss="dot")
+        np.testing.assert_allclose(z, _A(g["z"]), atol=TOL)
+
+
+# ---------------------------------------------------------------- closed forms
+
+def _linear_attention_causal(q, k, v, eta):
+    # eta * tril(Q K^T) V, diagonal included (each output sees its own key/value).
+    s = np.einsum("ntd,nsd->nts", q, k)
+    s = np.tril(s)
+    return eta * np.einsum("nts,nsd->ntd", s, v)
+
+
+@pytest.mark.parametrize("chunk", [1, 3, 16, 37])
+def test_dot_loss_equals_linear_attention_for_every_chunk(chunk):
+    """Negative dot-product loss, W0 = 0: the gradient -v k^T does not depend on W, so
+    every mini-batch size gives the linear-attention cumulative sum."""
+    rng = _rng(1)
+    q, k, v = _rand_chains(rng, 3, 37, 5)
+    w0 = np.zeros((3, 5, 5))
+    z, w = O.ttt_linear(q, k, v, w0, 0.3, chunk, loss="dot")
+    np.testing.assert_allclose(z, _linear_attention_causal(q, k, v, 0.3), atol=1e-12)
+    np.testing.assert_allclose(w, 0.3 * np.einsum("ntd,nte->nde", v, k), atol=1e-12)
+
+
+def test_theorem1_batch_gd_mse_from_zero_is_linear_attention():
+    """Linear inner model, batch GD (one chunk of all T tokens), W0 = 0, reconstruction
+    loss: the gradient at W0 = 0 is -v k^T, so the causal outputs are linear attention."""
+    rng = _rng(2)
+    q, k, v = _rand_chains(rng, 2, 24, 6)
+    z, _ = O.ttt_linear(q, k, v, np.zeros((2, 6, 6)), 0.7, 24)
+    np.testing.assert_allclose(z, _linear_attention_causal(q, k, v, 0.7), atol=1e-12)
+    # non-causal: every query reads the full sum
+    z, _ = O.ttt_linear(q, k, v, np.zeros((2, 6, 6)), 0.7, 24, causal=False)
+    full = 0.7 * np.einsum("ntd,nsd,nse->nte", q, k, v)
+    np.testing.assert_allclose(z, full, atol=1e-12)
+
+
+def test_noncausal_one_step_closed_form():
+    """One full-batch step: W' = W0 - eta (W0 K^T - V^T) K, Z = Q W'^T."""
+    rng = _rng(3)
+    q, k, v = _rand_chains(rng, 2, 11, 4)
+    w0 = 0.3 * rng.standard_normal((2, 4, 4))
+    eta = 0.05
+    z, w = O.ttt_linear(q, k, v, w0, eta, 11, causal=False)
+    Kt = np.swapaxes(k, 1, 2)
+    Wp = w0 - eta * (w0 @ Kt - np.swapaxes(v, 1, 2)) @ k
+    np.testing.assert_allclose(w, Wp, atol=1e-12)
+    np.testing.assert_allclose(z, q @ np.swapaxes(Wp, 1, 2), atol=1e-12)
+
+
+def test_noncausal_mlp_chunk_T_is_one_full_batch_step():
+    """Non-causal MLP with one chunk: W' = W - eta * sum of per-token gradients at W."""
+    rng = _rng(4)
+    q, k, v = _rand_chains(rng, 2, 9, 3)
+    w1 = 0.5 * rng.standard_normal((2, 5, 3))
+    w2 = 0.5 * rng.standard_normal((2, 3, 5))
+    eta = 0.2
+    z, a1, a2 = O.ttt_mlp(q, k, v, w1, w2, eta, 9, causal=False)
+    # matrix form of the summed gradient (independent of the per-token loop)
+    U = np.einsum("nhd,ntd->nth", w1, k)
+    A = U / (1 + np.exp(-U))
+    sg = 1 / (1 + np.exp(-U))
+    R = np.einsum("ndh,nth->ntd", w2, A) - v
+    dU = np.einsum("ntd,ndh->nth", R, w2) * sg * (1 + U * (1 - sg))
+    W1p = w1 - eta * np.einsum("nth,ntd->nhd", dU, k)
+    W2p = w2 - eta * np.einsum("ntd,nth->ndh", R, A)
+    np.testing.assert_allclose(a1, W1p, atol=1e-12)
+    np.testing.assert_allclose(a2, W2p, atol=1e-12)
+    Aq = np.einsum("nhd,ntd->nth", W1p, q)
+    Aq = Aq / (1 + np.exp(-Aq))
+    np.testing.assert_allclose(z, np.einsum("ndh,nth->ntd", W2p, Aq), atol=1e-12)
+
+
+# ---------------------------------------------------------------- finite differences
+
+def _fd_check(loss_fn, params, idx, grad, eps=1e-5):
+    """Central difference of loss_fn with respect to params[idx], compared to grad."""
+    P = [p.copy() for p in params]
+    num = np.zeros_like(P[idx])
+    it = np.nditer(P[idx], flags=["multi_index"])
+    for _ in it:
+        m = it.multi_index
+        old = P[idx][m]
+        P[idx][m] = old + eps
+        fp = loss_fn(*P)
+        P[idx][m] = old - eps
+        fm = loss_fn(*P)
+        P[idx][m] = old
+        num[m] = (fp - fm).sum() / (2 * eps)
+    scale = max(np.abs(grad).max(), 1e-3)
+    assert np.abs(num - grad).max() / scale < 1e-7, (num, grad)
+
+
+@pytest.mark.parametrize("loss", ["mse", "dot"])
+def test_linear_gradient_finite_differences(loss):
+    rng = _rng(5)
+    W = rng.standard_normal((1, 3, 4))
+    k = rng.standard_normal((1, 4))
+    v = rng.standard_normal((1, 3))
+    g = O.linear_grad(W, k, v, loss)
+    _fd_check(lambda W_: O.linear_loss(W_, k, v, loss), [W], 0, g)
+
+
+@pytest.mark.parametrize("loss", ["mse", "dot"])
+def test_mlp_gradient_finite_differences(loss):
+    rng = _rng(6)
+    W1 = rng.standard_normal((1, 7, 4))
+    W2 = rng.standard_normal((1, 4, 7))
+    k = rng.standard_normal((1, 4))
+    v = rng.standard_normal((1, 4))
+    g1, g2 = O.mlp_grad(W1, W2, k, v, loss)
+    _fd_check(lambda a, b: O.mlp_loss(a, b, k, v, loss), [W1, W2], 0, g1)
+    _fd_check(lambda a, b: O.mlp_loss(a, b, k, v, loss), [W1, W2], 1, g2)
+
+
+def test_silu_derivative_finite_differences():
+    u = np.linspace(-6, 6, 49)
+    eps = 1e-6
+    num = (O.silu(u + eps) - O.silu(u - eps)) / (2 * eps)
+    np.testing.assert_allclose(O.dsilu(u), num, atol=1e-8)
+    np.testing.assert_allclose(O.silu(u), u / (1 + np.exp(-u)), atol=1e-15)
+
+
+# ---------------------------------------------------------------- delta-rule invariants
+
+def test_linear_chunk1_equals_delta_rule():
+    """Mini-batch size 1 of the generic recurrence equals the delta rule written in its
+    closed form (prediction-error update)."""
+    rng = _rng(7)
+    q, k, v = _rand_chains(rng, 3, 40, 6)
+    w0 = 0.2 * rng.standard_normal((3, 6, 6))
+    z1, w1 = O.ttt_linear(q, k, v, w0, 0.05, 1)
+    z2, w2 = O.delta_rule(q, k, v, w0, 0.05)
+    np.testing.assert_allclose(z1, z2, atol=1e-12)
+    np.testing.assert_allclose(w1, w2, atol=1e-12)
+
+
+def test_perfect_write():
+    """Unit keys, eta = 1, one token per step: after writing (k_t, v_t) the state maps k_t
+    exactly to v_t, so querying with q_t = k_t returns v_t."""
+    rng = _rng(8)
+    q, k, v = _rand_chains(rng, 2, 30, 8, unit=True)
+    w0 = rng.standard_normal((2, 8, 8))
+    for fn in ("delta", "linear"):
+        if fn == "delta":
+            z, _ = O.delta_rule(k, k, v, w0, 1.0)
+        else:
+            z, _ = O.ttt_linear(k, k, v, w0, 1.0, 1)
+        np.testing.assert_allclose(z, v, atol=1e-10)
+
+
+@pytest.mark.parametrize("eta", [0.3, 1.0, 1.7])
+def test_repeated_write_contracts_geometrically(eta):
+    """Writing one unit key n times: W_n k - v = (1 - eta)^n (W_0 k - v)."""
+    rng = _rng(9)
+    d, n = 5, 12
+    kk = rng.standard_normal(d)
+    kk /= np.linalg.norm(kk)
+    vv = rng.standard_normal(d)
+    w0 = rng.standard_normal((d, d))
+    k = np.tile(kk, (n, 1))
+    v = np.tile(vv, (n, 1))
+    q = rng.standard_normal((n, d))
+    for fn in ("delta", "linear"):
+        if fn == "delta":
+            _, w = O.delta_rule(q, k, v, w0, eta)
+        else:
+            _, w = O.ttt_linear(q, k, v, w0, eta, 1)
+        np.testing.assert_allclose(w @ kk - vv, (1 - eta) ** n * (w0 @ kk - vv), atol=1e-10)
+
+
+def test_predictable_pairs_do_not_write():
+    """If every value is already predicted by the state (v = W0 k), no gradient is taken
+    and the state stays W0 for every chunk size."""
+    rng = _rng(10)
+    q, k, _ = _rand_chains(rng, 2, 20, 5)
+    w0 = rng.standard_normal((2, 5, 5))
+    v = np.einsum("nij,ntj->nti", w0, k)
+    for b in (1, 4, 20):
+        z, w = O.ttt_linear(q, k, v, w0, 0.4, b)
+        np.testing.assert_allclose(w, w0, atol=1e-12)
+        np.testing.assert_allclose(z, np.einsum("nij,ntj->nti", w0, q), atol=1e-12)
+
+
+def test_orthonormal_keys_make_every_chunk_size_exact():
+    """With orthonormal keys the gradient of token t at the chunk-start weights equals its
+    gradient at W_{t-1}, so every mini-batch size reproduces the b = 1 result."""
+    rng = _rng(11)
+    d, T = 8, 8
+    perm = rng.permutation(d)
+    basis, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    k = basis[:, perm].T[None]               # rows are orthonormal keys
+    q = rng.standard_normal((1, T, d))
+    v = rng.standard_normal((1, T, d))
+    w0 = rng.standard_normal((1, d, d))
+    ref, wref = O.ttt_linear(q, k, v, w0, 0.6, 1)
+    for b in (2, 3, 5, 8):
+        z, w = O.ttt_linear(q, k, v, w0, 0.6, b)
+        np.testing.assert_allclose(z, ref, atol=1e-12)
+        np.testing.assert_allclose(w, wref, atol=1e-12)
+
+
+def test_chunking_matters_for_correlated_keys():
+    """Guard against an oracle that silently ignores the chunk size."""
+    rng = _rng(12)
+    q, k, v = _rand_chains(rng, 1, 16, 4)
+    w0 = np.zeros((1, 4, 4))
+    z1, _ = O.ttt_linear(q, k, v, w0, 0.2, 1)
+    z4, _ = O.ttt_linear(q, k, v, w0, 0.2, 4)
+    assert np.abs(z1 - z4).max() > 1e-3
+
+
+# ---------------------------------------------------------------- state carry / padding
+
+@pytest.mark.parametrize("model", ["linear", "mlp"])
+def test_state_carry_at_chunk_boundary(model):
+    """Running T tokens in one call equals two calls split at a multiple of the chunk
+    size, the second starting from the first call's final state."""
+    rng = _rng(13)
+    q, k, v = _rand_chains(rng, 2, 40, 4, unit=True)
+    if model == "linear":
+        w0 = 0.1 * rng.standard_normal((2, 4, 4))
+        z, w = O.ttt_linear(q, k, v, w0, 0.3, 8)
+        za, wa = O.ttt_linear(q[:, :24], k[:, :24], v[:, :24], w0, 0.3, 8)
+        zb, wb = O.ttt_linear(q[:, 24:], k[:, 24:], v[:, 24:], wa, 0.3, 8)
+        np.testing.assert_allclose(w, wb, atol=1e-12)
+    else:
+        w1 = 0.3 * rng.standard_normal((2, 6, 4))
+        w2 = 0.3 * rng.standard_normal((2, 4, 6))
+        z, a1, a2 = O.ttt_mlp(q, k, v, w1, w2, 0.3, 8)
+        za, b1, b2 = O.ttt_mlp(q[:, :24], k[:, :24], v[:, :24], w1, w2, 0.3, 8)
+        zb, c1, c2 = O.ttt_mlp(q[:, 24:], k[:, 24:], v[:, 24:], b1, b2, 0.3, 8)
+        np.testing.assert_allclose(a1, c1, atol=1e-12)
+        np.testing.assert_allclose(a2, c2, atol=1e-12)
+    np.testing.assert_allclose(z, np.concatenate([za, zb], axis=1), atol=1e-12)
+
+
+def test_zero_tokens_change_nothing():
+    """Tokens with k = v = 0 have zero gradient (no bias, SiLU(0) = 0), so appending them
+    to a full-batch chunk leaves the trained weights and the other outputs unchanged."""
+    rng = _rng(14)
+    q, k, v = _rand_chains(rng, 2, 10, 4)
+    w1 = 0.4 * rng.standard_normal((2, 6, 4))
+    w2 = 0.4 * rng.standard_normal((2, 4, 6))
+    z, a1, a2 = O.ttt_mlp(q, k, v, w1, w2, 0.5, 10, causal=False)
+    pad = np.zeros((2, 3, 4))
+    qp = np.concatenate([q, rng.standard_normal((2, 3, 4))], axis=1)
+    zp, b1, b2 = O.ttt_mlp(qp, np.concatenate([k, pad], 1), np.concatenate([v, pad], 1),
+                           w1, w2, 0.5, 13, causal=False)
+    np.testing.assert_allclose(b1, a1, atol=1e-12)
+    np.testing.assert_allclose(b2, a2, atol=1e-12)
+    np.testing.assert_allclose(zp[:, :10], z, atol=1e-12)
+    # same for the linear model
+    w0 = rng.standard_normal((2, 4, 4))
+    z, w = O.ttt_linear(q, k, v, w0, 0.1, 10, causal=False)
+    zp, wp = O.ttt_linear(qp, np.concatenate([k, pad], 1), np.concatenate([v, pad], 1),
+                          w0, 0.1, 13, causal=False)
+    np.testing.assert_allclose(wp, w, atol=1e-12)
+    np.testing.assert_allclose(zp[:, :10], z, atol=1e-12)
+
+
+def test_state_broadcast_over_batch():
+    """A [H, d, d] initial state is shared by every batch element."""
+    rng = _rng(15)
+    q, k, v = [rng.standard_normal((3, 2, 10, 4)) for _ in range(3)]
+    w0 = rng.standard_normal((2, 4, 4))
+    z, w = O.ttt_linear(q, k, v, w0, 0.1, 4)
+    for b in range(3):
+        zb, wb = O.ttt_linear(q[b], k[b], v[b], w0, 0.1, 4)
+        np.testing.assert_allclose(z[b], zb, atol=1e-13)
+        np.testing.assert_allclose(w[b], wb, atol=1e-13)
+
+
+# ---------------------------------------------------------------- torch.autograd
+
+def _autograd_chunked(q, k, v, params, f, eta, chunk, causal):
+    """Mini-batch GD computed with torch.autograd for the gradients (float64, CPU)."""
+    import torch
+    T = q.shape[0]
+    P = [torch.tensor(p, dtype=torch.float64) for p in params]
+    Q, K, V = (torch.tensor(x, dtype=torch.float64) for x in (q, k, v))
+    Z = torch.zeros_like(Q)
+    for c0 in range(0, T, chunk):
+        Pc = [p.clone().requires_grad_(True) for p in P]
+        acc = [torch.zeros_like(p) for p in P]
+        cur = P
+        for t in range(c0, min(c0 + chunk, T)):
+            loss = 0.5 * ((f(Pc, K[t]) - V[t]) ** 2).sum()
+            grads = torch.autograd.grad(loss, Pc)
+            acc = [a + g for a, g in zip(acc, grads)]
+            cur = [pc.detach() - eta * a for pc, a in zip(Pc, acc)]
+            if causal:
+                with torch.no_grad():
+                    Z[t] = f(cur, Q[t])
+        P = cur
+    if not causal:
+        with torch.no_grad():
+            for t in range(T):
+                Z[t] = f(P, Q[t])
+    return Z.numpy(), [p.detach().numpy() for p in P]
+
+
+def _torch_mlp(P, x):
+    import torch
+    return P[1] @ torch.nn.functional.silu(P[0] @ x)
+
+
+def _torch_linear(P, x):
+    return P[0] @ x
+
+
+@pytest.mark.parametrize("chunk,causal", [(1, True), (4, True), (7, True), (13, False),
+                                          (5, False)])
+def test_mlp_matches_autograd(chunk, causal):
+    rng = _rng(16)
+    q, k, v = _rand_chains(rng, 1, 13, 3)
+    w1 = 0.5 * rng.standard_normal((6, 3))
+    w2 = 0.5 * rng.standard_normal((3, 6))
+    z, a1, a2 = O.ttt_mlp(q[0], k[0], v[0], w1, w2, 0.15, chunk, causal=causal)
+    zr, (r1, r2) = _autograd_chunked(q[0], k[0], v[0], [w1, w2], _torch_mlp, 0.15, chunk,
+                                     causal)
+    np.testing.assert_allclose(z, zr, atol=1e-12)
+    np.testing.assert_allclose(a1, r1, atol=1e-12)
+    np.testing.assert_allclose(a2, r2, atol=1e-12)
+
+
+@pytest.mark.parametrize("chunk,causal", [(1, True), (4, True), (6, False)])
+def test_linear_matches_autograd(chunk, causal):
+    rng = _rng(17)
+    q, k, v = _rand_chains(rng, 1, 14, 4)
+    w0 = 0.3 * rng.standard_normal((4, 4))
+    z, w = O.ttt_linear(q[0], k[0], v[0], w0, 0.1, chunk, causal=causal)
+    zr, (wr,) = _autograd_chunked(q[0], k[0], v[0], [w0], _torch_linear, 0.1, chunk, causal)
+    np.testing.assert_allclose(z, zr, atol=1e-12)
+    np.testing.assert_allclose(w, wr, atol=1e-12)
+
+
+# ---------------------------------------------------------------- edge cases
+
+def test_empty_sequence():
+    q = np.zeros((2, 0, 4))
+    w0 = np.ones((2, 4, 4))
+    z, w = O.ttt_linear(q, q, q, w0, 0.1, 16)
+    assert z.shape == (2, 0, 4)
+    np.testing.assert_array_equal(w, w0)
+
+
+def test_chunk_longer_than_sequence_is_one_chunk():
+    rng = _rng(18)
+    q, k, v = _rand_chains(rng, 1, 5, 3)
+    w0 = rng.standard_normal((1, 3, 3))
+    a = O.ttt_linear(q, k, v, w0, 0.1, 5)
+    b = O.ttt_linear(q, k, v, w0, 0.1, 64)
+    np.testing.assert_allclose(a[0], b[0], atol=1e-14)
+
+
+def test_ragged_last_chunk():
+    """T = 10 with chunk 4: the chunks are 4, 4, 2 tokens, i.e. the same as running the
+    first 8 tokens and then 2 tokens with chunk 2 from the carried state."""
+    rng = _rng(19)
+    q, k, v = _rand_chains(rng, 1, 10, 3)
+    w0 = rng.standard_normal((1, 3, 3))
+    z, w = O.ttt_linear(q, k, v, w0, 0.1, 4)
+    za, wa = O.ttt_linear(q[:, :8], k[:, :8], v[:, :8], w0, 0.1, 4)
+    zb, wb = O.ttt_linear(q[:, 8:], k[:, 8:], v[:, 8:], wa, 0.1, 2)
+    np.testing.assert_allclose(z, np.concatenate([za, zb], 1), atol=1e-13)
+    np.testing.assert_allclose(w, wb, atol=1e-13)
