@@ -1,0 +1,102 @@
+/*
+ * ttt.h - C ABI of libttt.so, the MI355X (gfx950) TTT-layer forward pass.
+ *
+ * The method (test-time training layers): a small inner model f(k; W) is trained inside
+ * the sequence by gradient descent on the reconstruction loss 1/2 ||f(k; W) - v||^2 and
+ * every output reads the trained model, z_t = f(q_t; W_t).  Tokens are processed in
+ * mini-batches ("chunks") of b consecutive tokens: every gradient of a chunk is taken at
+ * the weights left by the previous chunk, and W_t = W_chunk - eta * sum_{s<=t} grad l_s.
+ * b = 1 is the delta rule, one chunk of all tokens is batch gradient descent.
+ *   - update / output rule: blog page "TTT: Test-Time Training", section TTT (general
+ *     form); page "5.1 Fast weights and TTT layers", opening formula and section 1;
+ *   - mini-batch rule: wmrh.cn summary of Sun et al. 2024, section 1.2.2 (mini-batch TTT);
+ *   - non-causal full-batch use: ViT3 news page, section 1 (inner training setup).
+ *
+ * Conventions shared by every entry point
+ *   - Token tensors q, k, v, z are dense row-major [B][H][T][d] in the I/O dtype
+ *     (TTT_F32 = float32, TTT_BF16 = bfloat16).  They are device pointers (HIP global
+ *     memory) owned by the caller; outputs must not overlap inputs.
+ *   - States are float32, row-major, f(k; W) = W k with W[d_out][d_in]:
+ *       linear: W [d][d];   MLP: W1 [dh][d], W2 [d][dh]  (f(k) = W2 SiLU(W1 k)).
+ *     The initial state of (batch b, head h) starts at  base + b * batch_stride +
+ *     h * (state size); batch_stride 0 shares one [H][...] state across the batch.
+ *   - Final-state outputs (w_out, w1_out, w2_out) are dense [B][H][...] float32, or NULL.
+ *   - eta is the scalar inner learning rate; chunk >= 1 (a chunk longer than T is one
+ *     chunk of T tokens; when T is not a multiple of chunk the last chunk is shorter).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream).  Calls are
+ *     asynchronous, never synchronise, keep no pointer after returning and are thread-safe.
+ *   - Arguments are validated on the host before any HIP call.  Return values:
+ *       TTT_OK             work enqueued;
+ *       TTT_E_INVALID      a null required pointer, a non-positive size, chunk < 1, a
+ *                          non-finite eta, an unknown dtype or a size overflow;
+ *       TTT_E_UNSUPPORTED  a valid combination with no kernel (see each function);
+ *       TTT_E_HIP          a HIP runtime error (launch failure, workspace allocation).
+ *     ttt_last_error() returns the calling thread's message for the last non-OK status.
+ */
+#ifndef TTT_H_
+#define TTT_H_
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* ttt_stream_t; /* identical to hipStream_t */
+
+enum { TTT_OK = 0, TTT_E_INVALID = -1, TTT_E_UNSUPPORTED = -2, TTT_E_HIP = -3 };
+enum { TTT_F32 = 0, TTT_BF16 = 1 };
+
+/*
+ * TTT-Linear forward: f(k; W) = W k, reconstruction loss, mini-batch GD of size `chunk`.
+ * Gradient (W k - v) k^T ("Fast weights" page, section 1).  causal = 1: z_t = W_t q_t with
+ * W_t including the token's own update; causal = 0: every chunk is trained first and all
+ * queries read the final W (ViT3 news page, section 1).
+ *   q, k, v  [B][H][T][d] io_dtype            z      [B][H][T][d] io_dtype (out)
+ *   w0       float32, per (b, h) a [d][d]     w_out  [B][H][d][d] float32 (out) or NULL
+ * Supported: d in {16, 32, 64}, any chunk, both dtypes, causal 0/1.  T may be 0 (then z is
+ * untouched and w_out receives the initial state).
+ */
+int ttt_linear_fwd(const void* q, const void* k, const void* v,
+                   const float* w0, long long w0_batch_stride,
+                   void* z, float* w_out,
+                   int B, int H, int T, int d, int chunk, int causal, float eta,
+                   int io_dtype, ttt_stream_t stream);
+
+/*
+ * TTT-MLP forward: f(k; W1, W2) = W2 SiLU(W1 k) with hidden width dh, no bias (ViT3 news
+ * page, section 2: 2-layer SiLU inner MLP), reconstruction loss, mini-batch GD.
+ *   w1  float32, per (b, h) a [dh][d];  w2  float32, per (b, h) a [d][dh]; both use
+ *   w_batch_stride as the distance between batch elements (0 = shared across the batch).
+ *   w1_out [B][H][dh][d], w2_out [B][H][d][dh] float32 (out) or NULL.
+ * Supported: d in {16, 32, 64}, 1 <= dh <= 512, any chunk, both dtypes, causal 0/1.
+ * Some shapes run on a device workspace that the library allocates once per device on
+ * first use and keeps until the process exits (TTT_E_HIP if that allocation fails).
+ */
+int ttt_mlp_fwd(const void* q, const void* k, const void* v,
+                const float* w1, const float* w2, long long w_batch_stride,
+                void* z, float* w1_out, float* w2_out,
+                int B, int H, int T, int d, int dh, int chunk, int causal, float eta,
+                int io_dtype, ttt_stream_t stream);
+
+/*
+ * Delta rule (mini-batch of one token, causal): W_t = W_{t-1} + eta (v_t - W_{t-1} k_t) k_t^T,
+ * z_t = W_t q_t ("Fast weights" page, section 1).  Same arguments as ttt_linear_fwd
+ * without chunk / causal.  Supported: d in {16, 32, 64}, both dtypes.
+ */
+int delta_rule_fwd(const void* q, const void* k, const void* v,
+                   const float* w0, long long w0_batch_stride,
+                   void* z, float* w_out,
+                   int B, int H, int T, int d, float eta,
+                   int io_dtype, ttt_stream_t stream);
+
+/* Message for the calling thread's last non-OK status ("" if none).  Owned by the library;
+   valid until the thread's next call into it. */
+const char* ttt_last_error(void);
+
+/* ABI version of this header (incremented on any incompatible change). */
+int ttt_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TTT_H_ */

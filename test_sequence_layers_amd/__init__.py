@@ -1,0 +1,22 @@
+"""MI355X-native (gfx950) TTT-layer forward pass.
+
+The compute runs in libttt.so (C ABI, include/ttt.h): hand-written HIP kernels for the
+TTT-Linear, TTT-MLP and delta-rule forward passes.  This package holds the ctypes binding
+(argument marshalling only), the in-tree build script and the seeded synthetic workloads.
+"""
+from ._binding import (  # noqa: F401
+    LIB_PATH,
+    SIGNATURES,
+    TTT_BF16,
+    TTT_E_HIP,
+    TTT_E_INVALID,
+    TTT_E_UNSUPPORTED,
+    TTT_F32,
+    TTT_OK,
+    TTTError,
+    delta_rule_fwd,
+    last_error,
+    load_library,
+    ttt_linear_fwd,
+    ttt_mlp_fwd,
+)

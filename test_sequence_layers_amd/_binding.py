@@ -1,0 +1,203 @@
+"""ctypes binding of libttt.so.
+
+Argument marshalling only: every step of the forward pass runs in the library's HIP
+kernels.  PyTorch supplies device memory and the current stream.  There is no CPU
+fallback; if the library is missing every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libttt.so")
+
+TTT_OK, TTT_E_INVALID, TTT_E_UNSUPPORTED, TTT_E_HIP = 0, -1, -2, -3
+TTT_F32, TTT_BF16 = 0, 1
+
+_lib = None
+_lock = threading.Lock()
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_ll = ctypes.c_longlong
+_f = ctypes.c_float
+
+# name -> (restype, argtypes); mirrors include/ttt.h
+SIGNATURES = {
+    "ttt_linear_fwd": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
+    "ttt_mlp_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp,
+                         _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
+    "delta_rule_fwd": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp]),
+    "ttt_last_error": (ctypes.c_char_p, []),
+    "ttt_abi_version": (_i, []),
+}
+
+
+class TTTError(RuntimeError):
+    def __init__(self, code, message):
+        super().__init__(f"libttt error {code}: {message}")
+        self.code = code
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libttt.so once (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build it with `python -m test_sequence_layers_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+        return lib
+
+
+def last_error() -> str:
+    return load_library().ttt_last_error().decode()
+
+
+def _check(rc):
+    if rc != TTT_OK:
+        raise TTTError(rc, last_error())
+
+
+# --------------------------------------------------------------------------- torch wrappers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _io_dtype(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return TTT_F32
+    if t.dtype == torch.bfloat16:
+        return TTT_BF16
+    raise TypeError(f"token tensors must be float32 or bfloat16, got {t.dtype}")
+
+
+def _tokens(q, k, v):
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 4:
+            raise ValueError(f"{name} must be a [B, H, T, d] tensor")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on a GPU")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k and v must have the same shape")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k and v must have the same dtype")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k and v must be on the same device")
+    return tuple(q.shape)
+
+
+def _state(w, B, H, shape, name, device):
+    """Return (tensor, batch_stride_in_floats) for an initial state [H,...] or [B,H,...]."""
+    torch = _torch()
+    if not isinstance(w, torch.Tensor) or w.dtype != torch.float32 or not w.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 tensor")
+    if w.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    per = 1
+    for s in shape:
+        per *= s
+    if tuple(w.shape) == (H, *shape):
+        return w, 0
+    if tuple(w.shape) == (B, H, *shape):
+        return w, H * per
+    raise ValueError(f"{name} must have shape [H, {shape}] or [B, H, {shape}], got {tuple(w.shape)}")
+
+
+def _stream(device, stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _out(t, shape, dtype, device, name):
+    torch = _torch()
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}")
+    return t
+
+
+def ttt_linear_fwd(q, k, v, w0, eta, chunk, causal=True, *, z=None, w_out=None,
+                   return_state=False, stream=None):
+    """TTT-Linear forward.  q, k, v [B,H,T,d] (float32 or bfloat16, same device);
+    w0 float32 [H,d,d] (shared over the batch) or [B,H,d,d].  Returns z (and the final
+    state [B,H,d,d] when return_state or w_out is given)."""
+    torch = _torch()
+    lib = load_library()
+    B, H, T, d = _tokens(q, k, v)
+    w0, stride = _state(w0, B, H, (d, d), "w0", q.device)
+    z = _out(z, (B, H, T, d), q.dtype, q.device, "z")
+    if return_state or w_out is not None:
+        w_out = _out(w_out, (B, H, d, d), torch.float32, q.device, "w_out")
+    with torch.cuda.device(q.device):
+        rc = lib.ttt_linear_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), w0.data_ptr(), stride,
+                                z.data_ptr(), w_out.data_ptr() if w_out is not None else None,
+                                B, H, T, d, int(chunk), int(bool(causal)), float(eta),
+                                _io_dtype(q), _stream(q.device, stream))
+    _check(rc)
+    return (z, w_out) if w_out is not None else z
+
+
+def delta_rule_fwd(q, k, v, w0, eta, *, z=None, w_out=None, return_state=False, stream=None):
+    """Delta-rule forward (one token per update, causal).  Arguments as ttt_linear_fwd."""
+    torch = _torch()
+    lib = load_library()
+    B, H, T, d = _tokens(q, k, v)
+    w0, stride = _state(w0, B, H, (d, d), "w0", q.device)
+    z = _out(z, (B, H, T, d), q.dtype, q.device, "z")
+    if return_state or w_out is not None:
+        w_out = _out(w_out, (B, H, d, d), torch.float32, q.device, "w_out")
+    with torch.cuda.device(q.device):
+        rc = lib.delta_rule_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), w0.data_ptr(), stride,
+                                z.data_ptr(), w_out.data_ptr() if w_out is not None else None,
+                                B, H, T, d, float(eta), _io_dtype(q), _stream(q.device, stream))
+    _check(rc)
+    return (z, w_out) if w_out is not None else z
+
+
+def ttt_mlp_fwd(q, k, v, w1, w2, eta, chunk, causal=True, *, z=None, w1_out=None, w2_out=None,
+                return_state=False, stream=None):
+    """TTT-MLP forward, f(k) = W2 SiLU(W1 k).  w1 float32 [H,dh,d] or [B,H,dh,d], w2 float32
+    [H,d,dh] or [B,H,d,dh] (both shared or both per batch).  Returns z (and the final
+    states when return_state or an output state is given)."""
+    torch = _torch()
+    lib = load_library()
+    B, H, T, d = _tokens(q, k, v)
+    if w1.dim() < 2:
+        raise ValueError("w1 must be [H, dh, d] or [B, H, dh, d]")
+    dh = int(w1.shape[-2])
+    w1, s1 = _state(w1, B, H, (dh, d), "w1", q.device)
+    w2, s2 = _state(w2, B, H, (d, dh), "w2", q.device)
+    if s1 != s2:
+        raise ValueError("w1 and w2 must both be shared over the batch or both per batch")
+    z = _out(z, (B, H, T, d), q.dtype, q.device, "z")
+    want = return_state or w1_out is not None or w2_out is not None
+    if want:
+        w1_out = _out(w1_out, (B, H, dh, d), torch.float32, q.device, "w1_out")
+        w2_out = _out(w2_out, (B, H, d, dh), torch.float32, q.device, "w2_out")
+    with torch.cuda.device(q.device):
+        rc = lib.ttt_mlp_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), w1.data_ptr(),
+                             w2.data_ptr(), s1, z.data_ptr(),
+                             w1_out.data_ptr() if want else None,
+                             w2_out.data_ptr() if want else None,
+                             B, H, T, d, dh, int(chunk), int(bool(causal)), float(eta),
+                             _io_dtype(q), _stream(q.device, stream))
+    _check(rc)
+    return (z, w1_out, w2_out) if want else z

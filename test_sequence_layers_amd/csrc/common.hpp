@@ -1,0 +1,72 @@
+// Shared device/host helpers of libttt (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ttt {
+
+typedef __bf16 bf16;
+
+// Element conversion for the two I/O dtypes.  float -> bf16 rounds to nearest even
+// (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return static_cast<float>(x); }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }
+
+// SiLU and its derivative, fp32.  sigma(u) = 1 / (1 + exp(-u)).
+__device__ __forceinline__ float sigmoidf_(float u) { return 1.0f / (1.0f + __expf(-u)); }
+__device__ __forceinline__ float silu_(float u) { return u * sigmoidf_(u); }
+__device__ __forceinline__ float dsilu_(float u) {
+  const float s = sigmoidf_(u);
+  return s * (1.0f + u * (1.0f - s));
+}
+
+// Arguments of one forward call, as validated by the host API.
+struct LinearArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* w0;
+  long long w0_batch_stride;  // in floats
+  void* z;
+  float* w_out;
+  int B, H, T, d, chunk, causal;
+  float eta;
+};
+
+struct MlpArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* w1;
+  const float* w2;
+  long long w_batch_stride;  // in floats
+  void* z;
+  float* w1_out;
+  float* w2_out;
+  int B, H, T, d, dh, chunk, causal;
+  float eta;
+};
+
+// Host-side launchers (return a hipError_t; argument checks are done by the caller).
+hipError_t launch_linear_generic(const LinearArgs& a, bool bf16_io, hipStream_t s);
+hipError_t launch_mlp_generic(const MlpArgs& a, bool bf16_io, float* workspace, hipStream_t s);
+size_t mlp_generic_workspace_floats(const MlpArgs& a);
+
+// Matrix-core paths for the shapes they are written for (the *_supported predicates say
+// which); everything else runs on the generic kernels.
+bool linear_mfma_supported(const LinearArgs& a, bool bf16_io);
+hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s);
+bool delta_fast_supported(const LinearArgs& a, bool bf16_io);
+hipError_t launch_delta_fast(const LinearArgs& a, bool bf16_io, hipStream_t s);
+bool mlp_fast_supported(const MlpArgs& a, bool bf16_io);
+hipError_t launch_mlp_fast(const MlpArgs& a, hipStream_t s);
+
+// dst[b][h][:] = src + b * batch_stride + h * per_head (the state when T = 0).
+hipError_t launch_copy_state(float* dst, const float* src, long long batch_stride, int B, int H,
+                             size_t per_head, hipStream_t s);
+
+}  // namespace ttt

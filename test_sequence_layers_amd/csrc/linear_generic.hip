@@ -1,0 +1,159 @@
+// Generic TTT-Linear forward on the vector ALUs: any chunk size, causal or not, fp32 or
+// bf16 I/O, d in {16, 32, 64}.  One workgroup of 256 threads per (batch, head) chain.
+//
+// Method: mini-batch gradient descent on 1/2 ||W k - v||^2 (gradient (W k - v) k^T,
+// "Fast weights" page, section 1); inside a chunk every gradient is taken at the
+// chunk-start weights and W_t subtracts eta times the running sum (wmrh.cn summary of
+// Sun et al. 2024, section 1.2.2); z_t = W_t q_t (blog page "TTT: Test-Time Training",
+// general form).
+//
+// The chunk is walked in sub-blocks of S = 16 tokens.  Two fp32 states live in LDS:
+// Wc, the chunk-start weights every residual uses, and Wn, the weights after all earlier
+// sub-blocks of the chunk.  For a sub-block with residuals R = K Wc^T - V,
+//   z_t = Wn q_t - eta * sum_{s <= t in the sub-block} (q_t . k_s) r_s
+//   Wn  -= eta * R^T K,
+// and at the end of a chunk Wc <- Wn.  This equals the per-token recurrence up to
+// floating-point order.  With causal = 0 the training pass writes no output and a second
+// pass computes z_t = W_final q_t.
+#include "common.hpp"
+
+namespace ttt {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kSub = 16;
+
+template <typename IO, int D>
+__global__ __launch_bounds__(kThreads) void linear_generic_kernel(LinearArgs a) {
+  __shared__ float Wc[D][D + 1];
+  __shared__ float Wn[D][D + 1];
+  __shared__ float Qs[kSub][D + 1];
+  __shared__ float Ks[kSub][D + 1];
+  __shared__ float Vs[kSub][D + 1];
+  __shared__ float Rs[kSub][D + 1];
+  __shared__ float Ps[kSub][kSub + 1];
+
+  const int tid = threadIdx.x;
+  const int chain = blockIdx.x;
+  const int bi = chain / a.H;
+  const int hi = chain - bi * a.H;
+  const int T = a.T;
+  const float eta = a.eta;
+  const size_t tok0 = static_cast<size_t>(chain) * static_cast<size_t>(T) * D;
+  const IO* q = static_cast<const IO*>(a.q) + tok0;
+  const IO* k = static_cast<const IO*>(a.k) + tok0;
+  const IO* v = static_cast<const IO*>(a.v) + tok0;
+  IO* z = static_cast<IO*>(a.z) + tok0;
+  const float* w0 = a.w0 + bi * a.w0_batch_stride + static_cast<long long>(hi) * D * D;
+
+  for (int e = tid; e < D * D; e += kThreads) {
+    const float w = w0[e];
+    Wc[e / D][e % D] = w;
+    Wn[e / D][e % D] = w;
+  }
+  __syncthreads();
+
+  const int b = T > 0 ? min(a.chunk, T) : 1;
+  for (int c0 = 0; c0 < T; c0 += b) {
+    const int cend = min(c0 + b, T);
+    for (int s0 = c0; s0 < cend; s0 += kSub) {
+      const int n = min(kSub, cend - s0);
+      for (int e = tid; e < kSub * D; e += kThreads) {
+        const int t = e / D, j = e % D;
+        const bool in = t < n;
+        const size_t off = static_cast<size_t>(s0 + t) * D + j;
+        Qs[t][j] = in ? to_f32(q[off]) : 0.0f;
+        Ks[t][j] = in ? to_f32(k[off]) : 0.0f;
+        Vs[t][j] = in ? to_f32(v[off]) : 0.0f;
+      }
+      __syncthreads();
+      // Residuals at the chunk-start weights, and the causal in-block scores.
+      for (int e = tid; e < kSub * D; e += kThreads) {
+        const int t = e / D, i = e % D;
+        float acc = 0.0f;
+#pragma unroll 16
+        for (int j = 0; j < D; ++j) acc += Ks[t][j] * Wc[i][j];
+        Rs[t][i] = t < n ? acc - Vs[t][i] : 0.0f;
+      }
+      if (a.causal) {
+        for (int e = tid; e < kSub * kSub; e += kThreads) {
+          const int t = e / kSub, s = e % kSub;
+          float acc = 0.0f;
+          if (s <= t && t < n) {
+#pragma unroll 16
+            for (int j = 0; j < D; ++j) acc += Qs[t][j] * Ks[s][j];
+          }
+          Ps[t][s] = acc;
+        }
+      }
+      __syncthreads();
+      if (a.causal) {
+        for (int e = tid; e < kSub * D; e += kThreads) {
+          const int t = e / D, i = e % D;
+          if (t >= n) continue;
+          float acc = 0.0f;
+#pragma unroll 16
+          for (int j = 0; j < D; ++j) acc += Qs[t][j] * Wn[i][j];
+          float corr = 0.0f;
+          for (int s = 0; s <= t; ++s) corr += Ps[t][s] * Rs[s][i];
+          z[static_cast<size_t>(s0 + t) * D + i] = from_f32<IO>(acc - eta * corr);
+        }
+        __syncthreads();
+      }
+      for (int e = tid; e < D * D; e += kThreads) {
+        const int i = e / D, j = e % D;
+        float acc = 0.0f;
+        for (int t = 0; t < n; ++t) acc += Rs[t][i] * Ks[t][j];
+        Wn[i][j] -= eta * acc;
+      }
+      __syncthreads();
+    }
+    for (int e = tid; e < D * D; e += kThreads) Wc[e / D][e % D] = Wn[e / D][e % D];
+    __syncthreads();
+  }
+
+  if (!a.causal) {
+    for (int s0 = 0; s0 < T; s0 += kSub) {
+      const int n = min(kSub, T - s0);
+      for (int e = tid; e < kSub * D; e += kThreads) {
+        const int t = e / D, j = e % D;
+        Qs[t][j] = t < n ? to_f32(q[static_cast<size_t>(s0 + t) * D + j]) : 0.0f;
+      }
+      __syncthreads();
+      for (int e = tid; e < kSub * D; e += kThreads) {
+        const int t = e / D, i = e % D;
+        if (t >= n) continue;
+        float acc = 0.0f;
+#pragma unroll 16
+        for (int j = 0; j < D; ++j) acc += Qs[t][j] * Wn[i][j];
+        z[static_cast<size_t>(s0 + t) * D + i] = from_f32<IO>(acc);
+      }
+      __syncthreads();
+    }
+  }
+
+  if (a.w_out) {
+    float* wo = a.w_out + static_cast<size_t>(chain) * D * D;
+    for (int e = tid; e < D * D; e += kThreads) wo[e] = Wn[e / D][e % D];
+  }
+}
+
+template <typename IO>
+hipError_t launch_d(const LinearArgs& a, hipStream_t s) {
+  const dim3 grid(a.B * a.H), block(kThreads);
+  switch (a.d) {
+    case 16: hipLaunchKernelGGL((linear_generic_kernel<IO, 16>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((linear_generic_kernel<IO, 32>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((linear_generic_kernel<IO, 64>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_linear_generic(const LinearArgs& a, bool bf16_io, hipStream_t s) {
+  return bf16_io ? launch_d<bf16>(a, s) : launch_d<float>(a, s);
+}
+
+}  // namespace ttt

@@ -1,0 +1,197 @@
+// C ABI of libttt: argument validation, kernel selection and error reporting.
+// The functions are declared (with their argument conventions) in include/ttt.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+
+#include "../../include/ttt.h"
+#include "common.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(TTT_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool fits_int64(long long a, long long b, long long c, long long d) {
+  const long long lim = (1LL << 62);
+  long long x = a;
+  for (long long m : {b, c, d}) {
+    if (m != 0 && x > lim / m) return false;
+    x *= m;
+  }
+  return true;
+}
+
+int check_common(const char* fn, const void* q, const void* k, const void* v, const void* z,
+                 int B, int H, int T, int d, float eta, int io_dtype) {
+  if (B <= 0 || H <= 0 || d <= 0 || T < 0)
+    return fail(TTT_E_INVALID, "%s: sizes must be positive (B=%d H=%d T=%d d=%d)", fn, B, H, T, d);
+  if (io_dtype != TTT_F32 && io_dtype != TTT_BF16)
+    return fail(TTT_E_INVALID, "%s: unknown io_dtype %d", fn, io_dtype);
+  if (!std::isfinite(eta)) return fail(TTT_E_INVALID, "%s: eta must be finite", fn);
+  if (T > 0 && (!q || !k || !v || !z))
+    return fail(TTT_E_INVALID, "%s: q, k, v and z must be non-null", fn);
+  if (!fits_int64(B, H, T > 0 ? T : 1, d))
+    return fail(TTT_E_INVALID, "%s: B*H*T*d overflows", fn);
+  if (static_cast<long long>(B) * H > 0x7fffffffLL)
+    return fail(TTT_E_INVALID, "%s: B*H exceeds the grid limit", fn);
+  return TTT_OK;
+}
+
+// Device workspace for kernels that keep their state off-chip: one grow-only buffer per
+// device, allocated on first need and kept until the process exits.
+std::mutex g_ws_mutex;
+constexpr int kMaxDevices = 64;
+float* g_ws[kMaxDevices] = {};
+size_t g_ws_floats[kMaxDevices] = {};
+
+int get_workspace(size_t floats, float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(TTT_E_HIP, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  if (g_ws_floats[dev] < floats) {
+    if (g_ws[dev]) {
+      // The old buffer may still be in use by queued work on any stream.
+      e = hipDeviceSynchronize();
+      if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+      e = hipFree(g_ws[dev]);
+      if (e != hipSuccess) return hip_fail(e, "hipFree");
+      g_ws[dev] = nullptr;
+      g_ws_floats[dev] = 0;
+    }
+    void* p = nullptr;
+    e = hipMalloc(&p, floats * sizeof(float));
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
+    g_ws[dev] = static_cast<float*>(p);
+    g_ws_floats[dev] = floats;
+  }
+  *out = g_ws[dev];
+  return TTT_OK;
+}
+
+int copy_state(float* dst, const float* src, long long batch_stride, int B, int H,
+               size_t per_head, hipStream_t s) {
+  if (!dst) return TTT_OK;
+  hipError_t e = ttt::launch_copy_state(dst, src, batch_stride, B, H, per_head, s);
+  if (e != hipSuccess) return hip_fail(e, "state copy launch");
+  return TTT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ttt_abi_version(void) { return 1; }
+
+const char* ttt_last_error(void) { return g_last_error.c_str(); }
+
+int ttt_linear_fwd(const void* q, const void* k, const void* v, const float* w0,
+                   long long w0_batch_stride, void* z, float* w_out, int B, int H, int T,
+                   int d, int chunk, int causal, float eta, int io_dtype,
+                   ttt_stream_t stream) {
+  g_last_error.clear();
+  int rc = check_common("ttt_linear_fwd", q, k, v, z, B, H, T, d, eta, io_dtype);
+  if (rc != TTT_OK) return rc;
+  if (!w0) return fail(TTT_E_INVALID, "ttt_linear_fwd: w0 must be non-null");
+  if (chunk < 1) return fail(TTT_E_INVALID, "ttt_linear_fwd: chunk must be >= 1 (got %d)", chunk);
+  if (causal != 0 && causal != 1)
+    return fail(TTT_E_INVALID, "ttt_linear_fwd: causal must be 0 or 1");
+  if (w0_batch_stride < 0) return fail(TTT_E_INVALID, "ttt_linear_fwd: negative w0_batch_stride");
+  if (d != 16 && d != 32 && d != 64)
+    return fail(TTT_E_UNSUPPORTED, "ttt_linear_fwd: d=%d not supported (16, 32, 64)", d);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (T == 0) return copy_state(w_out, w0, w0_batch_stride, B, H, static_cast<size_t>(d) * d, s);
+
+  ttt::LinearArgs a{q, k, v, w0, w0_batch_stride, z, w_out, B, H, T, d, chunk, causal, eta};
+  const bool bf16 = io_dtype == TTT_BF16;
+  hipError_t e;
+  if (ttt::linear_mfma_supported(a, bf16))
+    e = ttt::launch_linear_mfma(a, s);
+  else
+    e = ttt::launch_linear_generic(a, bf16, s);
+  if (e != hipSuccess) return hip_fail(e, "ttt_linear_fwd launch");
+  return TTT_OK;
+}
+
+int delta_rule_fwd(const void* q, const void* k, const void* v, const float* w0,
+                   long long w0_batch_stride, void* z, float* w_out, int B, int H, int T,
+                   int d, float eta, int io_dtype, ttt_stream_t stream) {
+  g_last_error.clear();
+  int rc = check_common("delta_rule_fwd", q, k, v, z, B, H, T, d, eta, io_dtype);
+  if (rc != TTT_OK) return rc;
+  if (!w0) return fail(TTT_E_INVALID, "delta_rule_fwd: w0 must be non-null");
+  if (w0_batch_stride < 0) return fail(TTT_E_INVALID, "delta_rule_fwd: negative w0_batch_stride");
+  if (d != 16 && d != 32 && d != 64)
+    return fail(TTT_E_UNSUPPORTED, "delta_rule_fwd: d=%d not supported (16, 32, 64)", d);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (T == 0) return copy_state(w_out, w0, w0_batch_stride, B, H, static_cast<size_t>(d) * d, s);
+
+  ttt::LinearArgs a{q, k, v, w0, w0_batch_stride, z, w_out, B, H, T, d, 1, 1, eta};
+  const bool bf16 = io_dtype == TTT_BF16;
+  hipError_t e;
+  if (ttt::delta_fast_supported(a, bf16))
+    e = ttt::launch_delta_fast(a, bf16, s);
+  else
+    e = ttt::launch_linear_generic(a, bf16, s);
+  if (e != hipSuccess) return hip_fail(e, "delta_rule_fwd launch");
+  return TTT_OK;
+}
+
+int ttt_mlp_fwd(const void* q, const void* k, const void* v, const float* w1, const float* w2,
+                long long w_batch_stride, void* z, float* w1_out, float* w2_out, int B, int H,
+                int T, int d, int dh, int chunk, int causal, float eta, int io_dtype,
+                ttt_stream_t stream) {
+  g_last_error.clear();
+  int rc = check_common("ttt_mlp_fwd", q, k, v, z, B, H, T, d, eta, io_dtype);
+  if (rc != TTT_OK) return rc;
+  if (!w1 || !w2) return fail(TTT_E_INVALID, "ttt_mlp_fwd: w1 and w2 must be non-null");
+  if (dh <= 0) return fail(TTT_E_INVALID, "ttt_mlp_fwd: dh must be positive (got %d)", dh);
+  if (chunk < 1) return fail(TTT_E_INVALID, "ttt_mlp_fwd: chunk must be >= 1 (got %d)", chunk);
+  if (causal != 0 && causal != 1) return fail(TTT_E_INVALID, "ttt_mlp_fwd: causal must be 0 or 1");
+  if (w_batch_stride < 0) return fail(TTT_E_INVALID, "ttt_mlp_fwd: negative w_batch_stride");
+  if (d != 16 && d != 32 && d != 64)
+    return fail(TTT_E_UNSUPPORTED, "ttt_mlp_fwd: d=%d not supported (16, 32, 64)", d);
+  if (dh > 512) return fail(TTT_E_UNSUPPORTED, "ttt_mlp_fwd: dh=%d not supported (<= 512)", dh);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t per = static_cast<size_t>(d) * dh;
+  if (T == 0) {
+    rc = copy_state(w1_out, w1, w_batch_stride, B, H, per, s);
+    if (rc != TTT_OK) return rc;
+    return copy_state(w2_out, w2, w_batch_stride, B, H, per, s);
+  }
+  ttt::MlpArgs a{q, k, v, w1, w2, w_batch_stride, z, w1_out, w2_out,
+                 B, H, T, d, dh, chunk, causal, eta};
+  const bool bf16 = io_dtype == TTT_BF16;
+  hipError_t e;
+  if (ttt::mlp_fast_supported(a, bf16)) {
+    e = ttt::launch_mlp_fast(a, s);
+  } else {
+    float* ws = nullptr;
+    rc = get_workspace(ttt::mlp_generic_workspace_floats(a), &ws);
+    if (rc != TTT_OK) return rc;
+    e = ttt::launch_mlp_generic(a, bf16, ws, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "ttt_mlp_fwd launch");
+  return TTT_OK;
+}
+
+}  // extern "C"

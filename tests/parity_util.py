@@ -1,0 +1,72 @@
+"""Shared helpers of the GPU parity tests: run the HIP path and the oracle on the same
+seeded inputs and compare slab by slab (one slab = one (batch, head) sequence)."""
+import numpy as np
+
+from oracle import ttt_oracle as O
+from test_sequence_layers_amd.workloads import make_inputs, workload
+
+FP32_TOL = 1e-4   # relative Frobenius error per slab, float32 I/O
+BF16_TOL = 2e-2   # relative Frobenius error per slab, bfloat16 I/O, float32 state
+
+
+def tol_for(io):
+    return FP32_TOL if io == "f32" else BF16_TOL
+
+
+def slab_rel(z, ref):
+    """max over (b, h) of ||z - ref||_F / ||ref||_F (ref all-zero slabs use the abs error)."""
+    z = np.asarray(z, np.float64)
+    ref = np.asarray(ref, np.float64)
+    lead = ref.shape[:-2]
+    zz = z.reshape((-1,) + ref.shape[-2:])
+    rr = ref.reshape((-1,) + ref.shape[-2:])
+    num = np.sqrt(((zz - rr) ** 2).sum(axis=(-2, -1)))
+    den = np.sqrt((rr ** 2).sum(axis=(-2, -1)))
+    rel = np.where(den > 0, num / np.maximum(den, 1e-300), num)
+    return float(rel.max()) if rel.size else 0.0, rel.reshape(lead)
+
+
+def to_device(inp, io):
+    import torch
+    dt = torch.bfloat16 if io == "bf16" else torch.float32
+    out = {}
+    for key in ("q", "k", "v"):
+        out[key] = torch.from_numpy(np.ascontiguousarray(inp[key])).to("cuda").to(dt).contiguous()
+    for key in ("w0", "w1", "w2"):
+        if key in inp:
+            out[key] = torch.from_numpy(np.ascontiguousarray(inp[key])).to("cuda").contiguous()
+    return out
+
+
+def run_gpu(kind, dev, eta, chunk, causal, return_state=True):
+    import test_sequence_layers_amd as ttt
+    if kind == "linear":
+        return ttt.ttt_linear_fwd(dev["q"], dev["k"], dev["v"], dev["w0"], eta, chunk, causal,
+                                  return_state=return_state)
+    if kind == "delta":
+        return ttt.delta_rule_fwd(dev["q"], dev["k"], dev["v"], dev["w0"], eta,
+                                  return_state=return_state)
+    return ttt.ttt_mlp_fwd(dev["q"], dev["k"], dev["v"], dev["w1"], dev["w2"], eta, chunk,
+                           causal, return_state=return_state)
+
+
+def run_oracle(kind, inp, eta, chunk, causal, sel=None):
+    """Oracle on (optionally) a subset of (b, h) pairs: sel = list of (b, h)."""
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    if sel is not None:
+        bs = [b for b, _ in sel]
+        hs = [h for _, h in sel]
+        q, k, v = q[bs, hs][None], k[bs, hs][None], v[bs, hs][None]
+        pick = lambda w: w[hs][None] if w.ndim == 3 else w[bs, hs][None]
+    else:
+        pick = lambda w: w
+    if kind == "linear":
+        return O.ttt_linear(q, k, v, pick(inp["w0"]), eta, chunk, causal)
+    if kind == "delta":
+        return O.delta_rule(q, k, v, pick(inp["w0"]), eta)
+    return O.ttt_mlp(q, k, v, pick(inp["w1"]), pick(inp["w2"]), eta, chunk, causal)
+
+
+def to_np(t):
+    import torch
+    return t.detach().to(torch.float32).cpu().numpy()

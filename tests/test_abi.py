@@ -1,0 +1,142 @@
+"""Host-side checks of the C ABI (CPU only: no call here reaches a HIP runtime function).
+
+The library must load, export every function include/ttt.h declares, and reject invalid
+arguments with the documented status and message before touching the GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import test_sequence_layers_amd as ttt
+from test_sequence_layers_amd import _binding
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "ttt.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ttt.load_library()
+
+
+def test_header_declares_the_three_entry_points():
+    names = _declared_functions()
+    for n in ("ttt_linear_fwd", "ttt_mlp_fwd", "delta_rule_fwd", "ttt_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert name in _binding.SIGNATURES, f"binding lacks {name}"
+
+
+def test_abi_version(lib):
+    assert lib.ttt_abi_version() == 1
+
+
+FAKE = 0x1000  # never dereferenced: validation fails before any HIP call
+
+
+def _linear(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, w0=FAKE, stride=0, z=FAKE, w_out=None, B=1, H=1, T=16,
+             d=16, chunk=16, causal=1, eta=0.1, io=0)
+    a.update(kw)
+    return lib.ttt_linear_fwd(a["q"], a["k"], a["v"], a["w0"], a["stride"], a["z"], a["w_out"],
+                              a["B"], a["H"], a["T"], a["d"], a["chunk"], a["causal"],
+                              a["eta"], a["io"], None)
+
+
+def _mlp(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, w1=FAKE, w2=FAKE, stride=0, z=FAKE, B=1, H=1, T=16, d=16,
+             dh=32, chunk=16, causal=1, eta=0.1, io=0)
+    a.update(kw)
+    return lib.ttt_mlp_fwd(a["q"], a["k"], a["v"], a["w1"], a["w2"], a["stride"], a["z"], None,
+                           None, a["B"], a["H"], a["T"], a["d"], a["dh"], a["chunk"],
+                           a["causal"], a["eta"], a["io"], None)
+
+
+def _delta(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, w0=FAKE, stride=0, z=FAKE, B=1, H=1, T=16, d=16, eta=0.1,
+             io=0)
+    a.update(kw)
+    return lib.delta_rule_fwd(a["q"], a["k"], a["v"], a["w0"], a["stride"], a["z"], None,
+                              a["B"], a["H"], a["T"], a["d"], a["eta"], a["io"], None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(q=None), ttt.TTT_E_INVALID, "non-null"),
+    (dict(z=None), ttt.TTT_E_INVALID, "non-null"),
+    (dict(w0=None), ttt.TTT_E_INVALID, "w0"),
+    (dict(B=0), ttt.TTT_E_INVALID, "positive"),
+    (dict(H=-1), ttt.TTT_E_INVALID, "positive"),
+    (dict(T=-5), ttt.TTT_E_INVALID, "positive"),
+    (dict(d=0), ttt.TTT_E_INVALID, "positive"),
+    (dict(chunk=0), ttt.TTT_E_INVALID, "chunk"),
+    (dict(causal=2), ttt.TTT_E_INVALID, "causal"),
+    (dict(eta=float("nan")), ttt.TTT_E_INVALID, "finite"),
+    (dict(eta=float("inf")), ttt.TTT_E_INVALID, "finite"),
+    (dict(io=7), ttt.TTT_E_INVALID, "dtype"),
+    (dict(stride=-1), ttt.TTT_E_INVALID, "stride"),
+    (dict(B=1 << 30, H=1 << 30, T=1 << 30, d=64), ttt.TTT_E_INVALID, "overflow"),
+    (dict(d=48), ttt.TTT_E_UNSUPPORTED, "d=48"),
+    (dict(d=128), ttt.TTT_E_UNSUPPORTED, "d=128"),
+])
+def test_linear_rejects(lib, kw, code, msg):
+    assert _linear(lib, **kw) == code
+    assert msg in ttt.last_error()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(w1=None), ttt.TTT_E_INVALID, "w1"),
+    (dict(w2=None), ttt.TTT_E_INVALID, "w2"),
+    (dict(dh=0), ttt.TTT_E_INVALID, "dh"),
+    (dict(dh=1024), ttt.TTT_E_UNSUPPORTED, "dh=1024"),
+    (dict(d=100), ttt.TTT_E_UNSUPPORTED, "d=100"),
+    (dict(chunk=-3), ttt.TTT_E_INVALID, "chunk"),
+    (dict(io=2), ttt.TTT_E_INVALID, "dtype"),
+    (dict(v=None), ttt.TTT_E_INVALID, "non-null"),
+])
+def test_mlp_rejects(lib, kw, code, msg):
+    assert _mlp(lib, **kw) == code
+    assert msg in ttt.last_error()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(k=None), ttt.TTT_E_INVALID, "non-null"),
+    (dict(w0=None), ttt.TTT_E_INVALID, "w0"),
+    (dict(d=8), ttt.TTT_E_UNSUPPORTED, "d=8"),
+    (dict(eta=float("-inf")), ttt.TTT_E_INVALID, "finite"),
+])
+def test_delta_rejects(lib, kw, code, msg):
+    assert _delta(lib, **kw) == code
+    assert msg in ttt.last_error()
+
+
+def test_error_text_is_per_call(lib):
+    assert _linear(lib, chunk=0) == ttt.TTT_E_INVALID
+    assert "chunk" in ttt.last_error()
+    assert _linear(lib, d=48) == ttt.TTT_E_UNSUPPORTED
+    assert "chunk" not in ttt.last_error()
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="missing"):
+        _binding.load_library.__wrapped__(str(tmp_path / "nope.so")) if hasattr(
+            _binding.load_library, "__wrapped__") else _load_missing(tmp_path)
+
+
+def _load_missing(tmp_path):
+    saved = _binding._lib
+    try:
+        _binding._lib = None
+        _binding.load_library(str(tmp_path / "nope.so"))
+    finally:
+        _binding._lib = saved

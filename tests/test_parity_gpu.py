@@ -1,0 +1,164 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on seeded inputs.
+
+Small cases span several chunks/tiles and a ragged tail and are compared in full; the five
+measured workloads run at full size and are compared on sampled (batch, head) sequences,
+which the oracle computes independently of the others.
+"""
+import numpy as np
+import pytest
+import sys
+
+from tests.parity_util import (BF16_TOL, FP32_TOL, make_inputs, run_gpu, run_oracle, slab_rel,
+                               to_device, to_np, tol_for, workload)
+
+pytestmark = pytest.mark.gpu
+
+
+def _note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _check(kind, w, inp, sel=None, state_tol=None):
+    _note(f"[parity] {kind} {w.name} B={w.B} H={w.H} T={w.T} d={w.d} h={w.h} chunk={w.chunk} "
+          f"causal={w.causal} io={w.io} seed={w.seed}")
+    dev = to_device(inp, w.io)
+    out = run_gpu(kind, dev, w.eta, w.chunk, w.causal)
+    import torch
+    torch.cuda.synchronize()
+    z = to_np(out[0])
+    states = [to_np(s) for s in out[1:]]
+    ref = run_oracle(kind, inp, w.eta, w.chunk, w.causal, sel)
+    if sel is not None:
+        bs = [b for b, _ in sel]
+        hs = [h for _, h in sel]
+        z = z[bs, hs][None]
+        states = [s[bs, hs][None] for s in states]
+    assert np.isfinite(z).all()
+    tol = tol_for(w.io)
+    rel, _ = slab_rel(z, ref[0])
+    _note(f"[parity]   z rel {rel:.3e} (tol {tol})")
+    assert rel <= tol, rel
+    for s, r in zip(states, ref[1:]):
+        srel, _ = slab_rel(s, r)
+        _note(f"[parity]   state rel {srel:.3e}")
+        assert srel <= (state_tol or tol), srel
+    return rel
+
+
+# ------------------------------------------------------------------ TTT-Linear
+
+def test_linear_config_tiny_fp32():
+    w = workload(0)
+    _check("linear", w, make_inputs(w))
+
+
+@pytest.mark.parametrize("d", [16, 32, 64])
+@pytest.mark.parametrize("chunk", [1, 5, 16, 77])
+@pytest.mark.parametrize("causal", [True, False])
+def test_linear_fp32_shapes(d, chunk, causal):
+    w = workload(0).replace(B=2, H=3, T=77, d=d, chunk=chunk, causal=causal, init="normal",
+                            eta=0.2, seed=7 + d + chunk)
+    _check("linear", w, make_inputs(w))
+
+
+def test_linear_fp32_per_batch_state():
+    w = workload(0).replace(B=3, H=2, T=40, d=32, chunk=8, init="normal", seed=3)
+    inp = make_inputs(w)
+    rng = np.random.default_rng(0)
+    inp["w0"] = (0.05 * rng.standard_normal((3, 2, 32, 32))).astype(np.float32)
+    _check("linear", w, inp)
+
+
+@pytest.mark.parametrize("T", [16, 200, 333])
+def test_linear_bf16_d64_chunk16(T):
+    w = workload(1).replace(B=2, H=3, T=T, seed=11 + T)
+    _check("linear", w, make_inputs(w))
+
+
+@pytest.mark.parametrize("chunk,causal", [(16, False), (8, True), (32, True), (1, True)])
+def test_linear_bf16_other_modes(chunk, causal):
+    w = workload(1).replace(B=1, H=4, T=130, chunk=chunk, causal=causal, seed=5 + chunk)
+    _check("linear", w, make_inputs(w))
+
+
+def test_linear_config_full_size_sampled():
+    w = workload(1)
+    sel = [(0, 0), (3, 7), (7, 11)]
+    _check("linear", w, make_inputs(w), sel=sel)
+
+
+# ------------------------------------------------------------------ delta rule
+
+@pytest.mark.parametrize("d,io", [(16, "f32"), (64, "f32"), (64, "bf16"), (32, "bf16")])
+def test_delta_small(d, io):
+    w = workload(2).replace(B=2, H=2, T=150, d=d, io=io, init="normal", seed=21 + d)
+    _check("delta", w, make_inputs(w))
+
+
+def test_delta_config_full_size_sampled():
+    w = workload(2)
+    _check("delta", w, make_inputs(w), sel=[(0, 0), (3, 15)])
+
+
+# ------------------------------------------------------------------ TTT-MLP
+
+@pytest.mark.parametrize("chunk,causal", [(1, True), (4, True), (16, True), (37, True),
+                                          (37, False), (10, False)])
+def test_mlp_fp32_shapes(chunk, causal):
+    w = workload(3).replace(B=2, H=2, T=37, d=16, h=32, chunk=chunk, causal=causal, io="f32",
+                            seed=31 + chunk)
+    _check("mlp", w, make_inputs(w))
+
+
+def test_mlp_bf16_h256_small():
+    w = workload(3).replace(B=1, H=3, T=100, seed=41)
+    _check("mlp", w, make_inputs(w))
+
+
+def test_mlp_vision_small():
+    w = workload(4).replace(B=2, H=3, seed=42)
+    _check("mlp", w, make_inputs(w))
+
+
+def test_mlp_config_full_size_sampled():
+    w = workload(3)
+    _check("mlp", w, make_inputs(w), sel=[(0, 0), (5, 9)])
+
+
+def test_mlp_vision_config_full_size():
+    w = workload(4)
+    _check("mlp", w, make_inputs(w))
+
+
+# ------------------------------------------------------------------ edge cases
+
+def test_zero_length_sequence_returns_initial_state():
+    import torch
+    import test_sequence_layers_amd as ttt
+    q = torch.zeros((2, 3, 0, 16), device="cuda")
+    w0 = torch.randn((3, 16, 16), device="cuda")
+    z, w = ttt.ttt_linear_fwd(q, q, q, w0, 0.1, 16, return_state=True)
+    torch.cuda.synchronize()
+    assert z.shape == (2, 3, 0, 16)
+    assert torch.equal(w, w0.expand(2, 3, 16, 16))
+
+
+def test_zero_learning_rate_is_a_fixed_linear_map():
+    import torch
+    import test_sequence_layers_amd as ttt
+    w = workload(1).replace(B=1, H=2, T=48)
+    inp = make_inputs(w)
+    dev = to_device(inp, "f32")
+    z = ttt.ttt_linear_fwd(dev["q"], dev["k"], dev["v"], dev["w0"], 0.0, 16)
+    ref = torch.einsum("hij,bhtj->bhti", dev["w0"], dev["q"])
+    torch.cuda.synchronize()
+    assert torch.allclose(z, ref, atol=1e-5, rtol=1e-5)
+
+
+def test_unsupported_shape_raises():
+    import torch
+    import test_sequence_layers_amd as ttt
+    q = torch.zeros((1, 1, 4, 48), device="cuda")
+    with pytest.raises(ttt.TTTError, match="not supported"):
+        ttt.ttt_linear_fwd(q, q, q, torch.zeros((1, 48, 48), device="cuda"), 0.1, 4)
