@@ -1,0 +1,238 @@
+"""Benchmark of the TTT-layer forward pass on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu] [--no-others]
+
+A step is one forward call over one batch of the workload (default: TTT-Linear,
+B=8 H=12 T=2048 d=64, chunk 16, bf16 Q/K/V, fp32 state).  Inputs are seeded synthetic
+tensors already resident in HBM; R independent input/output sets are rotated so that the
+working set (R x ~100 MB) exceeds the 256 MB Infinity Cache and every step streams from
+HBM.  W warm-up steps, then K timed steps between two synchronisations, timed with HIP
+events recorded on the stream the kernels are launched on.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+FP32_VALU_PEAK_TFLOPS = 157.3
+
+
+def algorithmic_cost(w):
+    """(bytes, flops) of one forward call: Q, K, V read + Z written + initial state read;
+    flops of the method (tril-masked b x b products counted at half)."""
+    esz = 2 if w.io == "bf16" else 4
+    tok = w.B * w.H * w.T * w.d * esz
+    if w.kind in ("linear", "delta"):
+        state = w.H * w.d * w.d * 4
+        b = 1 if w.kind == "delta" else min(w.chunk, w.T)
+        # R = K W^T - V, Q W^T, W update: 3 x 2 d^2 per head-token; tril(QK^T) and P R:
+        # 2 x (b/2) x 2d ... counted as 2 b d per head-token.
+        fl = w.B * w.H * w.T * (6 * w.d * w.d + (2 * b * w.d if b > 1 else 0))
+    else:
+        state = 2 * w.H * w.d * w.h * 4
+        b = min(w.chunk, w.T)
+        per = 14 * w.d * w.h + (2 * b * (w.d + w.h) if w.causal else 0)
+        fl = w.B * w.H * w.T * per
+    return 4 * tok + state, fl
+
+
+def make_device_inputs(w, seed, torch):
+    import numpy as np
+    from test_sequence_layers_amd.workloads import make_inputs
+    inp = make_inputs(w, seed=seed)
+    dt = torch.bfloat16 if w.io == "bf16" else torch.float32
+    dev = {}
+    for key in ("q", "k", "v"):
+        dev[key] = torch.from_numpy(np.ascontiguousarray(inp[key])).to("cuda").to(dt).contiguous()
+    for key in ("w0", "w1", "w2"):
+        if key in inp:
+            dev[key] = torch.from_numpy(inp[key]).to("cuda").contiguous()
+    dev["z"] = torch.empty_like(dev["q"])
+    return dev
+
+
+def launch(w, dev, ttt):
+    if w.kind == "linear":
+        ttt.ttt_linear_fwd(dev["q"], dev["k"], dev["v"], dev["w0"], w.eta, w.chunk, w.causal,
+                           z=dev["z"])
+    elif w.kind == "delta":
+        ttt.delta_rule_fwd(dev["q"], dev["k"], dev["v"], dev["w0"], w.eta, z=dev["z"])
+    else:
+        ttt.ttt_mlp_fwd(dev["q"], dev["k"], dev["v"], dev["w1"], dev["w2"], w.eta, w.chunk,
+                        w.causal, z=dev["z"])
+
+
+def time_workload(w, steps, warmup, torch, ttt, rotate=None):
+    bytes_, flops = algorithmic_cost(w)
+    if rotate is None:
+        rotate = max(2, min(8, int(6 * 256e6 / max(bytes_, 1)) + 1))
+    sets = [make_device_inputs(w, w.seed + i, torch) for i in range(rotate)]
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        launch(w, sets[i % rotate], ttt)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        launch(w, sets[i % rotate], ttt)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    return {
+        "ms_per_step": ms,
+        "tokens_per_s": w.B * w.T / (ms * 1e-3),
+        "head_tokens_per_s": w.B * w.H * w.T / (ms * 1e-3),
+        "hbm_gbs": bytes_ / (ms * 1e-3) / 1e9,
+        "tflops": flops / (ms * 1e-3) / 1e12,
+        "bytes": bytes_,
+        "flops": flops,
+        "rotated_sets": rotate,
+    }
+
+
+def cpu_baseline(w, budget_s=15.0):
+    """Time the CPU oracle (float64, as it stands) on a bounded sample of the workload:
+    full-length sequences of a few (batch, head) chains.  Returns tokens/s scaled to the
+    metric's unit (a token counts once across its H heads)."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    from oracle import ttt_oracle as O
+    from test_sequence_layers_amd.workloads import make_inputs
+
+    def run(n_chains):
+        x = make_inputs(w, B=1, H=n_chains)
+        t0 = time.perf_counter()
+        if w.kind == "linear":
+            O.ttt_linear(x["q"], x["k"], x["v"], x["w0"], w.eta, w.chunk, w.causal)
+        elif w.kind == "delta":
+            O.delta_rule(x["q"], x["k"], x["v"], x["w0"], w.eta)
+        else:
+            O.ttt_mlp(x["q"], x["k"], x["v"], x["w1"], x["w2"], w.eta, w.chunk, w.causal)
+        return time.perf_counter() - t0
+
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        t1 = run(1)
+        n = int(max(1, min(w.B * w.H, budget_s / max(t1, 1e-6))))
+        tn = run(n) if n > 1 else t1
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    head_tokens = n * w.T
+    return {
+        "value": head_tokens / w.H / tn,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{n} of {w.B * w.H} (batch, head) sequences at full length T={w.T}, "
+                  f"float64 NumPy, one thread, {tn:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="linear_d64_T2048")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-others", action="store_true", help="time only the headline workload")
+    ap.add_argument("--rotate", type=int, default=None,
+                    help="input/output sets rotated per step (default: enough to exceed the 256 MB "
+                         "Infinity Cache; 1 = every step re-reads the same cache-warm buffers)")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="before timing, run one plain device copy of this many MB (counter scale)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    for key in ("RANK", "WORLD_SIZE"):
+        if int(os.environ.get(key, "0" if key == "RANK" else "1")) not in (0, 1):
+            print("multi-rank runs are not supported", file=sys.stderr)
+            sys.exit(2)
+
+    import torch
+
+    import test_sequence_layers_amd as ttt
+    from test_sequence_layers_amd.workloads import WORKLOADS, workload
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    ttt.load_library()
+
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb * (1 << 20) // 4
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    w = workload(args.workload)
+    res = time_workload(w, args.steps, args.warmup, torch, ttt, rotate=args.rotate)
+    peak = HBM_PEAK_GBS
+    roofline = {
+        "bound": "hbm",
+        "achieved": round(res["hbm_gbs"], 1),
+        "peak": peak,
+        "unit": "GB/s",
+        "frac": round(res["hbm_gbs"] / peak, 4),
+        "traffic": None,
+        "kernel": "ttt_linear (per launch: Q,K,V read + Z written + W0 read)",
+        "bytes_per_launch": res["bytes"],
+    }
+    line = {
+        "metric": "TTT-layer fwd tokens/sec at d=64,T=2048 + MFMA util % (1 MI355X)",
+        "value": round(res["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.io == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) Q/K/V, unit keys, W0 ~ N(0, 0.02^2))",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d": w.d,
+                   "chunk": w.chunk, "causal": w.causal, "eta": w.eta, "state": "f32",
+                   "rotated_input_sets": res["rotated_sets"]},
+        "mfma_util_pct": round(100 * res["tflops"] / BF16_MFMA_PEAK_TFLOPS, 3),
+        "roofline": roofline,
+    }
+    if not args.no_others:
+        others = {}
+        for o in WORKLOADS:
+            if o.name == w.name:
+                continue
+            r = time_workload(o, max(3, args.steps // 5), 2, torch, ttt)
+            others[o.name] = {
+                "tokens_per_s": round(r["tokens_per_s"], 1),
+                "ms_per_step": round(r["ms_per_step"], 5),
+                "hbm_gbs": round(r["hbm_gbs"], 1),
+                "tflops": round(r["tflops"], 3),
+                "mfma_util_pct": round(100 * r["tflops"] / BF16_MFMA_PEAK_TFLOPS, 3),
+            }
+        line["other_workloads"] = others
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -37,9 +37,17 @@ def _flags():
     ]
 
 
+# Extra flags for individual sources.  The matrix-core kernels keep MFMA results in
+# ordinary VGPRs (their values are read by vector instructions every chunk).
+EXTRA_FLAGS = {
+    "linear_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src):
     obj = os.path.join(OUT_DIR, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *_flags(), "-x", "hip", "-c", src, "-o", obj]
+    extra = EXTRA_FLAGS.get(os.path.basename(src), [])
+    cmd = [_hipcc(), *_flags(), *extra, "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -1,9 +1,8 @@
-// Placeholder predicates: no matrix-core path is registered yet.
+// Predicates of the matrix-core paths that are not written yet: these shapes run on the
+// generic kernels.
 #include "common.hpp"
 
 namespace ttt {
-bool linear_mfma_supported(const LinearArgs&, bool) { return false; }
-hipError_t launch_linear_mfma(const LinearArgs&, hipStream_t) { return hipErrorNotSupported; }
 bool delta_fast_supported(const LinearArgs&, bool) { return false; }
 hipError_t launch_delta_fast(const LinearArgs&, bool, hipStream_t) { return hipErrorNotSupported; }
 bool mlp_fast_supported(const MlpArgs&, bool) { return false; }
