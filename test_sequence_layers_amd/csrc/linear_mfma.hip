@@ -8,24 +8,24 @@
 //     W <- W - eta * R^T K                    update)
 // which equals the per-token recurrence up to floating-point order.
 //
-// Mapping.  The linear model is separable by output row: row i of W only needs v[i].  One
-// wave (one workgroup) owns 16 rows i0..i0+15 of one (batch, head) chain, so a chain is 4
-// independent waves that never communicate; workgroup ids are ordered so that the four
-// waves of a chain land on the same XCD and share its L2 for the Q/K re-reads.
-// Within the wave everything stays in registers, in the layouts the MFMA operands need:
+// Mapping.  One workgroup of 4 waves per (batch, head) chain.  The linear model is
+// separable by output row (row i of W only needs v[i]), so wave w owns rows 16w..16w+15 of
+// W and never exchanges state with the other waves.  A fifth wave streams Q/K/V chunks into
+// an LDS ring kRing chunks deep with direct-to-LDS buffer loads (no registers are spent on
+// data in flight), and wave 3 writes Z back with whole-row stores from an LDS staging
+// buffer.  One barrier per chunk publishes the next chunk and recycles a slot; the compute
+// waves read the next chunk's operands while they compute the current one.
+// Within a wave everything stays in registers, in the layouts the MFMA operands need:
 //   * the fp32 state W^T (64 x 16) is 4 accumulator tiles of v_mfma_f32_16x16x32_bf16;
-//     tile jb, accumulator row m holds input index j = 4 m + jb;
 //   * its bf16 copy is, lane for lane, the B operand of R = K W^T and the A operand of
-//     Z^T = W Q^T (v_mfma_f32_16x16x32_bf16), with K and Q loaded in the matching order;
+//     Z^T = W Q^T, with K and Q read from LDS in the matching order;
 //   * R comes out with tokens as rows, which is the B operand of the rank-16 update
 //     W^T += K^T (-eta R) and the A operand of the in-chunk correction (-eta R^T) P^T;
 //   * P^T = K Q^T comes out as the B operand of that correction;
-//   * -V enters R's accumulator through an MFMA with -I, which turns a row-major load of
-//     V into the accumulator layout;
+//   * -V enters R's accumulator through an MFMA with -I, which turns a row read of V into
+//     the accumulator layout;
 //   * products that contract over the 16 tokens use the same 16x16x32 instruction with the
-//     upper half of every operand zero (see chunk_step);
-//   * Z^T comes out with 4 consecutive output features per lane: one 8-byte store.
-// Q/K/V of the next kPrefetch chunks are in flight in registers while a chunk computes.
+//     upper half of one operand zero.
 #include "common.hpp"
 
 namespace ttt {
@@ -38,8 +38,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 64;
 constexpr int kB = 16;          // tokens per chunk
-constexpr int kSlices = 4;      // waves (16 output rows each) per chain
-constexpr int kPrefetch = 4;    // chunks in flight per wave
 
 struct ChunkRegs {
   u32x4 ka0, ka1;  // K[t = n][16 g + 0..7], K[n][16 g + 8..15]: the two A operands of K W^T
@@ -59,33 +57,50 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
-// Per-lane byte offsets inside a chunk (16 rows of 128 bytes), fixed for the whole kernel.
-struct LaneOffsets {
-  uint32_t row;      // n * 128 + 32 g          (K / Q operand rows)
-  uint32_t kt[4];    // (4 g + e) * 128 + 2 c0
-  uint32_t vz;       // n * 128 + 2 (i0 + 4 g)  (V load and Z store)
-};
+__device__ __forceinline__ bf16x8_t bf(const u32x4& x) { return __builtin_bit_cast(bf16x8_t, x); }
 
-// Buffer resource over one chunk: base at the chunk, range = bytes left in the sequence,
-// so rows past the end of the sequence read as zero and stores to them are dropped.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void* base, int left) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, left > 0 ? left : 0, 0x00020000);
+// LDS tiles.  A tile is one 16 x 64 bf16 chunk of one tensor (16 rows of 128 bytes = 8
+// pieces of 16 bytes).  Piece x of row t is stored at piece index t * 8 + (x ^ (t & 7)), so
+// the row-strided operand reads of a wave spread over the banks.
+constexpr int kTileBytes = kB * kD * 2;
+constexpr int kRing = 11;  // ring slots: chunks in flight ahead of the compute waves
+typedef __attribute__((address_space(3))) char lds_char;
+
+__device__ __forceinline__ int swz(int t, int x) { return t * 8 + (x ^ (t & 7)); }
+
+template <typename T>
+__device__ __forceinline__ T lds_load(const lds_char* base, int byte) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) T*>(base + byte);
+}
+template <typename T>
+__device__ __forceinline__ void lds_store(lds_char* base, int byte, T v) {
+  *reinterpret_cast<__attribute__((address_space(3))) T*>(base + byte) = v;
 }
 
+// Per-lane byte offsets inside a tile, fixed for the whole kernel.
+struct LaneOffsets {
+  int ka0, ka1;    // row n, pieces 2g and 2g+1
+  int kt[4][2];    // row 4g+e, piece 2 (n / 4) + h, dword n % 4
+  int vv;          // row n, piece 2w + g / 2, second half when g is odd
+};
 
-__device__ __forceinline__ void load_chunk(ChunkRegs& r, __amdgpu_buffer_rsrc_t q,
-                                           __amdgpu_buffer_rsrc_t k, __amdgpu_buffer_rsrc_t v,
-                                           const LaneOffsets& o) {
-  r.ka0 = __builtin_amdgcn_raw_buffer_load_b128(k, o.row, 0, 0);
-  r.ka1 = __builtin_amdgcn_raw_buffer_load_b128(k, o.row + 16, 0, 0);
-  r.qb0 = __builtin_amdgcn_raw_buffer_load_b128(q, o.row, 0, 0);
-  r.qb1 = __builtin_amdgcn_raw_buffer_load_b128(q, o.row + 16, 0, 0);
+// Reads a chunk's operands from its ring slot (Q tile at +0, K at +kTileBytes, V at
+// +2 kTileBytes).  Only compute waves run this, and their code path issues no
+// direct-to-LDS loads, so the compiler's own lgkmcnt waits order the reads.
+__device__ __forceinline__ void read_chunk(ChunkRegs& r, const lds_char* slot, const LaneOffsets& o) {
+  const lds_char* q = slot;
+  const lds_char* k = slot + kTileBytes;
+  const lds_char* v = slot + 2 * kTileBytes;
+  r.ka0 = lds_load<u32x4>(k, o.ka0);
+  r.ka1 = lds_load<u32x4>(k, o.ka1);
+  r.qb0 = lds_load<u32x4>(q, o.ka0);
+  r.qb1 = lds_load<u32x4>(q, o.ka1);
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    r.kt[e][0] = __builtin_amdgcn_raw_buffer_load_b32(k, o.kt[e], 0, 0);
-    r.kt[e][1] = __builtin_amdgcn_raw_buffer_load_b32(k, o.kt[e] + 16, 0, 0);
+    r.kt[e][0] = lds_load<uint32_t>(k, o.kt[e][0]);
+    r.kt[e][1] = lds_load<uint32_t>(k, o.kt[e][1]);
   }
-  r.vv = __builtin_amdgcn_raw_buffer_load_b64(v, o.vz, 0, 0);
+  r.vv = lds_load<u32x2>(v, o.vv);
 }
 
 // State: four fp32 accumulator tiles of W^T.  Tile jb = 2 h + p, row m of the tile holds
@@ -95,15 +110,6 @@ struct WState {
   float4_t t0, t1, t2, t3;
 };
 
-// Per-chunk values that do not depend on W, computed one chunk ahead.
-struct Ahead {
-  float4_t vneg;   // -V in the accumulator layout of R (rows t = 4g+e, column i0 + n)
-  u32x4 pb;        // masked P^T = tril(Q K^T)^T as a padded bf16 B operand
-  u32x4 kt0, kt1, kt2, kt3;  // K^T tiles (padded A operands of the update)
-};
-
-__device__ __forceinline__ bf16x8_t bf(const u32x4& x) { return __builtin_bit_cast(bf16x8_t, x); }
-
 // Chunk-independent constants of a lane.
 struct LaneConst {
   bf16x8_t neg_eye;        // -I as a padded B operand: slot s < 4 of lane (g, n) is row 4g+s
@@ -111,101 +117,140 @@ struct LaneConst {
   float neta;
 };
 
-// W-independent work of a chunk: -V via an MFMA with -I, P^T = K Q^T with the causal mask,
-// and the K^T gathers for the update.  Every accumulation chain in this file uses the one
-// opcode v_mfma_f32_16x16x32_bf16 and the K = 16 products are zero-padded (chaining a
-// 16x16x16 result into a 16x16x32 accumulator input was observed to read stale
-// accumulator values on gfx950).
-__device__ __forceinline__ void prepare(Ahead& a, const ChunkRegs& r, const LaneConst& lc) {
+// One chunk.  Every accumulation chain uses the one opcode v_mfma_f32_16x16x32_bf16 and
+// the K = 16 products are zero-padded (chaining a 16x16x16 result into a 16x16x32
+// accumulator input was observed to read stale accumulator values on gfx950).  Returns Z^T
+// for the lane (4 consecutive output features of token n) packed as bf16.
+__device__ __forceinline__ u32x2 chunk_step(WState& w, const ChunkRegs& r, const LaneConst& lc) {
   constexpr uint32_t kLo = 0x05040100u, kHi = 0x07060302u;
   const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-  const bf16x8_t ka0 = __builtin_bit_cast(bf16x8_t, r.ka0);
-  const bf16x8_t ka1 = __builtin_bit_cast(bf16x8_t, r.ka1);
-  const bf16x8_t qb0 = __builtin_bit_cast(bf16x8_t, r.qb0);
-  const bf16x8_t qb1 = __builtin_bit_cast(bf16x8_t, r.qb1);
-  const u32x4 vpad = {r.vv.x, r.vv.y, 0u, 0u};
-  a.vneg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf(vpad), lc.neg_eye, zero, 0, 0, 0);
-  float4_t pacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0, qb0, zero, 0, 0, 0);
-  pacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1, qb1, pacc, 0, 0, 0);
-  a.kt0 = u32x4{__builtin_amdgcn_perm(r.kt[1][0], r.kt[0][0], kLo),
-                __builtin_amdgcn_perm(r.kt[3][0], r.kt[2][0], kLo), 0u, 0u};
-  a.kt1 = u32x4{__builtin_amdgcn_perm(r.kt[1][0], r.kt[0][0], kHi),
-                __builtin_amdgcn_perm(r.kt[3][0], r.kt[2][0], kHi), 0u, 0u};
-  a.kt2 = u32x4{__builtin_amdgcn_perm(r.kt[1][1], r.kt[0][1], kLo),
-                __builtin_amdgcn_perm(r.kt[3][1], r.kt[2][1], kLo), 0u, 0u};
-  a.kt3 = u32x4{__builtin_amdgcn_perm(r.kt[1][1], r.kt[0][1], kHi),
-                __builtin_amdgcn_perm(r.kt[3][1], r.kt[2][1], kHi), 0u, 0u};
-  a.pb = u32x4{pack_bf16(pacc[0], pacc[1]) & lc.pmask0, pack_bf16(pacc[2], pacc[3]) & lc.pmask1,
-               0u, 0u};
-}
-
-// One chunk on the serial chain W -> R -> W, with the current chunk's output and the next
-// chunk's W-independent work placed in the latency gaps.  Returns Z^T for the lane (4
-// consecutive output features of token n) packed as bf16.  Scheduling barriers fix the
-// phase order; inside a phase the compiler may reorder.
-__device__ __forceinline__ u32x2 chunk_step(WState& w, Ahead& cur, Ahead& nxt_out,
-                                            const ChunkRegs& r, const ChunkRegs& rn,
-                                            const LaneConst& lc) {
-  const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  const bf16x8_t ka0 = bf(r.ka0), ka1 = bf(r.ka1), qb0 = bf(r.qb0), qb1 = bf(r.qb1);
   // bf16 copy of the chunk-start W^T in the B layout of K W^T: operand h, dword e holds
-  // j = 16 g + 8 h + 2 e + {0, 1}, matching the contiguous K row loads.
+  // j = 16 g + 8 h + 2 e + {0, 1}, matching the K row reads.
   const bf16x8_t wb0 = as_bf16x8(pack_bf16(w.t0[0], w.t1[0]), pack_bf16(w.t0[1], w.t1[1]),
                                  pack_bf16(w.t0[2], w.t1[2]), pack_bf16(w.t0[3], w.t1[3]));
   const bf16x8_t wb1 = as_bf16x8(pack_bf16(w.t2[0], w.t3[0]), pack_bf16(w.t2[1], w.t3[1]),
                                  pack_bf16(w.t2[2], w.t3[2]), pack_bf16(w.t2[3], w.t3[3]));
-  __builtin_amdgcn_sched_barrier(0);
-  // R = K W^T - V (chain), then Z^T = W Q^T (off chain; fills the matrix pipe)
-  float4_t racc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-      __builtin_bit_cast(bf16x8_t, r.ka0), wb0, cur.vneg, 0, 0, 0);
-  racc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.ka1), wb1, racc,
-                                                 0, 0, 0);
-  float4_t zacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb0, __builtin_bit_cast(bf16x8_t, r.qb0),
-                                                          zero, 0, 0, 0);
-  zacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb1, __builtin_bit_cast(bf16x8_t, r.qb1), zacc,
-                                                 0, 0, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  // -eta R as a padded bf16 operand (chain)
+  // R = K W^T - V (rows: tokens 4g+e, column: output feature i0 + n)
+  const u32x4 vpad = {r.vv.x, r.vv.y, 0u, 0u};
+  float4_t racc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf(vpad), lc.neg_eye, zero, 0, 0, 0);
+  racc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0, wb0, racc, 0, 0, 0);
+  racc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1, wb1, racc, 0, 0, 0);
+  // Z^T = W Q^T (first part) and P^T = K Q^T, independent of R
+  float4_t zacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb0, qb0, zero, 0, 0, 0);
+  zacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb1, qb1, zacc, 0, 0, 0);
+  float4_t pacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0, qb0, zero, 0, 0, 0);
+  pacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1, qb1, pacc, 0, 0, 0);
+  // K^T gathers for the update: tile 2h+p, lane (g, n), slot e = K[4g+e][c0 + 8h + p]
+  const u32x4 kt0 = {__builtin_amdgcn_perm(r.kt[1][0], r.kt[0][0], kLo),
+                     __builtin_amdgcn_perm(r.kt[3][0], r.kt[2][0], kLo), 0u, 0u};
+  const u32x4 kt1 = {__builtin_amdgcn_perm(r.kt[1][0], r.kt[0][0], kHi),
+                     __builtin_amdgcn_perm(r.kt[3][0], r.kt[2][0], kHi), 0u, 0u};
+  const u32x4 kt2 = {__builtin_amdgcn_perm(r.kt[1][1], r.kt[0][1], kLo),
+                     __builtin_amdgcn_perm(r.kt[3][1], r.kt[2][1], kLo), 0u, 0u};
+  const u32x4 kt3 = {__builtin_amdgcn_perm(r.kt[1][1], r.kt[0][1], kHi),
+                     __builtin_amdgcn_perm(r.kt[3][1], r.kt[2][1], kHi), 0u, 0u};
+  // -eta R as a padded bf16 operand
   const u32x4 rbu = {pack_bf16(lc.neta * racc[0], lc.neta * racc[1]),
                      pack_bf16(lc.neta * racc[2], lc.neta * racc[3]), 0u, 0u};
   const bf16x8_t rb = bf(rbu);
-  __builtin_amdgcn_sched_barrier(0);
-  // W^T += K^T (-eta R) (chain), then the in-chunk correction Z^T += (-eta R)^T P^T
-  w.t0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf(cur.kt0), rb, w.t0, 0, 0, 0);
-  w.t1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf(cur.kt1), rb, w.t1, 0, 0, 0);
-  w.t2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf(cur.kt2), rb, w.t2, 0, 0, 0);
-  w.t3 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf(cur.kt3), rb, w.t3, 0, 0, 0);
-  zacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rb, bf(cur.pb), zacc, 0, 0, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  // next chunk's W-independent work (off chain)
-  prepare(nxt_out, rn, lc);
-  __builtin_amdgcn_sched_barrier(0);
+  // W^T += K^T (-eta R)
+  w.t0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf(kt0), rb, w.t0, 0, 0, 0);
+  w.t1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf(kt1), rb, w.t1, 0, 0, 0);
+  w.t2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf(kt2), rb, w.t2, 0, 0, 0);
+  w.t3 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf(kt3), rb, w.t3, 0, 0, 0);
+  // Z^T += (-eta R)^T P^T with the causal mask applied to the packed pairs of P^T
+  const u32x4 pbu = {pack_bf16(pacc[0], pacc[1]) & lc.pmask0,
+                     pack_bf16(pacc[2], pacc[3]) & lc.pmask1, 0u, 0u};
+  zacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rb, bf(pbu), zacc, 0, 0, 0);
   const u32x2 out = {pack_bf16(zacc[0], zacc[1]), pack_bf16(zacc[2], zacc[3])};
   return out;
 }
 
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void linear_mfma_kernel(
-    LinearArgs a, int nchains) {
-  // Workgroup id -> (chain, slice): the 4 slices of a chain share id % 8 (one XCD).
-  const int id = blockIdx.x;
-  const int xcd = id & 7;
-  const int rr = id >> 3;
-  const int chain = (rr >> 2) * 8 + xcd;
-  const int slice = rr & 3;
-  if (chain >= nchains) return;
+// Buffer resource over one chunk of a sequence: base at the chunk, range = bytes left, so
+// rows past the end read as zero and stores to them are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void* base, int left) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, left > 0 ? left : 0,
+                                           0x00020000);
+}
 
-  const int lane = threadIdx.x;
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier for LDS traffic only: this wave's LDS writes are complete, then all
+// waves meet.  (The fence of __syncthreads() would also drain every outstanding global
+// load, i.e. the whole prefetch ring; the loads that the barrier publishes are waited for
+// explicitly with wait_vmcnt.  The compiler does not order LDS reads after direct-to-LDS
+// loads by itself, so that explicit wait is what makes the data visible.)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt/expcnt unconstrained
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ __volatile__("" ::: "memory");
+}
+
+constexpr int kComputeWaves = 4;
+constexpr int kThreads = 64 * (kComputeWaves + 1);
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) void linear_mfma_kernel(
+    LinearArgs a) {
+  __shared__ __attribute__((aligned(16))) char ring_mem[kRing * 3 * kTileBytes];
+  __shared__ __attribute__((aligned(16))) char zbuf_mem[2 * kTileBytes];
+  lds_char* ring = (lds_char*)(ring_mem);
+  lds_char* zbuf = (lds_char*)(zbuf_mem);
+
+  const int chain = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int T = a.T;
+  const int nchunks = (T + kB - 1) / kB;
+  const int seq_bytes = T * kD * 2;  // < 2^31: checked by linear_mfma_supported
+  const size_t tok0 = static_cast<size_t>(chain) * static_cast<size_t>(T) * kD;
+
+  if (wv == kComputeWaves) {
+    // Loader wave: streams Q, K, V of chunk c into ring slot c % kRing with direct-to-LDS
+    // loads, 6 instructions per chunk (2 per tensor, 8 rows each).  Lane l fills piece l
+    // of a half tile: row 8 hh + l / 8 at swizzled position l % 8, which holds global
+    // piece (l % 8) ^ (l / 8) of that row.  Barrier b publishes chunk b (b = 0 before the
+    // loop, then chunk c + 1 at barrier c) and frees the slot of chunk c.
+    const char* src[3] = {reinterpret_cast<const char*>(static_cast<const bf16*>(a.q) + tok0),
+                          reinterpret_cast<const char*>(static_cast<const bf16*>(a.k) + tok0),
+                          reinterpret_cast<const char*>(static_cast<const bf16*>(a.v) + tok0)};
+    const int lrow = lane >> 3;
+    const int lglob = lrow * 128 + (((lane & 7) ^ lrow) * 16);
+    auto issue = [&](int c) {
+      const int off = c * kTileBytes;
+      lds_char* dst = ring + (c % kRing) * 3 * kTileBytes;
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        const __amdgpu_buffer_rsrc_t rs = chunk_rsrc(src[t] + off, seq_bytes - off);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + t * kTileBytes, 16, lglob, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + t * kTileBytes + 1024, 16, lglob + 1024, 0, 0, 0);
+      }
+    };
+    for (int c = 0; c < kRing; ++c) issue(c);
+    wait_vmcnt<6 * (kRing - 1)>();  // chunk 0 landed
+    lds_barrier();
+    for (int c = 0; c < nchunks; ++c) {
+      wait_vmcnt<6 * (kRing - 2)>();  // chunk c + 1 landed
+      lds_barrier();
+      issue(c + kRing);
+    }
+    lds_barrier();
+    return;
+  }
+
+  // Compute waves: wave w owns output rows 16w .. 16w + 15.
   const int g = lane >> 4;
   const int n = lane & 15;
-  const int i0 = 16 * slice;
+  const int i0 = 16 * wv;
   const int bi = chain / a.H;
   const int hi = chain - bi * a.H;
-  const int T = a.T;
-  const float neta = -a.eta;
-
-  const size_t tok0 = static_cast<size_t>(chain) * static_cast<size_t>(T) * kD;
-  const char* q = reinterpret_cast<const char*>(static_cast<const bf16*>(a.q) + tok0);
-  const char* k = reinterpret_cast<const char*>(static_cast<const bf16*>(a.k) + tok0);
-  const char* v = reinterpret_cast<const char*>(static_cast<const bf16*>(a.v) + tok0);
   char* z = reinterpret_cast<char*>(static_cast<bf16*>(a.z) + tok0);
   const float* w0 = a.w0 + bi * a.w0_batch_stride + static_cast<long long>(hi) * kD * kD;
 
@@ -233,62 +278,53 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     lc.pmask1 = (4 * g + 2 <= n ? 0x0000FFFFu : 0u) | (4 * g + 3 <= n ? 0xFFFF0000u : 0u);
     lc.neta = -a.eta;
   }
-
   LaneOffsets o;
-  o.row = n * 128 + 32 * g;
-  const int c0 = 16 * (n >> 2) + 2 * (n & 3);
+  o.ka0 = swz(n, 2 * g) * 16;
+  o.ka1 = swz(n, 2 * g + 1) * 16;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) o.kt[e] = (4 * g + e) * 128 + 2 * c0;
-  o.vz = n * 128 + 2 * (i0 + 4 * g);
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) o.kt[e][h] = swz(4 * g + e, 2 * (n >> 2) + h) * 16 + 4 * (n & 3);
+  o.vv = swz(n, 2 * wv + (g >> 1)) * 16 + 8 * (g & 1);
+  const int zw = o.vv;  // lane (g, n) stages Z[n][i0 + 4g .. +3] where it read V from
 
-  // All chunks go through one loop; chunks past the end of the sequence read zeros (their
-  // residuals and updates are exactly zero) and their stores are dropped, which also
-  // handles a ragged last chunk.  The loop runs whole rounds of kPrefetch chunks over a
-  // ring of named register sets (no array, so nothing is demoted to memory).  Scheduling
-  // barriers between chunks keep the compiler from hoisting work above a chunk's loads'
-  // consumers, which would force a wait for the newest loads.
-  static_assert(kPrefetch == 4, "the ring below is written out for 4 slots");
-  constexpr int kChunkBytes = kB * kD * 2;
-  const int seq_bytes = T * kD * 2;  // < 2^31: checked by linear_mfma_supported
-  const int nchunks = (T + kB - 1) / kB;
-  const int nrounds = (nchunks + kPrefetch - 1) / kPrefetch;
-  ChunkRegs r0, r1, r2, r3;
-  Ahead ah0, ah1;
-#define TTT_LOAD(R, C)                                                              \
-  {                                                                                 \
-    const int off_ = (C) * kChunkBytes;                                             \
-    load_chunk(R, chunk_rsrc(q + off_, seq_bytes - off_), chunk_rsrc(k + off_, seq_bytes - off_), \
-               chunk_rsrc(v + off_, seq_bytes - off_), o);                          \
+  // Storer role (wave 3): writes a staged 16 x 64 Z tile with whole-row stores; lane l
+  // covers row l / 4, pieces 2 (l % 4) and 2 (l % 4) + 1.
+  const int srow = lane >> 2;
+  const int sp0 = 2 * (lane & 3);
+  auto store_z = [&](int c) {
+    const lds_char* zb = zbuf + (c & 1) * kTileBytes;
+    const u32x4 d0 = lds_load<u32x4>(zb, swz(srow, sp0) * 16);
+    const u32x4 d1 = lds_load<u32x4>(zb, swz(srow, sp0 + 1) * 16);
+    const int off = c * kTileBytes;
+    const __amdgpu_buffer_rsrc_t rs = chunk_rsrc(z + off, seq_bytes - off);
+    __builtin_amdgcn_raw_buffer_store_b128(d0, rs, srow * 128 + sp0 * 16, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(d1, rs, srow * 128 + sp0 * 16 + 16, 0, 0);
+  };
+
+  // Step c: after barrier c, read chunk c + 1 (published by that barrier) while computing
+  // chunk c from registers read in step c - 1; stage Z_c; wave 3 stores Z_{c-1}.
+  lds_barrier();  // chunk 0 published
+  ChunkRegs ra, rb;
+  read_chunk(ra, ring, o);
+  auto step = [&](int c, ChunkRegs& cur, ChunkRegs& nxt) {
+    lds_barrier();
+    read_chunk(nxt, ring + ((c + 1) % kRing) * 3 * kTileBytes, o);
+    if (wv == 3 && c > 0) store_z(c - 1);
+    const u32x2 zz = chunk_step(wacc, cur, lc);
+    lds_store<u32x2>(zbuf + (c & 1) * kTileBytes, zw, zz);
+  };
+  int c = 0;
+  for (; c + 2 <= nchunks; c += 2) {
+    step(c, ra, rb);
+    step(c + 1, rb, ra);
   }
-  // chunk C is in ring slot R with its look-ahead values in A; RN holds chunk C+1 and AN
-  // receives its look-ahead values.
-#define TTT_STEP(R, RN, A, AN, C)                                                   \
-  {                                                                                 \
-    __builtin_amdgcn_sched_barrier(0);                                              \
-    const u32x2 zz_ = chunk_step(wacc, A, AN, R, RN, lc);                           \
-    TTT_LOAD(R, (C) + kPrefetch)                                                    \
-    const int zo_ = (C) * kChunkBytes;                                              \
-    __builtin_amdgcn_raw_buffer_store_b64(zz_, chunk_rsrc(z + zo_, seq_bytes - zo_), o.vz, 0, 0); \
+  if (c < nchunks) {
+    step(c, ra, rb);
+    ++c;
   }
-  // Prologue loads in ring order (the loop-head wait must also hold on entry).
-  TTT_LOAD(r0, 0)
-  __builtin_amdgcn_sched_barrier(0);
-  TTT_LOAD(r1, 1)
-  __builtin_amdgcn_sched_barrier(0);
-  TTT_LOAD(r2, 2)
-  __builtin_amdgcn_sched_barrier(0);
-  TTT_LOAD(r3, 3)
-  __builtin_amdgcn_sched_barrier(0);
-  prepare(ah0, r0, lc);
-  for (int round = 0; round < nrounds; ++round) {
-    const int c = round * kPrefetch;
-    TTT_STEP(r0, r1, ah0, ah1, c + 0)
-    TTT_STEP(r1, r2, ah1, ah0, c + 1)
-    TTT_STEP(r2, r3, ah0, ah1, c + 2)
-    TTT_STEP(r3, r0, ah1, ah0, c + 3)
-  }
-#undef TTT_LOAD
-#undef TTT_STEP
+  lds_barrier();
+  if (wv == 3 && nchunks > 0) store_z(nchunks - 1);
 
   if (a.w_out) {
     float* wr = a.w_out + static_cast<size_t>(chain) * kD * kD + (i0 + n) * kD + 16 * g;
@@ -308,17 +344,14 @@ bool linear_mfma_supported(const LinearArgs& a, bool bf16_io) {
                        al(a.w0, 16) && (a.w0_batch_stride % 4) == 0 &&
                        (a.w_out == nullptr || al(a.w_out, 16));
   // byte offsets inside one sequence are 32-bit
-  const bool fits = static_cast<long long>(a.T) * kD * 2 + 2LL * kB * kD * 2 * kPrefetch < 0x7fffffffLL;
+  const bool fits = static_cast<long long>(a.T) * kD * 2 + 2LL * kTileBytes * (kRing + 1) < 0x7fffffffLL;
   return bf16_io && a.d == kD && a.chunk == kB && a.causal == 1 && a.T > 0 && aligned && fits;
 }
 
 hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s) {
-  const int nchains = a.B * a.H;
-  const long long groups8 = (static_cast<long long>(nchains) + 7) / 8;
-  const long long nwg = groups8 * 8 * kSlices;
-  if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(linear_mfma_kernel, dim3(static_cast<unsigned>(nwg)), dim3(64), 0, s, a,
-                     nchains);
+  const long long nchains = static_cast<long long>(a.B) * a.H;
+  if (nchains > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(linear_mfma_kernel, dim3(static_cast<unsigned>(nchains)), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
