@@ -24,7 +24,8 @@
  *   - eta is the scalar inner learning rate; chunk >= 1 (a chunk longer than T is one
  *     chunk of T tokens; when T is not a multiple of chunk the last chunk is shorter).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream).  Calls are
- *     asynchronous, never synchronise, keep no pointer after returning and are thread-safe.
+ *     asynchronous, never synchronise, keep no pointer after returning and are thread-safe;
+ *     any workspace a call needs is allocated and released in stream order on `stream`.
  *   - Arguments are validated on the host before any HIP call.  Return values:
  *       TTT_OK             work enqueued;
  *       TTT_E_INVALID      a null required pointer, a non-positive size, chunk < 1, a
@@ -68,8 +69,8 @@ int ttt_linear_fwd(const void* q, const void* k, const void* v,
  *   w_batch_stride as the distance between batch elements (0 = shared across the batch).
  *   w1_out [B][H][dh][d], w2_out [B][H][d][dh] float32 (out) or NULL.
  * Supported: d in {16, 32, 64}, 1 <= dh <= 512, any chunk, both dtypes, causal 0/1.
- * Some shapes run on a device workspace that the library allocates once per device on
- * first use and keeps until the process exits (TTT_E_HIP if that allocation fails).
+ * Some shapes use a device workspace that the call allocates and frees in stream order on
+ * `stream` (hipMallocAsync / hipFreeAsync; TTT_E_HIP if the allocation fails).
  */
 int ttt_mlp_fwd(const void* q, const void* k, const void* v,
                 const float* w1, const float* w2, long long w_batch_stride,
@@ -80,7 +81,8 @@ int ttt_mlp_fwd(const void* q, const void* k, const void* v,
 /*
  * Delta rule (mini-batch of one token, causal): W_t = W_{t-1} + eta (v_t - W_{t-1} k_t) k_t^T,
  * z_t = W_t q_t ("Fast weights" page, section 1).  Same arguments as ttt_linear_fwd
- * without chunk / causal.  Supported: d in {16, 32, 64}, both dtypes.
+ * without chunk / causal.  Supported: d in {16, 32, 64}, both dtypes.  The d = 64 bf16 path
+ * uses a stream-ordered device workspace of B*H*ceil(T/16)*512 bytes (as ttt_mlp_fwd).
  */
 int delta_rule_fwd(const void* q, const void* k, const void* v,
                    const float* w0, long long w0_batch_stride,

@@ -61,7 +61,8 @@ size_t mlp_generic_workspace_floats(const MlpArgs& a);
 bool linear_mfma_supported(const LinearArgs& a, bool bf16_io);
 hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s);
 bool delta_fast_supported(const LinearArgs& a, bool bf16_io);
-hipError_t launch_delta_fast(const LinearArgs& a, bool bf16_io, hipStream_t s);
+size_t delta_workspace_bytes(const LinearArgs& a);
+hipError_t launch_delta_fast(const LinearArgs& a, void* workspace, hipStream_t s);
 bool mlp_fast_supported(const MlpArgs& a, bool bf16_io);
 hipError_t launch_mlp_fast(const MlpArgs& a, hipStream_t s);
 

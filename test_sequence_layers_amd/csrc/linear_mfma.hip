@@ -1,5 +1,5 @@
 // TTT-Linear forward on the gfx950 matrix cores: d = 64, mini-batch b = 16, causal,
-// bf16 Q/K/V/Z, fp32 state.
+// bf16 Q/K/V/Z, fp32 state; and, on the same machinery, the exact delta rule (b = 1).
 //
 // Method (wmrh.cn summary of Sun et al. 2024, section 1.2.2, mini-batch TTT and its dual
 // form; gradient (W k - v) k^T from the "Fast weights" page, section 1).  For a chunk with
@@ -7,6 +7,15 @@
 //     Z = Q W^T - eta * tril(Q K^T) R        (tril keeps the diagonal: z_t sees its own
 //     W <- W - eta * R^T K                    update)
 // which equals the per-token recurrence up to floating-point order.
+//
+// Delta rule ("Fast weights" page, section 1: W_t = W_{t-1} + eta (v_t - W_{t-1} k_t) k_t^T,
+// z_t = W_t q_t), processed 16 tokens at a time exactly.  Inside a chunk starting from W,
+// the prediction errors u_t = v_t - W_{t-1} k_t satisfy
+//     u_t = (v_t - W k_t) - eta * sum_{s<t} (k_t . k_s) u_s,
+// i.e. (I + eta stril(K K^T)) U = -(K W^T - V).  With Tm = (I + eta stril(K K^T))^-1 and
+// R = Tm (K W^T - V) = -U, the chunk's outputs and update are the mini-batch formulas
+// above with this R (z_t = W q_t + eta sum_{s<=t} (q_t . k_s) u_s; W <- W + eta U^T K).
+// Tm depends only on K; delta_tmat_kernel computes it for every chunk beforehand.
 //
 // Mapping.  One workgroup of 4 waves per (batch, head) chain.  The linear model is
 // separable by output row (row i of W only needs v[i]), so wave w owns rows 16w..16w+15 of
@@ -44,6 +53,7 @@ struct ChunkRegs {
   u32x4 qb0, qb1;  // Q[n][16 g + 0..7], Q[n][16 g + 8..15]
   uint32_t kt[4][2];  // kt[e][h] = K[4 g + e][c0 + 8 h .. + 1],  c0 = 16 (n / 4) + 2 (n % 4)
   u32x2 vv;        // V[n][i0 + 4 g .. 4 g + 3]
+  u32x2 tm;        // delta rule: Tm[n][4 g .. 4 g + 3] (A operand of R = Tm R0)
 };
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
@@ -63,7 +73,15 @@ __device__ __forceinline__ bf16x8_t bf(const u32x4& x) { return __builtin_bit_ca
 // pieces of 16 bytes).  Piece x of row t is stored at piece index t * 8 + (x ^ (t & 7)), so
 // the row-strided operand reads of a wave spread over the banks.
 constexpr int kTileBytes = kB * kD * 2;
-constexpr int kRing = 11;  // ring slots: chunks in flight ahead of the compute waves
+constexpr int kTmBytes = kB * kB * 2;  // one 16 x 16 bf16 Tm matrix of the delta rule
+// Ring slots (chunks in flight ahead of the compute waves) and bytes per slot.  The loader
+// issues 6 loads per chunk (7 with Tm) and waits with a 6-bit vmcnt, which bounds the ring.
+template <bool kDelta> struct Ring {
+  static constexpr int kLoads = kDelta ? 7 : 6;
+  static constexpr int kSlots = kDelta ? 9 : 11;
+  static constexpr int kSlotBytes = 3 * kTileBytes + (kDelta ? 1024 : 0);
+  static_assert(kLoads * (kSlots - 1) < 64, "vmcnt is 6 bits");
+};
 typedef __attribute__((address_space(3))) char lds_char;
 
 __device__ __forceinline__ int swz(int t, int x) { return t * 8 + (x ^ (t & 7)); }
@@ -82,11 +100,13 @@ struct LaneOffsets {
   int ka0, ka1;    // row n, pieces 2g and 2g+1
   int kt[4][2];    // row 4g+e, piece 2 (n / 4) + h, dword n % 4
   int vv;          // row n, piece 2w + g / 2, second half when g is odd
+  int tm;          // Tm tile (row-major, unswizzled): row n, columns 4g .. 4g + 3
 };
 
 // Reads a chunk's operands from its ring slot (Q tile at +0, K at +kTileBytes, V at
 // +2 kTileBytes).  Only compute waves run this, and their code path issues no
 // direct-to-LDS loads, so the compiler's own lgkmcnt waits order the reads.
+template <bool kDelta>
 __device__ __forceinline__ void read_chunk(ChunkRegs& r, const lds_char* slot, const LaneOffsets& o) {
   const lds_char* q = slot;
   const lds_char* k = slot + kTileBytes;
@@ -101,6 +121,7 @@ __device__ __forceinline__ void read_chunk(ChunkRegs& r, const lds_char* slot, c
     r.kt[e][1] = lds_load<uint32_t>(k, o.kt[e][1]);
   }
   r.vv = lds_load<u32x2>(v, o.vv);
+  if (kDelta) r.tm = lds_load<u32x2>(slot + 3 * kTileBytes, o.tm);
 }
 
 // State: four fp32 accumulator tiles of W^T.  Tile jb = 2 h + p, row m of the tile holds
@@ -121,6 +142,7 @@ struct LaneConst {
 // the K = 16 products are zero-padded (chaining a 16x16x16 result into a 16x16x32
 // accumulator input was observed to read stale accumulator values on gfx950).  Returns Z^T
 // for the lane (4 consecutive output features of token n) packed as bf16.
+template <bool kDelta>
 __device__ __forceinline__ u32x2 chunk_step(WState& w, const ChunkRegs& r, const LaneConst& lc) {
   constexpr uint32_t kLo = 0x05040100u, kHi = 0x07060302u;
   const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -136,6 +158,12 @@ __device__ __forceinline__ u32x2 chunk_step(WState& w, const ChunkRegs& r, const
   float4_t racc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf(vpad), lc.neg_eye, zero, 0, 0, 0);
   racc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0, wb0, racc, 0, 0, 0);
   racc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1, wb1, racc, 0, 0, 0);
+  if (kDelta) {
+    // delta rule: R <- Tm R (Tm in the padded A layout, R0 in bf16 as the B operand)
+    const u32x4 r0b = {pack_bf16(racc[0], racc[1]), pack_bf16(racc[2], racc[3]), 0u, 0u};
+    const u32x4 tma = {r.tm.x, r.tm.y, 0u, 0u};
+    racc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf(tma), bf(r0b), zero, 0, 0, 0);
+  }
   // Z^T = W Q^T (first part) and P^T = K Q^T, independent of R
   float4_t zacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb0, qb0, zero, 0, 0, 0);
   zacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb1, qb1, zacc, 0, 0, 0);
@@ -196,9 +224,12 @@ __device__ __forceinline__ void lds_barrier() {
 constexpr int kComputeWaves = 4;
 constexpr int kThreads = 64 * (kComputeWaves + 1);
 
+template <bool kDelta>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) void linear_mfma_kernel(
-    LinearArgs a) {
-  __shared__ __attribute__((aligned(16))) char ring_mem[kRing * 3 * kTileBytes];
+    LinearArgs a, const bf16* tmat) {
+  using RG = Ring<kDelta>;
+  constexpr int kRing = RG::kSlots;
+  __shared__ __attribute__((aligned(16))) char ring_mem[kRing * RG::kSlotBytes];
   __shared__ __attribute__((aligned(16))) char zbuf_mem[2 * kTileBytes];
   lds_char* ring = (lds_char*)(ring_mem);
   lds_char* zbuf = (lds_char*)(zbuf_mem);
@@ -223,21 +254,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
                           reinterpret_cast<const char*>(static_cast<const bf16*>(a.v) + tok0)};
     const int lrow = lane >> 3;
     const int lglob = lrow * 128 + (((lane & 7) ^ lrow) * 16);
+    const char* tsrc = reinterpret_cast<const char*>(tmat) +
+                       (kDelta ? static_cast<size_t>(chain) * nchunks * kTmBytes : 0);
     auto issue = [&](int c) {
       const int off = c * kTileBytes;
-      lds_char* dst = ring + (c % kRing) * 3 * kTileBytes;
+      lds_char* dst = ring + (c % kRing) * RG::kSlotBytes;
 #pragma unroll
       for (int t = 0; t < 3; ++t) {
         const __amdgpu_buffer_rsrc_t rs = chunk_rsrc(src[t] + off, seq_bytes - off);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + t * kTileBytes, 16, lglob, 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + t * kTileBytes + 1024, 16, lglob + 1024, 0, 0, 0);
       }
+      if (kDelta) {
+        // Tm of chunk c: 512 bytes read by lanes 0..31; lanes 32..63 are out of range and
+        // fill the unused second half of the 1 KB area with zeros.
+        const __amdgpu_buffer_rsrc_t rs =
+            chunk_rsrc(tsrc + static_cast<size_t>(c) * kTmBytes, c < nchunks ? kTmBytes : 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + 3 * kTileBytes, 16, lane * 16, 0, 0, 0);
+      }
     };
     for (int c = 0; c < kRing; ++c) issue(c);
-    wait_vmcnt<6 * (kRing - 1)>();  // chunk 0 landed
+    wait_vmcnt<RG::kLoads * (kRing - 1)>();  // chunk 0 landed
     lds_barrier();
     for (int c = 0; c < nchunks; ++c) {
-      wait_vmcnt<6 * (kRing - 2)>();  // chunk c + 1 landed
+      wait_vmcnt<RG::kLoads * (kRing - 2)>();  // chunk c + 1 landed
       lds_barrier();
       issue(c + kRing);
     }
@@ -286,6 +326,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
 #pragma unroll
     for (int h = 0; h < 2; ++h) o.kt[e][h] = swz(4 * g + e, 2 * (n >> 2) + h) * 16 + 4 * (n & 3);
   o.vv = swz(n, 2 * wv + (g >> 1)) * 16 + 8 * (g & 1);
+  o.tm = n * 32 + 8 * g;
   const int zw = o.vv;  // lane (g, n) stages Z[n][i0 + 4g .. +3] where it read V from
 
   // Storer role (wave 3): writes a staged 16 x 64 Z tile with whole-row stores; lane l
@@ -306,12 +347,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   // chunk c from registers read in step c - 1; stage Z_c; wave 3 stores Z_{c-1}.
   lds_barrier();  // chunk 0 published
   ChunkRegs ra, rb;
-  read_chunk(ra, ring, o);
+  read_chunk<kDelta>(ra, ring, o);
   auto step = [&](int c, ChunkRegs& cur, ChunkRegs& nxt) {
     lds_barrier();
-    read_chunk(nxt, ring + ((c + 1) % kRing) * 3 * kTileBytes, o);
+    read_chunk<kDelta>(nxt, ring + ((c + 1) % kRing) * RG::kSlotBytes, o);
     if (wv == 3 && c > 0) store_z(c - 1);
-    const u32x2 zz = chunk_step(wacc, cur, lc);
+    const u32x2 zz = chunk_step<kDelta>(wacc, cur, lc);
     lds_store<u32x2>(zbuf + (c & 1) * kTileBytes, zw, zz);
   };
   int c = 0;
@@ -337,21 +378,95 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
 
 }  // namespace
 
-bool linear_mfma_supported(const LinearArgs& a, bool bf16_io) {
+static bool mfma_shape_ok(const LinearArgs& a) {
   auto al = [](const void* p, uintptr_t m) { return (reinterpret_cast<uintptr_t>(p) & (m - 1)) == 0; };
   // 16-byte vector loads of tokens and of the fp32 state rows
   const bool aligned = al(a.q, 16) && al(a.k, 16) && al(a.v, 16) && al(a.z, 16) &&
                        al(a.w0, 16) && (a.w0_batch_stride % 4) == 0 &&
                        (a.w_out == nullptr || al(a.w_out, 16));
   // byte offsets inside one sequence are 32-bit
-  const bool fits = static_cast<long long>(a.T) * kD * 2 + 2LL * kTileBytes * (kRing + 1) < 0x7fffffffLL;
-  return bf16_io && a.d == kD && a.chunk == kB && a.causal == 1 && a.T > 0 && aligned && fits;
+  const bool fits = static_cast<long long>(a.T) * kD * 2 + 2LL * kTileBytes * 16 < 0x7fffffffLL;
+  return a.d == kD && a.T > 0 && aligned && fits;
+}
+
+bool linear_mfma_supported(const LinearArgs& a, bool bf16_io) {
+  return bf16_io && a.chunk == kB && a.causal == 1 && mfma_shape_ok(a);
 }
 
 hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s) {
   const long long nchains = static_cast<long long>(a.B) * a.H;
   if (nchains > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(linear_mfma_kernel, dim3(static_cast<unsigned>(nchains)), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(linear_mfma_kernel<false>, dim3(static_cast<unsigned>(nchains)), dim3(kThreads),
+                     0, s, a, static_cast<const bf16*>(nullptr));
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------ delta rule
+
+// Tm = (I + eta stril(K K^T))^-1 for every chunk of every chain, in bf16, row-major
+// [chain][chunk][16][16].  One group of 16 lanes per chunk (16 chunks per workgroup):
+// lane j first computes column j of the strictly lower Gram matrix, then column j of Tm by
+// forward substitution, Tm[t][j] = [t == j] - eta sum_{s<t} (k_t . k_s) Tm[s][j].  Rows past
+// the end of the sequence have zero keys, so their rows of Tm are unit rows.
+__global__ __launch_bounds__(256) void delta_tmat_kernel(const bf16* __restrict__ k, bf16* __restrict__ tm,
+                                                         int T, int nchunks, long long total, float eta) {
+  __shared__ float ks[16][kB][kD + 1];
+  __shared__ float gram[16][kB][kB + 1];
+  const int grp = threadIdx.x >> 4;   // chunk within the workgroup
+  const int j = threadIdx.x & 15;
+  const long long id = static_cast<long long>(blockIdx.x) * 16 + grp;
+  const bool valid = id < total;
+  const long long chain = valid ? id / nchunks : 0;
+  const int c = valid ? static_cast<int>(id - chain * nchunks) : 0;
+  const bf16* kc = k + (static_cast<size_t>(chain) * T + static_cast<size_t>(c) * kB) * kD;
+  // lane j loads row j of the chunk (zero past the end of the sequence)
+  const bool row_in = valid && c * kB + j < T;
+  for (int x = 0; x < kD; ++x) ks[grp][j][x] = row_in ? static_cast<float>(kc[j * kD + x]) : 0.0f;
+  __syncthreads();
+  for (int t = 0; t < kB; ++t) {
+    float acc = 0.0f;
+    if (t > j)
+      for (int x = 0; x < kD; ++x) acc += ks[grp][t][x] * ks[grp][j][x];
+    gram[grp][t][j] = acc;
+  }
+  __syncthreads();
+  float col[kB];
+#pragma unroll
+  for (int t = 0; t < kB; ++t) {
+    float acc = (t == j) ? 1.0f : 0.0f;
+#pragma unroll
+    for (int s2 = 0; s2 < t; ++s2) acc -= eta * gram[grp][t][s2] * col[s2];
+    col[t] = acc;
+  }
+  if (valid) {
+    bf16* out = tm + static_cast<size_t>(id) * kB * kB;
+#pragma unroll
+    for (int t = 0; t < kB; ++t) out[t * kB + j] = static_cast<bf16>(col[t]);
+  }
+}
+
+bool delta_fast_supported(const LinearArgs& a, bool bf16_io) {
+  return bf16_io && mfma_shape_ok(a);
+}
+
+size_t delta_workspace_bytes(const LinearArgs& a) {
+  const long long nchunks = (a.T + kB - 1) / kB;
+  return static_cast<size_t>(a.B) * a.H * nchunks * kTmBytes;
+}
+
+hipError_t launch_delta_fast(const LinearArgs& a, void* workspace, hipStream_t s) {
+  const long long nchains = static_cast<long long>(a.B) * a.H;
+  const int nchunks = (a.T + kB - 1) / kB;
+  const long long total = nchains * nchunks;
+  const long long nblocks = (total + 15) / 16;
+  if (nchains > 0x7fffffffLL || nblocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  bf16* tm = static_cast<bf16*>(workspace);
+  hipLaunchKernelGGL(delta_tmat_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(256), 0, s,
+                     static_cast<const bf16*>(a.k), tm, a.T, nchunks, total, a.eta);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(linear_mfma_kernel<true>, dim3(static_cast<unsigned>(nchains)), dim3(kThreads),
+                     0, s, a, static_cast<const bf16*>(tm));
   return hipGetLastError();
 }
 

@@ -5,7 +5,6 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
-#include <mutex>
 #include <string>
 
 #include "../../include/ttt.h"
@@ -55,36 +54,25 @@ int check_common(const char* fn, const void* q, const void* k, const void* v, co
   return TTT_OK;
 }
 
-// Device workspace for kernels that keep their state off-chip: one grow-only buffer per
-// device, allocated on first need and kept until the process exits.
-std::mutex g_ws_mutex;
-constexpr int kMaxDevices = 64;
-float* g_ws[kMaxDevices] = {};
-size_t g_ws_floats[kMaxDevices] = {};
-
-int get_workspace(size_t floats, float** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  if (dev < 0 || dev >= kMaxDevices) return fail(TTT_E_HIP, "device index %d out of range", dev);
-  std::lock_guard<std::mutex> lock(g_ws_mutex);
-  if (g_ws_floats[dev] < floats) {
-    if (g_ws[dev]) {
-      // The old buffer may still be in use by queued work on any stream.
-      e = hipDeviceSynchronize();
-      if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-      e = hipFree(g_ws[dev]);
-      if (e != hipSuccess) return hip_fail(e, "hipFree");
-      g_ws[dev] = nullptr;
-      g_ws_floats[dev] = 0;
-    }
-    void* p = nullptr;
-    e = hipMalloc(&p, floats * sizeof(float));
-    if (e != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
-    g_ws[dev] = static_cast<float*>(p);
-    g_ws_floats[dev] = floats;
+// Per-call device workspace, allocated and released in stream order (hipMallocAsync /
+// hipFreeAsync on the caller's stream): the release is queued behind the kernels that use
+// it, so concurrent calls on different streams never share a workspace and the host never
+// waits.
+struct StreamBuffer {
+  void* ptr = nullptr;
+  hipStream_t stream = nullptr;
+  ~StreamBuffer() {
+    if (ptr) (void)hipFreeAsync(ptr, stream);
   }
-  *out = g_ws[dev];
+};
+
+int get_workspace(size_t bytes, hipStream_t s, StreamBuffer* out) {
+  out->stream = s;
+  hipError_t e = hipMallocAsync(&out->ptr, bytes > 0 ? bytes : 1, s);
+  if (e != hipSuccess) {
+    out->ptr = nullptr;
+    return hip_fail(e, "hipMallocAsync(workspace)");
+  }
   return TTT_OK;
 }
 
@@ -148,10 +136,14 @@ int delta_rule_fwd(const void* q, const void* k, const void* v, const float* w0,
   ttt::LinearArgs a{q, k, v, w0, w0_batch_stride, z, w_out, B, H, T, d, 1, 1, eta};
   const bool bf16 = io_dtype == TTT_BF16;
   hipError_t e;
-  if (ttt::delta_fast_supported(a, bf16))
-    e = ttt::launch_delta_fast(a, bf16, s);
-  else
+  StreamBuffer ws;
+  if (ttt::delta_fast_supported(a, bf16)) {
+    rc = get_workspace(ttt::delta_workspace_bytes(a), s, &ws);
+    if (rc != TTT_OK) return rc;
+    e = ttt::launch_delta_fast(a, ws.ptr, s);
+  } else {
     e = ttt::launch_linear_generic(a, bf16, s);
+  }
   if (e != hipSuccess) return hip_fail(e, "delta_rule_fwd launch");
   return TTT_OK;
 }
@@ -182,13 +174,13 @@ int ttt_mlp_fwd(const void* q, const void* k, const void* v, const float* w1, co
                  B, H, T, d, dh, chunk, causal, eta};
   const bool bf16 = io_dtype == TTT_BF16;
   hipError_t e;
+  StreamBuffer ws;
   if (ttt::mlp_fast_supported(a, bf16)) {
     e = ttt::launch_mlp_fast(a, s);
   } else {
-    float* ws = nullptr;
-    rc = get_workspace(ttt::mlp_generic_workspace_floats(a), &ws);
+    rc = get_workspace(ttt::mlp_generic_workspace_floats(a) * sizeof(float), s, &ws);
     if (rc != TTT_OK) return rc;
-    e = ttt::launch_mlp_generic(a, bf16, ws, s);
+    e = ttt::launch_mlp_generic(a, bf16, static_cast<float*>(ws.ptr), s);
   }
   if (e != hipSuccess) return hip_fail(e, "ttt_mlp_fwd launch");
   return TTT_OK;
