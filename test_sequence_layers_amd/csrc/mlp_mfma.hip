@@ -1,0 +1,416 @@
+// TTT-MLP forward on the gfx950 matrix cores: f(k) = W2 SiLU(W1 k), d = 64, hidden 256,
+// mini-batch b = 16, causal, bf16 Q/K/V/Z, fp32 state.
+//
+// Method: inner 2-layer SiLU MLP (ViT3 news page, section 2) trained by mini-batch GD on
+// 1/2 ||f(k) - v||^2 (wmrh.cn summary of Sun et al. 2024, section 1.2.2), z_t = f(q_t; W_t).
+// For a chunk with rows K, Q, V (16 x 64), chunk-start weights W1 [256 x 64], W2 [64 x 256]:
+//   U = K W1^T, A = SiLU(U), S = SiLU'(U), R = A W2^T - V,
+//   dU = (R W2) * S                                   (gradient of the hidden layer)
+//   W1 <- W1 - eta dU^T K,  W2 <- W2 - eta R^T A        (sum of the chunk's gradients)
+// and, because every hidden pre-activation of a query is linear in W1 and the output is
+// linear in W2, the causal outputs with the in-chunk updates are
+//   U_q = Q W1^T - eta tril(Q K^T) dU,  A_q = SiLU(U_q),
+//   Z   = A_q W2^T - eta tril(A_q A^T) R.
+// This equals the per-token recurrence up to floating-point order.
+//
+// Mapping.  One workgroup of 4 waves per (batch, head) chain.  Wave w owns hidden units
+// 64w .. 64w+63: its rows of W1 and columns of W2 live in its registers as fp32 MFMA
+// accumulator tiles (W1^T tiles with input rows, W2^T tiles with hidden rows, and a second
+// copy of W2 with output rows, because the forward pass contracts W2 over hidden units and
+// the backward pass over outputs; both copies receive the same rank-16 update).  The only
+// cross-wave sums, O = A W2^T and Z, go through LDS.  Every product is one
+// v_mfma_f32_16x16x32_bf16 per 16 x 16 x 32 block; products over the 16 tokens of a chunk
+// use the same instruction with the upper half of one operand zero.
+//
+// Layout conventions (C layout of a 16 x 16 tile: lane (g, n) = (lane / 16, lane % 16)
+// holds rows 4g + e, e = 0..3, of column n):
+//   * input index j of W1^T tiles: tile jb = 2h + p, row m <-> j = 16 (m/4) + 2 (m%4) + 8h + p,
+//     so that an operand over j matches the contiguous 16-byte row loads of K and Q;
+//   * hidden (hh) and output (i) indices are natural: tile a, row m <-> 16 a + m, and a
+//     64-wide contraction pairs tiles (2h, 2h+1), dword e = (row 4g+e of both).
+#include "common.hpp"
+
+namespace ttt {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr int kD = 64;        // model dim d
+constexpr int kH = 256;       // hidden width
+constexpr int kB = 16;        // chunk
+constexpr int kWaves = 4;     // hidden slices of 64
+constexpr int kTileBytes = kB * kD * 2;
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ bf16x8_t bf(const u32x4& x) { return __builtin_bit_cast(bf16x8_t, x); }
+__device__ __forceinline__ bf16x8_t op4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const u32x4 u = {a, b, c, d};
+  return bf(u);
+}
+// operand over a tile pair: dword e = (x[e], y[e])
+__device__ __forceinline__ bf16x8_t pair_op(const float4_t& x, const float4_t& y, float s = 1.0f) {
+  return op4(pack_bf16(s * x[0], s * y[0]), pack_bf16(s * x[1], s * y[1]),
+             pack_bf16(s * x[2], s * y[2]), pack_bf16(s * x[3], s * y[3]));
+}
+// K = 16 operand (4 values, contraction index 4 g + s) padded to the K = 32 layout
+__device__ __forceinline__ bf16x8_t pad_op(const float4_t& x, float s = 1.0f) {
+  return op4(pack_bf16(s * x[0], s * x[1]), pack_bf16(s * x[2], s * x[3]), 0u, 0u);
+}
+__device__ __forceinline__ float4_t mfma(const bf16x8_t& a, const bf16x8_t& b, const float4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float sigmoid_f(float u) { return 1.0f / (1.0f + __expf(-u)); }
+
+template <typename T>
+__device__ __forceinline__ T lds_load(const lds_char* base, int byte) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) T*>(base + byte);
+}
+template <typename T>
+__device__ __forceinline__ void lds_store(lds_char* base, int byte, T v) {
+  *reinterpret_cast<__attribute__((address_space(3))) T*>(base + byte) = v;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void* base, int left) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, left > 0 ? left : 0,
+                                           0x00020000);
+}
+
+// One chunk's token operands of a lane.
+struct ChunkIn {
+  u32x4 ka0, ka1;     // K[t = n][16 g + 0..7], K[n][16 g + 8..15]  (A operands over j)
+  u32x4 qb0, qb1;     // Q[n][16 g + 0..15]                          (B operands over j)
+  uint32_t kt[4][2];  // kt[e][h] = K[4 g + e][c0 + 8 h .. + 1], c0 = 16 (n / 4) + 2 (n % 4)
+  u32x2 vv;           // V[t = tid / 16][4 (tid % 16) .. + 3]         (for R = O - V)
+};
+
+struct Offsets {
+  int row;         // n * 128 + 32 g
+  int kt[4];       // (4 g + e) * 128 + 2 c0
+  int vv;          // (tid / 16) * 128 + 8 (tid % 16)
+};
+
+__device__ __forceinline__ void load_chunk(ChunkIn& r, const char* q, const char* k, const char* v,
+                                           int c, int seq_bytes, const Offsets& o) {
+  const int off = c * kTileBytes;
+  const __amdgpu_buffer_rsrc_t rq = chunk_rsrc(q + off, seq_bytes - off);
+  const __amdgpu_buffer_rsrc_t rk = chunk_rsrc(k + off, seq_bytes - off);
+  const __amdgpu_buffer_rsrc_t rv = chunk_rsrc(v + off, seq_bytes - off);
+  r.ka0 = __builtin_amdgcn_raw_buffer_load_b128(rk, o.row, 0, 0);
+  r.ka1 = __builtin_amdgcn_raw_buffer_load_b128(rk, o.row + 16, 0, 0);
+  r.qb0 = __builtin_amdgcn_raw_buffer_load_b128(rq, o.row, 0, 0);
+  r.qb1 = __builtin_amdgcn_raw_buffer_load_b128(rq, o.row + 16, 0, 0);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r.kt[e][0] = __builtin_amdgcn_raw_buffer_load_b32(rk, o.kt[e], 0, 0);
+    r.kt[e][1] = __builtin_amdgcn_raw_buffer_load_b32(rk, o.kt[e] + 16, 0, 0);
+  }
+  r.vv = __builtin_amdgcn_raw_buffer_load_b64(rv, o.vv, 0, 0);
+}
+
+struct State {
+  float4_t w1t[4][4];  // [jb][a]: W1^T tile, rows j (permuted, tile jb), cols hidden 16a + n
+  float4_t w2t[4][4];  // [a][it]: W2^T tile, rows hidden 16a + m, cols output 16it + n
+  float4_t w2[4][4];   // [it][a]: W2 tile, rows output 16it + m, cols hidden 16a + n
+};
+
+// LDS: per-wave partial sums of O^T and Z^T as [wave][t][i] fp32, and R = O - V as [t][i].
+struct Lds {
+  float opart[kWaves][kB][kD];
+  float zpart[kWaves][kB][kD];
+  float r[kB][kD];
+};
+
+__device__ __forceinline__ void barrier() { __syncthreads(); }
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void mlp_mfma_kernel(
+    MlpArgs a) {
+  __shared__ __attribute__((aligned(16))) Lds sh;
+  lds_char* opart = (lds_char*)(&sh.opart[0][0][0]);
+  lds_char* zpart = (lds_char*)(&sh.zpart[0][0][0]);
+  lds_char* rbuf = (lds_char*)(&sh.r[0][0]);
+
+  const int chain = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 4;
+  const int n = lane & 15;
+  const int bi = chain / a.H;
+  const int hi = chain - bi * a.H;
+  const int T = a.T;
+  const int nchunks = (T + kB - 1) / kB;
+  const int seq_bytes = T * kD * 2;
+  const float eta = a.eta;
+
+  const size_t tok0 = static_cast<size_t>(chain) * static_cast<size_t>(T) * kD;
+  const char* q = reinterpret_cast<const char*>(static_cast<const bf16*>(a.q) + tok0);
+  const char* k = reinterpret_cast<const char*>(static_cast<const bf16*>(a.k) + tok0);
+  const char* v = reinterpret_cast<const char*>(static_cast<const bf16*>(a.v) + tok0);
+  char* z = reinterpret_cast<char*>(static_cast<bf16*>(a.z) + tok0);
+  const size_t hd = static_cast<size_t>(kH) * kD;
+  const float* w1g = a.w1 + bi * a.w_batch_stride + static_cast<long long>(hi) * hd;
+  const float* w2g = a.w2 + bi * a.w_batch_stride + static_cast<long long>(hi) * hd;
+  const int h0 = 64 * wv;  // first hidden unit of this wave
+
+  // ---- initial state ----
+  State st;
+#pragma unroll
+  for (int aa = 0; aa < 4; ++aa) {
+    // W1^T tile (jb, aa): element e = W1[h0 + 16 aa + n][j], j = 16 g + 8 h + 2 e + p
+    const float* wr = w1g + static_cast<size_t>(h0 + 16 * aa + n) * kD + 16 * g;
+    const float4_t f0 = *reinterpret_cast<const float4_t*>(wr);
+    const float4_t f1 = *reinterpret_cast<const float4_t*>(wr + 4);
+    const float4_t f2 = *reinterpret_cast<const float4_t*>(wr + 8);
+    const float4_t f3 = *reinterpret_cast<const float4_t*>(wr + 12);
+    st.w1t[0][aa] = float4_t{f0[0], f0[2], f1[0], f1[2]};
+    st.w1t[1][aa] = float4_t{f0[1], f0[3], f1[1], f1[3]};
+    st.w1t[2][aa] = float4_t{f2[0], f2[2], f3[0], f3[2]};
+    st.w1t[3][aa] = float4_t{f2[1], f2[3], f3[1], f3[3]};
+  }
+#pragma unroll
+  for (int aa = 0; aa < 4; ++aa)
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      // W2^T tile (aa, it): element e = W2[16 it + n][h0 + 16 aa + 4 g + e]
+      st.w2t[aa][it] = *reinterpret_cast<const float4_t*>(
+          w2g + static_cast<size_t>(16 * it + n) * kH + h0 + 16 * aa + 4 * g);
+      // W2 tile (it, aa): element e = W2[16 it + 4 g + e][h0 + 16 aa + n]
+      float4_t x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = w2g[static_cast<size_t>(16 * it + 4 * g + e) * kH + h0 + 16 * aa + n];
+      st.w2[it][aa] = x;
+    }
+
+  // ---- constants ----
+  const uint32_t one = 0x3F80u;  // bf16 1.0
+  const bf16x8_t eye = op4((4 * g + 0 == n ? one : 0u) | (4 * g + 1 == n ? one << 16 : 0u),
+                           (4 * g + 2 == n ? one : 0u) | (4 * g + 3 == n ? one << 16 : 0u), 0u, 0u);
+  const bool keep[4] = {4 * g + 0 <= n, 4 * g + 1 <= n, 4 * g + 2 <= n, 4 * g + 3 <= n};
+  Offsets o;
+  o.row = n * 128 + 32 * g;
+  const int c0 = 16 * (n >> 2) + 2 * (n & 3);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o.kt[e] = (4 * g + e) * 128 + 2 * c0;
+  const int rt = tid >> 4;          // reduction role: row t and 4 outputs
+  const int ri = 4 * (tid & 15);
+  o.vv = rt * 128 + 2 * ri;
+  const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  constexpr uint32_t kLo = 0x05040100u, kHi = 0x07060302u;
+
+  // Z of the previous chunk: reduce the 4 partial sums and store (thread: row rt, 4 outputs)
+  auto reduce_store_z = [&](int c) {
+    float4_t s4 = zero;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) s4 += lds_load<float4_t>(zpart, ((w * kB + rt) * kD + ri) * 4);
+    const int off = c * kTileBytes;
+    const u32x2 out = {pack_bf16(s4[0], s4[1]), pack_bf16(s4[2], s4[3])};
+    __builtin_amdgcn_raw_buffer_store_b64(out, chunk_rsrc(z + off, seq_bytes - off), o.vv, 0, 0);
+  };
+
+  ChunkIn cur, nxt;
+  load_chunk(cur, q, k, v, 0, seq_bytes, o);
+  for (int c = 0; c < nchunks; ++c) {
+    load_chunk(nxt, q, k, v, c + 1, seq_bytes, o);  // prefetch (zeros past the end)
+    const bf16x8_t ka0 = bf(cur.ka0), ka1 = bf(cur.ka1), qb0 = bf(cur.qb0), qb1 = bf(cur.qb1);
+
+    // bf16 copies of this wave's chunk-start state
+    bf16x8_t w1b[2][4];  // [h][a]: operand over j (pairs of W1^T tiles 2h, 2h+1)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int aa = 0; aa < 4; ++aa) w1b[h][aa] = pair_op(st.w1t[2 * h][aa], st.w1t[2 * h + 1][aa]);
+
+    // U = K W1^T (rows t, hidden tile aa);  A = SiLU(U), S = SiLU'(U)
+    float4_t act[4], sd[4];
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa) {
+      float4_t u = mfma(ka0, w1b[0][aa], zero);
+      u = mfma(ka1, w1b[1][aa], u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float sg = sigmoid_f(u[e]);
+        act[aa][e] = u[e] * sg;
+        sd[aa][e] = sg * (1.0f + u[e] * (1.0f - sg));
+      }
+    }
+    // A^T (rows hidden) by an MFMA with I: A-operand = A tile (rows t) as K = 16 operand
+    float4_t actT[4];
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa) actT[aa] = mfma(pad_op(act[aa]), eye, zero);
+
+    // O^T partial = W2 A^T (rows output, cols t): contraction over this wave's 64 hidden
+    bf16x8_t atb[2];  // B operand over hidden: pairs of A^T tiles
+    atb[0] = pair_op(actT[0], actT[1]);
+    atb[1] = pair_op(actT[2], actT[3]);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      float4_t ot = mfma(pair_op(st.w2t[0][it], st.w2t[1][it]), atb[0], zero);
+      ot = mfma(pair_op(st.w2t[2][it], st.w2t[3][it]), atb[1], ot);
+      lds_store<float4_t>(opart, ((wv * kB + n) * kD + 16 * it + 4 * g) * 4, ot);
+    }
+    barrier();
+    // previous chunk's Z (its partials were written before this barrier)
+    if (c > 0) reduce_store_z(c - 1);
+    // R = sum of partials - V, fp32 in LDS
+    {
+      float4_t s4 = zero;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) s4 += lds_load<float4_t>(opart, ((w * kB + rt) * kD + ri) * 4);
+      const u32x2 vb = cur.vv;
+      s4[0] -= __builtin_bit_cast(float, vb.x << 16);
+      s4[1] -= __builtin_bit_cast(float, vb.x & 0xFFFF0000u);
+      s4[2] -= __builtin_bit_cast(float, vb.y << 16);
+      s4[3] -= __builtin_bit_cast(float, vb.y & 0xFFFF0000u);
+      lds_store<float4_t>(rbuf, (rt * kD + ri) * 4, s4);
+    }
+    barrier();
+
+    // R in the C layout (rows t) per output tile, and as row operands over outputs
+    float4_t rc[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      float4_t x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = lds_load<float>(rbuf, ((4 * g + e) * kD + 16 * it + n) * 4);
+      rc[it] = x;
+    }
+    bf16x8_t rrow[2];  // A operand of R W2 (m = t, k = output; pairs of output tiles)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float4_t f0 = lds_load<float4_t>(rbuf, (n * kD + 32 * h + 4 * g) * 4);
+      const float4_t f1 = lds_load<float4_t>(rbuf, (n * kD + 32 * h + 16 + 4 * g) * 4);
+      rrow[h] = pair_op(f0, f1);
+    }
+    // dU = (R W2) * S  (rows t, hidden tile aa); keep -eta dU as a padded operand
+    bf16x8_t dub[4];
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa) {
+      float4_t da = mfma(rrow[0], pair_op(st.w2[0][aa], st.w2[1][aa]), zero);
+      da = mfma(rrow[1], pair_op(st.w2[2][aa], st.w2[3][aa]), da);
+      dub[aa] = pad_op(da * sd[aa], -eta);
+    }
+    // -eta R and A as padded K = 16 operands (rows t)
+    bf16x8_t rb[4], ab[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) rb[it] = pad_op(rc[it], -eta);
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa) ab[aa] = pad_op(act[aa]);
+
+    // ---- outputs (use the chunk-start state) ----
+    // P^T = K Q^T with the causal mask s <= t, padded B operand
+    float4_t pt = mfma(ka0, qb0, zero);
+    pt = mfma(ka1, qb1, pt);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pt[e] = keep[e] ? pt[e] : 0.0f;
+    const bf16x8_t ptb = pad_op(pt);
+    // U_q^T = W1 Q^T - eta dU^T P^T (rows hidden tile aa, cols t);  A_q^T = SiLU(U_q^T)
+    float4_t aqT[4];
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa) {
+      float4_t u = mfma(w1b[0][aa], qb0, zero);
+      u = mfma(w1b[1][aa], qb1, u);
+      u = mfma(dub[aa], ptb, u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[e] = u[e] * sigmoid_f(u[e]);
+      aqT[aa] = u;
+    }
+    const bf16x8_t aqb0 = pair_op(aqT[0], aqT[1]), aqb1 = pair_op(aqT[2], aqT[3]);
+    // G^T = A A_q^T (rows s, cols t) over this wave's hidden units, masked s <= t
+    float4_t gt = mfma(atb[0], aqb0, zero);
+    gt = mfma(atb[1], aqb1, gt);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) gt[e] = keep[e] ? gt[e] : 0.0f;
+    const bf16x8_t gtb = pad_op(gt);
+    // Z^T partial = W2 A_q^T + (-eta R)^T G^T (rows output tile it, cols t)
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      float4_t zt = mfma(pair_op(st.w2t[0][it], st.w2t[1][it]), aqb0, zero);
+      zt = mfma(pair_op(st.w2t[2][it], st.w2t[3][it]), aqb1, zt);
+      zt = mfma(rb[it], gtb, zt);
+      lds_store<float4_t>(zpart, ((wv * kB + n) * kD + 16 * it + 4 * g) * 4, zt);
+    }
+
+    // ---- state update (sum of the chunk's gradients) ----
+    // W1^T += K^T (-eta dU): A = K^T gather for j tile jb, B = dU tile aa
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+      const int h = jb >> 1;
+      const uint32_t sel = (jb & 1) ? kHi : kLo;
+      const bf16x8_t kt = op4(__builtin_amdgcn_perm(cur.kt[1][h], cur.kt[0][h], sel),
+                              __builtin_amdgcn_perm(cur.kt[3][h], cur.kt[2][h], sel), 0u, 0u);
+#pragma unroll
+      for (int aa = 0; aa < 4; ++aa) st.w1t[jb][aa] = mfma(kt, dub[aa], st.w1t[jb][aa]);
+    }
+    // W2^T += A^T (-eta R): A-operand = A tile aa (rows t), B = -eta R tile it
+    // W2   += (-eta R)^T A: A-operand = -eta R tile it (rows t), B = A tile aa
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa)
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        st.w2t[aa][it] = mfma(ab[aa], rb[it], st.w2t[aa][it]);
+        st.w2[it][aa] = mfma(rb[it], ab[aa], st.w2[it][aa]);
+      }
+    cur = nxt;
+  }
+  barrier();
+  if (nchunks > 0) reduce_store_z(nchunks - 1);
+
+  // ---- final state ----
+  if (a.w1_out) {
+    float* o1 = a.w1_out + static_cast<size_t>(chain) * hd;
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa) {
+      float* wr = o1 + static_cast<size_t>(h0 + 16 * aa + n) * kD + 16 * g;
+      const float4_t* t = &st.w1t[0][aa];
+      (void)t;
+      *reinterpret_cast<float4_t*>(wr) =
+          float4_t{st.w1t[0][aa][0], st.w1t[1][aa][0], st.w1t[0][aa][1], st.w1t[1][aa][1]};
+      *reinterpret_cast<float4_t*>(wr + 4) =
+          float4_t{st.w1t[0][aa][2], st.w1t[1][aa][2], st.w1t[0][aa][3], st.w1t[1][aa][3]};
+      *reinterpret_cast<float4_t*>(wr + 8) =
+          float4_t{st.w1t[2][aa][0], st.w1t[3][aa][0], st.w1t[2][aa][1], st.w1t[3][aa][1]};
+      *reinterpret_cast<float4_t*>(wr + 12) =
+          float4_t{st.w1t[2][aa][2], st.w1t[3][aa][2], st.w1t[2][aa][3], st.w1t[3][aa][3]};
+    }
+  }
+  if (a.w2_out) {
+    float* o2 = a.w2_out + static_cast<size_t>(chain) * hd;
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa)
+#pragma unroll
+      for (int it = 0; it < 4; ++it)
+        *reinterpret_cast<float4_t*>(o2 + static_cast<size_t>(16 * it + n) * kH + h0 + 16 * aa + 4 * g) =
+            st.w2t[aa][it];
+  }
+}
+
+}  // namespace
+
+bool mlp_fast_supported(const MlpArgs& a, bool bf16_io) {
+  auto al = [](const void* p, uintptr_t m) { return (reinterpret_cast<uintptr_t>(p) & (m - 1)) == 0; };
+  const bool aligned = al(a.q, 16) && al(a.k, 16) && al(a.v, 16) && al(a.z, 16) && al(a.w1, 16) &&
+                       al(a.w2, 16) && (a.w_batch_stride % 4) == 0 &&
+                       (a.w1_out == nullptr || al(a.w1_out, 16)) &&
+                       (a.w2_out == nullptr || al(a.w2_out, 16));
+  const bool fits = static_cast<long long>(a.T) * kD * 2 + 4LL * kTileBytes < 0x7fffffffLL;
+  return bf16_io && a.d == kD && a.dh == kH && a.chunk == kB && a.causal == 1 && a.T > 0 &&
+         aligned && fits;
+}
+
+hipError_t launch_mlp_fast(const MlpArgs& a, hipStream_t s) {
+  const long long nchains = static_cast<long long>(a.B) * a.H;
+  if (nchains > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mlp_mfma_kernel, dim3(static_cast<unsigned>(nchains)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace ttt
