@@ -65,6 +65,8 @@ size_t delta_workspace_bytes(const LinearArgs& a);
 hipError_t launch_delta_fast(const LinearArgs& a, void* workspace, hipStream_t s);
 bool mlp_fast_supported(const MlpArgs& a, bool bf16_io);
 hipError_t launch_mlp_fast(const MlpArgs& a, hipStream_t s);
+bool mlp_nc_supported(const MlpArgs& a, bool bf16_io);
+hipError_t launch_mlp_nc(const MlpArgs& a, hipStream_t s);
 
 // dst[b][h][:] = src + b * batch_stride + h * per_head (the state when T = 0).
 hipError_t launch_copy_state(float* dst, const float* src, long long batch_stride, int B, int H,

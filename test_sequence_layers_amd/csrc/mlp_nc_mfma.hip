@@ -1,0 +1,329 @@
+// Non-causal full-batch TTT-MLP forward on the gfx950 matrix cores: f(k) = W2 SiLU(W1 k),
+// d = 64, hidden 64, one mini-batch holding every token, bf16 Q/K/V/Z, fp32 state.
+//
+// Method (ViT3 news page, section 1, inner training setup: the keys and values are a small
+// training set, one full-batch gradient step, then the trained inner model is applied to
+// every query; inner model: section 2, 2-layer SiLU MLP).  With U = K W1^T, A = SiLU(U),
+// S = SiLU'(U), R = A W2^T - V and dU = (R W2) * S over all N tokens:
+//   W1' = W1 - eta dU^T K,   W2' = W2 - eta R^T A,   Z = SiLU(Q W1'^T) W2'^T.
+//
+// Mapping.  One wave per (batch, head) chain; no LDS, no barriers.  Pass 1 streams the
+// tokens 16 at a time and accumulates the two gradient sums G1^T = K^T dU and
+// G2^T = A^T R in fp32 MFMA accumulator tiles while W1, W2 stay fixed as bf16 operands
+// (W2 in both orientations: the forward pass contracts it over hidden units, the backward
+// pass over outputs).  Pass 2 forms W1', W2' from the initial weights and the sums and
+// streams the queries.  Tokens past N (the last tile) read as zero and contribute nothing
+// (no bias, SiLU(0) = 0); their outputs are not stored.  Layouts follow the causal MLP
+// kernel: 16 x 16 C-layout tiles, the input index j permuted as j = 16 (m/4) + 2 (m%4) +
+// 8h + p in W1^T tile 2h+p so that operands over j match 16-byte row loads of K and Q, and
+// hidden / output indices natural.
+#include "common.hpp"
+
+namespace ttt {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kD = 64;
+constexpr int kH = 64;
+constexpr int kTile = 16;
+constexpr int kTileBytes = kTile * kD * 2;
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ bf16x8_t bf(const u32x4& x) { return __builtin_bit_cast(bf16x8_t, x); }
+__device__ __forceinline__ bf16x8_t op4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const u32x4 u = {a, b, c, d};
+  return bf(u);
+}
+__device__ __forceinline__ bf16x8_t pair_op(const float4_t& x, const float4_t& y) {
+  return op4(pack_bf16(x[0], y[0]), pack_bf16(x[1], y[1]), pack_bf16(x[2], y[2]), pack_bf16(x[3], y[3]));
+}
+__device__ __forceinline__ bf16x8_t pad_op(const float4_t& x) {
+  return op4(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), 0u, 0u);
+}
+__device__ __forceinline__ float4_t mfma(const bf16x8_t& a, const bf16x8_t& b, const float4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float sigmoid_f(float u) { return 1.0f / (1.0f + __expf(-u)); }
+__device__ __forceinline__ float bf_lo(uint32_t x) { return __builtin_bit_cast(float, x << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t x) { return __builtin_bit_cast(float, x & 0xFFFF0000u); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int left) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, left > 0 ? left : 0,
+                                           0x00020000);
+}
+
+// W1^T tiles [jb][a] (rows j permuted, cols hidden 16a + n) from W1 [hidden][d] fp32
+__device__ __forceinline__ void load_w1t(float4_t (&w)[4][4], const float* w1, int g, int n) {
+#pragma unroll
+  for (int aa = 0; aa < 4; ++aa) {
+    const float* wr = w1 + (16 * aa + n) * kD + 16 * g;
+    const float4_t f0 = *reinterpret_cast<const float4_t*>(wr);
+    const float4_t f1 = *reinterpret_cast<const float4_t*>(wr + 4);
+    const float4_t f2 = *reinterpret_cast<const float4_t*>(wr + 8);
+    const float4_t f3 = *reinterpret_cast<const float4_t*>(wr + 12);
+    w[0][aa] = float4_t{f0[0], f0[2], f1[0], f1[2]};
+    w[1][aa] = float4_t{f0[1], f0[3], f1[1], f1[3]};
+    w[2][aa] = float4_t{f2[0], f2[2], f3[0], f3[2]};
+    w[3][aa] = float4_t{f2[1], f2[3], f3[1], f3[3]};
+  }
+}
+// W2^T tiles [a][it] (rows hidden 16a + m, cols output 16it + n) from W2 [d][hidden]
+__device__ __forceinline__ void load_w2t(float4_t (&w)[4][4], const float* w2, int g, int n) {
+#pragma unroll
+  for (int aa = 0; aa < 4; ++aa)
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+      w[aa][it] = *reinterpret_cast<const float4_t*>(w2 + (16 * it + n) * kH + 16 * aa + 4 * g);
+}
+
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void mlp_nc_kernel(MlpArgs a) {
+  const int chain = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int g = lane >> 4;
+  const int n = lane & 15;
+  const int bi = chain / a.H;
+  const int hi = chain - bi * a.H;
+  const int T = a.T;
+  const int ntiles = (T + kTile - 1) / kTile;
+  const int seq_bytes = T * kD * 2;
+  const float eta = a.eta;
+
+  const size_t tok0 = static_cast<size_t>(chain) * static_cast<size_t>(T) * kD;
+  const char* q = reinterpret_cast<const char*>(static_cast<const bf16*>(a.q) + tok0);
+  const char* k = reinterpret_cast<const char*>(static_cast<const bf16*>(a.k) + tok0);
+  const char* v = reinterpret_cast<const char*>(static_cast<const bf16*>(a.v) + tok0);
+  char* z = reinterpret_cast<char*>(static_cast<bf16*>(a.z) + tok0);
+  const size_t hd = static_cast<size_t>(kH) * kD;
+  const float* w1g = a.w1 + bi * a.w_batch_stride + static_cast<long long>(hi) * hd;
+  const float* w2g = a.w2 + bi * a.w_batch_stride + static_cast<long long>(hi) * hd;
+
+  const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  constexpr uint32_t kLo = 0x05040100u, kHi = 0x07060302u;
+  const uint32_t one = 0x3F80u;  // bf16 1.0
+  const bf16x8_t eye = op4((4 * g + 0 == n ? one : 0u) | (4 * g + 1 == n ? one << 16 : 0u),
+                           (4 * g + 2 == n ? one : 0u) | (4 * g + 3 == n ? one << 16 : 0u), 0u, 0u);
+  const int row = n * 128 + 32 * g;  // K / Q operand rows (16 bytes at +0 and +16)
+  const int c0 = 16 * (n >> 2) + 2 * (n & 3);
+  int kto[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) kto[e] = (4 * g + e) * 128 + 2 * c0;
+
+  // ---- bf16 operands of the initial weights ----
+  bf16x8_t w1b[2][4];   // [h][a]: operand over j (B of K W1^T, A of W1 Q^T)
+  bf16x8_t w2tb[2][4];  // [h][it]: operand over hidden (A of W2 A^T)
+  bf16x8_t w2b[2][4];   // [h][a]: operand over outputs (B of R W2)
+  {
+    float4_t t[4][4];
+    load_w1t(t, w1g, g, n);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int aa = 0; aa < 4; ++aa) w1b[h][aa] = pair_op(t[2 * h][aa], t[2 * h + 1][aa]);
+    load_w2t(t, w2g, g, n);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int it = 0; it < 4; ++it) w2tb[h][it] = pair_op(t[2 * h][it], t[2 * h + 1][it]);
+    // W2 tiles [it][a]: rows output 16it + m, cols hidden 16a + n
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+#pragma unroll
+      for (int aa = 0; aa < 4; ++aa) {
+        float4_t x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = w2g[(16 * it + 4 * g + e) * kH + 16 * aa + n];
+        t[it][aa] = x;
+      }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int aa = 0; aa < 4; ++aa) w2b[h][aa] = pair_op(t[2 * h][aa], t[2 * h + 1][aa]);
+  }
+
+  // ---- pass 1: gradient sums over all tokens ----
+  float4_t g1t[4][4];  // sum of K^T dU, layout of W1^T
+  float4_t g2t[4][4];  // sum of A^T R, layout of W2^T
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      g1t[i][j] = zero;
+      g2t[i][j] = zero;
+    }
+  for (int tt = 0; tt < ntiles; ++tt) {
+    const int off = tt * kTileBytes;
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(k + off, seq_bytes - off);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(v + off, seq_bytes - off);
+    const bf16x8_t ka0 = bf(__builtin_amdgcn_raw_buffer_load_b128(rk, row, 0, 0));
+    const bf16x8_t ka1 = bf(__builtin_amdgcn_raw_buffer_load_b128(rk, row + 16, 0, 0));
+    uint32_t kt[4][2];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      kt[e][0] = __builtin_amdgcn_raw_buffer_load_b32(rk, kto[e], 0, 0);
+      kt[e][1] = __builtin_amdgcn_raw_buffer_load_b32(rk, kto[e] + 16, 0, 0);
+    }
+    u32x2 vv[4];  // V[t = n][16 it + 4 g .. + 3]
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+      vv[it] = __builtin_amdgcn_raw_buffer_load_b64(rv, n * 128 + 2 * (16 * it + 4 * g), 0, 0);
+
+    // U = K W1^T (rows t); A = SiLU(U), S = SiLU'(U)
+    float4_t act[4], sd[4];
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa) {
+      float4_t u = mfma(ka0, w1b[0][aa], zero);
+      u = mfma(ka1, w1b[1][aa], u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float sg = sigmoid_f(u[e]);
+        act[aa][e] = u[e] * sg;
+        sd[aa][e] = sg * (1.0f + u[e] * (1.0f - sg));
+      }
+    }
+    // A^T (rows hidden)
+    float4_t actT[4];
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa) actT[aa] = mfma(pad_op(act[aa]), eye, zero);
+    const bf16x8_t atb0 = pair_op(actT[0], actT[1]), atb1 = pair_op(actT[2], actT[3]);
+    // R^T = W2 A^T - V^T (rows output tile it, cols t)
+    float4_t rT[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      float4_t o = mfma(w2tb[0][it], atb0, zero);
+      o = mfma(w2tb[1][it], atb1, o);
+      o[0] -= bf_lo(vv[it].x);
+      o[1] -= bf_hi(vv[it].x);
+      o[2] -= bf_lo(vv[it].y);
+      o[3] -= bf_hi(vv[it].y);
+      rT[it] = o;
+    }
+    // dU = (R W2) * S (rows t): A-operand R (m = t, k = output) from pairs of R^T tiles
+    const bf16x8_t rrow0 = pair_op(rT[0], rT[1]), rrow1 = pair_op(rT[2], rT[3]);
+    bf16x8_t dub[4];
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa) {
+      float4_t da = mfma(rrow0, w2b[0][aa], zero);
+      da = mfma(rrow1, w2b[1][aa], da);
+      dub[aa] = pad_op(da * sd[aa]);
+    }
+    // R (rows t) from R^T by an MFMA with I, as padded operands
+    bf16x8_t rb[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) rb[it] = pad_op(mfma(pad_op(rT[it]), eye, zero));
+    // G1^T += K^T dU ; G2^T += A^T R
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+      const int h = jb >> 1;
+      const uint32_t sel = (jb & 1) ? kHi : kLo;
+      const bf16x8_t ktb = op4(__builtin_amdgcn_perm(kt[1][h], kt[0][h], sel),
+                               __builtin_amdgcn_perm(kt[3][h], kt[2][h], sel), 0u, 0u);
+#pragma unroll
+      for (int aa = 0; aa < 4; ++aa) g1t[jb][aa] = mfma(ktb, dub[aa], g1t[jb][aa]);
+    }
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa) {
+      const bf16x8_t ab = pad_op(act[aa]);
+#pragma unroll
+      for (int it = 0; it < 4; ++it) g2t[aa][it] = mfma(ab, rb[it], g2t[aa][it]);
+    }
+  }
+
+  // ---- trained weights W' = W - eta G, as bf16 operands ----
+  bf16x8_t w1nb[2][4], w2nb[2][4];
+  {
+    float4_t t[4][4];
+    load_w1t(t, w1g, g, n);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) t[i][j] -= eta * g1t[i][j];
+    if (a.w1_out) {
+      float* o1 = a.w1_out + static_cast<size_t>(chain) * hd;
+#pragma unroll
+      for (int aa = 0; aa < 4; ++aa) {
+        float* wr = o1 + (16 * aa + n) * kD + 16 * g;
+        *reinterpret_cast<float4_t*>(wr) = float4_t{t[0][aa][0], t[1][aa][0], t[0][aa][1], t[1][aa][1]};
+        *reinterpret_cast<float4_t*>(wr + 4) = float4_t{t[0][aa][2], t[1][aa][2], t[0][aa][3], t[1][aa][3]};
+        *reinterpret_cast<float4_t*>(wr + 8) = float4_t{t[2][aa][0], t[3][aa][0], t[2][aa][1], t[3][aa][1]};
+        *reinterpret_cast<float4_t*>(wr + 12) = float4_t{t[2][aa][2], t[3][aa][2], t[2][aa][3], t[3][aa][3]};
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int aa = 0; aa < 4; ++aa) w1nb[h][aa] = pair_op(t[2 * h][aa], t[2 * h + 1][aa]);
+    load_w2t(t, w2g, g, n);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) t[i][j] -= eta * g2t[i][j];
+    if (a.w2_out) {
+      float* o2 = a.w2_out + static_cast<size_t>(chain) * hd;
+#pragma unroll
+      for (int aa = 0; aa < 4; ++aa)
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+          *reinterpret_cast<float4_t*>(o2 + (16 * it + n) * kH + 16 * aa + 4 * g) = t[aa][it];
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int it = 0; it < 4; ++it) w2nb[h][it] = pair_op(t[2 * h][it], t[2 * h + 1][it]);
+  }
+
+  // ---- pass 2: Z^T = W2' SiLU(W1' Q^T) ----
+  for (int tt = 0; tt < ntiles; ++tt) {
+    const int off = tt * kTileBytes;
+    const __amdgpu_buffer_rsrc_t rq = tile_rsrc(q + off, seq_bytes - off);
+    const bf16x8_t qb0 = bf(__builtin_amdgcn_raw_buffer_load_b128(rq, row, 0, 0));
+    const bf16x8_t qb1 = bf(__builtin_amdgcn_raw_buffer_load_b128(rq, row + 16, 0, 0));
+    float4_t aq[4];
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa) {
+      float4_t u = mfma(w1nb[0][aa], qb0, zero);
+      u = mfma(w1nb[1][aa], qb1, u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[e] = u[e] * sigmoid_f(u[e]);
+      aq[aa] = u;
+    }
+    const bf16x8_t aqb0 = pair_op(aq[0], aq[1]), aqb1 = pair_op(aq[2], aq[3]);
+    const __amdgpu_buffer_rsrc_t rz = tile_rsrc(z + off, seq_bytes - off);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      float4_t zt = mfma(w2nb[0][it], aqb0, zero);
+      zt = mfma(w2nb[1][it], aqb1, zt);
+      const u32x2 out = {pack_bf16(zt[0], zt[1]), pack_bf16(zt[2], zt[3])};
+      __builtin_amdgcn_raw_buffer_store_b64(out, rz, n * 128 + 2 * (16 * it + 4 * g), 0, 0);
+    }
+  }
+}
+
+}  // namespace
+
+bool mlp_nc_supported(const MlpArgs& a, bool bf16_io) {
+  auto al = [](const void* p, uintptr_t m) { return (reinterpret_cast<uintptr_t>(p) & (m - 1)) == 0; };
+  const bool aligned = al(a.q, 16) && al(a.k, 16) && al(a.v, 16) && al(a.z, 16) && al(a.w1, 16) &&
+                       al(a.w2, 16) && (a.w_batch_stride % 4) == 0 &&
+                       (a.w1_out == nullptr || al(a.w1_out, 16)) &&
+                       (a.w2_out == nullptr || al(a.w2_out, 16));
+  const bool fits = static_cast<long long>(a.T) * kD * 2 + 2LL * kTileBytes < 0x7fffffffLL;
+  return bf16_io && a.d == kD && a.dh == kH && a.causal == 0 && a.chunk >= a.T && a.T > 0 &&
+         aligned && fits;
+}
+
+hipError_t launch_mlp_nc(const MlpArgs& a, hipStream_t s) {
+  const long long nchains = static_cast<long long>(a.B) * a.H;
+  if (nchains > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mlp_nc_kernel, dim3(static_cast<unsigned>(nchains)), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace ttt

@@ -177,6 +177,8 @@ int ttt_mlp_fwd(const void* q, const void* k, const void* v, const float* w1, co
   StreamBuffer ws;
   if (ttt::mlp_fast_supported(a, bf16)) {
     e = ttt::launch_mlp_fast(a, s);
+  } else if (ttt::mlp_nc_supported(a, bf16)) {
+    e = ttt::launch_mlp_nc(a, s);
   } else {
     rc = get_workspace(ttt::mlp_generic_workspace_floats(a) * sizeof(float), s, &ws);
     if (rc != TTT_OK) return rc;
