@@ -44,6 +44,24 @@ def algorithmic_cost(w):
     return 4 * tok + state, fl
 
 
+def measured_traffic(workload_name):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE for the kernel of
+    this workload, or None when no record exists or the kernel source has changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{workload_name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    src = os.path.join(ROOT, rec["source"])
+    if not os.path.exists(src):
+        return None
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
+            return None
+    return rec["fetch_bytes"] + rec["write_bytes"]
+
+
 def make_device_inputs(w, seed, torch):
     import numpy as np
     from test_sequence_layers_amd.workloads import make_inputs
@@ -192,8 +210,8 @@ def main():
         "peak": peak,
         "unit": "GB/s",
         "frac": round(res["hbm_gbs"] / peak, 4),
-        "traffic": None,
-        "kernel": "ttt_linear (per launch: Q,K,V read + Z written + W0 read)",
+        "traffic": measured_traffic(w.name),
+        "kernel": "linear_mfma_kernel (per launch: Q,K,V read + Z written + W0 read)",
         "bytes_per_launch": res["bytes"],
     }
     line = {
