@@ -20,10 +20,10 @@
 // Mapping.  One workgroup of 4 waves per (batch, head) chain.  The linear model is
 // separable by output row (row i of W only needs v[i]), so wave w owns rows 16w..16w+15 of
 // W and never exchanges state with the other waves.  A fifth wave streams Q/K/V chunks into
-// an LDS ring kRing chunks deep with direct-to-LDS buffer loads (no registers are spent on
-// data in flight), and wave 3 writes Z back with whole-row stores from an LDS staging
-// buffer.  One barrier per chunk publishes the next chunk and recycles a slot; the compute
-// waves read the next chunk's operands while they compute the current one.
+// an LDS ring with direct-to-LDS buffer loads (no registers are spent on data in flight);
+// one barrier per group of 4 chunks publishes chunks and recycles slots.  The compute
+// waves read the next chunk's operands while they compute the current one and store their
+// 16 columns of Z directly.
 // Within a wave everything stays in registers, in the layouts the MFMA operands need:
 //   * the fp32 state W^T (64 x 16) is 4 accumulator tiles of v_mfma_f32_16x16x32_bf16;
 //   * its bf16 copy is, lane for lane, the B operand of R = K W^T and the A operand of
@@ -74,13 +74,17 @@ __device__ __forceinline__ bf16x8_t bf(const u32x4& x) { return __builtin_bit_ca
 // the row-strided operand reads of a wave spread over the banks.
 constexpr int kTileBytes = kB * kD * 2;
 constexpr int kTmBytes = kB * kB * 2;  // one 16 x 16 bf16 Tm matrix of the delta rule
-// Ring slots (chunks in flight ahead of the compute waves) and bytes per slot.  The loader
-// issues 6 loads per chunk (7 with Tm) and waits with a 6-bit vmcnt, which bounds the ring.
+// Ring of kSlots chunk slots, published kGroup chunks per barrier.  The loader issues
+// kLoads loads per chunk (6, or 7 with Tm) and before barrier g waits until the chunks the
+// compute waves read in group g have landed, leaving kSlots - 2 kGroup chunks in flight;
+// the 6-bit vmcnt bounds that count.
+constexpr int kGroup = 4;
 template <bool kDelta> struct Ring {
   static constexpr int kLoads = kDelta ? 7 : 6;
-  static constexpr int kSlots = kDelta ? 9 : 11;
+  static constexpr int kSlots = 14;
   static constexpr int kSlotBytes = 3 * kTileBytes + (kDelta ? 1024 : 0);
-  static_assert(kLoads * (kSlots - 1) < 64, "vmcnt is 6 bits");
+  static_assert(kLoads * (kSlots - 1 - kGroup) < 64, "vmcnt is 6 bits");
+  static_assert(kSlots >= 2 * kGroup, "ring too small for the group");
 };
 typedef __attribute__((address_space(3))) char lds_char;
 
@@ -230,9 +234,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   using RG = Ring<kDelta>;
   constexpr int kRing = RG::kSlots;
   __shared__ __attribute__((aligned(16))) char ring_mem[kRing * RG::kSlotBytes];
-  __shared__ __attribute__((aligned(16))) char zbuf_mem[2 * kTileBytes];
   lds_char* ring = (lds_char*)(ring_mem);
-  lds_char* zbuf = (lds_char*)(zbuf_mem);
 
   const int chain = blockIdx.x;
   const int tid = threadIdx.x;
@@ -273,15 +275,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + 3 * kTileBytes, 16, lane * 16, 0, 0, 0);
       }
     };
+    // The compute waves read chunk 0 after barrier 0 and chunks kGroup g + 1 .. kGroup g +
+    // kGroup between barriers g and g + 1.  So barrier g publishes the chunks up to
+    // kGroup g + kGroup, and from g = 1 on it frees the slots of the chunks up to kGroup g,
+    // after which the loader refills the ring up to chunk kGroup g + kRing.
+    // Barrier 0 frees nothing; the wait before barrier 1 leaves chunks kGroup + kGroup + 1 ..
+    // kRing - 1 in flight, later waits leave kRing - 2 kGroup chunks in flight.
+    const int ngroups = (nchunks + kGroup - 1) / kGroup;
     for (int c = 0; c < kRing; ++c) issue(c);
-    wait_vmcnt<RG::kLoads * (kRing - 1)>();  // chunk 0 landed
+    wait_vmcnt<RG::kLoads * (kRing - 1 - kGroup)>();
     lds_barrier();
-    for (int c = 0; c < nchunks; ++c) {
-      wait_vmcnt<RG::kLoads * (kRing - 2)>();  // chunk c + 1 landed
+    if (ngroups > 1) {
+      wait_vmcnt<RG::kLoads * (kRing - 1 - 2 * kGroup)>();
       lds_barrier();
-      issue(c + kRing);
+#pragma unroll
+      for (int x = 0; x <= kGroup; ++x) issue(kRing + x);
     }
-    lds_barrier();
+    for (int grp = 2; grp < ngroups; ++grp) {
+      wait_vmcnt<RG::kLoads * (kRing - 2 * kGroup)>();
+      lds_barrier();
+#pragma unroll
+      for (int x = 1; x <= kGroup; ++x) issue(kGroup * (grp - 1) + kRing + x);
+    }
+    wait_vmcnt<0>();  // no load outlives the wave
     return;
   }
 
@@ -327,45 +343,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
     for (int h = 0; h < 2; ++h) o.kt[e][h] = swz(4 * g + e, 2 * (n >> 2) + h) * 16 + 4 * (n & 3);
   o.vv = swz(n, 2 * wv + (g >> 1)) * 16 + 8 * (g & 1);
   o.tm = n * 32 + 8 * g;
-  const int zw = o.vv;  // lane (g, n) stages Z[n][i0 + 4g .. +3] where it read V from
 
-  // Storer role (wave 3): writes a staged 16 x 64 Z tile with whole-row stores; lane l
-  // covers row l / 4, pieces 2 (l % 4) and 2 (l % 4) + 1.
-  const int srow = lane >> 2;
-  const int sp0 = 2 * (lane & 3);
-  auto store_z = [&](int c) {
-    const lds_char* zb = zbuf + (c & 1) * kTileBytes;
-    const u32x4 d0 = lds_load<u32x4>(zb, swz(srow, sp0) * 16);
-    const u32x4 d1 = lds_load<u32x4>(zb, swz(srow, sp0 + 1) * 16);
+  // Step c: compute chunk c from registers read in step c - 1 while reading chunk c + 1,
+  // and store this wave's 16 columns of Z_c (8 bytes per lane; rows past T are dropped by
+  // the buffer range).  Chunks past the end read as zeros and leave the state unchanged.
+  const int zoff = n * 128 + 2 * (i0 + 4 * g);
+  auto step = [&](int c, ChunkRegs& cur, ChunkRegs& nxt) {
+    __builtin_amdgcn_sched_barrier(0);  // keep steps apart (register pressure)
+    read_chunk<kDelta>(nxt, ring + ((c + 1) % kRing) * RG::kSlotBytes, o);
+    const u32x2 zz = chunk_step<kDelta>(wacc, cur, lc);
     const int off = c * kTileBytes;
-    const __amdgpu_buffer_rsrc_t rs = chunk_rsrc(z + off, seq_bytes - off);
-    __builtin_amdgcn_raw_buffer_store_b128(d0, rs, srow * 128 + sp0 * 16, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b128(d1, rs, srow * 128 + sp0 * 16 + 16, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(zz, chunk_rsrc(z + off, seq_bytes - off), zoff, 0, 0);
   };
-
-  // Step c: after barrier c, read chunk c + 1 (published by that barrier) while computing
-  // chunk c from registers read in step c - 1; stage Z_c; wave 3 stores Z_{c-1}.
-  lds_barrier();  // chunk 0 published
+  const int ngroups = (nchunks + kGroup - 1) / kGroup;
+  lds_barrier();  // barrier 0: chunks 0 .. kGroup published
   ChunkRegs ra, rb;
   read_chunk<kDelta>(ra, ring, o);
-  auto step = [&](int c, ChunkRegs& cur, ChunkRegs& nxt) {
-    lds_barrier();
-    read_chunk<kDelta>(nxt, ring + ((c + 1) % kRing) * RG::kSlotBytes, o);
-    if (wv == 3 && c > 0) store_z(c - 1);
-    const u32x2 zz = chunk_step<kDelta>(wacc, cur, lc);
-    lds_store<u32x2>(zbuf + (c & 1) * kTileBytes, zw, zz);
-  };
-  int c = 0;
-  for (; c + 2 <= nchunks; c += 2) {
-    step(c, ra, rb);
+  for (int grp = 0; grp < ngroups; ++grp) {
+    if (grp > 0) lds_barrier();
+    const int c = grp * kGroup;
+    static_assert(kGroup == 4, "the group below is written out for 4 chunks");
+    step(c + 0, ra, rb);
     step(c + 1, rb, ra);
+    step(c + 2, ra, rb);
+    step(c + 3, rb, ra);
   }
-  if (c < nchunks) {
-    step(c, ra, rb);
-    ++c;
-  }
-  lds_barrier();
-  if (wv == 3 && nchunks > 0) store_z(nchunks - 1);
 
   if (a.w_out) {
     float* wr = a.w_out + static_cast<size_t>(chain) * kD * kD + (i0 + n) * kD + 16 * g;
