@@ -126,7 +126,7 @@ struct ChunkRegs {
   u32x4 qb0, qb1;          // Q[n][8 g + 0..7], Q[n][32 + 8 g + 0..7]
   u32x2 kt0, kt1, kt2, kt3;  // tile t: K[4 g + s][j_t(n)], s = 0..3 (A operand of the update)
   u32x2 vv;                // V[n][i0 + 4 g .. 4 g + 3]
-  u32x2 tm;                // delta rule: Tm[n][4 g .. 4 g + 3]
+  u32x2 tm;                // delta rule: Tm[n][4 g .. 4 g + 3] (from the stored Tm^T)
 };
 
 // Per-lane byte offsets inside a slot, fixed for the whole kernel.
@@ -152,7 +152,7 @@ __device__ __forceinline__ void read_chunk(ChunkRegs& r, const lds_char* slot, c
   r.kt2 = lds_load_tr(k + o.kt1);
   r.kt3 = lds_load_tr(k + o.kt1 + 8);
   r.vv = lds_load<u32x2>(slot + kVOff + o.vv);
-  if (kDelta) r.tm = lds_load<u32x2>(slot + kTmOff + o.tm);
+  if (kDelta) r.tm = lds_load_tr(slot + kTmOff + o.tm);
 }
 
 struct WState {
@@ -284,8 +284,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
       const __amdgpu_buffer_rsrc_t rv = chunk_rsrc(vsrc + off, seq_bytes - off);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst + kVOff, 16, vglob, 0, 0, 0);
       if (kDelta) {
-        // Tm of chunk c: 512 bytes read by lanes 0..31; lanes 32..63 are out of range and
-        // fill the second half of the 1 KB area with zeros.
+        // Tm^T of chunk c: 512 bytes read by lanes 0..31; lanes 32..63 are out of range
+        // and fill the second half of the 1 KB area with zeros.
         const __amdgpu_buffer_rsrc_t rs =
             chunk_rsrc(tsrc + static_cast<size_t>(c) * kTmBytes, c < nchunks ? kTmBytes : 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + kTmOff, 16, lane * 16, 0, 0, 0);
@@ -349,7 +349,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   o.kt0 = swz(4 * g + (n >> 2), n & 3) * 16;
   o.kt1 = swz(4 * g + (n >> 2), 4 + (n & 3)) * 16;
   o.vv = vswz(n, 2 * wv + (g >> 1)) * 16 + 8 * (g & 1);
-  o.tm = n * 32 + 8 * g;
+  o.tm = (4 * g + (n >> 2)) * 32 + 8 * (n & 3);
 
   // Step c: compute chunk c from registers read in step c - 1 while reading chunk c + 1,
   // and store this wave's 16 columns of Z_c (8 bytes per lane; rows past T are dropped by
@@ -421,45 +421,74 @@ hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s) {
 
 // ------------------------------------------------------------------------------ delta rule
 
-// Tm = (I + eta stril(K K^T))^-1 for every chunk of every chain, in bf16, row-major
-// [chain][chunk][16][16].  One group of 16 lanes per chunk (16 chunks per workgroup):
-// lane j first computes column j of the strictly lower Gram matrix, then column j of Tm by
-// forward substitution, Tm[t][j] = [t == j] - eta sum_{s<t} (k_t . k_s) Tm[s][j].  Rows past
-// the end of the sequence have zero keys, so their rows of Tm are unit rows.
-__global__ __launch_bounds__(256) void delta_tmat_kernel(const bf16* __restrict__ k, bf16* __restrict__ tm,
-                                                         int T, int nchunks, long long total, float eta) {
-  __shared__ float ks[16][kB][kD + 1];
-  __shared__ float gram[16][kB][kB + 1];
-  const int grp = threadIdx.x >> 4;   // chunk within the workgroup
-  const int j = threadIdx.x & 15;
-  const long long id = static_cast<long long>(blockIdx.x) * 16 + grp;
-  const bool valid = id < total;
-  const long long chain = valid ? id / nchunks : 0;
-  const int c = valid ? static_cast<int>(id - chain * nchunks) : 0;
-  const bf16* kc = k + (static_cast<size_t>(chain) * T + static_cast<size_t>(c) * kB) * kD;
-  // lane j loads row j of the chunk (zero past the end of the sequence)
-  const bool row_in = valid && c * kB + j < T;
-  for (int x = 0; x < kD; ++x) ks[grp][j][x] = row_in ? static_cast<float>(kc[j * kD + x]) : 0.0f;
-  __syncthreads();
-  for (int t = 0; t < kB; ++t) {
-    float acc = 0.0f;
-    if (t > j)
-      for (int x = 0; x < kD; ++x) acc += ks[grp][t][x] * ks[grp][j][x];
-    gram[grp][t][j] = acc;
+// Tm = (I + eta stril(K K^T))^-1 for every chunk of every chain, stored transposed in bf16:
+// [chain][chunk][j][t] = Tm[t][j] (row j of the stored tile is column j of Tm).  One wave
+// per 4 chunks: the wave forms the Gram matrix G = K K^T of each chunk with two MFMAs (K
+// rows loaded straight into the operand layout; the A and B operands of K K^T are the same
+// registers), stages L = eta stril(G) in LDS, and then lane (q, j) solves column j of chunk
+// q by forward substitution in fp32, Tm[t][j] = [t == j] - sum_{s<t} L[t][s] Tm[s][j]
+// (the 16 lanes of a chunk read the same L row, a broadcast).  Rows past the end of the
+// sequence have zero keys, so their rows of Tm are unit rows.
+constexpr int kTmWaves = 4;
+constexpr int kTmChunksPerWave = 4;
+__global__ __launch_bounds__(64 * kTmWaves) void delta_tmat_kernel(const bf16* __restrict__ k, bf16* __restrict__ tmt,
+                                                                 int T, int nchunks, long long total, float eta) {
+  __shared__ float ls[kTmWaves][kTmChunksPerWave][kB][kB];
+  const int wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const int n = lane & 15;
+  const long long id0 = (static_cast<long long>(blockIdx.x) * kTmWaves + wv) * kTmChunksPerWave;
+  const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int q = 0; q < kTmChunksPerWave; ++q) {
+    const long long id = id0 + q;  // uniform in the wave
+    float4_t gacc = zero;
+    if (id < total) {
+      const long long chain = id / nchunks;
+      const int c = static_cast<int>(id - chain * nchunks);
+      const bf16* kc = k + (static_cast<size_t>(chain) * T + static_cast<size_t>(c) * kB) * kD;
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(kc), 0, (T - c * kB) * kD * 2, 0x00020000);
+      // lane (g, n): K[n][8 g .. 8 g + 7] and K[n][32 + 8 g ..]; rows past T read as zero
+      const u32x4 k0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, n * 128 + 16 * g, 0, 0));
+      const u32x4 k1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, n * 128 + 64 + 16 * g, 0, 0));
+      gacc = MFMA32(bf8(k0), bf8(k0), zero, 0, 0, 0);
+      gacc = MFMA32(bf8(k1), bf8(k1), gacc, 0, 0, 0);
+    }
+    // lane (g, n) holds G[4 g + e][n]; keep the strict lower triangle, scaled by eta
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ls[wv][q][4 * g + e][n] = (n < 4 * g + e) ? eta * gacc[e] : 0.0f;
   }
   __syncthreads();
-  float col[kB];
+  // lane (q, j): column j of chunk q
+  const int q = g;
+  const int j = n;
+  const float* lq = &ls[wv][q][0][0];
+  float x[kB];
 #pragma unroll
   for (int t = 0; t < kB; ++t) {
     float acc = (t == j) ? 1.0f : 0.0f;
 #pragma unroll
-    for (int s2 = 0; s2 < t; ++s2) acc -= eta * gram[grp][t][s2] * col[s2];
-    col[t] = acc;
-  }
-  if (valid) {
-    bf16* out = tm + static_cast<size_t>(id) * kB * kB;
+    for (int s4 = 0; s4 < t; s4 += 4) {
+      const float4_t l4 = *reinterpret_cast<const float4_t*>(lq + t * kB + s4);
 #pragma unroll
-    for (int t = 0; t < kB; ++t) out[t * kB + j] = static_cast<bf16>(col[t]);
+      for (int u = 0; u < 4; ++u)
+        if (s4 + u < t) acc -= l4[u] * x[s4 + u];
+    }
+    x[t] = acc;
+  }
+  const long long id = id0 + q;
+  if (id < total) {
+    u32x4 lo, hi;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      lo[u] = pack_bf16(x[2 * u], x[2 * u + 1]);
+      hi[u] = pack_bf16(x[8 + 2 * u], x[8 + 2 * u + 1]);
+    }
+    u32x4* out = reinterpret_cast<u32x4*>(tmt + static_cast<size_t>(id) * kB * kB + j * kB);
+    out[0] = lo;
+    out[1] = hi;
   }
 }
 
@@ -476,10 +505,11 @@ hipError_t launch_delta_fast(const LinearArgs& a, void* workspace, hipStream_t s
   const long long nchains = static_cast<long long>(a.B) * a.H;
   const int nchunks = (a.T + kB - 1) / kB;
   const long long total = nchains * nchunks;
-  const long long nblocks = (total + 15) / 16;
+  constexpr int kPerBlock = kTmWaves * kTmChunksPerWave;
+  const long long nblocks = (total + kPerBlock - 1) / kPerBlock;
   if (nchains > 0x7fffffffLL || nblocks > 0x7fffffffLL) return hipErrorInvalidValue;
   bf16* tm = static_cast<bf16*>(workspace);
-  hipLaunchKernelGGL(delta_tmat_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(256), 0, s,
+  hipLaunchKernelGGL(delta_tmat_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(64 * kTmWaves), 0, s,
                      static_cast<const bf16*>(a.k), tm, a.T, nchunks, total, a.eta);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
