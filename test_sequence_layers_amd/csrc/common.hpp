@@ -16,8 +16,10 @@ template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }
 
-// SiLU and its derivative, fp32.  sigma(u) = 1 / (1 + exp(-u)).
-__device__ __forceinline__ float sigmoidf_(float u) { return 1.0f / (1.0f + __expf(-u)); }
+// SiLU and its derivative, fp32.  sigma(u) = 1 / (1 + exp(-u)), with the hardware
+// exponential and reciprocal (v_exp_f32, v_rcp_f32: about 1 ulp each) instead of an IEEE
+// division; for large |u| the exponential saturates to 0 or inf and sigma to 1 or 0.
+__device__ __forceinline__ float sigmoidf_(float u) { return __builtin_amdgcn_rcpf(1.0f + __expf(-u)); }
 __device__ __forceinline__ float silu_(float u) { return u * sigmoidf_(u); }
 __device__ __forceinline__ float dsilu_(float u) {
   const float s = sigmoidf_(u);

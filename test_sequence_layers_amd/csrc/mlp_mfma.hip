@@ -68,7 +68,7 @@ __device__ __forceinline__ float4_t mfma(const bf16x8_t& a, const bf16x8_t& b, c
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float sigmoid_f(float u) { return 1.0f / (1.0f + __expf(-u)); }
+__device__ __forceinline__ float sigmoid_f(float u) { return sigmoidf_(u); }
 
 template <typename T>
 __device__ __forceinline__ T lds_load(const lds_char* base, int byte) {
