@@ -15,10 +15,11 @@
 //
 // Mapping.  One workgroup of 4 waves per (batch, head) chain.  Wave w owns hidden units
 // 64w .. 64w+63: its rows of W1 and columns of W2 live in its registers as fp32 MFMA
-// accumulator tiles (W1^T tiles with input rows, W2^T tiles with hidden rows, and a second
-// copy of W2 with output rows, because the forward pass contracts W2 over hidden units and
-// the backward pass over outputs; both copies receive the same rank-16 update).  The only
-// cross-wave sums, O = A W2^T and Z, go through LDS.  Every product is one
+// accumulator tiles (W1^T tiles with input rows, W2^T tiles with hidden rows).  The forward
+// pass contracts W2 over hidden units, which the W2^T tiles serve directly; the backward
+// pass contracts it over outputs, so each chunk the wave also writes its chunk-start W2 in
+// bf16 to LDS (rows: outputs) and reads the operand back with the transposing LDS read.
+// The only cross-wave sums, O = A W2^T and Z, go through LDS.  Every product is one
 // v_mfma_f32_16x16x32_bf16 per 16 x 16 x 32 block; products over the 16 tokens of a chunk
 // use the same instruction with the upper half of one operand zero.
 //
@@ -26,8 +27,11 @@
 // holds rows 4g + e, e = 0..3, of column n):
 //   * input index j of W1^T tiles: tile jb = 2h + p, row m <-> j = 16 (m/4) + 2 (m%4) + 8h + p,
 //     so that an operand over j matches the contiguous 16-byte row loads of K and Q;
-//   * hidden (hh) and output (i) indices are natural: tile a, row m <-> 16 a + m, and a
-//     64-wide contraction pairs tiles (2h, 2h+1), dword e = (row 4g+e of both).
+//   * hidden (hh) and output (i) indices are natural: tile a, row m <-> 16 a + m.  A
+//     contraction over 32 hidden units 32 h' .. 32 h' + 31 places tile 2h' in slots 0..3 and
+//     tile 2h' + 1 in slots 4..7 of each lane (cat_op), so lane group g covers hidden
+//     32 h' + 4 g + 0..3 and 32 h' + 16 + 4 g + 0..3;
+//   * a contraction over the 64 outputs takes them in natural order, 32 h + 8 g + s.
 #include "common.hpp"
 
 namespace ttt {
@@ -60,6 +64,12 @@ __device__ __forceinline__ bf16x8_t pair_op(const float4_t& x, const float4_t& y
   return op4(pack_bf16(s * x[0], s * y[0]), pack_bf16(s * x[1], s * y[1]),
              pack_bf16(s * x[2], s * y[2]), pack_bf16(s * x[3], s * y[3]));
 }
+// operand over a tile pair: slots 0..3 = x[0..3], slots 4..7 = y[0..3]
+__device__ __forceinline__ u32x4 cat_u(const float4_t& x, const float4_t& y) {
+  const u32x4 u = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])};
+  return u;
+}
+__device__ __forceinline__ bf16x8_t cat_op(const float4_t& x, const float4_t& y) { return bf(cat_u(x, y)); }
 // K = 16 operand (4 values, contraction index 4 g + s) padded to the K = 32 layout
 __device__ __forceinline__ bf16x8_t pad_op(const float4_t& x, float s = 1.0f) {
   return op4(pack_bf16(s * x[0], s * x[1]), pack_bf16(s * x[2], s * x[3]), 0u, 0u);
@@ -78,6 +88,19 @@ template <typename T>
 __device__ __forceinline__ void lds_store(lds_char* base, int byte, T v) {
   *reinterpret_cast<__attribute__((address_space(3))) T*>(base + byte) = v;
 }
+// gfx950 transposing LDS read: within 16 lanes, lane i receives element i % 4 of the 8 bytes
+// fetched by lane 4 s + i / 4 (s = 0..3).
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+__device__ __forceinline__ u32x2 lds_load_tr(const lds_char* base, int byte) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + byte)));
+}
+// Per-wave bf16 copy of W2 in LDS: row i (output), 64 hidden units in 16 units of 8 bytes;
+// unit u of row r sits at u ^ w2swz(r), a bijection on r mod 16 that keeps both the 8-byte
+// row writes (16 lanes, 16 rows) and the transposing reads (4 rows x 4 units) on distinct
+// banks.
+__device__ __forceinline__ int w2swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int w2off(int row, int unit) { return row * 128 + ((unit ^ w2swz(row)) * 8); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void* base, int left) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, left > 0 ? left : 0,
@@ -119,14 +142,15 @@ __device__ __forceinline__ void load_chunk(ChunkIn& r, const char* q, const char
 struct State {
   float4_t w1t[4][4];  // [jb][a]: W1^T tile, rows j (permuted, tile jb), cols hidden 16a + n
   float4_t w2t[4][4];  // [a][it]: W2^T tile, rows hidden 16a + m, cols output 16it + n
-  float4_t w2[4][4];   // [it][a]: W2 tile, rows output 16it + m, cols hidden 16a + n
 };
 
-// LDS: per-wave partial sums of O^T and Z^T as [wave][t][i] fp32, and R = O - V as [t][i].
+// LDS: per-wave partial sums of O^T and Z^T as [wave][t][i] fp32, R = O - V as [t][i], and
+// each wave's bf16 chunk-start W2 (swizzled rows of 128 bytes).
 struct Lds {
   float opart[kWaves][kB][kD];
   float zpart[kWaves][kB][kD];
   float r[kB][kD];
+  uint32_t w2b[kWaves][kD][kD / 2];
 };
 
 __device__ __forceinline__ void barrier() { __syncthreads(); }
@@ -137,6 +161,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   lds_char* opart = (lds_char*)(&sh.opart[0][0][0]);
   lds_char* zpart = (lds_char*)(&sh.zpart[0][0][0]);
   lds_char* rbuf = (lds_char*)(&sh.r[0][0]);
+  lds_char* w2lds = (lds_char*)(&sh.w2b[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)][0][0]);
 
   const int chain = blockIdx.x;
   const int tid = threadIdx.x;
@@ -183,11 +208,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       // W2^T tile (aa, it): element e = W2[16 it + n][h0 + 16 aa + 4 g + e]
       st.w2t[aa][it] = *reinterpret_cast<const float4_t*>(
           w2g + static_cast<size_t>(16 * it + n) * kH + h0 + 16 * aa + 4 * g);
-      // W2 tile (it, aa): element e = W2[16 it + 4 g + e][h0 + 16 aa + n]
-      float4_t x;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = w2g[static_cast<size_t>(16 * it + 4 * g + e) * kH + h0 + 16 * aa + n];
-      st.w2[it][aa] = x;
     }
 
   // ---- constants ----
@@ -247,14 +267,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int aa = 0; aa < 4; ++aa) actT[aa] = mfma(pad_op(act[aa]), eye, zero);
 
+    // bf16 chunk-start W2 as A operands over hidden (rows output 16 it + n), written also to
+    // this wave's LDS copy (rows output, 4 consecutive hidden units per 8 bytes)
+    u32x4 w2op[2][4];
+#pragma unroll
+    for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        w2op[hp][it] = cat_u(st.w2t[2 * hp][it], st.w2t[2 * hp + 1][it]);
+        const int row = 16 * it + n;
+        lds_store<u32x2>(w2lds, w2off(row, 4 * (2 * hp) + g), u32x2{w2op[hp][it].x, w2op[hp][it].y});
+        lds_store<u32x2>(w2lds, w2off(row, 4 * (2 * hp + 1) + g), u32x2{w2op[hp][it].z, w2op[hp][it].w});
+      }
     // O^T partial = W2 A^T (rows output, cols t): contraction over this wave's 64 hidden
-    bf16x8_t atb[2];  // B operand over hidden: pairs of A^T tiles
-    atb[0] = pair_op(actT[0], actT[1]);
-    atb[1] = pair_op(actT[2], actT[3]);
+    bf16x8_t atb[2];  // B operand over hidden: tile pairs of A^T
+    atb[0] = cat_op(actT[0], actT[1]);
+    atb[1] = cat_op(actT[2], actT[3]);
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      float4_t ot = mfma(pair_op(st.w2t[0][it], st.w2t[1][it]), atb[0], zero);
-      ot = mfma(pair_op(st.w2t[2][it], st.w2t[3][it]), atb[1], ot);
+      float4_t ot = mfma(bf(w2op[0][it]), atb[0], zero);
+      ot = mfma(bf(w2op[1][it]), atb[1], ot);
       lds_store<float4_t>(opart, ((wv * kB + n) * kD + 16 * it + 4 * g) * 4, ot);
     }
     barrier();
@@ -283,19 +315,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int e = 0; e < 4; ++e) x[e] = lds_load<float>(rbuf, ((4 * g + e) * kD + 16 * it + n) * 4);
       rc[it] = x;
     }
-    bf16x8_t rrow[2];  // A operand of R W2 (m = t, k = output; pairs of output tiles)
+    bf16x8_t rrow[2];  // A operand of R W2 (m = t, k = outputs 32 h + 8 g + 0..7)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const float4_t f0 = lds_load<float4_t>(rbuf, (n * kD + 32 * h + 4 * g) * 4);
-      const float4_t f1 = lds_load<float4_t>(rbuf, (n * kD + 32 * h + 16 + 4 * g) * 4);
-      rrow[h] = pair_op(f0, f1);
+      const float4_t f0 = lds_load<float4_t>(rbuf, (n * kD + 32 * h + 8 * g) * 4);
+      const float4_t f1 = lds_load<float4_t>(rbuf, (n * kD + 32 * h + 8 * g + 4) * 4);
+      rrow[h] = cat_op(f0, f1);
     }
-    // dU = (R W2) * S  (rows t, hidden tile aa); keep -eta dU as a padded operand
+    // dU = (R W2) * S  (rows t, hidden tile aa); keep -eta dU as a padded operand.  The B
+    // operand W2[32 h + 8 g + s][16 aa + n] comes from two transposing reads of the LDS copy:
+    // lane 4 s' + q of group g fetches row 32 h + 8 g + 4 half + s', hidden 16 aa + 4 q .. + 3.
     bf16x8_t dub[4];
 #pragma unroll
     for (int aa = 0; aa < 4; ++aa) {
-      float4_t da = mfma(rrow[0], pair_op(st.w2[0][aa], st.w2[1][aa]), zero);
-      da = mfma(rrow[1], pair_op(st.w2[2][aa], st.w2[3][aa]), da);
+      float4_t da = zero;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const u32x2 lo = lds_load_tr(w2lds, w2off(32 * h + 8 * g + (n >> 2), 4 * aa + (n & 3)));
+        const u32x2 hi2 = lds_load_tr(w2lds, w2off(32 * h + 8 * g + 4 + (n >> 2), 4 * aa + (n & 3)));
+        const u32x4 w2k = {lo.x, lo.y, hi2.x, hi2.y};
+        da = mfma(rrow[h], bf(w2k), da);
+      }
       dub[aa] = pad_op(da * sd[aa], -eta);
     }
     // -eta R and A as padded K = 16 operands (rows t)
@@ -323,7 +363,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int e = 0; e < 4; ++e) u[e] = u[e] * sigmoid_f(u[e]);
       aqT[aa] = u;
     }
-    const bf16x8_t aqb0 = pair_op(aqT[0], aqT[1]), aqb1 = pair_op(aqT[2], aqT[3]);
+    const bf16x8_t aqb0 = cat_op(aqT[0], aqT[1]), aqb1 = cat_op(aqT[2], aqT[3]);
     // G^T = A A_q^T (rows s, cols t) over this wave's hidden units, masked s <= t
     float4_t gt = mfma(atb[0], aqb0, zero);
     gt = mfma(atb[1], aqb1, gt);
@@ -333,8 +373,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // Z^T partial = W2 A_q^T + (-eta R)^T G^T (rows output tile it, cols t)
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      float4_t zt = mfma(pair_op(st.w2t[0][it], st.w2t[1][it]), aqb0, zero);
-      zt = mfma(pair_op(st.w2t[2][it], st.w2t[3][it]), aqb1, zt);
+      float4_t zt = mfma(bf(w2op[0][it]), aqb0, zero);
+      zt = mfma(bf(w2op[1][it]), aqb1, zt);
       zt = mfma(rb[it], gtb, zt);
       lds_store<float4_t>(zpart, ((wv * kB + n) * kD + 16 * it + 4 * g) * 4, zt);
     }
@@ -351,14 +391,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int aa = 0; aa < 4; ++aa) st.w1t[jb][aa] = mfma(kt, dub[aa], st.w1t[jb][aa]);
     }
     // W2^T += A^T (-eta R): A-operand = A tile aa (rows t), B = -eta R tile it
-    // W2   += (-eta R)^T A: A-operand = -eta R tile it (rows t), B = A tile aa
 #pragma unroll
     for (int aa = 0; aa < 4; ++aa)
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        st.w2t[aa][it] = mfma(ab[aa], rb[it], st.w2t[aa][it]);
-        st.w2[it][aa] = mfma(rb[it], ab[aa], st.w2[it][aa]);
-      }
+      for (int it = 0; it < 4; ++it) st.w2t[aa][it] = mfma(ab[aa], rb[it], st.w2t[aa][it]);
     cur = nxt;
   }
   barrier();
