@@ -145,11 +145,15 @@ struct State {
 };
 
 // LDS: per-wave partial sums of O^T and Z^T as [wave][t][i] fp32, R = O - V as [t][i], and
-// each wave's bf16 chunk-start W2 (swizzled rows of 128 bytes).
+// each wave's bf16 chunk-start W2 (swizzled rows of 128 bytes).  The fp32 rows are padded to
+// kRow = 68 floats (272 bytes, 16 mod 128), so the 16-byte accesses of 8 lanes to 8
+// consecutive rows, and 16 lanes of one row against 16 lanes 4 rows further, use distinct
+// banks.
+constexpr int kRow = kD + 4;
 struct Lds {
-  float opart[kWaves][kB][kD];
-  float zpart[kWaves][kB][kD];
-  float r[kB][kD];
+  float opart[kWaves][kB][kRow];
+  float zpart[kWaves][kB][kRow];
+  float r[kB][kRow];
   uint32_t w2b[kWaves][kD][kD / 2];
 };
 
@@ -230,7 +234,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   auto reduce_store_z = [&](int c) {
     float4_t s4 = zero;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) s4 += lds_load<float4_t>(zpart, ((w * kB + rt) * kD + ri) * 4);
+    for (int w = 0; w < kWaves; ++w) s4 += lds_load<float4_t>(zpart, ((w * kB + rt) * kRow + ri) * 4);
     const int off = c * kTileBytes;
     const u32x2 out = {pack_bf16(s4[0], s4[1]), pack_bf16(s4[2], s4[3])};
     __builtin_amdgcn_raw_buffer_store_b64(out, chunk_rsrc(z + off, seq_bytes - off), o.vv, 0, 0);
@@ -287,7 +291,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int it = 0; it < 4; ++it) {
       float4_t ot = mfma(bf(w2op[0][it]), atb[0], zero);
       ot = mfma(bf(w2op[1][it]), atb[1], ot);
-      lds_store<float4_t>(opart, ((wv * kB + n) * kD + 16 * it + 4 * g) * 4, ot);
+      lds_store<float4_t>(opart, ((wv * kB + n) * kRow + 16 * it + 4 * g) * 4, ot);
     }
     barrier();
     // previous chunk's Z (its partials were written before this barrier)
@@ -296,13 +300,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     {
       float4_t s4 = zero;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) s4 += lds_load<float4_t>(opart, ((w * kB + rt) * kD + ri) * 4);
+      for (int w = 0; w < kWaves; ++w) s4 += lds_load<float4_t>(opart, ((w * kB + rt) * kRow + ri) * 4);
       const u32x2 vb = cur.vv;
       s4[0] -= __builtin_bit_cast(float, vb.x << 16);
       s4[1] -= __builtin_bit_cast(float, vb.x & 0xFFFF0000u);
       s4[2] -= __builtin_bit_cast(float, vb.y << 16);
       s4[3] -= __builtin_bit_cast(float, vb.y & 0xFFFF0000u);
-      lds_store<float4_t>(rbuf, (rt * kD + ri) * 4, s4);
+      lds_store<float4_t>(rbuf, (rt * kRow + ri) * 4, s4);
     }
     barrier();
 
@@ -312,14 +316,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int it = 0; it < 4; ++it) {
       float4_t x;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = lds_load<float>(rbuf, ((4 * g + e) * kD + 16 * it + n) * 4);
+      for (int e = 0; e < 4; ++e) x[e] = lds_load<float>(rbuf, ((4 * g + e) * kRow + 16 * it + n) * 4);
       rc[it] = x;
     }
     bf16x8_t rrow[2];  // A operand of R W2 (m = t, k = outputs 32 h + 8 g + 0..7)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const float4_t f0 = lds_load<float4_t>(rbuf, (n * kD + 32 * h + 8 * g) * 4);
-      const float4_t f1 = lds_load<float4_t>(rbuf, (n * kD + 32 * h + 8 * g + 4) * 4);
+      const float4_t f0 = lds_load<float4_t>(rbuf, (n * kRow + 32 * h + 8 * g) * 4);
+      const float4_t f1 = lds_load<float4_t>(rbuf, (n * kRow + 32 * h + 8 * g + 4) * 4);
       rrow[h] = cat_op(f0, f1);
     }
     // dU = (R W2) * S  (rows t, hidden tile aa); keep -eta dU as a padded operand.  The B
@@ -376,7 +380,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       float4_t zt = mfma(bf(w2op[0][it]), aqb0, zero);
       zt = mfma(bf(w2op[1][it]), aqb1, zt);
       zt = mfma(rb[it], gtb, zt);
-      lds_store<float4_t>(zpart, ((wv * kB + n) * kD + 16 * it + 4 * g) * 4, zt);
+      lds_store<float4_t>(zpart, ((wv * kB + n) * kRow + 16 * it + 4 * g) * 4, zt);
     }
 
     // ---- state update (sum of the chunk's gradients) ----
