@@ -7,13 +7,16 @@
 // S = SiLU'(U), R = A W2^T - V and dU = (R W2) * S over all N tokens:
 //   W1' = W1 - eta dU^T K,   W2' = W2 - eta R^T A,   Z = SiLU(Q W1'^T) W2'^T.
 //
-// Mapping.  One wave per (batch, head) chain; no LDS, no barriers.  Pass 1 streams the
-// tokens 16 at a time and accumulates the two gradient sums G1^T = K^T dU and
-// G2^T = A^T R in fp32 MFMA accumulator tiles while W1, W2 stay fixed as bf16 operands
-// (W2 in both orientations: the forward pass contracts it over hidden units, the backward
-// pass over outputs).  Pass 2 forms W1', W2' from the initial weights and the sums and
-// streams the queries.  Tokens past N (the last tile) read as zero and contribute nothing
-// (no bias, SiLU(0) = 0); their outputs are not stored.  Layouts follow the causal MLP
+// Mapping.  One workgroup of kNcWaves = 2 waves per (batch, head) chain; wave w takes the
+// 16-token tiles w, w + 2, w + 4, ...  Pass 1 streams its tiles (the next tile's loads are
+// issued before the current tile is computed) and accumulates the partial gradient sums
+// G1^T = K^T dU and G2^T = A^T R in fp32 MFMA accumulator tiles, while W1, W2 stay fixed
+// as bf16 operands (W2 in both orientations: the forward pass contracts it over hidden
+// units, the backward pass over outputs).  The partial sums meet once in LDS: wave w adds
+// up half of the tiles, forms W' = W - eta G there, and both waves read all of W1', W2'
+// back.  Pass 2 streams the wave's query tiles.  With 768 waves for 384 chains every wave
+// keeps a SIMD to itself.  Tokens past N (the last tile) read as zero and contribute
+// nothing (no bias, SiLU(0) = 0); their outputs are not stored.  Layouts follow the causal MLP
 // kernel: 16 x 16 C-layout tiles, the input index j permuted as j = 16 (m/4) + 2 (m%4) +
 // 8h + p in W1^T tile 2h+p so that operands over j match 16-byte row loads of K and Q, and
 // hidden / output indices natural.
@@ -60,11 +63,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, in
                                            0x00020000);
 }
 
-// W1^T tiles [jb][a] (rows j permuted, cols hidden 16a + n) from W1 [hidden][d] fp32
+// W1^T tiles [jb][a] (rows j permuted, cols hidden 16a + n) from W1 [hidden][d] fp32 with
+// rows kWRow floats apart (the LDS copy)
 __device__ __forceinline__ void load_w1t(float4_t (&w)[4][4], const float* w1, int g, int n) {
 #pragma unroll
   for (int aa = 0; aa < 4; ++aa) {
-    const float* wr = w1 + (16 * aa + n) * kD + 16 * g;
+    const float* wr = w1 + (16 * aa + n) * (kD + 4) + 16 * g;
     const float4_t f0 = *reinterpret_cast<const float4_t*>(wr);
     const float4_t f1 = *reinterpret_cast<const float4_t*>(wr + 4);
     const float4_t f2 = *reinterpret_cast<const float4_t*>(wr + 8);
@@ -75,18 +79,53 @@ __device__ __forceinline__ void load_w1t(float4_t (&w)[4][4], const float* w1, i
     w[3][aa] = float4_t{f2[1], f2[3], f3[1], f3[3]};
   }
 }
-// W2^T tiles [a][it] (rows hidden 16a + m, cols output 16it + n) from W2 [d][hidden]
+// W2^T tiles [a][it] (rows hidden 16a + m, cols output 16it + n) from W2 [d][hidden] with
+// rows kWRow floats apart (the LDS copy)
 __device__ __forceinline__ void load_w2t(float4_t (&w)[4][4], const float* w2, int g, int n) {
 #pragma unroll
   for (int aa = 0; aa < 4; ++aa)
 #pragma unroll
     for (int it = 0; it < 4; ++it)
-      w[aa][it] = *reinterpret_cast<const float4_t*>(w2 + (16 * it + n) * kH + 16 * aa + 4 * g);
+      w[aa][it] = *reinterpret_cast<const float4_t*>(w2 + (16 * it + n) * (kH + 4) + 16 * aa + 4 * g);
 }
 
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void mlp_nc_kernel(MlpArgs a) {
+constexpr int kNcWaves = 2;
+
+// One tile's key-side operands of a lane.
+struct KvTile {
+  u32x4 ka0, ka1;     // K[t = n][16 g + 0..7], K[n][16 g + 8..15]
+  uint32_t kt[4][2];  // kt[e][h] = K[4 g + e][c0 + 8 h .. + 1]
+  u32x2 vv[4];        // V[t = n][16 it + 4 g .. + 3]
+};
+__device__ __forceinline__ void load_kv(KvTile& r, const char* k, const char* v, int tt, int seq_bytes,
+                                        int row, const int (&kto)[4], int g, int n) {
+  const int off = tt * kTileBytes;
+  const __amdgpu_buffer_rsrc_t rk = tile_rsrc(k + off, seq_bytes - off);
+  const __amdgpu_buffer_rsrc_t rv = tile_rsrc(v + off, seq_bytes - off);
+  r.ka0 = __builtin_amdgcn_raw_buffer_load_b128(rk, row, 0, 0);
+  r.ka1 = __builtin_amdgcn_raw_buffer_load_b128(rk, row + 16, 0, 0);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r.kt[e][0] = __builtin_amdgcn_raw_buffer_load_b32(rk, kto[e], 0, 0);
+    r.kt[e][1] = __builtin_amdgcn_raw_buffer_load_b32(rk, kto[e] + 16, 0, 0);
+  }
+#pragma unroll
+  for (int it = 0; it < 4; ++it)
+    r.vv[it] = __builtin_amdgcn_raw_buffer_load_b64(rv, n * 128 + 2 * (16 * it + 4 * g), 0, 0);
+}
+
+// fp32 weight rows staged in LDS, padded to 68 floats so that the 16-byte reads of 16
+// lanes in 16 consecutive rows spread over the banks
+constexpr int kWRow = kD + 4;
+__global__ __launch_bounds__(64 * kNcWaves) __attribute__((amdgpu_waves_per_eu(1, 1))) void mlp_nc_kernel(MlpArgs a) {
+  // partial gradient tiles [wave][tile f][lane], then the trained tiles in [0][f][lane]
+  __shared__ float4_t red[kNcWaves][16][64];
+  // the head's initial W1 [hidden][d] and W2 [d][hidden], read from global memory once per
+  // workgroup
+  __shared__ __attribute__((aligned(16))) float wsh[2][kH][kWRow];
   const int chain = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int n = lane & 15;
   const int bi = chain / a.H;
@@ -116,18 +155,56 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 #pragma unroll
   for (int e = 0; e < 4; ++e) kto[e] = (4 * g + e) * 128 + 2 * c0;
 
+  // K/V tiles are prefetched two tiles ahead (the wave's tiles i and i + 1 are in flight
+  // while it computes tile i - 1)
+  KvTile cur, nx1, nx2;
+  if (wv < ntiles) load_kv(cur, k, v, wv, seq_bytes, row, kto, g, n);
+  if (wv + kNcWaves < ntiles) load_kv(nx1, k, v, wv + kNcWaves, seq_bytes, row, kto, g, n);
+  {
+    // W1 and W2 (64 x 64 fp32 each) into LDS: thread x copies 16-byte pieces x, x + 128, ...
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const float* src = m ? w2g : w1g;
+#pragma unroll
+      for (int x = tid; x < kH * kD / 4; x += 64 * kNcWaves) {
+        const int r = x >> 4, c = (x & 15) * 4;
+        *reinterpret_cast<float4_t*>(&wsh[m][r][c]) = *reinterpret_cast<const float4_t*>(src + r * kD + c);
+      }
+    }
+  }
+  __syncthreads();
+  const float* w1l = &wsh[0][0][0];
+  const float* w2l = &wsh[1][0][0];
+  // this wave's half of the initial W tiles, for W' = W - eta G after pass 1 (tile f = 4 x + y
+  // of the [x][y] tile arrays, f in 8 w .. 8 w + 7)
+  float4_t w1own[2][4], w2own[2][4];
+#pragma unroll
+  for (int aa = 0; aa < 4; ++aa) {
+    const float* wr = w1l + (16 * aa + n) * kWRow + 16 * g + 8 * wv;
+    const float4_t f0 = *reinterpret_cast<const float4_t*>(wr);
+    const float4_t f1 = *reinterpret_cast<const float4_t*>(wr + 4);
+    w1own[0][aa] = float4_t{f0[0], f0[2], f1[0], f1[2]};
+    w1own[1][aa] = float4_t{f0[1], f0[3], f1[1], f1[3]};
+  }
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+      w2own[x][it] = *reinterpret_cast<const float4_t*>(w2l + (16 * it + n) * kWRow + 16 * (2 * wv + x) + 4 * g);
+
   // ---- bf16 operands of the initial weights ----
-  bf16x8_t w1b[2][4];   // [h][a]: operand over j (B of K W1^T, A of W1 Q^T)
+  bf16x8_t w1b[2][4];   // [h][a]: operand over j (B of K W1^T)
   bf16x8_t w2tb[2][4];  // [h][it]: operand over hidden (A of W2 A^T)
   bf16x8_t w2b[2][4];   // [h][a]: operand over outputs (B of R W2)
   {
     float4_t t[4][4];
-    load_w1t(t, w1g, g, n);
+    load_w1t(t, w1l, g, n);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int aa = 0; aa < 4; ++aa) w1b[h][aa] = pair_op(t[2 * h][aa], t[2 * h + 1][aa]);
-    load_w2t(t, w2g, g, n);
+    load_w2t(t, w2l, g, n);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -139,7 +216,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       for (int aa = 0; aa < 4; ++aa) {
         float4_t x;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = w2g[(16 * it + 4 * g + e) * kH + 16 * aa + n];
+        for (int e = 0; e < 4; ++e) x[e] = w2l[(16 * it + 4 * g + e) * kWRow + 16 * aa + n];
         t[it][aa] = x;
       }
 #pragma unroll
@@ -148,7 +225,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       for (int aa = 0; aa < 4; ++aa) w2b[h][aa] = pair_op(t[2 * h][aa], t[2 * h + 1][aa]);
   }
 
-  // ---- pass 1: gradient sums over all tokens ----
+  // ---- pass 1: partial gradient sums over this wave's tiles ----
   float4_t g1t[4][4];  // sum of K^T dU, layout of W1^T
   float4_t g2t[4][4];  // sum of A^T R, layout of W2^T
 #pragma unroll
@@ -158,23 +235,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       g1t[i][j] = zero;
       g2t[i][j] = zero;
     }
-  for (int tt = 0; tt < ntiles; ++tt) {
-    const int off = tt * kTileBytes;
-    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(k + off, seq_bytes - off);
-    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(v + off, seq_bytes - off);
-    const bf16x8_t ka0 = bf(__builtin_amdgcn_raw_buffer_load_b128(rk, row, 0, 0));
-    const bf16x8_t ka1 = bf(__builtin_amdgcn_raw_buffer_load_b128(rk, row + 16, 0, 0));
-    uint32_t kt[4][2];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      kt[e][0] = __builtin_amdgcn_raw_buffer_load_b32(rk, kto[e], 0, 0);
-      kt[e][1] = __builtin_amdgcn_raw_buffer_load_b32(rk, kto[e] + 16, 0, 0);
-    }
-    u32x2 vv[4];  // V[t = n][16 it + 4 g .. + 3]
-#pragma unroll
-    for (int it = 0; it < 4; ++it)
-      vv[it] = __builtin_amdgcn_raw_buffer_load_b64(rv, n * 128 + 2 * (16 * it + 4 * g), 0, 0);
-
+  for (int tt = wv; tt < ntiles; tt += kNcWaves) {
+    if (tt + 2 * kNcWaves < ntiles) load_kv(nx2, k, v, tt + 2 * kNcWaves, seq_bytes, row, kto, g, n);
+    const bf16x8_t ka0 = bf(cur.ka0), ka1 = bf(cur.ka1);
     // U = K W1^T (rows t); A = SiLU(U), S = SiLU'(U)
     float4_t act[4], sd[4];
 #pragma unroll
@@ -199,10 +262,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     for (int it = 0; it < 4; ++it) {
       float4_t o = mfma(w2tb[0][it], atb0, zero);
       o = mfma(w2tb[1][it], atb1, o);
-      o[0] -= bf_lo(vv[it].x);
-      o[1] -= bf_hi(vv[it].x);
-      o[2] -= bf_lo(vv[it].y);
-      o[3] -= bf_hi(vv[it].y);
+      o[0] -= bf_lo(cur.vv[it].x);
+      o[1] -= bf_hi(cur.vv[it].x);
+      o[2] -= bf_lo(cur.vv[it].y);
+      o[3] -= bf_hi(cur.vv[it].y);
       rT[it] = o;
     }
     // dU = (R W2) * S (rows t): A-operand R (m = t, k = output) from pairs of R^T tiles
@@ -223,8 +286,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     for (int jb = 0; jb < 4; ++jb) {
       const int h = jb >> 1;
       const uint32_t sel = (jb & 1) ? kHi : kLo;
-      const bf16x8_t ktb = op4(__builtin_amdgcn_perm(kt[1][h], kt[0][h], sel),
-                               __builtin_amdgcn_perm(kt[3][h], kt[2][h], sel), 0u, 0u);
+      const bf16x8_t ktb = op4(__builtin_amdgcn_perm(cur.kt[1][h], cur.kt[0][h], sel),
+                               __builtin_amdgcn_perm(cur.kt[3][h], cur.kt[2][h], sel), 0u, 0u);
 #pragma unroll
       for (int aa = 0; aa < 4; ++aa) g1t[jb][aa] = mfma(ktb, dub[aa], g1t[jb][aa]);
     }
@@ -234,18 +297,43 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 #pragma unroll
       for (int it = 0; it < 4; ++it) g2t[aa][it] = mfma(ab, rb[it], g2t[aa][it]);
     }
+    cur = nx1;
+    nx1 = nx2;
   }
 
-  // ---- trained weights W' = W - eta G, as bf16 operands ----
+  // queries of this wave's first tile, loaded while the sums are reduced
+  u32x4 qn0 = {0u, 0u, 0u, 0u}, qn1 = {0u, 0u, 0u, 0u};
+  if (wv < ntiles) {
+    const int off = wv * kTileBytes;
+    const __amdgpu_buffer_rsrc_t rq = tile_rsrc(q + off, seq_bytes - off);
+    qn0 = __builtin_amdgcn_raw_buffer_load_b128(rq, row, 0, 0);
+    qn1 = __builtin_amdgcn_raw_buffer_load_b128(rq, row + 16, 0, 0);
+  }
+
+  // ---- W' = W - eta G: the partial sums meet in LDS; wave w reduces tiles 8 w .. 8 w + 7 ----
+  // (tile f = 4 x + y of the [x][y] arrays)
   bf16x8_t w1nb[2][4], w2nb[2][4];
   {
     float4_t t[4][4];
-    load_w1t(t, w1g, g, n);
+    // W1
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int f = 0; f < 16; ++f) red[wv][f][lane] = g1t[f >> 2][f & 3];
+    __syncthreads();
 #pragma unroll
-      for (int j = 0; j < 4; ++j) t[i][j] -= eta * g1t[i][j];
-    if (a.w1_out) {
+    for (int i = 0; i < 8; ++i) {
+      const int f = 8 * wv + i;
+      float4_t sum = red[0][f][lane];
+#pragma unroll
+      for (int w = 1; w < kNcWaves; ++w) sum += red[w][f][lane];
+      w1own[i >> 2][i & 3] -= eta * sum;
+    }
+    __syncthreads();  // every partial read before the reduced tiles overwrite slot 0
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[0][8 * wv + i][lane] = w1own[i >> 2][i & 3];
+    __syncthreads();
+#pragma unroll
+    for (int f = 0; f < 16; ++f) t[f >> 2][f & 3] = red[0][f][lane];
+    if (a.w1_out && wv == 0) {
       float* o1 = a.w1_out + static_cast<size_t>(chain) * hd;
 #pragma unroll
       for (int aa = 0; aa < 4; ++aa) {
@@ -260,12 +348,26 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int aa = 0; aa < 4; ++aa) w1nb[h][aa] = pair_op(t[2 * h][aa], t[2 * h + 1][aa]);
-    load_w2t(t, w2g, g, n);
+    __syncthreads();  // every read of the W1 tiles before slot reuse
+    // W2
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int f = 0; f < 16; ++f) red[wv][f][lane] = g2t[f >> 2][f & 3];
+    __syncthreads();
 #pragma unroll
-      for (int j = 0; j < 4; ++j) t[i][j] -= eta * g2t[i][j];
-    if (a.w2_out) {
+    for (int i = 0; i < 8; ++i) {
+      const int f = 8 * wv + i;
+      float4_t sum = red[0][f][lane];
+#pragma unroll
+      for (int w = 1; w < kNcWaves; ++w) sum += red[w][f][lane];
+      w2own[i >> 2][i & 3] -= eta * sum;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[0][8 * wv + i][lane] = w2own[i >> 2][i & 3];
+    __syncthreads();
+#pragma unroll
+    for (int f = 0; f < 16; ++f) t[f >> 2][f & 3] = red[0][f][lane];
+    if (a.w2_out && wv == 0) {
       float* o2 = a.w2_out + static_cast<size_t>(chain) * hd;
 #pragma unroll
       for (int aa = 0; aa < 4; ++aa)
@@ -279,12 +381,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       for (int it = 0; it < 4; ++it) w2nb[h][it] = pair_op(t[2 * h][it], t[2 * h + 1][it]);
   }
 
-  // ---- pass 2: Z^T = W2' SiLU(W1' Q^T) ----
-  for (int tt = 0; tt < ntiles; ++tt) {
-    const int off = tt * kTileBytes;
-    const __amdgpu_buffer_rsrc_t rq = tile_rsrc(q + off, seq_bytes - off);
-    const bf16x8_t qb0 = bf(__builtin_amdgcn_raw_buffer_load_b128(rq, row, 0, 0));
-    const bf16x8_t qb1 = bf(__builtin_amdgcn_raw_buffer_load_b128(rq, row + 16, 0, 0));
+  // ---- pass 2: Z^T = W2' SiLU(W1' Q^T) over this wave's tiles ----
+  for (int tt = wv; tt < ntiles; tt += kNcWaves) {
+    const bf16x8_t qb0 = bf(qn0), qb1 = bf(qn1);
+    if (tt + kNcWaves < ntiles) {
+      const int offn = (tt + kNcWaves) * kTileBytes;
+      const __amdgpu_buffer_rsrc_t rqn = tile_rsrc(q + offn, seq_bytes - offn);
+      qn0 = __builtin_amdgcn_raw_buffer_load_b128(rqn, row, 0, 0);
+      qn1 = __builtin_amdgcn_raw_buffer_load_b128(rqn, row + 16, 0, 0);
+    }
     float4_t aq[4];
 #pragma unroll
     for (int aa = 0; aa < 4; ++aa) {
@@ -295,6 +400,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       aq[aa] = u;
     }
     const bf16x8_t aqb0 = pair_op(aq[0], aq[1]), aqb1 = pair_op(aq[2], aq[3]);
+    const int off = tt * kTileBytes;
     const __amdgpu_buffer_rsrc_t rz = tile_rsrc(z + off, seq_bytes - off);
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
@@ -322,7 +428,7 @@ bool mlp_nc_supported(const MlpArgs& a, bool bf16_io) {
 hipError_t launch_mlp_nc(const MlpArgs& a, hipStream_t s) {
   const long long nchains = static_cast<long long>(a.B) * a.H;
   if (nchains > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(mlp_nc_kernel, dim3(static_cast<unsigned>(nchains)), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(mlp_nc_kernel, dim3(static_cast<unsigned>(nchains)), dim3(64 * kNcWaves), 0, s, a);
   return hipGetLastError();
 }
 
