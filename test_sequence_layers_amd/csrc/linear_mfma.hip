@@ -354,11 +354,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   // Step c: compute chunk c from registers read in step c - 1 while reading chunk c + 1,
   // and store this wave's 16 columns of Z_c (8 bytes per lane; rows past T are dropped by
   // the buffer range).  Chunks past the end read as zeros and leave the state unchanged.
+  // The Z stores of a block of kRing chunks share one buffer resource, rebased once per
+  // block; the lane offsets of the block's chunks are precomputed, so a step's store needs
+  // no address arithmetic (the range check on the lane offset still drops rows past T).
   const int zoff = n * 128 + 2 * (i0 + 4 * g);
+  int zo[kRing];
+#pragma unroll
+  for (int i = 0; i < kRing; ++i) zo[i] = zoff + i * kTileBytes;
   lds_barrier();  // barrier 0: chunks 0 .. kGroup published
   ChunkRegs ra, rb;
   read_chunk<kDelta>(ra, ring, o);
   for (int gbase = 0; gbase < ngroups; gbase += kRing / kGroup) {
+    const int boff = gbase * kGroup * kTileBytes;
+    const __amdgpu_buffer_rsrc_t zrs = chunk_rsrc(z + boff, seq_bytes - boff);
 #pragma unroll
     for (int gg = 0; gg < kRing / kGroup; ++gg) {
       const int grp = gbase + gg;
@@ -366,15 +374,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
       if (grp > 0) lds_barrier();
 #pragma unroll
       for (int x = 0; x < kGroup; ++x) {
-        const int c = grp * kGroup + x;
         const int nslot = (gg * kGroup + x + 1) % kRing;  // compile-time slot of chunk c + 1
         ChunkRegs& cur = (x & 1) ? rb : ra;
         ChunkRegs& nxt = (x & 1) ? ra : rb;
         __builtin_amdgcn_sched_barrier(0);  // keep steps apart (register pressure)
         read_chunk<kDelta>(nxt, ring + nslot * RG::kSlotBytes, o);
         const u32x2 zz = chunk_step<kDelta>(wacc, cur, lc);
-        const int off = c * kTileBytes;
-        __builtin_amdgcn_raw_buffer_store_b64(zz, chunk_rsrc(z + off, seq_bytes - off), zoff, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(zz, zrs, zo[gg * kGroup + x], 0, 0);
       }
     }
   }
