@@ -82,6 +82,14 @@ def test_linear_bf16_other_modes(chunk, causal):
     _check("linear", w, make_inputs(w))
 
 
+@pytest.mark.parametrize("B,H", [(13, 1), (3, 5)])
+def test_linear_bf16_chain_count_not_multiple_of_8(B, H):
+    # the matrix-core kernel maps chains to block indices in groups of 8 (both workgroups of
+    # a chain on one XCD); 13 and 15 chains leave the last group partly empty
+    w = workload(1).replace(B=B, H=H, T=70, init="normal", seed=60 + B)
+    _check("linear", w, make_inputs(w))
+
+
 def test_linear_config_full_size_sampled():
     w = workload(1)
     sel = [(0, 0), (3, 7), (7, 11)]
@@ -93,6 +101,11 @@ def test_linear_config_full_size_sampled():
 @pytest.mark.parametrize("d,io", [(16, "f32"), (64, "f32"), (64, "bf16"), (32, "bf16")])
 def test_delta_small(d, io):
     w = workload(2).replace(B=2, H=2, T=150, d=d, io=io, init="normal", seed=21 + d)
+    _check("delta", w, make_inputs(w))
+
+
+def test_delta_bf16_chain_count_not_multiple_of_8():
+    w = workload(2).replace(B=5, H=3, T=45, init="normal", seed=70)
     _check("delta", w, make_inputs(w))
 
 
