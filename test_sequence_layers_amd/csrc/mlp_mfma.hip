@@ -13,24 +13,25 @@
 //   Z   = A_q W2^T - eta tril(A_q A^T) R.
 // This equals the per-token recurrence up to floating-point order.
 //
-// Mapping.  One workgroup of 4 waves per (batch, head) chain.  Wave w owns hidden units
-// 64w .. 64w+63: its rows of W1 and columns of W2 live in its registers as fp32 MFMA
-// accumulator tiles (W1^T tiles with input rows, W2^T tiles with hidden rows).  The forward
-// pass contracts W2 over hidden units, which the W2^T tiles serve directly; the backward
-// pass contracts it over outputs, so each chunk the wave also writes its chunk-start W2 in
-// bf16 to LDS (rows: outputs) and reads the operand back with the transposing LDS read.
-// The only cross-wave sums, O = A W2^T and Z, go through LDS.  Every product is one
-// v_mfma_f32_16x16x32_bf16 per 16 x 16 x 32 block; products over the 16 tokens of a chunk
-// use the same instruction with the upper half of one operand zero.
-//
+// Mapping.  One workgroup of 8 waves per (batch, head) chain, two per SIMD so that one
+// wave's dependency stalls are filled by the other's work.  Wave w owns hidden units
+// 32w .. 32w+31: its rows of W1 and columns of W2 live in its registers as fp32 MFMA
+// accumulator tiles (W1^T tiles with input rows, W2^T tiles with hidden rows), 64 values per
+// lane.  The forward pass contracts W2 over hidden units, which the W2^T tiles serve
+// directly; the backward pass contracts it over outputs, so each chunk the wave also
+// writes its chunk-start W2 in bf16 to LDS (rows: outputs) and reads the operand back with
+// the transposing LDS read.  The only cross-wave sums, O = A W2^T and Z, go through LDS.
+// Every product is one v_mfma_f32_16x16x32_bf16 per 16 x 16 x 32 block; products over the
+// 16 tokens of a chunk use the same instruction with the upper half of one operand zero.
+
 // Layout conventions (C layout of a 16 x 16 tile: lane (g, n) = (lane / 16, lane % 16)
 // holds rows 4g + e, e = 0..3, of column n):
 //   * input index j of W1^T tiles: tile jb = 2h + p, row m <-> j = 16 (m/4) + 2 (m%4) + 8h + p,
 //     so that an operand over j matches the contiguous 16-byte row loads of K and Q;
-//   * hidden (hh) and output (i) indices are natural: tile a, row m <-> 16 a + m.  A
-//     contraction over 32 hidden units 32 h' .. 32 h' + 31 places tile 2h' in slots 0..3 and
-//     tile 2h' + 1 in slots 4..7 of each lane (cat_op), so lane group g covers hidden
-//     32 h' + 4 g + 0..3 and 32 h' + 16 + 4 g + 0..3;
+//   * hidden (hh) and output (i) indices are natural: tile a, row m <-> 16 a + m.  The
+//     contraction over a wave's 32 hidden units places tile 0 in slots 0..3 and tile 1 in
+//     slots 4..7 of each lane (cat_op), so lane group g covers hidden 4 g + 0..3 and
+//     16 + 4 g + 0..3 of the wave's slice;
 //   * a contraction over the 64 outputs takes them in natural order, 32 h + 8 g + s.
 #include "common.hpp"
 
@@ -46,7 +47,9 @@ typedef __attribute__((address_space(3))) char lds_char;
 constexpr int kD = 64;        // model dim d
 constexpr int kH = 256;       // hidden width
 constexpr int kB = 16;        // chunk
-constexpr int kWaves = 4;     // hidden slices of 64
+constexpr int kWaves = 8;     // hidden slices of 32
+constexpr int kHT = kH / (16 * kWaves);  // hidden tiles per wave (2)
+static_assert(kHT == 2, "the wave's hidden contraction is one K = 32 block");
 constexpr int kTileBytes = kB * kD * 2;
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
@@ -95,12 +98,17 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 __device__ __forceinline__ u32x2 lds_load_tr(const lds_char* base, int byte) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + byte)));
 }
-// Per-wave bf16 copy of W2 in LDS: row i (output), 64 hidden units in 16 units of 8 bytes;
-// unit u of row r sits at u ^ w2swz(r), a bijection on r mod 16 that keeps both the 8-byte
-// row writes (16 lanes, 16 rows) and the transposing reads (4 rows x 4 units) on distinct
-// banks.
-__device__ __forceinline__ int w2swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-__device__ __forceinline__ int w2off(int row, int unit) { return row * 128 + ((unit ^ w2swz(row)) * 8); }
+// Per-wave bf16 copy of W2 in LDS: row i (output), the wave's 32 hidden units in 8 units of
+// 8 bytes (64-byte rows); unit u of row r sits at u ^ w2swz(r) with w2swz(r) the 3-bit
+// reversal of (r / 2) % 8.  The 8-byte row writes (16 lanes, rows r .. r + 15, one unit)
+// then cover all 16 bank pairs of a 128-byte window, and so do the transposing reads (rows
+// 4k .. 4k + 3, units 4 a .. 4 a + 3): rows 4k and 4k + 2 differ by 4 in the swizzle, which
+// moves the 4-unit block to the other half.
+__device__ __forceinline__ int w2swz(int r) {
+  const int m = (r >> 1) & 7;
+  return ((m & 1) << 2) | (m & 2) | ((m >> 2) & 1);
+}
+__device__ __forceinline__ int w2off(int row, int unit) { return row * 64 + ((unit ^ w2swz(row)) * 8); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void* base, int left) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, left > 0 ? left : 0,
@@ -112,13 +120,13 @@ struct ChunkIn {
   u32x4 ka0, ka1;     // K[t = n][16 g + 0..7], K[n][16 g + 8..15]  (A operands over j)
   u32x4 qb0, qb1;     // Q[n][16 g + 0..15]                          (B operands over j)
   uint32_t kt[4][2];  // kt[e][h] = K[4 g + e][c0 + 8 h .. + 1], c0 = 16 (n / 4) + 2 (n % 4)
-  u32x2 vv;           // V[t = tid / 16][4 (tid % 16) .. + 3]         (for R = O - V)
+  uint32_t vv;        // V[t = tid / 32][2 (tid % 32) .. + 1]         (for R = O - V)
 };
 
 struct Offsets {
   int row;         // n * 128 + 32 g
   int kt[4];       // (4 g + e) * 128 + 2 c0
-  int vv;          // (tid / 16) * 128 + 8 (tid % 16)
+  int vv;          // (tid / 32) * 128 + 4 (tid % 32)
 };
 
 __device__ __forceinline__ void load_chunk(ChunkIn& r, const char* q, const char* k, const char* v,
@@ -136,30 +144,31 @@ __device__ __forceinline__ void load_chunk(ChunkIn& r, const char* q, const char
     r.kt[e][0] = __builtin_amdgcn_raw_buffer_load_b32(rk, o.kt[e], 0, 0);
     r.kt[e][1] = __builtin_amdgcn_raw_buffer_load_b32(rk, o.kt[e] + 16, 0, 0);
   }
-  r.vv = __builtin_amdgcn_raw_buffer_load_b64(rv, o.vv, 0, 0);
+  r.vv = __builtin_amdgcn_raw_buffer_load_b32(rv, o.vv, 0, 0);
 }
 
 struct State {
-  float4_t w1t[4][4];  // [jb][a]: W1^T tile, rows j (permuted, tile jb), cols hidden 16a + n
-  float4_t w2t[4][4];  // [a][it]: W2^T tile, rows hidden 16a + m, cols output 16it + n
+  float4_t w1t[4][kHT];  // [jb][a]: W1^T tile, rows j (permuted, tile jb), cols hidden h0 + 16a + n
+  float4_t w2t[kHT][4];  // [a][it]: W2^T tile, rows hidden h0 + 16a + m, cols output 16it + n
 };
 
 // LDS: per-wave partial sums of O^T and Z^T as [wave][t][i] fp32, R = O - V as [t][i], and
-// each wave's bf16 chunk-start W2 (swizzled rows of 128 bytes).  The fp32 rows are padded to
+// each wave's bf16 chunk-start W2 (swizzled rows of 64 bytes).  The fp32 rows are padded to
 // kRow = 68 floats (272 bytes, 16 mod 128), so the 16-byte accesses of 8 lanes to 8
 // consecutive rows, and 16 lanes of one row against 16 lanes 4 rows further, use distinct
 // banks.
 constexpr int kRow = kD + 4;
+constexpr int kThreads = 64 * kWaves;
 struct Lds {
   float opart[kWaves][kB][kRow];
   float zpart[kWaves][kB][kRow];
   float r[kB][kRow];
-  uint32_t w2b[kWaves][kD][kD / 2];
+  uint32_t w2b[kWaves][kD][8 * kHT];
 };
 
 __device__ __forceinline__ void barrier() { __syncthreads(); }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void mlp_mfma_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void mlp_mfma_kernel(
     MlpArgs a) {
   __shared__ __attribute__((aligned(16))) Lds sh;
   lds_char* opart = (lds_char*)(&sh.opart[0][0][0]);
@@ -188,12 +197,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const size_t hd = static_cast<size_t>(kH) * kD;
   const float* w1g = a.w1 + bi * a.w_batch_stride + static_cast<long long>(hi) * hd;
   const float* w2g = a.w2 + bi * a.w_batch_stride + static_cast<long long>(hi) * hd;
-  const int h0 = 64 * wv;  // first hidden unit of this wave
+  const int h0 = 16 * kHT * wv;  // first hidden unit of this wave
 
   // ---- initial state ----
   State st;
 #pragma unroll
-  for (int aa = 0; aa < 4; ++aa) {
+  for (int aa = 0; aa < kHT; ++aa) {
     // W1^T tile (jb, aa): element e = W1[h0 + 16 aa + n][j], j = 16 g + 8 h + 2 e + p
     const float* wr = w1g + static_cast<size_t>(h0 + 16 * aa + n) * kD + 16 * g;
     const float4_t f0 = *reinterpret_cast<const float4_t*>(wr);
@@ -206,7 +215,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     st.w1t[3][aa] = float4_t{f2[1], f2[3], f3[1], f3[3]};
   }
 #pragma unroll
-  for (int aa = 0; aa < 4; ++aa)
+  for (int aa = 0; aa < kHT; ++aa)
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       // W2^T tile (aa, it): element e = W2[16 it + n][h0 + 16 aa + 4 g + e]
@@ -224,20 +233,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int c0 = 16 * (n >> 2) + 2 * (n & 3);
 #pragma unroll
   for (int e = 0; e < 4; ++e) o.kt[e] = (4 * g + e) * 128 + 2 * c0;
-  const int rt = tid >> 4;          // reduction role: row t and 4 outputs
-  const int ri = 4 * (tid & 15);
+  const int rt = tid >> 5;          // reduction role: row t and 2 outputs
+  const int ri = 2 * (tid & 31);
   o.vv = rt * 128 + 2 * ri;
   const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  typedef float float2_t __attribute__((ext_vector_type(2)));
+  const float2_t zero2 = {0.0f, 0.0f};
   constexpr uint32_t kLo = 0x05040100u, kHi = 0x07060302u;
 
-  // Z of the previous chunk: reduce the 4 partial sums and store (thread: row rt, 4 outputs)
+  // Z of the previous chunk: reduce the per-wave partial sums and store (thread: row rt,
+  // 2 outputs)
   auto reduce_store_z = [&](int c) {
-    float4_t s4 = zero;
+    float2_t s2 = zero2;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) s4 += lds_load<float4_t>(zpart, ((w * kB + rt) * kRow + ri) * 4);
+    for (int w = 0; w < kWaves; ++w) s2 += lds_load<float2_t>(zpart, ((w * kB + rt) * kRow + ri) * 4);
     const int off = c * kTileBytes;
-    const u32x2 out = {pack_bf16(s4[0], s4[1]), pack_bf16(s4[2], s4[3])};
-    __builtin_amdgcn_raw_buffer_store_b64(out, chunk_rsrc(z + off, seq_bytes - off), o.vv, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(pack_bf16(s2[0], s2[1]), chunk_rsrc(z + off, seq_bytes - off),
+                                          o.vv, 0, 0);
   };
 
   ChunkIn cur, nxt;
@@ -247,16 +259,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const bf16x8_t ka0 = bf(cur.ka0), ka1 = bf(cur.ka1), qb0 = bf(cur.qb0), qb1 = bf(cur.qb1);
 
     // bf16 copies of this wave's chunk-start state
-    bf16x8_t w1b[2][4];  // [h][a]: operand over j (pairs of W1^T tiles 2h, 2h+1)
+    bf16x8_t w1b[2][kHT];  // [h][a]: operand over j (pairs of W1^T tiles 2h, 2h+1)
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int aa = 0; aa < 4; ++aa) w1b[h][aa] = pair_op(st.w1t[2 * h][aa], st.w1t[2 * h + 1][aa]);
+      for (int aa = 0; aa < kHT; ++aa) w1b[h][aa] = pair_op(st.w1t[2 * h][aa], st.w1t[2 * h + 1][aa]);
 
     // U = K W1^T (rows t, hidden tile aa);  A = SiLU(U), S = SiLU'(U)
-    float4_t act[4], sd[4];
+    float4_t act[kHT], sd[kHT];
 #pragma unroll
-    for (int aa = 0; aa < 4; ++aa) {
+    for (int aa = 0; aa < kHT; ++aa) {
       float4_t u = mfma(ka0, w1b[0][aa], zero);
       u = mfma(ka1, w1b[1][aa], u);
 #pragma unroll
@@ -267,30 +279,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       }
     }
     // A^T (rows hidden) by an MFMA with I: A-operand = A tile (rows t) as K = 16 operand
-    float4_t actT[4];
+    float4_t actT[kHT];
 #pragma unroll
-    for (int aa = 0; aa < 4; ++aa) actT[aa] = mfma(pad_op(act[aa]), eye, zero);
+    for (int aa = 0; aa < kHT; ++aa) actT[aa] = mfma(pad_op(act[aa]), eye, zero);
 
-    // bf16 chunk-start W2 as A operands over hidden (rows output 16 it + n), written also to
-    // this wave's LDS copy (rows output, 4 consecutive hidden units per 8 bytes)
-    u32x4 w2op[2][4];
-#pragma unroll
-    for (int hp = 0; hp < 2; ++hp)
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        w2op[hp][it] = cat_u(st.w2t[2 * hp][it], st.w2t[2 * hp + 1][it]);
-        const int row = 16 * it + n;
-        lds_store<u32x2>(w2lds, w2off(row, 4 * (2 * hp) + g), u32x2{w2op[hp][it].x, w2op[hp][it].y});
-        lds_store<u32x2>(w2lds, w2off(row, 4 * (2 * hp + 1) + g), u32x2{w2op[hp][it].z, w2op[hp][it].w});
-      }
-    // O^T partial = W2 A^T (rows output, cols t): contraction over this wave's 64 hidden
-    bf16x8_t atb[2];  // B operand over hidden: tile pairs of A^T
-    atb[0] = cat_op(actT[0], actT[1]);
-    atb[1] = cat_op(actT[2], actT[3]);
+    // bf16 chunk-start W2 as A operands over the wave's hidden units (rows output
+    // 16 it + n), written also to this wave's LDS copy (rows output, 4 consecutive hidden
+    // units per 8 bytes)
+    u32x4 w2op[4];
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      float4_t ot = mfma(bf(w2op[0][it]), atb[0], zero);
-      ot = mfma(bf(w2op[1][it]), atb[1], ot);
+      w2op[it] = cat_u(st.w2t[0][it], st.w2t[1][it]);
+      const int row = 16 * it + n;
+      lds_store<u32x2>(w2lds, w2off(row, g), u32x2{w2op[it].x, w2op[it].y});
+      lds_store<u32x2>(w2lds, w2off(row, 4 + g), u32x2{w2op[it].z, w2op[it].w});
+    }
+    // O^T partial = W2 A^T (rows output, cols t): contraction over this wave's 32 hidden
+    const bf16x8_t atb = cat_op(actT[0], actT[1]);  // B operand over hidden
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const float4_t ot = mfma(bf(w2op[it]), atb, zero);
       lds_store<float4_t>(opart, ((wv * kB + n) * kRow + 16 * it + 4 * g) * 4, ot);
     }
     barrier();
@@ -298,15 +306,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if (c > 0) reduce_store_z(c - 1);
     // R = sum of partials - V, fp32 in LDS
     {
-      float4_t s4 = zero;
+      float2_t s2 = zero2;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) s4 += lds_load<float4_t>(opart, ((w * kB + rt) * kRow + ri) * 4);
-      const u32x2 vb = cur.vv;
-      s4[0] -= __builtin_bit_cast(float, vb.x << 16);
-      s4[1] -= __builtin_bit_cast(float, vb.x & 0xFFFF0000u);
-      s4[2] -= __builtin_bit_cast(float, vb.y << 16);
-      s4[3] -= __builtin_bit_cast(float, vb.y & 0xFFFF0000u);
-      lds_store<float4_t>(rbuf, (rt * kRow + ri) * 4, s4);
+      for (int w = 0; w < kWaves; ++w) s2 += lds_load<float2_t>(opart, ((w * kB + rt) * kRow + ri) * 4);
+      const uint32_t vb = cur.vv;
+      s2[0] -= __builtin_bit_cast(float, vb << 16);
+      s2[1] -= __builtin_bit_cast(float, vb & 0xFFFF0000u);
+      lds_store<float2_t>(rbuf, (rt * kRow + ri) * 4, s2);
     }
     barrier();
 
@@ -327,11 +333,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       rrow[h] = cat_op(f0, f1);
     }
     // dU = (R W2) * S  (rows t, hidden tile aa); keep -eta dU as a padded operand.  The B
-    // operand W2[32 h + 8 g + s][16 aa + n] comes from two transposing reads of the LDS copy:
-    // lane 4 s' + q of group g fetches row 32 h + 8 g + 4 half + s', hidden 16 aa + 4 q .. + 3.
-    bf16x8_t dub[4];
+    // operand W2[32 h + 8 g + s][h0 + 16 aa + n] comes from two transposing reads of the LDS
+    // copy: lane 4 s' + q of group g fetches row 32 h + 8 g + 4 half + s', hidden
+    // 16 aa + 4 q .. + 3 of the wave's slice.
+    bf16x8_t dub[kHT];
 #pragma unroll
-    for (int aa = 0; aa < 4; ++aa) {
+    for (int aa = 0; aa < kHT; ++aa) {
       float4_t da = zero;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -343,11 +350,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       dub[aa] = pad_op(da * sd[aa], -eta);
     }
     // -eta R and A as padded K = 16 operands (rows t)
-    bf16x8_t rb[4], ab[4];
+    bf16x8_t rb[4], ab[kHT];
 #pragma unroll
     for (int it = 0; it < 4; ++it) rb[it] = pad_op(rc[it], -eta);
 #pragma unroll
-    for (int aa = 0; aa < 4; ++aa) ab[aa] = pad_op(act[aa]);
+    for (int aa = 0; aa < kHT; ++aa) ab[aa] = pad_op(act[aa]);
 
     // ---- outputs (use the chunk-start state) ----
     // P^T = K Q^T with the causal mask s <= t, padded B operand
@@ -357,9 +364,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int e = 0; e < 4; ++e) pt[e] = keep[e] ? pt[e] : 0.0f;
     const bf16x8_t ptb = pad_op(pt);
     // U_q^T = W1 Q^T - eta dU^T P^T (rows hidden tile aa, cols t);  A_q^T = SiLU(U_q^T)
-    float4_t aqT[4];
+    float4_t aqT[kHT];
 #pragma unroll
-    for (int aa = 0; aa < 4; ++aa) {
+    for (int aa = 0; aa < kHT; ++aa) {
       float4_t u = mfma(w1b[0][aa], qb0, zero);
       u = mfma(w1b[1][aa], qb1, u);
       u = mfma(dub[aa], ptb, u);
@@ -367,18 +374,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int e = 0; e < 4; ++e) u[e] = u[e] * sigmoid_f(u[e]);
       aqT[aa] = u;
     }
-    const bf16x8_t aqb0 = cat_op(aqT[0], aqT[1]), aqb1 = cat_op(aqT[2], aqT[3]);
+    const bf16x8_t aqb = cat_op(aqT[0], aqT[1]);
     // G^T = A A_q^T (rows s, cols t) over this wave's hidden units, masked s <= t
-    float4_t gt = mfma(atb[0], aqb0, zero);
-    gt = mfma(atb[1], aqb1, gt);
+    float4_t gt = mfma(atb, aqb, zero);
 #pragma unroll
     for (int e = 0; e < 4; ++e) gt[e] = keep[e] ? gt[e] : 0.0f;
     const bf16x8_t gtb = pad_op(gt);
     // Z^T partial = W2 A_q^T + (-eta R)^T G^T (rows output tile it, cols t)
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      float4_t zt = mfma(bf(w2op[0][it]), aqb0, zero);
-      zt = mfma(bf(w2op[1][it]), aqb1, zt);
+      float4_t zt = mfma(bf(w2op[it]), aqb, zero);
       zt = mfma(rb[it], gtb, zt);
       lds_store<float4_t>(zpart, ((wv * kB + n) * kRow + 16 * it + 4 * g) * 4, zt);
     }
@@ -392,11 +397,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const bf16x8_t kt = op4(__builtin_amdgcn_perm(cur.kt[1][h], cur.kt[0][h], sel),
                               __builtin_amdgcn_perm(cur.kt[3][h], cur.kt[2][h], sel), 0u, 0u);
 #pragma unroll
-      for (int aa = 0; aa < 4; ++aa) st.w1t[jb][aa] = mfma(kt, dub[aa], st.w1t[jb][aa]);
+      for (int aa = 0; aa < kHT; ++aa) st.w1t[jb][aa] = mfma(kt, dub[aa], st.w1t[jb][aa]);
     }
     // W2^T += A^T (-eta R): A-operand = A tile aa (rows t), B = -eta R tile it
 #pragma unroll
-    for (int aa = 0; aa < 4; ++aa)
+    for (int aa = 0; aa < kHT; ++aa)
 #pragma unroll
       for (int it = 0; it < 4; ++it) st.w2t[aa][it] = mfma(ab[aa], rb[it], st.w2t[aa][it]);
     cur = nxt;
@@ -408,10 +413,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   if (a.w1_out) {
     float* o1 = a.w1_out + static_cast<size_t>(chain) * hd;
 #pragma unroll
-    for (int aa = 0; aa < 4; ++aa) {
+    for (int aa = 0; aa < kHT; ++aa) {
       float* wr = o1 + static_cast<size_t>(h0 + 16 * aa + n) * kD + 16 * g;
-      const float4_t* t = &st.w1t[0][aa];
-      (void)t;
       *reinterpret_cast<float4_t*>(wr) =
           float4_t{st.w1t[0][aa][0], st.w1t[1][aa][0], st.w1t[0][aa][1], st.w1t[1][aa][1]};
       *reinterpret_cast<float4_t*>(wr + 4) =
@@ -425,7 +428,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   if (a.w2_out) {
     float* o2 = a.w2_out + static_cast<size_t>(chain) * hd;
 #pragma unroll
-    for (int aa = 0; aa < 4; ++aa)
+    for (int aa = 0; aa < kHT; ++aa)
 #pragma unroll
       for (int it = 0; it < 4; ++it)
         *reinterpret_cast<float4_t*>(o2 + static_cast<size_t>(16 * it + n) * kH + h0 + 16 * aa + 4 * g) =
@@ -449,7 +452,7 @@ bool mlp_fast_supported(const MlpArgs& a, bool bf16_io) {
 hipError_t launch_mlp_fast(const MlpArgs& a, hipStream_t s) {
   const long long nchains = static_cast<long long>(a.B) * a.H;
   if (nchains > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(mlp_mfma_kernel, dim3(static_cast<unsigned>(nchains)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(mlp_mfma_kernel, dim3(static_cast<unsigned>(nchains)), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
