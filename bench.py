@@ -203,17 +203,32 @@ def main():
 
     w = workload(args.workload)
     res = time_workload(w, args.steps, args.warmup, torch, ttt, rotate=args.rotate)
-    peak = HBM_PEAK_GBS
-    roofline = {
-        "bound": "hbm",
-        "achieved": round(res["hbm_gbs"], 1),
-        "peak": peak,
-        "unit": "GB/s",
-        "frac": round(res["hbm_gbs"] / peak, 4),
-        "traffic": measured_traffic(w.name),
-        "kernel": "linear_mfma_kernel (per launch: Q,K,V read + Z written + W0 read)",
-        "bytes_per_launch": res["bytes"],
-    }
+    if w.kind == "mlp":
+        # dense bf16 contractions: priced against the matrix-core peak
+        kern = "mlp_mfma_kernel" if w.causal else "mlp_nc_mfma_kernel"
+        roofline = {
+            "bound": "mfma",
+            "achieved": round(res["tflops"], 2),
+            "peak": BF16_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(res["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4),
+            "traffic": measured_traffic(w.name),
+            "kernel": f"{kern} (per launch: the method's flops, tril products at half)",
+            "flops_per_launch": res["flops"],
+        }
+    else:
+        kern = ("linear_mfma_kernel" if w.kind == "linear"
+                else "delta_tmat_kernel + linear_mfma_kernel (whole call)")
+        roofline = {
+            "bound": "hbm",
+            "achieved": round(res["hbm_gbs"], 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(res["hbm_gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(w.name),
+            "kernel": f"{kern} (per launch: Q,K,V read + Z written + W0 read)",
+            "bytes_per_launch": res["bytes"],
+        }
     line = {
         "metric": "TTT-layer fwd tokens/sec at d=64,T=2048 + MFMA util % (1 MI355X)",
         "value": round(res["tokens_per_s"], 1),

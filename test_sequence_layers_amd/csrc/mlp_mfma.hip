@@ -152,17 +152,23 @@ struct State {
   float4_t w2t[kHT][4];  // [a][it]: W2^T tile, rows hidden h0 + 16a + m, cols output 16it + n
 };
 
-// LDS: per-wave partial sums of O^T and Z^T as [wave][t][i] fp32, R = O - V as [t][i], and
-// each wave's bf16 chunk-start W2 (swizzled rows of 64 bytes).  The fp32 rows are padded to
-// kRow = 68 floats (272 bytes, 16 mod 128), so the 16-byte accesses of 8 lanes to 8
-// consecutive rows, and 16 lanes of one row against 16 lanes 4 rows further, use distinct
-// banks.
+// LDS: per-wave partial sums of O^T and Z^T as [wave][t][i] fp32; -eta R = -eta (O - V) in
+// bf16 twice, as [t][i] (rows of 144 bytes) for the row operands over outputs and as [i][t]
+// (rows of 40 bytes) for the operands in the C layout; each wave's bf16 chunk-start W2
+// (swizzled rows of 64 bytes).  The fp32 rows are padded to kRow = 68 floats (272 bytes,
+// 16 mod 128), so the 16-byte accesses of 8 lanes to 8 consecutive rows, and 16 lanes of one
+// row against 16 lanes 4 rows further, use distinct banks; the two bf16 row strides keep the
+// 16-byte reads of 16 consecutive rows (36 dwords apart) and the 8-byte reads of 16
+// consecutive rows (10 dwords apart) on distinct banks.
 constexpr int kRow = kD + 4;
+constexpr int kRRow = 72;  // bf16 per row of -eta R [t][i]
+constexpr int kTRow = 20;  // bf16 per row of -eta R^T [i][t]
 constexpr int kThreads = 64 * kWaves;
 struct Lds {
   float opart[kWaves][kB][kRow];
   float zpart[kWaves][kB][kRow];
-  float r[kB][kRow];
+  uint16_t rr[kB][kRRow];
+  uint16_t rt[kD][kTRow];
   uint32_t w2b[kWaves][kD][8 * kHT];
 };
 
@@ -173,7 +179,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   __shared__ __attribute__((aligned(16))) Lds sh;
   lds_char* opart = (lds_char*)(&sh.opart[0][0][0]);
   lds_char* zpart = (lds_char*)(&sh.zpart[0][0][0]);
-  lds_char* rbuf = (lds_char*)(&sh.r[0][0]);
+  lds_char* rrb = (lds_char*)(&sh.rr[0][0]);
+  lds_char* rtb = (lds_char*)(&sh.rt[0][0]);
   lds_char* w2lds = (lds_char*)(&sh.w2b[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)][0][0]);
 
   const int chain = blockIdx.x;
@@ -252,9 +259,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                                           o.vv, 0, 0);
   };
 
-  ChunkIn cur, nxt;
-  load_chunk(cur, q, k, v, 0, seq_bytes, o);
-  for (int c = 0; c < nchunks; ++c) {
+  // One chunk: its operands in cur, the next chunk's loaded into nxt.
+  auto step = [&](const ChunkIn& cur, ChunkIn& nxt, int c) {
     load_chunk(nxt, q, k, v, c + 1, seq_bytes, o);  // prefetch (zeros past the end)
     const bf16x8_t ka0 = bf(cur.ka0), ka1 = bf(cur.ka1), qb0 = bf(cur.qb0), qb1 = bf(cur.qb1);
 
@@ -275,13 +281,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       for (int e = 0; e < 4; ++e) {
         const float sg = sigmoid_f(u[e]);
         act[aa][e] = u[e] * sg;
-        sd[aa][e] = sg * (1.0f + u[e] * (1.0f - sg));
+        sd[aa][e] = __builtin_fmaf(act[aa][e], 1.0f - sg, sg);  // sg (1 + u (1 - sg))
       }
     }
-    // A^T (rows hidden) by an MFMA with I: A-operand = A tile (rows t) as K = 16 operand
+    // A as padded K = 16 operands (rows t); A^T (rows hidden) by an MFMA with I
+    bf16x8_t ab[kHT];
     float4_t actT[kHT];
 #pragma unroll
-    for (int aa = 0; aa < kHT; ++aa) actT[aa] = mfma(pad_op(act[aa]), eye, zero);
+    for (int aa = 0; aa < kHT; ++aa) {
+      ab[aa] = pad_op(act[aa]);
+      actT[aa] = mfma(ab[aa], eye, zero);
+    }
 
     // bf16 chunk-start W2 as A operands over the wave's hidden units (rows output
     // 16 it + n), written also to this wave's LDS copy (rows output, 4 consecutive hidden
@@ -304,35 +314,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     barrier();
     // previous chunk's Z (its partials were written before this barrier)
     if (c > 0) reduce_store_z(c - 1);
-    // R = sum of partials - V, fp32 in LDS
+    // -eta R = -eta (sum of partials - V), to LDS in bf16 as [t][i] and [i][t]
     {
       float2_t s2 = zero2;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) s2 += lds_load<float2_t>(opart, ((w * kB + rt) * kRow + ri) * 4);
       const uint32_t vb = cur.vv;
-      s2[0] -= __builtin_bit_cast(float, vb << 16);
-      s2[1] -= __builtin_bit_cast(float, vb & 0xFFFF0000u);
-      lds_store<float2_t>(rbuf, (rt * kRow + ri) * 4, s2);
+      const uint32_t rp = pack_bf16((s2[0] - __builtin_bit_cast(float, vb << 16)) * (-eta),
+                                    (s2[1] - __builtin_bit_cast(float, vb & 0xFFFF0000u)) * (-eta));
+      lds_store<uint32_t>(rrb, (rt * kRRow + ri) * 2, rp);
+      lds_store<uint16_t>(rtb, (ri * kTRow + rt) * 2, static_cast<uint16_t>(rp));
+      lds_store<uint16_t>(rtb, ((ri + 1) * kTRow + rt) * 2, static_cast<uint16_t>(rp >> 16));
     }
     barrier();
 
-    // R in the C layout (rows t) per output tile, and as row operands over outputs
-    float4_t rc[4];
+    // -eta R tiles as padded K = 16 operands in the C layout (rows t = 4 g + 0..3 of column
+    // 16 it + n), and as row operands over outputs (m = t, k = outputs 32 h + 8 g + 0..7)
+    bf16x8_t rb[4];
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      float4_t x;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = lds_load<float>(rbuf, ((4 * g + e) * kRow + 16 * it + n) * 4);
-      rc[it] = x;
+      const u32x2 x = lds_load<u32x2>(rtb, ((16 * it + n) * kTRow + 4 * g) * 2);
+      rb[it] = op4(x.x, x.y, 0u, 0u);
     }
-    bf16x8_t rrow[2];  // A operand of R W2 (m = t, k = outputs 32 h + 8 g + 0..7)
+    bf16x8_t rrow[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const float4_t f0 = lds_load<float4_t>(rbuf, (n * kRow + 32 * h + 8 * g) * 4);
-      const float4_t f1 = lds_load<float4_t>(rbuf, (n * kRow + 32 * h + 8 * g + 4) * 4);
-      rrow[h] = cat_op(f0, f1);
-    }
-    // dU = (R W2) * S  (rows t, hidden tile aa); keep -eta dU as a padded operand.  The B
+    for (int h = 0; h < 2; ++h) rrow[h] = bf(lds_load<u32x4>(rrb, (n * kRRow + 32 * h + 8 * g) * 2));
+    // -eta dU = (-eta R W2) * S  (rows t, hidden tile aa), as a padded operand.  The B
     // operand W2[32 h + 8 g + s][h0 + 16 aa + n] comes from two transposing reads of the LDS
     // copy: lane 4 s' + q of group g fetches row 32 h + 8 g + 4 half + s', hidden
     // 16 aa + 4 q .. + 3 of the wave's slice.
@@ -347,14 +354,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const u32x4 w2k = {lo.x, lo.y, hi2.x, hi2.y};
         da = mfma(rrow[h], bf(w2k), da);
       }
-      dub[aa] = pad_op(da * sd[aa], -eta);
+      dub[aa] = pad_op(da * sd[aa]);
     }
-    // -eta R and A as padded K = 16 operands (rows t)
-    bf16x8_t rb[4], ab[kHT];
-#pragma unroll
-    for (int it = 0; it < 4; ++it) rb[it] = pad_op(rc[it], -eta);
-#pragma unroll
-    for (int aa = 0; aa < kHT; ++aa) ab[aa] = pad_op(act[aa]);
 
     // ---- outputs (use the chunk-start state) ----
     // P^T = K Q^T with the causal mask s <= t, padded B operand
@@ -404,7 +405,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int aa = 0; aa < kHT; ++aa)
 #pragma unroll
       for (int it = 0; it < 4; ++it) st.w2t[aa][it] = mfma(ab[aa], rb[it], st.w2t[aa][it]);
-    cur = nxt;
+  };
+
+  ChunkIn ca, cb;
+  load_chunk(ca, q, k, v, 0, seq_bytes, o);
+  for (int c = 0; c < nchunks; ++c) {
+    step(ca, cb, c);
+    ca = cb;
   }
   barrier();
   if (nchunks > 0) reduce_store_z(nchunks - 1);
