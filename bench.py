@@ -253,7 +253,7 @@ def main():
         for o in WORKLOADS:
             if o.name == w.name:
                 continue
-            r = time_workload(o, max(3, args.steps // 5), 2, torch, ttt)
+            r = time_workload(o, max(10, args.steps // 2), 5, torch, ttt)
             others[o.name] = {
                 "tokens_per_s": round(r["tokens_per_s"], 1),
                 "ms_per_step": round(r["ms_per_step"], 5),

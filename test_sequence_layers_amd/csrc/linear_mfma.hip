@@ -19,16 +19,27 @@
 //
 // Mapping.  The linear model is separable by output row (row i of W only needs v[i]), so a
 // (batch, head) chain is split over kSplit = 2 workgroups of 32 output rows each; within a
-// workgroup, wave w owns 16 rows and never exchanges state with the other wave.  The two
-// workgroups of a chain get block indices that are equal mod 8, which places them on the
-// same XCD, so their reads of the chain's Q and K meet in one L2.  Per chunk, each wave
-// issues about 60 instructions; with one wave per SIMD that issue rate, not memory, bounds
-// the kernel, and the split lets 192 CUs work instead of 96.
-// A third wave streams chunks into an LDS ring with direct-to-LDS buffer loads (no
-// registers are spent on data in flight); one barrier per group of 4 chunks publishes
-// chunks and recycles slots.  The compute waves read the next chunk's operands while they
-// compute the current one and store their 16 columns of Z directly.  The loop is unrolled
-// over the whole ring, so every LDS address is a per-lane base plus an immediate.
+// workgroup, chain wave w owns 16 rows and never exchanges state with the other chain wave.
+// The two workgroups of a chain get block indices that are equal mod 8, which places them
+// on the same XCD, so their reads of the chain's Q and K meet in one L2.
+// Work per workgroup, each on its own SIMD:
+//   * two chain waves run the state recursion only, two chunks per step (below), and hand
+//     each pair's bf16 start state and -eta R to an output wave through LDS;
+//   * two output waves form each chunk's Z one group of chunks later and store it;
+//   * a loader wave streams chunks into an LDS ring with direct-to-LDS buffer loads (no
+//     registers are spent on data in flight).  What bounds the kernel is this stream: a
+//     compute unit takes in at most about 38 GB/s (one 128-byte line per ~7 cycles, with
+//     the non-temporal policy), and a chunk costs a workgroup 48 lines (Q, K and V; the V
+//     half-rows cost whole lines).
+// One barrier per group of 4 chunks publishes chunks and handoffs and recycles ring slots and
+// handoff buffers.  The chain waves read a pair's operands one step ahead.  Loops are
+// unrolled over the whole ring, so every LDS address is a per-lane base plus an immediate.
+//
+// Two chunks per step.  From W = W_c, R_c = K_c W^T - V_c and, since W_{c+1} = W - eta R_c^T
+// K_c, R_{c+1} = (K_{c+1} W^T - V_{c+1}) + (K_{c+1} K_c^T)(-eta R_c) (delta rule: Tm times
+// each bracket); then one update W <- W - eta [R_c; R_{c+1}]^T [K_c; K_{c+1}] over 32
+// tokens.  So the state, its bf16 copy and the update are touched once per pair, and Z of
+// the second chunk is Q W_c^T + (Q K_c^T)(-eta R_c) + tril(Q K^T)(-eta R_{c+1}).
 // Within a wave everything stays in registers, in the layouts the MFMA operands need:
 //   * the fp32 state W^T (64 x 16) is 4 accumulator tiles; tile t = 2 kb + hf, row m holds
 //     input index j = 32 kb + 8 (m / 4) + 4 hf + m % 4, so lane (g, n) holds the four
@@ -36,20 +47,22 @@
 //   * its bf16 copy (tiles 2 kb and 2 kb + 1 side by side) is, lane for lane, the B operand
 //     of R = K W^T and the A operand of Z^T = W Q^T for input block kb, with K and Q read
 //     as 16-byte row pieces;
-//   * R comes out with tokens as rows, which is the B operand of the rank-16 update
-//     W^T += K^T (-eta R) (16x16x16 MFMA) and the A operand of the in-chunk correction
-//     (-eta R^T) P^T;
-//   * the K^T operand of the update is read with the gfx950 transposing LDS read
+//   * R comes out with tokens as rows: as bf16 pairs it is the B operand (over tokens) of
+//     the state update and of M (-eta R_c), and the A operand of the output corrections
+//     (-eta R^T) P^T (the handoff stores the bf16 operands lane by lane, so the output wave
+//     gets them in the same layouts);
+//   * the K^T operands of the update are read with the gfx950 transposing LDS read
 //     (ds_read_b64_tr_b16): within 16 lanes, lane i receives element i % 4 of the 8 bytes
 //     fetched by lane 4 s + i / 4, so lanes that fetch 4 consecutive inputs of token rows
-//     4 g .. 4 g + 3 hand each lane the 4 tokens of one input column;
-//   * P^T = K Q^T comes out as the B operand of that correction;
+//     4 g .. 4 g + 3 hand each lane the 4 tokens of one input column; the pair's two
+//     chunks fill slots 0..3 and 4..7 of one K = 32 operand;
+//   * M^T = K_c K_{c+1}^T, P^T = K Q^T and (K_c Q^T) come out in the layout of the A or B
+//     operands that use them;
 //   * -V enters R's accumulator through an MFMA with -I, which turns a row read of V into
 //     the accumulator layout;
 //   * every accumulator is written by one MFMA opcode only (chaining a 16x16x16 result into
 //     a 16x16x32 accumulator input was observed to read stale values on gfx950); products
-//     over the 16 tokens that share an accumulator with 16x16x32 products use 16x16x32
-//     with the upper half of one operand zero.
+//     over the 16 tokens of a chunk use 16x16x32 with the upper half of one operand zero.
 #include "common.hpp"
 
 namespace ttt {
@@ -68,33 +81,54 @@ constexpr int kD = 64;
 constexpr int kB = 16;                 // tokens per chunk
 constexpr int kTileBytes = kB * kD * 2;  // one 16 x 64 bf16 chunk of one tensor
 constexpr int kTmBytes = kB * kB * 2;  // one 16 x 16 bf16 Tm matrix of the delta rule
-constexpr int kComputeWaves = 2;
-constexpr int kSplit = 4 / kComputeWaves;  // workgroups per chain
-constexpr int kThreads = 64 * (kComputeWaves + 1);
+constexpr int kChainWaves = 2;
+constexpr int kOutWaves = kChainWaves;
+constexpr int kLoaderWave = kChainWaves + kOutWaves;
+constexpr int kSplit = 4 / kChainWaves;  // workgroups per chain
+constexpr int kThreads = 64 * (kLoaderWave + 1);
 constexpr int kHalfCols = kD / kSplit;  // output rows (= V columns) per workgroup
 
 // LDS ring of kRing slots, published kGroup chunks per barrier.  Slot layout: Q tile at 0
 // and K tile at 2 KB (16 rows of 128 bytes, 16-byte pieces swizzled by row), this
 // workgroup's 32 V columns at 4 KB (16 rows of 64 bytes, swizzled), and for the delta
-// rule the chunk's Tm (512 bytes, row-major, then 512 bytes of zeros) at 5 KB.  The
+// rule the chunk's Tm^T (512 bytes, row-major) at 5 KB.  The
 // loader issues kLoads direct-to-LDS loads per chunk; its waits before barriers are
 // bounded by the 6-bit vmcnt (a smaller count than needed only waits longer).
+// Barrier b publishes the chunks that the chain waves read after it (up to kGroup b +
+// kGroup + 1) and frees the slots of the chunks that the output waves finished before it (up
+// to kGroup b - kGroup - 1); the loader then refills up to kRing chunks past that.
 constexpr int kGroup = 4;
-constexpr int kRing = 16;
 constexpr int kVOff = 2 * kTileBytes;
 constexpr int kTmOff = kVOff + kB * kHalfCols * 2;
 // (Plain constants: a dependent static member passed to the direct-to-LDS load builtin
 // kept the host compiler from emitting the kernel's launch stub.)
 template <bool kDelta> struct Ring {
+  static constexpr int kRing = 24;
   static constexpr int kLoads = kDelta ? 6 : 5;
-  static constexpr int kSlotBytes = kTmOff + (kDelta ? 2 * kTmBytes : 0);
+  static constexpr int kSlotBytes = kTmOff + (kDelta ? kTmBytes : 0);
   static constexpr int clampw(int nchunks) {
     return nchunks * kLoads < 64 ? nchunks * kLoads : (63 / kLoads) * kLoads;
   }
-  static constexpr int kWait0 = clampw(kRing - 1 - kGroup);
-  static constexpr int kWait1 = clampw(kRing - 1 - 2 * kGroup);
-  static constexpr int kWaitN = clampw(kRing - 2 * kGroup);
+  static constexpr int kWait0 = clampw(kRing - 2 - kGroup);
+  static constexpr int kWait1 = clampw(kRing - 2 - 2 * kGroup);
+  static constexpr int kWaitN = clampw(kRing - 2 - 3 * kGroup);
+  static_assert(kRing % kGroup == 0 && kRing - 2 - 3 * kGroup >= 0, "ring too small");
 };
+constexpr int kRingMax = 24;
+// Cache policy of the streaming loads: non-temporal (each byte is read once per workgroup).
+constexpr int kNT = 2;
+
+// Handoff from a chain wave to its output wave, per pair of chunks: the bf16 W^T operands
+// of the pair's start state (two 16-byte pieces per lane) and -eta R of both chunks (8 bytes
+// per lane each), lane-major.  Two buffers of one group each, by group parity: the chain
+// waves fill one while the output waves read the other.
+constexpr int kHandW1 = 64 * 16;
+constexpr int kHandR0 = 2 * 64 * 16;
+constexpr int kHandR1 = kHandR0 + 64 * 8;
+constexpr int kHandPair = kHandR1 + 64 * 8;
+constexpr int kHandWave = (kGroup / 2) * kHandPair;
+constexpr int kHandGroup = kChainWaves * kHandWave;
+constexpr int kHandBytes = 2 * kHandGroup;
 
 // Swizzle of the 128-byte Q/K rows: logical 16-byte piece p of row r sits at piece
 // p ^ sig(r).  sig is a bijection on r mod 8, so the 8 lanes of a 16-byte row read (rows
@@ -107,7 +141,6 @@ __device__ __forceinline__ int swz(int r, int p) { return r * 8 + (p ^ sig(r)); 
 __device__ __forceinline__ int vswz(int r, int p) { return r * 4 + (p ^ ((r >> 1) & 3)); }
 
 __device__ __forceinline__ bf16x8_t bf8(const u32x4& x) { return __builtin_bit_cast(bf16x8_t, x); }
-__device__ __forceinline__ bf16x4_t bf4(const u32x2& x) { return __builtin_bit_cast(bf16x4_t, x); }
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
@@ -117,16 +150,21 @@ template <typename T>
 __device__ __forceinline__ T lds_load(const lds_char* p) {
   return *reinterpret_cast<const __attribute__((address_space(3))) T*>(p);
 }
+template <typename T>
+__device__ __forceinline__ void lds_store(lds_char* p, T v) {
+  *reinterpret_cast<__attribute__((address_space(3))) T*>(p) = v;
+}
 __device__ __forceinline__ u32x2 lds_load_tr(const lds_char* p) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
 }
 
-struct ChunkRegs {
-  u32x4 ka0, ka1;          // K[t = n][8 g + 0..7], K[n][32 + 8 g + 0..7]
-  u32x4 qb0, qb1;          // Q[n][8 g + 0..7], Q[n][32 + 8 g + 0..7]
-  u32x2 kt0, kt1, kt2, kt3;  // tile t: K[4 g + s][j_t(n)], s = 0..3 (A operand of the update)
-  u32x2 vv;                // V[n][i0 + 4 g .. 4 g + 3]
-  u32x2 tm;                // delta rule: Tm[n][4 g .. 4 g + 3] (from the stored Tm^T)
+// A pair of chunks' operands for a chain wave, read one pair ahead: K rows, V columns, the
+// K^T gathers and, for the delta rule, Tm.
+struct PairRegs {
+  u32x4 k[2][2];   // chunk e: K[n][8 g + 0..7], K[n][32 + 8 g + 0..7]
+  u32x2 v[2];      // chunk e: V[n][i0 + 4 g .. + 3]
+  u32x2 kt[2][4];  // chunk e, tile t: K[4 g + s][j_t(n)], s = 0..3
+  u32x2 tm[2];     // delta rule: chunk e's Tm[n][4 g .. 4 g + 3] (from the stored Tm^T)
 };
 
 // Per-lane byte offsets inside a slot, fixed for the whole kernel.
@@ -137,22 +175,23 @@ struct LaneOffsets {
   int tm;        // Tm row n, columns 4 g
 };
 
-// Reads a chunk's operands from its ring slot.  Only compute waves run this, and their code
-// path issues no direct-to-LDS loads, so the compiler's own lgkmcnt waits order the reads.
+// Ring reads of the chain waves.  Only chain waves run this, and their code path issues no
+// direct-to-LDS loads, so the compiler's own lgkmcnt waits order the reads.
 template <bool kDelta>
-__device__ __forceinline__ void read_chunk(ChunkRegs& r, const lds_char* slot, const LaneOffsets& o) {
-  const lds_char* q = slot;
-  const lds_char* k = slot + kTileBytes;
-  r.ka0 = lds_load<u32x4>(k + o.ka0);
-  r.ka1 = lds_load<u32x4>(k + o.ka1);
-  r.qb0 = lds_load<u32x4>(q + o.ka0);
-  r.qb1 = lds_load<u32x4>(q + o.ka1);
-  r.kt0 = lds_load_tr(k + o.kt0);
-  r.kt1 = lds_load_tr(k + o.kt0 + 8);
-  r.kt2 = lds_load_tr(k + o.kt1);
-  r.kt3 = lds_load_tr(k + o.kt1 + 8);
-  r.vv = lds_load<u32x2>(slot + kVOff + o.vv);
-  if (kDelta) r.tm = lds_load_tr(slot + kTmOff + o.tm);
+__device__ __forceinline__ void read_pair(PairRegs& r, const lds_char* s0, const lds_char* s1, const LaneOffsets& o) {
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const lds_char* slot = e ? s1 : s0;
+    const lds_char* k = slot + kTileBytes;
+    r.k[e][0] = lds_load<u32x4>(k + o.ka0);
+    r.k[e][1] = lds_load<u32x4>(k + o.ka1);
+    r.v[e] = lds_load<u32x2>(slot + kVOff + o.vv);
+    r.kt[e][0] = lds_load_tr(k + o.kt0);
+    r.kt[e][1] = lds_load_tr(k + o.kt0 + 8);
+    r.kt[e][2] = lds_load_tr(k + o.kt1);
+    r.kt[e][3] = lds_load_tr(k + o.kt1 + 8);
+    if (kDelta) r.tm[e] = lds_load_tr(slot + kTmOff + o.tm);
+  }
 }
 
 struct WState {
@@ -162,49 +201,107 @@ struct WState {
 // Chunk-independent constants of a lane.
 struct LaneConst {
   bf16x8_t neg_eye;        // -I as a padded B operand: slot s < 4 of lane (g, n) is row 4g+s
-  uint32_t pmask0, pmask1; // causal mask of P^T on packed bf16 pairs (row 4g+e kept if <= n)
   float neta;
 };
 
 #define MFMA32 __builtin_amdgcn_mfma_f32_16x16x32_bf16
-#define MFMA16 __builtin_amdgcn_mfma_f32_16x16x16bf16_1k
 
-// One chunk.  Returns Z^T for the lane (4 consecutive output features of token n) as bf16.
-template <bool kDelta>
-__device__ __forceinline__ u32x2 chunk_step(WState& w, const ChunkRegs& r, const LaneConst& lc) {
+// -V + K W^T for one chunk: V row n enters the accumulator through an MFMA with -I.
+__device__ __forceinline__ float4_t kw_minus_v(const u32x4& k0, const u32x4& k1, const u32x2& vv,
+                                              const bf16x8_t& wb0, const bf16x8_t& wb1, const LaneConst& lc) {
   const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-  // bf16 W^T: operand kb holds inputs 32 kb + 8 g + 0..7 of output row i0 + n
+  const u32x4 vpad = {vv.x, vv.y, 0u, 0u};
+  float4_t acc = MFMA32(bf8(vpad), lc.neg_eye, zero, 0, 0, 0);
+  acc = MFMA32(bf8(k0), wb0, acc, 0, 0, 0);
+  return MFMA32(bf8(k1), wb1, acc, 0, 0, 0);
+}
+// Delta rule: R = Tm X, with X in bf16 as the B operand and Tm in the padded A layout.
+__device__ __forceinline__ float4_t tm_apply(const u32x2& tm, const float4_t& x) {
+  const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  const u32x4 xb = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), 0u, 0u};
+  const u32x4 tma = {tm.x, tm.y, 0u, 0u};
+  return MFMA32(bf8(tma), bf8(xb), zero, 0, 0, 0);
+}
+__device__ __forceinline__ u32x2 neg_eta_bf16(const float4_t& r, float neta) {
+  const u32x2 x = {pack_bf16(neta * r[0], neta * r[1]), pack_bf16(neta * r[2], neta * r[3])};
+  return x;
+}
+
+// Chunks c, c + 1 (c even) of the state recursion, from W = W_c:
+//   R_c     = K_c W^T - V_c
+//   R_{c+1} = K_{c+1} W_{c+1}^T - V_{c+1} = (K_{c+1} W^T - V_{c+1}) + M (-eta R_c),
+//             M = K_{c+1} K_c^T, because W_{c+1} = W - eta R_c^T K_c
+//   W_{c+2} = W - eta [R_c; R_{c+1}]^T [K_c; K_{c+1}]   (one K = 32 MFMA per state tile)
+// (delta rule: each R is Tm times the bracket).  Only the second R waits for the first; the
+// state update and its bf16 copy happen once per pair.  Hands off the bf16 W_c and
+// -eta R_c, -eta R_{c+1} to the output wave (pair area h; lw = 16 lane, lr = 8 lane).
+template <bool kDelta>
+__device__ __forceinline__ void pair_step(WState& w, const PairRegs& r, const LaneConst& lc, lds_char* h, int lw,
+                                          int lr) {
+  const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
   const u32x4 wb0u = {pack_bf16(w.t0[0], w.t0[1]), pack_bf16(w.t0[2], w.t0[3]),
                       pack_bf16(w.t1[0], w.t1[1]), pack_bf16(w.t1[2], w.t1[3])};
   const u32x4 wb1u = {pack_bf16(w.t2[0], w.t2[1]), pack_bf16(w.t2[2], w.t2[3]),
                       pack_bf16(w.t3[0], w.t3[1]), pack_bf16(w.t3[2], w.t3[3])};
   const bf16x8_t wb0 = bf8(wb0u), wb1 = bf8(wb1u);
-  // R = K W^T - V (rows: tokens 4 g + e, column: output feature i0 + n)
-  const u32x4 vpad = {r.vv.x, r.vv.y, 0u, 0u};
-  float4_t racc = MFMA32(bf8(vpad), lc.neg_eye, zero, 0, 0, 0);
-  racc = MFMA32(bf8(r.ka0), wb0, racc, 0, 0, 0);
-  racc = MFMA32(bf8(r.ka1), wb1, racc, 0, 0, 0);
-  if (kDelta) {
-    // delta rule: R <- Tm R (Tm in the padded A layout, R in bf16 as the B operand)
-    const u32x4 r0b = {pack_bf16(racc[0], racc[1]), pack_bf16(racc[2], racc[3]), 0u, 0u};
-    const u32x4 tma = {r.tm.x, r.tm.y, 0u, 0u};
-    racc = MFMA32(bf8(tma), bf8(r0b), zero, 0, 0, 0);
+  float4_t r0 = kw_minus_v(r.k[0][0], r.k[0][1], r.v[0], wb0, wb1, lc);
+  const float4_t a1 = kw_minus_v(r.k[1][0], r.k[1][1], r.v[1], wb0, wb1, lc);
+  // M^T = K_c K_{c+1}^T in the C layout is M as the A operand: lane (g, n) = M[n][4 g + s]
+  float4_t mt = MFMA32(bf8(r.k[0][0]), bf8(r.k[1][0]), zero, 0, 0, 0);
+  mt = MFMA32(bf8(r.k[0][1]), bf8(r.k[1][1]), mt, 0, 0, 0);
+  if (kDelta) r0 = tm_apply(r.tm[0], r0);
+  const u32x2 rn0 = neg_eta_bf16(r0, lc.neta);
+  const u32x4 mpad = {pack_bf16(mt[0], mt[1]), pack_bf16(mt[2], mt[3]), 0u, 0u};
+  const u32x4 rpad0 = {rn0.x, rn0.y, 0u, 0u};
+  float4_t r1 = MFMA32(bf8(mpad), bf8(rpad0), a1, 0, 0, 0);
+  if (kDelta) r1 = tm_apply(r.tm[1], r1);
+  const u32x2 rn1 = neg_eta_bf16(r1, lc.neta);
+  lds_store<u32x4>(h + lw, wb0u);
+  lds_store<u32x4>(h + kHandW1 + lw, wb1u);
+  lds_store<u32x2>(h + kHandR0 + lr, rn0);
+  lds_store<u32x2>(h + kHandR1 + lr, rn1);
+  // W^T += K^T (-eta R) over the pair's 32 tokens: slots 0..3 chunk c, 4..7 chunk c + 1
+  const u32x4 rr = {rn0.x, rn0.y, rn1.x, rn1.y};
+  const u32x4 k0 = {r.kt[0][0].x, r.kt[0][0].y, r.kt[1][0].x, r.kt[1][0].y};
+  const u32x4 k1 = {r.kt[0][1].x, r.kt[0][1].y, r.kt[1][1].x, r.kt[1][1].y};
+  const u32x4 k2 = {r.kt[0][2].x, r.kt[0][2].y, r.kt[1][2].x, r.kt[1][2].y};
+  const u32x4 k3 = {r.kt[0][3].x, r.kt[0][3].y, r.kt[1][3].x, r.kt[1][3].y};
+  w.t0 = MFMA32(bf8(k0), bf8(rr), w.t0, 0, 0, 0);
+  w.t1 = MFMA32(bf8(k1), bf8(rr), w.t1, 0, 0, 0);
+  w.t2 = MFMA32(bf8(k2), bf8(rr), w.t2, 0, 0, 0);
+  w.t3 = MFMA32(bf8(k3), bf8(rr), w.t3, 0, 0, 0);
+}
+
+// One chunk's output from the pair's handoff h and the chunk's ring slot:
+//   Z^T = W Q^T + (-eta R)^T P^T,  P^T = K Q^T with the causal mask on its packed pairs.
+// For the second chunk of a pair W is the pair's start state W_c and the first chunk's
+// update enters as (-eta R_c)^T (K_c Q^T) (kprev: K_c's slot).  Returns Z^T for the lane (4
+// consecutive output features of token n) as bf16.
+template <bool kOdd>
+__device__ __forceinline__ u32x2 out_step(const lds_char* slot, const lds_char* kprev, const lds_char* h, int ka0,
+                                          int ka1, int lw, int lr, uint32_t pmask0, uint32_t pmask1) {
+  const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  const lds_char* q = slot;
+  const lds_char* k = slot + kTileBytes;
+  const bf16x8_t qb0 = bf8(lds_load<u32x4>(q + ka0)), qb1 = bf8(lds_load<u32x4>(q + ka1));
+  const bf16x8_t kb0 = bf8(lds_load<u32x4>(k + ka0)), kb1 = bf8(lds_load<u32x4>(k + ka1));
+  const bf16x8_t wb0 = bf8(lds_load<u32x4>(h + lw)), wb1 = bf8(lds_load<u32x4>(h + kHandW1 + lw));
+  const u32x2 rn = lds_load<u32x2>(h + (kOdd ? kHandR1 : kHandR0) + lr);
+  float4_t zacc = MFMA32(wb0, qb0, zero, 0, 0, 0);
+  zacc = MFMA32(wb1, qb1, zacc, 0, 0, 0);
+  float4_t pacc = MFMA32(kb0, qb0, zero, 0, 0, 0);
+  pacc = MFMA32(kb1, qb1, pacc, 0, 0, 0);
+  if (kOdd) {
+    const lds_char* kp = kprev + kTileBytes;
+    const bf16x8_t kp0 = bf8(lds_load<u32x4>(kp + ka0)), kp1 = bf8(lds_load<u32x4>(kp + ka1));
+    const u32x2 rp = lds_load<u32x2>(h + kHandR0 + lr);
+    float4_t xacc = MFMA32(kp0, qb0, zero, 0, 0, 0);
+    xacc = MFMA32(kp1, qb1, xacc, 0, 0, 0);
+    const u32x4 xm = {pack_bf16(xacc[0], xacc[1]), pack_bf16(xacc[2], xacc[3]), 0u, 0u};
+    const u32x4 rp4 = {rp.x, rp.y, 0u, 0u};
+    zacc = MFMA32(bf8(rp4), bf8(xm), zacc, 0, 0, 0);
   }
-  // Z^T = W Q^T (first part) and P^T = K Q^T, independent of R
-  float4_t zacc = MFMA32(wb0, bf8(r.qb0), zero, 0, 0, 0);
-  zacc = MFMA32(wb1, bf8(r.qb1), zacc, 0, 0, 0);
-  float4_t pacc = MFMA32(bf8(r.ka0), bf8(r.qb0), zero, 0, 0, 0);
-  pacc = MFMA32(bf8(r.ka1), bf8(r.qb1), pacc, 0, 0, 0);
-  // W^T += K^T (-eta R)
-  const u32x2 rn = {pack_bf16(lc.neta * racc[0], lc.neta * racc[1]),
-                    pack_bf16(lc.neta * racc[2], lc.neta * racc[3])};
-  w.t0 = MFMA16(bf4(r.kt0), bf4(rn), w.t0, 0, 0, 0);
-  w.t1 = MFMA16(bf4(r.kt1), bf4(rn), w.t1, 0, 0, 0);
-  w.t2 = MFMA16(bf4(r.kt2), bf4(rn), w.t2, 0, 0, 0);
-  w.t3 = MFMA16(bf4(r.kt3), bf4(rn), w.t3, 0, 0, 0);
-  // Z^T += (-eta R)^T P^T with the causal mask applied to the packed pairs of P^T
-  const u32x4 pm = {pack_bf16(pacc[0], pacc[1]) & lc.pmask0,
-                    pack_bf16(pacc[2], pacc[3]) & lc.pmask1, 0u, 0u};
+  const u32x4 pm = {pack_bf16(pacc[0], pacc[1]) & pmask0, pack_bf16(pacc[2], pacc[3]) & pmask1, 0u, 0u};
   const u32x4 rn4 = {rn.x, rn.y, 0u, 0u};
   zacc = MFMA32(bf8(rn4), bf8(pm), zacc, 0, 0, 0);
   const u32x2 out = {pack_bf16(zacc[0], zacc[1]), pack_bf16(zacc[2], zacc[3])};
@@ -241,8 +338,10 @@ template <bool kDelta>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) void linear_mfma_kernel(
     LinearArgs a, const bf16* tmat) {
   using RG = Ring<kDelta>;
-  __shared__ __attribute__((aligned(16))) char ring_mem[kRing * RG::kSlotBytes];
-  lds_char* ring = (lds_char*)(ring_mem);
+  constexpr int kRing = RG::kRing;
+  __shared__ __attribute__((aligned(16))) char lds_mem[kRing * RG::kSlotBytes + kHandBytes];
+  lds_char* ring = (lds_char*)(lds_mem);
+  lds_char* hand = ring + kRing * RG::kSlotBytes;
 
   // blockIdx = 8 kSplit (chain / 8) + 8 part + chain % 8: the parts of a chain share an XCD
   const int bidx = blockIdx.x;
@@ -252,13 +351,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
+  const int g = lane >> 4;
+  const int n = lane & 15;
   const int T = a.T;
   const int nchunks = (T + kB - 1) / kB;
   const int ngroups = (nchunks + kGroup - 1) / kGroup;
   const int seq_bytes = T * kD * 2;  // < 2^31: checked by linear_mfma_supported
   const size_t tok0 = static_cast<size_t>(chain) * static_cast<size_t>(T) * kD;
+  const int lw = 16 * lane, lr = 8 * lane;  // lane offsets in a handoff
+  // Every wave meets barriers 0 .. ngroups.  Chain waves compute group grp (chunks kGroup grp
+  // .. + kGroup - 1) between barriers grp and grp + 1 and hand it off; output waves finish it
+  // between barriers grp + 1 and grp + 2.
 
-  if (wv == kComputeWaves) {
+  if (wv == kLoaderWave) {
     // Loader wave: streams chunk c into ring slot c % kRing with direct-to-LDS loads.  Lane
     // l of a Q/K half tile fills physical piece l % 8 of row 8 hh + l / 8, i.e. loads that
     // row's logical piece (l % 8) ^ sig(l / 8); lane l of the V load fills physical piece
@@ -276,52 +381,87 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
       const int off = c * kTileBytes;
       lds_char* dst = ring + (c % kRing) * RG::kSlotBytes;
       const __amdgpu_buffer_rsrc_t rq = chunk_rsrc(qsrc + off, seq_bytes - off);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, dst, 16, lglob, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, dst + 1024, 16, lglob + 1024, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, dst, 16, lglob, 0, 0, kNT);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, dst + 1024, 16, lglob + 1024, 0, 0, kNT);
       const __amdgpu_buffer_rsrc_t rk = chunk_rsrc(ksrc + off, seq_bytes - off);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dst + kTileBytes, 16, lglob, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dst + kTileBytes + 1024, 16, lglob + 1024, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dst + kTileBytes, 16, lglob, 0, 0, kNT);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dst + kTileBytes + 1024, 16, lglob + 1024, 0, 0, kNT);
       const __amdgpu_buffer_rsrc_t rv = chunk_rsrc(vsrc + off, seq_bytes - off);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst + kVOff, 16, vglob, 0, 0, 0);
-      if (kDelta) {
-        // Tm^T of chunk c: 512 bytes read by lanes 0..31; lanes 32..63 are out of range
-        // and fill the second half of the 1 KB area with zeros.
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst + kVOff, 16, vglob, 0, 0, kNT);
+      if (kDelta && lane < 32) {
+        // Tm^T of chunk c: 512 bytes, 16 per lane (zeros past the last chunk)
         const __amdgpu_buffer_rsrc_t rs =
             chunk_rsrc(tsrc + static_cast<size_t>(c) * kTmBytes, c < nchunks ? kTmBytes : 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + kTmOff, 16, lane * 16, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + kTmOff, 16, lane * 16, 0, 0, kNT);
       }
     };
-    // The compute waves read chunk 0 after barrier 0 and chunks kGroup g + 1 .. kGroup g +
-    // kGroup between barriers g and g + 1.  So barrier g publishes the chunks up to
-    // kGroup g + kGroup, and from g = 1 on it frees the slots of the chunks up to kGroup g,
-    // after which the loader refills the ring up to chunk kGroup g + kRing.  Barrier 0
-    // frees nothing.
+    // Chain waves read chunks 0, 1 after barrier 0 and chunks up to kGroup b + kGroup + 1
+    // after barrier b (one pair ahead); output waves read chunks kGroup (b - 1) .. kGroup b - 1 after barrier
+    // b.  So barrier b must publish the chunks up to kGroup b + kGroup + 1, and from b = 2 on it
+    // frees the slots of the chunks up to kGroup b - kGroup - 1 (barriers 0 and 1 free
+    // nothing), after which the loader refills the ring up to chunk kGroup b - kGroup - 1 +
+    // kRing.
     for (int c = 0; c < kRing; ++c) issue(c);
     wait_vmcnt<RG::kWait0>();
-    lds_barrier();
-    if (ngroups > 1) {
-      wait_vmcnt<RG::kWait1>();
-      lds_barrier();
-#pragma unroll
-      for (int x = 0; x <= kGroup; ++x) issue(kRing + x);
-    }
-    for (int grp = 2; grp < ngroups; ++grp) {
+    lds_barrier();  // barrier 0
+    wait_vmcnt<RG::kWait1>();
+    lds_barrier();  // barrier 1
+    for (int b = 2; b <= ngroups; ++b) {
       wait_vmcnt<RG::kWaitN>();
-      lds_barrier();
+      lds_barrier();  // barrier b
+      if (b < ngroups) {
 #pragma unroll
-      for (int x = 1; x <= kGroup; ++x) issue(kGroup * (grp - 1) + kRing + x);
+        for (int x = 0; x < kGroup; ++x) issue(kGroup * b - 2 * kGroup + kRing + x);
+      }
     }
     wait_vmcnt<0>();  // no load outlives the wave
     return;
   }
 
-  // Compute waves: wave w of part p owns output rows i0 .. i0 + 15, i0 = 32 p + 16 w.
-  const int g = lane >> 4;
-  const int n = lane & 15;
+  LaneOffsets o;
+  o.ka0 = swz(n, g) * 16;
+  o.ka1 = swz(n, 4 + g) * 16;
+
+  if (wv >= kChainWaves) {
+    // Output wave ow: Z columns i0 .. i0 + 15 of chain wave ow's rows.  Each chunk's store
+    // is 8 bytes per lane (rows past T are dropped by the buffer range); the stores of a
+    // block of kRing chunks share one buffer resource, rebased once per block.
+    const int ow = wv - kChainWaves;
+    const int i0 = kHalfCols * part + 16 * ow;
+    char* z = reinterpret_cast<char*>(static_cast<bf16*>(a.z) + tok0);
+    const uint32_t pmask0 = (4 * g + 0 <= n ? 0x0000FFFFu : 0u) | (4 * g + 1 <= n ? 0xFFFF0000u : 0u);
+    const uint32_t pmask1 = (4 * g + 2 <= n ? 0x0000FFFFu : 0u) | (4 * g + 3 <= n ? 0xFFFF0000u : 0u);
+    const int zoff = n * 128 + 2 * (i0 + 4 * g);
+    lds_char* hw = hand + ow * kHandWave;
+    lds_barrier();  // barrier 0
+    for (int gbase = 0; gbase < ngroups; gbase += kRing / kGroup) {
+      const int boff = gbase * kGroup * kTileBytes;
+      const __amdgpu_buffer_rsrc_t zrs = chunk_rsrc(z + boff, seq_bytes - boff);
+#pragma unroll
+      for (int gg = 0; gg < kRing / kGroup; ++gg) {
+        const int grp = gbase + gg;
+        if (grp >= ngroups) break;
+        lds_barrier();  // barrier grp + 1: group grp's handoffs are complete
+        const lds_char* hg = hw + (grp & 1) * kHandGroup;
+#pragma unroll
+        for (int x = 0; x < kGroup; x += 2) {
+          const int slot = gg * kGroup + x;  // chunk kGroup grp + x, mod kRing
+          const lds_char* s0 = ring + slot * RG::kSlotBytes;
+          const lds_char* hp = hg + (x / 2) * kHandPair;
+          const u32x2 z0 = out_step<false>(s0, s0, hp, o.ka0, o.ka1, lw, lr, pmask0, pmask1);
+          const u32x2 z1 = out_step<true>(s0 + RG::kSlotBytes, s0, hp, o.ka0, o.ka1, lw, lr, pmask0, pmask1);
+          __builtin_amdgcn_raw_buffer_store_b64(z0, zrs, zoff + slot * kTileBytes, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b64(z1, zrs, zoff + (slot + 1) * kTileBytes, 0, 0);
+        }
+      }
+    }
+    return;
+  }
+
+  // Chain waves: wave w of part p owns output rows i0 .. i0 + 15, i0 = 32 p + 16 w.
   const int i0 = kHalfCols * part + 16 * wv;
   const int bi = chain / a.H;
   const int hi = chain - bi * a.H;
-  char* z = reinterpret_cast<char*>(static_cast<bf16*>(a.z) + tok0);
   const float* w0 = a.w0 + bi * a.w0_batch_stride + static_cast<long long>(hi) * kD * kD;
 
   WState wacc;
@@ -339,51 +479,39 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
                        (4 * g + 2 == n ? one_neg : 0u) | (4 * g + 3 == n ? one_neg << 16 : 0u),
                        0u, 0u};
     lc.neg_eye = bf8(eye);
-    lc.pmask0 = (4 * g + 0 <= n ? 0x0000FFFFu : 0u) | (4 * g + 1 <= n ? 0xFFFF0000u : 0u);
-    lc.pmask1 = (4 * g + 2 <= n ? 0x0000FFFFu : 0u) | (4 * g + 3 <= n ? 0xFFFF0000u : 0u);
     lc.neta = -a.eta;
   }
-  LaneOffsets o;
-  o.ka0 = swz(n, g) * 16;
-  o.ka1 = swz(n, 4 + g) * 16;
   o.kt0 = swz(4 * g + (n >> 2), n & 3) * 16;
   o.kt1 = swz(4 * g + (n >> 2), 4 + (n & 3)) * 16;
   o.vv = vswz(n, 2 * wv + (g >> 1)) * 16 + 8 * (g & 1);
   o.tm = (4 * g + (n >> 2)) * 32 + 8 * (n & 3);
 
-  // Step c: compute chunk c from registers read in step c - 1 while reading chunk c + 1,
-  // and store this wave's 16 columns of Z_c (8 bytes per lane; rows past T are dropped by
-  // the buffer range).  Chunks past the end read as zeros and leave the state unchanged.
-  // The Z stores of a block of kRing chunks share one buffer resource, rebased once per
-  // block; the lane offsets of the block's chunks are precomputed, so a step's store needs
-  // no address arithmetic (the range check on the lane offset still drops rows past T).
-  const int zoff = n * 128 + 2 * (i0 + 4 * g);
-  int zo[kRing];
-#pragma unroll
-  for (int i = 0; i < kRing; ++i) zo[i] = zoff + i * kTileBytes;
-  lds_barrier();  // barrier 0: chunks 0 .. kGroup published
-  ChunkRegs ra, rb;
-  read_chunk<kDelta>(ra, ring, o);
+  // Pair step p computes chunks 2p, 2p + 1 from registers read in step p - 1 while reading
+  // chunks 2p + 2, 2p + 3.  Chunks past the end read as zeros and leave the state unchanged.
+  lds_char* hw = hand + wv * kHandWave;
+  lds_barrier();  // barrier 0: chunks 0 .. kGroup + 1 published
+  PairRegs ra, rb;
+  read_pair<kDelta>(ra, ring, ring + RG::kSlotBytes, o);
   for (int gbase = 0; gbase < ngroups; gbase += kRing / kGroup) {
-    const int boff = gbase * kGroup * kTileBytes;
-    const __amdgpu_buffer_rsrc_t zrs = chunk_rsrc(z + boff, seq_bytes - boff);
 #pragma unroll
     for (int gg = 0; gg < kRing / kGroup; ++gg) {
       const int grp = gbase + gg;
       if (grp >= ngroups) break;
-      if (grp > 0) lds_barrier();
+      if (grp > 0) lds_barrier();  // barrier grp
+      lds_char* hg = hw + (grp & 1) * kHandGroup;
 #pragma unroll
-      for (int x = 0; x < kGroup; ++x) {
-        const int nslot = (gg * kGroup + x + 1) % kRing;  // compile-time slot of chunk c + 1
-        ChunkRegs& cur = (x & 1) ? rb : ra;
-        ChunkRegs& nxt = (x & 1) ? ra : rb;
+      for (int x = 0; x < kGroup; x += 2) {
+        const int s2 = (gg * kGroup + x + 2) % kRing;  // compile-time slots of chunks c + 2, c + 3
+        const int s3 = (gg * kGroup + x + 3) % kRing;
+        const PairRegs& cur = (x & 2) ? rb : ra;
+        PairRegs& nxt = (x & 2) ? ra : rb;
         __builtin_amdgcn_sched_barrier(0);  // keep steps apart (register pressure)
-        read_chunk<kDelta>(nxt, ring + nslot * RG::kSlotBytes, o);
-        const u32x2 zz = chunk_step<kDelta>(wacc, cur, lc);
-        __builtin_amdgcn_raw_buffer_store_b64(zz, zrs, zo[gg * kGroup + x], 0, 0);
+        read_pair<kDelta>(nxt, ring + s2 * RG::kSlotBytes, ring + s3 * RG::kSlotBytes, o);
+        pair_step<kDelta>(wacc, cur, lc, hg + (x / 2) * kHandPair, lw, lr);
       }
     }
   }
+  lds_barrier();  // barrier ngroups: the last group's handoffs are complete
 
   if (a.w_out) {
     float* wr = a.w_out + static_cast<size_t>(chain) * kD * kD + (i0 + n) * kD + 8 * g;
@@ -404,7 +532,7 @@ static bool mfma_shape_ok(const LinearArgs& a) {
                        (a.w_out == nullptr || al(a.w_out, 16));
   // byte offsets inside one sequence, including the loads the ring issues past the end,
   // are 32-bit
-  const bool fits = static_cast<long long>(a.T) * kD * 2 + 2LL * kTileBytes * (kRing + 2 * kGroup) < 0x7fffffffLL;
+  const bool fits = static_cast<long long>(a.T) * kD * 2 + 2LL * kTileBytes * (kRingMax + 2 * kGroup) < 0x7fffffffLL;
   return a.d == kD && a.T > 0 && aligned && fits;
 }
 
