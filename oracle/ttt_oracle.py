@@ -23,6 +23,12 @@ define the method; no line numbers are given on purpose):
   the previous mini-batch (W_0 for the first one), and
       W_t = W_{t'} - eta * sum_{s = t'+1..t} grad l_s(W_{t'})          (cumulative sum).
   b = 1 is plain online GD, b = T is batch GD.
+* Per-token learning rates (optional eta_tok): the "Fast weights" page writes the step
+  as W_t = W_{t-1} - eta_t grad l_t(W_{t-1}) with a rate per step (opening formula and
+  section 1), and the wmrh.cn summary, section 2.2.3 ("learnable eta"), makes it a function
+  of the token, eta(x) = eta_base * sigmoid(theta_lr . x).  The rate of token t is
+  eta * eta_tok[..., t]; in a mini-batch each token's gradient is scaled by its own rate,
+      W_t = W_{t'} - sum_{s = t'+1..t} eta_s grad l_s(W_{t'}).
 * Output rule: z_t = f(q_t; W_t), i.e. the output is read after the token's own update
   (blog page "TTT / 通用表示"; "Fast weights" page opening formula).
 * Non-causal variant (ViT3 news page, "1. inner training setup", observation 2): the keys
@@ -154,6 +160,15 @@ def _broadcast_state(w, lead, dtype):
     return np.array(full.reshape((n,) + w.shape[-2:]), dtype=dtype, copy=True)
 
 
+def _token_rates(eta, eta_tok, lead, T, dtype):
+    """Per-token rates eta * eta_tok broadcast to the chains, [N, T]; None without eta_tok."""
+    if eta_tok is None:
+        return None
+    r = np.broadcast_to(np.asarray(eta_tok).astype(dtype), tuple(lead) + (T,))
+    n = int(np.prod(lead)) if lead else 1
+    return dtype(eta) * np.array(r.reshape(n, T), dtype=dtype, copy=True)
+
+
 def _check_chunk(T, chunk):
     if not (isinstance(chunk, (int, np.integer)) and chunk >= 1):
         raise ValueError("chunk must be a positive integer")
@@ -165,11 +180,12 @@ def _check_chunk(T, chunk):
 # The recurrences
 # ----------------------------------------------------------------------------------------
 
-def ttt_linear(q, k, v, w0, eta, chunk, causal=True, loss="mse", dtype=np.float64):
+def ttt_linear(q, k, v, w0, eta, chunk, causal=True, loss="mse", dtype=np.float64, eta_tok=None):
     """TTT layer with the linear inner model, mini-batch GD of size `chunk`.
 
     q, k, v: [..., T, d]; w0: [..., d, d] (broadcast over the leading dims, e.g. [H, d, d]
-    shared by every batch element).  Returns (z [..., T, d], w_final [..., d, d]).
+    shared by every batch element); eta_tok: optional per-token rate factors [..., T].
+    Returns (z [..., T, d], w_final [..., d, d]).
 
     The last chunk is shorter when T is not a multiple of `chunk`.  causal=False trains
     over every chunk first and then applies the final weights to every query.
@@ -182,6 +198,7 @@ def ttt_linear(q, k, v, w0, eta, chunk, causal=True, loss="mse", dtype=np.float6
     N, T, d = q2.shape
     W = _broadcast_state(w0, lead, dtype)
     b = _check_chunk(T, chunk)
+    et = _token_rates(eta, eta_tok, lead, T, dtype)
     eta = dtype(eta)
     z = np.zeros((N, T, d), dtype=dtype)
     for c0 in range(0, T, b):
@@ -189,8 +206,12 @@ def ttt_linear(q, k, v, w0, eta, chunk, causal=True, loss="mse", dtype=np.float6
         G = np.zeros_like(Wc)              # running sum of this mini-batch's gradients
         Wt = Wc
         for t in range(c0, min(c0 + b, T)):
-            G = G + linear_grad(Wc, k2[:, t], v2[:, t], loss)
-            Wt = Wc - eta * G              # W_t, materialised
+            if et is None:
+                G = G + linear_grad(Wc, k2[:, t], v2[:, t], loss)
+                Wt = Wc - eta * G              # W_t, materialised
+            else:                              # rate-weighted sum, each token its own rate
+                G = G + et[:, t, None, None] * linear_grad(Wc, k2[:, t], v2[:, t], loss)
+                Wt = Wc - G
             if causal:
                 z[:, t] = linear_f(Wt, q2[:, t])
         W = Wt
@@ -200,11 +221,12 @@ def ttt_linear(q, k, v, w0, eta, chunk, causal=True, loss="mse", dtype=np.float6
     return z.reshape(tuple(lead) + (T, d)), W.reshape(tuple(lead) + (d, d))
 
 
-def ttt_mlp(q, k, v, w1, w2, eta, chunk, causal=True, loss="mse", dtype=np.float64):
+def ttt_mlp(q, k, v, w1, w2, eta, chunk, causal=True, loss="mse", dtype=np.float64, eta_tok=None):
     """TTT layer with the 2-layer SiLU MLP inner model, mini-batch GD of size `chunk`.
 
     q, k, v: [..., T, d]; w1: [..., h, d]; w2: [..., d, h] (broadcast over the leading
-    dims).  Returns (z [..., T, d], w1_final [..., h, d], w2_final [..., d, h]).
+    dims); eta_tok: optional per-token rate factors [..., T].
+    Returns (z [..., T, d], w1_final [..., h, d], w2_final [..., d, h]).
     """
     if loss not in LOSSES:
         raise ValueError(loss)
@@ -218,6 +240,7 @@ def ttt_mlp(q, k, v, w1, w2, eta, chunk, causal=True, loss="mse", dtype=np.float
     if W1.shape[-1] != d or W2.shape[-2:] != (d, h):
         raise ValueError("w1 must be [..., h, d] and w2 [..., d, h]")
     b = _check_chunk(T, chunk)
+    et = _token_rates(eta, eta_tok, lead, T, dtype)
     eta = dtype(eta)
     z = np.zeros((N, T, d), dtype=dtype)
     for c0 in range(0, T, b):
@@ -227,10 +250,16 @@ def ttt_mlp(q, k, v, w1, w2, eta, chunk, causal=True, loss="mse", dtype=np.float
         W1t, W2t = W1c, W2c
         for t in range(c0, min(c0 + b, T)):
             g1, g2 = mlp_grad(W1c, W2c, k2[:, t], v2[:, t], loss)
-            G1 = G1 + g1
-            G2 = G2 + g2
-            W1t = W1c - eta * G1
-            W2t = W2c - eta * G2
+            if et is None:
+                G1 = G1 + g1
+                G2 = G2 + g2
+                W1t = W1c - eta * G1
+                W2t = W2c - eta * G2
+            else:                              # rate-weighted sums, each token its own rate
+                G1 = G1 + et[:, t, None, None] * g1
+                G2 = G2 + et[:, t, None, None] * g2
+                W1t = W1c - G1
+                W2t = W2c - G2
             if causal:
                 z[:, t] = mlp_f(W1t, W2t, q2[:, t])
         W1, W2 = W1t, W2t
@@ -241,22 +270,27 @@ def ttt_mlp(q, k, v, w1, w2, eta, chunk, causal=True, loss="mse", dtype=np.float
             W2.reshape(tuple(lead) + (d, h)))
 
 
-def delta_rule(q, k, v, w0, eta, dtype=np.float64):
+def delta_rule(q, k, v, w0, eta, dtype=np.float64, eta_tok=None):
     """The delta rule, written out as its closed-form update.
 
-    "Fast weights" page, section 1: W_t = W_{t-1} + eta (v_t - W_{t-1} k_t) k_t^T, and the
-    output z_t = W_t q_t.  Returns (z [..., T, d], w_final [..., d, d]).
+    "Fast weights" page, section 1: W_t = W_{t-1} + eta_t (v_t - W_{t-1} k_t) k_t^T, and the
+    output z_t = W_t q_t; eta_t = eta, or eta * eta_tok[..., t] with per-token factors.
+    Returns (z [..., T, d], w_final [..., d, d]).
     """
     q2, lead = _flatten_tokens(q, dtype)
     k2, _ = _flatten_tokens(k, dtype)
     v2, _ = _flatten_tokens(v, dtype)
     N, T, d = q2.shape
     W = _broadcast_state(w0, lead, dtype)
+    et = _token_rates(eta, eta_tok, lead, T, dtype)
     eta = dtype(eta)
     z = np.zeros((N, T, d), dtype=dtype)
     for t in range(T):
         kt = k2[:, t]
         err = v2[:, t] - np.einsum("nij,nj->ni", W, kt)      # prediction error
-        W = W + eta * np.einsum("ni,nj->nij", err, kt)
+        if et is None:
+            W = W + eta * np.einsum("ni,nj->nij", err, kt)
+        else:
+            W = W + et[:, t, None, None] * np.einsum("ni,nj->nij", err, kt)
         z[:, t] = np.einsum("nij,nj->ni", W, q2[:, t])
     return z.reshape(tuple(lead) + (T, d)), W.reshape(tuple(lead) + (d, d))

@@ -30,10 +30,11 @@ MUTATIONS = {
         'W = W + eta * np.einsum("ni,nj->nij", err, kt)',
         'W = W + eta * np.einsum("ni,nj->nij", kt, err)'),
     "delta_rule_output_before_write": (
-        '        W = W + eta * np.einsum("ni,nj->nij", err, kt)\n'
+        '            W = W + et[:, t, None, None] * np.einsum("ni,nj->nij", err, kt)\n'
         '        z[:, t] = np.einsum("nij,nj->ni", W, q2[:, t])',
-        '        z[:, t] = np.einsum("nij,nj->ni", W, q2[:, t])\n'
-        '        W = W + eta * np.einsum("ni,nj->nij", err, kt)'),
+        '            W = W + et[:, t, None, None] * np.einsum("ni,nj->nij", err, kt)\n'
+        '        z[:, t] = np.einsum("nij,nj->ni", W - np.einsum("ni,nj->nij", err, kt) * '
+        '(eta if et is None else et[:, t, None, None]), q2[:, t])'),
     "silu_derivative_missing_term": ("return s * (1.0 + u * (1.0 - s))", "return s"),
     "silu_is_sigmoid": ("return u / (1.0 + np.exp(-u))", "return 1.0 / (1.0 + np.exp(-u))"),
     "mlp_backward_skips_activation": (
@@ -43,8 +44,20 @@ MUTATIONS = {
     "mlp_gradient_at_current_weights": (
         "g1, g2 = mlp_grad(W1c, W2c, k2[:, t]", "g1, g2 = mlp_grad(W1t, W2t, k2[:, t]"),
     "last_token_of_chunk_dropped": (
-        "for t in range(c0, min(c0 + b, T)):\n            G = G + linear_grad",
-        "for t in range(c0, min(c0 + b, T) - 1):\n            G = G + linear_grad"),
+        "for t in range(c0, min(c0 + b, T)):\n            if et is None:\n                G = G + linear_grad",
+        "for t in range(c0, min(c0 + b, T) - 1):\n            if et is None:\n                G = G + linear_grad"),
+    "token_rate_of_previous_token": (
+        "G = G + et[:, t, None, None] * linear_grad", "G = G + et[:, max(t - 1, 0), None, None] * linear_grad"),
+    "token_rate_applied_twice": (
+        "                G = G + et[:, t, None, None] * linear_grad(Wc, k2[:, t], v2[:, t], loss)\n"
+        "                Wt = Wc - G",
+        "                G = G + et[:, t, None, None] * linear_grad(Wc, k2[:, t], v2[:, t], loss)\n"
+        "                Wt = Wc - eta * G"),
+    "mlp_second_layer_ignores_token_rate": (
+        "G2 = G2 + et[:, t, None, None] * g2", "G2 = G2 + eta * g2"),
+    "delta_rule_ignores_token_rate": (
+        'W = W + et[:, t, None, None] * np.einsum("ni,nj->nij", err, kt)',
+        'W = W + eta * np.einsum("ni,nj->nij", err, kt)'),
     "noncausal_reads_initial_weights": (
         "    if not causal:\n        for t in range(T):\n            z[:, t] = linear_f(W, q2[:, t])",
         "    if not causal:\n        W = _broadcast_state(w0, lead, dtype)\n"

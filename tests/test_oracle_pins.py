@@ -355,12 +355,14 @@ def test_state_broadcast_over_batch():
 # ---------------------------------------------------------------- torch.autograd
 
 def _autograd_chunked(q, k, v, params, f, eta, chunk, causal):
-    """Mini-batch GD computed with torch.autograd for the gradients (float64, CPU)."""
+    """Mini-batch GD computed with torch.autograd for the gradients (float64, CPU).  eta is
+    a scalar, or one rate per token (each token's gradient scaled by its own rate)."""
     import torch
     T = q.shape[0]
     P = [torch.tensor(p, dtype=torch.float64) for p in params]
     Q, K, V = (torch.tensor(x, dtype=torch.float64) for x in (q, k, v))
     Z = torch.zeros_like(Q)
+    per_token = np.ndim(eta) > 0
     for c0 in range(0, T, chunk):
         Pc = [p.clone().requires_grad_(True) for p in P]
         acc = [torch.zeros_like(p) for p in P]
@@ -368,8 +370,12 @@ def _autograd_chunked(q, k, v, params, f, eta, chunk, causal):
         for t in range(c0, min(c0 + chunk, T)):
             loss = 0.5 * ((f(Pc, K[t]) - V[t]) ** 2).sum()
             grads = torch.autograd.grad(loss, Pc)
-            acc = [a + g for a, g in zip(acc, grads)]
-            cur = [pc.detach() - eta * a for pc, a in zip(Pc, acc)]
+            if per_token:
+                acc = [a + float(eta[t]) * g for a, g in zip(acc, grads)]
+                cur = [pc.detach() - a for pc, a in zip(Pc, acc)]
+            else:
+                acc = [a + g for a, g in zip(acc, grads)]
+                cur = [pc.detach() - eta * a for pc, a in zip(Pc, acc)]
             if causal:
                 with torch.no_grad():
                     Z[t] = f(cur, Q[t])
@@ -414,6 +420,111 @@ def test_linear_matches_autograd(chunk, causal):
     zr, (wr,) = _autograd_chunked(q[0], k[0], v[0], [w0], _torch_linear, 0.1, chunk, causal)
     np.testing.assert_allclose(z, zr, atol=1e-12)
     np.testing.assert_allclose(w, wr, atol=1e-12)
+
+
+# ---------------------------------------------------------------- per-token rates
+# The "Fast weights" page writes the step with a rate per step, eta_t; the wmrh.cn summary,
+# section 2.2.3, makes the rate a function of the token.  In a mini-batch each token's
+# gradient is scaled by its own rate: W_t = W_{t'} - sum_{s<=t} eta_s grad l_s(W_{t'}).
+
+@pytest.mark.parametrize("chunk,causal", [(1, True), (4, True), (5, False)])
+def test_linear_token_rates_match_autograd(chunk, causal):
+    rng = _rng(30)
+    q, k, v = _rand_chains(rng, 1, 13, 4)
+    w0 = 0.3 * rng.standard_normal((4, 4))
+    r = rng.uniform(0.2, 1.0, 13)
+    z, w = O.ttt_linear(q[0], k[0], v[0], w0, 0.4, chunk, causal=causal, eta_tok=r)
+    zr, (wr,) = _autograd_chunked(q[0], k[0], v[0], [w0], _torch_linear, 0.4 * r, chunk, causal)
+    np.testing.assert_allclose(z, zr, atol=1e-12)
+    np.testing.assert_allclose(w, wr, atol=1e-12)
+
+
+@pytest.mark.parametrize("chunk,causal", [(1, True), (4, True), (13, False)])
+def test_mlp_token_rates_match_autograd(chunk, causal):
+    rng = _rng(31)
+    q, k, v = _rand_chains(rng, 1, 13, 3)
+    w1 = 0.5 * rng.standard_normal((6, 3))
+    w2 = 0.5 * rng.standard_normal((3, 6))
+    r = rng.uniform(0.2, 1.0, 13)
+    z, a1, a2 = O.ttt_mlp(q[0], k[0], v[0], w1, w2, 0.15, chunk, causal=causal, eta_tok=r)
+    zr, (r1, r2) = _autograd_chunked(q[0], k[0], v[0], [w1, w2], _torch_mlp, 0.15 * r, chunk,
+                                     causal)
+    np.testing.assert_allclose(z, zr, atol=1e-12)
+    np.testing.assert_allclose(a1, r1, atol=1e-12)
+    np.testing.assert_allclose(a2, r2, atol=1e-12)
+
+
+@pytest.mark.parametrize("model,chunk", [("linear", 1), ("linear", 4), ("mlp", 4), ("delta", 1)])
+def test_zero_rate_token_equals_zero_key(model, chunk):
+    """A token whose rate is 0 writes nothing; so does a token whose key is 0 (the gradient
+    of W k and of W2 SiLU(W1 k) vanishes at k = 0).  Both runs must agree, which pins
+    that token t's own gradient carries rate t."""
+    rng = _rng(32)
+    q, k, v = _rand_chains(rng, 2, 12, 4)
+    r = rng.uniform(0.3, 1.0, (2, 12))
+    mask = np.zeros((2, 12), dtype=bool)
+    mask[0, [1, 4, 5, 11]] = True
+    mask[1, [0, 7]] = True
+    r0 = np.where(mask, 0.0, r)
+    k0 = np.where(mask[..., None], 0.0, k)
+    if model == "linear":
+        w0 = 0.3 * rng.standard_normal((2, 4, 4))
+        a = O.ttt_linear(q, k, v, w0, 0.5, chunk, eta_tok=r0)
+        b = O.ttt_linear(q, k0, v, w0, 0.5, chunk, eta_tok=r)
+    elif model == "delta":
+        w0 = 0.3 * rng.standard_normal((2, 4, 4))
+        a = O.delta_rule(q, k, v, w0, 0.5, eta_tok=r0)
+        b = O.delta_rule(q, k0, v, w0, 0.5, eta_tok=r)
+    else:
+        w1 = 0.4 * rng.standard_normal((2, 6, 4))
+        w2 = 0.4 * rng.standard_normal((2, 4, 6))
+        a = O.ttt_mlp(q, k, v, w1, w2, 0.5, chunk, eta_tok=r0)
+        b = O.ttt_mlp(q, k0, v, w1, w2, 0.5, chunk, eta_tok=r)
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(x, y, atol=1e-12)
+
+
+def test_linear_token_rates_dual_form():
+    """Matrix form of one chunk with rates e (derived separately, not a loop over tokens):
+    R = K W^T - V, Z = Q W^T - tril(Q K^T) diag(e) R, W <- W - (diag(e) R)^T K."""
+    rng = _rng(33)
+    T, d, b, eta = 21, 4, 8, 0.7
+    q, k, v = _rand_chains(rng, 1, T, d)
+    w0 = 0.3 * rng.standard_normal((d, d))
+    r = rng.uniform(0.1, 1.0, T)
+    z, w = O.ttt_linear(q, k, v, w0[None], eta, b, eta_tok=r[None])
+    W = w0.copy()
+    Z = np.zeros((T, d))
+    for c0 in range(0, T, b):
+        Q, K, V = q[0, c0:c0 + b], k[0, c0:c0 + b], v[0, c0:c0 + b]
+        e = eta * r[c0:c0 + b]
+        R = K @ W.T - V
+        Z[c0:c0 + b] = Q @ W.T - np.tril(Q @ K.T) @ (e[:, None] * R)
+        W = W - (e[:, None] * R).T @ K
+    np.testing.assert_allclose(z[0], Z, atol=1e-12)
+    np.testing.assert_allclose(w[0], W, atol=1e-12)
+
+
+def test_linear_chunk1_equals_delta_rule_with_token_rates():
+    rng = _rng(34)
+    q, k, v = _rand_chains(rng, 3, 17, 5, unit=True)
+    w0 = 0.2 * rng.standard_normal((3, 5, 5))
+    r = rng.uniform(0.0, 1.0, (3, 17))
+    za, wa = O.ttt_linear(q, k, v, w0, 0.9, 1, eta_tok=r)
+    zb, wb = O.delta_rule(q, k, v, w0, 0.9, eta_tok=r)
+    np.testing.assert_allclose(za, zb, atol=1e-12)
+    np.testing.assert_allclose(wa, wb, atol=1e-12)
+
+
+def test_constant_token_rates_equal_scalar_rate():
+    rng = _rng(35)
+    q, k, v = _rand_chains(rng, 2, 11, 4)
+    w1 = 0.4 * rng.standard_normal((2, 6, 4))
+    w2 = 0.4 * rng.standard_normal((2, 4, 6))
+    a = O.ttt_mlp(q, k, v, w1, w2, 0.3, 4, eta_tok=np.full((2, 11), 0.5))
+    b = O.ttt_mlp(q, k, v, w1, w2, 0.15, 4)
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(x, y, atol=1e-12)
 
 
 # ---------------------------------------------------------------- edge cases
