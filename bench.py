@@ -62,15 +62,17 @@ def measured_traffic(workload_name):
     return rec["fetch_bytes"] + rec["write_bytes"]
 
 
-def make_device_inputs(w, seed, torch):
+def make_device_inputs(w, seed, torch, rates=False):
     import numpy as np
-    from test_sequence_layers_amd.workloads import make_inputs
+    from test_sequence_layers_amd.workloads import make_inputs, make_token_rates
     inp = make_inputs(w, seed=seed)
+    if rates:
+        inp["eta_tok"] = make_token_rates(w, seed)
     dt = torch.bfloat16 if w.io == "bf16" else torch.float32
     dev = {}
     for key in ("q", "k", "v"):
         dev[key] = torch.from_numpy(np.ascontiguousarray(inp[key])).to("cuda").to(dt).contiguous()
-    for key in ("w0", "w1", "w2"):
+    for key in ("w0", "w1", "w2", "eta_tok"):
         if key in inp:
             dev[key] = torch.from_numpy(inp[key]).to("cuda").contiguous()
     dev["z"] = torch.empty_like(dev["q"])
@@ -78,21 +80,24 @@ def make_device_inputs(w, seed, torch):
 
 
 def launch(w, dev, ttt):
+    et = dev.get("eta_tok")
     if w.kind == "linear":
         ttt.ttt_linear_fwd(dev["q"], dev["k"], dev["v"], dev["w0"], w.eta, w.chunk, w.causal,
-                           z=dev["z"])
+                           eta_tok=et, z=dev["z"])
     elif w.kind == "delta":
-        ttt.delta_rule_fwd(dev["q"], dev["k"], dev["v"], dev["w0"], w.eta, z=dev["z"])
+        ttt.delta_rule_fwd(dev["q"], dev["k"], dev["v"], dev["w0"], w.eta, eta_tok=et, z=dev["z"])
     else:
         ttt.ttt_mlp_fwd(dev["q"], dev["k"], dev["v"], dev["w1"], dev["w2"], w.eta, w.chunk,
-                        w.causal, z=dev["z"])
+                        w.causal, eta_tok=et, z=dev["z"])
 
 
-def time_workload(w, steps, warmup, torch, ttt, rotate=None):
+def time_workload(w, steps, warmup, torch, ttt, rotate=None, rates=False):
     bytes_, flops = algorithmic_cost(w)
+    if rates:
+        bytes_ += w.B * w.H * w.T * 4  # the rate factors, read once
     if rotate is None:
         rotate = max(2, min(8, int(6 * 256e6 / max(bytes_, 1)) + 1))
-    sets = [make_device_inputs(w, w.seed + i, torch) for i in range(rotate)]
+    sets = [make_device_inputs(w, w.seed + i, torch, rates) for i in range(rotate)]
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         launch(w, sets[i % rotate], ttt)
@@ -172,6 +177,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=None,
                     help="input/output sets rotated per step (default: enough to exceed the 256 MB "
                          "Infinity Cache; 1 = every step re-reads the same cache-warm buffers)")
+    ap.add_argument("--token-rates", action="store_true",
+                    help="time the workload with per-token rate factors eta_tok [B, H, T]")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="before timing, run one plain device copy of this many MB (counter scale)")
     args = ap.parse_args()
@@ -202,7 +209,8 @@ def main():
         torch.cuda.synchronize()
 
     w = workload(args.workload)
-    res = time_workload(w, args.steps, args.warmup, torch, ttt, rotate=args.rotate)
+    res = time_workload(w, args.steps, args.warmup, torch, ttt, rotate=args.rotate,
+                        rates=args.token_rates)
     if w.kind == "mlp":
         # dense bf16 contractions: priced against the matrix-core peak
         kern = "mlp_mfma_kernel" if w.causal else "mlp_nc_mfma_kernel"
@@ -244,6 +252,7 @@ def main():
         "data": "synthetic (seeded N(0,1) Q/K/V, unit keys, W0 ~ N(0, 0.02^2))",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d": w.d,
                    "chunk": w.chunk, "causal": w.causal, "eta": w.eta, "state": "f32",
+                   "per_token_rates": bool(args.token_rates),
                    "rotated_input_sets": res["rotated_sets"]},
         "mfma_util_pct": round(100 * res["tflops"] / BF16_MFMA_PEAK_TFLOPS, 3),
         "roofline": roofline,
@@ -255,6 +264,16 @@ def main():
                 continue
             r = time_workload(o, max(10, args.steps // 2), 5, torch, ttt)
             others[o.name] = {
+                "tokens_per_s": round(r["tokens_per_s"], 1),
+                "ms_per_step": round(r["ms_per_step"], 5),
+                "hbm_gbs": round(r["hbm_gbs"], 1),
+                "tflops": round(r["tflops"], 3),
+                "mfma_util_pct": round(100 * r["tflops"] / BF16_MFMA_PEAK_TFLOPS, 3),
+            }
+        if not args.token_rates:
+            # the headline workload again with per-token rate factors (uniform in [0, 1))
+            r = time_workload(w, max(10, args.steps // 2), 5, torch, ttt, rates=True)
+            others[w.name + "+token_rates"] = {
                 "tokens_per_s": round(r["tokens_per_s"], 1),
                 "ms_per_step": round(r["ms_per_step"], 5),
                 "hbm_gbs": round(r["hbm_gbs"], 1),

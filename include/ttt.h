@@ -23,13 +23,22 @@
  *   - Final-state outputs (w_out, w1_out, w2_out) are dense [B][H][...] float32, or NULL.
  *   - eta is the scalar inner learning rate; chunk >= 1 (a chunk longer than T is one
  *     chunk of T tokens; when T is not a multiple of chunk the last chunk is shorter).
+ *   - eta_tok (optional, NULL for none): per-token rate factors, float32 [B][H][T], a device
+ *     pointer owned by the caller, 4-byte aligned.  Token t of (b, h) then learns at rate
+ *     eta * eta_tok[(b H + h) T + t], and in a mini-batch each token's gradient carries its
+ *     own rate: W_t = W_chunk - sum_{s<=t} eta_s grad l_s.  The "Fast weights" page writes
+ *     the step with a per-step rate (opening formula); the wmrh.cn summary, section 2.2.3,
+ *     makes it a function of the token, eta_base * sigmoid(theta . x_t), which a caller
+ *     passes as eta = eta_base and eta_tok = sigmoid(theta . x_t).  The factors are read as
+ *     they are (not validated on the host; non-finite factors give non-finite outputs).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream).  Calls are
  *     asynchronous, never synchronise, keep no pointer after returning and are thread-safe;
  *     any workspace a call needs is allocated and released in stream order on `stream`.
  *   - Arguments are validated on the host before any HIP call.  Return values:
  *       TTT_OK             work enqueued;
  *       TTT_E_INVALID      a null required pointer, a non-positive size, chunk < 1, a
- *                          non-finite eta, an unknown dtype or a size overflow;
+ *                          non-finite eta, a misaligned eta_tok, an unknown dtype or a
+ *                          size overflow;
  *       TTT_E_UNSUPPORTED  a valid combination with no kernel (see each function);
  *       TTT_E_HIP          a HIP runtime error (launch failure, workspace allocation).
  *     ttt_last_error() returns the calling thread's message for the last non-OK status.
@@ -60,7 +69,7 @@ int ttt_linear_fwd(const void* q, const void* k, const void* v,
                    const float* w0, long long w0_batch_stride,
                    void* z, float* w_out,
                    int B, int H, int T, int d, int chunk, int causal, float eta,
-                   int io_dtype, ttt_stream_t stream);
+                   const float* eta_tok, int io_dtype, ttt_stream_t stream);
 
 /*
  * TTT-MLP forward: f(k; W1, W2) = W2 SiLU(W1 k) with hidden width dh, no bias (ViT3 news
@@ -76,18 +85,19 @@ int ttt_mlp_fwd(const void* q, const void* k, const void* v,
                 const float* w1, const float* w2, long long w_batch_stride,
                 void* z, float* w1_out, float* w2_out,
                 int B, int H, int T, int d, int dh, int chunk, int causal, float eta,
-                int io_dtype, ttt_stream_t stream);
+                const float* eta_tok, int io_dtype, ttt_stream_t stream);
 
 /*
- * Delta rule (mini-batch of one token, causal): W_t = W_{t-1} + eta (v_t - W_{t-1} k_t) k_t^T,
- * z_t = W_t q_t ("Fast weights" page, section 1).  Same arguments as ttt_linear_fwd
- * without chunk / causal.  Supported: d in {16, 32, 64}, both dtypes.  The d = 64 bf16 path
- * uses a stream-ordered device workspace of B*H*ceil(T/16)*512 bytes (as ttt_mlp_fwd).
+ * Delta rule (mini-batch of one token, causal): W_t = W_{t-1} + eta_t (v_t - W_{t-1} k_t) k_t^T,
+ * z_t = W_t q_t ("Fast weights" page, section 1), eta_t = eta or eta * eta_tok[t].  Same
+ * arguments as ttt_linear_fwd without chunk / causal.  Supported: d in {16, 32, 64}, both
+ * dtypes.  The d = 64 bf16 path uses a stream-ordered device workspace of
+ * B*H*ceil(T/16)*512 bytes (as ttt_mlp_fwd).
  */
 int delta_rule_fwd(const void* q, const void* k, const void* v,
                    const float* w0, long long w0_batch_stride,
                    void* z, float* w_out,
-                   int B, int H, int T, int d, float eta,
+                   int B, int H, int T, int d, float eta, const float* eta_tok,
                    int io_dtype, ttt_stream_t stream);
 
 /* Message for the calling thread's last non-OK status ("" if none).  Owned by the library;

@@ -25,10 +25,11 @@ _f = ctypes.c_float
 
 # name -> (restype, argtypes); mirrors include/ttt.h
 SIGNATURES = {
-    "ttt_linear_fwd": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
+    "ttt_linear_fwd": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _i,
+                            _vp]),
     "ttt_mlp_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp,
-                         _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
-    "delta_rule_fwd": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp]),
+                         _i, _i, _i, _i, _i, _i, _i, _f, _vp, _i, _vp]),
+    "delta_rule_fwd": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _i, _i, _i, _i, _f, _vp, _i, _vp]),
     "ttt_last_error": (ctypes.c_char_p, []),
     "ttt_abi_version": (_i, []),
 }
@@ -118,6 +119,18 @@ def _state(w, B, H, shape, name, device):
     raise ValueError(f"{name} must have shape [H, {shape}] or [B, H, {shape}], got {tuple(w.shape)}")
 
 
+def _rates(eta_tok, B, H, T, device):
+    """Device pointer of optional per-token rate factors [B, H, T] float32 (None -> NULL)."""
+    torch = _torch()
+    if eta_tok is None:
+        return None
+    if (not isinstance(eta_tok, torch.Tensor) or eta_tok.dtype != torch.float32
+            or not eta_tok.is_contiguous() or tuple(eta_tok.shape) != (B, H, T)
+            or eta_tok.device != device):
+        raise ValueError(f"eta_tok must be a contiguous float32 tensor of shape {(B, H, T)} on {device}")
+    return eta_tok.data_ptr()
+
+
 def _stream(device, stream):
     torch = _torch()
     if stream is None:
@@ -134,11 +147,12 @@ def _out(t, shape, dtype, device, name):
     return t
 
 
-def ttt_linear_fwd(q, k, v, w0, eta, chunk, causal=True, *, z=None, w_out=None,
+def ttt_linear_fwd(q, k, v, w0, eta, chunk, causal=True, *, eta_tok=None, z=None, w_out=None,
                    return_state=False, stream=None):
     """TTT-Linear forward.  q, k, v [B,H,T,d] (float32 or bfloat16, same device);
-    w0 float32 [H,d,d] (shared over the batch) or [B,H,d,d].  Returns z (and the final
-    state [B,H,d,d] when return_state or w_out is given)."""
+    w0 float32 [H,d,d] (shared over the batch) or [B,H,d,d]; eta_tok optional float32
+    [B,H,T] per-token rate factors (token t learns at eta * eta_tok[t]).  Returns z (and
+    the final state [B,H,d,d] when return_state or w_out is given)."""
     torch = _torch()
     lib = load_library()
     B, H, T, d = _tokens(q, k, v)
@@ -150,12 +164,14 @@ def ttt_linear_fwd(q, k, v, w0, eta, chunk, causal=True, *, z=None, w_out=None,
         rc = lib.ttt_linear_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), w0.data_ptr(), stride,
                                 z.data_ptr(), w_out.data_ptr() if w_out is not None else None,
                                 B, H, T, d, int(chunk), int(bool(causal)), float(eta),
+                                _rates(eta_tok, B, H, T, q.device),
                                 _io_dtype(q), _stream(q.device, stream))
     _check(rc)
     return (z, w_out) if w_out is not None else z
 
 
-def delta_rule_fwd(q, k, v, w0, eta, *, z=None, w_out=None, return_state=False, stream=None):
+def delta_rule_fwd(q, k, v, w0, eta, *, eta_tok=None, z=None, w_out=None, return_state=False,
+                   stream=None):
     """Delta-rule forward (one token per update, causal).  Arguments as ttt_linear_fwd."""
     torch = _torch()
     lib = load_library()
@@ -167,16 +183,17 @@ def delta_rule_fwd(q, k, v, w0, eta, *, z=None, w_out=None, return_state=False, 
     with torch.cuda.device(q.device):
         rc = lib.delta_rule_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), w0.data_ptr(), stride,
                                 z.data_ptr(), w_out.data_ptr() if w_out is not None else None,
-                                B, H, T, d, float(eta), _io_dtype(q), _stream(q.device, stream))
+                                B, H, T, d, float(eta), _rates(eta_tok, B, H, T, q.device),
+                                _io_dtype(q), _stream(q.device, stream))
     _check(rc)
     return (z, w_out) if w_out is not None else z
 
 
-def ttt_mlp_fwd(q, k, v, w1, w2, eta, chunk, causal=True, *, z=None, w1_out=None, w2_out=None,
-                return_state=False, stream=None):
+def ttt_mlp_fwd(q, k, v, w1, w2, eta, chunk, causal=True, *, eta_tok=None, z=None, w1_out=None,
+                w2_out=None, return_state=False, stream=None):
     """TTT-MLP forward, f(k) = W2 SiLU(W1 k).  w1 float32 [H,dh,d] or [B,H,dh,d], w2 float32
-    [H,d,dh] or [B,H,d,dh] (both shared or both per batch).  Returns z (and the final
-    states when return_state or an output state is given)."""
+    [H,d,dh] or [B,H,d,dh] (both shared or both per batch); eta_tok as in ttt_linear_fwd.
+    Returns z (and the final states when return_state or an output state is given)."""
     torch = _torch()
     lib = load_library()
     B, H, T, d = _tokens(q, k, v)
@@ -198,6 +215,7 @@ def ttt_mlp_fwd(q, k, v, w1, w2, eta, chunk, causal=True, *, z=None, w1_out=None
                              w1_out.data_ptr() if want else None,
                              w2_out.data_ptr() if want else None,
                              B, H, T, d, dh, int(chunk), int(bool(causal)), float(eta),
+                             _rates(eta_tok, B, H, T, q.device),
                              _io_dtype(q), _stream(q.device, stream))
     _check(rc)
     return (z, w1_out, w2_out) if want else z

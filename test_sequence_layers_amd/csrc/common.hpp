@@ -37,6 +37,7 @@ struct LinearArgs {
   float* w_out;
   int B, H, T, d, chunk, causal;
   float eta;
+  const float* eta_tok;  // per-token rate factors [B][H][T] (rate eta * eta_tok[t]) or null
 };
 
 struct MlpArgs {
@@ -51,6 +52,7 @@ struct MlpArgs {
   float* w2_out;
   int B, H, T, d, dh, chunk, causal;
   float eta;
+  const float* eta_tok;  // per-token rate factors [B][H][T] (rate eta * eta_tok[t]) or null
 };
 
 // Host-side launchers (return a hipError_t; argument checks are done by the caller).

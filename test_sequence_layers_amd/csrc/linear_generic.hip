@@ -7,11 +7,16 @@
 // Sun et al. 2024, section 1.2.2); z_t = W_t q_t (blog page "TTT: Test-Time Training",
 // general form).
 //
+// With per-token rates (eta_t = eta * eta_tok[t]; the "Fast weights" page writes the
+// step with a per-step rate, and the wmrh.cn summary, section 2.2.3, makes it a function
+// of the token) each token's gradient carries its own rate.
+//
 // The chunk is walked in sub-blocks of S = 16 tokens.  Two fp32 states live in LDS:
 // Wc, the chunk-start weights every residual uses, and Wn, the weights after all earlier
-// sub-blocks of the chunk.  For a sub-block with residuals R = K Wc^T - V,
-//   z_t = Wn q_t - eta * sum_{s <= t in the sub-block} (q_t . k_s) r_s
-//   Wn  -= eta * R^T K,
+// sub-blocks of the chunk.  For a sub-block with rate-scaled residuals
+// R = diag(eta_t) (K Wc^T - V),
+//   z_t = Wn q_t - sum_{s <= t in the sub-block} (q_t . k_s) r_s
+//   Wn  -= R^T K,
 // and at the end of a chunk Wc <- Wn.  This equals the per-token recurrence up to
 // floating-point order.  With causal = 0 the training pass writes no output and a second
 // pass computes z_t = W_final q_t.
@@ -45,6 +50,7 @@ __global__ __launch_bounds__(kThreads) void linear_generic_kernel(LinearArgs a) 
   const IO* v = static_cast<const IO*>(a.v) + tok0;
   IO* z = static_cast<IO*>(a.z) + tok0;
   const float* w0 = a.w0 + bi * a.w0_batch_stride + static_cast<long long>(hi) * D * D;
+  const float* etok = a.eta_tok ? a.eta_tok + static_cast<size_t>(chain) * T : nullptr;
 
   for (int e = tid; e < D * D; e += kThreads) {
     const float w = w0[e];
@@ -67,13 +73,14 @@ __global__ __launch_bounds__(kThreads) void linear_generic_kernel(LinearArgs a) 
         Vs[t][j] = in ? to_f32(v[off]) : 0.0f;
       }
       __syncthreads();
-      // Residuals at the chunk-start weights, and the causal in-block scores.
+      // Rate-scaled residuals at the chunk-start weights, and the causal in-block scores.
       for (int e = tid; e < kSub * D; e += kThreads) {
         const int t = e / D, i = e % D;
         float acc = 0.0f;
 #pragma unroll 16
         for (int j = 0; j < D; ++j) acc += Ks[t][j] * Wc[i][j];
-        Rs[t][i] = t < n ? acc - Vs[t][i] : 0.0f;
+        const float rate = t < n ? (etok ? eta * etok[s0 + t] : eta) : 0.0f;
+        Rs[t][i] = t < n ? rate * (acc - Vs[t][i]) : 0.0f;
       }
       if (a.causal) {
         for (int e = tid; e < kSub * kSub; e += kThreads) {
@@ -96,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void linear_generic_kernel(LinearArgs a) 
           for (int j = 0; j < D; ++j) acc += Qs[t][j] * Wn[i][j];
           float corr = 0.0f;
           for (int s = 0; s <= t; ++s) corr += Ps[t][s] * Rs[s][i];
-          z[static_cast<size_t>(s0 + t) * D + i] = from_f32<IO>(acc - eta * corr);
+          z[static_cast<size_t>(s0 + t) * D + i] = from_f32<IO>(acc - corr);
         }
         __syncthreads();
       }
@@ -104,7 +111,7 @@ __global__ __launch_bounds__(kThreads) void linear_generic_kernel(LinearArgs a) 
         const int i = e / D, j = e % D;
         float acc = 0.0f;
         for (int t = 0; t < n; ++t) acc += Rs[t][i] * Ks[t][j];
-        Wn[i][j] -= eta * acc;
+        Wn[i][j] -= acc;
       }
       __syncthreads();
     }

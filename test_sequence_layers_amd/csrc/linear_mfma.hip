@@ -91,7 +91,8 @@ constexpr int kHalfCols = kD / kSplit;  // output rows (= V columns) per workgro
 // LDS ring of kRing slots, published kGroup chunks per barrier.  Slot layout: Q tile at 0
 // and K tile at 2 KB (16 rows of 128 bytes, 16-byte pieces swizzled by row), this
 // workgroup's 32 V columns at 4 KB (16 rows of 64 bytes, swizzled), and for the delta
-// rule the chunk's Tm^T (512 bytes, row-major) at 5 KB.  The
+// rule the chunk's Tm^T (512 bytes, row-major) after that; with per-token rates, the
+// chunk's 16 rate factors (64 bytes) sit between V and Tm^T.  The
 // loader issues kLoads direct-to-LDS loads per chunk; its waits before barriers are
 // bounded by the 6-bit vmcnt (a smaller count than needed only waits longer).
 // Barrier b publishes the chunks that the chain waves read after it (up to kGroup b +
@@ -99,13 +100,16 @@ constexpr int kHalfCols = kD / kSplit;  // output rows (= V columns) per workgro
 // to kGroup b - kGroup - 1); the loader then refills up to kRing chunks past that.
 constexpr int kGroup = 4;
 constexpr int kVOff = 2 * kTileBytes;
-constexpr int kTmOff = kVOff + kB * kHalfCols * 2;
+constexpr int kEtaOff = kVOff + kB * kHalfCols * 2;  // per-token rate factors (64 bytes)
+constexpr int kEtaBytes = kB * 4;
+constexpr int kTmOffNoRates = kEtaOff;
+constexpr int kTmOffRates = kEtaOff + kEtaBytes;
 // (Plain constants: a dependent static member passed to the direct-to-LDS load builtin
 // kept the host compiler from emitting the kernel's launch stub.)
-template <bool kDelta> struct Ring {
+template <bool kDelta, bool kTok> struct Ring {
   static constexpr int kRing = 24;
-  static constexpr int kLoads = kDelta ? 6 : 5;
-  static constexpr int kSlotBytes = kTmOff + (kDelta ? kTmBytes : 0);
+  static constexpr int kLoads = 5 + (kDelta ? 1 : 0) + (kTok ? 1 : 0);
+  static constexpr int kSlotBytes = (kTok ? kTmOffRates : kTmOffNoRates) + (kDelta ? kTmBytes : 0);
   static constexpr int clampw(int nchunks) {
     return nchunks * kLoads < 64 ? nchunks * kLoads : (63 / kLoads) * kLoads;
   }
@@ -165,6 +169,7 @@ struct PairRegs {
   u32x2 v[2];      // chunk e: V[n][i0 + 4 g .. + 3]
   u32x2 kt[2][4];  // chunk e, tile t: K[4 g + s][j_t(n)], s = 0..3
   u32x2 tm[2];     // delta rule: chunk e's Tm[n][4 g .. 4 g + 3] (from the stored Tm^T)
+  float4_t et[2];  // per-token rates: chunk e's factors of tokens 4 g .. 4 g + 3
 };
 
 // Per-lane byte offsets inside a slot, fixed for the whole kernel.
@@ -173,12 +178,14 @@ struct LaneOffsets {
   int kt0, kt1;  // transposing reads: row 4 g + n / 4, pieces n % 4 and 4 + n % 4
   int vv;        // V row n, columns i0 - 32 part + 4 g
   int tm;        // Tm row n, columns 4 g
+  int et;        // rate factors of tokens 4 g .. 4 g + 3
 };
 
 // Ring reads of the chain waves.  Only chain waves run this, and their code path issues no
 // direct-to-LDS loads, so the compiler's own lgkmcnt waits order the reads.
-template <bool kDelta>
+template <bool kDelta, bool kTok>
 __device__ __forceinline__ void read_pair(PairRegs& r, const lds_char* s0, const lds_char* s1, const LaneOffsets& o) {
+  constexpr int kTmOff = kTok ? kTmOffRates : kTmOffNoRates;
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const lds_char* slot = e ? s1 : s0;
@@ -191,6 +198,7 @@ __device__ __forceinline__ void read_pair(PairRegs& r, const lds_char* s0, const
     r.kt[e][2] = lds_load_tr(k + o.kt1);
     r.kt[e][3] = lds_load_tr(k + o.kt1 + 8);
     if (kDelta) r.tm[e] = lds_load_tr(slot + kTmOff + o.tm);
+    if (kTok) r.et[e] = lds_load<float4_t>(slot + kEtaOff + o.et);
   }
 }
 
@@ -226,6 +234,12 @@ __device__ __forceinline__ u32x2 neg_eta_bf16(const float4_t& r, float neta) {
   const u32x2 x = {pack_bf16(neta * r[0], neta * r[1]), pack_bf16(neta * r[2], neta * r[3])};
   return x;
 }
+// -eta_t R with a rate factor per row (token 4 g + e)
+__device__ __forceinline__ u32x2 neg_eta_bf16(const float4_t& r, float neta, const float4_t& et) {
+  const u32x2 x = {pack_bf16((neta * et[0]) * r[0], (neta * et[1]) * r[1]),
+                   pack_bf16((neta * et[2]) * r[2], (neta * et[3]) * r[3])};
+  return x;
+}
 
 // Chunks c, c + 1 (c even) of the state recursion, from W = W_c:
 //   R_c     = K_c W^T - V_c
@@ -235,7 +249,7 @@ __device__ __forceinline__ u32x2 neg_eta_bf16(const float4_t& r, float neta) {
 // (delta rule: each R is Tm times the bracket).  Only the second R waits for the first; the
 // state update and its bf16 copy happen once per pair.  Hands off the bf16 W_c and
 // -eta R_c, -eta R_{c+1} to the output wave (pair area h; lw = 16 lane, lr = 8 lane).
-template <bool kDelta>
+template <bool kDelta, bool kTok>
 __device__ __forceinline__ void pair_step(WState& w, const PairRegs& r, const LaneConst& lc, lds_char* h, int lw,
                                           int lr) {
   const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -250,12 +264,12 @@ __device__ __forceinline__ void pair_step(WState& w, const PairRegs& r, const La
   float4_t mt = MFMA32(bf8(r.k[0][0]), bf8(r.k[1][0]), zero, 0, 0, 0);
   mt = MFMA32(bf8(r.k[0][1]), bf8(r.k[1][1]), mt, 0, 0, 0);
   if (kDelta) r0 = tm_apply(r.tm[0], r0);
-  const u32x2 rn0 = neg_eta_bf16(r0, lc.neta);
+  const u32x2 rn0 = kTok ? neg_eta_bf16(r0, lc.neta, r.et[0]) : neg_eta_bf16(r0, lc.neta);
   const u32x4 mpad = {pack_bf16(mt[0], mt[1]), pack_bf16(mt[2], mt[3]), 0u, 0u};
   const u32x4 rpad0 = {rn0.x, rn0.y, 0u, 0u};
   float4_t r1 = MFMA32(bf8(mpad), bf8(rpad0), a1, 0, 0, 0);
   if (kDelta) r1 = tm_apply(r.tm[1], r1);
-  const u32x2 rn1 = neg_eta_bf16(r1, lc.neta);
+  const u32x2 rn1 = kTok ? neg_eta_bf16(r1, lc.neta, r.et[1]) : neg_eta_bf16(r1, lc.neta);
   lds_store<u32x4>(h + lw, wb0u);
   lds_store<u32x4>(h + kHandW1 + lw, wb1u);
   lds_store<u32x2>(h + kHandR0 + lr, rn0);
@@ -334,10 +348,11 @@ __device__ __forceinline__ void lds_barrier() {
   __asm__ __volatile__("" ::: "memory");
 }
 
-template <bool kDelta>
+template <bool kDelta, bool kTok>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) void linear_mfma_kernel(
     LinearArgs a, const bf16* tmat) {
-  using RG = Ring<kDelta>;
+  using RG = Ring<kDelta, kTok>;
+  constexpr int kTmOff = kTok ? kTmOffRates : kTmOffNoRates;
   constexpr int kRing = RG::kRing;
   __shared__ __attribute__((aligned(16))) char lds_mem[kRing * RG::kSlotBytes + kHandBytes];
   lds_char* ring = (lds_char*)(lds_mem);
@@ -377,6 +392,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
     const int vglob = vrow * 128 + part * (kHalfCols * 2) + (((lane & 3) ^ ((vrow >> 1) & 3)) * 16);
     const char* tsrc = reinterpret_cast<const char*>(tmat) +
                        (kDelta ? static_cast<size_t>(chain) * nchunks * kTmBytes : 0);
+    const char* esrc = kTok ? reinterpret_cast<const char*>(a.eta_tok + static_cast<size_t>(chain) * T) : nullptr;
     auto issue = [&](int c) {
       const int off = c * kTileBytes;
       lds_char* dst = ring + (c % kRing) * RG::kSlotBytes;
@@ -388,6 +404,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dst + kTileBytes + 1024, 16, lglob + 1024, 0, 0, kNT);
       const __amdgpu_buffer_rsrc_t rv = chunk_rsrc(vsrc + off, seq_bytes - off);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst + kVOff, 16, vglob, 0, 0, kNT);
+      if (kTok && lane < kB) {
+        // rate factors of chunk c's tokens: 4 bytes per lane (zeros past the end)
+        const __amdgpu_buffer_rsrc_t re = chunk_rsrc(esrc + c * kEtaBytes, T * 4 - c * kEtaBytes);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(re, dst + kEtaOff, 4, lane * 4, 0, 0, kNT);
+      }
       if (kDelta && lane < 32) {
         // Tm^T of chunk c: 512 bytes, 16 per lane (zeros past the last chunk)
         const __amdgpu_buffer_rsrc_t rs =
@@ -485,13 +506,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   o.kt1 = swz(4 * g + (n >> 2), 4 + (n & 3)) * 16;
   o.vv = vswz(n, 2 * wv + (g >> 1)) * 16 + 8 * (g & 1);
   o.tm = (4 * g + (n >> 2)) * 32 + 8 * (n & 3);
+  o.et = 16 * g;
 
   // Pair step p computes chunks 2p, 2p + 1 from registers read in step p - 1 while reading
   // chunks 2p + 2, 2p + 3.  Chunks past the end read as zeros and leave the state unchanged.
   lds_char* hw = hand + wv * kHandWave;
   lds_barrier();  // barrier 0: chunks 0 .. kGroup + 1 published
   PairRegs ra, rb;
-  read_pair<kDelta>(ra, ring, ring + RG::kSlotBytes, o);
+  read_pair<kDelta, kTok>(ra, ring, ring + RG::kSlotBytes, o);
   for (int gbase = 0; gbase < ngroups; gbase += kRing / kGroup) {
 #pragma unroll
     for (int gg = 0; gg < kRing / kGroup; ++gg) {
@@ -506,8 +528,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
         const PairRegs& cur = (x & 2) ? rb : ra;
         PairRegs& nxt = (x & 2) ? ra : rb;
         __builtin_amdgcn_sched_barrier(0);  // keep steps apart (register pressure)
-        read_pair<kDelta>(nxt, ring + s2 * RG::kSlotBytes, ring + s3 * RG::kSlotBytes, o);
-        pair_step<kDelta>(wacc, cur, lc, hg + (x / 2) * kHandPair, lw, lr);
+        read_pair<kDelta, kTok>(nxt, ring + s2 * RG::kSlotBytes, ring + s3 * RG::kSlotBytes, o);
+        pair_step<kDelta, kTok>(wacc, cur, lc, hg + (x / 2) * kHandPair, lw, lr);
       }
     }
   }
@@ -548,14 +570,20 @@ bool linear_mfma_supported(const LinearArgs& a, bool bf16_io) {
 hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s) {
   const long long nblocks = mfma_grid(a);
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(linear_mfma_kernel<false>, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads),
-                     0, s, a, static_cast<const bf16*>(nullptr));
+  if (a.eta_tok)
+    hipLaunchKernelGGL((linear_mfma_kernel<false, true>), dim3(static_cast<unsigned>(nblocks)), dim3(kThreads),
+                       0, s, a, static_cast<const bf16*>(nullptr));
+  else
+    hipLaunchKernelGGL((linear_mfma_kernel<false, false>), dim3(static_cast<unsigned>(nblocks)), dim3(kThreads),
+                       0, s, a, static_cast<const bf16*>(nullptr));
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------------------------ delta rule
 
-// Tm = (I + eta stril(K K^T))^-1 for every chunk of every chain, stored transposed in bf16:
+// Tm = (I + eta stril(K K^T) diag(eta_tok))^-1 for every chunk of every chain (diag(eta_tok)
+// = I without per-token rates: the write of token s carries its own rate, so column s of
+// the strict lower triangle is scaled by it), stored transposed in bf16:
 // [chain][chunk][j][t] = Tm[t][j] (row j of the stored tile is column j of Tm).  One wave
 // per 4 chunks: the wave forms the Gram matrix G = K K^T of each chunk with two MFMAs (K
 // rows loaded straight into the operand layout; the A and B operands of K K^T are the same
@@ -566,7 +594,8 @@ hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s) {
 constexpr int kTmWaves = 4;
 constexpr int kTmChunksPerWave = 4;
 __global__ __launch_bounds__(64 * kTmWaves) void delta_tmat_kernel(const bf16* __restrict__ k, bf16* __restrict__ tmt,
-                                                                 int T, int nchunks, long long total, float eta) {
+                                                                 int T, int nchunks, long long total, float eta,
+                                                                 const float* __restrict__ etok) {
   __shared__ float ls[kTmWaves][kTmChunksPerWave][kB][kB];
   const int wv = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -578,9 +607,16 @@ __global__ __launch_bounds__(64 * kTmWaves) void delta_tmat_kernel(const bf16* _
   for (int q = 0; q < kTmChunksPerWave; ++q) {
     const long long id = id0 + q;  // uniform in the wave
     float4_t gacc = zero;
+    float rate = eta;
     if (id < total) {
       const long long chain = id / nchunks;
       const int c = static_cast<int>(id - chain * nchunks);
+      if (etok) {  // uniform: rate factor of token n of the chunk (zero past T)
+        const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(etok + static_cast<size_t>(chain) * T + static_cast<size_t>(c) * kB), 0,
+            (T - c * kB) * 4, 0x00020000);
+        rate = eta * __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(re, n * 4, 0, 0));
+      }
       const bf16* kc = k + (static_cast<size_t>(chain) * T + static_cast<size_t>(c) * kB) * kD;
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(kc), 0, (T - c * kB) * kD * 2, 0x00020000);
@@ -590,9 +626,10 @@ __global__ __launch_bounds__(64 * kTmWaves) void delta_tmat_kernel(const bf16* _
       gacc = MFMA32(bf8(k0), bf8(k0), zero, 0, 0, 0);
       gacc = MFMA32(bf8(k1), bf8(k1), gacc, 0, 0, 0);
     }
-    // lane (g, n) holds G[4 g + e][n]; keep the strict lower triangle, scaled by eta
+    // lane (g, n) holds G[4 g + e][n]; keep the strict lower triangle, scaled by the rate of
+    // token n (column)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ls[wv][q][4 * g + e][n] = (n < 4 * g + e) ? eta * gacc[e] : 0.0f;
+    for (int e = 0; e < 4; ++e) ls[wv][q][4 * g + e][n] = (n < 4 * g + e) ? rate * gacc[e] : 0.0f;
   }
   __syncthreads();
   // lane (q, j): column j of chunk q
@@ -644,13 +681,17 @@ hipError_t launch_delta_fast(const LinearArgs& a, void* workspace, hipStream_t s
   if (nchains > 0x7fffffffLL || nblocks > 0x7fffffffLL) return hipErrorInvalidValue;
   bf16* tm = static_cast<bf16*>(workspace);
   hipLaunchKernelGGL(delta_tmat_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(64 * kTmWaves), 0, s,
-                     static_cast<const bf16*>(a.k), tm, a.T, nchunks, total, a.eta);
+                     static_cast<const bf16*>(a.k), tm, a.T, nchunks, total, a.eta, a.eta_tok);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long nmain = mfma_grid(a);
   if (nmain > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(linear_mfma_kernel<true>, dim3(static_cast<unsigned>(nmain)), dim3(kThreads),
-                     0, s, a, static_cast<const bf16*>(tm));
+  if (a.eta_tok)
+    hipLaunchKernelGGL((linear_mfma_kernel<true, true>), dim3(static_cast<unsigned>(nmain)), dim3(kThreads),
+                       0, s, a, static_cast<const bf16*>(tm));
+  else
+    hipLaunchKernelGGL((linear_mfma_kernel<true, false>), dim3(static_cast<unsigned>(nmain)), dim3(kThreads),
+                       0, s, a, static_cast<const bf16*>(tm));
   return hipGetLastError();
 }
 

@@ -7,13 +7,17 @@
 // Per token, with u = W1 k, a = SiLU(u), r = W2 a - v:
 //   dW2 = r a^T,   dW1 = ((W2^T r) * SiLU'(u)) k^T.
 //
+// With per-token rates (eta_t = eta * eta_tok[t]; "Fast weights" page, opening formula;
+// wmrh.cn summary, section 2.2.3) each token's gradients carry its own rate: r and du
+// below are scaled by eta_t.
+//
 // The chunk is walked in sub-blocks of S = 16 tokens.  The states are kept in a global
 // workspace (4 dh d floats per chain): W1c/W2c, the chunk-start weights every gradient is
 // taken at, and W1n/W2n, the weights after all earlier sub-blocks of the chunk.  For a
 // sub-block, every hidden pre-activation of a query is linear in W1, so
-//   u^q_t = W1n q_t - eta * sum_{s<=t} (q_t . k_s) du_s,   a^q_t = SiLU(u^q_t),
-//   z_t   = W2n a^q_t - eta * sum_{s<=t} (a^q_t . a_s) r_s,
-// then W1n -= eta dU^T K and W2n -= eta R^T A; at the end of a chunk W1c/W2c <- W1n/W2n.
+//   u^q_t = W1n q_t - sum_{s<=t} (q_t . k_s) du_s,   a^q_t = SiLU(u^q_t),
+//   z_t   = W2n a^q_t - sum_{s<=t} (a^q_t . a_s) r_s,
+// then W1n -= dU^T K and W2n -= R^T A; at the end of a chunk W1c/W2c <- W1n/W2n.
 #include "common.hpp"
 
 namespace ttt {
@@ -65,6 +69,7 @@ __global__ __launch_bounds__(kThreads) void mlp_generic_kernel(MlpArgs a, float*
   IO* z = static_cast<IO*>(a.z) + tok0;
   const float* w1i = a.w1 + bi * a.w_batch_stride + static_cast<long long>(hi) * hd;
   const float* w2i = a.w2 + bi * a.w_batch_stride + static_cast<long long>(hi) * hd;
+  const float* etok = a.eta_tok ? a.eta_tok + static_cast<size_t>(chain) * T : nullptr;
   float* W1c = ws + static_cast<size_t>(chain) * 4 * hd;  // [h][D]
   float* W2c = W1c + hd;                                  // [D][h]
   float* W1n = W2c + hd;
@@ -101,12 +106,13 @@ __global__ __launch_bounds__(kThreads) void mlp_generic_kernel(MlpArgs a, float*
         DU[e] = in ? dsilu_(u) : 0.0f;
       }
       __syncthreads();
-      // second layer and residual: r = W2c a - v
+      // second layer and rate-scaled residual: r = eta_t (W2c a - v)
       for (int e = tid; e < kSub * D; e += kThreads) {
         const int t = e / D, i = e % D;
         float o = 0.0f;
         for (int c = 0; c < h; ++c) o += Ab[t * h + c] * W2c[static_cast<size_t>(i) * h + c];
-        Rs[e] = t < n ? o - Vs[e] : 0.0f;
+        const float rate = t < n ? (etok ? eta * etok[s0 + t] : eta) : 0.0f;
+        Rs[e] = t < n ? rate * (o - Vs[e]) : 0.0f;
       }
       __syncthreads();
       // backward to the hidden pre-activation: du = (W2c^T r) * SiLU'(u)
@@ -134,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void mlp_generic_kernel(MlpArgs a, float*
           for (int j = 0; j < D; ++j) u += Qs[t * D + j] * W1n[static_cast<size_t>(c) * D + j];
           float corr = 0.0f;
           for (int s = 0; s <= t && s < kSub; ++s) corr += Ps[t * kSub + s] * DU[s * h + c];
-          AQ[e] = t < n ? silu_(u - eta * corr) : 0.0f;
+          AQ[e] = t < n ? silu_(u - corr) : 0.0f;
         }
         __syncthreads();
         for (int e = tid; e < kSub * kSub; e += kThreads) {
@@ -152,22 +158,22 @@ __global__ __launch_bounds__(kThreads) void mlp_generic_kernel(MlpArgs a, float*
           for (int c = 0; c < h; ++c) o += AQ[t * h + c] * W2n[static_cast<size_t>(i) * h + c];
           float corr = 0.0f;
           for (int s = 0; s <= t; ++s) corr += P2[t * kSub + s] * Rs[s * D + i];
-          z[static_cast<size_t>(s0 + t) * D + i] = from_f32<IO>(o - eta * corr);
+          z[static_cast<size_t>(s0 + t) * D + i] = from_f32<IO>(o - corr);
         }
         __syncthreads();
       }
-      // W1n -= eta dU^T K ; W2n -= eta R^T A
+      // W1n -= dU^T K ; W2n -= R^T A  (rates are in dU and R)
       for (size_t e = tid; e < hd; e += kThreads) {
         const int c = static_cast<int>(e / D), j = static_cast<int>(e % D);
         float acc = 0.0f;
         for (int t = 0; t < n; ++t) acc += DU[t * h + c] * Ks[t * D + j];
-        W1n[e] -= eta * acc;
+        W1n[e] -= acc;
       }
       for (size_t e = tid; e < hd; e += kThreads) {
         const int i = static_cast<int>(e / h), c = static_cast<int>(e % h);
         float acc = 0.0f;
         for (int t = 0; t < n; ++t) acc += Rs[t * D + i] * Ab[t * h + c];
-        W2n[e] -= eta * acc;
+        W2n[e] -= acc;
       }
       __syncthreads();
     }

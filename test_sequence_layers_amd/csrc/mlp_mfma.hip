@@ -7,6 +7,8 @@
 //   U = K W1^T, A = SiLU(U), S = SiLU'(U), R = A W2^T - V,
 //   dU = (R W2) * S                                   (gradient of the hidden layer)
 //   W1 <- W1 - eta dU^T K,  W2 <- W2 - eta R^T A        (sum of the chunk's gradients)
+// (with per-token rates, eta times a row of R or dU is that token's rate: "Fast weights"
+// page, opening formula; wmrh.cn summary, section 2.2.3)
 // and, because every hidden pre-activation of a query is linear in W1 and the output is
 // linear in W2, the causal outputs with the in-chunk updates are
 //   U_q = Q W1^T - eta tril(Q K^T) dU,  A_q = SiLU(U_q),
@@ -121,16 +123,18 @@ struct ChunkIn {
   u32x4 qb0, qb1;     // Q[n][16 g + 0..15]                          (B operands over j)
   uint32_t kt[4][2];  // kt[e][h] = K[4 g + e][c0 + 8 h .. + 1], c0 = 16 (n / 4) + 2 (n % 4)
   uint32_t vv;        // V[t = tid / 32][2 (tid % 32) .. + 1]         (for R = O - V)
+  float et;           // rate factor of token tid / 32 (1 without per-token rates)
 };
 
 struct Offsets {
   int row;         // n * 128 + 32 g
   int kt[4];       // (4 g + e) * 128 + 2 c0
   int vv;          // (tid / 32) * 128 + 4 (tid % 32)
+  int et;          // (tid / 32) * 4
 };
 
 __device__ __forceinline__ void load_chunk(ChunkIn& r, const char* q, const char* k, const char* v,
-                                           int c, int seq_bytes, const Offsets& o) {
+                                           const float* etok, int c, int seq_bytes, const Offsets& o) {
   const int off = c * kTileBytes;
   const __amdgpu_buffer_rsrc_t rq = chunk_rsrc(q + off, seq_bytes - off);
   const __amdgpu_buffer_rsrc_t rk = chunk_rsrc(k + off, seq_bytes - off);
@@ -145,6 +149,12 @@ __device__ __forceinline__ void load_chunk(ChunkIn& r, const char* q, const char
     r.kt[e][1] = __builtin_amdgcn_raw_buffer_load_b32(rk, o.kt[e] + 16, 0, 0);
   }
   r.vv = __builtin_amdgcn_raw_buffer_load_b32(rv, o.vv, 0, 0);
+  r.et = 1.0f;
+  if (etok) {  // uniform: per-token rate factors of the chunk, 4 bytes per token
+    const int eoff = c * kB * 4;
+    const __amdgpu_buffer_rsrc_t re = chunk_rsrc(etok + c * kB, (seq_bytes >> 5) - eoff);
+    r.et = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(re, o.et, 0, 0));
+  }
 }
 
 struct State {
@@ -201,6 +211,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const char* k = reinterpret_cast<const char*>(static_cast<const bf16*>(a.k) + tok0);
   const char* v = reinterpret_cast<const char*>(static_cast<const bf16*>(a.v) + tok0);
   char* z = reinterpret_cast<char*>(static_cast<bf16*>(a.z) + tok0);
+  const float* etok = a.eta_tok ? a.eta_tok + static_cast<size_t>(chain) * T : nullptr;
   const size_t hd = static_cast<size_t>(kH) * kD;
   const float* w1g = a.w1 + bi * a.w_batch_stride + static_cast<long long>(hi) * hd;
   const float* w2g = a.w2 + bi * a.w_batch_stride + static_cast<long long>(hi) * hd;
@@ -243,6 +254,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int rt = tid >> 5;          // reduction role: row t and 2 outputs
   const int ri = 2 * (tid & 31);
   o.vv = rt * 128 + 2 * ri;
+  o.et = rt * 4;
   const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
   typedef float float2_t __attribute__((ext_vector_type(2)));
   const float2_t zero2 = {0.0f, 0.0f};
@@ -261,7 +273,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   // One chunk: its operands in cur, the next chunk's loaded into nxt.
   auto step = [&](const ChunkIn& cur, ChunkIn& nxt, int c) {
-    load_chunk(nxt, q, k, v, c + 1, seq_bytes, o);  // prefetch (zeros past the end)
+    load_chunk(nxt, q, k, v, etok, c + 1, seq_bytes, o);  // prefetch (zeros past the end)
     const bf16x8_t ka0 = bf(cur.ka0), ka1 = bf(cur.ka1), qb0 = bf(cur.qb0), qb1 = bf(cur.qb1);
 
     // bf16 copies of this wave's chunk-start state
@@ -314,14 +326,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     barrier();
     // previous chunk's Z (its partials were written before this barrier)
     if (c > 0) reduce_store_z(c - 1);
-    // -eta R = -eta (sum of partials - V), to LDS in bf16 as [t][i] and [i][t]
+    // -eta_t R = -eta_t (sum of partials - V), to LDS in bf16 as [t][i] and [i][t]
     {
       float2_t s2 = zero2;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) s2 += lds_load<float2_t>(opart, ((w * kB + rt) * kRow + ri) * 4);
       const uint32_t vb = cur.vv;
-      const uint32_t rp = pack_bf16((s2[0] - __builtin_bit_cast(float, vb << 16)) * (-eta),
-                                    (s2[1] - __builtin_bit_cast(float, vb & 0xFFFF0000u)) * (-eta));
+      const float nrate = -eta * cur.et;
+      const uint32_t rp = pack_bf16((s2[0] - __builtin_bit_cast(float, vb << 16)) * nrate,
+                                    (s2[1] - __builtin_bit_cast(float, vb & 0xFFFF0000u)) * nrate);
       lds_store<uint32_t>(rrb, (rt * kRRow + ri) * 2, rp);
       lds_store<uint16_t>(rtb, (ri * kTRow + rt) * 2, static_cast<uint16_t>(rp));
       lds_store<uint16_t>(rtb, ((ri + 1) * kTRow + rt) * 2, static_cast<uint16_t>(rp >> 16));
@@ -408,7 +421,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   };
 
   ChunkIn ca, cb;
-  load_chunk(ca, q, k, v, 0, seq_bytes, o);
+  load_chunk(ca, q, k, v, etok, 0, seq_bytes, o);
   for (int c = 0; c < nchunks; ++c) {
     step(ca, cb, c);
     ca = cb;
@@ -453,7 +466,7 @@ bool mlp_fast_supported(const MlpArgs& a, bool bf16_io) {
                        (a.w2_out == nullptr || al(a.w2_out, 16));
   const bool fits = static_cast<long long>(a.T) * kD * 2 + 4LL * kTileBytes < 0x7fffffffLL;
   return bf16_io && a.d == kD && a.dh == kH && a.chunk == kB && a.causal == 1 && a.T > 0 &&
-         aligned && fits;
+         aligned && fits && (a.eta_tok == nullptr || al(a.eta_tok, 4));
 }
 
 hipError_t launch_mlp_fast(const MlpArgs& a, hipStream_t s) {

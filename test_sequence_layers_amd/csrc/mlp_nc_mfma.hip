@@ -6,6 +6,8 @@
 // every query; inner model: section 2, 2-layer SiLU MLP).  With U = K W1^T, A = SiLU(U),
 // S = SiLU'(U), R = A W2^T - V and dU = (R W2) * S over all N tokens:
 //   W1' = W1 - eta dU^T K,   W2' = W2 - eta R^T A,   Z = SiLU(Q W1'^T) W2'^T.
+// With per-token rates each row t of R (and so of dU) is scaled by token t's rate factor
+// ("Fast weights" page, opening formula; wmrh.cn summary, section 2.2.3).
 //
 // Mapping.  One workgroup of kNcWaves = 2 waves per (batch, head) chain; wave w takes the
 // 16-token tiles w, w + 2, w + 4, ...  Pass 1 streams its tiles (the next tile's loads are
@@ -96,9 +98,10 @@ struct KvTile {
   u32x4 ka0, ka1;     // K[t = n][16 g + 0..7], K[n][16 g + 8..15]
   uint32_t kt[4][2];  // kt[e][h] = K[4 g + e][c0 + 8 h .. + 1]
   u32x2 vv[4];        // V[t = n][16 it + 4 g .. + 3]
+  float et;           // rate factor of token n (1 without per-token rates)
 };
-__device__ __forceinline__ void load_kv(KvTile& r, const char* k, const char* v, int tt, int seq_bytes,
-                                        int row, const int (&kto)[4], int g, int n) {
+__device__ __forceinline__ void load_kv(KvTile& r, const char* k, const char* v, const float* etok, int tt,
+                                        int seq_bytes, int row, const int (&kto)[4], int g, int n) {
   const int off = tt * kTileBytes;
   const __amdgpu_buffer_rsrc_t rk = tile_rsrc(k + off, seq_bytes - off);
   const __amdgpu_buffer_rsrc_t rv = tile_rsrc(v + off, seq_bytes - off);
@@ -112,6 +115,11 @@ __device__ __forceinline__ void load_kv(KvTile& r, const char* k, const char* v,
 #pragma unroll
   for (int it = 0; it < 4; ++it)
     r.vv[it] = __builtin_amdgcn_raw_buffer_load_b64(rv, n * 128 + 2 * (16 * it + 4 * g), 0, 0);
+  r.et = 1.0f;
+  if (etok) {  // uniform: 4 bytes per token, zero past T
+    const __amdgpu_buffer_rsrc_t re = tile_rsrc(etok + tt * kTile, (seq_bytes >> 5) - tt * kTile * 4);
+    r.et = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(re, n * 4, 0, 0));
+  }
 }
 
 // fp32 weight rows staged in LDS, padded to 68 floats so that the 16-byte reads of 16
@@ -140,6 +148,7 @@ __global__ __launch_bounds__(64 * kNcWaves) __attribute__((amdgpu_waves_per_eu(1
   const char* k = reinterpret_cast<const char*>(static_cast<const bf16*>(a.k) + tok0);
   const char* v = reinterpret_cast<const char*>(static_cast<const bf16*>(a.v) + tok0);
   char* z = reinterpret_cast<char*>(static_cast<bf16*>(a.z) + tok0);
+  const float* etok = a.eta_tok ? a.eta_tok + static_cast<size_t>(chain) * T : nullptr;
   const size_t hd = static_cast<size_t>(kH) * kD;
   const float* w1g = a.w1 + bi * a.w_batch_stride + static_cast<long long>(hi) * hd;
   const float* w2g = a.w2 + bi * a.w_batch_stride + static_cast<long long>(hi) * hd;
@@ -158,8 +167,8 @@ __global__ __launch_bounds__(64 * kNcWaves) __attribute__((amdgpu_waves_per_eu(1
   // K/V tiles are prefetched two tiles ahead (the wave's tiles i and i + 1 are in flight
   // while it computes tile i - 1)
   KvTile cur, nx1, nx2;
-  if (wv < ntiles) load_kv(cur, k, v, wv, seq_bytes, row, kto, g, n);
-  if (wv + kNcWaves < ntiles) load_kv(nx1, k, v, wv + kNcWaves, seq_bytes, row, kto, g, n);
+  if (wv < ntiles) load_kv(cur, k, v, etok, wv, seq_bytes, row, kto, g, n);
+  if (wv + kNcWaves < ntiles) load_kv(nx1, k, v, etok, wv + kNcWaves, seq_bytes, row, kto, g, n);
   {
     // W1 and W2 (64 x 64 fp32 each) into LDS: thread x copies 16-byte pieces x, x + 128, ...
     const int tid = threadIdx.x;
@@ -236,7 +245,7 @@ __global__ __launch_bounds__(64 * kNcWaves) __attribute__((amdgpu_waves_per_eu(1
       g2t[i][j] = zero;
     }
   for (int tt = wv; tt < ntiles; tt += kNcWaves) {
-    if (tt + 2 * kNcWaves < ntiles) load_kv(nx2, k, v, tt + 2 * kNcWaves, seq_bytes, row, kto, g, n);
+    if (tt + 2 * kNcWaves < ntiles) load_kv(nx2, k, v, etok, tt + 2 * kNcWaves, seq_bytes, row, kto, g, n);
     const bf16x8_t ka0 = bf(cur.ka0), ka1 = bf(cur.ka1);
     // U = K W1^T (rows t); A = SiLU(U), S = SiLU'(U)
     float4_t act[4], sd[4];
@@ -256,7 +265,8 @@ __global__ __launch_bounds__(64 * kNcWaves) __attribute__((amdgpu_waves_per_eu(1
 #pragma unroll
     for (int aa = 0; aa < 4; ++aa) actT[aa] = mfma(pad_op(act[aa]), eye, zero);
     const bf16x8_t atb0 = pair_op(actT[0], actT[1]), atb1 = pair_op(actT[2], actT[3]);
-    // R^T = W2 A^T - V^T (rows output tile it, cols t)
+    // R^T = W2 A^T - V^T (rows output tile it, cols t), times the rate factor of token t
+    // (its gradients carry its own rate)
     float4_t rT[4];
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
@@ -266,7 +276,7 @@ __global__ __launch_bounds__(64 * kNcWaves) __attribute__((amdgpu_waves_per_eu(1
       o[1] -= bf_hi(cur.vv[it].x);
       o[2] -= bf_lo(cur.vv[it].y);
       o[3] -= bf_hi(cur.vv[it].y);
-      rT[it] = o;
+      rT[it] = o * cur.et;
     }
     // dU = (R W2) * S (rows t): A-operand R (m = t, k = output) from pairs of R^T tiles
     const bf16x8_t rrow0 = pair_op(rT[0], rT[1]), rrow1 = pair_op(rT[2], rT[3]);
@@ -422,7 +432,7 @@ bool mlp_nc_supported(const MlpArgs& a, bool bf16_io) {
                        (a.w2_out == nullptr || al(a.w2_out, 16));
   const bool fits = static_cast<long long>(a.T) * kD * 2 + 2LL * kTileBytes < 0x7fffffffLL;
   return bf16_io && a.d == kD && a.dh == kH && a.causal == 0 && a.chunk >= a.T && a.T > 0 &&
-         aligned && fits;
+         aligned && fits && (a.eta_tok == nullptr || al(a.eta_tok, 4));
 }
 
 hipError_t launch_mlp_nc(const MlpArgs& a, hipStream_t s) {

@@ -39,12 +39,14 @@ bool fits_int64(long long a, long long b, long long c, long long d) {
 }
 
 int check_common(const char* fn, const void* q, const void* k, const void* v, const void* z,
-                 int B, int H, int T, int d, float eta, int io_dtype) {
+                 int B, int H, int T, int d, float eta, const float* eta_tok, int io_dtype) {
   if (B <= 0 || H <= 0 || d <= 0 || T < 0)
     return fail(TTT_E_INVALID, "%s: sizes must be positive (B=%d H=%d T=%d d=%d)", fn, B, H, T, d);
   if (io_dtype != TTT_F32 && io_dtype != TTT_BF16)
     return fail(TTT_E_INVALID, "%s: unknown io_dtype %d", fn, io_dtype);
   if (!std::isfinite(eta)) return fail(TTT_E_INVALID, "%s: eta must be finite", fn);
+  if (eta_tok && (reinterpret_cast<uintptr_t>(eta_tok) & 3) != 0)
+    return fail(TTT_E_INVALID, "%s: eta_tok must be 4-byte aligned", fn);
   if (T > 0 && (!q || !k || !v || !z))
     return fail(TTT_E_INVALID, "%s: q, k, v and z must be non-null", fn);
   if (!fits_int64(B, H, T > 0 ? T : 1, d))
@@ -88,16 +90,16 @@ int copy_state(float* dst, const float* src, long long batch_stride, int B, int 
 
 extern "C" {
 
-int ttt_abi_version(void) { return 1; }
+int ttt_abi_version(void) { return 2; }
 
 const char* ttt_last_error(void) { return g_last_error.c_str(); }
 
 int ttt_linear_fwd(const void* q, const void* k, const void* v, const float* w0,
                    long long w0_batch_stride, void* z, float* w_out, int B, int H, int T,
-                   int d, int chunk, int causal, float eta, int io_dtype,
+                   int d, int chunk, int causal, float eta, const float* eta_tok, int io_dtype,
                    ttt_stream_t stream) {
   g_last_error.clear();
-  int rc = check_common("ttt_linear_fwd", q, k, v, z, B, H, T, d, eta, io_dtype);
+  int rc = check_common("ttt_linear_fwd", q, k, v, z, B, H, T, d, eta, eta_tok, io_dtype);
   if (rc != TTT_OK) return rc;
   if (!w0) return fail(TTT_E_INVALID, "ttt_linear_fwd: w0 must be non-null");
   if (chunk < 1) return fail(TTT_E_INVALID, "ttt_linear_fwd: chunk must be >= 1 (got %d)", chunk);
@@ -109,7 +111,7 @@ int ttt_linear_fwd(const void* q, const void* k, const void* v, const float* w0,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (T == 0) return copy_state(w_out, w0, w0_batch_stride, B, H, static_cast<size_t>(d) * d, s);
 
-  ttt::LinearArgs a{q, k, v, w0, w0_batch_stride, z, w_out, B, H, T, d, chunk, causal, eta};
+  ttt::LinearArgs a{q, k, v, w0, w0_batch_stride, z, w_out, B, H, T, d, chunk, causal, eta, eta_tok};
   const bool bf16 = io_dtype == TTT_BF16;
   hipError_t e;
   if (ttt::linear_mfma_supported(a, bf16))
@@ -122,9 +124,9 @@ int ttt_linear_fwd(const void* q, const void* k, const void* v, const float* w0,
 
 int delta_rule_fwd(const void* q, const void* k, const void* v, const float* w0,
                    long long w0_batch_stride, void* z, float* w_out, int B, int H, int T,
-                   int d, float eta, int io_dtype, ttt_stream_t stream) {
+                   int d, float eta, const float* eta_tok, int io_dtype, ttt_stream_t stream) {
   g_last_error.clear();
-  int rc = check_common("delta_rule_fwd", q, k, v, z, B, H, T, d, eta, io_dtype);
+  int rc = check_common("delta_rule_fwd", q, k, v, z, B, H, T, d, eta, eta_tok, io_dtype);
   if (rc != TTT_OK) return rc;
   if (!w0) return fail(TTT_E_INVALID, "delta_rule_fwd: w0 must be non-null");
   if (w0_batch_stride < 0) return fail(TTT_E_INVALID, "delta_rule_fwd: negative w0_batch_stride");
@@ -133,7 +135,7 @@ int delta_rule_fwd(const void* q, const void* k, const void* v, const float* w0,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (T == 0) return copy_state(w_out, w0, w0_batch_stride, B, H, static_cast<size_t>(d) * d, s);
 
-  ttt::LinearArgs a{q, k, v, w0, w0_batch_stride, z, w_out, B, H, T, d, 1, 1, eta};
+  ttt::LinearArgs a{q, k, v, w0, w0_batch_stride, z, w_out, B, H, T, d, 1, 1, eta, eta_tok};
   const bool bf16 = io_dtype == TTT_BF16;
   hipError_t e;
   StreamBuffer ws;
@@ -150,10 +152,10 @@ int delta_rule_fwd(const void* q, const void* k, const void* v, const float* w0,
 
 int ttt_mlp_fwd(const void* q, const void* k, const void* v, const float* w1, const float* w2,
                 long long w_batch_stride, void* z, float* w1_out, float* w2_out, int B, int H,
-                int T, int d, int dh, int chunk, int causal, float eta, int io_dtype,
-                ttt_stream_t stream) {
+                int T, int d, int dh, int chunk, int causal, float eta, const float* eta_tok,
+                int io_dtype, ttt_stream_t stream) {
   g_last_error.clear();
-  int rc = check_common("ttt_mlp_fwd", q, k, v, z, B, H, T, d, eta, io_dtype);
+  int rc = check_common("ttt_mlp_fwd", q, k, v, z, B, H, T, d, eta, eta_tok, io_dtype);
   if (rc != TTT_OK) return rc;
   if (!w1 || !w2) return fail(TTT_E_INVALID, "ttt_mlp_fwd: w1 and w2 must be non-null");
   if (dh <= 0) return fail(TTT_E_INVALID, "ttt_mlp_fwd: dh must be positive (got %d)", dh);
@@ -171,7 +173,7 @@ int ttt_mlp_fwd(const void* q, const void* k, const void* v, const float* w1, co
     return copy_state(w2_out, w2, w_batch_stride, B, H, per, s);
   }
   ttt::MlpArgs a{q, k, v, w1, w2, w_batch_stride, z, w1_out, w2_out,
-                 B, H, T, d, dh, chunk, causal, eta};
+                 B, H, T, d, dh, chunk, causal, eta, eta_tok};
   const bool bf16 = io_dtype == TTT_BF16;
   hipError_t e;
   StreamBuffer ws;

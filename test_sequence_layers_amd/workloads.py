@@ -130,3 +130,10 @@ def make_inputs(w: Workload, seed: Optional[int] = None, **overrides) -> dict:
         q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
     out["q"], out["k"], out["v"] = q, k, v
     return out
+
+
+def make_token_rates(w: Workload, seed: int, lo: float = 0.0, hi: float = 1.0) -> np.ndarray:
+    """Seeded per-token rate factors [B, H, T] float32, uniform in [lo, hi): the range of a
+    sigmoid gate.  A separate stream, so the workload's other inputs are unchanged."""
+    rng = np.random.default_rng(10_000 + seed)
+    return rng.uniform(lo, hi, size=(w.B, w.H, w.T)).astype(np.float32)

@@ -3,7 +3,7 @@ seeded inputs and compare slab by slab (one slab = one (batch, head) sequence)."
 import numpy as np
 
 from oracle import ttt_oracle as O
-from test_sequence_layers_amd.workloads import make_inputs, workload
+from test_sequence_layers_amd.workloads import make_inputs, make_token_rates, workload
 
 FP32_TOL = 1e-4   # relative Frobenius error per slab, float32 I/O
 BF16_TOL = 2e-2   # relative Frobenius error per slab, bfloat16 I/O, float32 state
@@ -32,7 +32,7 @@ def to_device(inp, io):
     out = {}
     for key in ("q", "k", "v"):
         out[key] = torch.from_numpy(np.ascontiguousarray(inp[key])).to("cuda").to(dt).contiguous()
-    for key in ("w0", "w1", "w2"):
+    for key in ("w0", "w1", "w2", "eta_tok"):
         if key in inp:
             out[key] = torch.from_numpy(np.ascontiguousarray(inp[key])).to("cuda").contiguous()
     return out
@@ -40,31 +40,34 @@ def to_device(inp, io):
 
 def run_gpu(kind, dev, eta, chunk, causal, return_state=True):
     import test_sequence_layers_amd as ttt
+    et = dev.get("eta_tok")
     if kind == "linear":
         return ttt.ttt_linear_fwd(dev["q"], dev["k"], dev["v"], dev["w0"], eta, chunk, causal,
-                                  return_state=return_state)
+                                  eta_tok=et, return_state=return_state)
     if kind == "delta":
-        return ttt.delta_rule_fwd(dev["q"], dev["k"], dev["v"], dev["w0"], eta,
+        return ttt.delta_rule_fwd(dev["q"], dev["k"], dev["v"], dev["w0"], eta, eta_tok=et,
                                   return_state=return_state)
     return ttt.ttt_mlp_fwd(dev["q"], dev["k"], dev["v"], dev["w1"], dev["w2"], eta, chunk,
-                           causal, return_state=return_state)
+                           causal, eta_tok=et, return_state=return_state)
 
 
 def run_oracle(kind, inp, eta, chunk, causal, sel=None):
     """Oracle on (optionally) a subset of (b, h) pairs: sel = list of (b, h)."""
     q, k, v = inp["q"], inp["k"], inp["v"]
+    et = inp.get("eta_tok")
     if sel is not None:
         bs = [b for b, _ in sel]
         hs = [h for _, h in sel]
         q, k, v = q[bs, hs][None], k[bs, hs][None], v[bs, hs][None]
+        et = et[bs, hs][None] if et is not None else None
         pick = lambda w: w[hs][None] if w.ndim == 3 else w[bs, hs][None]
     else:
         pick = lambda w: w
     if kind == "linear":
-        return O.ttt_linear(q, k, v, pick(inp["w0"]), eta, chunk, causal)
+        return O.ttt_linear(q, k, v, pick(inp["w0"]), eta, chunk, causal, eta_tok=et)
     if kind == "delta":
-        return O.delta_rule(q, k, v, pick(inp["w0"]), eta)
-    return O.ttt_mlp(q, k, v, pick(inp["w1"]), pick(inp["w2"]), eta, chunk, causal)
+        return O.delta_rule(q, k, v, pick(inp["w0"]), eta, eta_tok=et)
+    return O.ttt_mlp(q, k, v, pick(inp["w1"]), pick(inp["w2"]), eta, chunk, causal, eta_tok=et)
 
 
 def to_np(t):

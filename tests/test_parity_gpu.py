@@ -8,8 +8,8 @@ import numpy as np
 import pytest
 import sys
 
-from tests.parity_util import (BF16_TOL, FP32_TOL, make_inputs, run_gpu, run_oracle, slab_rel,
-                               to_device, to_np, tol_for, workload)
+from tests.parity_util import (BF16_TOL, FP32_TOL, make_inputs, make_token_rates, run_gpu,
+                               run_oracle, slab_rel, to_device, to_np, tol_for, workload)
 
 pytestmark = pytest.mark.gpu
 
@@ -175,3 +175,59 @@ def test_unsupported_shape_raises():
     q = torch.zeros((1, 1, 4, 48), device="cuda")
     with pytest.raises(ttt.TTTError, match="not supported"):
         ttt.ttt_linear_fwd(q, q, q, torch.zeros((1, 48, 48), device="cuda"), 0.1, 4)
+
+
+# ------------------------------------------------------------------ per-token rates
+# token t learns at eta * eta_tok[t]; every kernel path (generic, matrix-core linear and
+# delta rule, causal and non-causal MLP) against the oracle with the same factors
+
+def _with_rates(w, seed, lo=0.0, hi=1.0):
+    inp = make_inputs(w)
+    inp["eta_tok"] = make_token_rates(w, seed, lo, hi)
+    return inp
+
+
+@pytest.mark.parametrize("chunk,causal", [(5, True), (16, False), (1, True)])
+def test_token_rates_linear_fp32(chunk, causal):
+    w = workload(0).replace(B=2, H=3, T=77, d=32, chunk=chunk, causal=causal, init="normal",
+                            eta=0.4, seed=80 + chunk)
+    _check("linear", w, _with_rates(w, 1))
+
+
+@pytest.mark.parametrize("T", [16, 200, 333])
+def test_token_rates_linear_bf16_d64_chunk16(T):
+    w = workload(1).replace(B=2, H=3, T=T, init="normal", eta=0.5, seed=90 + T)
+    _check("linear", w, _with_rates(w, 2))
+
+
+def test_token_rates_linear_config_full_size_sampled():
+    w = workload(1)
+    _check("linear", w, _with_rates(w, 3), sel=[(0, 0), (5, 9)])
+
+
+@pytest.mark.parametrize("d,io", [(16, "f32"), (64, "bf16")])
+def test_token_rates_delta(d, io):
+    w = workload(2).replace(B=2, H=2, T=150, d=d, io=io, init="normal", seed=100 + d)
+    _check("delta", w, _with_rates(w, 4))
+
+
+def test_token_rates_delta_config_full_size_sampled():
+    w = workload(2)
+    _check("delta", w, _with_rates(w, 5), sel=[(1, 3)])
+
+
+@pytest.mark.parametrize("chunk,causal", [(4, True), (37, False)])
+def test_token_rates_mlp_fp32(chunk, causal):
+    w = workload(3).replace(B=1, H=2, T=37, d=16, h=24, io="f32", chunk=chunk, causal=causal,
+                            seed=110 + chunk)
+    _check("mlp", w, _with_rates(w, 6))
+
+
+def test_token_rates_mlp_bf16_h256():
+    w = workload(3).replace(B=2, H=2, T=70, seed=120)
+    _check("mlp", w, _with_rates(w, 7))
+
+
+def test_token_rates_mlp_vision():
+    w = workload(4).replace(B=2, H=3, seed=130)
+    _check("mlp", w, _with_rates(w, 8))
