@@ -79,19 +79,19 @@ def make_device_inputs(w, seed, torch, rates=False):
     return dev
 
 
-def launch(w, dev, ttt):
+def launch(w, dev, ttt, loss="mse"):
     et = dev.get("eta_tok")
     if w.kind == "linear":
         ttt.ttt_linear_fwd(dev["q"], dev["k"], dev["v"], dev["w0"], w.eta, w.chunk, w.causal,
-                           eta_tok=et, z=dev["z"])
+                           eta_tok=et, loss=loss, z=dev["z"])
     elif w.kind == "delta":
         ttt.delta_rule_fwd(dev["q"], dev["k"], dev["v"], dev["w0"], w.eta, eta_tok=et, z=dev["z"])
     else:
         ttt.ttt_mlp_fwd(dev["q"], dev["k"], dev["v"], dev["w1"], dev["w2"], w.eta, w.chunk,
-                        w.causal, eta_tok=et, z=dev["z"])
+                        w.causal, eta_tok=et, loss=loss, z=dev["z"])
 
 
-def time_workload(w, steps, warmup, torch, ttt, rotate=None, rates=False):
+def time_workload(w, steps, warmup, torch, ttt, rotate=None, rates=False, loss="mse"):
     bytes_, flops = algorithmic_cost(w)
     if rates:
         bytes_ += w.B * w.H * w.T * 4  # the rate factors, read once
@@ -100,13 +100,13 @@ def time_workload(w, steps, warmup, torch, ttt, rotate=None, rates=False):
     sets = [make_device_inputs(w, w.seed + i, torch, rates) for i in range(rotate)]
     stream = torch.cuda.current_stream()
     for i in range(warmup):
-        launch(w, sets[i % rotate], ttt)
+        launch(w, sets[i % rotate], ttt, loss)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(steps):
-        launch(w, sets[i % rotate], ttt)
+        launch(w, sets[i % rotate], ttt, loss)
     stop.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / steps
@@ -270,10 +270,17 @@ def main():
                 "tflops": round(r["tflops"], 3),
                 "mfma_util_pct": round(100 * r["tflops"] / BF16_MFMA_PEAK_TFLOPS, 3),
             }
+        # variants: the headline workload with per-token rate factors (uniform in [0, 1)),
+        # and the dot-product loss on the headline and the vision workloads
+        variants = []
         if not args.token_rates:
-            # the headline workload again with per-token rate factors (uniform in [0, 1))
-            r = time_workload(w, max(10, args.steps // 2), 5, torch, ttt, rates=True)
-            others[w.name + "+token_rates"] = {
+            variants.append((w, "+token_rates", dict(rates=True)))
+        variants.append((w, "+dot_loss", dict(loss="dot")))
+        variants += [(o, "+dot_loss", dict(loss="dot")) for o in WORKLOADS
+                     if o.name == "mlp_vision_N196"]
+        for o, tag, kw in variants:
+            r = time_workload(o, max(10, args.steps // 2), 5, torch, ttt, **kw)
+            others[o.name + tag] = {
                 "tokens_per_s": round(r["tokens_per_s"], 1),
                 "ms_per_step": round(r["ms_per_step"], 5),
                 "hbm_gbs": round(r["hbm_gbs"], 1),

@@ -31,14 +31,19 @@
  *     makes it a function of the token, eta_base * sigmoid(theta . x_t), which a caller
  *     passes as eta = eta_base and eta_tok = sigmoid(theta . x_t).  The factors are read as
  *     they are (not validated on the host; non-finite factors give non-finite outputs).
+ *   - loss (ttt_linear_fwd, ttt_mlp_fwd): TTT_LOSS_MSE, the reconstruction loss
+ *     1/2 ||f(k; W) - v||^2 ("Fast weights" page, opening formula), or TTT_LOSS_DOT, the
+ *     negative dot product -v^T f(k; W) (blog page, section TTT / 如何理解; the ViT3 news
+ *     page, section 2, uses it for the vision model).  With TTT_LOSS_DOT the error term
+ *     f(k; W) - v of every gradient becomes -v, so the gradients no longer depend on W.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream).  Calls are
  *     asynchronous, never synchronise, keep no pointer after returning and are thread-safe;
  *     any workspace a call needs is allocated and released in stream order on `stream`.
  *   - Arguments are validated on the host before any HIP call.  Return values:
  *       TTT_OK             work enqueued;
  *       TTT_E_INVALID      a null required pointer, a non-positive size, chunk < 1, a
- *                          non-finite eta, a misaligned eta_tok, an unknown dtype or a
- *                          size overflow;
+ *                          non-finite eta, a misaligned eta_tok, an unknown dtype or loss,
+ *                          or a size overflow;
  *       TTT_E_UNSUPPORTED  a valid combination with no kernel (see each function);
  *       TTT_E_HIP          a HIP runtime error (launch failure, workspace allocation).
  *     ttt_last_error() returns the calling thread's message for the last non-OK status.
@@ -54,6 +59,7 @@ typedef struct ihipStream_t* ttt_stream_t; /* identical to hipStream_t */
 
 enum { TTT_OK = 0, TTT_E_INVALID = -1, TTT_E_UNSUPPORTED = -2, TTT_E_HIP = -3 };
 enum { TTT_F32 = 0, TTT_BF16 = 1 };
+enum { TTT_LOSS_MSE = 0, TTT_LOSS_DOT = 1 };
 
 /*
  * TTT-Linear forward: f(k; W) = W k, reconstruction loss, mini-batch GD of size `chunk`.
@@ -69,7 +75,7 @@ int ttt_linear_fwd(const void* q, const void* k, const void* v,
                    const float* w0, long long w0_batch_stride,
                    void* z, float* w_out,
                    int B, int H, int T, int d, int chunk, int causal, float eta,
-                   const float* eta_tok, int io_dtype, ttt_stream_t stream);
+                   const float* eta_tok, int loss, int io_dtype, ttt_stream_t stream);
 
 /*
  * TTT-MLP forward: f(k; W1, W2) = W2 SiLU(W1 k) with hidden width dh, no bias (ViT3 news
@@ -85,7 +91,7 @@ int ttt_mlp_fwd(const void* q, const void* k, const void* v,
                 const float* w1, const float* w2, long long w_batch_stride,
                 void* z, float* w1_out, float* w2_out,
                 int B, int H, int T, int d, int dh, int chunk, int causal, float eta,
-                const float* eta_tok, int io_dtype, ttt_stream_t stream);
+                const float* eta_tok, int loss, int io_dtype, ttt_stream_t stream);
 
 /*
  * Delta rule (mini-batch of one token, causal): W_t = W_{t-1} + eta_t (v_t - W_{t-1} k_t) k_t^T,

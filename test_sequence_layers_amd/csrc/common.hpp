@@ -38,6 +38,7 @@ struct LinearArgs {
   int B, H, T, d, chunk, causal;
   float eta;
   const float* eta_tok;  // per-token rate factors [B][H][T] (rate eta * eta_tok[t]) or null
+  int dot_loss;          // 1: loss -v^T f(k), error term -v; 0: 1/2 ||f(k) - v||^2
 };
 
 struct MlpArgs {
@@ -53,6 +54,7 @@ struct MlpArgs {
   int B, H, T, d, dh, chunk, causal;
   float eta;
   const float* eta_tok;  // per-token rate factors [B][H][T] (rate eta * eta_tok[t]) or null
+  int dot_loss;          // 1: loss -v^T f(k), error term -v; 0: 1/2 ||f(k) - v||^2
 };
 
 // Host-side launchers (return a hipError_t; argument checks are done by the caller).

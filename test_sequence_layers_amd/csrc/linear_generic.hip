@@ -2,7 +2,8 @@
 // bf16 I/O, d in {16, 32, 64}.  One workgroup of 256 threads per (batch, head) chain.
 //
 // Method: mini-batch gradient descent on 1/2 ||W k - v||^2 (gradient (W k - v) k^T,
-// "Fast weights" page, section 1); inside a chunk every gradient is taken at the
+// "Fast weights" page, section 1), or on the negative dot product -v^T W k (gradient
+// -v k^T; blog page "TTT: Test-Time Training", section TTT / 如何理解); inside a chunk every gradient is taken at the
 // chunk-start weights and W_t subtracts eta times the running sum (wmrh.cn summary of
 // Sun et al. 2024, section 1.2.2); z_t = W_t q_t (blog page "TTT: Test-Time Training",
 // general form).
@@ -80,7 +81,8 @@ __global__ __launch_bounds__(kThreads) void linear_generic_kernel(LinearArgs a) 
 #pragma unroll 16
         for (int j = 0; j < D; ++j) acc += Ks[t][j] * Wc[i][j];
         const float rate = t < n ? (etok ? eta * etok[s0 + t] : eta) : 0.0f;
-        Rs[t][i] = t < n ? rate * (acc - Vs[t][i]) : 0.0f;
+        const float err = a.dot_loss ? -Vs[t][i] : acc - Vs[t][i];  // dl/df: f - v or -v
+        Rs[t][i] = t < n ? rate * err : 0.0f;
       }
       if (a.causal) {
         for (int e = tid; e < kSub * kSub; e += kThreads) {

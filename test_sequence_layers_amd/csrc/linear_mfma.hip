@@ -2,8 +2,10 @@
 // bf16 Q/K/V/Z, fp32 state; and, on the same machinery, the exact delta rule (b = 1).
 //
 // Method (wmrh.cn summary of Sun et al. 2024, section 1.2.2, mini-batch TTT and its dual
-// form; gradient (W k - v) k^T from the "Fast weights" page, section 1).  For a chunk with
-// rows Q, K, V (16 x 64) and chunk-start weights W, with R = K W^T - V:
+// form; gradient (W k - v) k^T from the "Fast weights" page, section 1; with the negative
+// dot-product loss of the blog page, section TTT / 如何理解, the gradient is -v k^T and
+// R = -V below).  For a chunk with rows Q, K, V (16 x 64) and chunk-start weights W, with
+// R = K W^T - V:
 //     Z = Q W^T - eta * tril(Q K^T) R        (tril keeps the diagonal: z_t sees its own
 //     W <- W - eta * R^T K                    update)
 // which equals the per-token recurrence up to floating-point order.
@@ -249,7 +251,7 @@ __device__ __forceinline__ u32x2 neg_eta_bf16(const float4_t& r, float neta, con
 // (delta rule: each R is Tm times the bracket).  Only the second R waits for the first; the
 // state update and its bf16 copy happen once per pair.  Hands off the bf16 W_c and
 // -eta R_c, -eta R_{c+1} to the output wave (pair area h; lw = 16 lane, lr = 8 lane).
-template <bool kDelta, bool kTok>
+template <bool kDelta, bool kTok, bool kDot>
 __device__ __forceinline__ void pair_step(WState& w, const PairRegs& r, const LaneConst& lc, lds_char* h, int lw,
                                           int lr) {
   const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -258,18 +260,29 @@ __device__ __forceinline__ void pair_step(WState& w, const PairRegs& r, const La
   const u32x4 wb1u = {pack_bf16(w.t2[0], w.t2[1]), pack_bf16(w.t2[2], w.t2[3]),
                       pack_bf16(w.t3[0], w.t3[1]), pack_bf16(w.t3[2], w.t3[3])};
   const bf16x8_t wb0 = bf8(wb0u), wb1 = bf8(wb1u);
-  float4_t r0 = kw_minus_v(r.k[0][0], r.k[0][1], r.v[0], wb0, wb1, lc);
-  const float4_t a1 = kw_minus_v(r.k[1][0], r.k[1][1], r.v[1], wb0, wb1, lc);
-  // M^T = K_c K_{c+1}^T in the C layout is M as the A operand: lane (g, n) = M[n][4 g + s]
-  float4_t mt = MFMA32(bf8(r.k[0][0]), bf8(r.k[1][0]), zero, 0, 0, 0);
-  mt = MFMA32(bf8(r.k[0][1]), bf8(r.k[1][1]), mt, 0, 0, 0);
-  if (kDelta) r0 = tm_apply(r.tm[0], r0);
-  const u32x2 rn0 = kTok ? neg_eta_bf16(r0, lc.neta, r.et[0]) : neg_eta_bf16(r0, lc.neta);
-  const u32x4 mpad = {pack_bf16(mt[0], mt[1]), pack_bf16(mt[2], mt[3]), 0u, 0u};
-  const u32x4 rpad0 = {rn0.x, rn0.y, 0u, 0u};
-  float4_t r1 = MFMA32(bf8(mpad), bf8(rpad0), a1, 0, 0, 0);
-  if (kDelta) r1 = tm_apply(r.tm[1], r1);
-  const u32x2 rn1 = kTok ? neg_eta_bf16(r1, lc.neta, r.et[1]) : neg_eta_bf16(r1, lc.neta);
+  float4_t r0, r1;
+  u32x2 rn0, rn1;
+  if (kDot) {
+    // dot-product loss: the error term is -v whatever W is, so neither R needs the state
+    const u32x4 vpad0 = {r.v[0].x, r.v[0].y, 0u, 0u}, vpad1 = {r.v[1].x, r.v[1].y, 0u, 0u};
+    r0 = MFMA32(bf8(vpad0), lc.neg_eye, zero, 0, 0, 0);
+    r1 = MFMA32(bf8(vpad1), lc.neg_eye, zero, 0, 0, 0);
+    rn0 = kTok ? neg_eta_bf16(r0, lc.neta, r.et[0]) : neg_eta_bf16(r0, lc.neta);
+    rn1 = kTok ? neg_eta_bf16(r1, lc.neta, r.et[1]) : neg_eta_bf16(r1, lc.neta);
+  } else {
+    r0 = kw_minus_v(r.k[0][0], r.k[0][1], r.v[0], wb0, wb1, lc);
+    const float4_t a1 = kw_minus_v(r.k[1][0], r.k[1][1], r.v[1], wb0, wb1, lc);
+    // M^T = K_c K_{c+1}^T in the C layout is M as the A operand: lane (g, n) = M[n][4 g + s]
+    float4_t mt = MFMA32(bf8(r.k[0][0]), bf8(r.k[1][0]), zero, 0, 0, 0);
+    mt = MFMA32(bf8(r.k[0][1]), bf8(r.k[1][1]), mt, 0, 0, 0);
+    if (kDelta) r0 = tm_apply(r.tm[0], r0);
+    rn0 = kTok ? neg_eta_bf16(r0, lc.neta, r.et[0]) : neg_eta_bf16(r0, lc.neta);
+    const u32x4 mpad = {pack_bf16(mt[0], mt[1]), pack_bf16(mt[2], mt[3]), 0u, 0u};
+    const u32x4 rpad0 = {rn0.x, rn0.y, 0u, 0u};
+    r1 = MFMA32(bf8(mpad), bf8(rpad0), a1, 0, 0, 0);
+    if (kDelta) r1 = tm_apply(r.tm[1], r1);
+    rn1 = kTok ? neg_eta_bf16(r1, lc.neta, r.et[1]) : neg_eta_bf16(r1, lc.neta);
+  }
   lds_store<u32x4>(h + lw, wb0u);
   lds_store<u32x4>(h + kHandW1 + lw, wb1u);
   lds_store<u32x2>(h + kHandR0 + lr, rn0);
@@ -348,7 +361,7 @@ __device__ __forceinline__ void lds_barrier() {
   __asm__ __volatile__("" ::: "memory");
 }
 
-template <bool kDelta, bool kTok>
+template <bool kDelta, bool kTok, bool kDot>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) void linear_mfma_kernel(
     LinearArgs a, const bf16* tmat) {
   using RG = Ring<kDelta, kTok>;
@@ -529,7 +542,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
         PairRegs& nxt = (x & 2) ? ra : rb;
         __builtin_amdgcn_sched_barrier(0);  // keep steps apart (register pressure)
         read_pair<kDelta, kTok>(nxt, ring + s2 * RG::kSlotBytes, ring + s3 * RG::kSlotBytes, o);
-        pair_step<kDelta, kTok>(wacc, cur, lc, hg + (x / 2) * kHandPair, lw, lr);
+        pair_step<kDelta, kTok, kDot>(wacc, cur, lc, hg + (x / 2) * kHandPair, lw, lr);
       }
     }
   }
@@ -570,12 +583,19 @@ bool linear_mfma_supported(const LinearArgs& a, bool bf16_io) {
 hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s) {
   const long long nblocks = mfma_grid(a);
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (a.eta_tok)
-    hipLaunchKernelGGL((linear_mfma_kernel<false, true>), dim3(static_cast<unsigned>(nblocks)), dim3(kThreads),
-                       0, s, a, static_cast<const bf16*>(nullptr));
-  else
-    hipLaunchKernelGGL((linear_mfma_kernel<false, false>), dim3(static_cast<unsigned>(nblocks)), dim3(kThreads),
-                       0, s, a, static_cast<const bf16*>(nullptr));
+  const dim3 grid(static_cast<unsigned>(nblocks)), block(kThreads);
+  const bf16* none = nullptr;
+  if (a.dot_loss) {
+    if (a.eta_tok)
+      hipLaunchKernelGGL((linear_mfma_kernel<false, true, true>), grid, block, 0, s, a, none);
+    else
+      hipLaunchKernelGGL((linear_mfma_kernel<false, false, true>), grid, block, 0, s, a, none);
+  } else {
+    if (a.eta_tok)
+      hipLaunchKernelGGL((linear_mfma_kernel<false, true, false>), grid, block, 0, s, a, none);
+    else
+      hipLaunchKernelGGL((linear_mfma_kernel<false, false, false>), grid, block, 0, s, a, none);
+  }
   return hipGetLastError();
 }
 
@@ -687,10 +707,10 @@ hipError_t launch_delta_fast(const LinearArgs& a, void* workspace, hipStream_t s
   const long long nmain = mfma_grid(a);
   if (nmain > 0x7fffffffLL) return hipErrorInvalidValue;
   if (a.eta_tok)
-    hipLaunchKernelGGL((linear_mfma_kernel<true, true>), dim3(static_cast<unsigned>(nmain)), dim3(kThreads),
+    hipLaunchKernelGGL((linear_mfma_kernel<true, true, false>), dim3(static_cast<unsigned>(nmain)), dim3(kThreads),
                        0, s, a, static_cast<const bf16*>(tm));
   else
-    hipLaunchKernelGGL((linear_mfma_kernel<true, false>), dim3(static_cast<unsigned>(nmain)), dim3(kThreads),
+    hipLaunchKernelGGL((linear_mfma_kernel<true, false, false>), dim3(static_cast<unsigned>(nmain)), dim3(kThreads),
                        0, s, a, static_cast<const bf16*>(tm));
   return hipGetLastError();
 }

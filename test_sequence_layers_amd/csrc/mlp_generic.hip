@@ -3,8 +3,9 @@
 // One workgroup of 256 threads per (batch, head) chain.
 //
 // Method: inner 2-layer SiLU MLP (ViT3 news page, section 2) trained by mini-batch GD on
-// 1/2 ||f(k) - v||^2 (wmrh.cn summary of Sun et al. 2024, section 1.2.2), z_t = f(q_t; W_t).
-// Per token, with u = W1 k, a = SiLU(u), r = W2 a - v:
+// 1/2 ||f(k) - v||^2 (wmrh.cn summary of Sun et al. 2024, section 1.2.2), z_t = f(q_t; W_t),
+// or on the negative dot product -v^T f(k) (ViT3 news page, section 2), whose error term is
+// r = -v.  Per token, with u = W1 k, a = SiLU(u), r = W2 a - v:
 //   dW2 = r a^T,   dW1 = ((W2^T r) * SiLU'(u)) k^T.
 //
 // With per-token rates (eta_t = eta * eta_tok[t]; "Fast weights" page, opening formula;
@@ -112,7 +113,8 @@ __global__ __launch_bounds__(kThreads) void mlp_generic_kernel(MlpArgs a, float*
         float o = 0.0f;
         for (int c = 0; c < h; ++c) o += Ab[t * h + c] * W2c[static_cast<size_t>(i) * h + c];
         const float rate = t < n ? (etok ? eta * etok[s0 + t] : eta) : 0.0f;
-        Rs[e] = t < n ? rate * (o - Vs[e]) : 0.0f;
+        const float err = a.dot_loss ? -Vs[e] : o - Vs[e];  // dl/df: f - v or -v
+        Rs[e] = t < n ? rate * err : 0.0f;
       }
       __syncthreads();
       // backward to the hidden pre-activation: du = (W2c^T r) * SiLU'(u)

@@ -8,7 +8,8 @@
 //   dU = (R W2) * S                                   (gradient of the hidden layer)
 //   W1 <- W1 - eta dU^T K,  W2 <- W2 - eta R^T A        (sum of the chunk's gradients)
 // (with per-token rates, eta times a row of R or dU is that token's rate: "Fast weights"
-// page, opening formula; wmrh.cn summary, section 2.2.3)
+// page, opening formula; wmrh.cn summary, section 2.2.3; with the negative dot-product loss
+// -v^T f(k) of the ViT3 news page, section 2, R = -V)
 // and, because every hidden pre-activation of a query is linear in W1 and the output is
 // linear in W2, the causal outputs with the in-chunk updates are
 //   U_q = Q W1^T - eta tril(Q K^T) dU,  A_q = SiLU(U_q),
@@ -184,6 +185,7 @@ struct Lds {
 
 __device__ __forceinline__ void barrier() { __syncthreads(); }
 
+template <bool kDot>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void mlp_mfma_kernel(
     MlpArgs a) {
   __shared__ __attribute__((aligned(16))) Lds sh;
@@ -317,11 +319,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       lds_store<u32x2>(w2lds, w2off(row, 4 + g), u32x2{w2op[it].z, w2op[it].w});
     }
     // O^T partial = W2 A^T (rows output, cols t): contraction over this wave's 32 hidden
+    // (not needed with the dot-product loss, whose error term is -V)
     const bf16x8_t atb = cat_op(actT[0], actT[1]);  // B operand over hidden
+    if (!kDot) {
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const float4_t ot = mfma(bf(w2op[it]), atb, zero);
-      lds_store<float4_t>(opart, ((wv * kB + n) * kRow + 16 * it + 4 * g) * 4, ot);
+      for (int it = 0; it < 4; ++it) {
+        const float4_t ot = mfma(bf(w2op[it]), atb, zero);
+        lds_store<float4_t>(opart, ((wv * kB + n) * kRow + 16 * it + 4 * g) * 4, ot);
+      }
     }
     barrier();
     // previous chunk's Z (its partials were written before this barrier)
@@ -329,8 +334,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // -eta_t R = -eta_t (sum of partials - V), to LDS in bf16 as [t][i] and [i][t]
     {
       float2_t s2 = zero2;
+      if (!kDot) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) s2 += lds_load<float2_t>(opart, ((w * kB + rt) * kRow + ri) * 4);
+        for (int w = 0; w < kWaves; ++w) s2 += lds_load<float2_t>(opart, ((w * kB + rt) * kRow + ri) * 4);
+      }
       const uint32_t vb = cur.vv;
       const float nrate = -eta * cur.et;
       const uint32_t rp = pack_bf16((s2[0] - __builtin_bit_cast(float, vb << 16)) * nrate,
@@ -472,7 +479,10 @@ bool mlp_fast_supported(const MlpArgs& a, bool bf16_io) {
 hipError_t launch_mlp_fast(const MlpArgs& a, hipStream_t s) {
   const long long nchains = static_cast<long long>(a.B) * a.H;
   if (nchains > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(mlp_mfma_kernel, dim3(static_cast<unsigned>(nchains)), dim3(kThreads), 0, s, a);
+  if (a.dot_loss)
+    hipLaunchKernelGGL(mlp_mfma_kernel<true>, dim3(static_cast<unsigned>(nchains)), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(mlp_mfma_kernel<false>, dim3(static_cast<unsigned>(nchains)), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

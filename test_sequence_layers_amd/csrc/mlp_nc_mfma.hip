@@ -7,7 +7,8 @@
 // S = SiLU'(U), R = A W2^T - V and dU = (R W2) * S over all N tokens:
 //   W1' = W1 - eta dU^T K,   W2' = W2 - eta R^T A,   Z = SiLU(Q W1'^T) W2'^T.
 // With per-token rates each row t of R (and so of dU) is scaled by token t's rate factor
-// ("Fast weights" page, opening formula; wmrh.cn summary, section 2.2.3).
+// ("Fast weights" page, opening formula; wmrh.cn summary, section 2.2.3).  With the
+// negative dot-product loss -v^T f(k), the ViT3 page's own inner loss (section 2), R = -V.
 //
 // Mapping.  One workgroup of kNcWaves = 2 waves per (batch, head) chain; wave w takes the
 // 16-token tiles w, w + 2, w + 4, ...  Pass 1 streams its tiles (the next tile's loads are
@@ -125,6 +126,7 @@ __device__ __forceinline__ void load_kv(KvTile& r, const char* k, const char* v,
 // fp32 weight rows staged in LDS, padded to 68 floats so that the 16-byte reads of 16
 // lanes in 16 consecutive rows spread over the banks
 constexpr int kWRow = kD + 4;
+template <bool kDot>
 __global__ __launch_bounds__(64 * kNcWaves) __attribute__((amdgpu_waves_per_eu(1, 1))) void mlp_nc_kernel(MlpArgs a) {
   // partial gradient tiles [wave][tile f][lane], then the trained tiles in [0][f][lane]
   __shared__ float4_t red[kNcWaves][16][64];
@@ -270,8 +272,11 @@ __global__ __launch_bounds__(64 * kNcWaves) __attribute__((amdgpu_waves_per_eu(1
     float4_t rT[4];
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      float4_t o = mfma(w2tb[0][it], atb0, zero);
-      o = mfma(w2tb[1][it], atb1, o);
+      float4_t o = zero;  // the dot-product loss's error term is -V alone
+      if (!kDot) {
+        o = mfma(w2tb[0][it], atb0, zero);
+        o = mfma(w2tb[1][it], atb1, o);
+      }
       o[0] -= bf_lo(cur.vv[it].x);
       o[1] -= bf_hi(cur.vv[it].x);
       o[2] -= bf_lo(cur.vv[it].y);
@@ -438,7 +443,10 @@ bool mlp_nc_supported(const MlpArgs& a, bool bf16_io) {
 hipError_t launch_mlp_nc(const MlpArgs& a, hipStream_t s) {
   const long long nchains = static_cast<long long>(a.B) * a.H;
   if (nchains > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(mlp_nc_kernel, dim3(static_cast<unsigned>(nchains)), dim3(64 * kNcWaves), 0, s, a);
+  if (a.dot_loss)
+    hipLaunchKernelGGL(mlp_nc_kernel<true>, dim3(static_cast<unsigned>(nchains)), dim3(64 * kNcWaves), 0, s, a);
+  else
+    hipLaunchKernelGGL(mlp_nc_kernel<false>, dim3(static_cast<unsigned>(nchains)), dim3(64 * kNcWaves), 0, s, a);
   return hipGetLastError();
 }
 

@@ -90,17 +90,19 @@ int copy_state(float* dst, const float* src, long long batch_stride, int B, int 
 
 extern "C" {
 
-int ttt_abi_version(void) { return 2; }
+int ttt_abi_version(void) { return 3; }
 
 const char* ttt_last_error(void) { return g_last_error.c_str(); }
 
 int ttt_linear_fwd(const void* q, const void* k, const void* v, const float* w0,
                    long long w0_batch_stride, void* z, float* w_out, int B, int H, int T,
-                   int d, int chunk, int causal, float eta, const float* eta_tok, int io_dtype,
-                   ttt_stream_t stream) {
+                   int d, int chunk, int causal, float eta, const float* eta_tok, int loss,
+                   int io_dtype, ttt_stream_t stream) {
   g_last_error.clear();
   int rc = check_common("ttt_linear_fwd", q, k, v, z, B, H, T, d, eta, eta_tok, io_dtype);
   if (rc != TTT_OK) return rc;
+  if (loss != TTT_LOSS_MSE && loss != TTT_LOSS_DOT)
+    return fail(TTT_E_INVALID, "ttt_linear_fwd: unknown loss %d", loss);
   if (!w0) return fail(TTT_E_INVALID, "ttt_linear_fwd: w0 must be non-null");
   if (chunk < 1) return fail(TTT_E_INVALID, "ttt_linear_fwd: chunk must be >= 1 (got %d)", chunk);
   if (causal != 0 && causal != 1)
@@ -111,7 +113,8 @@ int ttt_linear_fwd(const void* q, const void* k, const void* v, const float* w0,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (T == 0) return copy_state(w_out, w0, w0_batch_stride, B, H, static_cast<size_t>(d) * d, s);
 
-  ttt::LinearArgs a{q, k, v, w0, w0_batch_stride, z, w_out, B, H, T, d, chunk, causal, eta, eta_tok};
+  ttt::LinearArgs a{q, k, v, w0, w0_batch_stride, z, w_out, B, H, T, d, chunk, causal, eta, eta_tok,
+                    loss == TTT_LOSS_DOT ? 1 : 0};
   const bool bf16 = io_dtype == TTT_BF16;
   hipError_t e;
   if (ttt::linear_mfma_supported(a, bf16))
@@ -135,7 +138,7 @@ int delta_rule_fwd(const void* q, const void* k, const void* v, const float* w0,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (T == 0) return copy_state(w_out, w0, w0_batch_stride, B, H, static_cast<size_t>(d) * d, s);
 
-  ttt::LinearArgs a{q, k, v, w0, w0_batch_stride, z, w_out, B, H, T, d, 1, 1, eta, eta_tok};
+  ttt::LinearArgs a{q, k, v, w0, w0_batch_stride, z, w_out, B, H, T, d, 1, 1, eta, eta_tok, 0};
   const bool bf16 = io_dtype == TTT_BF16;
   hipError_t e;
   StreamBuffer ws;
@@ -153,10 +156,12 @@ int delta_rule_fwd(const void* q, const void* k, const void* v, const float* w0,
 int ttt_mlp_fwd(const void* q, const void* k, const void* v, const float* w1, const float* w2,
                 long long w_batch_stride, void* z, float* w1_out, float* w2_out, int B, int H,
                 int T, int d, int dh, int chunk, int causal, float eta, const float* eta_tok,
-                int io_dtype, ttt_stream_t stream) {
+                int loss, int io_dtype, ttt_stream_t stream) {
   g_last_error.clear();
   int rc = check_common("ttt_mlp_fwd", q, k, v, z, B, H, T, d, eta, eta_tok, io_dtype);
   if (rc != TTT_OK) return rc;
+  if (loss != TTT_LOSS_MSE && loss != TTT_LOSS_DOT)
+    return fail(TTT_E_INVALID, "ttt_mlp_fwd: unknown loss %d", loss);
   if (!w1 || !w2) return fail(TTT_E_INVALID, "ttt_mlp_fwd: w1 and w2 must be non-null");
   if (dh <= 0) return fail(TTT_E_INVALID, "ttt_mlp_fwd: dh must be positive (got %d)", dh);
   if (chunk < 1) return fail(TTT_E_INVALID, "ttt_mlp_fwd: chunk must be >= 1 (got %d)", chunk);
@@ -173,7 +178,7 @@ int ttt_mlp_fwd(const void* q, const void* k, const void* v, const float* w1, co
     return copy_state(w2_out, w2, w_batch_stride, B, H, per, s);
   }
   ttt::MlpArgs a{q, k, v, w1, w2, w_batch_stride, z, w1_out, w2_out,
-                 B, H, T, d, dh, chunk, causal, eta, eta_tok};
+                 B, H, T, d, dh, chunk, causal, eta, eta_tok, loss == TTT_LOSS_DOT ? 1 : 0};
   const bool bf16 = io_dtype == TTT_BF16;
   hipError_t e;
   StreamBuffer ws;

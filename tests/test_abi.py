@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ttt_abi_version() == 2
+    assert lib.ttt_abi_version() == 3
 
 
 FAKE = 0x1000  # never dereferenced: validation fails before any HIP call
@@ -47,20 +47,20 @@ FAKE = 0x1000  # never dereferenced: validation fails before any HIP call
 
 def _linear(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, w0=FAKE, stride=0, z=FAKE, w_out=None, B=1, H=1, T=16,
-             d=16, chunk=16, causal=1, eta=0.1, eta_tok=None, io=0)
+             d=16, chunk=16, causal=1, eta=0.1, eta_tok=None, loss=0, io=0)
     a.update(kw)
     return lib.ttt_linear_fwd(a["q"], a["k"], a["v"], a["w0"], a["stride"], a["z"], a["w_out"],
                               a["B"], a["H"], a["T"], a["d"], a["chunk"], a["causal"],
-                              a["eta"], a["eta_tok"], a["io"], None)
+                              a["eta"], a["eta_tok"], a["loss"], a["io"], None)
 
 
 def _mlp(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, w1=FAKE, w2=FAKE, stride=0, z=FAKE, B=1, H=1, T=16, d=16,
-             dh=32, chunk=16, causal=1, eta=0.1, eta_tok=None, io=0)
+             dh=32, chunk=16, causal=1, eta=0.1, eta_tok=None, loss=0, io=0)
     a.update(kw)
     return lib.ttt_mlp_fwd(a["q"], a["k"], a["v"], a["w1"], a["w2"], a["stride"], a["z"], None,
                            None, a["B"], a["H"], a["T"], a["d"], a["dh"], a["chunk"],
-                           a["causal"], a["eta"], a["eta_tok"], a["io"], None)
+                           a["causal"], a["eta"], a["eta_tok"], a["loss"], a["io"], None)
 
 
 def _delta(lib, **kw):
@@ -90,6 +90,7 @@ def _delta(lib, **kw):
     (dict(d=48), ttt.TTT_E_UNSUPPORTED, "d=48"),
     (dict(d=128), ttt.TTT_E_UNSUPPORTED, "d=128"),
     (dict(eta_tok=FAKE + 2), ttt.TTT_E_INVALID, "eta_tok"),
+    (dict(loss=2), ttt.TTT_E_INVALID, "loss"),
 ])
 def test_linear_rejects(lib, kw, code, msg):
     assert _linear(lib, **kw) == code
@@ -106,6 +107,7 @@ def test_linear_rejects(lib, kw, code, msg):
     (dict(io=2), ttt.TTT_E_INVALID, "dtype"),
     (dict(v=None), ttt.TTT_E_INVALID, "non-null"),
     (dict(eta_tok=FAKE + 1), ttt.TTT_E_INVALID, "eta_tok"),
+    (dict(loss=-1), ttt.TTT_E_INVALID, "loss"),
 ])
 def test_mlp_rejects(lib, kw, code, msg):
     assert _mlp(lib, **kw) == code

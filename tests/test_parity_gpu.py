@@ -19,16 +19,16 @@ def _note(msg):
     sys.stdout.flush()
 
 
-def _check(kind, w, inp, sel=None, state_tol=None):
+def _check(kind, w, inp, sel=None, state_tol=None, loss="mse"):
     _note(f"[parity] {kind} {w.name} B={w.B} H={w.H} T={w.T} d={w.d} h={w.h} chunk={w.chunk} "
-          f"causal={w.causal} io={w.io} seed={w.seed}")
+          f"causal={w.causal} io={w.io} seed={w.seed} loss={loss} rates={'eta_tok' in inp}")
     dev = to_device(inp, w.io)
-    out = run_gpu(kind, dev, w.eta, w.chunk, w.causal)
+    out = run_gpu(kind, dev, w.eta, w.chunk, w.causal, loss=loss)
     import torch
     torch.cuda.synchronize()
     z = to_np(out[0])
     states = [to_np(s) for s in out[1:]]
-    ref = run_oracle(kind, inp, w.eta, w.chunk, w.causal, sel)
+    ref = run_oracle(kind, inp, w.eta, w.chunk, w.causal, sel, loss=loss)
     if sel is not None:
         bs = [b for b, _ in sel]
         hs = [h for _, h in sel]
@@ -231,3 +231,45 @@ def test_token_rates_mlp_bf16_h256():
 def test_token_rates_mlp_vision():
     w = workload(4).replace(B=2, H=3, seed=130)
     _check("mlp", w, _with_rates(w, 8))
+
+
+# ------------------------------------------------------------------ dot-product loss
+# loss -v^T f(k): the error term of every gradient is -v (blog page, TTT / 如何理解; ViT3
+# news page, section 2); every kernel path against the oracle with loss="dot"
+
+@pytest.mark.parametrize("chunk,causal", [(5, True), (16, False)])
+def test_dot_loss_linear_fp32(chunk, causal):
+    w = workload(0).replace(B=2, H=2, T=61, d=32, chunk=chunk, causal=causal, init="normal",
+                            eta=0.1, seed=140 + chunk)
+    _check("linear", w, make_inputs(w), loss="dot")
+
+
+@pytest.mark.parametrize("T,rates", [(200, False), (333, True)])
+def test_dot_loss_linear_bf16_d64_chunk16(T, rates):
+    w = workload(1).replace(B=2, H=3, T=T, init="normal", eta=0.05, seed=150 + T)
+    inp = _with_rates(w, 9) if rates else make_inputs(w)
+    _check("linear", w, inp, loss="dot")
+
+
+@pytest.mark.parametrize("chunk,causal", [(4, True), (37, False)])
+def test_dot_loss_mlp_fp32(chunk, causal):
+    w = workload(3).replace(B=1, H=2, T=37, d=16, h=24, io="f32", chunk=chunk, causal=causal,
+                            seed=160 + chunk)
+    _check("mlp", w, make_inputs(w), loss="dot")
+
+
+@pytest.mark.parametrize("rates", [False, True])
+def test_dot_loss_mlp_bf16_h256(rates):
+    w = workload(3).replace(B=2, H=2, T=70, eta=0.05, seed=170)
+    _check("mlp", w, _with_rates(w, 10) if rates else make_inputs(w), loss="dot")
+
+
+@pytest.mark.parametrize("rates", [False, True])
+def test_dot_loss_mlp_vision(rates):
+    w = workload(4).replace(B=2, H=3, eta=0.1, seed=180)
+    _check("mlp", w, _with_rates(w, 11) if rates else make_inputs(w), loss="dot")
+
+
+def test_dot_loss_mlp_vision_config_full_size():
+    w = workload(4).replace(eta=0.1)
+    _check("mlp", w, make_inputs(w), loss="dot", sel=[(0, 0), (40, 5)])
