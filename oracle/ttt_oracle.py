@@ -55,6 +55,7 @@ __all__ = [
     "ttt_linear",
     "ttt_mlp",
     "delta_rule",
+    "ttt_linear_vjp",
 ]
 
 LOSSES = ("mse", "dot")
@@ -294,3 +295,56 @@ def delta_rule(q, k, v, w0, eta, dtype=np.float64, eta_tok=None):
             W = W + et[:, t, None, None] * np.einsum("ni,nj->nij", err, kt)
         z[:, t] = np.einsum("nij,nj->ni", W, q2[:, t])
     return z.reshape(tuple(lead) + (T, d)), W.reshape(tuple(lead) + (d, d))
+
+
+# ----------------------------------------------------------------------------------------
+# Gradients of the layer (outer-loop backward pass)
+# ----------------------------------------------------------------------------------------
+
+def ttt_linear_vjp(q, k, v, w0, eta, chunk, dz, dw_out=None):
+    """Vector-Jacobian product of the causal TTT-Linear layer (reconstruction loss).
+
+    The outer loop trains K, V, Q projections and the initial state by backpropagating
+    through the inner updates (wmrh.cn summary, section 2.2: the outer loop; "Fast weights"
+    page, opening paragraph: the slow parameters, initialisation and rate are trained on
+    the outer objective).  For upstream gradients dz [..., T, d] of z and dw_out [..., d, d]
+    of the final state (or None), returns (dq, dk, dv [..., T, d], dw0 [..., d, d]) with
+    dw0 per chain (not summed over a shared leading dimension).
+
+    The definition, written out: the primal recurrence of ttt_linear, in float64 torch
+    tensors, differentiated by torch.autograd (reverse mode) -- no hand-derived backward.
+    """
+    import torch
+    q2, lead = _flatten_tokens(q, np.float64)
+    k2, _ = _flatten_tokens(k, np.float64)
+    v2, _ = _flatten_tokens(v, np.float64)
+    N, T, d = q2.shape
+    W0 = _broadcast_state(w0, lead, np.float64)
+    dz2, _ = _flatten_tokens(dz, np.float64)
+    b = _check_chunk(T, chunk)
+    Q = torch.tensor(q2, requires_grad=True)
+    K = torch.tensor(k2, requires_grad=True)
+    V = torch.tensor(v2, requires_grad=True)
+    Wi = torch.tensor(W0, requires_grad=True)
+    W = Wi
+    zs = []
+    for c0 in range(0, T, b):
+        Wc = W
+        G = torch.zeros_like(Wc)
+        Wt = Wc
+        for t in range(c0, min(c0 + b, T)):
+            r = torch.einsum("nij,nj->ni", Wc, K[:, t]) - V[:, t]
+            G = G + torch.einsum("ni,nj->nij", r, K[:, t])
+            Wt = Wc - eta * G
+            zs.append(torch.einsum("nij,nj->ni", Wt, Q[:, t]))
+        W = Wt
+    Z = torch.stack(zs, dim=1) if zs else torch.zeros((N, 0, d), dtype=torch.float64)
+    outs, grads = [Z], [torch.tensor(dz2)]
+    if dw_out is not None:
+        outs.append(W)
+        grads.append(torch.tensor(_broadcast_state(dw_out, lead, np.float64)))
+    dq, dk, dv, dw0 = torch.autograd.grad(outs, (Q, K, V, Wi), grads, allow_unused=True)
+    shape = tuple(lead) + (T, d)
+    zero = lambda t: np.zeros((N, T, d)) if t is None else t.numpy()
+    return (zero(dq).reshape(shape), zero(dk).reshape(shape), zero(dv).reshape(shape),
+            (np.zeros_like(W0) if dw0 is None else dw0.numpy()).reshape(tuple(lead) + (d, d)))

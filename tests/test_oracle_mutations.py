@@ -58,6 +58,12 @@ MUTATIONS = {
     "delta_rule_ignores_token_rate": (
         'W = W + et[:, t, None, None] * np.einsum("ni,nj->nij", err, kt)',
         'W = W + eta * np.einsum("ni,nj->nij", err, kt)'),
+    "vjp_residual_at_current_weights": (
+        'r = torch.einsum("nij,nj->ni", Wc, K[:, t]) - V[:, t]',
+        'r = torch.einsum("nij,nj->ni", Wt, K[:, t]) - V[:, t]'),
+    "vjp_output_before_update": (
+        'zs.append(torch.einsum("nij,nj->ni", Wt, Q[:, t]))',
+        'zs.append(torch.einsum("nij,nj->ni", Wc, Q[:, t]))'),
     "noncausal_reads_initial_weights": (
         "    if not causal:\n        for t in range(T):\n            z[:, t] = linear_f(W, q2[:, t])",
         "    if not causal:\n        W = _broadcast_state(w0, lead, dtype)\n"

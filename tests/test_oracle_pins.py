@@ -527,6 +527,53 @@ def test_constant_token_rates_equal_scalar_rate():
         np.testing.assert_allclose(x, y, atol=1e-12)
 
 
+# ---------------------------------------------------------------- layer gradients
+# The vjp is pinned to central finite differences of the numpy forward (which shares no code
+# with the torch recurrence the vjp differentiates).
+
+def _fd_vjp(q, k, v, w0, eta, chunk, dz, dw, which, direction, h=1e-6):
+    args = dict(q=q, k=k, v=v, w0=w0)
+
+    def L(x):
+        a = dict(args)
+        a[which] = x
+        z, w = O.ttt_linear(a["q"], a["k"], a["v"], a["w0"], eta, chunk)
+        return float(np.sum(z * dz) + (np.sum(w * dw) if dw is not None else 0.0))
+    x = args[which]
+    return (L(x + h * direction) - L(x - h * direction)) / (2 * h)
+
+
+@pytest.mark.parametrize("chunk,with_dw", [(1, False), (4, True), (3, True), (10, False)])
+def test_linear_vjp_matches_finite_differences(chunk, with_dw):
+    rng = _rng(40 + chunk)
+    N, T, d = 2, 10, 4
+    q, k, v = _rand_chains(rng, N, T, d)
+    w0 = 0.3 * rng.standard_normal((N, d, d))
+    dz = rng.standard_normal((N, T, d))
+    dw = rng.standard_normal((N, d, d)) if with_dw else None
+    grads = dict(zip(("q", "k", "v", "w0"), O.ttt_linear_vjp(q, k, v, w0, 0.2, chunk, dz, dw)))
+    for which, x in (("q", q), ("k", k), ("v", v), ("w0", w0)):
+        for _ in range(2):
+            direction = rng.standard_normal(x.shape)
+            fd = _fd_vjp(q, k, v, w0, 0.2, chunk, dz, dw, which, direction)
+            an = float(np.sum(grads[which] * direction))
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (which, fd, an)
+
+
+def test_linear_vjp_zero_rate_is_the_fixed_map():
+    """eta = 0: z = W0 q, so dq = dz W0, dw0 = sum_t dz_t q_t^T (+ dw_out), dk = dv = 0."""
+    rng = _rng(45)
+    q, k, v = _rand_chains(rng, 1, 7, 3)
+    w0 = rng.standard_normal((1, 3, 3))
+    dz = rng.standard_normal((1, 7, 3))
+    dw = rng.standard_normal((1, 3, 3))
+    dq, dk, dv, dw0 = O.ttt_linear_vjp(q, k, v, w0, 0.0, 4, dz, dw)
+    np.testing.assert_allclose(dq[0], dz[0] @ w0[0], atol=1e-13)
+    np.testing.assert_allclose(dw0[0], dz[0].T @ q[0] + dw[0], atol=1e-13)
+    np.testing.assert_array_equal(dk, 0.0)
+    np.testing.assert_array_equal(dv, 0.0)
+
+
 # ---------------------------------------------------------------- edge cases
 
 def test_empty_sequence():
