@@ -122,6 +122,27 @@ def time_workload(w, steps, warmup, torch, ttt, rotate=None, rates=False, loss="
     }
 
 
+def time_backward(w, steps, warmup, torch, ttt):
+    """Event-timed ttt_linear_bwd calls on the workload (inputs resident in HBM)."""
+    dev = make_device_inputs(w, w.seed, torch)
+    g = torch.Generator(device="cuda").manual_seed(w.seed)
+    dz = torch.randn(dev["q"].shape, generator=g, device="cuda").to(dev["q"].dtype)
+    call = lambda: ttt.ttt_linear_bwd(dev["q"], dev["k"], dev["v"], dev["w0"], w.eta, w.chunk, dz)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        call()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    return {"ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3)}
+
+
 def cpu_baseline(w, budget_s=15.0):
     """Time the CPU oracle (float64, as it stands) on a bounded sample of the workload:
     full-length sequences of a few (batch, head) chains.  Returns tokens/s scaled to the
@@ -278,6 +299,13 @@ def main():
         variants.append((w, "+dot_loss", dict(loss="dot")))
         variants += [(o, "+dot_loss", dict(loss="dot")) for o in WORKLOADS
                      if o.name == "mlp_vision_N196"]
+        # backward pass of the headline workload (dz ~ N(0, 1), dw_out = 0)
+        if w.kind == "linear":
+            r = time_backward(w, max(10, args.steps // 2), 3, torch, ttt)
+            others[w.name + "+backward"] = {
+                "tokens_per_s": round(r["tokens_per_s"], 1),
+                "ms_per_step": round(r["ms_per_step"], 5),
+            }
         for o, tag, kw in variants:
             r = time_workload(o, max(10, args.steps // 2), 5, torch, ttt, **kw)
             others[o.name + tag] = {

@@ -106,6 +106,29 @@ int delta_rule_fwd(const void* q, const void* k, const void* v,
                    int B, int H, int T, int d, float eta, const float* eta_tok,
                    int io_dtype, ttt_stream_t stream);
 
+/*
+ * Backward pass of the causal TTT-Linear layer (reconstruction loss, scalar eta): the
+ * gradients the outer loop needs to train the projections and the initial state through
+ * the inner updates (wmrh.cn summary of Sun et al. 2024, section 2.2; "Fast weights" page,
+ * opening paragraph).  For the forward call ttt_linear_fwd(q, k, v, w0, ..., chunk,
+ * causal = 1, eta, NULL, TTT_LOSS_MSE) and upstream gradients dz of z and dw_out of the
+ * final state, writes
+ *   dq, dk, dv  [B][H][T][d] io_dtype (out)
+ *   dw0         [B][H][d][d] float32 (out): per (b, h) sequence; when w0 is shared over the
+ *               batch (w0_batch_stride 0) its gradient is the sum of dw0 over b.
+ *   dz          [B][H][T][d] io_dtype;  dw_out [B][H][d][d] float32 or NULL (zero).
+ * Supported: d in {16, 32, 64}, chunks of at most 16 tokens (min(chunk, T) <= 16), both
+ * dtypes.  The call recomputes the forward pass and keeps its chunk-start states in a
+ * stream-ordered workspace of B*H*ceil(T/chunk)*d*d*4 bytes.  T = 0 copies dw_out to dw0
+ * (zeros without it).
+ */
+int ttt_linear_bwd(const void* q, const void* k, const void* v,
+                   const float* w0, long long w0_batch_stride,
+                   const void* dz, const float* dw_out,
+                   void* dq, void* dk, void* dv, float* dw0,
+                   int B, int H, int T, int d, int chunk, float eta,
+                   int io_dtype, ttt_stream_t stream);
+
 /* Message for the calling thread's last non-OK status ("" if none).  Owned by the library;
    valid until the thread's next call into it. */
 const char* ttt_last_error(void);

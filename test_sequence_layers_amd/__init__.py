@@ -1,7 +1,7 @@
-"""MI355X-native (gfx950) TTT-layer forward pass.
+"""MI355X-native (gfx950) TTT layers.
 
 The compute runs in libttt.so (C ABI, include/ttt.h): hand-written HIP kernels for the
-TTT-Linear, TTT-MLP and delta-rule forward passes.  This package holds the ctypes binding
+TTT-Linear, TTT-MLP and delta-rule forward passes and the TTT-Linear backward pass.  This package holds the ctypes binding
 (argument marshalling only), the in-tree build script and the seeded synthetic workloads.
 """
 from ._binding import (  # noqa: F401
@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     delta_rule_fwd,
     last_error,
     load_library,
+    ttt_linear_bwd,
     ttt_linear_fwd,
     ttt_mlp_fwd,
 )

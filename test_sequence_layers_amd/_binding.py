@@ -30,6 +30,8 @@ SIGNATURES = {
     "ttt_mlp_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp,
                          _i, _i, _i, _i, _i, _i, _i, _f, _vp, _i, _i, _vp]),
     "delta_rule_fwd": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _i, _i, _i, _i, _f, _vp, _i, _vp]),
+    "ttt_linear_bwd": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp, _vp, _vp, _vp,
+                            _i, _i, _i, _i, _i, _f, _i, _vp]),
     "ttt_last_error": (ctypes.c_char_p, []),
     "ttt_abi_version": (_i, []),
 }
@@ -178,6 +180,34 @@ def ttt_linear_fwd(q, k, v, w0, eta, chunk, causal=True, *, eta_tok=None, loss="
                                 _io_dtype(q), _stream(q.device, stream))
     _check(rc)
     return (z, w_out) if w_out is not None else z
+
+
+def ttt_linear_bwd(q, k, v, w0, eta, chunk, dz, dw_out=None, *, stream=None):
+    """Gradients of the causal TTT-Linear layer (reconstruction loss, scalar eta) for the
+    upstream gradients dz [B,H,T,d] (dtype of q) and dw_out [B,H,d,d] float32 (or None).
+    Returns (dq, dk, dv, dw0) with dw0 [B,H,d,d] per sequence (sum it over the batch when w0
+    is shared)."""
+    torch = _torch()
+    lib = load_library()
+    B, H, T, d = _tokens(q, k, v)
+    w0, stride = _state(w0, B, H, (d, d), "w0", q.device)
+    if (not isinstance(dz, torch.Tensor) or tuple(dz.shape) != (B, H, T, d) or dz.dtype != q.dtype
+            or dz.device != q.device or not dz.is_contiguous()):
+        raise ValueError(f"dz must be a contiguous {q.dtype} tensor of shape {(B, H, T, d)}")
+    if dw_out is not None:
+        dw_out = _out(dw_out, (B, H, d, d), torch.float32, q.device, "dw_out")
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(q)
+    dv = torch.empty_like(q)
+    dw0 = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        rc = lib.ttt_linear_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), w0.data_ptr(), stride,
+                                dz.data_ptr(), dw_out.data_ptr() if dw_out is not None else None,
+                                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dw0.data_ptr(),
+                                B, H, T, d, int(chunk), float(eta), _io_dtype(q),
+                                _stream(q.device, stream))
+    _check(rc)
+    return dq, dk, dv, dw0
 
 
 def delta_rule_fwd(q, k, v, w0, eta, *, eta_tok=None, z=None, w_out=None, return_state=False,

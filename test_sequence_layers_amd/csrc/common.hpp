@@ -39,6 +39,23 @@ struct LinearArgs {
   float eta;
   const float* eta_tok;  // per-token rate factors [B][H][T] (rate eta * eta_tok[t]) or null
   int dot_loss;          // 1: loss -v^T f(k), error term -v; 0: 1/2 ||f(k) - v||^2
+  float* w_hist;         // generic kernel only: chunk-start states [B][H][nchunks][d][d] or null
+};
+
+// Backward pass of the causal TTT-Linear layer (reconstruction loss, scalar rate).
+struct LinearBwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dz;
+  const float* dw_out;  // upstream gradient of the final state [B][H][d][d] or null
+  const float* w_hist;  // chunk-start states [B][H][nchunks][d][d] (from the forward)
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dw0;           // [B][H][d][d]
+  int B, H, T, d, chunk;
+  float eta;
 };
 
 struct MlpArgs {
@@ -74,7 +91,10 @@ hipError_t launch_mlp_fast(const MlpArgs& a, hipStream_t s);
 bool mlp_nc_supported(const MlpArgs& a, bool bf16_io);
 hipError_t launch_mlp_nc(const MlpArgs& a, hipStream_t s);
 
-// dst[b][h][:] = src + b * batch_stride + h * per_head (the state when T = 0).
+hipError_t launch_linear_bwd_generic(const LinearBwdArgs& a, bool bf16_io, hipStream_t s);
+
+// dst[b][h][:] = src + b * batch_stride + h * per_head (the state when T = 0); zeros when
+// src is null.
 hipError_t launch_copy_state(float* dst, const float* src, long long batch_stride, int B, int H,
                              size_t per_head, hipStream_t s);
 

@@ -61,8 +61,13 @@ __global__ __launch_bounds__(kThreads) void linear_generic_kernel(LinearArgs a) 
   __syncthreads();
 
   const int b = T > 0 ? min(a.chunk, T) : 1;
+  const int nchunks = (T + b - 1) / b;
   for (int c0 = 0; c0 < T; c0 += b) {
     const int cend = min(c0 + b, T);
+    if (a.w_hist) {  // chunk-start state, for the backward pass
+      float* wh = a.w_hist + (static_cast<size_t>(chain) * nchunks + c0 / b) * D * D;
+      for (int e = tid; e < D * D; e += kThreads) wh[e] = Wc[e / D][e % D];
+    }
     for (int s0 = c0; s0 < cend; s0 += kSub) {
       const int n = min(kSub, cend - s0);
       for (int e = tid; e < kSub * D; e += kThreads) {
@@ -96,7 +101,7 @@ __global__ __launch_bounds__(kThreads) void linear_generic_kernel(LinearArgs a) 
         }
       }
       __syncthreads();
-      if (a.causal) {
+      if (a.causal && a.z) {
         for (int e = tid; e < kSub * D; e += kThreads) {
           const int t = e / D, i = e % D;
           if (t >= n) continue;
@@ -121,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void linear_generic_kernel(LinearArgs a) 
     __syncthreads();
   }
 
-  if (!a.causal) {
+  if (!a.causal && a.z) {
     for (int s0 = 0; s0 < T; s0 += kSub) {
       const int n = min(kSub, T - s0);
       for (int e = tid; e < kSub * D; e += kThreads) {

@@ -153,6 +153,46 @@ int delta_rule_fwd(const void* q, const void* k, const void* v, const float* w0,
   return TTT_OK;
 }
 
+int ttt_linear_bwd(const void* q, const void* k, const void* v, const float* w0,
+                   long long w0_batch_stride, const void* dz, const float* dw_out, void* dq,
+                   void* dk, void* dv, float* dw0, int B, int H, int T, int d, int chunk,
+                   float eta, int io_dtype, ttt_stream_t stream) {
+  g_last_error.clear();
+  int rc = check_common("ttt_linear_bwd", q, k, v, dz, B, H, T, d, eta, nullptr, io_dtype);
+  if (rc != TTT_OK) return rc;
+  if (!w0 || !dw0) return fail(TTT_E_INVALID, "ttt_linear_bwd: w0 and dw0 must be non-null");
+  if (T > 0 && (!dq || !dk || !dv))
+    return fail(TTT_E_INVALID, "ttt_linear_bwd: dq, dk and dv must be non-null");
+  if (chunk < 1) return fail(TTT_E_INVALID, "ttt_linear_bwd: chunk must be >= 1 (got %d)", chunk);
+  if (w0_batch_stride < 0) return fail(TTT_E_INVALID, "ttt_linear_bwd: negative w0_batch_stride");
+  if (d != 16 && d != 32 && d != 64)
+    return fail(TTT_E_UNSUPPORTED, "ttt_linear_bwd: d=%d not supported (16, 32, 64)", d);
+  if (T > 0 && (chunk < T ? chunk : T) > 16)
+    return fail(TTT_E_UNSUPPORTED, "ttt_linear_bwd: chunks of more than 16 tokens not supported");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t dd = static_cast<size_t>(d) * d;
+  if (T == 0) return copy_state(dw0, dw_out, static_cast<long long>(H) * dd, B, H, dd, s);
+
+  // chunk-start states of the forward pass, recomputed into a stream-ordered workspace
+  const int b = chunk < T ? chunk : T;
+  const long long nchunks = (T + b - 1) / b;
+  if (!fits_int64(B, H, nchunks, static_cast<long long>(dd)))
+    return fail(TTT_E_INVALID, "ttt_linear_bwd: state history overflows");
+  StreamBuffer ws;
+  rc = get_workspace(static_cast<size_t>(B) * H * nchunks * dd * sizeof(float), s, &ws);
+  if (rc != TTT_OK) return rc;
+  const bool bf16 = io_dtype == TTT_BF16;
+  ttt::LinearArgs f{q, k, v, w0, w0_batch_stride, nullptr, nullptr, B, H, T, d, chunk, 1, eta,
+                    nullptr, 0, static_cast<float*>(ws.ptr)};
+  hipError_t e = ttt::launch_linear_generic(f, bf16, s);
+  if (e != hipSuccess) return hip_fail(e, "ttt_linear_bwd state launch");
+  ttt::LinearBwdArgs g{q, k, v, dz, dw_out, static_cast<const float*>(ws.ptr), dq, dk, dv, dw0,
+                       B, H, T, d, chunk, eta};
+  e = ttt::launch_linear_bwd_generic(g, bf16, s);
+  if (e != hipSuccess) return hip_fail(e, "ttt_linear_bwd launch");
+  return TTT_OK;
+}
+
 int ttt_mlp_fwd(const void* q, const void* k, const void* v, const float* w1, const float* w2,
                 long long w_batch_stride, void* z, float* w1_out, float* w2_out, int B, int H,
                 int T, int d, int dh, int chunk, int causal, float eta, const float* eta_tok,

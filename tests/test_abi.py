@@ -28,7 +28,7 @@ def lib():
 
 def test_header_declares_the_three_entry_points():
     names = _declared_functions()
-    for n in ("ttt_linear_fwd", "ttt_mlp_fwd", "delta_rule_fwd", "ttt_last_error"):
+    for n in ("ttt_linear_fwd", "ttt_mlp_fwd", "delta_rule_fwd", "ttt_linear_bwd", "ttt_last_error"):
         assert n in names
 
 
@@ -123,6 +123,31 @@ def test_mlp_rejects(lib, kw, code, msg):
 ])
 def test_delta_rejects(lib, kw, code, msg):
     assert _delta(lib, **kw) == code
+    assert msg in ttt.last_error()
+
+
+def _bwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, w0=FAKE, stride=0, dz=FAKE, dw_out=None, dq=FAKE, dk=FAKE,
+             dv=FAKE, dw0=FAKE, B=1, H=1, T=16, d=16, chunk=16, eta=0.1, io=0)
+    a.update(kw)
+    return lib.ttt_linear_bwd(a["q"], a["k"], a["v"], a["w0"], a["stride"], a["dz"], a["dw_out"],
+                              a["dq"], a["dk"], a["dv"], a["dw0"], a["B"], a["H"], a["T"],
+                              a["d"], a["chunk"], a["eta"], a["io"], None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(dz=None), ttt.TTT_E_INVALID, "non-null"),
+    (dict(dq=None), ttt.TTT_E_INVALID, "dq"),
+    (dict(dw0=None), ttt.TTT_E_INVALID, "dw0"),
+    (dict(w0=None), ttt.TTT_E_INVALID, "w0"),
+    (dict(chunk=0), ttt.TTT_E_INVALID, "chunk"),
+    (dict(eta=float("nan")), ttt.TTT_E_INVALID, "finite"),
+    (dict(io=3), ttt.TTT_E_INVALID, "dtype"),
+    (dict(d=48), ttt.TTT_E_UNSUPPORTED, "d=48"),
+    (dict(chunk=32, T=64), ttt.TTT_E_UNSUPPORTED, "16 tokens"),
+])
+def test_linear_bwd_rejects(lib, kw, code, msg):
+    assert _bwd(lib, **kw) == code
     assert msg in ttt.last_error()
 
 

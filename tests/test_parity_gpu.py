@@ -273,3 +273,76 @@ def test_dot_loss_mlp_vision(rates):
 def test_dot_loss_mlp_vision_config_full_size():
     w = workload(4).replace(eta=0.1)
     _check("mlp", w, make_inputs(w), loss="dot", sel=[(0, 0), (40, 5)])
+
+
+# ------------------------------------------------------------------ backward pass
+# ttt_linear_bwd against the oracle's vector-Jacobian product (autograd of the primal
+# recurrence in float64, pinned to finite differences)
+
+def _check_bwd(w, inp, with_dw, sel=None, seed=0):
+    import torch
+    import test_sequence_layers_amd as ttt
+    from oracle import ttt_oracle as O
+    _note(f"[parity] linear_bwd B={w.B} H={w.H} T={w.T} d={w.d} chunk={w.chunk} io={w.io} "
+          f"dw_out={with_dw} seed={w.seed}")
+    rng = np.random.default_rng(20_000 + seed)
+    dz = rng.standard_normal((w.B, w.H, w.T, w.d)).astype(np.float32)
+    if w.io == "bf16":
+        dz = to_np(torch.from_numpy(dz).to(torch.bfloat16))
+    dw = rng.standard_normal((w.B, w.H, w.d, w.d)).astype(np.float32) if with_dw else None
+    dev = to_device(inp, w.io)
+    dt = dev["q"].dtype
+    dzd = torch.from_numpy(dz).to("cuda").to(dt).contiguous()
+    dwd = torch.from_numpy(dw).to("cuda").contiguous() if with_dw else None
+    out = ttt.ttt_linear_bwd(dev["q"], dev["k"], dev["v"], dev["w0"], w.eta, w.chunk, dzd, dwd)
+    torch.cuda.synchronize()
+    got = [to_np(t) for t in out]
+    q, k, v, dzz = inp["q"], inp["k"], inp["v"], dz
+    w0 = np.broadcast_to(inp["w0"], (w.B, w.H, w.d, w.d)) if inp["w0"].ndim == 3 else inp["w0"]
+    dww = dw
+    if sel is not None:
+        bs = [b for b, _ in sel]
+        hs = [h for _, h in sel]
+        q, k, v, dzz, w0 = q[bs, hs][None], k[bs, hs][None], v[bs, hs][None], dzz[bs, hs][None], w0[bs, hs][None]
+        dww = dw[bs, hs][None] if dw is not None else None
+        got = [g[bs, hs][None] for g in got]
+    ref = O.ttt_linear_vjp(q, k, v, w0, w.eta, w.chunk, dzz, dww)
+    tol = tol_for(w.io)
+    for name, g, r in zip(("dq", "dk", "dv", "dw0"), got, ref):
+        assert np.isfinite(g).all(), name
+        rel, _ = slab_rel(g, r)
+        _note(f"[parity]   {name} rel {rel:.3e} (tol {tol})")
+        assert rel <= tol, (name, rel)
+
+
+@pytest.mark.parametrize("d,chunk,with_dw", [(16, 4, True), (16, 1, False), (32, 16, True),
+                                             (16, 37, False)])
+def test_linear_bwd_fp32(d, chunk, with_dw):
+    w = workload(0).replace(B=2, H=2, T=37 if chunk != 37 else 13, d=d, chunk=chunk,
+                            init="normal", eta=0.3, seed=190 + d + chunk)
+    _check_bwd(w, make_inputs(w), with_dw, seed=d + chunk)
+
+
+@pytest.mark.parametrize("T", [16, 200])
+def test_linear_bwd_bf16_d64_chunk16(T):
+    w = workload(1).replace(B=2, H=3, T=T, seed=200 + T)
+    _check_bwd(w, make_inputs(w), True, seed=T)
+
+
+def test_linear_bwd_config_full_size_sampled():
+    w = workload(1)
+    _check_bwd(w, make_inputs(w), True, sel=[(6, 4)], seed=1)
+
+
+def test_linear_bwd_empty_sequence_copies_dw_out():
+    import torch
+    import test_sequence_layers_amd as ttt
+    q = torch.zeros((2, 3, 0, 16), device="cuda")
+    w0 = torch.randn((3, 16, 16), device="cuda")
+    dw = torch.randn((2, 3, 16, 16), device="cuda")
+    dq, dk, dv, dw0 = ttt.ttt_linear_bwd(q, q, q, w0, 0.1, 16, q, dw)
+    torch.cuda.synchronize()
+    assert torch.equal(dw0, dw)
+    _, _, _, dw0 = ttt.ttt_linear_bwd(q, q, q, w0, 0.1, 16, q)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dw0).item() == 0
