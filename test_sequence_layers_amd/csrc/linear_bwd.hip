@@ -1,6 +1,7 @@
 // Backward pass of the causal TTT-Linear layer on the vector ALUs (reconstruction loss,
-// scalar rate, chunk <= 16, fp32 or bf16 I/O, d in {16, 32, 64}).  One workgroup of 256
-// threads per (batch, head) chain walks the chunks from last to first.
+// scalar rate, chunk <= 16, fp32 or bf16 I/O, d in {16, 32, 64}).  One workgroup of 1024
+// threads (16 waves, four per SIMD, which hides the LDS latency of the short dot products)
+// per (batch, head) chain walks the chunks from last to first.
 //
 // The outer loop trains the projections and the initial state through the inner updates
 // (wmrh.cn summary of Sun et al. 2024, section 2.2; "Fast weights" page, opening
@@ -21,7 +22,7 @@
 namespace ttt {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;
 constexpr int kMaxB = 16;
 
 template <typename IO, int D>

@@ -1,5 +1,6 @@
 // Generic TTT-Linear forward on the vector ALUs: any chunk size, causal or not, fp32 or
-// bf16 I/O, d in {16, 32, 64}.  One workgroup of 256 threads per (batch, head) chain.
+// bf16 I/O, d in {16, 32, 64}.  One workgroup of 1024 threads (16 waves, four per SIMD, so
+// the LDS latency of the small dot products is hidden) per (batch, head) chain.
 //
 // Method: mini-batch gradient descent on 1/2 ||W k - v||^2 (gradient (W k - v) k^T,
 // "Fast weights" page, section 1), or on the negative dot product -v^T W k (gradient
@@ -26,7 +27,7 @@
 namespace ttt {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;
 constexpr int kSub = 16;
 
 template <typename IO, int D>
