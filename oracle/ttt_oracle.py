@@ -33,7 +33,11 @@ define the method; no line numbers are given on purpose):
   (blog page "TTT / 通用表示"; "Fast weights" page opening formula).
 * Non-causal variant (ViT3 news page, "1. inner training setup", observation 2): the keys
   and values are used as a small data set to train the inner model (here: one pass of
-  mini-batch GD over all chunks), and every query then reads the final weights.
+  mini-batch GD over all chunks), and every query then reads the final weights.  The same
+  page (observation 2, the figure on inner batch size and epochs) splits the N pairs into
+  consecutive mini-batches (several updates per epoch) and trains for several epochs; an
+  epoch here is one such pass over every chunk in order, starting from the weights the
+  previous epoch left (optional `epochs`, non-causal only).
 
 The recurrence is written out literally: the gradient of each token is materialised, the
 per-token weights W_t are materialised, and there is no blocking, fusion or dual form.
@@ -170,6 +174,15 @@ def _token_rates(eta, eta_tok, lead, T, dtype):
     return dtype(eta) * np.array(r.reshape(n, T), dtype=dtype, copy=True)
 
 
+def _check_epochs(epochs, causal):
+    if not (isinstance(epochs, (int, np.integer)) and epochs >= 1):
+        raise ValueError("epochs must be a positive integer")
+    # A second pass would let a causal output see tokens after its own position.
+    if causal and epochs != 1:
+        raise ValueError("several epochs are defined for the non-causal layer only")
+    return int(epochs)
+
+
 def _check_chunk(T, chunk):
     if not (isinstance(chunk, (int, np.integer)) and chunk >= 1):
         raise ValueError("chunk must be a positive integer")
@@ -181,7 +194,8 @@ def _check_chunk(T, chunk):
 # The recurrences
 # ----------------------------------------------------------------------------------------
 
-def ttt_linear(q, k, v, w0, eta, chunk, causal=True, loss="mse", dtype=np.float64, eta_tok=None):
+def ttt_linear(q, k, v, w0, eta, chunk, causal=True, loss="mse", dtype=np.float64, eta_tok=None,
+               epochs=1):
     """TTT layer with the linear inner model, mini-batch GD of size `chunk`.
 
     q, k, v: [..., T, d]; w0: [..., d, d] (broadcast over the leading dims, e.g. [H, d, d]
@@ -189,7 +203,8 @@ def ttt_linear(q, k, v, w0, eta, chunk, causal=True, loss="mse", dtype=np.float6
     Returns (z [..., T, d], w_final [..., d, d]).
 
     The last chunk is shorter when T is not a multiple of `chunk`.  causal=False trains
-    over every chunk first and then applies the final weights to every query.
+    over every chunk first (`epochs` passes) and then applies the final weights to every
+    query.
     """
     if loss not in LOSSES:
         raise ValueError(loss)
@@ -199,10 +214,12 @@ def ttt_linear(q, k, v, w0, eta, chunk, causal=True, loss="mse", dtype=np.float6
     N, T, d = q2.shape
     W = _broadcast_state(w0, lead, dtype)
     b = _check_chunk(T, chunk)
+    epochs = _check_epochs(epochs, causal)
     et = _token_rates(eta, eta_tok, lead, T, dtype)
     eta = dtype(eta)
     z = np.zeros((N, T, d), dtype=dtype)
-    for c0 in range(0, T, b):
+    chunk_starts = [c0 for _ in range(epochs) for c0 in range(0, T, b)]
+    for c0 in chunk_starts:
         Wc = W.copy()                      # weights left by the previous mini-batch
         G = np.zeros_like(Wc)              # running sum of this mini-batch's gradients
         Wt = Wc
@@ -222,11 +239,13 @@ def ttt_linear(q, k, v, w0, eta, chunk, causal=True, loss="mse", dtype=np.float6
     return z.reshape(tuple(lead) + (T, d)), W.reshape(tuple(lead) + (d, d))
 
 
-def ttt_mlp(q, k, v, w1, w2, eta, chunk, causal=True, loss="mse", dtype=np.float64, eta_tok=None):
+def ttt_mlp(q, k, v, w1, w2, eta, chunk, causal=True, loss="mse", dtype=np.float64, eta_tok=None,
+            epochs=1):
     """TTT layer with the 2-layer SiLU MLP inner model, mini-batch GD of size `chunk`.
 
     q, k, v: [..., T, d]; w1: [..., h, d]; w2: [..., d, h] (broadcast over the leading
-    dims); eta_tok: optional per-token rate factors [..., T].
+    dims); eta_tok: optional per-token rate factors [..., T]; epochs: passes over the
+    chunks before the queries are read (non-causal only).
     Returns (z [..., T, d], w1_final [..., h, d], w2_final [..., d, h]).
     """
     if loss not in LOSSES:
@@ -241,10 +260,12 @@ def ttt_mlp(q, k, v, w1, w2, eta, chunk, causal=True, loss="mse", dtype=np.float
     if W1.shape[-1] != d or W2.shape[-2:] != (d, h):
         raise ValueError("w1 must be [..., h, d] and w2 [..., d, h]")
     b = _check_chunk(T, chunk)
+    epochs = _check_epochs(epochs, causal)
     et = _token_rates(eta, eta_tok, lead, T, dtype)
     eta = dtype(eta)
     z = np.zeros((N, T, d), dtype=dtype)
-    for c0 in range(0, T, b):
+    chunk_starts = [c0 for _ in range(epochs) for c0 in range(0, T, b)]
+    for c0 in chunk_starts:
         W1c, W2c = W1.copy(), W2.copy()
         G1 = np.zeros_like(W1c)
         G2 = np.zeros_like(W2c)

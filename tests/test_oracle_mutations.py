@@ -64,6 +64,16 @@ MUTATIONS = {
     "vjp_output_before_update": (
         'zs.append(torch.einsum("nij,nj->ni", Wt, Q[:, t]))',
         'zs.append(torch.einsum("nij,nj->ni", Wc, Q[:, t]))'),
+    "epochs_ignored": (
+        "chunk_starts = [c0 for _ in range(epochs) for c0", "chunk_starts = [c0 for _ in range(1) for c0"),
+    "mlp_epochs_ignored": (
+        "    chunk_starts = [c0 for _ in range(epochs) for c0 in range(0, T, b)]\n    for c0 in chunk_starts:\n        W1c",
+        "    chunk_starts = [c0 for _ in range(1) for c0 in range(0, T, b)]\n    for c0 in chunk_starts:\n        W1c"),
+    "epoch_restarts_from_initial_weights": (
+        "    for c0 in chunk_starts:\n        Wc = W.copy()",
+        "    for i, c0 in enumerate(chunk_starts):\n"
+        "        W = _broadcast_state(w0, lead, dtype) if (i and c0 == 0) else W\n"
+        "        Wc = W.copy()"),
     "noncausal_reads_initial_weights": (
         "    if not causal:\n        for t in range(T):\n            z[:, t] = linear_f(W, q2[:, t])",
         "    if not causal:\n        W = _broadcast_state(w0, lead, dtype)\n"

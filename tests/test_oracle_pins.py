@@ -354,16 +354,20 @@ def test_state_broadcast_over_batch():
 
 # ---------------------------------------------------------------- torch.autograd
 
-def _autograd_chunked(q, k, v, params, f, eta, chunk, causal):
+def _autograd_chunked(q, k, v, params, f, eta, chunk, causal, epochs=1):
     """Mini-batch GD computed with torch.autograd for the gradients (float64, CPU).  eta is
-    a scalar, or one rate per token (each token's gradient scaled by its own rate)."""
+    a scalar, or one rate per token (each token's gradient scaled by its own rate); the
+    non-causal layer may pass over the chunks several times (epochs)."""
     import torch
     T = q.shape[0]
     P = [torch.tensor(p, dtype=torch.float64) for p in params]
     Q, K, V = (torch.tensor(x, dtype=torch.float64) for x in (q, k, v))
     Z = torch.zeros_like(Q)
     per_token = np.ndim(eta) > 0
-    for c0 in range(0, T, chunk):
+    starts = []
+    for _ in range(epochs):
+        starts += list(range(0, T, chunk))
+    for c0 in starts:
         Pc = [p.clone().requires_grad_(True) for p in P]
         acc = [torch.zeros_like(p) for p in P]
         cur = P
@@ -420,6 +424,72 @@ def test_linear_matches_autograd(chunk, causal):
     zr, (wr,) = _autograd_chunked(q[0], k[0], v[0], [w0], _torch_linear, 0.1, chunk, causal)
     np.testing.assert_allclose(z, zr, atol=1e-12)
     np.testing.assert_allclose(w, wr, atol=1e-12)
+
+
+# ---------------------------------------------------------------- epochs (non-causal)
+# ViT3 news page, observation 2 and its figure on inner batch size and epochs: the N pairs
+# are split into consecutive mini-batches and the inner model is trained for several
+# epochs before every query reads the final weights.
+
+@pytest.mark.parametrize("epochs,rates", [(1, False), (2, False), (5, False), (3, True)])
+def test_noncausal_full_batch_epochs_closed_form(epochs, rates):
+    # Full-batch GD on sum_t r_t/2 ||W k_t - v_t||^2 is the affine map
+    # W -> W (I - eta K^T D K) + eta V^T D K (D = diag(r)), whose fixed point is
+    # W* = V^T D K (K^T D K)^{-1}; after E steps W_E = W* + (W0 - W*) (I - eta K^T D K)^E.
+    rng = _rng(40)
+    T, d = 11, 4
+    q, k, v = (x[0] for x in _rand_chains(rng, 1, T, d))
+    w0 = 0.3 * rng.standard_normal((d, d))
+    eta = 0.05
+    r = rng.uniform(0.2, 1.0, T) if rates else np.ones(T)
+    z, w = O.ttt_linear(q, k, v, w0, eta, T, causal=False, epochs=epochs,
+                        eta_tok=r if rates else None)
+    KDK = k.T @ (r[:, None] * k)
+    Wstar = v.T @ (r[:, None] * k) @ np.linalg.inv(KDK)
+    WE = Wstar + (w0 - Wstar) @ np.linalg.matrix_power(np.eye(d) - eta * KDK, epochs)
+    np.testing.assert_allclose(w, WE, atol=1e-10)
+    np.testing.assert_allclose(z, q @ WE.T, atol=1e-10)
+
+
+@pytest.mark.parametrize("chunk,epochs", [(3, 2), (7, 4), (20, 3)])
+def test_noncausal_dot_loss_epochs_add_up(chunk, epochs):
+    # The dot loss's gradient -v k^T does not depend on W, so every chunking and epoch
+    # count give W0 + E eta V^T K.
+    rng = _rng(41)
+    T, d = 20, 5
+    q, k, v = (x[0] for x in _rand_chains(rng, 1, T, d))
+    w0 = rng.standard_normal((d, d))
+    z, w = O.ttt_linear(q, k, v, w0, 0.07, chunk, causal=False, loss="dot", epochs=epochs)
+    WE = w0 + epochs * 0.07 * v.T @ k
+    np.testing.assert_allclose(w, WE, atol=1e-12)
+    np.testing.assert_allclose(z, q @ WE.T, atol=1e-12)
+
+
+@pytest.mark.parametrize("model,chunk,epochs", [("linear", 6, 2), ("linear", 14, 3),
+                                                ("mlp", 5, 3), ("mlp", 13, 2)])
+def test_epochs_match_autograd(model, chunk, epochs):
+    rng = _rng(42)
+    q, k, v = (x[0] for x in _rand_chains(rng, 1, 13, 3))
+    if model == "linear":
+        params, f = [0.3 * rng.standard_normal((3, 3))], _torch_linear
+        z, *w = O.ttt_linear(q, k, v, params[0], 0.1, chunk, causal=False, epochs=epochs)
+    else:
+        params = [0.5 * rng.standard_normal((6, 3)), 0.5 * rng.standard_normal((3, 6))]
+        f = _torch_mlp
+        z, *w = O.ttt_mlp(q, k, v, params[0], params[1], 0.1, chunk, causal=False,
+                          epochs=epochs)
+    zr, wr = _autograd_chunked(q, k, v, params, f, 0.1, chunk, False, epochs=epochs)
+    np.testing.assert_allclose(z, zr, atol=1e-12)
+    for a, b in zip(w, wr):
+        np.testing.assert_allclose(a, b, atol=1e-12)
+
+
+def test_causal_layer_rejects_epochs():
+    q = k = v = np.zeros((4, 2))
+    with pytest.raises(ValueError):
+        O.ttt_linear(q, k, v, np.zeros((2, 2)), 0.1, 2, causal=True, epochs=2)
+    with pytest.raises(ValueError):
+        O.ttt_mlp(q, k, v, np.zeros((3, 2)), np.zeros((2, 3)), 0.1, 2, causal=True, epochs=2)
 
 
 # ---------------------------------------------------------------- per-token rates
