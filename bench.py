@@ -25,9 +25,10 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 FP32_VALU_PEAK_TFLOPS = 157.3
 
 
-def algorithmic_cost(w):
+def algorithmic_cost(w, epochs=1):
     """(bytes, flops) of one forward call: Q, K, V read + Z written + initial state read;
-    flops of the method (tril-masked b x b products counted at half)."""
+    flops of the method (tril-masked b x b products counted at half).  With several epochs
+    (non-causal) the training flops repeat per epoch; the bytes stay those read once."""
     esz = 2 if w.io == "bf16" else 4
     tok = w.B * w.H * w.T * w.d * esz
     if w.kind in ("linear", "delta"):
@@ -35,11 +36,12 @@ def algorithmic_cost(w):
         b = 1 if w.kind == "delta" else min(w.chunk, w.T)
         # R = K W^T - V, Q W^T, W update: 3 x 2 d^2 per head-token; tril(QK^T) and P R:
         # 2 x (b/2) x 2d ... counted as 2 b d per head-token.
-        fl = w.B * w.H * w.T * (6 * w.d * w.d + (2 * b * w.d if b > 1 else 0))
+        fl = w.B * w.H * w.T * ((4 * epochs + 2) * w.d * w.d + (2 * b * w.d if b > 1 else 0))
     else:
         state = 2 * w.H * w.d * w.h * 4
         b = min(w.chunk, w.T)
-        per = 14 * w.d * w.h + (2 * b * (w.d + w.h) if w.causal else 0)
+        # training: U, O, R W2, both gradient sums (10 d h); queries: 4 d h
+        per = (10 * epochs + 4) * w.d * w.h + (2 * b * (w.d + w.h) if w.causal else 0)
         fl = w.B * w.H * w.T * per
     return 4 * tok + state, fl
 
@@ -79,20 +81,20 @@ def make_device_inputs(w, seed, torch, rates=False):
     return dev
 
 
-def launch(w, dev, ttt, loss="mse"):
+def launch(w, dev, ttt, loss="mse", epochs=1):
     et = dev.get("eta_tok")
     if w.kind == "linear":
         ttt.ttt_linear_fwd(dev["q"], dev["k"], dev["v"], dev["w0"], w.eta, w.chunk, w.causal,
-                           eta_tok=et, loss=loss, z=dev["z"])
+                           eta_tok=et, loss=loss, epochs=epochs, z=dev["z"])
     elif w.kind == "delta":
         ttt.delta_rule_fwd(dev["q"], dev["k"], dev["v"], dev["w0"], w.eta, eta_tok=et, z=dev["z"])
     else:
         ttt.ttt_mlp_fwd(dev["q"], dev["k"], dev["v"], dev["w1"], dev["w2"], w.eta, w.chunk,
-                        w.causal, eta_tok=et, loss=loss, z=dev["z"])
+                        w.causal, eta_tok=et, loss=loss, epochs=epochs, z=dev["z"])
 
 
-def time_workload(w, steps, warmup, torch, ttt, rotate=None, rates=False, loss="mse"):
-    bytes_, flops = algorithmic_cost(w)
+def time_workload(w, steps, warmup, torch, ttt, rotate=None, rates=False, loss="mse", epochs=1):
+    bytes_, flops = algorithmic_cost(w, epochs)
     if rates:
         bytes_ += w.B * w.H * w.T * 4  # the rate factors, read once
     if rotate is None:
@@ -100,13 +102,13 @@ def time_workload(w, steps, warmup, torch, ttt, rotate=None, rates=False, loss="
     sets = [make_device_inputs(w, w.seed + i, torch, rates) for i in range(rotate)]
     stream = torch.cuda.current_stream()
     for i in range(warmup):
-        launch(w, sets[i % rotate], ttt, loss)
+        launch(w, sets[i % rotate], ttt, loss, epochs)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(steps):
-        launch(w, sets[i % rotate], ttt, loss)
+        launch(w, sets[i % rotate], ttt, loss, epochs)
     stop.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / steps
@@ -292,13 +294,18 @@ def main():
                 "mfma_util_pct": round(100 * r["tflops"] / BF16_MFMA_PEAK_TFLOPS, 3),
             }
         # variants: the headline workload with per-token rate factors (uniform in [0, 1)),
-        # and the dot-product loss on the headline and the vision workloads
+        # the dot-product loss on the headline and the vision workloads, and mini-batches
+        # with epochs on the vision workload
         variants = []
         if not args.token_rates:
             variants.append((w, "+token_rates", dict(rates=True)))
         variants.append((w, "+dot_loss", dict(loss="dot")))
         variants += [(o, "+dot_loss", dict(loss="dot")) for o in WORKLOADS
                      if o.name == "mlp_vision_N196"]
+        # the vision workload in four consecutive mini-batches of 49 pairs, two epochs
+        # (eta 0.01: at eta 1 several steps diverge)
+        variants += [(o.replace(chunk=49, eta=0.01), "+chunk49_epochs2", dict(epochs=2))
+                     for o in WORKLOADS if o.name == "mlp_vision_N196"]
         # backward pass of the headline workload (dz ~ N(0, 1), dw_out = 0)
         if w.kind == "linear":
             r = time_backward(w, max(10, args.steps // 2), 3, torch, ttt)

@@ -36,6 +36,11 @@
  *     negative dot product -v^T f(k; W) (blog page, section TTT / 如何理解; the ViT3 news
  *     page, section 2, uses it for the vision model).  With TTT_LOSS_DOT the error term
  *     f(k; W) - v of every gradient becomes -v, so the gradients no longer depend on W.
+ *   - epochs (ttt_linear_fwd, ttt_mlp_fwd): passes of mini-batch GD over all chunks, in
+ *     order, each starting from the weights the previous pass left, before the outputs are
+ *     read (ViT3 news page, observation 2 and its figure on inner batch size and epochs).
+ *     epochs >= 1; epochs > 1 requires causal = 0 (TTT_E_INVALID otherwise), since a second
+ *     pass would let a causal output see later tokens.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream).  Calls are
  *     asynchronous, never synchronise, keep no pointer after returning and are thread-safe;
  *     any workspace a call needs is allocated and released in stream order on `stream`.
@@ -43,7 +48,7 @@
  *       TTT_OK             work enqueued;
  *       TTT_E_INVALID      a null required pointer, a non-positive size, chunk < 1, a
  *                          non-finite eta, a misaligned eta_tok, an unknown dtype or loss,
- *                          or a size overflow;
+ *                          epochs < 1 (or > 1 with causal = 1), or a size overflow;
  *       TTT_E_UNSUPPORTED  a valid combination with no kernel (see each function);
  *       TTT_E_HIP          a HIP runtime error (launch failure, workspace allocation).
  *     ttt_last_error() returns the calling thread's message for the last non-OK status.
@@ -64,8 +69,8 @@ enum { TTT_LOSS_MSE = 0, TTT_LOSS_DOT = 1 };
 /*
  * TTT-Linear forward: f(k; W) = W k, reconstruction loss, mini-batch GD of size `chunk`.
  * Gradient (W k - v) k^T ("Fast weights" page, section 1).  causal = 1: z_t = W_t q_t with
- * W_t including the token's own update; causal = 0: every chunk is trained first and all
- * queries read the final W (ViT3 news page, section 1).
+ * W_t including the token's own update; causal = 0: every chunk is trained first (for
+ * `epochs` passes) and all queries read the final W (ViT3 news page, section 1).
  *   q, k, v  [B][H][T][d] io_dtype            z      [B][H][T][d] io_dtype (out)
  *   w0       float32, per (b, h) a [d][d]     w_out  [B][H][d][d] float32 (out) or NULL
  * Supported: d in {16, 32, 64}, any chunk, both dtypes, causal 0/1.  T may be 0 (then z is
@@ -75,7 +80,8 @@ int ttt_linear_fwd(const void* q, const void* k, const void* v,
                    const float* w0, long long w0_batch_stride,
                    void* z, float* w_out,
                    int B, int H, int T, int d, int chunk, int causal, float eta,
-                   const float* eta_tok, int loss, int io_dtype, ttt_stream_t stream);
+                   const float* eta_tok, int loss, int epochs, int io_dtype,
+                   ttt_stream_t stream);
 
 /*
  * TTT-MLP forward: f(k; W1, W2) = W2 SiLU(W1 k) with hidden width dh, no bias (ViT3 news
@@ -91,7 +97,8 @@ int ttt_mlp_fwd(const void* q, const void* k, const void* v,
                 const float* w1, const float* w2, long long w_batch_stride,
                 void* z, float* w1_out, float* w2_out,
                 int B, int H, int T, int d, int dh, int chunk, int causal, float eta,
-                const float* eta_tok, int loss, int io_dtype, ttt_stream_t stream);
+                const float* eta_tok, int loss, int epochs, int io_dtype,
+                ttt_stream_t stream);
 
 /*
  * Delta rule (mini-batch of one token, causal): W_t = W_{t-1} + eta_t (v_t - W_{t-1} k_t) k_t^T,

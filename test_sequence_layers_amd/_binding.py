@@ -26,9 +26,9 @@ _f = ctypes.c_float
 # name -> (restype, argtypes); mirrors include/ttt.h
 SIGNATURES = {
     "ttt_linear_fwd": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _i,
-                            _i, _vp]),
+                            _i, _i, _vp]),
     "ttt_mlp_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp,
-                         _i, _i, _i, _i, _i, _i, _i, _f, _vp, _i, _i, _vp]),
+                         _i, _i, _i, _i, _i, _i, _i, _f, _vp, _i, _i, _i, _vp]),
     "delta_rule_fwd": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _i, _i, _i, _i, _f, _vp, _i, _vp]),
     "ttt_linear_bwd": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp, _vp, _vp, _vp,
                             _i, _i, _i, _i, _i, _f, _i, _vp]),
@@ -158,12 +158,13 @@ def _out(t, shape, dtype, device, name):
     return t
 
 
-def ttt_linear_fwd(q, k, v, w0, eta, chunk, causal=True, *, eta_tok=None, loss="mse", z=None,
-                   w_out=None, return_state=False, stream=None):
+def ttt_linear_fwd(q, k, v, w0, eta, chunk, causal=True, *, eta_tok=None, loss="mse", epochs=1,
+                   z=None, w_out=None, return_state=False, stream=None):
     """TTT-Linear forward.  q, k, v [B,H,T,d] (float32 or bfloat16, same device);
     w0 float32 [H,d,d] (shared over the batch) or [B,H,d,d]; eta_tok optional float32
     [B,H,T] per-token rate factors (token t learns at eta * eta_tok[t]); loss "mse"
-    (reconstruction) or "dot" (negative dot product).  Returns z (and the final state
+    (reconstruction) or "dot" (negative dot product); epochs: passes over the chunks
+    before the queries are read (non-causal only).  Returns z (and the final state
     [B,H,d,d] when return_state or w_out is given)."""
     torch = _torch()
     lib = load_library()
@@ -176,7 +177,7 @@ def ttt_linear_fwd(q, k, v, w0, eta, chunk, causal=True, *, eta_tok=None, loss="
         rc = lib.ttt_linear_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), w0.data_ptr(), stride,
                                 z.data_ptr(), w_out.data_ptr() if w_out is not None else None,
                                 B, H, T, d, int(chunk), int(bool(causal)), float(eta),
-                                _rates(eta_tok, B, H, T, q.device), _loss(loss),
+                                _rates(eta_tok, B, H, T, q.device), _loss(loss), int(epochs),
                                 _io_dtype(q), _stream(q.device, stream))
     _check(rc)
     return (z, w_out) if w_out is not None else z
@@ -229,10 +230,10 @@ def delta_rule_fwd(q, k, v, w0, eta, *, eta_tok=None, z=None, w_out=None, return
     return (z, w_out) if w_out is not None else z
 
 
-def ttt_mlp_fwd(q, k, v, w1, w2, eta, chunk, causal=True, *, eta_tok=None, loss="mse", z=None,
-                w1_out=None, w2_out=None, return_state=False, stream=None):
+def ttt_mlp_fwd(q, k, v, w1, w2, eta, chunk, causal=True, *, eta_tok=None, loss="mse", epochs=1,
+                z=None, w1_out=None, w2_out=None, return_state=False, stream=None):
     """TTT-MLP forward, f(k) = W2 SiLU(W1 k).  w1 float32 [H,dh,d] or [B,H,dh,d], w2 float32
-    [H,d,dh] or [B,H,d,dh] (both shared or both per batch); eta_tok and loss as in
+    [H,d,dh] or [B,H,d,dh] (both shared or both per batch); eta_tok, loss and epochs as in
     ttt_linear_fwd.
     Returns z (and the final states when return_state or an output state is given)."""
     torch = _torch()
@@ -256,7 +257,7 @@ def ttt_mlp_fwd(q, k, v, w1, w2, eta, chunk, causal=True, *, eta_tok=None, loss=
                              w1_out.data_ptr() if want else None,
                              w2_out.data_ptr() if want else None,
                              B, H, T, d, dh, int(chunk), int(bool(causal)), float(eta),
-                             _rates(eta_tok, B, H, T, q.device), _loss(loss),
+                             _rates(eta_tok, B, H, T, q.device), _loss(loss), int(epochs),
                              _io_dtype(q), _stream(q.device, stream))
     _check(rc)
     return (z, w1_out, w2_out) if want else z

@@ -40,6 +40,7 @@ struct LinearArgs {
   const float* eta_tok;  // per-token rate factors [B][H][T] (rate eta * eta_tok[t]) or null
   int dot_loss;          // 1: loss -v^T f(k), error term -v; 0: 1/2 ||f(k) - v||^2
   float* w_hist;         // generic kernel only: chunk-start states [B][H][nchunks][d][d] or null
+  int epochs = 1;        // passes over the chunks before the outputs (non-causal only)
 };
 
 // Backward pass of the causal TTT-Linear layer (reconstruction loss, scalar rate).
@@ -72,6 +73,7 @@ struct MlpArgs {
   float eta;
   const float* eta_tok;  // per-token rate factors [B][H][T] (rate eta * eta_tok[t]) or null
   int dot_loss;          // 1: loss -v^T f(k), error term -v; 0: 1/2 ||f(k) - v||^2
+  int epochs = 1;        // passes over the chunks before the outputs (non-causal only)
 };
 
 // Host-side launchers (return a hipError_t; argument checks are done by the caller).

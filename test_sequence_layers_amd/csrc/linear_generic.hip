@@ -20,8 +20,9 @@
 //   z_t = Wn q_t - sum_{s <= t in the sub-block} (q_t . k_s) r_s
 //   Wn  -= R^T K,
 // and at the end of a chunk Wc <- Wn.  This equals the per-token recurrence up to
-// floating-point order.  With causal = 0 the training pass writes no output and a second
-// pass computes z_t = W_final q_t.
+// floating-point order.  With causal = 0 the training pass (repeated for `epochs` passes
+// over the chunks, ViT3 news page, observation 2) writes no output and a second pass
+// computes z_t = W_final q_t.
 #include "common.hpp"
 
 namespace ttt {
@@ -63,7 +64,8 @@ __global__ __launch_bounds__(kThreads) void linear_generic_kernel(LinearArgs a) 
 
   const int b = T > 0 ? min(a.chunk, T) : 1;
   const int nchunks = (T + b - 1) / b;
-  for (int c0 = 0; c0 < T; c0 += b) {
+  for (int step = 0; step < a.epochs * nchunks; ++step) {
+    const int c0 = (step % nchunks) * b;
     const int cend = min(c0 + b, T);
     if (a.w_hist) {  // chunk-start state, for the backward pass
       float* wh = a.w_hist + (static_cast<size_t>(chain) * nchunks + c0 / b) * D * D;

@@ -1,6 +1,7 @@
 // Generic TTT-MLP forward on the vector ALUs: f(k) = W2 SiLU(W1 k) with hidden width dh,
 // any chunk size, causal or not, fp32 or bf16 I/O, d in {16, 32, 64}, dh <= 512.
-// One workgroup of 256 threads per (batch, head) chain.
+// One workgroup of 1024 threads (16 waves, four per SIMD, hiding LDS latency) per (batch,
+// head) chain.
 //
 // Method: inner 2-layer SiLU MLP (ViT3 news page, section 2) trained by mini-batch GD on
 // 1/2 ||f(k) - v||^2 (wmrh.cn summary of Sun et al. 2024, section 1.2.2), z_t = f(q_t; W_t),
@@ -18,13 +19,15 @@
 // sub-block, every hidden pre-activation of a query is linear in W1, so
 //   u^q_t = W1n q_t - sum_{s<=t} (q_t . k_s) du_s,   a^q_t = SiLU(u^q_t),
 //   z_t   = W2n a^q_t - sum_{s<=t} (a^q_t . a_s) r_s,
-// then W1n -= dU^T K and W2n -= R^T A; at the end of a chunk W1c/W2c <- W1n/W2n.
+// then W1n -= dU^T K and W2n -= R^T A; at the end of a chunk W1c/W2c <- W1n/W2n.  The
+// non-causal layer may repeat the pass over the chunks for several epochs (ViT3 news page,
+// observation 2) before every query reads the final weights.
 #include "common.hpp"
 
 namespace ttt {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;
 constexpr int kSub = 16;
 
 template <int D>
@@ -84,7 +87,9 @@ __global__ __launch_bounds__(kThreads) void mlp_generic_kernel(MlpArgs a, float*
   __syncthreads();
 
   const int b = T > 0 ? min(a.chunk, T) : 1;
-  for (int c0 = 0; c0 < T; c0 += b) {
+  const int nchunks = (T + b - 1) / b;
+  for (int step = 0; step < a.epochs * nchunks; ++step) {  // epochs > 1: non-causal only
+    const int c0 = (step % nchunks) * b;
     const int cend = min(c0 + b, T);
     for (int s0 = c0; s0 < cend; s0 += kSub) {
       const int n = min(kSub, cend - s0);

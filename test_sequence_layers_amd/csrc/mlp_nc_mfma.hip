@@ -1,5 +1,6 @@
-// Non-causal full-batch TTT-MLP forward on the gfx950 matrix cores: f(k) = W2 SiLU(W1 k),
-// d = 64, hidden 64, one mini-batch holding every token, bf16 Q/K/V/Z, fp32 state.
+// Non-causal TTT-MLP forward on the gfx950 matrix cores: f(k) = W2 SiLU(W1 k), d = 64,
+// hidden 64, bf16 Q/K/V/Z, fp32 state; one full-batch step, or several consecutive
+// mini-batches and epochs.
 //
 // Method (ViT3 news page, section 1, inner training setup: the keys and values are a small
 // training set, one full-batch gradient step, then the trained inner model is applied to
@@ -9,6 +10,9 @@
 // With per-token rates each row t of R (and so of dU) is scaled by token t's rate factor
 // ("Fast weights" page, opening formula; wmrh.cn summary, section 2.2.3).  With the
 // negative dot-product loss -v^T f(k), the ViT3 page's own inner loss (section 2), R = -V.
+// The same page (observation 2 and its figure on inner batch size and epochs) also splits
+// the N pairs into consecutive mini-batches, one update each, and repeats the pass for
+// several epochs: every step takes its gradients at the weights the previous step left.
 //
 // Mapping.  One workgroup of kNcWaves = 2 waves per (batch, head) chain; wave w takes the
 // 16-token tiles w, w + 2, w + 4, ...  Pass 1 streams its tiles (the next tile's loads are
@@ -17,7 +21,8 @@
 // as bf16 operands (W2 in both orientations: the forward pass contracts it over hidden
 // units, the backward pass over outputs).  The partial sums meet once in LDS: wave w adds
 // up half of the tiles, forms W' = W - eta G there, and both waves read all of W1', W2'
-// back.  Pass 2 streams the wave's query tiles.  With 768 waves for 384 chains every wave
+// back (between steps through the LDS copy of the weights, which the next step's operands
+// are built from).  Pass 2 streams the wave's query tiles.  With 768 waves for 384 chains every wave
 // keeps a SIMD to itself.  Tokens past N (the last tile) read as zero and contribute
 // nothing (no bias, SiLU(0) = 0); their outputs are not stored.  Layouts follow the causal MLP
 // kernel: 16 x 16 C-layout tiles, the input index j permuted as j = 16 (m/4) + 2 (m%4) +
@@ -36,7 +41,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kD = 64;
 constexpr int kH = 64;
 constexpr int kTile = 16;
-constexpr int kTileBytes = kTile * kD * 2;
+constexpr int kRowBytes = kD * 2;  // one token row of K, V, Q or Z
+constexpr int kTileBytes = kTile * kRowBytes;
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -166,11 +172,28 @@ __global__ __launch_bounds__(64 * kNcWaves) __attribute__((amdgpu_waves_per_eu(1
 #pragma unroll
   for (int e = 0; e < 4; ++e) kto[e] = (4 * g + e) * 128 + 2 * c0;
 
+  // Training steps: `epochs` passes over the mini-batches [m0, m0 + b) of b = min(chunk, T)
+  // tokens (the last one may be shorter).  A step streams only its own tokens: its tiles
+  // are addressed from the mini-batch start and bounded by its end, so a tile's rows past
+  // the mini-batch read as zero and add nothing to the sums.
+  const int mb = min(a.chunk, T);
+  const int nmb = (T + mb - 1) / mb;
+  const int nsteps = nmb * a.epochs;
+  int m0 = 0;                                // first token of the current step
+  int ns = mb;                               // its tokens
+  int ntl = (ns + kTile - 1) / kTile;        // its tiles
+
   // K/V tiles are prefetched two tiles ahead (the wave's tiles i and i + 1 are in flight
   // while it computes tile i - 1)
   KvTile cur, nx1, nx2;
-  if (wv < ntiles) load_kv(cur, k, v, etok, wv, seq_bytes, row, kto, g, n);
-  if (wv + kNcWaves < ntiles) load_kv(nx1, k, v, etok, wv + kNcWaves, seq_bytes, row, kto, g, n);
+  auto prefetch = [&](int start, int len, int tiles) {  // this wave's first two tiles of a step
+    const char* ks = k + start * kRowBytes;
+    const char* vs = v + start * kRowBytes;
+    const float* es = etok ? etok + start : nullptr;
+    if (wv < tiles) load_kv(cur, ks, vs, es, wv, len * kRowBytes, row, kto, g, n);
+    if (wv + kNcWaves < tiles) load_kv(nx1, ks, vs, es, wv + kNcWaves, len * kRowBytes, row, kto, g, n);
+  };
+  prefetch(m0, ns, ntl);
   {
     // W1 and W2 (64 x 64 fp32 each) into LDS: thread x copies 16-byte pieces x, x + 128, ...
     const int tid = threadIdx.x;
@@ -185,152 +208,160 @@ __global__ __launch_bounds__(64 * kNcWaves) __attribute__((amdgpu_waves_per_eu(1
     }
   }
   __syncthreads();
-  const float* w1l = &wsh[0][0][0];
-  const float* w2l = &wsh[1][0][0];
-  // this wave's half of the initial W tiles, for W' = W - eta G after pass 1 (tile f = 4 x + y
-  // of the [x][y] tile arrays, f in 8 w .. 8 w + 7)
-  float4_t w1own[2][4], w2own[2][4];
-#pragma unroll
-  for (int aa = 0; aa < 4; ++aa) {
-    const float* wr = w1l + (16 * aa + n) * kWRow + 16 * g + 8 * wv;
-    const float4_t f0 = *reinterpret_cast<const float4_t*>(wr);
-    const float4_t f1 = *reinterpret_cast<const float4_t*>(wr + 4);
-    w1own[0][aa] = float4_t{f0[0], f0[2], f1[0], f1[2]};
-    w1own[1][aa] = float4_t{f0[1], f0[3], f1[1], f1[3]};
-  }
-#pragma unroll
-  for (int x = 0; x < 2; ++x)
-#pragma unroll
-    for (int it = 0; it < 4; ++it)
-      w2own[x][it] = *reinterpret_cast<const float4_t*>(w2l + (16 * it + n) * kWRow + 16 * (2 * wv + x) + 4 * g);
+  float* w1l = &wsh[0][0][0];
+  float* w2l = &wsh[1][0][0];
 
-  // ---- bf16 operands of the initial weights ----
   bf16x8_t w1b[2][4];   // [h][a]: operand over j (B of K W1^T)
   bf16x8_t w2tb[2][4];  // [h][it]: operand over hidden (A of W2 A^T)
   bf16x8_t w2b[2][4];   // [h][a]: operand over outputs (B of R W2)
-  {
-    float4_t t[4][4];
-    load_w1t(t, w1l, g, n);
+  // this wave's half of the W tiles, for W' = W - eta G after pass 1 (tile f = 4 x + y of
+  // the [x][y] tile arrays, f in 8 w .. 8 w + 7)
+  float4_t w1own[2][4], w2own[2][4];
+  u32x4 qn0 = {0u, 0u, 0u, 0u}, qn1 = {0u, 0u, 0u, 0u};
+  for (int step = 0;; ++step) {
+    // ---- bf16 operands of the current weights (the LDS copy) ----
+    {
+      float4_t t[4][4];
+      load_w1t(t, w1l, g, n);
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int aa = 0; aa < 4; ++aa) w1b[h][aa] = pair_op(t[2 * h][aa], t[2 * h + 1][aa]);
-    load_w2t(t, w2l, g, n);
+        for (int aa = 0; aa < 4; ++aa) w1b[h][aa] = pair_op(t[2 * h][aa], t[2 * h + 1][aa]);
+      load_w2t(t, w2l, g, n);
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int it = 0; it < 4; ++it) w2tb[h][it] = pair_op(t[2 * h][it], t[2 * h + 1][it]);
-    // W2 tiles [it][a]: rows output 16it + m, cols hidden 16a + n
+        for (int it = 0; it < 4; ++it) w2tb[h][it] = pair_op(t[2 * h][it], t[2 * h + 1][it]);
+      // W2 tiles [it][a]: rows output 16it + m, cols hidden 16a + n
 #pragma unroll
-    for (int it = 0; it < 4; ++it)
+      for (int it = 0; it < 4; ++it)
+#pragma unroll
+        for (int aa = 0; aa < 4; ++aa) {
+          float4_t x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = w2l[(16 * it + 4 * g + e) * kWRow + 16 * aa + n];
+          t[it][aa] = x;
+        }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int aa = 0; aa < 4; ++aa) w2b[h][aa] = pair_op(t[2 * h][aa], t[2 * h + 1][aa]);
+    }
+
+    // ---- pass 1: partial gradient sums over this wave's tiles of the step ----
+    float4_t g1t[4][4];  // sum of K^T dU, layout of W1^T
+    float4_t g2t[4][4];  // sum of A^T R, layout of W2^T
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        g1t[i][j] = zero;
+        g2t[i][j] = zero;
+      }
+    const char* ks = k + m0 * kRowBytes;
+    const char* vs = v + m0 * kRowBytes;
+    const float* es = etok ? etok + m0 : nullptr;
+    for (int tt = wv; tt < ntl; tt += kNcWaves) {
+      if (tt + 2 * kNcWaves < ntl) load_kv(nx2, ks, vs, es, tt + 2 * kNcWaves, ns * kRowBytes, row, kto, g, n);
+      const bf16x8_t ka0 = bf(cur.ka0), ka1 = bf(cur.ka1);
+      // U = K W1^T (rows t); A = SiLU(U), S = SiLU'(U)
+      float4_t act[4], sd[4];
 #pragma unroll
       for (int aa = 0; aa < 4; ++aa) {
-        float4_t x;
+        float4_t u = mfma(ka0, w1b[0][aa], zero);
+        u = mfma(ka1, w1b[1][aa], u);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = w2l[(16 * it + 4 * g + e) * kWRow + 16 * aa + n];
-        t[it][aa] = x;
+        for (int e = 0; e < 4; ++e) {
+          const float sg = sigmoid_f(u[e]);
+          act[aa][e] = u[e] * sg;
+          sd[aa][e] = sg * (1.0f + u[e] * (1.0f - sg));
+        }
+      }
+      // A^T (rows hidden)
+      float4_t actT[4];
+#pragma unroll
+      for (int aa = 0; aa < 4; ++aa) actT[aa] = mfma(pad_op(act[aa]), eye, zero);
+      const bf16x8_t atb0 = pair_op(actT[0], actT[1]), atb1 = pair_op(actT[2], actT[3]);
+      // R^T = W2 A^T - V^T (rows output tile it, cols t), times the rate factor of token t
+      // (its gradients carry its own rate)
+      float4_t rT[4];
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        float4_t o = zero;  // the dot-product loss's error term is -V alone
+        if (!kDot) {
+          o = mfma(w2tb[0][it], atb0, zero);
+          o = mfma(w2tb[1][it], atb1, o);
+        }
+        o[0] -= bf_lo(cur.vv[it].x);
+        o[1] -= bf_hi(cur.vv[it].x);
+        o[2] -= bf_lo(cur.vv[it].y);
+        o[3] -= bf_hi(cur.vv[it].y);
+        rT[it] = o * cur.et;
+      }
+      // dU = (R W2) * S (rows t): A-operand R (m = t, k = output) from pairs of R^T tiles
+      const bf16x8_t rrow0 = pair_op(rT[0], rT[1]), rrow1 = pair_op(rT[2], rT[3]);
+      bf16x8_t dub[4];
+#pragma unroll
+      for (int aa = 0; aa < 4; ++aa) {
+        float4_t da = mfma(rrow0, w2b[0][aa], zero);
+        da = mfma(rrow1, w2b[1][aa], da);
+        dub[aa] = pad_op(da * sd[aa]);
+      }
+      // R (rows t) from R^T by an MFMA with I, as padded operands
+      bf16x8_t rb[4];
+#pragma unroll
+      for (int it = 0; it < 4; ++it) rb[it] = pad_op(mfma(pad_op(rT[it]), eye, zero));
+      // G1^T += K^T dU ; G2^T += A^T R
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb) {
+        const int h = jb >> 1;
+        const uint32_t sel = (jb & 1) ? kHi : kLo;
+        const bf16x8_t ktb = op4(__builtin_amdgcn_perm(cur.kt[1][h], cur.kt[0][h], sel),
+                                 __builtin_amdgcn_perm(cur.kt[3][h], cur.kt[2][h], sel), 0u, 0u);
+#pragma unroll
+        for (int aa = 0; aa < 4; ++aa) g1t[jb][aa] = mfma(ktb, dub[aa], g1t[jb][aa]);
       }
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int aa = 0; aa < 4; ++aa) {
+        const bf16x8_t ab = pad_op(act[aa]);
 #pragma unroll
-      for (int aa = 0; aa < 4; ++aa) w2b[h][aa] = pair_op(t[2 * h][aa], t[2 * h + 1][aa]);
-  }
-
-  // ---- pass 1: partial gradient sums over this wave's tiles ----
-  float4_t g1t[4][4];  // sum of K^T dU, layout of W1^T
-  float4_t g2t[4][4];  // sum of A^T R, layout of W2^T
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      g1t[i][j] = zero;
-      g2t[i][j] = zero;
-    }
-  for (int tt = wv; tt < ntiles; tt += kNcWaves) {
-    if (tt + 2 * kNcWaves < ntiles) load_kv(nx2, k, v, etok, tt + 2 * kNcWaves, seq_bytes, row, kto, g, n);
-    const bf16x8_t ka0 = bf(cur.ka0), ka1 = bf(cur.ka1);
-    // U = K W1^T (rows t); A = SiLU(U), S = SiLU'(U)
-    float4_t act[4], sd[4];
-#pragma unroll
-    for (int aa = 0; aa < 4; ++aa) {
-      float4_t u = mfma(ka0, w1b[0][aa], zero);
-      u = mfma(ka1, w1b[1][aa], u);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float sg = sigmoid_f(u[e]);
-        act[aa][e] = u[e] * sg;
-        sd[aa][e] = sg * (1.0f + u[e] * (1.0f - sg));
+        for (int it = 0; it < 4; ++it) g2t[aa][it] = mfma(ab, rb[it], g2t[aa][it]);
       }
+      cur = nx1;
+      nx1 = nx2;
     }
-    // A^T (rows hidden)
-    float4_t actT[4];
-#pragma unroll
-    for (int aa = 0; aa < 4; ++aa) actT[aa] = mfma(pad_op(act[aa]), eye, zero);
-    const bf16x8_t atb0 = pair_op(actT[0], actT[1]), atb1 = pair_op(actT[2], actT[3]);
-    // R^T = W2 A^T - V^T (rows output tile it, cols t), times the rate factor of token t
-    // (its gradients carry its own rate)
-    float4_t rT[4];
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      float4_t o = zero;  // the dot-product loss's error term is -V alone
-      if (!kDot) {
-        o = mfma(w2tb[0][it], atb0, zero);
-        o = mfma(w2tb[1][it], atb1, o);
+
+    const bool last = step + 1 == nsteps;
+    if (last) {
+      // queries of this wave's first tile, loaded while the sums are reduced
+      if (wv < ntiles) {
+        const int off = wv * kTileBytes;
+        const __amdgpu_buffer_rsrc_t rq = tile_rsrc(q + off, seq_bytes - off);
+        qn0 = __builtin_amdgcn_raw_buffer_load_b128(rq, row, 0, 0);
+        qn1 = __builtin_amdgcn_raw_buffer_load_b128(rq, row + 16, 0, 0);
       }
-      o[0] -= bf_lo(cur.vv[it].x);
-      o[1] -= bf_hi(cur.vv[it].x);
-      o[2] -= bf_lo(cur.vv[it].y);
-      o[3] -= bf_hi(cur.vv[it].y);
-      rT[it] = o * cur.et;
+    } else {
+      // the next step's first tiles, loaded while the sums are reduced
+      m0 = ((step + 1) % nmb) * mb;
+      ns = min(mb, T - m0);
+      ntl = (ns + kTile - 1) / kTile;
+      prefetch(m0, ns, ntl);
     }
-    // dU = (R W2) * S (rows t): A-operand R (m = t, k = output) from pairs of R^T tiles
-    const bf16x8_t rrow0 = pair_op(rT[0], rT[1]), rrow1 = pair_op(rT[2], rT[3]);
-    bf16x8_t dub[4];
+
+    // ---- W -= eta G: the partial sums meet in LDS; wave w reduces tiles 8 w .. 8 w + 7 ----
 #pragma unroll
     for (int aa = 0; aa < 4; ++aa) {
-      float4_t da = mfma(rrow0, w2b[0][aa], zero);
-      da = mfma(rrow1, w2b[1][aa], da);
-      dub[aa] = pad_op(da * sd[aa]);
-    }
-    // R (rows t) from R^T by an MFMA with I, as padded operands
-    bf16x8_t rb[4];
-#pragma unroll
-    for (int it = 0; it < 4; ++it) rb[it] = pad_op(mfma(pad_op(rT[it]), eye, zero));
-    // G1^T += K^T dU ; G2^T += A^T R
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-      const int h = jb >> 1;
-      const uint32_t sel = (jb & 1) ? kHi : kLo;
-      const bf16x8_t ktb = op4(__builtin_amdgcn_perm(cur.kt[1][h], cur.kt[0][h], sel),
-                               __builtin_amdgcn_perm(cur.kt[3][h], cur.kt[2][h], sel), 0u, 0u);
-#pragma unroll
-      for (int aa = 0; aa < 4; ++aa) g1t[jb][aa] = mfma(ktb, dub[aa], g1t[jb][aa]);
+      const float* wr = w1l + (16 * aa + n) * kWRow + 16 * g + 8 * wv;
+      const float4_t f0 = *reinterpret_cast<const float4_t*>(wr);
+      const float4_t f1 = *reinterpret_cast<const float4_t*>(wr + 4);
+      w1own[0][aa] = float4_t{f0[0], f0[2], f1[0], f1[2]};
+      w1own[1][aa] = float4_t{f0[1], f0[3], f1[1], f1[3]};
     }
 #pragma unroll
-    for (int aa = 0; aa < 4; ++aa) {
-      const bf16x8_t ab = pad_op(act[aa]);
+    for (int x = 0; x < 2; ++x)
 #pragma unroll
-      for (int it = 0; it < 4; ++it) g2t[aa][it] = mfma(ab, rb[it], g2t[aa][it]);
-    }
-    cur = nx1;
-    nx1 = nx2;
-  }
-
-  // queries of this wave's first tile, loaded while the sums are reduced
-  u32x4 qn0 = {0u, 0u, 0u, 0u}, qn1 = {0u, 0u, 0u, 0u};
-  if (wv < ntiles) {
-    const int off = wv * kTileBytes;
-    const __amdgpu_buffer_rsrc_t rq = tile_rsrc(q + off, seq_bytes - off);
-    qn0 = __builtin_amdgcn_raw_buffer_load_b128(rq, row, 0, 0);
-    qn1 = __builtin_amdgcn_raw_buffer_load_b128(rq, row + 16, 0, 0);
-  }
-
-  // ---- W' = W - eta G: the partial sums meet in LDS; wave w reduces tiles 8 w .. 8 w + 7 ----
-  // (tile f = 4 x + y of the [x][y] arrays)
-  bf16x8_t w1nb[2][4], w2nb[2][4];
-  {
-    float4_t t[4][4];
-    // W1
+      for (int it = 0; it < 4; ++it)
+        w2own[x][it] = *reinterpret_cast<const float4_t*>(w2l + (16 * it + n) * kWRow + 16 * (2 * wv + x) + 4 * g);
 #pragma unroll
     for (int f = 0; f < 16; ++f) red[wv][f][lane] = g1t[f >> 2][f & 3];
     __syncthreads();
@@ -342,7 +373,42 @@ __global__ __launch_bounds__(64 * kNcWaves) __attribute__((amdgpu_waves_per_eu(1
       for (int w = 1; w < kNcWaves; ++w) sum += red[w][f][lane];
       w1own[i >> 2][i & 3] -= eta * sum;
     }
-    __syncthreads();  // every partial read before the reduced tiles overwrite slot 0
+    __syncthreads();  // every partial read before the W2 partials overwrite the slots
+#pragma unroll
+    for (int f = 0; f < 16; ++f) red[wv][f][lane] = g2t[f >> 2][f & 3];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int f = 8 * wv + i;
+      float4_t sum = red[0][f][lane];
+#pragma unroll
+      for (int w = 1; w < kNcWaves; ++w) sum += red[w][f][lane];
+      w2own[i >> 2][i & 3] -= eta * sum;
+    }
+    __syncthreads();  // every partial read before slot 0 is reused
+    if (last) break;
+    // the updated tiles back into the LDS copy, from which the next step builds its
+    // operands (the inverse of the reads above; the two waves cover all 64 x 64 entries)
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa) {
+      float* wr = w1l + (16 * aa + n) * kWRow + 16 * g + 8 * wv;
+      const float4_t o0 = w1own[0][aa], o1 = w1own[1][aa];
+      *reinterpret_cast<float4_t*>(wr) = float4_t{o0[0], o1[0], o0[1], o1[1]};
+      *reinterpret_cast<float4_t*>(wr + 4) = float4_t{o0[2], o1[2], o0[3], o1[3]};
+    }
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int it = 0; it < 4; ++it)
+        *reinterpret_cast<float4_t*>(w2l + (16 * it + n) * kWRow + 16 * (2 * wv + x) + 4 * g) = w2own[x][it];
+    __syncthreads();
+  }
+
+  // ---- the trained tiles to both waves (and to w1_out / w2_out) ----
+  bf16x8_t w1nb[2][4], w2nb[2][4];
+  {
+    float4_t t[4][4];
+    // W1
 #pragma unroll
     for (int i = 0; i < 8; ++i) red[0][8 * wv + i][lane] = w1own[i >> 2][i & 3];
     __syncthreads();
@@ -365,18 +431,6 @@ __global__ __launch_bounds__(64 * kNcWaves) __attribute__((amdgpu_waves_per_eu(1
       for (int aa = 0; aa < 4; ++aa) w1nb[h][aa] = pair_op(t[2 * h][aa], t[2 * h + 1][aa]);
     __syncthreads();  // every read of the W1 tiles before slot reuse
     // W2
-#pragma unroll
-    for (int f = 0; f < 16; ++f) red[wv][f][lane] = g2t[f >> 2][f & 3];
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int f = 8 * wv + i;
-      float4_t sum = red[0][f][lane];
-#pragma unroll
-      for (int w = 1; w < kNcWaves; ++w) sum += red[w][f][lane];
-      w2own[i >> 2][i & 3] -= eta * sum;
-    }
-    __syncthreads();
 #pragma unroll
     for (int i = 0; i < 8; ++i) red[0][8 * wv + i][lane] = w2own[i >> 2][i & 3];
     __syncthreads();
@@ -436,7 +490,7 @@ bool mlp_nc_supported(const MlpArgs& a, bool bf16_io) {
                        (a.w1_out == nullptr || al(a.w1_out, 16)) &&
                        (a.w2_out == nullptr || al(a.w2_out, 16));
   const bool fits = static_cast<long long>(a.T) * kD * 2 + 2LL * kTileBytes < 0x7fffffffLL;
-  return bf16_io && a.d == kD && a.dh == kH && a.causal == 0 && a.chunk >= a.T && a.T > 0 &&
+  return bf16_io && a.d == kD && a.dh == kH && a.causal == 0 && a.T > 0 && a.epochs >= 1 &&
          aligned && fits && (a.eta_tok == nullptr || al(a.eta_tok, 4));
 }
 

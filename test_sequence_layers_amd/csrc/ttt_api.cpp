@@ -56,6 +56,15 @@ int check_common(const char* fn, const void* q, const void* k, const void* v, co
   return TTT_OK;
 }
 
+// Several epochs revisit every token, which only the non-causal layer may do (a causal
+// output must not depend on later tokens).
+int check_epochs(const char* fn, int epochs, int causal) {
+  if (epochs < 1) return fail(TTT_E_INVALID, "%s: epochs must be >= 1 (got %d)", fn, epochs);
+  if (causal == 1 && epochs != 1)
+    return fail(TTT_E_INVALID, "%s: epochs > 1 needs causal = 0 (got %d)", fn, epochs);
+  return TTT_OK;
+}
+
 // Per-call device workspace, allocated and released in stream order (hipMallocAsync /
 // hipFreeAsync on the caller's stream): the release is queued behind the kernels that use
 // it, so concurrent calls on different streams never share a workspace and the host never
@@ -90,19 +99,21 @@ int copy_state(float* dst, const float* src, long long batch_stride, int B, int 
 
 extern "C" {
 
-int ttt_abi_version(void) { return 3; }
+int ttt_abi_version(void) { return 4; }
 
 const char* ttt_last_error(void) { return g_last_error.c_str(); }
 
 int ttt_linear_fwd(const void* q, const void* k, const void* v, const float* w0,
                    long long w0_batch_stride, void* z, float* w_out, int B, int H, int T,
                    int d, int chunk, int causal, float eta, const float* eta_tok, int loss,
-                   int io_dtype, ttt_stream_t stream) {
+                   int epochs, int io_dtype, ttt_stream_t stream) {
   g_last_error.clear();
   int rc = check_common("ttt_linear_fwd", q, k, v, z, B, H, T, d, eta, eta_tok, io_dtype);
   if (rc != TTT_OK) return rc;
   if (loss != TTT_LOSS_MSE && loss != TTT_LOSS_DOT)
     return fail(TTT_E_INVALID, "ttt_linear_fwd: unknown loss %d", loss);
+  rc = check_epochs("ttt_linear_fwd", epochs, causal);
+  if (rc != TTT_OK) return rc;
   if (!w0) return fail(TTT_E_INVALID, "ttt_linear_fwd: w0 must be non-null");
   if (chunk < 1) return fail(TTT_E_INVALID, "ttt_linear_fwd: chunk must be >= 1 (got %d)", chunk);
   if (causal != 0 && causal != 1)
@@ -115,6 +126,7 @@ int ttt_linear_fwd(const void* q, const void* k, const void* v, const float* w0,
 
   ttt::LinearArgs a{q, k, v, w0, w0_batch_stride, z, w_out, B, H, T, d, chunk, causal, eta, eta_tok,
                     loss == TTT_LOSS_DOT ? 1 : 0};
+  a.epochs = epochs;
   const bool bf16 = io_dtype == TTT_BF16;
   hipError_t e;
   if (ttt::linear_mfma_supported(a, bf16))
@@ -196,12 +208,14 @@ int ttt_linear_bwd(const void* q, const void* k, const void* v, const float* w0,
 int ttt_mlp_fwd(const void* q, const void* k, const void* v, const float* w1, const float* w2,
                 long long w_batch_stride, void* z, float* w1_out, float* w2_out, int B, int H,
                 int T, int d, int dh, int chunk, int causal, float eta, const float* eta_tok,
-                int loss, int io_dtype, ttt_stream_t stream) {
+                int loss, int epochs, int io_dtype, ttt_stream_t stream) {
   g_last_error.clear();
   int rc = check_common("ttt_mlp_fwd", q, k, v, z, B, H, T, d, eta, eta_tok, io_dtype);
   if (rc != TTT_OK) return rc;
   if (loss != TTT_LOSS_MSE && loss != TTT_LOSS_DOT)
     return fail(TTT_E_INVALID, "ttt_mlp_fwd: unknown loss %d", loss);
+  rc = check_epochs("ttt_mlp_fwd", epochs, causal);
+  if (rc != TTT_OK) return rc;
   if (!w1 || !w2) return fail(TTT_E_INVALID, "ttt_mlp_fwd: w1 and w2 must be non-null");
   if (dh <= 0) return fail(TTT_E_INVALID, "ttt_mlp_fwd: dh must be positive (got %d)", dh);
   if (chunk < 1) return fail(TTT_E_INVALID, "ttt_mlp_fwd: chunk must be >= 1 (got %d)", chunk);
@@ -219,6 +233,7 @@ int ttt_mlp_fwd(const void* q, const void* k, const void* v, const float* w1, co
   }
   ttt::MlpArgs a{q, k, v, w1, w2, w_batch_stride, z, w1_out, w2_out,
                  B, H, T, d, dh, chunk, causal, eta, eta_tok, loss == TTT_LOSS_DOT ? 1 : 0};
+  a.epochs = epochs;
   const bool bf16 = io_dtype == TTT_BF16;
   hipError_t e;
   StreamBuffer ws;

@@ -38,20 +38,20 @@ def to_device(inp, io):
     return out
 
 
-def run_gpu(kind, dev, eta, chunk, causal, return_state=True, loss="mse"):
+def run_gpu(kind, dev, eta, chunk, causal, return_state=True, loss="mse", epochs=1):
     import test_sequence_layers_amd as ttt
     et = dev.get("eta_tok")
     if kind == "linear":
         return ttt.ttt_linear_fwd(dev["q"], dev["k"], dev["v"], dev["w0"], eta, chunk, causal,
-                                  eta_tok=et, loss=loss, return_state=return_state)
+                                  eta_tok=et, loss=loss, epochs=epochs, return_state=return_state)
     if kind == "delta":
         return ttt.delta_rule_fwd(dev["q"], dev["k"], dev["v"], dev["w0"], eta, eta_tok=et,
                                   return_state=return_state)
     return ttt.ttt_mlp_fwd(dev["q"], dev["k"], dev["v"], dev["w1"], dev["w2"], eta, chunk,
-                           causal, eta_tok=et, loss=loss, return_state=return_state)
+                           causal, eta_tok=et, loss=loss, epochs=epochs, return_state=return_state)
 
 
-def run_oracle(kind, inp, eta, chunk, causal, sel=None, loss="mse"):
+def run_oracle(kind, inp, eta, chunk, causal, sel=None, loss="mse", epochs=1):
     """Oracle on (optionally) a subset of (b, h) pairs: sel = list of (b, h)."""
     q, k, v = inp["q"], inp["k"], inp["v"]
     et = inp.get("eta_tok")
@@ -64,11 +64,12 @@ def run_oracle(kind, inp, eta, chunk, causal, sel=None, loss="mse"):
     else:
         pick = lambda w: w
     if kind == "linear":
-        return O.ttt_linear(q, k, v, pick(inp["w0"]), eta, chunk, causal, loss=loss, eta_tok=et)
+        return O.ttt_linear(q, k, v, pick(inp["w0"]), eta, chunk, causal, loss=loss, eta_tok=et,
+                            epochs=epochs)
     if kind == "delta":
         return O.delta_rule(q, k, v, pick(inp["w0"]), eta, eta_tok=et)
     return O.ttt_mlp(q, k, v, pick(inp["w1"]), pick(inp["w2"]), eta, chunk, causal, loss=loss,
-                     eta_tok=et)
+                     eta_tok=et, epochs=epochs)
 
 
 def to_np(t):

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ttt_abi_version() == 3
+    assert lib.ttt_abi_version() == 4
 
 
 FAKE = 0x1000  # never dereferenced: validation fails before any HIP call
@@ -47,20 +47,21 @@ FAKE = 0x1000  # never dereferenced: validation fails before any HIP call
 
 def _linear(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, w0=FAKE, stride=0, z=FAKE, w_out=None, B=1, H=1, T=16,
-             d=16, chunk=16, causal=1, eta=0.1, eta_tok=None, loss=0, io=0)
+             d=16, chunk=16, causal=1, eta=0.1, eta_tok=None, loss=0, epochs=1, io=0)
     a.update(kw)
     return lib.ttt_linear_fwd(a["q"], a["k"], a["v"], a["w0"], a["stride"], a["z"], a["w_out"],
                               a["B"], a["H"], a["T"], a["d"], a["chunk"], a["causal"],
-                              a["eta"], a["eta_tok"], a["loss"], a["io"], None)
+                              a["eta"], a["eta_tok"], a["loss"], a["epochs"], a["io"], None)
 
 
 def _mlp(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, w1=FAKE, w2=FAKE, stride=0, z=FAKE, B=1, H=1, T=16, d=16,
-             dh=32, chunk=16, causal=1, eta=0.1, eta_tok=None, loss=0, io=0)
+             dh=32, chunk=16, causal=1, eta=0.1, eta_tok=None, loss=0, epochs=1, io=0)
     a.update(kw)
     return lib.ttt_mlp_fwd(a["q"], a["k"], a["v"], a["w1"], a["w2"], a["stride"], a["z"], None,
                            None, a["B"], a["H"], a["T"], a["d"], a["dh"], a["chunk"],
-                           a["causal"], a["eta"], a["eta_tok"], a["loss"], a["io"], None)
+                           a["causal"], a["eta"], a["eta_tok"], a["loss"], a["epochs"], a["io"],
+                           None)
 
 
 def _delta(lib, **kw):
@@ -91,6 +92,9 @@ def _delta(lib, **kw):
     (dict(d=128), ttt.TTT_E_UNSUPPORTED, "d=128"),
     (dict(eta_tok=FAKE + 2), ttt.TTT_E_INVALID, "eta_tok"),
     (dict(loss=2), ttt.TTT_E_INVALID, "loss"),
+    (dict(epochs=0), ttt.TTT_E_INVALID, "epochs"),
+    (dict(epochs=2), ttt.TTT_E_INVALID, "causal = 0"),
+    (dict(epochs=-1, causal=0), ttt.TTT_E_INVALID, "epochs"),
 ])
 def test_linear_rejects(lib, kw, code, msg):
     assert _linear(lib, **kw) == code
@@ -108,6 +112,8 @@ def test_linear_rejects(lib, kw, code, msg):
     (dict(v=None), ttt.TTT_E_INVALID, "non-null"),
     (dict(eta_tok=FAKE + 1), ttt.TTT_E_INVALID, "eta_tok"),
     (dict(loss=-1), ttt.TTT_E_INVALID, "loss"),
+    (dict(epochs=0, causal=0), ttt.TTT_E_INVALID, "epochs"),
+    (dict(epochs=3), ttt.TTT_E_INVALID, "causal = 0"),
 ])
 def test_mlp_rejects(lib, kw, code, msg):
     assert _mlp(lib, **kw) == code

@@ -19,16 +19,17 @@ def _note(msg):
     sys.stdout.flush()
 
 
-def _check(kind, w, inp, sel=None, state_tol=None, loss="mse"):
+def _check(kind, w, inp, sel=None, state_tol=None, loss="mse", epochs=1):
     _note(f"[parity] {kind} {w.name} B={w.B} H={w.H} T={w.T} d={w.d} h={w.h} chunk={w.chunk} "
-          f"causal={w.causal} io={w.io} seed={w.seed} loss={loss} rates={'eta_tok' in inp}")
+          f"causal={w.causal} io={w.io} seed={w.seed} loss={loss} rates={'eta_tok' in inp} "
+          f"epochs={epochs}")
     dev = to_device(inp, w.io)
-    out = run_gpu(kind, dev, w.eta, w.chunk, w.causal, loss=loss)
+    out = run_gpu(kind, dev, w.eta, w.chunk, w.causal, loss=loss, epochs=epochs)
     import torch
     torch.cuda.synchronize()
     z = to_np(out[0])
     states = [to_np(s) for s in out[1:]]
-    ref = run_oracle(kind, inp, w.eta, w.chunk, w.causal, sel, loss=loss)
+    ref = run_oracle(kind, inp, w.eta, w.chunk, w.causal, sel, loss=loss, epochs=epochs)
     if sel is not None:
         bs = [b for b, _ in sel]
         hs = [h for _, h in sel]
@@ -273,6 +274,44 @@ def test_dot_loss_mlp_vision(rates):
 def test_dot_loss_mlp_vision_config_full_size():
     w = workload(4).replace(eta=0.1)
     _check("mlp", w, make_inputs(w), loss="dot", sel=[(0, 0), (40, 5)])
+
+
+# ------------------------------------------------------------------ mini-batches and epochs
+# Non-causal layer trained over consecutive mini-batches (N/2, N/3, N/4 of the N pairs) for
+# several epochs before the queries read it (ViT3 news page, observation 2).  The rates keep
+# the recurrence bounded: at the vision workload's eta = 1 several steps diverge in float64.
+
+@pytest.mark.parametrize("chunk,epochs", [(196, 2), (98, 1), (66, 1), (49, 2), (49, 4), (16, 1),
+                                          (5, 2), (300, 3)])
+def test_epochs_mlp_vision(chunk, epochs):
+    w = workload(4).replace(B=2, H=3, chunk=chunk, unit_keys=True, eta=0.1, seed=200 + chunk)
+    _check("mlp", w, make_inputs(w), epochs=epochs)
+
+
+@pytest.mark.parametrize("loss,rates", [("mse", True), ("dot", False), ("dot", True)])
+def test_epochs_mlp_vision_loss_and_rates(loss, rates):
+    w = workload(4).replace(B=2, H=3, chunk=66, unit_keys=True, eta=0.1, seed=210)
+    _check("mlp", w, _with_rates(w, 12) if rates else make_inputs(w), loss=loss, epochs=2)
+
+
+def test_epochs_mlp_vision_config_full_size():
+    w = workload(4).replace(chunk=49, eta=0.01)
+    _check("mlp", w, make_inputs(w), epochs=2, sel=[(0, 0), (17, 3), (63, 5)])
+
+
+@pytest.mark.parametrize("chunk,epochs", [(10, 3), (37, 2)])
+def test_epochs_mlp_fp32(chunk, epochs):
+    w = workload(3).replace(B=2, H=2, T=37, d=16, h=32, chunk=chunk, causal=False, io="f32",
+                            eta=0.05, seed=220 + chunk)
+    _check("mlp", w, make_inputs(w), epochs=epochs)
+
+
+@pytest.mark.parametrize("d,chunk,epochs,io", [(16, 16, 2, "f32"), (32, 77, 3, "f32"),
+                                               (64, 49, 2, "bf16")])
+def test_epochs_linear(d, chunk, epochs, io):
+    w = workload(0).replace(B=2, H=3, T=196, d=d, chunk=chunk, causal=False, init="normal",
+                            eta=0.1, io=io, seed=230 + d)
+    _check("linear", w, make_inputs(w), epochs=epochs)
 
 
 # ------------------------------------------------------------------ backward pass
