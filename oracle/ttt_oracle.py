@@ -29,6 +29,14 @@ define the method; no line numbers are given on purpose):
   of the token, eta(x) = eta_base * sigmoid(theta_lr . x).  The rate of token t is
   eta * eta_tok[..., t]; in a mini-batch each token's gradient is scaled by its own rate,
       W_t = W_{t'} - sum_{s = t'+1..t} eta_s grad l_s(W_{t'}).
+* Paper instantiation with layer norm and residual (optional `ln`): the wmrh.cn summary of
+  Sun et al. 2024, section 2.2.1, always wraps the inner model as
+      f(x) = x + LN(f_res(x)),
+  f_res the linear map W x or a 2-layer MLP with hidden width 4 d and a GELU activation;
+  LN(y) = gamma * (y - mean(y)) / sqrt(var(y) + eps) + beta over the d features (biased
+  variance), gamma and beta fixed during the inner loop (outer-loop parameters, one pair per
+  head).  GELU is u * Phi(u), Phi the standard normal CDF (the exact form).  The loss is
+  unchanged: 1/2 ||f(k) - v||^2 or -v^T f(k).
 * Output rule: z_t = f(q_t; W_t), i.e. the output is read after the token's own update
   (blog page "TTT / 通用表示"; "Fast weights" page opening formula).
 * Non-causal variant (ViT3 news page, "1. inner training setup", observation 2): the keys
@@ -46,10 +54,15 @@ It is vectorised only over independent (batch, head) chains.
 from __future__ import annotations
 
 import numpy as np
+from scipy.special import erf
 
 __all__ = [
     "silu",
     "dsilu",
+    "gelu",
+    "dgelu",
+    "layer_norm",
+    "layer_norm_vjp",
     "linear_f",
     "mlp_f",
     "linear_loss",
@@ -80,66 +93,114 @@ def dsilu(u):
     return s * (1.0 + u * (1.0 - s))
 
 
-def linear_f(W, x):
-    """f(x; W) = W x.  W [N, d_out, d_in], x [N, d_in] -> [N, d_out]."""
-    return np.einsum("nij,nj->ni", W, x)
+def gelu(u):
+    """GELU(u) = u * Phi(u), Phi(u) = (1 + erf(u / sqrt 2)) / 2 (the paper MLP's activation)."""
+    return 0.5 * u * (1.0 + erf(u / np.sqrt(2.0)))
 
 
-def mlp_f(W1, W2, x):
-    """f(x; W1, W2) = W2 SiLU(W1 x).  W1 [N, h, d], W2 [N, d, h], x [N, d] -> [N, d]."""
-    return np.einsum("nih,nh->ni", W2, silu(np.einsum("nhj,nj->nh", W1, x)))
+def dgelu(u):
+    """d/du GELU(u) = Phi(u) + u * phi(u), phi the standard normal density."""
+    return 0.5 * (1.0 + erf(u / np.sqrt(2.0))) + u * np.exp(-0.5 * u * u) / np.sqrt(2.0 * np.pi)
 
 
-def linear_loss(W, k, v, loss="mse"):
-    """Per-chain loss value: 1/2||W k - v||^2 (mse) or -v^T W k (dot).  -> [N]."""
-    y = linear_f(W, k)
+ACTIVATIONS = {"silu": (silu, dsilu), "gelu": (gelu, dgelu)}
+
+
+def layer_norm(y, gamma, beta, eps):
+    """LN over the last axis: gamma * (y - mean) / sqrt(var + eps) + beta, biased variance.
+    y [N, d]; gamma, beta [N, d]."""
+    mu = y.mean(axis=-1, keepdims=True)
+    var = ((y - mu) ** 2).mean(axis=-1, keepdims=True)
+    return gamma * (y - mu) / np.sqrt(var + eps) + beta
+
+
+def layer_norm_vjp(y, gamma, eps, g):
+    """dl/dy given dl/dLN(y) = g (chain rule through the mean and the variance):
+    with s = sqrt(var + eps), xh = (y - mean) / s and gg = gamma * g,
+        dl/dy = (gg - mean(gg) - xh * mean(gg * xh)) / s."""
+    mu = y.mean(axis=-1, keepdims=True)
+    s = np.sqrt(((y - mu) ** 2).mean(axis=-1, keepdims=True) + eps)
+    xh = (y - mu) / s
+    gg = gamma * g
+    return (gg - gg.mean(axis=-1, keepdims=True) - xh * (gg * xh).mean(axis=-1, keepdims=True)) / s
+
+
+def _wrap(res, x, ln):
+    """The inner model's output from f_res(x): res itself, or x + LN(res) with ln given."""
+    return res if ln is None else x + layer_norm(res, ln[0], ln[1], ln[2])
+
+
+def _unwrap_vjp(res, err, ln):
+    """dl/df_res from dl/df = err (identity without ln; through LN otherwise)."""
+    return err if ln is None else layer_norm_vjp(res, ln[0], ln[2], err)
+
+
+def _error(out, v, loss):
+    """dl/df: f - v for 1/2 ||f - v||^2, -v for -v^T f."""
+    if loss == "mse":
+        return out - v
+    if loss == "dot":
+        return -v
+    raise ValueError(loss)
+
+
+def linear_f(W, x, ln=None):
+    """f(x; W) = W x, or x + LN(W x) with ln = (gamma [N, d], beta [N, d], eps).
+    W [N, d_out, d_in], x [N, d_in] -> [N, d_out]."""
+    return _wrap(np.einsum("nij,nj->ni", W, x), x, ln)
+
+
+def mlp_f(W1, W2, x, act="silu", ln=None):
+    """f(x; W1, W2) = W2 act(W1 x), or x + LN(W2 act(W1 x)) with ln given.
+    W1 [N, h, d], W2 [N, d, h], x [N, d] -> [N, d]."""
+    fa = ACTIVATIONS[act][0]
+    return _wrap(np.einsum("nih,nh->ni", W2, fa(np.einsum("nhj,nj->nh", W1, x))), x, ln)
+
+
+def linear_loss(W, k, v, loss="mse", ln=None):
+    """Per-chain loss value: 1/2||f(k) - v||^2 (mse) or -v^T f(k) (dot).  -> [N]."""
+    y = linear_f(W, k, ln)
     if loss == "mse":
         return 0.5 * np.sum((y - v) ** 2, axis=-1)
     return -np.sum(v * y, axis=-1)
 
 
-def mlp_loss(W1, W2, k, v, loss="mse"):
-    """Per-chain loss value of the 2-layer SiLU inner MLP.  -> [N]."""
-    y = mlp_f(W1, W2, k)
+def mlp_loss(W1, W2, k, v, loss="mse", act="silu", ln=None):
+    """Per-chain loss value of the 2-layer inner MLP.  -> [N]."""
+    y = mlp_f(W1, W2, k, act, ln)
     if loss == "mse":
         return 0.5 * np.sum((y - v) ** 2, axis=-1)
     return -np.sum(v * y, axis=-1)
 
 
-def linear_grad(W, k, v, loss="mse"):
-    """Gradient of the loss with respect to W for f(k; W) = W k.
+def linear_grad(W, k, v, loss="mse", ln=None):
+    """Gradient of the loss with respect to W for f(k; W) = W k (or k + LN(W k)).
 
     mse: (W k - v) k^T  ("Fast weights" page, section 1, gradient of the linear model).
     dot: -v k^T         (blog page, "TTT / 如何理解", gradient of the negative dot product,
                           written here in the column-vector form).
+    With ln the error term f(k) - v (or -v) first passes back through the layer norm.
     W [N, d, d], k, v [N, d] -> [N, d, d].
     """
-    if loss == "mse":
-        r = linear_f(W, k) - v
-    elif loss == "dot":
-        r = -v
-    else:
-        raise ValueError(loss)
+    y = np.einsum("nij,nj->ni", W, k)
+    r = _unwrap_vjp(y, _error(_wrap(y, k, ln), v, loss), ln)
     return np.einsum("ni,nj->nij", r, k)
 
 
-def mlp_grad(W1, W2, k, v, loss="mse"):
-    """Gradients (dW1, dW2) of the loss for f(k) = W2 SiLU(W1 k), by the chain rule.
+def mlp_grad(W1, W2, k, v, loss="mse", act="silu", ln=None):
+    """Gradients (dW1, dW2) of the loss for f(k) = W2 act(W1 k) (or k + LN of it), by the
+    chain rule.
 
-    u = W1 k, a = SiLU(u), y = W2 a, dl/dy = y - v (mse) or -v (dot),
-    dW2 = (dl/dy) a^T, dW1 = ((W2^T dl/dy) * SiLU'(u)) k^T.
+    u = W1 k, a = act(u), y = W2 a, dl/dy = f - v (mse) or -v (dot), passed back through
+    the layer norm when ln is given; dW2 = (dl/dy) a^T, dW1 = ((W2^T dl/dy) * act'(u)) k^T.
     """
+    fa, dfa = ACTIVATIONS[act]
     u = np.einsum("nhj,nj->nh", W1, k)
-    a = silu(u)
+    a = fa(u)
     y = np.einsum("nih,nh->ni", W2, a)
-    if loss == "mse":
-        r = y - v
-    elif loss == "dot":
-        r = -v
-    else:
-        raise ValueError(loss)
+    r = _unwrap_vjp(y, _error(_wrap(y, k, ln), v, loss), ln)
     g2 = np.einsum("ni,nh->nih", r, a)
-    du = np.einsum("nih,ni->nh", W2, r) * dsilu(u)
+    du = np.einsum("nih,ni->nh", W2, r) * dfa(u)
     g1 = np.einsum("nh,nj->nhj", du, k)
     return g1, g2
 
@@ -174,6 +235,20 @@ def _token_rates(eta, eta_tok, lead, T, dtype):
     return dtype(eta) * np.array(r.reshape(n, T), dtype=dtype, copy=True)
 
 
+def _ln_params(ln, lead, d, dtype):
+    """(gamma [N, d], beta [N, d], eps) broadcast against the chains, or None.  gamma and
+    beta broadcast like the states (e.g. [H, d], one pair per head)."""
+    if ln is None:
+        return None
+    gamma, beta, eps = ln
+    n = int(np.prod(lead)) if lead else 1
+    g = np.broadcast_to(np.asarray(gamma).astype(dtype), tuple(lead) + (d,)).reshape(n, d)
+    b = np.broadcast_to(np.asarray(beta).astype(dtype), tuple(lead) + (d,)).reshape(n, d)
+    if not eps > 0:
+        raise ValueError("the layer norm's eps must be positive")
+    return np.array(g, copy=True), np.array(b, copy=True), dtype(eps)
+
+
 def _check_epochs(epochs, causal):
     if not (isinstance(epochs, (int, np.integer)) and epochs >= 1):
         raise ValueError("epochs must be a positive integer")
@@ -195,12 +270,13 @@ def _check_chunk(T, chunk):
 # ----------------------------------------------------------------------------------------
 
 def ttt_linear(q, k, v, w0, eta, chunk, causal=True, loss="mse", dtype=np.float64, eta_tok=None,
-               epochs=1):
+               epochs=1, ln=None):
     """TTT layer with the linear inner model, mini-batch GD of size `chunk`.
 
     q, k, v: [..., T, d]; w0: [..., d, d] (broadcast over the leading dims, e.g. [H, d, d]
-    shared by every batch element); eta_tok: optional per-token rate factors [..., T].
-    Returns (z [..., T, d], w_final [..., d, d]).
+    shared by every batch element); eta_tok: optional per-token rate factors [..., T];
+    ln: optional (gamma, beta, eps), gamma and beta [..., d] (e.g. [H, d]), for the inner
+    model f(x) = x + LN(W x).  Returns (z [..., T, d], w_final [..., d, d]).
 
     The last chunk is shorter when T is not a multiple of `chunk`.  causal=False trains
     over every chunk first (`epochs` passes) and then applies the final weights to every
@@ -213,6 +289,7 @@ def ttt_linear(q, k, v, w0, eta, chunk, causal=True, loss="mse", dtype=np.float6
     v2, _ = _flatten_tokens(v, dtype)
     N, T, d = q2.shape
     W = _broadcast_state(w0, lead, dtype)
+    lnp = _ln_params(ln, lead, d, dtype)
     b = _check_chunk(T, chunk)
     epochs = _check_epochs(epochs, causal)
     et = _token_rates(eta, eta_tok, lead, T, dtype)
@@ -225,27 +302,28 @@ def ttt_linear(q, k, v, w0, eta, chunk, causal=True, loss="mse", dtype=np.float6
         Wt = Wc
         for t in range(c0, min(c0 + b, T)):
             if et is None:
-                G = G + linear_grad(Wc, k2[:, t], v2[:, t], loss)
+                G = G + linear_grad(Wc, k2[:, t], v2[:, t], loss, lnp)
                 Wt = Wc - eta * G              # W_t, materialised
             else:                              # rate-weighted sum, each token its own rate
-                G = G + et[:, t, None, None] * linear_grad(Wc, k2[:, t], v2[:, t], loss)
+                G = G + et[:, t, None, None] * linear_grad(Wc, k2[:, t], v2[:, t], loss, lnp)
                 Wt = Wc - G
             if causal:
-                z[:, t] = linear_f(Wt, q2[:, t])
+                z[:, t] = linear_f(Wt, q2[:, t], lnp)
         W = Wt
     if not causal:
         for t in range(T):
-            z[:, t] = linear_f(W, q2[:, t])
+            z[:, t] = linear_f(W, q2[:, t], lnp)
     return z.reshape(tuple(lead) + (T, d)), W.reshape(tuple(lead) + (d, d))
 
 
 def ttt_mlp(q, k, v, w1, w2, eta, chunk, causal=True, loss="mse", dtype=np.float64, eta_tok=None,
-            epochs=1):
-    """TTT layer with the 2-layer SiLU MLP inner model, mini-batch GD of size `chunk`.
+            epochs=1, act="silu", ln=None):
+    """TTT layer with the 2-layer MLP inner model, mini-batch GD of size `chunk`.
 
     q, k, v: [..., T, d]; w1: [..., h, d]; w2: [..., d, h] (broadcast over the leading
     dims); eta_tok: optional per-token rate factors [..., T]; epochs: passes over the
-    chunks before the queries are read (non-causal only).
+    chunks before the queries are read (non-causal only); act: "silu" (ViT3 inner MLP) or
+    "gelu" (the paper's TTT-MLP); ln: optional (gamma, beta, eps) for f(x) = x + LN(MLP(x)).
     Returns (z [..., T, d], w1_final [..., h, d], w2_final [..., d, h]).
     """
     if loss not in LOSSES:
@@ -259,6 +337,9 @@ def ttt_mlp(q, k, v, w1, w2, eta, chunk, causal=True, loss="mse", dtype=np.float
     h = W1.shape[-2]
     if W1.shape[-1] != d or W2.shape[-2:] != (d, h):
         raise ValueError("w1 must be [..., h, d] and w2 [..., d, h]")
+    if act not in ACTIVATIONS:
+        raise ValueError(act)
+    lnp = _ln_params(ln, lead, d, dtype)
     b = _check_chunk(T, chunk)
     epochs = _check_epochs(epochs, causal)
     et = _token_rates(eta, eta_tok, lead, T, dtype)
@@ -271,7 +352,7 @@ def ttt_mlp(q, k, v, w1, w2, eta, chunk, causal=True, loss="mse", dtype=np.float
         G2 = np.zeros_like(W2c)
         W1t, W2t = W1c, W2c
         for t in range(c0, min(c0 + b, T)):
-            g1, g2 = mlp_grad(W1c, W2c, k2[:, t], v2[:, t], loss)
+            g1, g2 = mlp_grad(W1c, W2c, k2[:, t], v2[:, t], loss, act, lnp)
             if et is None:
                 G1 = G1 + g1
                 G2 = G2 + g2
@@ -283,11 +364,11 @@ def ttt_mlp(q, k, v, w1, w2, eta, chunk, causal=True, loss="mse", dtype=np.float
                 W1t = W1c - G1
                 W2t = W2c - G2
             if causal:
-                z[:, t] = mlp_f(W1t, W2t, q2[:, t])
+                z[:, t] = mlp_f(W1t, W2t, q2[:, t], act, lnp)
         W1, W2 = W1t, W2t
     if not causal:
         for t in range(T):
-            z[:, t] = mlp_f(W1, W2, q2[:, t])
+            z[:, t] = mlp_f(W1, W2, q2[:, t], act, lnp)
     return (z.reshape(tuple(lead) + (T, d)), W1.reshape(tuple(lead) + (h, d)),
             W2.reshape(tuple(lead) + (d, h)))
 

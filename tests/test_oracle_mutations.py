@@ -15,7 +15,7 @@ import tests.test_oracle_pins as pins
 
 MUTATIONS = {
     "output_reads_chunk_start_weights": (
-        "z[:, t] = linear_f(Wt, q2[:, t])", "z[:, t] = linear_f(Wc, q2[:, t])"),
+        "z[:, t] = linear_f(Wt, q2[:, t], lnp)", "z[:, t] = linear_f(Wc, q2[:, t], lnp)"),
     "gradient_at_current_not_chunk_start": (
         "G = G + linear_grad(Wc, k2[:, t]", "G = G + linear_grad(Wt, k2[:, t]"),
     "dropped_learning_rate": ("Wt = Wc - eta * G", "Wt = Wc - G"),
@@ -23,9 +23,8 @@ MUTATIONS = {
     "transposed_linear_gradient": (
         'return np.einsum("ni,nj->nij", r, k)', 'return np.einsum("ni,nj->nij", k, r)'),
     "transposed_linear_model": (
-        'return np.einsum("nij,nj->ni", W, x)', 'return np.einsum("nji,nj->ni", W, x)'),
-    "dot_loss_sign": ("        r = -v\n    else:\n        raise ValueError(loss)\n    return np.einsum",
-                      "        r = v\n    else:\n        raise ValueError(loss)\n    return np.einsum"),
+        'return _wrap(np.einsum("nij,nj->ni", W, x)', 'return _wrap(np.einsum("nji,nj->ni", W, x)'),
+    "dot_loss_sign": ('    if loss == "dot":\n        return -v', '    if loss == "dot":\n        return v'),
     "delta_rule_transposed_write": (
         'W = W + eta * np.einsum("ni,nj->nij", err, kt)',
         'W = W + eta * np.einsum("ni,nj->nij", kt, err)'),
@@ -38,7 +37,7 @@ MUTATIONS = {
     "silu_derivative_missing_term": ("return s * (1.0 + u * (1.0 - s))", "return s"),
     "silu_is_sigmoid": ("return u / (1.0 + np.exp(-u))", "return 1.0 / (1.0 + np.exp(-u))"),
     "mlp_backward_skips_activation": (
-        'du = np.einsum("nih,ni->nh", W2, r) * dsilu(u)',
+        'du = np.einsum("nih,ni->nh", W2, r) * dfa(u)',
         'du = np.einsum("nih,ni->nh", W2, r)'),
     "mlp_second_layer_not_updated": ("W2t = W2c - eta * G2", "W2t = W2c"),
     "mlp_gradient_at_current_weights": (
@@ -49,9 +48,9 @@ MUTATIONS = {
     "token_rate_of_previous_token": (
         "G = G + et[:, t, None, None] * linear_grad", "G = G + et[:, max(t - 1, 0), None, None] * linear_grad"),
     "token_rate_applied_twice": (
-        "                G = G + et[:, t, None, None] * linear_grad(Wc, k2[:, t], v2[:, t], loss)\n"
+        "                G = G + et[:, t, None, None] * linear_grad(Wc, k2[:, t], v2[:, t], loss, lnp)\n"
         "                Wt = Wc - G",
-        "                G = G + et[:, t, None, None] * linear_grad(Wc, k2[:, t], v2[:, t], loss)\n"
+        "                G = G + et[:, t, None, None] * linear_grad(Wc, k2[:, t], v2[:, t], loss, lnp)\n"
         "                Wt = Wc - eta * G"),
     "mlp_second_layer_ignores_token_rate": (
         "G2 = G2 + et[:, t, None, None] * g2", "G2 = G2 + eta * g2"),
@@ -74,10 +73,29 @@ MUTATIONS = {
         "    for i, c0 in enumerate(chunk_starts):\n"
         "        W = _broadcast_state(w0, lead, dtype) if (i and c0 == 0) else W\n"
         "        Wc = W.copy()"),
+    "ln_vjp_drops_variance_term": (
+        "gg - gg.mean(axis=-1, keepdims=True) - xh * (gg * xh).mean(axis=-1, keepdims=True)",
+        "gg - gg.mean(axis=-1, keepdims=True)"),
+    "ln_vjp_drops_mean_term": (
+        "gg - gg.mean(axis=-1, keepdims=True) - xh", "gg - xh"),
+    "ln_unbiased_variance": (
+        "var = ((y - mu) ** 2).mean(axis=-1, keepdims=True)",
+        "var = ((y - mu) ** 2).sum(axis=-1, keepdims=True) / (y.shape[-1] - 1)"),
+    "ln_eps_outside_sqrt": (
+        "return gamma * (y - mu) / np.sqrt(var + eps) + beta",
+        "return gamma * (y - mu) / (np.sqrt(var) + eps) + beta"),
+    "ln_residual_dropped": (
+        "return res if ln is None else x + layer_norm(", "return res if ln is None else layer_norm("),
+    "ln_gradient_skips_layer_norm": (
+        "return err if ln is None else layer_norm_vjp(res, ln[0], ln[2], err)", "return err"),
+    "gelu_derivative_missing_density_term": (
+        "return 0.5 * (1.0 + erf(u / np.sqrt(2.0))) + u * np.exp(-0.5 * u * u) / np.sqrt(2.0 * np.pi)",
+        "return 0.5 * (1.0 + erf(u / np.sqrt(2.0)))"),
+    "gelu_is_silu": ('"gelu": (gelu, dgelu)', '"gelu": (silu, dsilu)'),
     "noncausal_reads_initial_weights": (
-        "    if not causal:\n        for t in range(T):\n            z[:, t] = linear_f(W, q2[:, t])",
+        "    if not causal:\n        for t in range(T):\n            z[:, t] = linear_f(W, q2[:, t], lnp)",
         "    if not causal:\n        W = _broadcast_state(w0, lead, dtype)\n"
-        "        for t in range(T):\n            z[:, t] = linear_f(W, q2[:, t])"),
+        "        for t in range(T):\n            z[:, t] = linear_f(W, q2[:, t], lnp)"),
 }
 
 

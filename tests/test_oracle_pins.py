@@ -202,6 +202,119 @@ def test_silu_derivative_finite_differences():
     np.testing.assert_allclose(O.silu(u), u / (1 + np.exp(-u)), atol=1e-15)
 
 
+# ---------------------------------------------------------------- layer norm, residual, GELU
+# The paper's inner models (wmrh.cn summary, section 2.2.1): f(x) = x + LN(f_res(x)), f_res
+# linear or a 2-layer MLP with GELU; gamma, beta fixed during the inner loop.
+
+def _ln_args(rng, N, d, eps=1e-5):
+    return (1.0 + 0.3 * rng.standard_normal((N, d)), 0.2 * rng.standard_normal((N, d)), eps)
+
+
+def test_gelu_textbook_values():
+    # GELU(u) = u Phi(u); Phi(1), Phi(2) from the standard normal table
+    u = np.array([-1.0, 0.0, 1.0, 2.0])
+    want = np.array([-0.15865525393145707, 0.0, 0.8413447460685429, 2 * 0.9772498680518208])
+    np.testing.assert_allclose(O.gelu(u), want, atol=1e-15)
+    np.testing.assert_allclose(O.gelu(np.array([30.0, -30.0])), [30.0, 0.0], atol=1e-12)
+
+
+def test_gelu_derivative_finite_differences():
+    u = np.linspace(-6, 6, 49)
+    h = 1e-6
+    num = (O.gelu(u + h) - O.gelu(u - h)) / (2 * h)
+    np.testing.assert_allclose(O.dgelu(u), num, atol=1e-8)
+
+
+def test_layer_norm_standardises_and_ignores_shift_and_scale():
+    rng = _rng(50)
+    y = 3.0 + 2.0 * rng.standard_normal((5, 8))
+    one, zero = np.ones((5, 8)), np.zeros((5, 8))
+    x = O.layer_norm(y, one, zero, 1e-12)
+    np.testing.assert_allclose(x.mean(axis=-1), 0.0, atol=1e-12)
+    np.testing.assert_allclose((x ** 2).mean(axis=-1), 1.0, atol=1e-9)   # biased variance
+    np.testing.assert_allclose(O.layer_norm(7.0 * y - 4.0, one, zero, 1e-12), x, atol=1e-9)
+    g, b = _ln_args(rng, 5, 8)[:2]
+    np.testing.assert_allclose(O.layer_norm(y, g, b, 1e-12), g * x + b, atol=1e-12)
+
+
+def test_layer_norm_vjp_finite_differences():
+    rng = _rng(51)
+    y = rng.standard_normal((1, 6))
+    g, b, eps = _ln_args(rng, 1, 6, eps=0.3)    # a large eps so that it matters
+    up = rng.standard_normal((1, 6))
+    grad = O.layer_norm_vjp(y, g, eps, up)
+    _fd_check(lambda y_: (up * O.layer_norm(y_, g, b, eps)).sum(axis=-1), [y], 0, grad)
+
+
+@pytest.mark.parametrize("loss", ["mse", "dot"])
+def test_linear_ln_gradient_finite_differences(loss):
+    rng = _rng(52)
+    W = rng.standard_normal((1, 5, 5))
+    k, v = rng.standard_normal((1, 5)), rng.standard_normal((1, 5))
+    ln = _ln_args(rng, 1, 5, eps=0.05)
+    g = O.linear_grad(W, k, v, loss, ln)
+    _fd_check(lambda W_: O.linear_loss(W_, k, v, loss, ln), [W], 0, g)
+
+
+@pytest.mark.parametrize("loss,act,with_ln", [("mse", "gelu", True), ("dot", "gelu", True),
+                                              ("mse", "silu", True), ("mse", "gelu", False)])
+def test_mlp_ln_gelu_gradient_finite_differences(loss, act, with_ln):
+    rng = _rng(53)
+    W1 = rng.standard_normal((1, 7, 4))
+    W2 = rng.standard_normal((1, 4, 7))
+    k, v = rng.standard_normal((1, 4)), rng.standard_normal((1, 4))
+    ln = _ln_args(rng, 1, 4, eps=0.05) if with_ln else None
+    g1, g2 = O.mlp_grad(W1, W2, k, v, loss, act, ln)
+    fn = lambda a, b: O.mlp_loss(a, b, k, v, loss, act, ln)
+    _fd_check(fn, [W1, W2], 0, g1)
+    _fd_check(fn, [W1, W2], 1, g2)
+
+
+def test_ln_with_zero_gain_never_learns():
+    # gamma = 0 makes LN(.) the constant beta: f(x) = x + beta, every gradient is zero, the
+    # state never moves and z_t = q_t + beta
+    rng = _rng(54)
+    q, k, v = (x[0] for x in _rand_chains(rng, 1, 9, 4))
+    w0 = rng.standard_normal((4, 4))
+    beta = rng.standard_normal(4)
+    z, w = O.ttt_linear(q, k, v, w0, 0.5, 3, ln=(np.zeros(4), beta, 1e-5))
+    np.testing.assert_allclose(w, w0, atol=0)
+    np.testing.assert_allclose(z, q + beta, atol=1e-15)
+    w1, w2 = rng.standard_normal((6, 4)), rng.standard_normal((4, 6))
+    z, a1, a2 = O.ttt_mlp(q, k, v, w1, w2, 0.5, 4, act="gelu", ln=(np.zeros(4), beta, 1e-5))
+    np.testing.assert_allclose(a1, w1, atol=0)
+    np.testing.assert_allclose(a2, w2, atol=0)
+    np.testing.assert_allclose(z, q + beta, atol=1e-15)
+
+
+@pytest.mark.parametrize("model,chunk,causal", [("linear", 1, True), ("linear", 4, True),
+                                                ("linear", 5, False), ("mlp", 1, True),
+                                                ("mlp", 4, True), ("mlp", 13, False)])
+def test_ln_models_match_autograd(model, chunk, causal):
+    """Recurrence with f(x) = x + LN(f_res(x)) against torch.autograd through torch's own
+    layer_norm and (exact) gelu."""
+    import torch
+    F = torch.nn.functional
+    rng = _rng(55)
+    d = 4
+    q, k, v = (x[0] for x in _rand_chains(rng, 1, 13, d))
+    gam, bet, eps = 1.0 + 0.3 * rng.standard_normal(d), 0.2 * rng.standard_normal(d), 1e-3
+    G, Bt = torch.tensor(gam), torch.tensor(bet)
+    if model == "linear":
+        params = [0.5 * rng.standard_normal((d, d))]
+        f = lambda P, x: x + F.layer_norm(P[0] @ x, (d,), G, Bt, eps)
+        z, *w = O.ttt_linear(q, k, v, params[0], 0.2, chunk, causal=causal, ln=(gam, bet, eps))
+    else:
+        params = [0.5 * rng.standard_normal((6, d)), 0.5 * rng.standard_normal((d, 6))]
+        f = lambda P, x: x + F.layer_norm(P[1] @ F.gelu(P[0] @ x), (d,), G, Bt, eps)
+        z, *w = O.ttt_mlp(q, k, v, params[0], params[1], 0.2, chunk, causal=causal, act="gelu",
+                          ln=(gam, bet, eps))
+    zr, wr = _autograd_chunked(q, k, v, params, f, 0.2, chunk, causal)
+    np.testing.assert_allclose(z, zr, atol=1e-11)
+    for a, b in zip(w, wr):
+        np.testing.assert_allclose(a, b, atol=1e-11)
+
+
 # ---------------------------------------------------------------- delta-rule invariants
 
 def test_linear_chunk1_equals_delta_rule():
