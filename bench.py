@@ -64,17 +64,19 @@ def measured_traffic(workload_name):
     return rec["fetch_bytes"] + rec["write_bytes"]
 
 
-def make_device_inputs(w, seed, torch, rates=False):
+def make_device_inputs(w, seed, torch, rates=False, paper=False):
     import numpy as np
-    from test_sequence_layers_amd.workloads import make_inputs, make_token_rates
+    from test_sequence_layers_amd.workloads import make_inputs, make_ln_params, make_token_rates
     inp = make_inputs(w, seed=seed)
     if rates:
         inp["eta_tok"] = make_token_rates(w, seed)
+    if paper:
+        inp["ln_w"], inp["ln_b"] = make_ln_params(w, seed)
     dt = torch.bfloat16 if w.io == "bf16" else torch.float32
     dev = {}
     for key in ("q", "k", "v"):
         dev[key] = torch.from_numpy(np.ascontiguousarray(inp[key])).to("cuda").to(dt).contiguous()
-    for key in ("w0", "w1", "w2", "eta_tok"):
+    for key in ("w0", "w1", "w2", "eta_tok", "ln_w", "ln_b"):
         if key in inp:
             dev[key] = torch.from_numpy(inp[key]).to("cuda").contiguous()
     dev["z"] = torch.empty_like(dev["q"])
@@ -83,6 +85,15 @@ def make_device_inputs(w, seed, torch, rates=False):
 
 def launch(w, dev, ttt, loss="mse", epochs=1):
     et = dev.get("eta_tok")
+    if "ln_w" in dev:  # the paper's inner models: x + LN(f_res(x)), GELU in the MLP
+        ln = (dev["ln_w"], dev["ln_b"])
+        if w.kind == "linear":
+            ttt.ttt_linear_ln_fwd(dev["q"], dev["k"], dev["v"], dev["w0"], *ln, w.eta, w.chunk,
+                                  w.causal, eta_tok=et, loss=loss, epochs=epochs, z=dev["z"])
+        else:
+            ttt.ttt_mlp_ln_fwd(dev["q"], dev["k"], dev["v"], dev["w1"], dev["w2"], *ln, w.eta,
+                               w.chunk, w.causal, eta_tok=et, loss=loss, epochs=epochs, z=dev["z"])
+        return
     if w.kind == "linear":
         ttt.ttt_linear_fwd(dev["q"], dev["k"], dev["v"], dev["w0"], w.eta, w.chunk, w.causal,
                            eta_tok=et, loss=loss, epochs=epochs, z=dev["z"])
@@ -93,13 +104,14 @@ def launch(w, dev, ttt, loss="mse", epochs=1):
                         w.causal, eta_tok=et, loss=loss, epochs=epochs, z=dev["z"])
 
 
-def time_workload(w, steps, warmup, torch, ttt, rotate=None, rates=False, loss="mse", epochs=1):
+def time_workload(w, steps, warmup, torch, ttt, rotate=None, rates=False, loss="mse", epochs=1,
+                  paper=False):
     bytes_, flops = algorithmic_cost(w, epochs)
     if rates:
         bytes_ += w.B * w.H * w.T * 4  # the rate factors, read once
     if rotate is None:
         rotate = max(2, min(8, int(6 * 256e6 / max(bytes_, 1)) + 1))
-    sets = [make_device_inputs(w, w.seed + i, torch, rates) for i in range(rotate)]
+    sets = [make_device_inputs(w, w.seed + i, torch, rates, paper) for i in range(rotate)]
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         launch(w, sets[i % rotate], ttt, loss, epochs)
@@ -294,8 +306,8 @@ def main():
                 "mfma_util_pct": round(100 * r["tflops"] / BF16_MFMA_PEAK_TFLOPS, 3),
             }
         # variants: the headline workload with per-token rate factors (uniform in [0, 1)),
-        # the dot-product loss on the headline and the vision workloads, and mini-batches
-        # with epochs on the vision workload
+        # the dot-product loss on the headline and the vision workloads, mini-batches with
+        # epochs on the vision workload
         variants = []
         if not args.token_rates:
             variants.append((w, "+token_rates", dict(rates=True)))
@@ -306,6 +318,10 @@ def main():
         # (eta 0.01: at eta 1 several steps diverge)
         variants += [(o.replace(chunk=49, eta=0.01), "+chunk49_epochs2", dict(epochs=2))
                      for o in WORKLOADS if o.name == "mlp_vision_N196"]
+        # the paper's inner models (x + LN(f_res(x)); GELU in the MLP) on the headline linear
+        # and the causal MLP workloads
+        variants += [(o, "+paper_ln", dict(paper=True)) for o in WORKLOADS
+                     if o.name in ("linear_d64_T2048", "mlp_h256_T2048")]
         # backward pass of the headline workload (dz ~ N(0, 1), dw_out = 0)
         if w.kind == "linear":
             r = time_backward(w, max(10, args.steps // 2), 3, torch, ttt)

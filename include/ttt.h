@@ -101,6 +101,36 @@ int ttt_mlp_fwd(const void* q, const void* k, const void* v,
                 ttt_stream_t stream);
 
 /*
+ * The paper's instantiation of the inner model (wmrh.cn summary of Sun et al. 2024, section
+ * 2.2.1: layer norm and a residual connection are always included, for stability):
+ *   f(x) = x + LN(f_res(x)),   LN(y) = ln_weight * (y - mean(y)) / sqrt(var(y) + ln_eps) + ln_bias
+ * over the d features of a token (biased variance).  ttt_linear_ln_fwd: f_res(x) = W x (the
+ * paper's TTT-Linear); ttt_mlp_ln_fwd: f_res(x) = W2 GELU(W1 x) with GELU(u) = u Phi(u), Phi
+ * the standard normal CDF (the paper's TTT-MLP, hidden width dh, 4 d in the paper).  The
+ * loss, the update and output rules and every other argument are those of ttt_linear_fwd /
+ * ttt_mlp_fwd; only W (W1, W2) is trained, the layer norm's parameters are fixed.
+ *   ln_weight, ln_bias  float32 [H][d] device pointers (one gain and bias per head, shared
+ *                       over the batch), owned by the caller;  ln_eps > 0 and finite.
+ * Supported: as ttt_linear_fwd / ttt_mlp_fwd (these run on the vector-ALU kernels).
+ * TTT_E_INVALID additionally for a null ln_weight / ln_bias or a bad ln_eps.
+ */
+int ttt_linear_ln_fwd(const void* q, const void* k, const void* v,
+                      const float* w0, long long w0_batch_stride,
+                      const float* ln_weight, const float* ln_bias, float ln_eps,
+                      void* z, float* w_out,
+                      int B, int H, int T, int d, int chunk, int causal, float eta,
+                      const float* eta_tok, int loss, int epochs, int io_dtype,
+                      ttt_stream_t stream);
+
+int ttt_mlp_ln_fwd(const void* q, const void* k, const void* v,
+                   const float* w1, const float* w2, long long w_batch_stride,
+                   const float* ln_weight, const float* ln_bias, float ln_eps,
+                   void* z, float* w1_out, float* w2_out,
+                   int B, int H, int T, int d, int dh, int chunk, int causal, float eta,
+                   const float* eta_tok, int loss, int epochs, int io_dtype,
+                   ttt_stream_t stream);
+
+/*
  * Delta rule (mini-batch of one token, causal): W_t = W_{t-1} + eta_t (v_t - W_{t-1} k_t) k_t^T,
  * z_t = W_t q_t ("Fast weights" page, section 1), eta_t = eta or eta * eta_tok[t].  Same
  * arguments as ttt_linear_fwd without chunk / causal.  Supported: d in {16, 32, 64}, both

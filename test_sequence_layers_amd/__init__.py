@@ -1,8 +1,10 @@
 """MI355X-native (gfx950) TTT layers.
 
 The compute runs in libttt.so (C ABI, include/ttt.h): hand-written HIP kernels for the
-TTT-Linear, TTT-MLP and delta-rule forward passes and the TTT-Linear backward pass.  This package holds the ctypes binding
-(argument marshalling only), the in-tree build script and the seeded synthetic workloads.
+TTT-Linear, TTT-MLP and delta-rule forward passes (plain inner models, and the paper's with
+layer norm and residual) and the TTT-Linear backward pass.  This package holds the ctypes
+binding (argument marshalling only), the in-tree build script and the seeded synthetic
+workloads.
 """
 from ._binding import (  # noqa: F401
     LIB_PATH,
@@ -19,5 +21,7 @@ from ._binding import (  # noqa: F401
     load_library,
     ttt_linear_bwd,
     ttt_linear_fwd,
+    ttt_linear_ln_fwd,
     ttt_mlp_fwd,
+    ttt_mlp_ln_fwd,
 )

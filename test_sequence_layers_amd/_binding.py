@@ -29,6 +29,10 @@ SIGNATURES = {
                             _i, _i, _vp]),
     "ttt_mlp_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp,
                          _i, _i, _i, _i, _i, _i, _i, _f, _vp, _i, _i, _i, _vp]),
+    "ttt_linear_ln_fwd": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _f, _vp, _vp, _i, _i, _i, _i, _i,
+                               _i, _f, _vp, _i, _i, _i, _vp]),
+    "ttt_mlp_ln_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _ll, _vp, _vp, _f, _vp, _vp, _vp,
+                            _i, _i, _i, _i, _i, _i, _i, _f, _vp, _i, _i, _i, _vp]),
     "delta_rule_fwd": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _i, _i, _i, _i, _f, _vp, _i, _vp]),
     "ttt_linear_bwd": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp, _vp, _vp, _vp,
                             _i, _i, _i, _i, _i, _f, _i, _vp]),
@@ -158,6 +162,40 @@ def _out(t, shape, dtype, device, name):
     return t
 
 
+def _ln(ln_weight, ln_bias, ln_eps, H, d, device):
+    """Pointers of the per-head layer-norm gain and bias ([H, d] float32 each)."""
+    torch = _torch()
+    for name, t in (("ln_weight", ln_weight), ("ln_bias", ln_bias)):
+        if (not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or not t.is_contiguous()
+                or tuple(t.shape) != (H, d) or t.device != device):
+            raise ValueError(f"{name} must be a contiguous float32 tensor [H, d] = [{H}, {d}] on {device}")
+    return ln_weight.data_ptr(), ln_bias.data_ptr(), float(ln_eps)
+
+
+def _linear(q, k, v, w0, eta, chunk, causal, ln, eta_tok, loss, epochs, z, w_out, return_state,
+            stream):
+    torch = _torch()
+    lib = load_library()
+    B, H, T, d = _tokens(q, k, v)
+    w0, stride = _state(w0, B, H, (d, d), "w0", q.device)
+    z = _out(z, (B, H, T, d), q.dtype, q.device, "z")
+    if return_state or w_out is not None:
+        w_out = _out(w_out, (B, H, d, d), torch.float32, q.device, "w_out")
+    tail = (z.data_ptr(), w_out.data_ptr() if w_out is not None else None,
+            B, H, T, d, int(chunk), int(bool(causal)), float(eta),
+            _rates(eta_tok, B, H, T, q.device), _loss(loss), int(epochs),
+            _io_dtype(q), _stream(q.device, stream))
+    with torch.cuda.device(q.device):
+        if ln is None:
+            rc = lib.ttt_linear_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), w0.data_ptr(), stride,
+                                    *tail)
+        else:
+            rc = lib.ttt_linear_ln_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), w0.data_ptr(),
+                                       stride, *_ln(*ln, H, d, q.device), *tail)
+    _check(rc)
+    return (z, w_out) if w_out is not None else z
+
+
 def ttt_linear_fwd(q, k, v, w0, eta, chunk, causal=True, *, eta_tok=None, loss="mse", epochs=1,
                    z=None, w_out=None, return_state=False, stream=None):
     """TTT-Linear forward.  q, k, v [B,H,T,d] (float32 or bfloat16, same device);
@@ -166,21 +204,17 @@ def ttt_linear_fwd(q, k, v, w0, eta, chunk, causal=True, *, eta_tok=None, loss="
     (reconstruction) or "dot" (negative dot product); epochs: passes over the chunks
     before the queries are read (non-causal only).  Returns z (and the final state
     [B,H,d,d] when return_state or w_out is given)."""
-    torch = _torch()
-    lib = load_library()
-    B, H, T, d = _tokens(q, k, v)
-    w0, stride = _state(w0, B, H, (d, d), "w0", q.device)
-    z = _out(z, (B, H, T, d), q.dtype, q.device, "z")
-    if return_state or w_out is not None:
-        w_out = _out(w_out, (B, H, d, d), torch.float32, q.device, "w_out")
-    with torch.cuda.device(q.device):
-        rc = lib.ttt_linear_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), w0.data_ptr(), stride,
-                                z.data_ptr(), w_out.data_ptr() if w_out is not None else None,
-                                B, H, T, d, int(chunk), int(bool(causal)), float(eta),
-                                _rates(eta_tok, B, H, T, q.device), _loss(loss), int(epochs),
-                                _io_dtype(q), _stream(q.device, stream))
-    _check(rc)
-    return (z, w_out) if w_out is not None else z
+    return _linear(q, k, v, w0, eta, chunk, causal, None, eta_tok, loss, epochs, z, w_out,
+                   return_state, stream)
+
+
+def ttt_linear_ln_fwd(q, k, v, w0, ln_weight, ln_bias, eta, chunk, causal=True, *, ln_eps=1e-6,
+                      eta_tok=None, loss="mse", epochs=1, z=None, w_out=None,
+                      return_state=False, stream=None):
+    """The paper's TTT-Linear, f(x) = x + LN(W x) with per-head ln_weight, ln_bias float32
+    [H, d]; every other argument as ttt_linear_fwd."""
+    return _linear(q, k, v, w0, eta, chunk, causal, (ln_weight, ln_bias, ln_eps), eta_tok, loss,
+                   epochs, z, w_out, return_state, stream)
 
 
 def ttt_linear_bwd(q, k, v, w0, eta, chunk, dz, dw_out=None, *, stream=None):
@@ -230,12 +264,8 @@ def delta_rule_fwd(q, k, v, w0, eta, *, eta_tok=None, z=None, w_out=None, return
     return (z, w_out) if w_out is not None else z
 
 
-def ttt_mlp_fwd(q, k, v, w1, w2, eta, chunk, causal=True, *, eta_tok=None, loss="mse", epochs=1,
-                z=None, w1_out=None, w2_out=None, return_state=False, stream=None):
-    """TTT-MLP forward, f(k) = W2 SiLU(W1 k).  w1 float32 [H,dh,d] or [B,H,dh,d], w2 float32
-    [H,d,dh] or [B,H,d,dh] (both shared or both per batch); eta_tok, loss and epochs as in
-    ttt_linear_fwd.
-    Returns z (and the final states when return_state or an output state is given)."""
+def _mlp(q, k, v, w1, w2, eta, chunk, causal, ln, eta_tok, loss, epochs, z, w1_out, w2_out,
+         return_state, stream):
     torch = _torch()
     lib = load_library()
     B, H, T, d = _tokens(q, k, v)
@@ -251,13 +281,35 @@ def ttt_mlp_fwd(q, k, v, w1, w2, eta, chunk, causal=True, *, eta_tok=None, loss=
     if want:
         w1_out = _out(w1_out, (B, H, dh, d), torch.float32, q.device, "w1_out")
         w2_out = _out(w2_out, (B, H, d, dh), torch.float32, q.device, "w2_out")
+    tail = (z.data_ptr(), w1_out.data_ptr() if want else None, w2_out.data_ptr() if want else None,
+            B, H, T, d, dh, int(chunk), int(bool(causal)), float(eta),
+            _rates(eta_tok, B, H, T, q.device), _loss(loss), int(epochs),
+            _io_dtype(q), _stream(q.device, stream))
     with torch.cuda.device(q.device):
-        rc = lib.ttt_mlp_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), w1.data_ptr(),
-                             w2.data_ptr(), s1, z.data_ptr(),
-                             w1_out.data_ptr() if want else None,
-                             w2_out.data_ptr() if want else None,
-                             B, H, T, d, dh, int(chunk), int(bool(causal)), float(eta),
-                             _rates(eta_tok, B, H, T, q.device), _loss(loss), int(epochs),
-                             _io_dtype(q), _stream(q.device, stream))
+        if ln is None:
+            rc = lib.ttt_mlp_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), w1.data_ptr(),
+                                 w2.data_ptr(), s1, *tail)
+        else:
+            rc = lib.ttt_mlp_ln_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), w1.data_ptr(),
+                                    w2.data_ptr(), s1, *_ln(*ln, H, d, q.device), *tail)
     _check(rc)
     return (z, w1_out, w2_out) if want else z
+
+
+def ttt_mlp_fwd(q, k, v, w1, w2, eta, chunk, causal=True, *, eta_tok=None, loss="mse", epochs=1,
+                z=None, w1_out=None, w2_out=None, return_state=False, stream=None):
+    """TTT-MLP forward, f(k) = W2 SiLU(W1 k).  w1 float32 [H,dh,d] or [B,H,dh,d], w2 float32
+    [H,d,dh] or [B,H,d,dh] (both shared or both per batch); eta_tok, loss and epochs as in
+    ttt_linear_fwd.
+    Returns z (and the final states when return_state or an output state is given)."""
+    return _mlp(q, k, v, w1, w2, eta, chunk, causal, None, eta_tok, loss, epochs, z, w1_out,
+                w2_out, return_state, stream)
+
+
+def ttt_mlp_ln_fwd(q, k, v, w1, w2, ln_weight, ln_bias, eta, chunk, causal=True, *, ln_eps=1e-6,
+                   eta_tok=None, loss="mse", epochs=1, z=None, w1_out=None, w2_out=None,
+                   return_state=False, stream=None):
+    """The paper's TTT-MLP, f(x) = x + LN(W2 GELU(W1 x)) with per-head ln_weight, ln_bias
+    float32 [H, d]; every other argument as ttt_mlp_fwd."""
+    return _mlp(q, k, v, w1, w2, eta, chunk, causal, (ln_weight, ln_bias, ln_eps), eta_tok, loss,
+                epochs, z, w1_out, w2_out, return_state, stream)

@@ -26,6 +26,45 @@ __device__ __forceinline__ float dsilu_(float u) {
   return s * (1.0f + u * (1.0f - s));
 }
 
+// GELU(u) = u Phi(u) with the exact normal CDF Phi(u) = (1 + erf(u / sqrt 2)) / 2, and its
+// derivative Phi(u) + u phi(u) (phi the standard normal density).
+__device__ __forceinline__ float gelu_(float u) { return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f)); }
+__device__ __forceinline__ float dgelu_(float u) {
+  return 0.5f * (1.0f + erff(u * 0.70710678118654752f)) + u * 0.39894228040143268f * __expf(-0.5f * u * u);
+}
+
+// Sum over aligned groups of W consecutive lanes of a wave (W a power of two <= 64).  Every
+// lane of the wave must take part.
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// Layer norm over the D features of a token held one per lane by D consecutive lanes:
+// xh = (y - mean) / sqrt(var + eps) (biased variance) and rstd = 1 / sqrt(var + eps).
+struct LnRow {
+  float xh, rstd;
+};
+template <int D>
+__device__ __forceinline__ LnRow ln_row(float y, float eps) {
+  const float mu = group_sum<D>(y) * (1.0f / D);
+  const float dy = y - mu;
+  const float var = group_sum<D>(dy * dy) * (1.0f / D);
+  const float rstd = 1.0f / sqrtf(var + eps);
+  return {dy * rstd, rstd};
+}
+// dl/dy of LN(y) = gamma xh + beta given dl/dLN = g (chain rule through the mean and the
+// variance): rstd (gg - mean(gg) - xh mean(gg xh)), gg = gamma g.
+template <int D>
+__device__ __forceinline__ float ln_row_vjp(const LnRow& s, float gamma, float g) {
+  const float gg = gamma * g;
+  const float m1 = group_sum<D>(gg) * (1.0f / D);
+  const float m2 = group_sum<D>(gg * s.xh) * (1.0f / D);
+  return s.rstd * (gg - m1 - s.xh * m2);
+}
+
 // Arguments of one forward call, as validated by the host API.
 struct LinearArgs {
   const void* q;
@@ -41,6 +80,10 @@ struct LinearArgs {
   int dot_loss;          // 1: loss -v^T f(k), error term -v; 0: 1/2 ||f(k) - v||^2
   float* w_hist;         // generic kernel only: chunk-start states [B][H][nchunks][d][d] or null
   int epochs = 1;        // passes over the chunks before the outputs (non-causal only)
+  // the paper's inner model f(x) = x + LN(W x): per-head gamma, beta [H][d] (null: f = W x)
+  const float* ln_w = nullptr;
+  const float* ln_b = nullptr;
+  float ln_eps = 0.0f;
 };
 
 // Backward pass of the causal TTT-Linear layer (reconstruction loss, scalar rate).
@@ -74,6 +117,11 @@ struct MlpArgs {
   const float* eta_tok;  // per-token rate factors [B][H][T] (rate eta * eta_tok[t]) or null
   int dot_loss;          // 1: loss -v^T f(k), error term -v; 0: 1/2 ||f(k) - v||^2
   int epochs = 1;        // passes over the chunks before the outputs (non-causal only)
+  // the paper's TTT-MLP: f(x) = x + LN(W2 GELU(W1 x)), per-head gamma, beta [H][d]
+  // (null: f = W2 SiLU(W1 x))
+  const float* ln_w = nullptr;
+  const float* ln_b = nullptr;
+  float ln_eps = 0.0f;
 };
 
 // Host-side launchers (return a hipError_t; argument checks are done by the caller).

@@ -23,6 +23,14 @@
 // floating-point order.  With causal = 0 the training pass (repeated for `epochs` passes
 // over the chunks, ViT3 news page, observation 2) writes no output and a second pass
 // computes z_t = W_final q_t.
+//
+// kLN: the paper's instantiation f(x) = x + LN(W x) (wmrh.cn summary, section 2.2.1), LN with
+// per-head gamma, beta.  The state still changes only through the residual rows (the
+// gradient is r k^T with r = dl/d(W k)), so the dual form above is unchanged: the residual
+// row is y = Wc k passed through LN and back, r = LN'(y)^T (k + LN(y) - v), and the output
+// row is z = q + LN(Wn q - sum_s (q . k_s) r_s).  Each of the kSub x D elements of a
+// sub-block belongs to one thread (kThreads >= kSub D), so a token's D features sit in D
+// consecutive lanes and the LN statistics are shuffle sums inside that lane group.
 #include "common.hpp"
 
 namespace ttt {
@@ -31,7 +39,9 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kSub = 16;
 
-template <typename IO, int D>
+static_assert(kThreads >= kSub * 64, "one sub-block element per thread");
+
+template <typename IO, int D, bool kLN>
 __global__ __launch_bounds__(kThreads) void linear_generic_kernel(LinearArgs a) {
   __shared__ float Wc[D][D + 1];
   __shared__ float Wn[D][D + 1];
@@ -54,6 +64,10 @@ __global__ __launch_bounds__(kThreads) void linear_generic_kernel(LinearArgs a) 
   IO* z = static_cast<IO*>(a.z) + tok0;
   const float* w0 = a.w0 + bi * a.w0_batch_stride + static_cast<long long>(hi) * D * D;
   const float* etok = a.eta_tok ? a.eta_tok + static_cast<size_t>(chain) * T : nullptr;
+  // LN gain and bias of this thread's feature (the feature index of a sub-block element is
+  // tid % D in every loop below)
+  const float gam = kLN ? a.ln_w[hi * D + tid % D] : 0.0f;
+  const float bet = kLN ? a.ln_b[hi * D + tid % D] : 0.0f;
 
   for (int e = tid; e < D * D; e += kThreads) {
     const float w = w0[e];
@@ -89,7 +103,14 @@ __global__ __launch_bounds__(kThreads) void linear_generic_kernel(LinearArgs a) 
 #pragma unroll 16
         for (int j = 0; j < D; ++j) acc += Ks[t][j] * Wc[i][j];
         const float rate = t < n ? (etok ? eta * etok[s0 + t] : eta) : 0.0f;
-        const float err = a.dot_loss ? -Vs[t][i] : acc - Vs[t][i];  // dl/df: f - v or -v
+        float err;  // dl/d(W k): f - v or -v, through the layer norm with kLN
+        if constexpr (kLN) {
+          const LnRow st = ln_row<D>(acc, a.ln_eps);
+          const float f = Ks[t][i] + gam * st.xh + bet;
+          err = ln_row_vjp<D>(st, gam, a.dot_loss ? -Vs[t][i] : f - Vs[t][i]);
+        } else {
+          err = a.dot_loss ? -Vs[t][i] : acc - Vs[t][i];
+        }
         Rs[t][i] = t < n ? rate * err : 0.0f;
       }
       if (a.causal) {
@@ -107,13 +128,14 @@ __global__ __launch_bounds__(kThreads) void linear_generic_kernel(LinearArgs a) 
       if (a.causal && a.z) {
         for (int e = tid; e < kSub * D; e += kThreads) {
           const int t = e / D, i = e % D;
-          if (t >= n) continue;
           float acc = 0.0f;
 #pragma unroll 16
           for (int j = 0; j < D; ++j) acc += Qs[t][j] * Wn[i][j];
           float corr = 0.0f;
           for (int s = 0; s <= t; ++s) corr += Ps[t][s] * Rs[s][i];
-          z[static_cast<size_t>(s0 + t) * D + i] = from_f32<IO>(acc - corr);
+          float zt = acc - corr;
+          if constexpr (kLN) zt = Qs[t][i] + gam * ln_row<D>(zt, a.ln_eps).xh + bet;
+          if (t < n) z[static_cast<size_t>(s0 + t) * D + i] = from_f32<IO>(zt);
         }
         __syncthreads();
       }
@@ -139,11 +161,11 @@ __global__ __launch_bounds__(kThreads) void linear_generic_kernel(LinearArgs a) 
       __syncthreads();
       for (int e = tid; e < kSub * D; e += kThreads) {
         const int t = e / D, i = e % D;
-        if (t >= n) continue;
         float acc = 0.0f;
 #pragma unroll 16
         for (int j = 0; j < D; ++j) acc += Qs[t][j] * Wn[i][j];
-        z[static_cast<size_t>(s0 + t) * D + i] = from_f32<IO>(acc);
+        if constexpr (kLN) acc = Qs[t][i] + gam * ln_row<D>(acc, a.ln_eps).xh + bet;
+        if (t < n) z[static_cast<size_t>(s0 + t) * D + i] = from_f32<IO>(acc);
       }
       __syncthreads();
     }
@@ -155,13 +177,13 @@ __global__ __launch_bounds__(kThreads) void linear_generic_kernel(LinearArgs a) 
   }
 }
 
-template <typename IO>
+template <typename IO, bool kLN>
 hipError_t launch_d(const LinearArgs& a, hipStream_t s) {
   const dim3 grid(a.B * a.H), block(kThreads);
   switch (a.d) {
-    case 16: hipLaunchKernelGGL((linear_generic_kernel<IO, 16>), grid, block, 0, s, a); break;
-    case 32: hipLaunchKernelGGL((linear_generic_kernel<IO, 32>), grid, block, 0, s, a); break;
-    case 64: hipLaunchKernelGGL((linear_generic_kernel<IO, 64>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((linear_generic_kernel<IO, 16, kLN>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((linear_generic_kernel<IO, 32, kLN>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((linear_generic_kernel<IO, 64, kLN>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -170,7 +192,8 @@ hipError_t launch_d(const LinearArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_linear_generic(const LinearArgs& a, bool bf16_io, hipStream_t s) {
-  return bf16_io ? launch_d<bf16>(a, s) : launch_d<float>(a, s);
+  if (a.ln_w) return bf16_io ? launch_d<bf16, true>(a, s) : launch_d<float, true>(a, s);
+  return bf16_io ? launch_d<bf16, false>(a, s) : launch_d<float, false>(a, s);
 }
 
 }  // namespace ttt

@@ -568,7 +568,7 @@ static bool mfma_shape_ok(const LinearArgs& a) {
   // byte offsets inside one sequence, including the loads the ring issues past the end,
   // are 32-bit
   const bool fits = static_cast<long long>(a.T) * kD * 2 + 2LL * kTileBytes * (kRingMax + 2 * kGroup) < 0x7fffffffLL;
-  return a.d == kD && a.T > 0 && aligned && fits;
+  return a.d == kD && a.T > 0 && a.ln_w == nullptr && aligned && fits;
 }
 
 static long long mfma_grid(const LinearArgs& a) {

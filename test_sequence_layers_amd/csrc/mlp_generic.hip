@@ -22,6 +22,13 @@
 // then W1n -= dU^T K and W2n -= R^T A; at the end of a chunk W1c/W2c <- W1n/W2n.  The
 // non-causal layer may repeat the pass over the chunks for several epochs (ViT3 news page,
 // observation 2) before every query reads the final weights.
+//
+// kPaper: the paper's TTT-MLP, f(x) = x + LN(W2 GELU(W1 x)) (wmrh.cn summary, section 2.2.1),
+// LN with per-head gamma, beta.  The dual form is unchanged with GELU in place of SiLU; the
+// residual row r = dl/d(W2 a) passes the error k + LN(y) - v back through the layer norm of
+// y = W2c a, and the output row is z = q + LN(y_q) with y_q the dual-form pre-LN output.
+// Each of the kSub x D output elements of a sub-block belongs to one thread, so a token's D
+// features sit in D consecutive lanes and the LN statistics are shuffle sums among them.
 #include "common.hpp"
 
 namespace ttt {
@@ -45,7 +52,14 @@ struct MlpLds {
   static __host__ __device__ size_t total(int h) { return aq(h) + static_cast<size_t>(kSub) * h; }
 };
 
-template <typename IO, int D>
+static_assert(kThreads >= kSub * 64, "one output element of a sub-block per thread");
+
+template <bool kPaper>
+__device__ __forceinline__ float act_(float u) { return kPaper ? gelu_(u) : silu_(u); }
+template <bool kPaper>
+__device__ __forceinline__ float dact_(float u) { return kPaper ? dgelu_(u) : dsilu_(u); }
+
+template <typename IO, int D, bool kPaper>
 __global__ __launch_bounds__(kThreads) void mlp_generic_kernel(MlpArgs a, float* ws) {
   extern __shared__ float lds[];
   const int h = a.dh;
@@ -78,6 +92,9 @@ __global__ __launch_bounds__(kThreads) void mlp_generic_kernel(MlpArgs a, float*
   float* W2c = W1c + hd;                                  // [D][h]
   float* W1n = W2c + hd;
   float* W2n = W1n + hd;
+  // LN gain and bias of this thread's output feature (tid % D in every kSub x D loop)
+  const float gam = kPaper ? a.ln_w[hi * D + tid % D] : 0.0f;
+  const float bet = kPaper ? a.ln_b[hi * D + tid % D] : 0.0f;
 
   for (size_t e = tid; e < hd; e += kThreads) {
     const float x1 = w1i[e], x2 = w2i[e];
@@ -102,14 +119,14 @@ __global__ __launch_bounds__(kThreads) void mlp_generic_kernel(MlpArgs a, float*
         Vs[e] = in ? to_f32(v[off]) : 0.0f;
       }
       __syncthreads();
-      // key forward, first layer: u = W1c k, a = SiLU(u), keep SiLU'(u)
+      // key forward, first layer: u = W1c k, a = act(u), keep act'(u)
       for (int e = tid; e < kSub * h; e += kThreads) {
         const int t = e / h, c = e % h;
         float u = 0.0f;
         for (int j = 0; j < D; ++j) u += Ks[t * D + j] * W1c[static_cast<size_t>(c) * D + j];
         const bool in = t < n;
-        Ab[e] = in ? silu_(u) : 0.0f;
-        DU[e] = in ? dsilu_(u) : 0.0f;
+        Ab[e] = in ? act_<kPaper>(u) : 0.0f;
+        DU[e] = in ? dact_<kPaper>(u) : 0.0f;
       }
       __syncthreads();
       // second layer and rate-scaled residual: r = eta_t (W2c a - v)
@@ -118,11 +135,18 @@ __global__ __launch_bounds__(kThreads) void mlp_generic_kernel(MlpArgs a, float*
         float o = 0.0f;
         for (int c = 0; c < h; ++c) o += Ab[t * h + c] * W2c[static_cast<size_t>(i) * h + c];
         const float rate = t < n ? (etok ? eta * etok[s0 + t] : eta) : 0.0f;
-        const float err = a.dot_loss ? -Vs[e] : o - Vs[e];  // dl/df: f - v or -v
+        float err;  // dl/d(W2 a): f - v or -v, through the layer norm with kPaper
+        if constexpr (kPaper) {
+          const LnRow st = ln_row<D>(o, a.ln_eps);
+          const float f = Ks[e] + gam * st.xh + bet;
+          err = ln_row_vjp<D>(st, gam, a.dot_loss ? -Vs[e] : f - Vs[e]);
+        } else {
+          err = a.dot_loss ? -Vs[e] : o - Vs[e];
+        }
         Rs[e] = t < n ? rate * err : 0.0f;
       }
       __syncthreads();
-      // backward to the hidden pre-activation: du = (W2c^T r) * SiLU'(u)
+      // backward to the hidden pre-activation: du = (W2c^T r) * act'(u)
       for (int e = tid; e < kSub * h; e += kThreads) {
         const int t = e / h, c = e % h;
         float g = 0.0f;
@@ -147,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void mlp_generic_kernel(MlpArgs a, float*
           for (int j = 0; j < D; ++j) u += Qs[t * D + j] * W1n[static_cast<size_t>(c) * D + j];
           float corr = 0.0f;
           for (int s = 0; s <= t && s < kSub; ++s) corr += Ps[t * kSub + s] * DU[s * h + c];
-          AQ[e] = t < n ? silu_(u - corr) : 0.0f;
+          AQ[e] = t < n ? act_<kPaper>(u - corr) : 0.0f;
         }
         __syncthreads();
         for (int e = tid; e < kSub * kSub; e += kThreads) {
@@ -160,12 +184,13 @@ __global__ __launch_bounds__(kThreads) void mlp_generic_kernel(MlpArgs a, float*
         __syncthreads();
         for (int e = tid; e < kSub * D; e += kThreads) {
           const int t = e / D, i = e % D;
-          if (t >= n) continue;
           float o = 0.0f;
           for (int c = 0; c < h; ++c) o += AQ[t * h + c] * W2n[static_cast<size_t>(i) * h + c];
           float corr = 0.0f;
           for (int s = 0; s <= t; ++s) corr += P2[t * kSub + s] * Rs[s * D + i];
-          z[static_cast<size_t>(s0 + t) * D + i] = from_f32<IO>(o - corr);
+          float zt = o - corr;
+          if constexpr (kPaper) zt = Qs[e] + gam * ln_row<D>(zt, a.ln_eps).xh + bet;
+          if (t < n) z[static_cast<size_t>(s0 + t) * D + i] = from_f32<IO>(zt);
         }
         __syncthreads();
       }
@@ -203,15 +228,15 @@ __global__ __launch_bounds__(kThreads) void mlp_generic_kernel(MlpArgs a, float*
         const int t = e / h, c = e % h;
         float u = 0.0f;
         for (int j = 0; j < D; ++j) u += Qs[t * D + j] * W1n[static_cast<size_t>(c) * D + j];
-        AQ[e] = silu_(u);
+        AQ[e] = act_<kPaper>(u);
       }
       __syncthreads();
       for (int e = tid; e < kSub * D; e += kThreads) {
         const int t = e / D, i = e % D;
-        if (t >= n) continue;
         float o = 0.0f;
         for (int c = 0; c < h; ++c) o += AQ[t * h + c] * W2n[static_cast<size_t>(i) * h + c];
-        z[static_cast<size_t>(s0 + t) * D + i] = from_f32<IO>(o);
+        if constexpr (kPaper) o = Qs[e] + gam * ln_row<D>(o, a.ln_eps).xh + bet;
+        if (t < n) z[static_cast<size_t>(s0 + t) * D + i] = from_f32<IO>(o);
       }
       __syncthreads();
     }
@@ -227,25 +252,25 @@ __global__ __launch_bounds__(kThreads) void mlp_generic_kernel(MlpArgs a, float*
   }
 }
 
-template <typename IO, int D>
+template <typename IO, int D, bool kPaper>
 hipError_t launch_one(const MlpArgs& a, float* ws, hipStream_t s) {
   const size_t lds = MlpLds<D>::total(a.dh) * sizeof(float);
   if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&mlp_generic_kernel<IO, D>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&mlp_generic_kernel<IO, D, kPaper>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((mlp_generic_kernel<IO, D>), dim3(a.B * a.H), dim3(kThreads), lds, s, a, ws);
+  hipLaunchKernelGGL((mlp_generic_kernel<IO, D, kPaper>), dim3(a.B * a.H), dim3(kThreads), lds, s, a, ws);
   return hipGetLastError();
 }
 
-template <typename IO>
+template <typename IO, bool kPaper>
 hipError_t launch_d(const MlpArgs& a, float* ws, hipStream_t s) {
   switch (a.d) {
-    case 16: return launch_one<IO, 16>(a, ws, s);
-    case 32: return launch_one<IO, 32>(a, ws, s);
-    case 64: return launch_one<IO, 64>(a, ws, s);
+    case 16: return launch_one<IO, 16, kPaper>(a, ws, s);
+    case 32: return launch_one<IO, 32, kPaper>(a, ws, s);
+    case 64: return launch_one<IO, 64, kPaper>(a, ws, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -257,7 +282,8 @@ size_t mlp_generic_workspace_floats(const MlpArgs& a) {
 }
 
 hipError_t launch_mlp_generic(const MlpArgs& a, bool bf16_io, float* ws, hipStream_t s) {
-  return bf16_io ? launch_d<bf16>(a, ws, s) : launch_d<float>(a, ws, s);
+  if (a.ln_w) return bf16_io ? launch_d<bf16, true>(a, ws, s) : launch_d<float, true>(a, ws, s);
+  return bf16_io ? launch_d<bf16, false>(a, ws, s) : launch_d<float, false>(a, ws, s);
 }
 
 }  // namespace ttt

@@ -490,7 +490,7 @@ bool mlp_nc_supported(const MlpArgs& a, bool bf16_io) {
                        (a.w1_out == nullptr || al(a.w1_out, 16)) &&
                        (a.w2_out == nullptr || al(a.w2_out, 16));
   const bool fits = static_cast<long long>(a.T) * kD * 2 + 2LL * kTileBytes < 0x7fffffffLL;
-  return bf16_io && a.d == kD && a.dh == kH && a.causal == 0 && a.T > 0 && a.epochs >= 1 &&
+  return bf16_io && a.d == kD && a.dh == kH && a.causal == 0 && a.T > 0 && a.epochs >= 1 && a.ln_w == nullptr &&
          aligned && fits && (a.eta_tok == nullptr || al(a.eta_tok, 4));
 }
 

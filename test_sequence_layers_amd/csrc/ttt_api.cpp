@@ -95,47 +95,107 @@ int copy_state(float* dst, const float* src, long long batch_stride, int B, int 
   return TTT_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int ttt_abi_version(void) { return 4; }
-
-const char* ttt_last_error(void) { return g_last_error.c_str(); }
-
-int ttt_linear_fwd(const void* q, const void* k, const void* v, const float* w0,
-                   long long w0_batch_stride, void* z, float* w_out, int B, int H, int T,
-                   int d, int chunk, int causal, float eta, const float* eta_tok, int loss,
-                   int epochs, int io_dtype, ttt_stream_t stream) {
-  g_last_error.clear();
-  int rc = check_common("ttt_linear_fwd", q, k, v, z, B, H, T, d, eta, eta_tok, io_dtype);
+// Shared by ttt_linear_fwd (f(x) = W x, ln_w null) and ttt_linear_ln_fwd (x + LN(W x)).
+int linear_fwd(const char* fn, const void* q, const void* k, const void* v, const float* w0,
+               long long w0_batch_stride, const float* ln_w, const float* ln_b, float ln_eps,
+               void* z, float* w_out, int B, int H, int T, int d, int chunk, int causal,
+               float eta, const float* eta_tok, int loss, int epochs, int io_dtype,
+               ttt_stream_t stream) {
+  int rc = check_common(fn, q, k, v, z, B, H, T, d, eta, eta_tok, io_dtype);
   if (rc != TTT_OK) return rc;
   if (loss != TTT_LOSS_MSE && loss != TTT_LOSS_DOT)
-    return fail(TTT_E_INVALID, "ttt_linear_fwd: unknown loss %d", loss);
-  rc = check_epochs("ttt_linear_fwd", epochs, causal);
+    return fail(TTT_E_INVALID, "%s: unknown loss %d", fn, loss);
+  rc = check_epochs(fn, epochs, causal);
   if (rc != TTT_OK) return rc;
-  if (!w0) return fail(TTT_E_INVALID, "ttt_linear_fwd: w0 must be non-null");
-  if (chunk < 1) return fail(TTT_E_INVALID, "ttt_linear_fwd: chunk must be >= 1 (got %d)", chunk);
+  if (!w0) return fail(TTT_E_INVALID, "%s: w0 must be non-null", fn);
+  if (chunk < 1) return fail(TTT_E_INVALID, "%s: chunk must be >= 1 (got %d)", fn, chunk);
   if (causal != 0 && causal != 1)
-    return fail(TTT_E_INVALID, "ttt_linear_fwd: causal must be 0 or 1");
-  if (w0_batch_stride < 0) return fail(TTT_E_INVALID, "ttt_linear_fwd: negative w0_batch_stride");
+    return fail(TTT_E_INVALID, "%s: causal must be 0 or 1", fn);
+  if (w0_batch_stride < 0) return fail(TTT_E_INVALID, "%s: negative w0_batch_stride", fn);
   if (d != 16 && d != 32 && d != 64)
-    return fail(TTT_E_UNSUPPORTED, "ttt_linear_fwd: d=%d not supported (16, 32, 64)", d);
+    return fail(TTT_E_UNSUPPORTED, "%s: d=%d not supported (16, 32, 64)", fn, d);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (T == 0) return copy_state(w_out, w0, w0_batch_stride, B, H, static_cast<size_t>(d) * d, s);
 
   ttt::LinearArgs a{q, k, v, w0, w0_batch_stride, z, w_out, B, H, T, d, chunk, causal, eta, eta_tok,
                     loss == TTT_LOSS_DOT ? 1 : 0};
   a.epochs = epochs;
+  a.ln_w = ln_w;
+  a.ln_b = ln_b;
+  a.ln_eps = ln_eps;
   const bool bf16 = io_dtype == TTT_BF16;
   hipError_t e;
   if (ttt::linear_mfma_supported(a, bf16))
     e = ttt::launch_linear_mfma(a, s);
   else
     e = ttt::launch_linear_generic(a, bf16, s);
-  if (e != hipSuccess) return hip_fail(e, "ttt_linear_fwd launch");
+  if (e != hipSuccess) return fail(TTT_E_HIP, "%s launch: %s", fn, hipGetErrorString(e));
   return TTT_OK;
 }
+
+int check_ln(const char* fn, const float* ln_w, const float* ln_b, float ln_eps) {
+  if (!ln_w || !ln_b) return fail(TTT_E_INVALID, "%s: ln_weight and ln_bias must be non-null", fn);
+  if (!std::isfinite(ln_eps) || !(ln_eps > 0.0f))
+    return fail(TTT_E_INVALID, "%s: ln_eps must be finite and positive", fn);
+  return TTT_OK;
+}
+
+// Shared by ttt_mlp_fwd (W2 SiLU(W1 x), ln_w null) and ttt_mlp_ln_fwd (x + LN(W2 GELU(W1 x))).
+int mlp_fwd(const char* fn, const void* q, const void* k, const void* v, const float* w1,
+            const float* w2, long long w_batch_stride, const float* ln_w, const float* ln_b,
+            float ln_eps, void* z, float* w1_out, float* w2_out, int B, int H, int T, int d,
+            int dh, int chunk, int causal, float eta, const float* eta_tok, int loss, int epochs,
+            int io_dtype, ttt_stream_t stream) {
+  int rc = check_common(fn, q, k, v, z, B, H, T, d, eta, eta_tok, io_dtype);
+  if (rc != TTT_OK) return rc;
+  if (loss != TTT_LOSS_MSE && loss != TTT_LOSS_DOT)
+    return fail(TTT_E_INVALID, "%s: unknown loss %d", fn, loss);
+  rc = check_epochs(fn, epochs, causal);
+  if (rc != TTT_OK) return rc;
+  if (!w1 || !w2) return fail(TTT_E_INVALID, "%s: w1 and w2 must be non-null", fn);
+  if (dh <= 0) return fail(TTT_E_INVALID, "%s: dh must be positive (got %d)", fn, dh);
+  if (chunk < 1) return fail(TTT_E_INVALID, "%s: chunk must be >= 1 (got %d)", fn, chunk);
+  if (causal != 0 && causal != 1) return fail(TTT_E_INVALID, "%s: causal must be 0 or 1", fn);
+  if (w_batch_stride < 0) return fail(TTT_E_INVALID, "%s: negative w_batch_stride", fn);
+  if (d != 16 && d != 32 && d != 64)
+    return fail(TTT_E_UNSUPPORTED, "%s: d=%d not supported (16, 32, 64)", fn, d);
+  if (dh > 512) return fail(TTT_E_UNSUPPORTED, "%s: dh=%d not supported (<= 512)", fn, dh);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t per = static_cast<size_t>(d) * dh;
+  if (T == 0) {
+    rc = copy_state(w1_out, w1, w_batch_stride, B, H, per, s);
+    if (rc != TTT_OK) return rc;
+    return copy_state(w2_out, w2, w_batch_stride, B, H, per, s);
+  }
+  ttt::MlpArgs a{q, k, v, w1, w2, w_batch_stride, z, w1_out, w2_out,
+                 B, H, T, d, dh, chunk, causal, eta, eta_tok, loss == TTT_LOSS_DOT ? 1 : 0};
+  a.epochs = epochs;
+  a.ln_w = ln_w;
+  a.ln_b = ln_b;
+  a.ln_eps = ln_eps;
+  const bool bf16 = io_dtype == TTT_BF16;
+  hipError_t e;
+  StreamBuffer ws;
+  if (ttt::mlp_fast_supported(a, bf16)) {
+    e = ttt::launch_mlp_fast(a, s);
+  } else if (ttt::mlp_nc_supported(a, bf16)) {
+    e = ttt::launch_mlp_nc(a, s);
+  } else {
+    rc = get_workspace(ttt::mlp_generic_workspace_floats(a) * sizeof(float), s, &ws);
+    if (rc != TTT_OK) return rc;
+    e = ttt::launch_mlp_generic(a, bf16, static_cast<float*>(ws.ptr), s);
+  }
+  if (e != hipSuccess) return fail(TTT_E_HIP, "%s launch: %s", fn, hipGetErrorString(e));
+  return TTT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ttt_abi_version(void) { return 5; }
+
+const char* ttt_last_error(void) { return g_last_error.c_str(); }
 
 int delta_rule_fwd(const void* q, const void* k, const void* v, const float* w0,
                    long long w0_batch_stride, void* z, float* w_out, int B, int H, int T,
@@ -205,49 +265,49 @@ int ttt_linear_bwd(const void* q, const void* k, const void* v, const float* w0,
   return TTT_OK;
 }
 
+int ttt_linear_fwd(const void* q, const void* k, const void* v, const float* w0,
+                   long long w0_batch_stride, void* z, float* w_out, int B, int H, int T,
+                   int d, int chunk, int causal, float eta, const float* eta_tok, int loss,
+                   int epochs, int io_dtype, ttt_stream_t stream) {
+  g_last_error.clear();
+  return linear_fwd("ttt_linear_fwd", q, k, v, w0, w0_batch_stride, nullptr, nullptr, 0.0f, z,
+                    w_out, B, H, T, d, chunk, causal, eta, eta_tok, loss, epochs, io_dtype, stream);
+}
+
+int ttt_linear_ln_fwd(const void* q, const void* k, const void* v, const float* w0,
+                      long long w0_batch_stride, const float* ln_weight, const float* ln_bias,
+                      float ln_eps, void* z, float* w_out, int B, int H, int T, int d, int chunk,
+                      int causal, float eta, const float* eta_tok, int loss, int epochs,
+                      int io_dtype, ttt_stream_t stream) {
+  g_last_error.clear();
+  const int rc = check_ln("ttt_linear_ln_fwd", ln_weight, ln_bias, ln_eps);
+  if (rc != TTT_OK) return rc;
+  return linear_fwd("ttt_linear_ln_fwd", q, k, v, w0, w0_batch_stride, ln_weight, ln_bias, ln_eps,
+                    z, w_out, B, H, T, d, chunk, causal, eta, eta_tok, loss, epochs, io_dtype,
+                    stream);
+}
+
 int ttt_mlp_fwd(const void* q, const void* k, const void* v, const float* w1, const float* w2,
                 long long w_batch_stride, void* z, float* w1_out, float* w2_out, int B, int H,
                 int T, int d, int dh, int chunk, int causal, float eta, const float* eta_tok,
                 int loss, int epochs, int io_dtype, ttt_stream_t stream) {
   g_last_error.clear();
-  int rc = check_common("ttt_mlp_fwd", q, k, v, z, B, H, T, d, eta, eta_tok, io_dtype);
+  return mlp_fwd("ttt_mlp_fwd", q, k, v, w1, w2, w_batch_stride, nullptr, nullptr, 0.0f, z,
+                 w1_out, w2_out, B, H, T, d, dh, chunk, causal, eta, eta_tok, loss, epochs,
+                 io_dtype, stream);
+}
+
+int ttt_mlp_ln_fwd(const void* q, const void* k, const void* v, const float* w1, const float* w2,
+                   long long w_batch_stride, const float* ln_weight, const float* ln_bias,
+                   float ln_eps, void* z, float* w1_out, float* w2_out, int B, int H, int T,
+                   int d, int dh, int chunk, int causal, float eta, const float* eta_tok,
+                   int loss, int epochs, int io_dtype, ttt_stream_t stream) {
+  g_last_error.clear();
+  const int rc = check_ln("ttt_mlp_ln_fwd", ln_weight, ln_bias, ln_eps);
   if (rc != TTT_OK) return rc;
-  if (loss != TTT_LOSS_MSE && loss != TTT_LOSS_DOT)
-    return fail(TTT_E_INVALID, "ttt_mlp_fwd: unknown loss %d", loss);
-  rc = check_epochs("ttt_mlp_fwd", epochs, causal);
-  if (rc != TTT_OK) return rc;
-  if (!w1 || !w2) return fail(TTT_E_INVALID, "ttt_mlp_fwd: w1 and w2 must be non-null");
-  if (dh <= 0) return fail(TTT_E_INVALID, "ttt_mlp_fwd: dh must be positive (got %d)", dh);
-  if (chunk < 1) return fail(TTT_E_INVALID, "ttt_mlp_fwd: chunk must be >= 1 (got %d)", chunk);
-  if (causal != 0 && causal != 1) return fail(TTT_E_INVALID, "ttt_mlp_fwd: causal must be 0 or 1");
-  if (w_batch_stride < 0) return fail(TTT_E_INVALID, "ttt_mlp_fwd: negative w_batch_stride");
-  if (d != 16 && d != 32 && d != 64)
-    return fail(TTT_E_UNSUPPORTED, "ttt_mlp_fwd: d=%d not supported (16, 32, 64)", d);
-  if (dh > 512) return fail(TTT_E_UNSUPPORTED, "ttt_mlp_fwd: dh=%d not supported (<= 512)", dh);
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const size_t per = static_cast<size_t>(d) * dh;
-  if (T == 0) {
-    rc = copy_state(w1_out, w1, w_batch_stride, B, H, per, s);
-    if (rc != TTT_OK) return rc;
-    return copy_state(w2_out, w2, w_batch_stride, B, H, per, s);
-  }
-  ttt::MlpArgs a{q, k, v, w1, w2, w_batch_stride, z, w1_out, w2_out,
-                 B, H, T, d, dh, chunk, causal, eta, eta_tok, loss == TTT_LOSS_DOT ? 1 : 0};
-  a.epochs = epochs;
-  const bool bf16 = io_dtype == TTT_BF16;
-  hipError_t e;
-  StreamBuffer ws;
-  if (ttt::mlp_fast_supported(a, bf16)) {
-    e = ttt::launch_mlp_fast(a, s);
-  } else if (ttt::mlp_nc_supported(a, bf16)) {
-    e = ttt::launch_mlp_nc(a, s);
-  } else {
-    rc = get_workspace(ttt::mlp_generic_workspace_floats(a) * sizeof(float), s, &ws);
-    if (rc != TTT_OK) return rc;
-    e = ttt::launch_mlp_generic(a, bf16, static_cast<float*>(ws.ptr), s);
-  }
-  if (e != hipSuccess) return hip_fail(e, "ttt_mlp_fwd launch");
-  return TTT_OK;
+  return mlp_fwd("ttt_mlp_ln_fwd", q, k, v, w1, w2, w_batch_stride, ln_weight, ln_bias, ln_eps,
+                 z, w1_out, w2_out, B, H, T, d, dh, chunk, causal, eta, eta_tok, loss, epochs,
+                 io_dtype, stream);
 }
 
 }  // extern "C"

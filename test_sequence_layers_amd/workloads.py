@@ -137,3 +137,12 @@ def make_token_rates(w: Workload, seed: int, lo: float = 0.0, hi: float = 1.0) -
     sigmoid gate.  A separate stream, so the workload's other inputs are unchanged."""
     rng = np.random.default_rng(10_000 + seed)
     return rng.uniform(lo, hi, size=(w.B, w.H, w.T)).astype(np.float32)
+
+
+def make_ln_params(w: Workload, seed: int) -> tuple:
+    """Seeded per-head layer-norm gain and bias, float32 [H, d] each: gain 1 + 0.1 N(0, 1),
+    bias 0.1 N(0, 1) (near their usual initial values 1 and 0).  A separate stream."""
+    rng = np.random.default_rng(20_000 + seed)
+    gain = (1.0 + 0.1 * rng.standard_normal((w.H, w.d))).astype(np.float32)
+    bias = (0.1 * rng.standard_normal((w.H, w.d))).astype(np.float32)
+    return gain, bias

@@ -26,9 +26,10 @@ def lib():
     return ttt.load_library()
 
 
-def test_header_declares_the_three_entry_points():
+def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for n in ("ttt_linear_fwd", "ttt_mlp_fwd", "delta_rule_fwd", "ttt_linear_bwd", "ttt_last_error"):
+    for n in ("ttt_linear_fwd", "ttt_mlp_fwd", "delta_rule_fwd", "ttt_linear_bwd",
+              "ttt_linear_ln_fwd", "ttt_mlp_ln_fwd", "ttt_last_error", "ttt_abi_version"):
         assert n in names
 
 
@@ -39,7 +40,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ttt_abi_version() == 4
+    assert lib.ttt_abi_version() == 5
 
 
 FAKE = 0x1000  # never dereferenced: validation fails before any HIP call
@@ -155,6 +156,46 @@ def _bwd(lib, **kw):
 def test_linear_bwd_rejects(lib, kw, code, msg):
     assert _bwd(lib, **kw) == code
     assert msg in ttt.last_error()
+
+
+def _linear_ln(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, w0=FAKE, stride=0, ln_w=FAKE, ln_b=FAKE, eps=1e-6, z=FAKE,
+             w_out=None, B=1, H=1, T=16, d=16, chunk=16, causal=1, eta=0.1, eta_tok=None, loss=0,
+             epochs=1, io=0)
+    a.update(kw)
+    return lib.ttt_linear_ln_fwd(a["q"], a["k"], a["v"], a["w0"], a["stride"], a["ln_w"],
+                                 a["ln_b"], a["eps"], a["z"], a["w_out"], a["B"], a["H"], a["T"],
+                                 a["d"], a["chunk"], a["causal"], a["eta"], a["eta_tok"],
+                                 a["loss"], a["epochs"], a["io"], None)
+
+
+def _mlp_ln(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, w1=FAKE, w2=FAKE, stride=0, ln_w=FAKE, ln_b=FAKE, eps=1e-6,
+             z=FAKE, B=1, H=1, T=16, d=16, dh=64, chunk=16, causal=1, eta=0.1, eta_tok=None,
+             loss=0, epochs=1, io=0)
+    a.update(kw)
+    return lib.ttt_mlp_ln_fwd(a["q"], a["k"], a["v"], a["w1"], a["w2"], a["stride"], a["ln_w"],
+                              a["ln_b"], a["eps"], a["z"], None, None, a["B"], a["H"], a["T"],
+                              a["d"], a["dh"], a["chunk"], a["causal"], a["eta"], a["eta_tok"],
+                              a["loss"], a["epochs"], a["io"], None)
+
+
+@pytest.mark.parametrize("fn", [_linear_ln, _mlp_ln])
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(ln_w=None), ttt.TTT_E_INVALID, "ln_weight"),
+    (dict(ln_b=None), ttt.TTT_E_INVALID, "ln_bias"),
+    (dict(eps=0.0), ttt.TTT_E_INVALID, "ln_eps"),
+    (dict(eps=-1e-5), ttt.TTT_E_INVALID, "ln_eps"),
+    (dict(eps=float("nan")), ttt.TTT_E_INVALID, "ln_eps"),
+    (dict(q=None), ttt.TTT_E_INVALID, "non-null"),
+    (dict(d=48), ttt.TTT_E_UNSUPPORTED, "d=48"),
+    (dict(epochs=2), ttt.TTT_E_INVALID, "causal = 0"),
+    (dict(loss=5), ttt.TTT_E_INVALID, "loss"),
+])
+def test_paper_models_reject(lib, fn, kw, code, msg):
+    assert fn(lib, **kw) == code
+    assert msg in ttt.last_error()
+    assert ("ttt_linear_ln_fwd" if fn is _linear_ln else "ttt_mlp_ln_fwd") in ttt.last_error()
 
 
 def test_error_text_is_per_call(lib):

@@ -8,7 +8,8 @@ import numpy as np
 import pytest
 import sys
 
-from tests.parity_util import (BF16_TOL, FP32_TOL, make_inputs, make_token_rates, run_gpu,
+from tests.parity_util import (BF16_TOL, FP32_TOL, make_inputs, make_ln_params, make_token_rates,
+                               run_gpu,
                                run_oracle, slab_rel, to_device, to_np, tol_for, workload)
 
 pytestmark = pytest.mark.gpu
@@ -22,7 +23,7 @@ def _note(msg):
 def _check(kind, w, inp, sel=None, state_tol=None, loss="mse", epochs=1):
     _note(f"[parity] {kind} {w.name} B={w.B} H={w.H} T={w.T} d={w.d} h={w.h} chunk={w.chunk} "
           f"causal={w.causal} io={w.io} seed={w.seed} loss={loss} rates={'eta_tok' in inp} "
-          f"epochs={epochs}")
+          f"epochs={epochs} paper_ln={'ln_w' in inp}")
     dev = to_device(inp, w.io)
     out = run_gpu(kind, dev, w.eta, w.chunk, w.causal, loss=loss, epochs=epochs)
     import torch
@@ -312,6 +313,76 @@ def test_epochs_linear(d, chunk, epochs, io):
     w = workload(0).replace(B=2, H=3, T=196, d=d, chunk=chunk, causal=False, init="normal",
                             eta=0.1, io=io, seed=230 + d)
     _check("linear", w, make_inputs(w), epochs=epochs)
+
+
+# ------------------------------------------------------------------ the paper's inner models
+# f(x) = x + LN(f_res(x)), f_res = W x or W2 GELU(W1 x) (wmrh.cn summary, section 2.2.1):
+# ttt_linear_ln_fwd / ttt_mlp_ln_fwd against the oracle's ln / act="gelu"
+
+def _with_ln(w, seed, rates_seed=None):
+    inp = make_inputs(w)
+    inp["ln_w"], inp["ln_b"] = make_ln_params(w, seed)
+    if rates_seed is not None:
+        inp["eta_tok"] = make_token_rates(w, rates_seed)
+    return inp
+
+
+@pytest.mark.parametrize("d", [16, 32, 64])
+@pytest.mark.parametrize("chunk,causal", [(1, True), (5, True), (16, True), (77, False)])
+def test_paper_linear_fp32(d, chunk, causal):
+    w = workload(0).replace(B=2, H=3, T=77, d=d, chunk=chunk, causal=causal, init="normal",
+                            eta=0.2, seed=300 + d + chunk)
+    _check("linear", w, _with_ln(w, 1))
+
+
+@pytest.mark.parametrize("T,rates,loss", [(16, False, "mse"), (200, False, "mse"),
+                                          (333, True, "mse"), (200, False, "dot")])
+def test_paper_linear_bf16_d64_chunk16(T, rates, loss):
+    w = workload(1).replace(B=2, H=3, T=T, seed=310 + T)
+    _check("linear", w, _with_ln(w, 2, 13 if rates else None), loss=loss)
+
+
+def test_paper_linear_noncausal_epochs():
+    w = workload(1).replace(B=2, H=3, T=196, chunk=49, causal=False, seed=320)
+    _check("linear", w, _with_ln(w, 3), epochs=2)
+
+
+def test_paper_linear_config_full_size_sampled():
+    w = workload(1)
+    _check("linear", w, _with_ln(w, 4), sel=[(0, 0), (7, 11)])
+
+
+@pytest.mark.parametrize("chunk,causal", [(1, True), (4, True), (16, True), (37, False),
+                                          (10, False)])
+def test_paper_mlp_fp32(chunk, causal):
+    w = workload(3).replace(B=2, H=2, T=37, d=16, h=64, chunk=chunk, causal=causal, io="f32",
+                            seed=330 + chunk)
+    inp = _with_ln(w, 5)
+    if chunk == 1:
+        # With N(0, 0.02^2) initial weights the spread of the LN input (about 1.5e-3) is of
+        # the order of sqrt(eps), and one-token steps then amplify a 1e-7 perturbation of the
+        # inputs about 300x in the float64 oracle itself; ten times larger initial weights
+        # keep the same path well conditioned (chunks 4 and 16 agree to ~2e-7 either way).
+        inp["w1"], inp["w2"] = inp["w1"] * 10, inp["w2"] * 10
+    _check("mlp", w, inp)
+
+
+@pytest.mark.parametrize("T,rates,loss", [(100, False, "mse"), (70, True, "mse"),
+                                          (70, False, "dot")])
+def test_paper_mlp_bf16_h256(T, rates, loss):
+    # the paper's TTT-MLP: hidden 4 d = 256, GELU, LN + residual, mini-batch 16
+    w = workload(3).replace(B=2, H=2, T=T, seed=340 + T)
+    _check("mlp", w, _with_ln(w, 6, 14 if rates else None), loss=loss)
+
+
+def test_paper_mlp_vision_noncausal_epochs():
+    w = workload(4).replace(B=2, H=3, chunk=98, unit_keys=True, eta=0.1, seed=350)
+    _check("mlp", w, _with_ln(w, 7), epochs=2)
+
+
+def test_paper_mlp_config_full_size_sampled():
+    w = workload(3)
+    _check("mlp", w, _with_ln(w, 8), sel=[(0, 0), (6, 10)])
 
 
 # ------------------------------------------------------------------ backward pass
