@@ -16,6 +16,13 @@
 //   Z   = A_q W2^T - eta tril(A_q A^T) R.
 // This equals the per-token recurrence up to floating-point order.
 //
+// kPaper: the paper's TTT-MLP (wmrh.cn summary, section 2.2.1), f(x) = x + LN(W2 GELU(W1 x))
+// with per-head LN gain and bias.  GELU (u Phi(u), exact) replaces SiLU; the state still
+// changes only through R = dl/d(A W2^T), which is now the error k + LN(O) - v (or -v) passed
+// back through the layer norm of each token's row of O; and Z = q + LN(Z_pre) with Z_pre
+// the dual-form output above.  Both reductions already give a token's 64 outputs to 32
+// consecutive lanes (two each), so the LN statistics are 32-lane shuffle sums there.
+//
 // Mapping.  One workgroup of 8 waves per (batch, head) chain, two per SIMD so that one
 // wave's dependency stalls are filled by the other's work.  Wave w owns hidden units
 // 32w .. 32w+31: its rows of W1 and columns of W2 live in its registers as fp32 MFMA
@@ -124,6 +131,7 @@ struct ChunkIn {
   u32x4 qb0, qb1;     // Q[n][16 g + 0..15]                          (B operands over j)
   uint32_t kt[4][2];  // kt[e][h] = K[4 g + e][c0 + 8 h .. + 1], c0 = 16 (n / 4) + 2 (n % 4)
   uint32_t vv;        // V[t = tid / 32][2 (tid % 32) .. + 1]         (for R = O - V)
+  uint32_t kv, qv;    // K and Q at the same place (residual of the LN model only)
   float et;           // rate factor of token tid / 32 (1 without per-token rates)
 };
 
@@ -134,6 +142,7 @@ struct Offsets {
   int et;          // (tid / 32) * 4
 };
 
+template <bool kPaper>
 __device__ __forceinline__ void load_chunk(ChunkIn& r, const char* q, const char* k, const char* v,
                                            const float* etok, int c, int seq_bytes, const Offsets& o) {
   const int off = c * kTileBytes;
@@ -150,6 +159,8 @@ __device__ __forceinline__ void load_chunk(ChunkIn& r, const char* q, const char
     r.kt[e][1] = __builtin_amdgcn_raw_buffer_load_b32(rk, o.kt[e] + 16, 0, 0);
   }
   r.vv = __builtin_amdgcn_raw_buffer_load_b32(rv, o.vv, 0, 0);
+  r.kv = kPaper ? __builtin_amdgcn_raw_buffer_load_b32(rk, o.vv, 0, 0) : 0u;
+  r.qv = kPaper ? __builtin_amdgcn_raw_buffer_load_b32(rq, o.vv, 0, 0) : 0u;
   r.et = 1.0f;
   if (etok) {  // uniform: per-token rate factors of the chunk, 4 bytes per token
     const int eoff = c * kB * 4;
@@ -181,11 +192,96 @@ struct Lds {
   uint16_t rr[kB][kRRow];
   uint16_t rt[kD][kTRow];
   uint32_t w2b[kWaves][kD][8 * kHT];
+  float lnp[2][kD];  // the head's LN gain and bias (kPaper)
 };
 
 __device__ __forceinline__ void barrier() { __syncthreads(); }
 
-template <bool kDot>
+// Phi(u), the standard normal CDF, and exp(-u^2 / 2), branch-free: erfc(x) for x >= 0 by
+// Abramowitz and Stegun, Handbook of Mathematical Functions, formula 7.1.26
+// (t = 1 / (1 + p x), erfc(x) = (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) e^{-x^2},
+// |error| <= 1.5e-7) at x = |u| / sqrt 2, whose e^{-x^2} is the exp(-u^2 / 2) that the
+// derivative of GELU needs as well.  Largest errors over [-12, 12] in float32: 3e-7 for Phi,
+// 4e-7 for GELU and its derivative (far below the bf16 rounding of the operands).
+__device__ __forceinline__ float phi_cdf(float u, float& ex) {
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f * 0.70710678118654752f, fabsf(u), 1.0f));
+  float poly = __builtin_fmaf(t, 1.061405429f, -1.453152027f);
+  poly = __builtin_fmaf(t, poly, 1.421413741f);
+  poly = __builtin_fmaf(t, poly, -0.284496736f);
+  poly = __builtin_fmaf(t, poly, 0.254829592f);
+  ex = __expf(-0.5f * u * u);
+  const float half_erfc = 0.5f * t * poly * ex;  // (1 - erf(|u| / sqrt 2)) / 2
+  return u >= 0.0f ? 1.0f - half_erfc : half_erfc;
+}
+
+// the inner activation and its derivative: SiLU (u sigma(u)), or GELU (u Phi(u)) for kPaper
+template <bool kPaper>
+__device__ __forceinline__ void act_grad(float u, float& act, float& der) {
+  if constexpr (kPaper) {
+    float ex;
+    const float ph = phi_cdf(u, ex);
+    act = u * ph;
+    der = __builtin_fmaf(u * 0.39894228040143268f, ex, ph);  // Phi(u) + u phi(u)
+  } else {
+    const float sg = sigmoid_f(u);
+    act = u * sg;
+    der = __builtin_fmaf(act, 1.0f - sg, sg);  // sg (1 + u (1 - sg))
+  }
+}
+template <bool kPaper>
+__device__ __forceinline__ float act_only(float u) {
+  if constexpr (kPaper) {
+    float ex;
+    return u * phi_cdf(u, ex);
+  }
+  return u * sigmoid_f(u);
+}
+
+// Two sums over aligned groups of 32 lanes at once (every lane of the wave takes part).
+// Within each row of 16 lanes: offsets 1 and 2 by DPP quad permutations, 4 and 8 by the DPP
+// half-row and row mirrors (lane i with 7 - i, then with 15 - i: each pairs lanes holding
+// disjoint partial sums), after which every lane of a row holds the row's sum; the two rows
+// of a 32-lane group are then added from v_readlane of lanes 0, 16, 32 and 48.  Every lane
+// of a group ends with the same bits.
+typedef float float2_t __attribute__((ext_vector_type(2)));
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp<0x141>(x);  // row_half_mirror
+  x += dpp<0x140>(x);  // row_mirror
+  return x;
+}
+__device__ __forceinline__ float lane_f(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+__device__ __forceinline__ float2_t sum32x2(float2_t x) {
+  const float a = row_sum16(x[0]), b = row_sum16(x[1]);
+  const float a_lo = lane_f(a, 0) + lane_f(a, 16), a_hi = lane_f(a, 32) + lane_f(a, 48);
+  const float b_lo = lane_f(b, 0) + lane_f(b, 16), b_hi = lane_f(b, 32) + lane_f(b, 48);
+  const bool upper = (threadIdx.x & 32) != 0;
+  return float2_t{upper ? a_hi : a_lo, upper ? b_hi : b_lo};
+}
+
+// Layer-norm statistics of a token's 64 outputs held two per lane by 32 consecutive lanes
+// (mean and mean square in one pass: E[y^2] - mean^2 costs the variance a relative error of
+// about 6e-8 (mean / std)^2 in fp32, below the bf16 resolution of the outputs unless the
+// mean exceeds ~250 standard deviations)
+struct Ln2 {
+  float2_t xh;
+  float rstd;
+};
+__device__ __forceinline__ Ln2 ln2_row(float2_t y, float eps) {
+  const float2_t m = sum32x2(float2_t{y[0] + y[1], y[0] * y[0] + y[1] * y[1]}) * (1.0f / kD);
+  const float var = fmaxf(m[1] - m[0] * m[0], 0.0f);
+  const float rstd = 1.0f / sqrtf(var + eps);
+  return {(y - m[0]) * rstd, rstd};
+}
+
+template <bool kDot, bool kPaper>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void mlp_mfma_kernel(
     MlpArgs a) {
   __shared__ __attribute__((aligned(16))) Lds sh;
@@ -218,6 +314,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const float* w1g = a.w1 + bi * a.w_batch_stride + static_cast<long long>(hi) * hd;
   const float* w2g = a.w2 + bi * a.w_batch_stride + static_cast<long long>(hi) * hd;
   const int h0 = 16 * kHT * wv;  // first hidden unit of this wave
+  // the head's LN gain and bias into LDS (read by the reductions, after the first barrier)
+  if (kPaper && tid < 2 * kD) sh.lnp[tid / kD][tid % kD] = (tid < kD ? a.ln_w : a.ln_b)[hi * kD + tid % kD];
 
   // ---- initial state ----
   State st;
@@ -258,8 +356,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   o.vv = rt * 128 + 2 * ri;
   o.et = rt * 4;
   const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-  typedef float float2_t __attribute__((ext_vector_type(2)));
   const float2_t zero2 = {0.0f, 0.0f};
+  uint32_t qv_prev = 0u;  // Q of the previous chunk at this thread's outputs (kPaper)
   constexpr uint32_t kLo = 0x05040100u, kHi = 0x07060302u;
 
   // Z of the previous chunk: reduce the per-wave partial sums and store (thread: row rt,
@@ -268,6 +366,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     float2_t s2 = zero2;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) s2 += lds_load<float2_t>(zpart, ((w * kB + rt) * kRow + ri) * 4);
+    if constexpr (kPaper) {  // z = q + LN(z_pre)
+      const float2_t lng = *reinterpret_cast<const float2_t*>(&sh.lnp[0][ri]);
+      const float2_t lnb = *reinterpret_cast<const float2_t*>(&sh.lnp[1][ri]);
+      const Ln2 st2 = ln2_row(s2, a.ln_eps);
+      s2 = float2_t{__builtin_bit_cast(float, qv_prev << 16), __builtin_bit_cast(float, qv_prev & 0xFFFF0000u)} +
+           lng * st2.xh + lnb;
+    }
     const int off = c * kTileBytes;
     __builtin_amdgcn_raw_buffer_store_b32(pack_bf16(s2[0], s2[1]), chunk_rsrc(z + off, seq_bytes - off),
                                           o.vv, 0, 0);
@@ -275,7 +380,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   // One chunk: its operands in cur, the next chunk's loaded into nxt.
   auto step = [&](const ChunkIn& cur, ChunkIn& nxt, int c) {
-    load_chunk(nxt, q, k, v, etok, c + 1, seq_bytes, o);  // prefetch (zeros past the end)
+    load_chunk<kPaper>(nxt, q, k, v, etok, c + 1, seq_bytes, o);  // prefetch (zeros past the end)
     const bf16x8_t ka0 = bf(cur.ka0), ka1 = bf(cur.ka1), qb0 = bf(cur.qb0), qb1 = bf(cur.qb1);
 
     // bf16 copies of this wave's chunk-start state
@@ -285,7 +390,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
       for (int aa = 0; aa < kHT; ++aa) w1b[h][aa] = pair_op(st.w1t[2 * h][aa], st.w1t[2 * h + 1][aa]);
 
-    // U = K W1^T (rows t, hidden tile aa);  A = SiLU(U), S = SiLU'(U)
+    // U = K W1^T (rows t, hidden tile aa);  A = act(U), S = act'(U)
     float4_t act[kHT], sd[kHT];
 #pragma unroll
     for (int aa = 0; aa < kHT; ++aa) {
@@ -293,9 +398,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       u = mfma(ka1, w1b[1][aa], u);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float sg = sigmoid_f(u[e]);
-        act[aa][e] = u[e] * sg;
-        sd[aa][e] = __builtin_fmaf(act[aa][e], 1.0f - sg, sg);  // sg (1 + u (1 - sg))
+        float av, dv;
+        act_grad<kPaper>(u[e], av, dv);
+        act[aa][e] = av;
+        sd[aa][e] = dv;
       }
     }
     // A as padded K = 16 operands (rows t); A^T (rows hidden) by an MFMA with I
@@ -319,9 +425,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       lds_store<u32x2>(w2lds, w2off(row, 4 + g), u32x2{w2op[it].z, w2op[it].w});
     }
     // O^T partial = W2 A^T (rows output, cols t): contraction over this wave's 32 hidden
-    // (not needed with the dot-product loss, whose error term is -V)
+    // (not needed with the dot-product loss, whose error term is -V, unless a layer norm
+    // follows: its backward needs O)
     const bf16x8_t atb = cat_op(actT[0], actT[1]);  // B operand over hidden
-    if (!kDot) {
+    if (!kDot || kPaper) {
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
         const float4_t ot = mfma(bf(w2op[it]), atb, zero);
@@ -334,14 +441,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // -eta_t R = -eta_t (sum of partials - V), to LDS in bf16 as [t][i] and [i][t]
     {
       float2_t s2 = zero2;
-      if (!kDot) {
+      if (!kDot || kPaper) {
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) s2 += lds_load<float2_t>(opart, ((w * kB + rt) * kRow + ri) * 4);
       }
       const uint32_t vb = cur.vv;
+      const float2_t vr = {__builtin_bit_cast(float, vb << 16), __builtin_bit_cast(float, vb & 0xFFFF0000u)};
+      float2_t r2;  // dl/dO of this thread's two outputs
+      if constexpr (kPaper) {
+        // f = k + LN(O); the error f - v (or -v) back through the layer norm
+        const float2_t lng = *reinterpret_cast<const float2_t*>(&sh.lnp[0][ri]);
+        const float2_t lnb = *reinterpret_cast<const float2_t*>(&sh.lnp[1][ri]);
+        const Ln2 st2 = ln2_row(s2, a.ln_eps);
+        const float2_t kr = {__builtin_bit_cast(float, cur.kv << 16),
+                             __builtin_bit_cast(float, cur.kv & 0xFFFF0000u)};
+        const float2_t err = kDot ? -vr : kr + lng * st2.xh + lnb - vr;
+        const float2_t gg = lng * err;
+        const float2_t m = sum32x2(float2_t{gg[0] + gg[1], gg[0] * st2.xh[0] + gg[1] * st2.xh[1]}) * (1.0f / kD);
+        r2 = st2.rstd * (gg - m[0] - st2.xh * m[1]);
+      } else {
+        r2 = s2 - vr;
+      }
       const float nrate = -eta * cur.et;
-      const uint32_t rp = pack_bf16((s2[0] - __builtin_bit_cast(float, vb << 16)) * nrate,
-                                    (s2[1] - __builtin_bit_cast(float, vb & 0xFFFF0000u)) * nrate);
+      const uint32_t rp = pack_bf16(r2[0] * nrate, r2[1] * nrate);
       lds_store<uint32_t>(rrb, (rt * kRRow + ri) * 2, rp);
       lds_store<uint16_t>(rtb, (ri * kTRow + rt) * 2, static_cast<uint16_t>(rp));
       lds_store<uint16_t>(rtb, ((ri + 1) * kTRow + rt) * 2, static_cast<uint16_t>(rp >> 16));
@@ -384,7 +506,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int e = 0; e < 4; ++e) pt[e] = keep[e] ? pt[e] : 0.0f;
     const bf16x8_t ptb = pad_op(pt);
-    // U_q^T = W1 Q^T - eta dU^T P^T (rows hidden tile aa, cols t);  A_q^T = SiLU(U_q^T)
+    // U_q^T = W1 Q^T - eta dU^T P^T (rows hidden tile aa, cols t);  A_q^T = act(U_q^T)
     float4_t aqT[kHT];
 #pragma unroll
     for (int aa = 0; aa < kHT; ++aa) {
@@ -392,7 +514,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       u = mfma(w1b[1][aa], qb1, u);
       u = mfma(dub[aa], ptb, u);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) u[e] = u[e] * sigmoid_f(u[e]);
+      for (int e = 0; e < 4; ++e) u[e] = act_only<kPaper>(u[e]);
       aqT[aa] = u;
     }
     const bf16x8_t aqb = cat_op(aqT[0], aqT[1]);
@@ -425,10 +547,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int aa = 0; aa < kHT; ++aa)
 #pragma unroll
       for (int it = 0; it < 4; ++it) st.w2t[aa][it] = mfma(ab[aa], rb[it], st.w2t[aa][it]);
+    qv_prev = cur.qv;
   };
 
   ChunkIn ca, cb;
-  load_chunk(ca, q, k, v, etok, 0, seq_bytes, o);
+  load_chunk<kPaper>(ca, q, k, v, etok, 0, seq_bytes, o);
   for (int c = 0; c < nchunks; ++c) {
     step(ca, cb, c);
     ca = cb;
@@ -472,17 +595,23 @@ bool mlp_fast_supported(const MlpArgs& a, bool bf16_io) {
                        (a.w1_out == nullptr || al(a.w1_out, 16)) &&
                        (a.w2_out == nullptr || al(a.w2_out, 16));
   const bool fits = static_cast<long long>(a.T) * kD * 2 + 4LL * kTileBytes < 0x7fffffffLL;
-  return bf16_io && a.d == kD && a.dh == kH && a.chunk == kB && a.causal == 1 && a.T > 0 && a.ln_w == nullptr &&
+  return bf16_io && a.d == kD && a.dh == kH && a.chunk == kB && a.causal == 1 && a.T > 0 &&
          aligned && fits && (a.eta_tok == nullptr || al(a.eta_tok, 4));
 }
 
 hipError_t launch_mlp_fast(const MlpArgs& a, hipStream_t s) {
   const long long nchains = static_cast<long long>(a.B) * a.H;
   if (nchains > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (a.dot_loss)
-    hipLaunchKernelGGL(mlp_mfma_kernel<true>, dim3(static_cast<unsigned>(nchains)), dim3(kThreads), 0, s, a);
+  const dim3 grid(static_cast<unsigned>(nchains)), block(kThreads);
+  const bool paper = a.ln_w != nullptr;  // the paper's TTT-MLP: GELU, LN and residual
+  if (paper && a.dot_loss)
+    hipLaunchKernelGGL((mlp_mfma_kernel<true, true>), grid, block, 0, s, a);
+  else if (paper)
+    hipLaunchKernelGGL((mlp_mfma_kernel<false, true>), grid, block, 0, s, a);
+  else if (a.dot_loss)
+    hipLaunchKernelGGL((mlp_mfma_kernel<true, false>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL(mlp_mfma_kernel<false>, dim3(static_cast<unsigned>(nchains)), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((mlp_mfma_kernel<false, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
