@@ -41,6 +41,7 @@ def _flags():
 # ordinary VGPRs (their values are read by vector instructions every chunk).
 EXTRA_FLAGS = {
     "linear_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "linear_ln_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

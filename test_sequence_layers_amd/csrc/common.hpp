@@ -133,6 +133,8 @@ size_t mlp_generic_workspace_floats(const MlpArgs& a);
 // which); everything else runs on the generic kernels.
 bool linear_mfma_supported(const LinearArgs& a, bool bf16_io);
 hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s);
+bool linear_ln_mfma_supported(const LinearArgs& a, bool bf16_io);
+hipError_t launch_linear_ln_mfma(const LinearArgs& a, hipStream_t s);
 bool delta_fast_supported(const LinearArgs& a, bool bf16_io);
 size_t delta_workspace_bytes(const LinearArgs& a);
 hipError_t launch_delta_fast(const LinearArgs& a, void* workspace, hipStream_t s);

@@ -127,6 +127,8 @@ int linear_fwd(const char* fn, const void* q, const void* k, const void* v, cons
   hipError_t e;
   if (ttt::linear_mfma_supported(a, bf16))
     e = ttt::launch_linear_mfma(a, s);
+  else if (ttt::linear_ln_mfma_supported(a, bf16))
+    e = ttt::launch_linear_ln_mfma(a, s);
   else
     e = ttt::launch_linear_generic(a, bf16, s);
   if (e != hipSuccess) return fail(TTT_E_HIP, "%s launch: %s", fn, hipGetErrorString(e));

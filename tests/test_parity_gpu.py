@@ -342,6 +342,15 @@ def test_paper_linear_bf16_d64_chunk16(T, rates, loss):
     _check("linear", w, _with_ln(w, 2, 13 if rates else None), loss=loss)
 
 
+def test_paper_linear_bf16_per_batch_state():
+    # a [B, H, d, d] initial state (w0_batch_stride = H d^2) and a ragged last chunk
+    w = workload(1).replace(B=3, H=2, T=77, seed=315)
+    inp = _with_ln(w, 9)
+    rng = np.random.default_rng(316)
+    inp["w0"] = (0.05 * rng.standard_normal((w.B, w.H, w.d, w.d))).astype(np.float32)
+    _check("linear", w, inp)
+
+
 def test_paper_linear_noncausal_epochs():
     w = workload(1).replace(B=2, H=3, T=196, chunk=49, causal=False, seed=320)
     _check("linear", w, _with_ln(w, 3), epochs=2)
