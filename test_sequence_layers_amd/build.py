@@ -42,6 +42,7 @@ def _flags():
 EXTRA_FLAGS = {
     "linear_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "linear_ln_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "linear_bwd_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -144,6 +144,12 @@ bool mlp_nc_supported(const MlpArgs& a, bool bf16_io);
 hipError_t launch_mlp_nc(const MlpArgs& a, hipStream_t s);
 
 hipError_t launch_linear_bwd_generic(const LinearBwdArgs& a, bool bf16_io, hipStream_t s);
+// matrix-core backward (bf16, d = 64, chunk 16): the forward recomputation (fwd: q, k, v, w0,
+// w0_batch_stride, B, H, T, eta) stores the bf16 chunk-start states in the workspace
+bool linear_bwd_mfma_supported(const LinearBwdArgs& a, bool bf16_io);
+size_t linear_bwd_mfma_workspace_bytes(const LinearBwdArgs& a);
+hipError_t launch_linear_bwd_mfma(const LinearArgs& fwd, const LinearBwdArgs& a, void* workspace,
+                                  hipStream_t s);
 
 // dst[b][h][:] = src + b * batch_stride + h * per_head (the state when T = 0); zeros when
 // src is null.

@@ -247,6 +247,21 @@ int ttt_linear_bwd(const void* q, const void* k, const void* v, const float* w0,
   const size_t dd = static_cast<size_t>(d) * d;
   if (T == 0) return copy_state(dw0, dw_out, static_cast<long long>(H) * dd, B, H, dd, s);
 
+  const bool bf16 = io_dtype == TTT_BF16;
+  {
+    // matrix-core path: bf16 chunk-start states (8 KB per chunk) in a stream-ordered workspace
+    ttt::LinearBwdArgs g{q, k, v, dz, dw_out, nullptr, dq, dk, dv, dw0, B, H, T, d, chunk, eta};
+    if (ttt::linear_bwd_mfma_supported(g, bf16)) {
+      StreamBuffer ws;
+      rc = get_workspace(ttt::linear_bwd_mfma_workspace_bytes(g), s, &ws);
+      if (rc != TTT_OK) return rc;
+      ttt::LinearArgs f{q, k, v, w0, w0_batch_stride, nullptr, nullptr, B, H, T, d, chunk, 1, eta,
+                        nullptr, 0, nullptr};
+      hipError_t e = ttt::launch_linear_bwd_mfma(f, g, ws.ptr, s);
+      if (e != hipSuccess) return hip_fail(e, "ttt_linear_bwd launch");
+      return TTT_OK;
+    }
+  }
   // chunk-start states of the forward pass, recomputed into a stream-ordered workspace
   const int b = chunk < T ? chunk : T;
   const long long nchunks = (T + b - 1) / b;
@@ -255,7 +270,6 @@ int ttt_linear_bwd(const void* q, const void* k, const void* v, const float* w0,
   StreamBuffer ws;
   rc = get_workspace(static_cast<size_t>(B) * H * nchunks * dd * sizeof(float), s, &ws);
   if (rc != TTT_OK) return rc;
-  const bool bf16 = io_dtype == TTT_BF16;
   ttt::LinearArgs f{q, k, v, w0, w0_batch_stride, nullptr, nullptr, B, H, T, d, chunk, 1, eta,
                     nullptr, 0, static_cast<float*>(ws.ptr)};
   hipError_t e = ttt::launch_linear_generic(f, bf16, s);

@@ -448,6 +448,19 @@ def test_linear_bwd_bf16_d64_chunk16(T):
     _check_bwd(w, make_inputs(w), True, seed=T)
 
 
+@pytest.mark.parametrize("T,with_dw,per_batch,eta", [(77, False, False, 0.125), (33, True, True, 0.125),
+                                                     (1000, False, False, 0.5)])
+def test_linear_bwd_bf16_matrix_core_cases(T, with_dw, per_batch, eta):
+    # the matrix-core backward without an upstream state gradient, with a [B, H, d, d] initial
+    # state, ragged last chunks and a larger rate
+    w = workload(1).replace(B=2, H=3, T=T, eta=eta, seed=210 + T)
+    inp = make_inputs(w)
+    if per_batch:
+        rng = np.random.default_rng(211)
+        inp["w0"] = (0.05 * rng.standard_normal((w.B, w.H, w.d, w.d))).astype(np.float32)
+    _check_bwd(w, inp, with_dw, seed=T + 1)
+
+
 def test_linear_bwd_config_full_size_sampled():
     w = workload(1)
     _check_bwd(w, make_inputs(w), True, sel=[(6, 4)], seed=1)
