@@ -73,6 +73,7 @@ __all__ = [
     "ttt_mlp",
     "delta_rule",
     "ttt_linear_vjp",
+    "ttt_mlp_vjp",
 ]
 
 LOSSES = ("mse", "dot")
@@ -450,3 +451,68 @@ def ttt_linear_vjp(q, k, v, w0, eta, chunk, dz, dw_out=None):
     zero = lambda t: np.zeros((N, T, d)) if t is None else t.numpy()
     return (zero(dq).reshape(shape), zero(dk).reshape(shape), zero(dv).reshape(shape),
             (np.zeros_like(W0) if dw0 is None else dw0.numpy()).reshape(tuple(lead) + (d, d)))
+
+
+def ttt_mlp_vjp(q, k, v, w1, w2, eta, chunk, dz, dw1_out=None, dw2_out=None):
+    """Vector-Jacobian product of the causal TTT-MLP layer (2-layer SiLU inner MLP,
+    reconstruction loss), the MLP counterpart of ttt_linear_vjp.
+
+    For upstream gradients dz [..., T, d] of z and dw1_out [..., h, d], dw2_out [..., d, h]
+    of the final states (or None), returns (dq, dk, dv [..., T, d], dw1 [..., h, d],
+    dw2 [..., d, h]) per chain.
+
+    The definition, written out: the primal recurrence of ttt_mlp (each token's gradient by
+    the chain rule, summed at the chunk-start weights, the output read after the update), in
+    float64 torch tensors, differentiated by torch.autograd -- so the second-order terms (the
+    gradient of the inner gradient) come from autograd, not from a hand derivation.
+    """
+    import torch
+    q2, lead = _flatten_tokens(q, np.float64)
+    k2, _ = _flatten_tokens(k, np.float64)
+    v2, _ = _flatten_tokens(v, np.float64)
+    N, T, d = q2.shape
+    W1i = torch.tensor(_broadcast_state(w1, lead, np.float64), requires_grad=True)
+    W2i = torch.tensor(_broadcast_state(w2, lead, np.float64), requires_grad=True)
+    h = W1i.shape[-2]
+    dz2, _ = _flatten_tokens(dz, np.float64)
+    b = _check_chunk(T, chunk)
+    Q = torch.tensor(q2, requires_grad=True)
+    K = torch.tensor(k2, requires_grad=True)
+    V = torch.tensor(v2, requires_grad=True)
+    silu_t = lambda u: u * torch.sigmoid(u)
+
+    def dsilu_t(u):
+        s = torch.sigmoid(u)
+        return s * (1.0 + u * (1.0 - s))
+
+    W1, W2 = W1i, W2i
+    zs = []
+    for c0 in range(0, T, b):
+        W1c, W2c = W1, W2
+        G1 = torch.zeros_like(W1c)
+        G2 = torch.zeros_like(W2c)
+        W1t, W2t = W1c, W2c
+        for t in range(c0, min(c0 + b, T)):
+            u = torch.einsum("nhj,nj->nh", W1c, K[:, t])
+            a = silu_t(u)
+            r = torch.einsum("nih,nh->ni", W2c, a) - V[:, t]
+            du = torch.einsum("nih,ni->nh", W2c, r) * dsilu_t(u)
+            G1 = G1 + torch.einsum("nh,nj->nhj", du, K[:, t])
+            G2 = G2 + torch.einsum("ni,nh->nih", r, a)
+            W1t = W1c - eta * G1
+            W2t = W2c - eta * G2
+            zs.append(torch.einsum("nih,nh->ni", W2t, silu_t(torch.einsum("nhj,nj->nh", W1t, Q[:, t]))))
+        W1, W2 = W1t, W2t
+    Z = torch.stack(zs, dim=1) if zs else torch.zeros((N, 0, d), dtype=torch.float64)
+    outs, grads = [Z], [torch.tensor(dz2)]
+    if dw1_out is not None:
+        outs.append(W1)
+        grads.append(torch.tensor(_broadcast_state(dw1_out, lead, np.float64)))
+    if dw2_out is not None:
+        outs.append(W2)
+        grads.append(torch.tensor(_broadcast_state(dw2_out, lead, np.float64)))
+    res = torch.autograd.grad(outs, (Q, K, V, W1i, W2i), grads, allow_unused=True)
+    shape = tuple(lead) + (T, d)
+    tok = lambda t: (np.zeros((N, T, d)) if t is None else t.numpy()).reshape(shape)
+    st = lambda t, like, sh: (np.zeros(like.shape) if t is None else t.numpy()).reshape(tuple(lead) + sh)
+    return (tok(res[0]), tok(res[1]), tok(res[2]), st(res[3], W1i, (h, d)), st(res[4], W2i, (d, h)))

@@ -63,6 +63,11 @@ MUTATIONS = {
     "vjp_output_before_update": (
         'zs.append(torch.einsum("nij,nj->ni", Wt, Q[:, t]))',
         'zs.append(torch.einsum("nij,nj->ni", Wc, Q[:, t]))'),
+    "mlp_vjp_gradient_at_current_weights": (
+        'u = torch.einsum("nhj,nj->nh", W1c, K[:, t])', 'u = torch.einsum("nhj,nj->nh", W1t, K[:, t])'),
+    "mlp_vjp_output_before_update": (
+        'zs.append(torch.einsum("nih,nh->ni", W2t, silu_t(torch.einsum("nhj,nj->nh", W1t, Q[:, t]))))',
+        'zs.append(torch.einsum("nih,nh->ni", W2c, silu_t(torch.einsum("nhj,nj->nh", W1c, Q[:, t]))))'),
     "epochs_ignored": (
         "chunk_starts = [c0 for _ in range(epochs) for c0", "chunk_starts = [c0 for _ in range(1) for c0"),
     "mlp_epochs_ignored": (

@@ -757,6 +757,57 @@ def test_linear_vjp_zero_rate_is_the_fixed_map():
     np.testing.assert_array_equal(dv, 0.0)
 
 
+def _fd_mlp_vjp(args, eta, chunk, dz, dw1, dw2, which, direction, h=1e-6):
+    def L(x):
+        a = dict(args)
+        a[which] = x
+        z, w1, w2 = O.ttt_mlp(a["q"], a["k"], a["v"], a["w1"], a["w2"], eta, chunk)
+        out = float(np.sum(z * dz))
+        if dw1 is not None:
+            out += float(np.sum(w1 * dw1) + np.sum(w2 * dw2))
+        return out
+    x = args[which]
+    return (L(x + h * direction) - L(x - h * direction)) / (2 * h)
+
+
+@pytest.mark.parametrize("chunk,with_dw", [(1, False), (4, True), (3, True), (9, False)])
+def test_mlp_vjp_matches_finite_differences(chunk, with_dw):
+    rng = _rng(60 + chunk)
+    N, T, d, hdim = 2, 9, 3, 5
+    q, k, v = _rand_chains(rng, N, T, d)
+    args = dict(q=q, k=k, v=v, w1=0.5 * rng.standard_normal((N, hdim, d)),
+                w2=0.5 * rng.standard_normal((N, d, hdim)))
+    dz = rng.standard_normal((N, T, d))
+    dw1 = rng.standard_normal((N, hdim, d)) if with_dw else None
+    dw2 = rng.standard_normal((N, d, hdim)) if with_dw else None
+    grads = dict(zip(("q", "k", "v", "w1", "w2"),
+                     O.ttt_mlp_vjp(q, k, v, args["w1"], args["w2"], 0.2, chunk, dz, dw1, dw2)))
+    for which in ("q", "k", "v", "w1", "w2"):
+        for _ in range(2):
+            direction = rng.standard_normal(args[which].shape)
+            fd = _fd_mlp_vjp(args, 0.2, chunk, dz, dw1, dw2, which, direction)
+            an = float(np.sum(grads[which] * direction))
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (which, fd, an)
+
+
+def test_mlp_vjp_zero_rate_is_the_fixed_map():
+    """eta = 0: z_t = W2 SiLU(W1 q_t) with u = W1 q_t, so dw2 = sum dz_t SiLU(u_t)^T,
+    dq_t = W1^T ((W2^T dz_t) * SiLU'(u_t)), dw1 = sum ((W2^T dz_t) * SiLU'(u_t)) q_t^T, and
+    dk = dv = 0."""
+    rng = _rng(65)
+    q, k, v = _rand_chains(rng, 1, 6, 3)
+    w1, w2 = rng.standard_normal((1, 4, 3)), rng.standard_normal((1, 3, 4))
+    dz = rng.standard_normal((1, 6, 3))
+    dq, dk, dv, dw1, dw2 = O.ttt_mlp_vjp(q, k, v, w1, w2, 0.0, 4, dz)
+    u = q[0] @ w1[0].T
+    gu = (dz[0] @ w2[0]) * (1 / (1 + np.exp(-u))) * (1 + u * (1 - 1 / (1 + np.exp(-u))))
+    np.testing.assert_allclose(dw2[0], dz[0].T @ (u / (1 + np.exp(-u))), atol=1e-12)
+    np.testing.assert_allclose(dq[0], gu @ w1[0], atol=1e-12)
+    np.testing.assert_allclose(dw1[0], gu.T @ q[0], atol=1e-12)
+    np.testing.assert_array_equal(dk, 0.0)
+    np.testing.assert_array_equal(dv, 0.0)
+
+
 # ---------------------------------------------------------------- edge cases
 
 def test_empty_sequence():
