@@ -166,6 +166,28 @@ int ttt_linear_bwd(const void* q, const void* k, const void* v,
                    int B, int H, int T, int d, int chunk, float eta,
                    int io_dtype, ttt_stream_t stream);
 
+/*
+ * Backward pass of the causal TTT-MLP layer (f(k) = W2 SiLU(W1 k), reconstruction loss, scalar
+ * eta), the MLP counterpart of ttt_linear_bwd.  For the forward call ttt_mlp_fwd(q, k, v, w1,
+ * w2, ..., chunk, causal = 1, eta, NULL, TTT_LOSS_MSE, 1) and upstream gradients dz of z and
+ * dw1_out, dw2_out of the final states, writes
+ *   dq, dk, dv  [B][H][T][d] io_dtype (out)
+ *   dw1 [B][H][dh][d], dw2 [B][H][d][dh] float32 (out), per (b, h) sequence (sum over b for a
+ *               state shared over the batch).
+ *   dz [B][H][T][d] io_dtype;  dw1_out, dw2_out float32 of the same shapes as dw1, dw2, or
+ *   NULL (zero).
+ * Supported: d in {16, 32, 64}, 1 <= dh <= 256, chunks of at most 16 tokens, both dtypes.  The
+ * call recomputes the forward pass and keeps its chunk-start states in stream-ordered
+ * workspaces (B*H*ceil(T/chunk)*2*d*dh*4 bytes, plus the forward's 4*d*dh*4 bytes per
+ * sequence).  T = 0 copies dw1_out, dw2_out to dw1, dw2 (zeros without them).
+ */
+int ttt_mlp_bwd(const void* q, const void* k, const void* v,
+                const float* w1, const float* w2, long long w_batch_stride,
+                const void* dz, const float* dw1_out, const float* dw2_out,
+                void* dq, void* dk, void* dv, float* dw1, float* dw2,
+                int B, int H, int T, int d, int dh, int chunk, float eta,
+                int io_dtype, ttt_stream_t stream);
+
 /* Message for the calling thread's last non-OK status ("" if none).  Owned by the library;
    valid until the thread's next call into it. */
 const char* ttt_last_error(void);

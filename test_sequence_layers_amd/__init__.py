@@ -2,7 +2,7 @@
 
 The compute runs in libttt.so (C ABI, include/ttt.h): hand-written HIP kernels for the
 TTT-Linear, TTT-MLP and delta-rule forward passes (plain inner models, and the paper's with
-layer norm and residual) and the TTT-Linear backward pass.  This package holds the ctypes
+layer norm and residual) and the TTT-Linear and TTT-MLP backward passes.  This package holds the ctypes
 binding (argument marshalling only), the in-tree build script and the seeded synthetic
 workloads.
 """
@@ -22,6 +22,7 @@ from ._binding import (  # noqa: F401
     ttt_linear_bwd,
     ttt_linear_fwd,
     ttt_linear_ln_fwd,
+    ttt_mlp_bwd,
     ttt_mlp_fwd,
     ttt_mlp_ln_fwd,
 )

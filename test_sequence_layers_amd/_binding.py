@@ -36,6 +36,8 @@ SIGNATURES = {
     "delta_rule_fwd": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _i, _i, _i, _i, _f, _vp, _i, _vp]),
     "ttt_linear_bwd": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp, _vp, _vp, _vp,
                             _i, _i, _i, _i, _i, _f, _i, _vp]),
+    "ttt_mlp_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                         _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
     "ttt_last_error": (ctypes.c_char_p, []),
     "ttt_abi_version": (_i, []),
 }
@@ -243,6 +245,43 @@ def ttt_linear_bwd(q, k, v, w0, eta, chunk, dz, dw_out=None, *, stream=None):
                                 _stream(q.device, stream))
     _check(rc)
     return dq, dk, dv, dw0
+
+
+def ttt_mlp_bwd(q, k, v, w1, w2, eta, chunk, dz, dw1_out=None, dw2_out=None, *, stream=None):
+    """Gradients of the causal TTT-MLP layer (SiLU, reconstruction loss, scalar eta) for the
+    upstream gradients dz [B,H,T,d] (dtype of q) and dw1_out [B,H,dh,d], dw2_out [B,H,d,dh]
+    float32 (or None).  Returns (dq, dk, dv, dw1, dw2) with the state gradients per sequence
+    (sum them over the batch when the states are shared)."""
+    torch = _torch()
+    lib = load_library()
+    B, H, T, d = _tokens(q, k, v)
+    if w1.dim() < 2:
+        raise ValueError("w1 must be [H, dh, d] or [B, H, dh, d]")
+    dh = int(w1.shape[-2])
+    w1, s1 = _state(w1, B, H, (dh, d), "w1", q.device)
+    w2, s2 = _state(w2, B, H, (d, dh), "w2", q.device)
+    if s1 != s2:
+        raise ValueError("w1 and w2 must both be shared over the batch or both per batch")
+    if (not isinstance(dz, torch.Tensor) or tuple(dz.shape) != (B, H, T, d) or dz.dtype != q.dtype
+            or dz.device != q.device or not dz.is_contiguous()):
+        raise ValueError(f"dz must be a contiguous {q.dtype} tensor of shape {(B, H, T, d)}")
+    if (dw1_out is None) != (dw2_out is None):
+        raise ValueError("give both dw1_out and dw2_out, or neither")
+    if dw1_out is not None:
+        dw1_out = _out(dw1_out, (B, H, dh, d), torch.float32, q.device, "dw1_out")
+        dw2_out = _out(dw2_out, (B, H, d, dh), torch.float32, q.device, "dw2_out")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dw1 = torch.empty((B, H, dh, d), dtype=torch.float32, device=q.device)
+    dw2 = torch.empty((B, H, d, dh), dtype=torch.float32, device=q.device)
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    with torch.cuda.device(q.device):
+        rc = lib.ttt_mlp_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), w1.data_ptr(), w2.data_ptr(),
+                             s1, dz.data_ptr(), ptr(dw1_out), ptr(dw2_out), dq.data_ptr(),
+                             dk.data_ptr(), dv.data_ptr(), dw1.data_ptr(), dw2.data_ptr(),
+                             B, H, T, d, dh, int(chunk), float(eta), _io_dtype(q),
+                             _stream(q.device, stream))
+    _check(rc)
+    return dq, dk, dv, dw1, dw2
 
 
 def delta_rule_fwd(q, k, v, w0, eta, *, eta_tok=None, z=None, w_out=None, return_state=False,

@@ -122,6 +122,26 @@ struct MlpArgs {
   const float* ln_w = nullptr;
   const float* ln_b = nullptr;
   float ln_eps = 0.0f;
+  // generic kernel only: chunk-start states [B][H][nchunks][W1 (h d), W2 (d h)] or null
+  float* w_hist = nullptr;
+};
+
+// Backward pass of the causal TTT-MLP layer (SiLU, reconstruction loss, scalar rate).
+struct MlpBwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dz;
+  const float* dw1_out;  // upstream gradients of the final states [B][H][h][d], [B][H][d][h] or null
+  const float* dw2_out;
+  const float* w_hist;   // chunk-start states (from the forward)
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dw1;            // [B][H][h][d]
+  float* dw2;            // [B][H][d][h]
+  int B, H, T, d, dh, chunk;
+  float eta;
 };
 
 // Host-side launchers (return a hipError_t; argument checks are done by the caller).
@@ -144,6 +164,7 @@ bool mlp_nc_supported(const MlpArgs& a, bool bf16_io);
 hipError_t launch_mlp_nc(const MlpArgs& a, hipStream_t s);
 
 hipError_t launch_linear_bwd_generic(const LinearBwdArgs& a, bool bf16_io, hipStream_t s);
+hipError_t launch_mlp_bwd_generic(const MlpBwdArgs& a, bool bf16_io, hipStream_t s);
 // matrix-core backward (bf16, d = 64, chunk 16): the forward recomputation (fwd: q, k, v, w0,
 // w0_batch_stride, B, H, T, eta) stores the bf16 chunk-start states in the workspace
 bool linear_bwd_mfma_supported(const LinearBwdArgs& a, bool bf16_io);

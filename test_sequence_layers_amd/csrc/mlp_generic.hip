@@ -107,6 +107,13 @@ __global__ __launch_bounds__(kThreads) void mlp_generic_kernel(MlpArgs a, float*
   const int nchunks = (T + b - 1) / b;
   for (int step = 0; step < a.epochs * nchunks; ++step) {  // epochs > 1: non-causal only
     const int c0 = (step % nchunks) * b;
+    if (a.w_hist) {  // chunk-start states, for the backward pass
+      float* wh = a.w_hist + (static_cast<size_t>(chain) * nchunks + c0 / b) * 2 * hd;
+      for (size_t e = tid; e < hd; e += kThreads) {
+        wh[e] = W1c[e];
+        wh[hd + e] = W2c[e];
+      }
+    }
     const int cend = min(c0 + b, T);
     for (int s0 = c0; s0 < cend; s0 += kSub) {
       const int n = min(kSub, cend - s0);
@@ -163,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void mlp_generic_kernel(MlpArgs a, float*
         }
       }
       __syncthreads();
-      if (a.causal) {
+      if (a.causal && a.z) {  // outputs (skipped when only the states are wanted)
         // query hidden layer at W1_t (dual form of the in-block W1 updates)
         for (int e = tid; e < kSub * h; e += kThreads) {
           const int t = e / h, c = e % h;
@@ -216,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void mlp_generic_kernel(MlpArgs a, float*
     __syncthreads();
   }
 
-  if (!a.causal) {
+  if (!a.causal && a.z) {
     for (int s0 = 0; s0 < T; s0 += kSub) {
       const int n = min(kSub, T - s0);
       for (int e = tid; e < kSub * D; e += kThreads) {

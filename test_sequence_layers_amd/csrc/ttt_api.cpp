@@ -195,7 +195,7 @@ int mlp_fwd(const char* fn, const void* q, const void* k, const void* v, const f
 
 extern "C" {
 
-int ttt_abi_version(void) { return 5; }
+int ttt_abi_version(void) { return 6; }
 
 const char* ttt_last_error(void) { return g_last_error.c_str(); }
 
@@ -278,6 +278,57 @@ int ttt_linear_bwd(const void* q, const void* k, const void* v, const float* w0,
                        B, H, T, d, chunk, eta};
   e = ttt::launch_linear_bwd_generic(g, bf16, s);
   if (e != hipSuccess) return hip_fail(e, "ttt_linear_bwd launch");
+  return TTT_OK;
+}
+
+int ttt_mlp_bwd(const void* q, const void* k, const void* v, const float* w1, const float* w2,
+                long long w_batch_stride, const void* dz, const float* dw1_out,
+                const float* dw2_out, void* dq, void* dk, void* dv, float* dw1, float* dw2, int B,
+                int H, int T, int d, int dh, int chunk, float eta, int io_dtype,
+                ttt_stream_t stream) {
+  g_last_error.clear();
+  int rc = check_common("ttt_mlp_bwd", q, k, v, dz, B, H, T, d, eta, nullptr, io_dtype);
+  if (rc != TTT_OK) return rc;
+  if (!w1 || !w2 || !dw1 || !dw2)
+    return fail(TTT_E_INVALID, "ttt_mlp_bwd: w1, w2, dw1 and dw2 must be non-null");
+  if (T > 0 && (!dq || !dk || !dv))
+    return fail(TTT_E_INVALID, "ttt_mlp_bwd: dq, dk and dv must be non-null");
+  if (dh <= 0) return fail(TTT_E_INVALID, "ttt_mlp_bwd: dh must be positive (got %d)", dh);
+  if (chunk < 1) return fail(TTT_E_INVALID, "ttt_mlp_bwd: chunk must be >= 1 (got %d)", chunk);
+  if (w_batch_stride < 0) return fail(TTT_E_INVALID, "ttt_mlp_bwd: negative w_batch_stride");
+  if (d != 16 && d != 32 && d != 64)
+    return fail(TTT_E_UNSUPPORTED, "ttt_mlp_bwd: d=%d not supported (16, 32, 64)", d);
+  if (dh > 256) return fail(TTT_E_UNSUPPORTED, "ttt_mlp_bwd: dh=%d not supported (<= 256)", dh);
+  if (T > 0 && (chunk < T ? chunk : T) > 16)
+    return fail(TTT_E_UNSUPPORTED, "ttt_mlp_bwd: chunks of more than 16 tokens not supported");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t per = static_cast<size_t>(d) * dh;
+  if (T == 0) {
+    const long long st = static_cast<long long>(H) * static_cast<long long>(per);
+    rc = copy_state(dw1, dw1_out, st, B, H, per, s);
+    if (rc != TTT_OK) return rc;
+    return copy_state(dw2, dw2_out, st, B, H, per, s);
+  }
+  const int b = chunk < T ? chunk : T;
+  const long long nchunks = (T + b - 1) / b;
+  if (!fits_int64(B, H, nchunks, 2LL * static_cast<long long>(per)))
+    return fail(TTT_E_INVALID, "ttt_mlp_bwd: state history overflows");
+  // forward recomputation on the generic kernel, storing the chunk-start states
+  StreamBuffer hist, fws;
+  rc = get_workspace(static_cast<size_t>(B) * H * nchunks * 2 * per * sizeof(float), s, &hist);
+  if (rc != TTT_OK) return rc;
+  ttt::MlpArgs f{q, k, v, w1, w2, w_batch_stride, nullptr, nullptr, nullptr,
+                 B, H, T, d, dh, chunk, 1, eta, nullptr, 0};
+  f.w_hist = static_cast<float*>(hist.ptr);
+  rc = get_workspace(ttt::mlp_generic_workspace_floats(f) * sizeof(float), s, &fws);
+  if (rc != TTT_OK) return rc;
+  const bool bf16 = io_dtype == TTT_BF16;
+  hipError_t e = ttt::launch_mlp_generic(f, bf16, static_cast<float*>(fws.ptr), s);
+  if (e != hipSuccess) return hip_fail(e, "ttt_mlp_bwd state launch");
+  ttt::MlpBwdArgs g{q, k, v, dz, dw1_out, dw2_out, static_cast<const float*>(hist.ptr), dq, dk, dv,
+                    dw1, dw2, B, H, T, d, dh, chunk, eta};
+  e = ttt::launch_mlp_bwd_generic(g, bf16, s);
+  if (e != hipSuccess) return hip_fail(e, "ttt_mlp_bwd launch");
   return TTT_OK;
 }
 

@@ -28,7 +28,7 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for n in ("ttt_linear_fwd", "ttt_mlp_fwd", "delta_rule_fwd", "ttt_linear_bwd",
+    for n in ("ttt_linear_fwd", "ttt_mlp_fwd", "delta_rule_fwd", "ttt_linear_bwd", "ttt_mlp_bwd",
               "ttt_linear_ln_fwd", "ttt_mlp_ln_fwd", "ttt_last_error", "ttt_abi_version"):
         assert n in names
 
@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ttt_abi_version() == 5
+    assert lib.ttt_abi_version() == 6
 
 
 FAKE = 0x1000  # never dereferenced: validation fails before any HIP call
@@ -196,6 +196,32 @@ def test_paper_models_reject(lib, fn, kw, code, msg):
     assert fn(lib, **kw) == code
     assert msg in ttt.last_error()
     assert ("ttt_linear_ln_fwd" if fn is _linear_ln else "ttt_mlp_ln_fwd") in ttt.last_error()
+
+
+def _mlp_bwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, w1=FAKE, w2=FAKE, stride=0, dz=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+             dw1=FAKE, dw2=FAKE, B=1, H=1, T=16, d=16, dh=32, chunk=16, eta=0.1, io=0)
+    a.update(kw)
+    return lib.ttt_mlp_bwd(a["q"], a["k"], a["v"], a["w1"], a["w2"], a["stride"], a["dz"], None,
+                           None, a["dq"], a["dk"], a["dv"], a["dw1"], a["dw2"], a["B"], a["H"],
+                           a["T"], a["d"], a["dh"], a["chunk"], a["eta"], a["io"], None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(dz=None), ttt.TTT_E_INVALID, "non-null"),
+    (dict(dw2=None), ttt.TTT_E_INVALID, "dw2"),
+    (dict(w1=None), ttt.TTT_E_INVALID, "w1"),
+    (dict(dk=None), ttt.TTT_E_INVALID, "dk"),
+    (dict(dh=0), ttt.TTT_E_INVALID, "dh"),
+    (dict(dh=300), ttt.TTT_E_UNSUPPORTED, "dh=300"),
+    (dict(chunk=0), ttt.TTT_E_INVALID, "chunk"),
+    (dict(chunk=32, T=64), ttt.TTT_E_UNSUPPORTED, "16 tokens"),
+    (dict(eta=float("inf")), ttt.TTT_E_INVALID, "finite"),
+    (dict(d=24), ttt.TTT_E_UNSUPPORTED, "d=24"),
+])
+def test_mlp_bwd_rejects(lib, kw, code, msg):
+    assert _mlp_bwd(lib, **kw) == code
+    assert msg in ttt.last_error()
 
 
 def test_error_text_is_per_call(lib):

@@ -466,6 +466,75 @@ def test_linear_bwd_config_full_size_sampled():
     _check_bwd(w, make_inputs(w), True, sel=[(6, 4)], seed=1)
 
 
+def _check_mlp_bwd(w, inp, with_dw, sel=None, seed=0):
+    import torch
+    import test_sequence_layers_amd as ttt
+    from oracle import ttt_oracle as O
+    _note(f"[parity] mlp_bwd B={w.B} H={w.H} T={w.T} d={w.d} h={w.h} chunk={w.chunk} io={w.io} "
+          f"dw_out={with_dw} seed={w.seed}")
+    rng = np.random.default_rng(30_000 + seed)
+    dz = rng.standard_normal((w.B, w.H, w.T, w.d)).astype(np.float32)
+    if w.io == "bf16":
+        dz = to_np(torch.from_numpy(dz).to(torch.bfloat16))
+    dw1 = rng.standard_normal((w.B, w.H, w.h, w.d)).astype(np.float32) if with_dw else None
+    dw2 = rng.standard_normal((w.B, w.H, w.d, w.h)).astype(np.float32) if with_dw else None
+    dev = to_device(inp, w.io)
+    dzd = torch.from_numpy(dz).to("cuda").to(dev["q"].dtype).contiguous()
+    dd1 = torch.from_numpy(dw1).to("cuda").contiguous() if with_dw else None
+    dd2 = torch.from_numpy(dw2).to("cuda").contiguous() if with_dw else None
+    out = ttt.ttt_mlp_bwd(dev["q"], dev["k"], dev["v"], dev["w1"], dev["w2"], w.eta, w.chunk, dzd,
+                          dd1, dd2)
+    torch.cuda.synchronize()
+    got = [to_np(t) for t in out]
+    bc = lambda x, sh: np.broadcast_to(x, (w.B, w.H) + sh) if x.ndim == 3 else x
+    q, k, v, dzz = inp["q"], inp["k"], inp["v"], dz
+    w1, w2 = bc(inp["w1"], (w.h, w.d)), bc(inp["w2"], (w.d, w.h))
+    if sel is not None:
+        bs = [b for b, _ in sel]
+        hs = [h for _, h in sel]
+        pick = lambda x: x[bs, hs][None] if x is not None else None
+        q, k, v, dzz, w1, w2, dw1, dw2 = map(pick, (q, k, v, dzz, w1, w2, dw1, dw2))
+        got = [g[bs, hs][None] for g in got]
+    ref = O.ttt_mlp_vjp(q, k, v, w1, w2, w.eta, w.chunk, dzz, dw1, dw2)
+    tol = tol_for(w.io)
+    for name, g, r in zip(("dq", "dk", "dv", "dw1", "dw2"), got, ref):
+        assert np.isfinite(g).all(), name
+        rel, _ = slab_rel(g, r)
+        _note(f"[parity]   {name} rel {rel:.3e} (tol {tol})")
+        assert rel <= tol, (name, rel)
+
+
+@pytest.mark.parametrize("d,h,chunk,with_dw", [(16, 32, 4, True), (16, 32, 1, False),
+                                               (32, 64, 16, True), (16, 24, 5, False),
+                                               (64, 64, 16, False)])
+def test_mlp_bwd_fp32(d, h, chunk, with_dw):
+    w = workload(3).replace(B=2, H=2, T=37, d=d, h=h, chunk=chunk, io="f32", eta=0.2,
+                            seed=500 + d + h + chunk)
+    _check_mlp_bwd(w, make_inputs(w), with_dw, seed=d + chunk)
+
+
+@pytest.mark.parametrize("T,with_dw", [(16, True), (70, False)])
+def test_mlp_bwd_bf16_h256(T, with_dw):
+    w = workload(3).replace(B=2, H=2, T=T, seed=520 + T)
+    _check_mlp_bwd(w, make_inputs(w), with_dw, seed=T)
+
+
+def test_mlp_bwd_config_full_size_sampled():
+    w = workload(3)
+    _check_mlp_bwd(w, make_inputs(w), True, sel=[(3, 7)], seed=2)
+
+
+def test_mlp_bwd_empty_sequence_copies_state_gradients():
+    import torch
+    import test_sequence_layers_amd as ttt
+    q = torch.zeros((2, 3, 0, 16), device="cuda")
+    w1, w2 = torch.randn((3, 8, 16), device="cuda"), torch.randn((3, 16, 8), device="cuda")
+    d1, d2 = torch.randn((2, 3, 8, 16), device="cuda"), torch.randn((2, 3, 16, 8), device="cuda")
+    *_, g1, g2 = ttt.ttt_mlp_bwd(q, q, q, w1, w2, 0.1, 16, q, d1, d2)
+    torch.cuda.synchronize()
+    assert torch.equal(g1, d1) and torch.equal(g2, d2)
+
+
 def test_linear_bwd_empty_sequence_copies_dw_out():
     import torch
     import test_sequence_layers_amd as ttt
