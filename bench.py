@@ -137,11 +137,16 @@ def time_workload(w, steps, warmup, torch, ttt, rotate=None, rates=False, loss="
 
 
 def time_backward(w, steps, warmup, torch, ttt):
-    """Event-timed ttt_linear_bwd calls on the workload (inputs resident in HBM)."""
+    """Event-timed ttt_linear_bwd / ttt_mlp_bwd calls on the workload (inputs resident in
+    HBM; seeded dZ ~ N(0, 1), no upstream state gradient)."""
     dev = make_device_inputs(w, w.seed, torch)
     g = torch.Generator(device="cuda").manual_seed(w.seed)
     dz = torch.randn(dev["q"].shape, generator=g, device="cuda").to(dev["q"].dtype)
-    call = lambda: ttt.ttt_linear_bwd(dev["q"], dev["k"], dev["v"], dev["w0"], w.eta, w.chunk, dz)
+    if w.kind == "linear":
+        call = lambda: ttt.ttt_linear_bwd(dev["q"], dev["k"], dev["v"], dev["w0"], w.eta, w.chunk, dz)
+    else:
+        call = lambda: ttt.ttt_mlp_bwd(dev["q"], dev["k"], dev["v"], dev["w1"], dev["w2"], w.eta,
+                                       w.chunk, dz)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -322,10 +327,14 @@ def main():
         # and the causal MLP workloads
         variants += [(o, "+paper_ln", dict(paper=True)) for o in WORKLOADS
                      if o.name in ("linear_d64_T2048", "mlp_h256_T2048")]
-        # backward pass of the headline workload (dz ~ N(0, 1), dw_out = 0)
-        if w.kind == "linear":
-            r = time_backward(w, max(10, args.steps // 2), 3, torch, ttt)
-            others[w.name + "+backward"] = {
+        # backward passes of the headline linear workload and of the causal MLP workload
+        # (dz ~ N(0, 1), no upstream state gradient)
+        bwd = [w] if w.kind == "linear" else []
+        bwd += [o for o in WORKLOADS if o.name == "mlp_h256_T2048"]
+        for o in bwd:
+            r = time_backward(o, max(10, args.steps // 2) if o.kind == "linear" else 3,
+                              3 if o.kind == "linear" else 1, torch, ttt)
+            others[o.name + "+backward"] = {
                 "tokens_per_s": round(r["tokens_per_s"], 1),
                 "ms_per_step": round(r["ms_per_step"], 5),
             }
