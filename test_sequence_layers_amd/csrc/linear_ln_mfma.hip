@@ -95,24 +95,32 @@ __device__ __forceinline__ float row_sum16(float x) {
   return x;
 }
 
-// LDS ring of kRing chunk slots, filled by a loader wave with direct-to-LDS buffer loads
-// (rows past T read as zero).  Slot: Q, K, V tiles (16 rows of 128 bytes; the 16-byte
-// pieces of row r are stored XOR-swizzled by r % 8, so that 16-byte reads of one piece
-// from 8 consecutive rows fall on distinct banks), then the 16 rate factors.  (A separate
-// loader keeps the compute wave free of pending LDS loads, before whose destination the
-// compiler would otherwise make every LDS read wait.)  Barrier b publishes chunk b and
-// frees the slot of chunk b - 1; the loader then refills that slot with chunk b - 1 + kRing.
-// Before barrier b the loader's loads of chunk b are complete once at most kRing - 2 later
-// chunks (kRing - 1 before barrier 0) are outstanding.
+// Three waves per chain: the chain wave runs the state recursion (R and the update) and
+// hands each chunk's bf16 state operand and -eta R operand to the output wave, which forms
+// that chunk's Z one step later; a loader wave fills an LDS ring of kRing chunk slots with
+// direct-to-LDS buffer loads (rows past T read as zero).  Slot: Q, K, V tiles (16 rows of
+// 128 bytes; the 16-byte pieces of row r are stored XOR-swizzled by r % 8, so that 16-byte
+// reads of one piece from 8 consecutive rows fall on distinct banks), then the 16 rate
+// factors.  (A separate loader keeps the compute waves free of pending LDS loads, before
+// whose destination the compiler would otherwise make every LDS read wait.)
+// Barrier b (b = 0 .. nchunks) publishes chunk b to the chain wave and chunk b - 1's handoff
+// to the output wave, and frees the slot of chunk b - 2, which the loader then refills with
+// chunk b - 2 + kRing.  Before barrier b the loads of chunk b are complete once at most
+// kRing - 3 later chunks are outstanding (more before barrier 2: a smaller count then only
+// waits longer).
 constexpr int kRing = 8;
 constexpr int kSlotQ = 0, kSlotK = kTileBytes, kSlotV = 2 * kTileBytes, kSlotE = 3 * kTileBytes;
 constexpr int kSlotBytes = kSlotE + kB * 4;
 template <bool kTok> struct Counts {
   static constexpr int kLoads = 6 + (kTok ? 1 : 0);
-  static constexpr int kWait0 = (kRing - 1) * kLoads;
-  static constexpr int kWait = (kRing - 2) * kLoads;
-  static_assert(kWait0 < 64, "vmcnt is 6 bits");
+  static constexpr int kWait = (kRing - 3) * kLoads;
+  static_assert(kWait < 64, "vmcnt is 6 bits");
 };
+// Handoff buffer (two, used in turn): the bf16 chunk-start state operands wop[kb][it] at
+// 1024 (4 kb + it) + 16 lane, then the -eta R operands (first 8 bytes of each padded
+// operand) at 8192 + 512 it + 8 lane: consecutive lanes write consecutive addresses.
+constexpr int kHandR = 8 * 1024;
+constexpr int kHandBytes = kHandR + 4 * 512;
 
 // Workgroup barrier for LDS traffic only: this wave's LDS reads are complete, then both
 // waves meet (the fence of __syncthreads() would also drain this wave's outstanding stores).
@@ -135,11 +143,15 @@ template <typename T>
 __device__ __forceinline__ T lds_load(const lds_char* p) {
   return *reinterpret_cast<const __attribute__((address_space(3))) T*>(p);
 }
+template <typename T>
+__device__ __forceinline__ void lds_store(lds_char* p, const T& x) {
+  *reinterpret_cast<__attribute__((address_space(3))) T*>(p) = x;
+}
 
 template <bool kTok, bool kDot>
-__global__ __launch_bounds__(128) void linear_ln_mfma_kernel(LinearArgs a) {
+__global__ __launch_bounds__(192) void linear_ln_mfma_kernel(LinearArgs a) {
   const int chain = blockIdx.x;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // 0: compute, 1: loader
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // 0: chain, 1: output, 2: loader
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int n = lane & 15;
@@ -162,7 +174,9 @@ __global__ __launch_bounds__(128) void linear_ln_mfma_kernel(LinearArgs a) {
   const float eps = a.ln_eps;
   using CT = Counts<kTok>;
   __shared__ __attribute__((aligned(16))) char ring_mem[kRing * kSlotBytes];
+  __shared__ __attribute__((aligned(16))) char hand_mem[2 * kHandBytes];
   lds_char* ring = (lds_char*)(ring_mem);
+  lds_char* hand = (lds_char*)(hand_mem);
 
   // ---- the state: W^T tiles [kb][hf][it] ----
   float4_t wt[2][2][4];
@@ -250,15 +264,12 @@ __global__ __launch_bounds__(128) void linear_ln_mfma_kernel(LinearArgs a) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(re, dst + kSlotE, 4, lane * 4, 0, 0, 0);
     }
   };
-  if (wv == 1) {
+  if (wv == 2) {
     for (int c = 0; c < kRing; ++c) issue(c);
-    for (int b = 0; b < nchunks; ++b) {
-      if (b == 0)
-        wait_vmcnt<CT::kWait0>();
-      else
-        wait_vmcnt<CT::kWait>();
+    for (int b = 0; b <= nchunks; ++b) {
+      wait_vmcnt<CT::kWait>();
       lds_barrier();  // barrier b
-      if (b >= 1) issue(b - 1 + kRing);
+      if (b >= 2) issue(b - 2 + kRing);
     }
     wait_vmcnt<0>();  // no load into LDS outlives the wave
     return;
@@ -267,24 +278,95 @@ __global__ __launch_bounds__(128) void linear_ln_mfma_kernel(LinearArgs a) {
   // this lane's read offsets in a slot: piece P of row n sits at n * 128 + 16 (P ^ (n % 8))
   auto piece = [&](int p) { return n * kRowBytes + 16 * (p ^ (n & 7)); };
 
-  // One chunk (its loads were issued kPre steps earlier).
+  // ---- output wave: Z of chunk c from its handoff ----
+  if (wv == 1) {
+    auto out_step = [&](int c) {
+      const lds_char* sl = ring + (c % kRing) * kSlotBytes;
+      const lds_char* hb = hand + (c & 1) * kHandBytes;
+      bf16x8_t kop[2], qop[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        kop[kb] = bf(lds_load<u32x4>(sl + kSlotK + piece(4 * kb + g)));
+        qop[kb] = bf(lds_load<u32x4>(sl + kSlotQ + piece(4 * kb + g)));
+      }
+      bf16x8_t wop[2][4], rb[4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int it = 0; it < 4; ++it) wop[kb][it] = bf(lds_load<u32x4>(hb + 1024 * (4 * kb + it) + 16 * lane));
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const u32x2 r = lds_load<u32x2>(hb + kHandR + 512 * it + 8 * lane);
+        rb[it] = op4(r.x, r.y, 0u, 0u);
+      }
+      // Z^T (rows: outputs 16 it + 4 g + e; columns: tokens n)
+      float4_t pt = mfma(kop[0], qop[0], zero);  // P^T = K Q^T, masked s <= t
+      pt = mfma(kop[1], qop[1], pt);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pt[e] = keep[e] ? pt[e] : 0.0f;
+      const bf16x8_t ptb = pad_op(pt);
+      float4_t zt[4];
+      float z1 = 0.0f, z2 = 0.0f;
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        zt[it] = mfma(wop[0][it], qop[0], zero);
+        zt[it] = mfma(wop[1][it], qop[1], zt[it]);
+        zt[it] = mfma(rb[it], ptb, zt[it]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          z1 += zt[it][e];
+          z2 += zt[it][e] * zt[it][e];
+        }
+      }
+      // a token's 64 outputs: 16 in this lane, the rest in lanes n + 16, n + 32, n + 48
+      z1 += __shfl_xor(z1, 16, 64);
+      z2 += __shfl_xor(z2, 16, 64);
+      z1 += __shfl_xor(z1, 32, 64);
+      z2 += __shfl_xor(z2, 32, 64);
+      const float mu = z1 * (1.0f / kD);
+      const float rs = 1.0f / sqrtf(fmaxf(z2 * (1.0f / kD) - mu * mu, 0.0f) + eps);
+      const int off = c * kTileBytes;
+      const __amdgpu_buffer_rsrc_t rz = chunk_rsrc(z + off, seq_bytes - off);
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const float4_t gz = *reinterpret_cast<const float4_t*>(&lnp[0][16 * it + 4 * g]);
+        const float4_t bz = *reinterpret_cast<const float4_t*>(&lnp[1][16 * it + 4 * g]);
+        const u32x2 qr = lds_load<u32x2>(sl + kSlotQ + piece(2 * it + (g >> 1)) + 8 * (g & 1));
+        const float4_t o = float4_t{bf_lo(qr.x), bf_hi(qr.x), bf_lo(qr.y), bf_hi(qr.y)} +
+                           gz * ((zt[it] - mu) * rs) + bz;
+        const u32x2 out = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
+        __builtin_amdgcn_raw_buffer_store_b64(out, rz, n * kRowBytes + 32 * it + 8 * g, 0, 0);
+      }
+    };
+    lds_barrier();  // barrier 0
+    for (int b = 1; b <= nchunks; ++b) {
+      lds_barrier();  // barrier b: chunk b - 1's handoff is complete
+      out_step(b - 1);
+    }
+    return;
+  }
+
+  // ---- chain wave: R, the handoff and the update of chunk c ----
   auto step = [&](int c) {
     const lds_char* sl = ring + (c % kRing) * kSlotBytes;
-    bf16x8_t kop[2], qop[2];
+    lds_char* hb = hand + (c & 1) * kHandBytes;
+    bf16x8_t kop[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      kop[kb] = bf(lds_load<u32x4>(sl + kSlotK + piece(4 * kb + g)));
-      qop[kb] = bf(lds_load<u32x4>(sl + kSlotQ + piece(4 * kb + g)));
-    }
+    for (int kb = 0; kb < 2; ++kb) kop[kb] = bf(lds_load<u32x4>(sl + kSlotK + piece(4 * kb + g)));
     float4_t et = {1.0f, 1.0f, 1.0f, 1.0f};
     if (kTok) et = lds_load<float4_t>(sl + kSlotE + 16 * g);
 
-    // bf16 chunk-start state
+    // bf16 chunk-start state (also handed to the output wave)
     bf16x8_t wop[2][4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int it = 0; it < 4; ++it) wop[kb][it] = cat_op(wt[kb][0][it], wt[kb][1][it]);
+      for (int it = 0; it < 4; ++it) {
+        const u32x4 u = {pack_bf16(wt[kb][0][it][0], wt[kb][0][it][1]), pack_bf16(wt[kb][0][it][2], wt[kb][0][it][3]),
+                         pack_bf16(wt[kb][1][it][0], wt[kb][1][it][1]), pack_bf16(wt[kb][1][it][2], wt[kb][1][it][3])};
+        wop[kb][it] = bf(u);
+        lds_store<u32x4>(hb + 1024 * (4 * kb + it) + 16 * lane, u);
+      }
 
     // ---- R (rows: tokens 4 g + e; columns: outputs 16 it + n) ----
     float4_t y[4];
@@ -316,7 +398,7 @@ __global__ __launch_bounds__(128) void linear_ln_mfma_kernel(LinearArgs a) {
       const float4_t kv = mfma(bf(kvr), sel_kv, zero);
       err[it] = kDot ? kv : kv + gr[it] * xh[it] + br[it];
     }
-    bf16x8_t rb[4];  // -eta_t R as padded operands
+    bf16x8_t rb[4];  // -eta_t R as padded operands (also handed to the output wave)
     {
       float4_t m1 = zero, m2 = zero;
 #pragma unroll
@@ -332,47 +414,11 @@ __global__ __launch_bounds__(128) void linear_ln_mfma_kernel(LinearArgs a) {
       }
       const float4_t sc = float4_t{rstd[0], rstd[1], rstd[2], rstd[3]} * et * -eta;
 #pragma unroll
-      for (int it = 0; it < 4; ++it) rb[it] = pad_op(sc * (gr[it] * err[it] - m1 - xh[it] * m2));
-    }
-
-    // ---- outputs: Z^T (rows: outputs 16 it + 4 g + e; columns: tokens n) ----
-    float4_t pt = mfma(kop[0], qop[0], zero);  // P^T = K Q^T, masked s <= t
-    pt = mfma(kop[1], qop[1], pt);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) pt[e] = keep[e] ? pt[e] : 0.0f;
-    const bf16x8_t ptb = pad_op(pt);
-    float4_t zt[4];
-    float z1 = 0.0f, z2 = 0.0f;
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      zt[it] = mfma(wop[0][it], qop[0], zero);
-      zt[it] = mfma(wop[1][it], qop[1], zt[it]);
-      zt[it] = mfma(rb[it], ptb, zt[it]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        z1 += zt[it][e];
-        z2 += zt[it][e] * zt[it][e];
-      }
-    }
-    // a token's 64 outputs: 16 in this lane, the rest in lanes n + 16, n + 32, n + 48
-    z1 += __shfl_xor(z1, 16, 64);
-    z2 += __shfl_xor(z2, 16, 64);
-    z1 += __shfl_xor(z1, 32, 64);
-    z2 += __shfl_xor(z2, 32, 64);
-    {
-      const float mu = z1 * (1.0f / kD);
-      const float rs = 1.0f / sqrtf(fmaxf(z2 * (1.0f / kD) - mu * mu, 0.0f) + eps);
-      const int off = c * kTileBytes;
-      const __amdgpu_buffer_rsrc_t rz = chunk_rsrc(z + off, seq_bytes - off);
-#pragma unroll
       for (int it = 0; it < 4; ++it) {
-        const float4_t gz = *reinterpret_cast<const float4_t*>(&lnp[0][16 * it + 4 * g]);
-        const float4_t bz = *reinterpret_cast<const float4_t*>(&lnp[1][16 * it + 4 * g]);
-        const u32x2 qr = lds_load<u32x2>(sl + kSlotQ + piece(2 * it + (g >> 1)) + 8 * (g & 1));
-        const float4_t o = float4_t{bf_lo(qr.x), bf_hi(qr.x), bf_lo(qr.y), bf_hi(qr.y)} +
-                           gz * ((zt[it] - mu) * rs) + bz;
-        const u32x2 out = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
-        __builtin_amdgcn_raw_buffer_store_b64(out, rz, n * kRowBytes + 32 * it + 8 * g, 0, 0);
+        const float4_t r = sc * (gr[it] * err[it] - m1 - xh[it] * m2);
+        const u32x2 rp = {pack_bf16(r[0], r[1]), pack_bf16(r[2], r[3])};
+        rb[it] = op4(rp.x, rp.y, 0u, 0u);
+        lds_store<u32x2>(hb + kHandR + 512 * it + 8 * lane, rp);
       }
     }
 
@@ -388,9 +434,10 @@ __global__ __launch_bounds__(128) void linear_ln_mfma_kernel(LinearArgs a) {
   };
 
   for (int c = 0; c < nchunks; ++c) {
-    lds_barrier();  // barrier c: chunk c is in its slot
+    lds_barrier();  // barrier c: chunk c is in its slot, the handoff buffer c % 2 is free
     step(c);
   }
+  lds_barrier();  // barrier nchunks: the last handoff is complete
 
   if (a.w_out) {
     float* wo = a.w_out + static_cast<size_t>(chain) * kD * kD;
@@ -420,7 +467,7 @@ bool linear_ln_mfma_supported(const LinearArgs& a, bool bf16_io) {
 hipError_t launch_linear_ln_mfma(const LinearArgs& a, hipStream_t s) {
   const long long nchains = static_cast<long long>(a.B) * a.H;
   if (nchains > 0x7fffffffLL) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<unsigned>(nchains)), block(128);  // compute wave + loader wave
+  const dim3 grid(static_cast<unsigned>(nchains)), block(192);  // chain, output and loader waves
   const bool tok = a.eta_tok != nullptr;
   if (tok && a.dot_loss)
     hipLaunchKernelGGL((linear_ln_mfma_kernel<true, true>), grid, block, 0, s, a);
