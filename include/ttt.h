@@ -177,9 +177,11 @@ int ttt_linear_bwd(const void* q, const void* k, const void* v,
  *   dz [B][H][T][d] io_dtype;  dw1_out, dw2_out float32 of the same shapes as dw1, dw2, or
  *   NULL (zero).
  * Supported: d in {16, 32, 64}, 1 <= dh <= 256, chunks of at most 16 tokens, both dtypes.  The
- * call recomputes the forward pass and keeps its chunk-start states in stream-ordered
- * workspaces (B*H*ceil(T/chunk)*2*d*dh*4 bytes, plus the forward's 4*d*dh*4 bytes per
- * sequence).  T = 0 copies dw1_out, dw2_out to dw1, dw2 (zeros without them).
+ * call recomputes the forward pass and keeps its chunk-start states in a stream-ordered
+ * workspace: bf16 with d = 64, dh = 256, chunk = 16 and 16-byte aligned buffers (matrix
+ * cores; B*H*ceil(T/16)*64 KB), else float32 (B*H*ceil(T/chunk)*2*d*dh*4 bytes, plus the
+ * forward's 4*d*dh*4 bytes per sequence).  T = 0 copies dw1_out, dw2_out to dw1, dw2 (zeros
+ * without them).
  */
 int ttt_mlp_bwd(const void* q, const void* k, const void* v,
                 const float* w1, const float* w2, long long w_batch_stride,

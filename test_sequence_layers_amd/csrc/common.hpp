@@ -165,6 +165,12 @@ hipError_t launch_mlp_nc(const MlpArgs& a, hipStream_t s);
 
 hipError_t launch_linear_bwd_generic(const LinearBwdArgs& a, bool bf16_io, hipStream_t s);
 hipError_t launch_mlp_bwd_generic(const MlpBwdArgs& a, bool bf16_io, hipStream_t s);
+// matrix-core forward pass that stores the bf16 chunk-start states (64 KB per chunk), and
+// the matrix-core backward pass reading them (d = 64, hidden 256, chunk 16, bf16)
+hipError_t launch_mlp_fwd_hist(const MlpArgs& a, void* hist, hipStream_t s);
+bool mlp_bwd_mfma_supported(const MlpBwdArgs& a, bool bf16_io);
+size_t mlp_bwd_mfma_workspace_bytes(const MlpBwdArgs& a);
+hipError_t launch_mlp_bwd_mfma(const MlpBwdArgs& a, const void* ws, hipStream_t s);
 // matrix-core backward (bf16, d = 64, chunk 16): the forward recomputation (fwd: q, k, v, w0,
 // w0_batch_stride, B, H, T, eta) stores the bf16 chunk-start states in the workspace
 bool linear_bwd_mfma_supported(const LinearBwdArgs& a, bool bf16_io);

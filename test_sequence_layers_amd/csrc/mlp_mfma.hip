@@ -281,9 +281,12 @@ __device__ __forceinline__ Ln2 ln2_row(float2_t y, float eps) {
   return {(y - m[0]) * rstd, rstd};
 }
 
-template <bool kDot, bool kPaper>
+// kHist: the state recursion alone (no outputs), storing every chunk-start state as the
+// bf16 values the products use: W1 rows [256][64] then W2 rows [64][256] (64 KB per chunk,
+// chunk c of chain ch at hist + (ch nchunks + c) 64 KB), for the backward pass.
+template <bool kDot, bool kPaper, bool kHist>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void mlp_mfma_kernel(
-    MlpArgs a) {
+    MlpArgs a, char* hist) {
   __shared__ __attribute__((aligned(16))) Lds sh;
   lds_char* opart = (lds_char*)(&sh.opart[0][0][0]);
   lds_char* zpart = (lds_char*)(&sh.zpart[0][0][0]);
@@ -389,6 +392,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int aa = 0; aa < kHT; ++aa) w1b[h][aa] = pair_op(st.w1t[2 * h][aa], st.w1t[2 * h + 1][aa]);
+    char* hc = nullptr;  // this chunk's stored state (kHist)
+    if constexpr (kHist) {
+      hc = hist + (static_cast<size_t>(chain) * nchunks + c) * (2 * kH * kD * 2);
+      // lane: W1[h0 + 16 a + n][16 g + 8 h .. + 7]
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int aa = 0; aa < kHT; ++aa)
+          *reinterpret_cast<u32x4*>(hc + ((h0 + 16 * aa + n) * kD + 16 * g + 8 * h) * 2) =
+              __builtin_bit_cast(u32x4, w1b[h][aa]);
+    }
 
     // U = K W1^T (rows t, hidden tile aa);  A = act(U), S = act'(U)
     float4_t act[kHT], sd[kHT];
@@ -423,6 +437,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const int row = 16 * it + n;
       lds_store<u32x2>(w2lds, w2off(row, g), u32x2{w2op[it].x, w2op[it].y});
       lds_store<u32x2>(w2lds, w2off(row, 4 + g), u32x2{w2op[it].z, w2op[it].w});
+      if constexpr (kHist) {  // W2[16 it + n][h0 + 4 g .. + 3] and [h0 + 16 + 4 g .. + 3]
+        char* w2r = hc + kH * kD * 2 + (row * kH + h0 + 4 * g) * 2;
+        *reinterpret_cast<u32x2*>(w2r) = u32x2{w2op[it].x, w2op[it].y};
+        *reinterpret_cast<u32x2*>(w2r + 32) = u32x2{w2op[it].z, w2op[it].w};
+      }
     }
     // O^T partial = W2 A^T (rows output, cols t): contraction over this wave's 32 hidden
     // (not needed with the dot-product loss, whose error term is -V, unless a layer norm
@@ -437,7 +456,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     barrier();
     // previous chunk's Z (its partials were written before this barrier)
-    if (c > 0) reduce_store_z(c - 1);
+    if (!kHist && c > 0) reduce_store_z(c - 1);
     // -eta_t R = -eta_t (sum of partials - V), to LDS in bf16 as [t][i] and [i][t]
     {
       float2_t s2 = zero2;
@@ -500,35 +519,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 
     // ---- outputs (use the chunk-start state) ----
-    // P^T = K Q^T with the causal mask s <= t, padded B operand
-    float4_t pt = mfma(ka0, qb0, zero);
-    pt = mfma(ka1, qb1, pt);
+    if constexpr (!kHist) {
+      // P^T = K Q^T with the causal mask s <= t, padded B operand
+      float4_t pt = mfma(ka0, qb0, zero);
+      pt = mfma(ka1, qb1, pt);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pt[e] = keep[e] ? pt[e] : 0.0f;
-    const bf16x8_t ptb = pad_op(pt);
-    // U_q^T = W1 Q^T - eta dU^T P^T (rows hidden tile aa, cols t);  A_q^T = act(U_q^T)
-    float4_t aqT[kHT];
+      for (int e = 0; e < 4; ++e) pt[e] = keep[e] ? pt[e] : 0.0f;
+      const bf16x8_t ptb = pad_op(pt);
+      // U_q^T = W1 Q^T - eta dU^T P^T (rows hidden tile aa, cols t);  A_q^T = act(U_q^T)
+      float4_t aqT[kHT];
 #pragma unroll
-    for (int aa = 0; aa < kHT; ++aa) {
-      float4_t u = mfma(w1b[0][aa], qb0, zero);
-      u = mfma(w1b[1][aa], qb1, u);
-      u = mfma(dub[aa], ptb, u);
+      for (int aa = 0; aa < kHT; ++aa) {
+        float4_t u = mfma(w1b[0][aa], qb0, zero);
+        u = mfma(w1b[1][aa], qb1, u);
+        u = mfma(dub[aa], ptb, u);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) u[e] = act_only<kPaper>(u[e]);
-      aqT[aa] = u;
-    }
-    const bf16x8_t aqb = cat_op(aqT[0], aqT[1]);
-    // G^T = A A_q^T (rows s, cols t) over this wave's hidden units, masked s <= t
-    float4_t gt = mfma(atb, aqb, zero);
+        for (int e = 0; e < 4; ++e) u[e] = act_only<kPaper>(u[e]);
+        aqT[aa] = u;
+      }
+      const bf16x8_t aqb = cat_op(aqT[0], aqT[1]);
+      // G^T = A A_q^T (rows s, cols t) over this wave's hidden units, masked s <= t
+      float4_t gt = mfma(atb, aqb, zero);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) gt[e] = keep[e] ? gt[e] : 0.0f;
-    const bf16x8_t gtb = pad_op(gt);
-    // Z^T partial = W2 A_q^T + (-eta R)^T G^T (rows output tile it, cols t)
+      for (int e = 0; e < 4; ++e) gt[e] = keep[e] ? gt[e] : 0.0f;
+      const bf16x8_t gtb = pad_op(gt);
+      // Z^T partial = W2 A_q^T + (-eta R)^T G^T (rows output tile it, cols t)
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      float4_t zt = mfma(bf(w2op[it]), aqb, zero);
-      zt = mfma(rb[it], gtb, zt);
-      lds_store<float4_t>(zpart, ((wv * kB + n) * kRow + 16 * it + 4 * g) * 4, zt);
+      for (int it = 0; it < 4; ++it) {
+        float4_t zt = mfma(bf(w2op[it]), aqb, zero);
+        zt = mfma(rb[it], gtb, zt);
+        lds_store<float4_t>(zpart, ((wv * kB + n) * kRow + 16 * it + 4 * g) * 4, zt);
+      }
     }
 
     // ---- state update (sum of the chunk's gradients) ----
@@ -557,7 +578,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     ca = cb;
   }
   barrier();
-  if (nchunks > 0) reduce_store_z(nchunks - 1);
+  if (!kHist && nchunks > 0) reduce_store_z(nchunks - 1);
 
   // ---- final state ----
   if (a.w1_out) {
@@ -605,13 +626,22 @@ hipError_t launch_mlp_fast(const MlpArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(nchains)), block(kThreads);
   const bool paper = a.ln_w != nullptr;  // the paper's TTT-MLP: GELU, LN and residual
   if (paper && a.dot_loss)
-    hipLaunchKernelGGL((mlp_mfma_kernel<true, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((mlp_mfma_kernel<true, true, false>), grid, block, 0, s, a, nullptr);
   else if (paper)
-    hipLaunchKernelGGL((mlp_mfma_kernel<false, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((mlp_mfma_kernel<false, true, false>), grid, block, 0, s, a, nullptr);
   else if (a.dot_loss)
-    hipLaunchKernelGGL((mlp_mfma_kernel<true, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((mlp_mfma_kernel<true, false, false>), grid, block, 0, s, a, nullptr);
   else
-    hipLaunchKernelGGL((mlp_mfma_kernel<false, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((mlp_mfma_kernel<false, false, false>), grid, block, 0, s, a, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_mlp_fwd_hist(const MlpArgs& a, void* hist, hipStream_t s) {
+  const long long nchains = static_cast<long long>(a.B) * a.H;
+  if (nchains > 0x7fffffffLL || a.ln_w != nullptr || a.dot_loss || a.eta_tok != nullptr)
+    return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(nchains)), block(kThreads);
+  hipLaunchKernelGGL((mlp_mfma_kernel<false, false, true>), grid, block, 0, s, a, static_cast<char*>(hist));
   return hipGetLastError();
 }
 

@@ -313,20 +313,34 @@ int ttt_mlp_bwd(const void* q, const void* k, const void* v, const float* w1, co
   const long long nchunks = (T + b - 1) / b;
   if (!fits_int64(B, H, nchunks, 2LL * static_cast<long long>(per)))
     return fail(TTT_E_INVALID, "ttt_mlp_bwd: state history overflows");
+  const bool bf16 = io_dtype == TTT_BF16;
+  ttt::MlpBwdArgs g{q, k, v, dz, dw1_out, dw2_out, nullptr, dq, dk, dv,
+                    dw1, dw2, B, H, T, d, dh, chunk, eta};
+  ttt::MlpArgs f{q, k, v, w1, w2, w_batch_stride, nullptr, nullptr, nullptr,
+                 B, H, T, d, dh, chunk, 1, eta, nullptr, 0};
+  hipError_t e;
+  if (ttt::mlp_bwd_mfma_supported(g, bf16) && ttt::mlp_fast_supported(f, bf16)) {
+    // matrix cores: the forward pass stores its bf16 chunk-start states, the backward pass
+    // reads them
+    StreamBuffer hist;
+    rc = get_workspace(ttt::mlp_bwd_mfma_workspace_bytes(g), s, &hist);
+    if (rc != TTT_OK) return rc;
+    e = ttt::launch_mlp_fwd_hist(f, hist.ptr, s);
+    if (e != hipSuccess) return hip_fail(e, "ttt_mlp_bwd state launch");
+    e = ttt::launch_mlp_bwd_mfma(g, hist.ptr, s);
+    if (e != hipSuccess) return hip_fail(e, "ttt_mlp_bwd launch");
+    return TTT_OK;
+  }
   // forward recomputation on the generic kernel, storing the chunk-start states
   StreamBuffer hist, fws;
   rc = get_workspace(static_cast<size_t>(B) * H * nchunks * 2 * per * sizeof(float), s, &hist);
   if (rc != TTT_OK) return rc;
-  ttt::MlpArgs f{q, k, v, w1, w2, w_batch_stride, nullptr, nullptr, nullptr,
-                 B, H, T, d, dh, chunk, 1, eta, nullptr, 0};
   f.w_hist = static_cast<float*>(hist.ptr);
   rc = get_workspace(ttt::mlp_generic_workspace_floats(f) * sizeof(float), s, &fws);
   if (rc != TTT_OK) return rc;
-  const bool bf16 = io_dtype == TTT_BF16;
-  hipError_t e = ttt::launch_mlp_generic(f, bf16, static_cast<float*>(fws.ptr), s);
+  e = ttt::launch_mlp_generic(f, bf16, static_cast<float*>(fws.ptr), s);
   if (e != hipSuccess) return hip_fail(e, "ttt_mlp_bwd state launch");
-  ttt::MlpBwdArgs g{q, k, v, dz, dw1_out, dw2_out, static_cast<const float*>(hist.ptr), dq, dk, dv,
-                    dw1, dw2, B, H, T, d, dh, chunk, eta};
+  g.w_hist = static_cast<const float*>(hist.ptr);
   e = ttt::launch_mlp_bwd_generic(g, bf16, s);
   if (e != hipSuccess) return hip_fail(e, "ttt_mlp_bwd launch");
   return TTT_OK;
