@@ -73,9 +73,6 @@ constexpr int kHistBytes = kW1Bytes + kD * kRow2;  // one chunk's two states
 constexpr int kTileBytes = kB * kRow1;
 constexpr int kQ = 0, kK = kTileBytes, kZ = 2 * kTileBytes;
 constexpr int kChunkBytes = 3 * kTileBytes;
-constexpr int kOStride = 20;  // floats per output row of the O^T sums [i][t]
-constexpr int kTStride = 68;  // floats per token row of the [t][.] sums
-static_assert(kB * kTStride <= kD * kOStride, "the dR sums share the O sums' array");
 
 // One chunk's inputs: its two states and its Q, K, dZ tiles.  The two buffers are separate
 // LDS objects, so that the compiler can tell a read of one from the loads into the other.
@@ -83,12 +80,12 @@ struct Buf {
   char hist[kHistBytes];
   char chunk[kChunkBytes];
 };
+// Cross-wave sums: red[s][tile][lane], four slots of four C-layout tiles, lane-major (also
+// the exchange of the waves' A^T operands, xch[wave][lane], in its first 8 KB).
 struct Lds {
-  float acc[kD * kOStride];    // O^T sums, then dR sums
-  float accq[kB * kTStride];   // dQ sums
-  float acck[kB * kTStride];   // dK sums
-  char rb[kTileBytes];         // R, bf16 rows
-  char drb[kTileBytes];        // dR, bf16 rows
+  float4_t red[4][4][64];
+  char rb[kTileBytes];   // R, bf16 rows
+  char drb[kTileBytes];  // dR, bf16 rows
 };
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
@@ -185,17 +182,25 @@ __device__ __forceinline__ u32x2 trd(const lds_char* b, int row, int col) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + so<kRowB>(row, col))));
 }
 
+// Compiler-only fence: LDS values read before it are read again after it instead of being
+// held in registers (register pressure).
+__device__ __forceinline__ void reread() { __asm__ __volatile__("" ::: "memory"); }
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
-// Barrier for LDS traffic only (the fence of __syncthreads() would drain outstanding stores).
+// Barrier for LDS traffic only (the fence of __syncthreads() would drain outstanding stores);
+// no instruction is scheduled across it (which keeps each phase's values out of the others'
+// register budgets).
 __device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   __asm__ __volatile__("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 __global__ __launch_bounds__(kThreads) void mlp_bwd_mfma_kernel(MlpBwdArgs a, const char* hist) {
@@ -225,27 +230,9 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_mfma_kernel(MlpBwdArgs a, co
   char* dv = reinterpret_cast<char*>(static_cast<bf16*>(a.dv) + tok0);
   const char* hch = hist + static_cast<size_t>(chain) * nchunks * kHistBytes;
 
-  for (int i = tid; i < kD * kOStride; i += kThreads) sh.acc[i] = 0.0f;
-  for (int i = tid; i < kB * kTStride; i += kThreads) {
-    sh.accq[i] = 0.0f;
-    sh.acck[i] = 0.0f;
-  }
 
   const int h0 = 32 * wv;
-  const uint32_t one = 0x3F80u;  // bf16 1.0
-  const bf16x8_t eye = pad2(u32x2{(4 * g_ + 0 == n_ ? one : 0u) | (4 * g_ + 1 == n_ ? one << 16 : 0u),
-                                  (4 * g_ + 2 == n_ ? one : 0u) | (4 * g_ + 3 == n_ ? one << 16 : 0u)});
-  // C-layout masks: keep = row 4 g + e <= column n; keepT = column n <= row 4 g + e
-  bool keep[4], keepT[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    keep[e] = 4 * g_ + e <= n_;
-    keepT[e] = n_ <= 4 * g_ + e;
-  }
   const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-  auto tp = [&](const float4_t& x) { return mfma(pad2(pack4(x)), eye, zero); };  // transpose of a tile
-  const int rt = tid >> 5;        // finishing role: token row rt, features ri, ri + 1
-  const int ri = 2 * (tid & 31);
 
   // ---- G1, G2 (from the caller's gradients of the final states, or zero) ----
   const size_t hd = static_cast<size_t>(kH) * kD;
@@ -265,15 +252,32 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_mfma_kernel(MlpBwdArgs a, co
         g2t[aa][it] = i2 ? *reinterpret_cast<const float4_t*>(i2 + (16 * it + n_) * kH + h0 + 16 * aa + 4 * g_) : zero;
   }
 
-  // dQ and dK of chunk cc from their sums (finishing role), clearing the sums
-  auto store_qk = [&](int cc) {
-    const int o = cc * kTileBytes;
-    const float2_t sq = *reinterpret_cast<const float2_t*>(&sh.accq[rt * kTStride + ri]);
-    const float2_t sk = *reinterpret_cast<const float2_t*>(&sh.acck[rt * kTStride + ri]);
-    *reinterpret_cast<float2_t*>(&sh.accq[rt * kTStride + ri]) = float2_t{0.0f, 0.0f};
-    *reinterpret_cast<float2_t*>(&sh.acck[rt * kTStride + ri]) = float2_t{0.0f, 0.0f};
-    __builtin_amdgcn_raw_buffer_store_b32(pack_bf16(sq[0], sq[1]), rsrc(dq + o, seq_bytes - o), rt * kRow1 + 2 * ri, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b32(pack_bf16(sk[0], sk[1]), rsrc(dk + o, seq_bytes - o), rt * kRow1 + 2 * ri, 0, 0);
+  u32x4* const xch = reinterpret_cast<u32x4*>(&sh.red[0][0][0]);
+  // Sum over the 8 waves of four C-layout tiles x (every wave calls it): waves 4..7 store,
+  // waves 0..3 add their partner's and store; then slot s holds the sum of waves s, s + 4,
+  // and wave w < 4 finishes tile w with sum4().
+  // (lane indices below come from an opaque copy: recomputed, not held in registers)
+  auto opaque_lane = [&]() {
+    int ln = lane;
+    __asm__ volatile("" : "+v"(ln));
+    return ln;
+  };
+  auto reduce8 = [&](float4_t (&x)[4]) {
+    const int ln = opaque_lane();
+    if (wv >= 4) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) sh.red[wv - 4][t][ln] = x[t];
+    }
+    lds_barrier();
+    if (wv < 4) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) sh.red[wv][t][ln] = x[t] + sh.red[wv][t][ln];
+    }
+    lds_barrier();
+  };
+  auto sum4 = [&]() {
+    const int ln = opaque_lane();
+    return sh.red[0][wv][ln] + sh.red[1][wv][ln] + sh.red[2][wv][ln] + sh.red[3][wv][ln];
   };
 
   // This wave's share of the loads of chunk c into buffer b: W1 rows 32 w .. 32 w + 31,
@@ -281,16 +285,19 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_mfma_kernel(MlpBwdArgs a, co
   // LDS loads (1 KB each: lane l fills physical piece l % 8 of row l / 8, or piece l % 32 of
   // row l / 32 in W2, with the row's logical piece under the swizzle; rows past T read as
   // zero).
-  const int r8 = lane >> 3;
-  const int src8 = r8 * kRow1 + 16 * ((lane & 7) ^ swz(r8));
   auto issue = [&](Buf& b, int c) {
+    // (offsets from an opaque copy of the lane index: recomputed here, not held in registers)
+    int ln = lane;
+    __asm__ volatile("" : "+v"(ln));
+    const int r8 = ln >> 3;
+    const int src8 = r8 * kRow1 + 16 * ((ln & 7) ^ swz(r8));
     const lds_char* hb = (const lds_char*)(&b.hist[0]);
     const u32x4 dh = desc(hch + static_cast<size_t>(c) * kHistBytes, kHistBytes);
 #pragma unroll
     for (int m = 4 * wv; m < 4 * wv + 4; ++m) {
       dma16(dh, hb + 1024 * m, src8 + 1024 * m);
-      const int row = 2 * m + (lane >> 5);
-      dma16(dh, hb + kW1Bytes + 1024 * m, kW1Bytes + row * kRow2 + 16 * ((lane & 31) ^ swz(row)));
+      const int row = 2 * m + (ln >> 5);
+      dma16(dh, hb + kW1Bytes + 1024 * m, kW1Bytes + row * kRow2 + 16 * ((ln & 31) ^ swz(row)));
     }
     const int off = c * kTileBytes, m = wv & 1;
     const lds_char* cb = (const lds_char*)(&b.chunk[0]) + 1024 * m;
@@ -301,17 +308,31 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_mfma_kernel(MlpBwdArgs a, co
     else if (wv < 6)
       dma16(desc(dz + off, seq_bytes - off), cb + kZ, src8 + 1024 * m);
   };
-  auto load_v = [&](int c) {  // V at the finishing role's place
+  // V at this lane's place of output tile w % 4: V[n][16 (w % 4) + 4 g .. + 3]
+  auto load_v = [&](int c) {
+    int ln = lane;
+    __asm__ volatile("" : "+v"(ln));
     const int off = c * kTileBytes;
-    return __builtin_amdgcn_raw_buffer_load_b32(rsrc(v + off, seq_bytes - off), rt * kRow1 + 2 * ri, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b64(rsrc(v + off, seq_bytes - off), (ln & 15) * kRow1 + 32 * (wv & 3) + 8 * (ln >> 4), 0, 0);
   };
 
   // One chunk: its inputs in rd (V in vv), the next chunk's loads into wr (V into vv).
-  auto run = [&](Buf& rd, Buf& wr, int c, uint32_t& vv_io) {
+  auto run = [&](Buf& rd, Buf& wr, int c, u32x2& vv_io) {
     // the lane's coordinates, opaque to the compiler here: the many LDS offsets derived from
     // them are recomputed each chunk (a few ALU operations) instead of held in registers
     int g = g_, n = n_;
     __asm__ volatile("" : "+v"(g), "+v"(n));
+    const uint32_t one = 0x3F80u;  // bf16 1.0
+    const bf16x8_t eye = pad2(u32x2{(4 * g + 0 == n ? one : 0u) | (4 * g + 1 == n ? one << 16 : 0u),
+                                    (4 * g + 2 == n ? one : 0u) | (4 * g + 3 == n ? one << 16 : 0u)});
+    auto tp = [&](const float4_t& x) { return mfma(pad2(pack4(x)), eye, zero); };  // transpose of a tile
+    // C-layout masks: keep = row 4 g + e <= column n; keepT = column n <= row 4 g + e
+    bool keep[4], keepT[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      keep[e] = 4 * g + e <= n;
+      keepT[e] = n <= 4 * g + e;
+    }
     const lds_char* W1s = (const lds_char*)(&rd.hist[0]);
     const lds_char* W2s = W1s + kW1Bytes;
     const lds_char* Qs = (const lds_char*)(&rd.chunk[0]) + kQ;
@@ -320,7 +341,7 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_mfma_kernel(MlpBwdArgs a, co
     const int off = c * kTileBytes;
     wait_vmcnt<0>();  // this wave's loads of chunk c
     lds_barrier();    // B0: chunk c is in rd; wr is free
-    const uint32_t vv = vv_io;
+    const u32x2 vv = vv_io;
     if (c > 0) {
       issue(wr, c - 1);
       vv_io = load_v(c - 1);
@@ -348,15 +369,7 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_mfma_kernel(MlpBwdArgs a, co
       }
     }
     const bf16x8_t atb = cat_op(at[0], at[1]);  // A rows t over hidden / A^T over hidden
-    // O^T (rows i, cols t) = W2 A^T, summed over the waves
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int r = 16 * it + n;
-      const bf16x8_t w2 = join2(rd8<kRow2>(W2s, r, h0 + 4 * g), rd8<kRow2>(W2s, r, h0 + 16 + 4 * g));
-      const float4_t ot = mfma(w2, atb, zero);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) atomicAdd(&sh.acc[(16 * it + 4 * g + e) * kOStride + n], ot[e]);
-    }
+    xch[wv * 64 + 16 * g + n] = __builtin_bit_cast(u32x4, atb);  // for O = A W2^T over all hidden units
     u32x2 ab[2];  // A with token rows (operand over tokens)
 #pragma unroll
     for (int aa = 0; aa < 2; ++aa) ab[aa] = pack4(tp(at[aa]));
@@ -377,15 +390,21 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_mfma_kernel(MlpBwdArgs a, co
     }
     lds_barrier();  // B1
 
-    // ---- R = O - V to bf16 rows; dQ, dK of chunk c + 1 ----
-    {
-      float* o0 = &sh.acc[ri * kOStride + rt];
-      float* o1 = &sh.acc[(ri + 1) * kOStride + rt];
-      const float r0 = *o0 - bf_lo(vv), r1 = *o1 - bf_hi(vv);
-      *o0 = 0.0f;
-      *o1 = 0.0f;
-      lds_st<uint32_t>(rbl + so<kRow1>(rt, ri), pack_bf16(r0, r1));
-      if (c + 1 < nchunks) store_qk(c + 1);
+    // ---- waves 0..3: O^T tile w (rows i = 16 w + 4 g + e, cols t) = W2 A^T over all 256
+    // hidden units (A^T operands of every wave); R = O - V to bf16 rows ----
+    if (wv < 4) {
+      float4_t x0 = zero, x1 = zero;
+#pragma unroll
+      for (int w = 0; w < kWaves; w += 2) {
+        const int r = 16 * wv + n;
+        x0 = mfma(join2(rd8<kRow2>(W2s, r, 32 * w + 4 * g), rd8<kRow2>(W2s, r, 32 * w + 16 + 4 * g)),
+                  bf(xch[w * 64 + 16 * g + n]), x0);
+        x1 = mfma(join2(rd8<kRow2>(W2s, r, 32 * w + 32 + 4 * g), rd8<kRow2>(W2s, r, 32 * w + 48 + 4 * g)),
+                  bf(xch[(w + 1) * 64 + 16 * g + n]), x1);
+      }
+      const float4_t o = x0 + x1;
+      const u32x2 rp = {pack_bf16(o[0] - bf_lo(vv.x), o[1] - bf_hi(vv.x)), pack_bf16(o[2] - bf_lo(vv.y), o[3] - bf_hi(vv.y))};
+      lds_st<u32x2>(rbl + so<kRow1>(n, 16 * wv + 4 * g), rp);
     }
     lds_barrier();  // B2
 
@@ -437,11 +456,13 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_mfma_kernel(MlpBwdArgs a, co
       nnb = pack4(nn, -eta);  // operand -eta N^T (rows s over t)
     }
     // Nb^T (rows s, cols t) and Nb (rows t, cols s) = -eta tril(dZ R^T)
+    reread();
+    const u32x4 rn0b = rd16<kRow1>(rbl, n, 8 * g), rn1b = rd16<kRow1>(rbl, n, 32 + 8 * g);
     const u32x4 zn0 = rd16<kRow1>(Zs, n, 8 * g), zn1 = rd16<kRow1>(Zs, n, 32 + 8 * g);
     u32x2 nbtb, nbb;
     {
-      float4_t nbt = mfma(bf(rn1), bf(zn1), mfma(bf(rn0), bf(zn0), zero));
-      float4_t nb = mfma(bf(zn1), bf(rn1), mfma(bf(zn0), bf(rn0), zero));
+      float4_t nbt = mfma(bf(rn1b), bf(zn1), mfma(bf(rn0b), bf(zn0), zero));
+      float4_t nb = mfma(bf(zn1), bf(rn1b), mfma(bf(zn0), bf(rn0b), zero));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         nbt[e] = keep[e] ? nbt[e] : 0.0f;
@@ -455,8 +476,9 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_mfma_kernel(MlpBwdArgs a, co
 #pragma unroll
     for (int aa = 0; aa < 2; ++aa) {
       float4_t x = mfma(pad2(nbtb), pad2(ab[aa]), zero);
-      x = mfma(bf(zn0), w2k(aa, 0), x);
-      x = mfma(bf(zn1), w2k(aa, 1), x);
+      reread();
+      x = mfma(bf(rd16<kRow1>(Zs, n, 8 * g)), w2k(aa, 0), x);
+      x = mfma(bf(rd16<kRow1>(Zs, n, 32 + 8 * g)), w2k(aa, 1), x);
       duqb[aa] = pack4(x * sqt[aa]);
     }
     const bf16x8_t duqc = cat_op(mfma(pad2(duqb[0]), eye, zero), mfma(pad2(duqb[1]), eye, zero));
@@ -491,30 +513,28 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_mfma_kernel(MlpBwdArgs a, co
     u32x2 ddsb[2];  // ddU phi'(U) with token rows
 #pragma unroll
     for (int aa = 0; aa < 2; ++aa) ddsb[aa] = pack4(tp(dds[aa]));
-    // ---- dR (rows s, cols i) = -eta N^T dZ - eta A G2^T + (ddU phi') W2^T, summed ----
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int r = 16 * it + n;
-      const bf16x8_t w2 = join2(rd8<kRow2>(W2s, r, h0 + 4 * g), rd8<kRow2>(W2s, r, h0 + 16 + 4 * g));
-      const u32x2 ztr = trd<kRow1>(Zs, 4 * g + (n >> 2), 16 * it + 4 * (n & 3));
-      float4_t x = mfma(pad2(nnb), pad2(ztr), zero);
-      x = mfma(atb, cat_op(g2t[0][it], g2t[1][it], -eta), x);
-      x = mfma(ddsc, w2, x);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) atomicAdd(&sh.acc[(4 * g + e) * kTStride + 16 * it + n], x[e]);
-    }
-    lds_barrier();  // B3
-
-    // ---- dR to bf16 rows; dV = -dR ----
+    // ---- dR^T (rows i, cols s) = -eta dZ^T N - eta G2 A^T + W2 (ddU phi')^T, summed ----
     {
-      float2_t* p = reinterpret_cast<float2_t*>(&sh.acc[rt * kTStride + ri]);
-      const float2_t d2 = *p;
-      *p = float2_t{0.0f, 0.0f};
-      lds_st<uint32_t>(drbl + so<kRow1>(rt, ri), pack_bf16(d2[0], d2[1]));
-      __builtin_amdgcn_raw_buffer_store_b32(pack_bf16(-d2[0], -d2[1]), rsrc(dv + off, seq_bytes - off),
-                                            rt * kRow1 + 2 * ri, 0, 0);
+      float4_t x[4];
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int r = 16 * it + n;
+        const bf16x8_t w2 = join2(rd8<kRow2>(W2s, r, h0 + 4 * g), rd8<kRow2>(W2s, r, h0 + 16 + 4 * g));
+        const u32x2 ztr = trd<kRow1>(Zs, 4 * g + (n >> 2), 16 * it + 4 * (n & 3));
+        x[it] = mfma(pad2(ztr), pad2(nnb), zero);
+        x[it] = mfma(cat_op(g2t[0][it], g2t[1][it], -eta), atb, x[it]);
+        x[it] = mfma(w2, ddsc, x[it]);
+      }
+      reduce8(x);
     }
-    lds_barrier();  // B4
+    // ---- waves 0..3: dR[t][16 w + 4 g .. + 3] to bf16 rows; dV = -dR ----
+    if (wv < 4) {
+      const float4_t d4 = sum4();
+      lds_st<u32x2>(drbl + so<kRow1>(n, 16 * wv + 4 * g), pack4(d4));
+      __builtin_amdgcn_raw_buffer_store_b64(pack4(d4, -1.0f), rsrc(dv + off, seq_bytes - off),
+                                            n * kRow1 + 32 * wv + 8 * g, 0, 0);
+    }
+    lds_barrier();  // dR rows complete
 
     // ---- dA^T (rows hidden, cols t) = Aq^T Nb - eta G2^T R^T + W2^T dR^T;  dUk^T ----
     const u32x4 drn0 = rd16<kRow1>(drbl, n, 8 * g), drn1 = rd16<kRow1>(drbl, n, 32 + 8 * g);
@@ -536,32 +556,7 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_mfma_kernel(MlpBwdArgs a, co
     u32x2 dukb[2];  // dUk with token rows
 #pragma unroll
     for (int aa = 0; aa < 2; ++aa) dukb[aa] = pack4(tp(dukt[aa]));
-    // ---- dQ (rows t) = dUq W1 + Mb K;  dK (rows s) = Mb^T Q - eta dU G1 + dUk W1, summed ----
-#pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-      const int col = 16 * jt + 4 * (n & 3);
-      const bf16x8_t w1h = join2(trd<kRow1>(W1s, h0 + 4 * g + (n >> 2), col), trd<kRow1>(W1s, h0 + 16 + 4 * g + (n >> 2), col));
-      const u32x2 ktr = trd<kRow1>(Ks, 4 * g + (n >> 2), col);
-      const u32x2 qtr = trd<kRow1>(Qs, 4 * g + (n >> 2), col);
-      float4_t xq = mfma(duqc, w1h, zero);
-      xq = mfma(pad2(mbtb), pad2(ktr), xq);
-      float4_t xk = mfma(pad2(mbb), pad2(qtr), zero);
-      xk = mfma(duc, cat_op(tp(g1t[jt][0]), tp(g1t[jt][1]), -eta), xk);
-      xk = mfma(dukc, w1h, xk);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        atomicAdd(&sh.accq[(4 * g + e) * kTStride + 16 * jt + n], xq[e]);
-        atomicAdd(&sh.acck[(4 * g + e) * kTStride + 16 * jt + n], xk[e]);
-      }
-    }
-    // ---- G1^T += Q^T dUq + K^T dUk;  G2^T += Aq^T dZ + (ddU phi')^T R + A^T dR ----
-#pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-      const int col = 16 * jt + 4 * (n & 3);
-      const bf16x8_t qk = join2(trd<kRow1>(Qs, 4 * g + (n >> 2), col), trd<kRow1>(Ks, 4 * g + (n >> 2), col));
-#pragma unroll
-      for (int aa = 0; aa < 2; ++aa) g1t[jt][aa] = mfma(qk, join2(duqb[aa], dukb[aa]), g1t[jt][aa]);
-    }
+    // ---- G2^T += Aq^T dZ + (ddU phi')^T R + A^T dR (G2 has had its last use) ----
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int col = 16 * it + 4 * (n & 3);
@@ -574,18 +569,57 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_mfma_kernel(MlpBwdArgs a, co
         g2t[aa][it] = mfma(pad2(ab[aa]), pad2(drtr), g2t[aa][it]);
       }
     }
+    // ---- dQ^T (rows j, cols t) = W1^T dUq^T + K^T Mb^T, summed; waves 0..3 store
+    // dQ[t][16 w + 4 g .. + 3] ----
+    {
+      float4_t x[4];
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        const int col = 16 * jt + 4 * (n & 3);
+        const bf16x8_t w1h = join2(trd<kRow1>(W1s, h0 + 4 * g + (n >> 2), col), trd<kRow1>(W1s, h0 + 16 + 4 * g + (n >> 2), col));
+        x[jt] = mfma(w1h, duqc, zero);
+        x[jt] = mfma(pad2(trd<kRow1>(Ks, 4 * g + (n >> 2), col)), pad2(mbtb), x[jt]);
+      }
+      reduce8(x);
+      if (wv < 4)
+        __builtin_amdgcn_raw_buffer_store_b64(pack4(sum4()), rsrc(dq + off, seq_bytes - off), n * kRow1 + 32 * wv + 8 * g, 0, 0);
+      lds_barrier();  // the dQ sums are read
+    }
+    // ---- dK^T (rows j, cols s) = Q^T Mb - eta G1^T dU^T + W1^T dUk^T (G1 before this
+    // chunk's update), summed; waves 0..3 store dK ----
+    {
+      float4_t x[4];
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        const int col = 16 * jt + 4 * (n & 3);
+        const bf16x8_t w1h = join2(trd<kRow1>(W1s, h0 + 4 * g + (n >> 2), col), trd<kRow1>(W1s, h0 + 16 + 4 * g + (n >> 2), col));
+        x[jt] = mfma(pad2(trd<kRow1>(Qs, 4 * g + (n >> 2), col)), pad2(mbb), zero);
+        x[jt] = mfma(cat_op(tp(g1t[jt][0]), tp(g1t[jt][1]), -eta), duc, x[jt]);
+        x[jt] = mfma(w1h, dukc, x[jt]);
+        __builtin_amdgcn_sched_barrier(0);  // one tile at a time (register pressure)
+      }
+      reduce8(x);
+      if (wv < 4)
+        __builtin_amdgcn_raw_buffer_store_b64(pack4(sum4()), rsrc(dk + off, seq_bytes - off), n * kRow1 + 32 * wv + 8 * g, 0, 0);
+    }
+    // ---- G1^T += Q^T dUq + K^T dUk ----
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      const int col = 16 * jt + 4 * (n & 3);
+      const bf16x8_t qk = join2(trd<kRow1>(Qs, 4 * g + (n >> 2), col), trd<kRow1>(Ks, 4 * g + (n >> 2), col));
+#pragma unroll
+      for (int aa = 0; aa < 2; ++aa) g1t[jt][aa] = mfma(qk, join2(duqb[aa], dukb[aa]), g1t[jt][aa]);
+    }
   };
 
   issue(buf0, nchunks - 1);
-  uint32_t vv = load_v(nchunks - 1);
+  u32x2 vv = load_v(nchunks - 1);
   // chunks from last to first, alternating buffers (step s holds chunk nchunks - 1 - s in
   // buf0 for even s, buf1 for odd s)
   for (int s = 0; s < nchunks; s += 2) {
     run(buf0, buf1, nchunks - 1 - s, vv);
     if (s + 1 < nchunks) run(buf1, buf0, nchunks - 2 - s, vv);
   }
-  lds_barrier();  // end
-  store_qk(0);
 
   // ---- dL/dW1, dL/dW2 of the initial states ----
   float* o1 = a.dw1 + chain * hd;
