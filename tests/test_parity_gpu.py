@@ -519,6 +519,20 @@ def test_mlp_bwd_bf16_h256(T, with_dw):
     _check_mlp_bwd(w, make_inputs(w), with_dw, seed=T)
 
 
+@pytest.mark.parametrize("T,with_dw,per_batch,eta", [(77, True, True, 0.1), (33, False, False, 0.3),
+                                                     (200, True, False, 0.1)])
+def test_mlp_bwd_bf16_matrix_core_cases(T, with_dw, per_batch, eta):
+    # the matrix-core backward (and its history-mode forward) with [B, H, h, d] / [B, H, d, h]
+    # initial states, no upstream state gradient, ragged last chunks and a larger rate
+    w = workload(3).replace(B=2, H=2, T=T, eta=eta, seed=540 + T)
+    inp = make_inputs(w)
+    if per_batch:
+        rng = np.random.default_rng(541)
+        inp["w1"] = (0.02 * rng.standard_normal((w.B, w.H, w.h, w.d))).astype(np.float32)
+        inp["w2"] = (0.02 * rng.standard_normal((w.B, w.H, w.d, w.h))).astype(np.float32)
+    _check_mlp_bwd(w, inp, with_dw, seed=T + 3)
+
+
 def test_mlp_bwd_config_full_size_sampled():
     w = workload(3)
     _check_mlp_bwd(w, make_inputs(w), True, sel=[(3, 7)], seed=2)
