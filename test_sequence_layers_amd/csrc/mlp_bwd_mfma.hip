@@ -20,14 +20,17 @@
 // which stores them as the bf16 values its products use (W1 rows [256][64], then W2 rows
 // [64][256]: 64 KB per chunk); rows past T are zero everywhere and add nothing.
 //
-// Mapping.  One workgroup per (batch, head) chain walks the chunks from last to first:
-//   * 8 compute waves; wave w owns hidden units 32 w .. 32 w + 31 and keeps its rows of G1
-//     and columns of G2 in fp32 accumulator tiles;
-//   * 2 loader waves stream each chunk's two states and its Q, K, dZ tiles into LDS with
-//     direct-to-LDS loads, one chunk ahead (two buffers);
-//   * sums over hidden units (O for R, then dR, dQ, dK) are LDS float atomics of the
-//     waves' partial products into fp32 arrays, finished by all threads after a barrier
-//     (R and dR also to bf16 rows in LDS).  Five barriers per chunk.
+// Mapping.  One workgroup of 8 waves per (batch, head) chain walks the chunks from last to
+// first:
+//   * wave w owns hidden units 32 w .. 32 w + 31 and keeps its rows of G1 and columns of G2
+//     in fp32 accumulator tiles;
+//   * each wave loads its share of the next chunk's two states and Q, K, dZ tiles into the
+//     other of two LDS buffers with direct-to-LDS loads;
+//   * sums over hidden units: O = A W2^T is formed whole by waves 0..3 (one output tile
+//     each) from the bf16 A^T operands all waves exchange through LDS; dR, dQ and dK, which
+//     hold terms with the per-wave G slices, are summed from per-wave partial tiles in pairs
+//     (waves 4..7 store, waves 0..3 add, then sum the four slots).  R and dR go to bf16 rows
+//     in LDS.  Ten barriers per chunk.
 //
 // Layouts (v_mfma_f32_16x16x32_bf16; C layout: lane (g, n) = (lane / 16, lane % 16) holds
 // rows 4 g + e, e = 0..3, of column n; A operand: lane holds A[n][8 g + s]; B: B[8 g + s][n]):
@@ -134,9 +137,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int byt
 }
 
 // 16 bytes per lane, global -> LDS (M0 = the wave's 1 KB destination block), issued from
-// inline assembly: the compiler's wait insertion does not see these loads, which would make
-// every LDS atomic wait for them; their completion is awaited explicitly (vmcnt) before the
-// barrier that publishes them.  One wait state separates the M0 write from its use.
+// inline assembly so that the compiler's wait insertion does not see them (for the builtin
+// it makes every LDS access it cannot prove disjoint, atomics included, wait for all
+// outstanding loads); their completion is awaited explicitly (vmcnt) before the barrier that
+// publishes them.  One wait state separates the M0 write from its use.
 __device__ __forceinline__ u32x4 desc(const void* base, int bytes) {
   const uint64_t p = reinterpret_cast<uint64_t>(base);
   return u32x4{static_cast<uint32_t>(p), static_cast<uint32_t>(p >> 32) & 0xFFFFu,
