@@ -46,11 +46,11 @@ def algorithmic_cost(w, epochs=1):
     return 4 * tok + state, fl
 
 
-def measured_traffic(workload_name):
-    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE for the kernel of
-    this workload, or None when no record exists or the kernel source has changed since."""
+def _profile_record(workload_name, kind):
+    """A committed rocprofv3 counter record (profiles/<workload>_<kind>.json), or None when
+    none exists or the kernel source has changed since it was taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"{workload_name}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{workload_name}_{kind}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -61,7 +61,21 @@ def measured_traffic(workload_name):
     with open(src, "rb") as f:
         if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
             return None
-    return rec["fetch_bytes"] + rec["write_bytes"]
+    return rec
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE for the kernel of
+    this workload, or None when no record exists or the kernel source has changed since."""
+    rec = _profile_record(workload_name, "traffic")
+    return None if rec is None else rec["fetch_bytes"] + rec["write_bytes"]
+
+
+def measured_mfma_util(workload_name):
+    """MFMA utilisation (%) of this workload's kernel from the rocprofv3 derived counter
+    MfmaUtil (matrix-core busy cycles over active cycles of all SIMDs), or None."""
+    rec = _profile_record(workload_name, "mfma")
+    return None if rec is None else rec["mfma_util_pct"]
 
 
 def make_device_inputs(w, seed, torch, rates=False, paper=False):
@@ -260,7 +274,7 @@ def main():
             "peak": BF16_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(res["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4),
-            "traffic": measured_traffic(w.name),
+            "traffic": None if args.token_rates else measured_traffic(w.name),
             "kernel": f"{kern} (per launch: the method's flops, tril products at half)",
             "flops_per_launch": res["flops"],
         }
@@ -273,7 +287,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(res["hbm_gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(w.name),
+            "traffic": None if args.token_rates else measured_traffic(w.name),
             "kernel": f"{kern} (per launch: Q,K,V read + Z written + W0 read)",
             "bytes_per_launch": res["bytes"],
         }
@@ -295,6 +309,7 @@ def main():
                    "per_token_rates": bool(args.token_rates),
                    "rotated_input_sets": res["rotated_sets"]},
         "mfma_util_pct": round(100 * res["tflops"] / BF16_MFMA_PEAK_TFLOPS, 3),
+        "mfma_util_rocprof_pct": None if args.token_rates else measured_mfma_util(w.name),
         "roofline": roofline,
     }
     if not args.no_others:
@@ -310,6 +325,8 @@ def main():
                 "tflops": round(r["tflops"], 3),
                 "mfma_util_pct": round(100 * r["tflops"] / BF16_MFMA_PEAK_TFLOPS, 3),
             }
+            if measured_mfma_util(o.name) is not None:
+                others[o.name]["mfma_util_rocprof_pct"] = measured_mfma_util(o.name)
         # variants: the headline workload with per-token rate factors (uniform in [0, 1)),
         # the dot-product loss on the headline and the vision workloads, mini-batches with
         # epochs on the vision workload
