@@ -404,7 +404,7 @@ def delta_rule(q, k, v, w0, eta, dtype=np.float64, eta_tok=None):
 # Gradients of the layer (outer-loop backward pass)
 # ----------------------------------------------------------------------------------------
 
-def ttt_linear_vjp(q, k, v, w0, eta, chunk, dz, dw_out=None):
+def ttt_linear_vjp(q, k, v, w0, eta, chunk, dz, dw_out=None, eta_tok=None):
     """Vector-Jacobian product of the causal TTT-Linear layer (reconstruction loss).
 
     The outer loop trains K, V, Q projections and the initial state by backpropagating
@@ -412,7 +412,10 @@ def ttt_linear_vjp(q, k, v, w0, eta, chunk, dz, dw_out=None):
     page, opening paragraph: the slow parameters, initialisation and rate are trained on
     the outer objective).  For upstream gradients dz [..., T, d] of z and dw_out [..., d, d]
     of the final state (or None), returns (dq, dk, dv [..., T, d], dw0 [..., d, d]) with
-    dw0 per chain (not summed over a shared leading dimension).
+    dw0 per chain (not summed over a shared leading dimension).  With per-token rate factors
+    eta_tok [..., T] (token t's gradient taken with rate eta * eta_tok[t], as in ttt_linear;
+    wmrh.cn summary, section 2.2.3, the learnable rate) it also returns their gradient
+    deta_tok [..., T] (per chain).
 
     The definition, written out: the primal recurrence of ttt_linear, in float64 torch
     tensors, differentiated by torch.autograd (reverse mode) -- no hand-derived backward.
@@ -429,6 +432,9 @@ def ttt_linear_vjp(q, k, v, w0, eta, chunk, dz, dw_out=None):
     K = torch.tensor(k2, requires_grad=True)
     V = torch.tensor(v2, requires_grad=True)
     Wi = torch.tensor(W0, requires_grad=True)
+    E = None
+    if eta_tok is not None:
+        E = torch.tensor(np.asarray(eta_tok, dtype=np.float64).reshape(N, T), requires_grad=True)
     W = Wi
     zs = []
     for c0 in range(0, T, b):
@@ -437,6 +443,8 @@ def ttt_linear_vjp(q, k, v, w0, eta, chunk, dz, dw_out=None):
         Wt = Wc
         for t in range(c0, min(c0 + b, T)):
             r = torch.einsum("nij,nj->ni", Wc, K[:, t]) - V[:, t]
+            if E is not None:
+                r = r * E[:, t, None]  # token t's gradient with its own rate factor
             G = G + torch.einsum("ni,nj->nij", r, K[:, t])
             Wt = Wc - eta * G
             zs.append(torch.einsum("nij,nj->ni", Wt, Q[:, t]))
@@ -446,11 +454,17 @@ def ttt_linear_vjp(q, k, v, w0, eta, chunk, dz, dw_out=None):
     if dw_out is not None:
         outs.append(W)
         grads.append(torch.tensor(_broadcast_state(dw_out, lead, np.float64)))
-    dq, dk, dv, dw0 = torch.autograd.grad(outs, (Q, K, V, Wi), grads, allow_unused=True)
+    wrt = (Q, K, V, Wi) + ((E,) if E is not None else ())
+    got = torch.autograd.grad(outs, wrt, grads, allow_unused=True)
+    dq, dk, dv, dw0 = got[:4]
     shape = tuple(lead) + (T, d)
     zero = lambda t: np.zeros((N, T, d)) if t is None else t.numpy()
-    return (zero(dq).reshape(shape), zero(dk).reshape(shape), zero(dv).reshape(shape),
-            (np.zeros_like(W0) if dw0 is None else dw0.numpy()).reshape(tuple(lead) + (d, d)))
+    res = (zero(dq).reshape(shape), zero(dk).reshape(shape), zero(dv).reshape(shape),
+           (np.zeros_like(W0) if dw0 is None else dw0.numpy()).reshape(tuple(lead) + (d, d)))
+    if E is not None:
+        de = got[4]
+        res = res + ((np.zeros((N, T)) if de is None else de.numpy()).reshape(tuple(lead) + (T,)),)
+    return res
 
 
 def ttt_mlp_vjp(q, k, v, w1, w2, eta, chunk, dz, dw1_out=None, dw2_out=None):

@@ -743,6 +743,45 @@ def test_linear_vjp_matches_finite_differences(chunk, with_dw):
             assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (which, fd, an)
 
 
+@pytest.mark.parametrize("chunk,with_dw", [(1, True), (4, False), (3, True)])
+def test_linear_vjp_token_rates_match_finite_differences(chunk, with_dw):
+    """Per-token rate factors: every gradient, the factors' own included, against central
+    differences of the numpy forward with the same factors."""
+    rng = _rng(50 + chunk)
+    N, T, d = 2, 9, 4
+    q, k, v = _rand_chains(rng, N, T, d)
+    w0 = 0.3 * rng.standard_normal((N, d, d))
+    et = rng.uniform(0.2, 1.5, (N, T))
+    dz = rng.standard_normal((N, T, d))
+    dw = rng.standard_normal((N, d, d)) if with_dw else None
+    args = dict(q=q, k=k, v=v, w0=w0, et=et)
+
+    def L(a):
+        z, w = O.ttt_linear(a["q"], a["k"], a["v"], a["w0"], 0.2, chunk, eta_tok=a["et"])
+        return float(np.sum(z * dz) + (np.sum(w * dw) if dw is not None else 0.0))
+    grads = dict(zip(("q", "k", "v", "w0", "et"), O.ttt_linear_vjp(q, k, v, w0, 0.2, chunk, dz, dw, eta_tok=et)))
+    h = 1e-6
+    for which in ("q", "k", "v", "w0", "et"):
+        direction = rng.standard_normal(args[which].shape)
+        ap, am = dict(args), dict(args)
+        ap[which] = args[which] + h * direction
+        am[which] = args[which] - h * direction
+        fd = (L(ap) - L(am)) / (2 * h)
+        an = float(np.sum(grads[which] * direction))
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (which, fd, an)
+
+
+def test_linear_vjp_unit_token_rates_match_no_rates():
+    rng = _rng(55)
+    q, k, v = _rand_chains(rng, 1, 11, 3)
+    w0 = rng.standard_normal((1, 3, 3))
+    dz = rng.standard_normal((1, 11, 3))
+    base = O.ttt_linear_vjp(q, k, v, w0, 0.3, 4, dz)
+    with_rates = O.ttt_linear_vjp(q, k, v, w0, 0.3, 4, dz, eta_tok=np.ones((1, 11)))
+    for a, b in zip(base, with_rates[:4]):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
+
+
 def test_linear_vjp_zero_rate_is_the_fixed_map():
     """eta = 0: z = W0 q, so dq = dz W0, dw0 = sum_t dz_t q_t^T (+ dw_out), dk = dv = 0."""
     rng = _rng(45)
