@@ -144,15 +144,17 @@ int delta_rule_fwd(const void* q, const void* k, const void* v,
                    int io_dtype, ttt_stream_t stream);
 
 /*
- * Backward pass of the causal TTT-Linear layer (reconstruction loss, scalar eta): the
- * gradients the outer loop needs to train the projections and the initial state through
- * the inner updates (wmrh.cn summary of Sun et al. 2024, section 2.2; "Fast weights" page,
- * opening paragraph).  For the forward call ttt_linear_fwd(q, k, v, w0, ..., chunk,
- * causal = 1, eta, NULL, TTT_LOSS_MSE) and upstream gradients dz of z and dw_out of the
- * final state, writes
+ * Backward pass of the causal TTT-Linear layer (reconstruction loss): the gradients the
+ * outer loop needs to train the projections, the initial state and per-token rates through
+ * the inner updates (wmrh.cn summary of Sun et al. 2024, sections 2.2 and 2.2.3; "Fast
+ * weights" page, opening paragraph).  For the forward call ttt_linear_fwd(q, k, v, w0, ...,
+ * chunk, causal = 1, eta, eta_tok, TTT_LOSS_MSE, 1) and upstream gradients dz of z and
+ * dw_out of the final state, writes
  *   dq, dk, dv  [B][H][T][d] io_dtype (out)
  *   dw0         [B][H][d][d] float32 (out): per (b, h) sequence; when w0 is shared over the
  *               batch (w0_batch_stride 0) its gradient is the sum of dw0 over b.
+ *   deta_tok    [B][H][T] float32 (out) or NULL: the gradient of the per-token rate factors
+ *               eta_tok [B][H][T] (or NULL: the scalar rate); needs eta_tok.
  *   dz          [B][H][T][d] io_dtype;  dw_out [B][H][d][d] float32 or NULL (zero).
  * Supported: d in {16, 32, 64}, chunks of at most 16 tokens (min(chunk, T) <= 16), both
  * dtypes.  The call recomputes the forward pass and keeps its chunk-start states in a
@@ -164,6 +166,7 @@ int ttt_linear_bwd(const void* q, const void* k, const void* v,
                    const void* dz, const float* dw_out,
                    void* dq, void* dk, void* dv, float* dw0,
                    int B, int H, int T, int d, int chunk, float eta,
+                   const float* eta_tok, float* deta_tok,
                    int io_dtype, ttt_stream_t stream);
 
 /*

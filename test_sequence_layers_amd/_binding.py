@@ -35,7 +35,7 @@ SIGNATURES = {
                             _i, _i, _i, _i, _i, _i, _i, _f, _vp, _i, _i, _i, _vp]),
     "delta_rule_fwd": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _i, _i, _i, _i, _f, _vp, _i, _vp]),
     "ttt_linear_bwd": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp, _vp, _vp, _vp,
-                            _i, _i, _i, _i, _i, _f, _i, _vp]),
+                            _i, _i, _i, _i, _i, _f, _vp, _vp, _i, _vp]),
     "ttt_mlp_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                          _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
     "ttt_last_error": (ctypes.c_char_p, []),
@@ -219,11 +219,12 @@ def ttt_linear_ln_fwd(q, k, v, w0, ln_weight, ln_bias, eta, chunk, causal=True, 
                    epochs, z, w_out, return_state, stream)
 
 
-def ttt_linear_bwd(q, k, v, w0, eta, chunk, dz, dw_out=None, *, stream=None):
-    """Gradients of the causal TTT-Linear layer (reconstruction loss, scalar eta) for the
-    upstream gradients dz [B,H,T,d] (dtype of q) and dw_out [B,H,d,d] float32 (or None).
-    Returns (dq, dk, dv, dw0) with dw0 [B,H,d,d] per sequence (sum it over the batch when w0
-    is shared)."""
+def ttt_linear_bwd(q, k, v, w0, eta, chunk, dz, dw_out=None, *, eta_tok=None, stream=None):
+    """Gradients of the causal TTT-Linear layer (reconstruction loss) for the upstream
+    gradients dz [B,H,T,d] (dtype of q) and dw_out [B,H,d,d] float32 (or None).  Returns
+    (dq, dk, dv, dw0) with dw0 [B,H,d,d] per sequence (sum it over the batch when w0 is
+    shared); with per-token rate factors eta_tok [B,H,T] float32 (as in ttt_linear_fwd) also
+    their gradient, (dq, dk, dv, dw0, deta_tok)."""
     torch = _torch()
     lib = load_library()
     B, H, T, d = _tokens(q, k, v)
@@ -237,14 +238,17 @@ def ttt_linear_bwd(q, k, v, w0, eta, chunk, dz, dw_out=None, *, stream=None):
     dk = torch.empty_like(q)
     dv = torch.empty_like(q)
     dw0 = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
+    et = _rates(eta_tok, B, H, T, q.device)
+    deta = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if et is not None else None
     with torch.cuda.device(q.device):
         rc = lib.ttt_linear_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), w0.data_ptr(), stride,
                                 dz.data_ptr(), dw_out.data_ptr() if dw_out is not None else None,
                                 dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dw0.data_ptr(),
-                                B, H, T, d, int(chunk), float(eta), _io_dtype(q),
+                                B, H, T, d, int(chunk), float(eta), et,
+                                deta.data_ptr() if deta is not None else None, _io_dtype(q),
                                 _stream(q.device, stream))
     _check(rc)
-    return dq, dk, dv, dw0
+    return (dq, dk, dv, dw0) if deta is None else (dq, dk, dv, dw0, deta)
 
 
 def ttt_mlp_bwd(q, k, v, w1, w2, eta, chunk, dz, dw1_out=None, dw2_out=None, *, stream=None):

@@ -100,6 +100,10 @@ struct LinearBwdArgs {
   float* dw0;           // [B][H][d][d]
   int B, H, T, d, chunk;
   float eta;
+  // per-token rate factors [B][H][T] (rate eta * eta_tok[t]) or null; their gradient
+  // [B][H][T] (out; vector-ALU kernel only) or null
+  const float* eta_tok = nullptr;
+  float* deta_tok = nullptr;
 };
 
 struct MlpArgs {

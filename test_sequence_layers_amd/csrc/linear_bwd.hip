@@ -1,5 +1,5 @@
 // Backward pass of the causal TTT-Linear layer on the vector ALUs (reconstruction loss,
-// scalar rate, chunk <= 16, fp32 or bf16 I/O, d in {16, 32, 64}).  One workgroup of 1024
+// scalar rate or per-token rate factors, chunk <= 16, fp32 or bf16 I/O, d in {16, 32, 64}).  One workgroup of 1024
 // threads (16 waves, four per SIMD, which hides the LDS latency of the short dot products)
 // per (batch, head) chain walks the chunks from last to first.
 //
@@ -15,6 +15,10 @@
 //     dQ  = dZ W + dP K
 //     dK  = -eta R G + dP^T Q + dR W
 //     dL/dW_c = G + dZ^T Q + dR^T K
+// With per-token rate factors e_t (token t's gradient taken with rate eta e_t; wmrh.cn
+// summary, section 2.2.3) R is replaced by Rt = diag(e) R in Z and in the update; the lines
+// above then give dRt (in place of dR, with Rt in dP and in -eta Rt G), and
+//     dR = diag(e) dRt,   de_t = <dRt_t, R_t>.
 // The chunk-start states W_c come from a forward recomputation that stores them
 // (w_hist); the recursion in G is serial over the chunks, everything else is per chunk.
 #include "common.hpp"
@@ -33,8 +37,10 @@ __global__ __launch_bounds__(kThreads) void linear_bwd_generic_kernel(LinearBwdA
   __shared__ float Ks[kMaxB][D + 1];
   __shared__ float Vs[kMaxB][D + 1];
   __shared__ float dZ[kMaxB][D + 1];
-  __shared__ float Rs[kMaxB][D + 1];
+  __shared__ float Rs[kMaxB][D + 1];   // R, or diag(e) R with rate factors
+  __shared__ float R0[kMaxB][D + 1];   // R (rate factors only)
   __shared__ float dR[kMaxB][D + 1];
+  __shared__ float et[kMaxB];
   __shared__ float Ps[kMaxB][kMaxB + 1];
   __shared__ float dP[kMaxB][kMaxB + 1];
 
@@ -53,6 +59,8 @@ __global__ __launch_bounds__(kThreads) void linear_bwd_generic_kernel(LinearBwdA
   IO* dk = static_cast<IO*>(a.dk) + tok0;
   IO* dv = static_cast<IO*>(a.dv) + tok0;
   const float* wh = a.w_hist + static_cast<size_t>(chain) * nchunks * D * D;
+  const float* etok = a.eta_tok ? a.eta_tok + static_cast<size_t>(chain) * T : nullptr;
+  float* detok = a.deta_tok ? a.deta_tok + static_cast<size_t>(chain) * T : nullptr;
 
   for (int e = tid; e < D * D; e += kThreads)
     G[e / D][e % D] = a.dw_out ? a.dw_out[static_cast<size_t>(chain) * D * D + e] : 0.0f;
@@ -71,6 +79,7 @@ __global__ __launch_bounds__(kThreads) void linear_bwd_generic_kernel(LinearBwdA
       Vs[t][j] = in ? to_f32(v[off]) : 0.0f;
       dZ[t][j] = in ? to_f32(dz[off]) : 0.0f;
     }
+    if (tid < kMaxB) et[tid] = etok && tid < n ? etok[c0 + tid] : 1.0f;
     __syncthreads();
     // forward quantities of the chunk: R = K W^T - V, P = tril(Q K^T)
     for (int e = tid; e < kMaxB * D; e += kThreads) {
@@ -78,7 +87,9 @@ __global__ __launch_bounds__(kThreads) void linear_bwd_generic_kernel(LinearBwdA
       float acc = 0.0f;
 #pragma unroll 16
       for (int j = 0; j < D; ++j) acc += Ks[t][j] * Wc[i][j];
-      Rs[t][i] = t < n ? acc - Vs[t][i] : 0.0f;
+      const float r = t < n ? acc - Vs[t][i] : 0.0f;
+      Rs[t][i] = et[t] * r;
+      if (etok) R0[t][i] = r;
     }
     for (int e = tid; e < kMaxB * kMaxB; e += kThreads) {
       const int t = e / kMaxB, s = e % kMaxB;
@@ -109,6 +120,16 @@ __global__ __launch_bounds__(kThreads) void linear_bwd_generic_kernel(LinearBwdA
       dP[t][s] = -eta * acc;
     }
     __syncthreads();
+    if (etok) {  // dR holds dRt: the factors' gradient, then dR = diag(e) dRt
+      if (detok && tid < n) {
+        float acc = 0.0f;
+        for (int i = 0; i < D; ++i) acc += dR[tid][i] * R0[tid][i];
+        detok[c0 + tid] = acc;
+      }
+      __syncthreads();
+      for (int e = tid; e < kMaxB * D; e += kThreads) dR[e / D][e % D] *= et[e / D];
+      __syncthreads();
+    }
     // dQ = dZ W + dP K,  dK = -eta R G + dP^T Q + dR W,  dV = -dR
     for (int e = tid; e < kMaxB * D; e += kThreads) {
       const int t = e / D, j = e % D;

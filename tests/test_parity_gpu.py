@@ -398,12 +398,12 @@ def test_paper_mlp_config_full_size_sampled():
 # ttt_linear_bwd against the oracle's vector-Jacobian product (autograd of the primal
 # recurrence in float64, pinned to finite differences)
 
-def _check_bwd(w, inp, with_dw, sel=None, seed=0):
+def _check_bwd(w, inp, with_dw, sel=None, seed=0, rates=False):
     import torch
     import test_sequence_layers_amd as ttt
     from oracle import ttt_oracle as O
     _note(f"[parity] linear_bwd B={w.B} H={w.H} T={w.T} d={w.d} chunk={w.chunk} io={w.io} "
-          f"dw_out={with_dw} seed={w.seed}")
+          f"dw_out={with_dw} rates={rates} seed={w.seed}")
     rng = np.random.default_rng(20_000 + seed)
     dz = rng.standard_normal((w.B, w.H, w.T, w.d)).astype(np.float32)
     if w.io == "bf16":
@@ -413,7 +413,10 @@ def _check_bwd(w, inp, with_dw, sel=None, seed=0):
     dt = dev["q"].dtype
     dzd = torch.from_numpy(dz).to("cuda").to(dt).contiguous()
     dwd = torch.from_numpy(dw).to("cuda").contiguous() if with_dw else None
-    out = ttt.ttt_linear_bwd(dev["q"], dev["k"], dev["v"], dev["w0"], w.eta, w.chunk, dzd, dwd)
+    et = make_token_rates(w, seed) if rates else None
+    etd = torch.from_numpy(et).to("cuda").contiguous() if rates else None
+    out = ttt.ttt_linear_bwd(dev["q"], dev["k"], dev["v"], dev["w0"], w.eta, w.chunk, dzd, dwd,
+                             eta_tok=etd)
     torch.cuda.synchronize()
     got = [to_np(t) for t in out]
     q, k, v, dzz = inp["q"], inp["k"], inp["v"], dz
@@ -424,14 +427,34 @@ def _check_bwd(w, inp, with_dw, sel=None, seed=0):
         hs = [h for _, h in sel]
         q, k, v, dzz, w0 = q[bs, hs][None], k[bs, hs][None], v[bs, hs][None], dzz[bs, hs][None], w0[bs, hs][None]
         dww = dw[bs, hs][None] if dw is not None else None
+        et = et[bs, hs][None] if rates else None
         got = [g[bs, hs][None] for g in got]
-    ref = O.ttt_linear_vjp(q, k, v, w0, w.eta, w.chunk, dzz, dww)
+    ref = O.ttt_linear_vjp(q, k, v, w0, w.eta, w.chunk, dzz, dww, eta_tok=et)
     tol = tol_for(w.io)
-    for name, g, r in zip(("dq", "dk", "dv", "dw0"), got, ref):
+    for name, g, r in zip(("dq", "dk", "dv", "dw0", "deta_tok"), got, ref):
         assert np.isfinite(g).all(), name
         rel, _ = slab_rel(g, r)
         _note(f"[parity]   {name} rel {rel:.3e} (tol {tol})")
         assert rel <= tol, (name, rel)
+
+
+@pytest.mark.parametrize("d,chunk,with_dw", [(16, 4, True), (16, 1, False), (32, 16, True)])
+def test_linear_bwd_token_rates_fp32(d, chunk, with_dw):
+    # per-token rate factors in [0, 1) and their gradient (the learnable rate)
+    w = workload(0).replace(B=2, H=2, T=37, d=d, chunk=chunk, init="normal", eta=0.3,
+                            seed=230 + d + chunk)
+    _check_bwd(w, make_inputs(w), with_dw, seed=d + chunk, rates=True)
+
+
+@pytest.mark.parametrize("T,with_dw", [(77, True), (200, False)])
+def test_linear_bwd_token_rates_bf16_d64(T, with_dw):
+    w = workload(1).replace(B=2, H=3, T=T, seed=240 + T)
+    _check_bwd(w, make_inputs(w), with_dw, seed=T, rates=True)
+
+
+def test_linear_bwd_token_rates_full_size_sampled():
+    w = workload(1)
+    _check_bwd(w, make_inputs(w), True, sel=[(2, 9)], seed=5, rates=True)
 
 
 @pytest.mark.parametrize("d,chunk,with_dw", [(16, 4, True), (16, 1, False), (32, 16, True),
