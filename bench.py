@@ -150,14 +150,16 @@ def time_workload(w, steps, warmup, torch, ttt, rotate=None, rates=False, loss="
     }
 
 
-def time_backward(w, steps, warmup, torch, ttt):
+def time_backward(w, steps, warmup, torch, ttt, rates=False):
     """Event-timed ttt_linear_bwd / ttt_mlp_bwd calls on the workload (inputs resident in
-    HBM; seeded dZ ~ N(0, 1), no upstream state gradient)."""
-    dev = make_device_inputs(w, w.seed, torch)
+    HBM; seeded dZ ~ N(0, 1), no upstream state gradient; rates: TTT-Linear with per-token
+    rate factors, their gradient included)."""
+    dev = make_device_inputs(w, w.seed, torch, rates=rates)
     g = torch.Generator(device="cuda").manual_seed(w.seed)
     dz = torch.randn(dev["q"].shape, generator=g, device="cuda").to(dev["q"].dtype)
     if w.kind == "linear":
-        call = lambda: ttt.ttt_linear_bwd(dev["q"], dev["k"], dev["v"], dev["w0"], w.eta, w.chunk, dz)
+        call = lambda: ttt.ttt_linear_bwd(dev["q"], dev["k"], dev["v"], dev["w0"], w.eta, w.chunk, dz,
+                                          eta_tok=dev.get("eta_tok"))
     else:
         call = lambda: ttt.ttt_mlp_bwd(dev["q"], dev["k"], dev["v"], dev["w1"], dev["w2"], w.eta,
                                        w.chunk, dz)
@@ -355,6 +357,12 @@ def main():
                 "tokens_per_s": round(r["tokens_per_s"], 1),
                 "ms_per_step": round(r["ms_per_step"], 5),
             }
+            if o.kind == "linear":
+                r = time_backward(o, max(10, args.steps // 2), 3, torch, ttt, rates=True)
+                others[o.name + "+backward+token_rates"] = {
+                    "tokens_per_s": round(r["tokens_per_s"], 1),
+                    "ms_per_step": round(r["ms_per_step"], 5),
+                }
         for o, tag, kw in variants:
             r = time_workload(o, max(10, args.steps // 2), 5, torch, ttt, **kw)
             others[o.name + tag] = {

@@ -101,7 +101,7 @@ struct LinearBwdArgs {
   int B, H, T, d, chunk;
   float eta;
   // per-token rate factors [B][H][T] (rate eta * eta_tok[t]) or null; their gradient
-  // [B][H][T] (out; vector-ALU kernel only) or null
+  // [B][H][T] (out) or null
   const float* eta_tok = nullptr;
   float* deta_tok = nullptr;
 };

@@ -7,6 +7,10 @@
 // W_{c+1} = W - eta R^T K) and G = dL/dW_{c+1}, our chain-rule derivation gives
 //     dR = -eta (K G^T + P^T dZ),  dV = -dR,  dP = -eta tril(dZ R^T),
 //     dQ = dZ W + dP K,  dK = -eta R G + dP^T Q + dR W,  dL/dW_c = G + dZ^T Q + dR^T K.
+// With per-token rate factors e_t (token t's gradient at rate eta e_t; wmrh.cn summary,
+// section 2.2.3) Rt = diag(e) R replaces R in Z and in the update; the lines above then hold
+// for Rt (Rt in dP and in -eta Rt G, the dR line giving dRt), and dR = diag(e) dRt,
+// de_t = <dRt_t, R_t>.
 // Two kernels:
 //   * linear_fwd_hist_kernel recomputes the forward chain (R and the update only) and stores
 //     every chunk-start state W_c as bf16 rows [64][64] (the precision the forward products
@@ -148,6 +152,7 @@ __device__ __forceinline__ int src_off(int h, int lane) {
 constexpr int kRingF = 8;
 constexpr int kSlotFK = 0, kSlotFV = kTileBytes, kSlotFBytes = 2 * kTileBytes;
 
+template <bool kTok>
 __global__ __launch_bounds__(128) void linear_fwd_hist_kernel(LinearArgs a, bf16* whist) {
   __shared__ __attribute__((aligned(16))) char ring_mem[kRingF * kSlotFBytes];
   lds_char* ring = (lds_char*)(ring_mem);
@@ -191,8 +196,21 @@ __global__ __launch_bounds__(128) void linear_fwd_hist_kernel(LinearArgs a, bf16
     }
   bf16* wh = whist + static_cast<size_t>(chain) * nchunks * (kD * kD);
   const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  // rate factors of tokens 4 g + 0..3 of chunk c (zero past T), loaded a chunk ahead
+  const float* etok = kTok ? a.eta_tok + static_cast<size_t>(chain) * T : nullptr;
+  auto load_e = [&](int c) {
+    float4_t e = {1.0f, 1.0f, 1.0f, 1.0f};
+    if constexpr (kTok) {
+      const __amdgpu_buffer_rsrc_t re = rsrc(etok + c * kB, (T - c * kB) * 4);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) e[x] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(re, (4 * g + x) * 4, 0, 0));
+    }
+    return e;
+  };
+  float4_t ecur = load_e(0);
 
   for (int c = 0; c < nchunks; ++c) {
+    const float4_t enext = (kTok && c + 1 < nchunks) ? load_e(c + 1) : ecur;
     lds_barrier();
     const lds_char* sl = ring + (c % kRingF) * kSlotFBytes;
     // bf16 chunk-start state: the operand, and the stored copy (row 16 it + n, 8 inputs)
@@ -217,7 +235,7 @@ __global__ __launch_bounds__(128) void linear_fwd_hist_kernel(LinearArgs a, bf16
       r = mfma(kop[1], wop[1][it], r);
       // V in the C layout: tokens 4 g + e of column 16 it + n (a transposing read)
       r -= unpack4(tr(sl + kSlotFV, 4 * g + (n >> 2), 16 * it + 4 * (n & 3)));
-      rb[it] = pad_op(r * -eta);
+      rb[it] = pad_op(r * (ecur * -eta));
     }
     // W^T += K^T (-eta R): K^T rows j in the tile order, tokens 4 g + s (transposing reads)
 #pragma unroll
@@ -228,6 +246,7 @@ __global__ __launch_bounds__(128) void linear_fwd_hist_kernel(LinearArgs a, bf16
 #pragma unroll
         for (int it = 0; it < 4; ++it) wt[kb][hf][it] = mfma(ktb, rb[it], wt[kb][hf][it]);
       }
+    ecur = enext;
   }
 }
 
@@ -237,6 +256,7 @@ constexpr int kSlotQ = 0, kSlotK = kTileBytes, kSlotV = 2 * kTileBytes, kSlotZ =
 constexpr int kSlotW = 4 * kTileBytes;
 constexpr int kSlotBBytes = kSlotW + kStateBytes;
 
+template <bool kTok>
 __global__ __launch_bounds__(128) void linear_bwd_mfma_kernel(LinearBwdArgs a, const bf16* whist) {
   __shared__ __attribute__((aligned(16))) char ring_mem[kRingB * kSlotBBytes];
   __shared__ __attribute__((aligned(16))) char gcopy_mem[kStateBytes];  // bf16 G rows [i][j]
@@ -312,9 +332,20 @@ __global__ __launch_bounds__(128) void linear_bwd_mfma_kernel(LinearBwdArgs a, c
     keep_t[e] = 4 * g + e <= n;
   }
 
+  // the rate factor of token n of chunk c (zero past T), loaded a chunk ahead
+  const float* etok = kTok ? a.eta_tok + static_cast<size_t>(chain) * T : nullptr;
+  float* detok = kTok && a.deta_tok ? a.deta_tok + static_cast<size_t>(chain) * T : nullptr;
+  auto load_e = [&](int c) {
+    if constexpr (kTok)
+      return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc(etok + c * kB, (T - c * kB) * 4), n * 4, 0, 0));
+    return 1.0f;
+  };
+  float ecur = load_e(nchunks - 1);
+
   for (int kk = 0; kk < nchunks; ++kk) {
-    lds_barrier();  // barrier kk: this step's chunk is in its slot
     const int c = nchunks - 1 - kk;
+    const float enext = (kTok && c > 0) ? load_e(c - 1) : ecur;
+    lds_barrier();  // barrier kk: this step's chunk is in its slot
     const lds_char* sl = ring + (kk % kRingB) * kSlotBBytes;
     const lds_char* sq = sl + kSlotQ;
     const lds_char* sk = sl + kSlotK;
@@ -352,10 +383,10 @@ __global__ __launch_bounds__(128) void linear_bwd_mfma_kernel(LinearBwdArgs a, c
       rt[it] = mfma(wop[1][it], kr[1], rt[it]);
       rt[it] -= unpack4(lds_ld<u32x2>(sv + sw(n, 16 * it + 4 * g)));
     }
-    bf16x8_t rtop[2], zcat[2];  // over outputs: tiles 2 h, 2 h + 1 side by side
+    bf16x8_t rtop[2], zcat[2];  // over outputs: tiles 2 h, 2 h + 1 side by side (Rt^T)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      rtop[h] = cat_op(rt[2 * h], rt[2 * h + 1]);
+      rtop[h] = kTok ? cat_op(rt[2 * h] * ecur, rt[2 * h + 1] * ecur) : cat_op(rt[2 * h], rt[2 * h + 1]);
       zcat[h] = join2(zq[2 * h], zq[2 * h + 1]);
     }
 
@@ -385,6 +416,20 @@ __global__ __launch_bounds__(128) void linear_bwd_mfma_kernel(LinearBwdArgs a, c
       x = mfma(gop[1][it], kr[1], x);
       x = mfma(pad2(ztr[it]), pmb, x);
       drt[it] = x * -eta;
+    }
+    if constexpr (kTok) {
+      // de_n = <dRt_n, R_n>: this lane's 16 outputs, then the other three lane groups'
+      float p = 0.0f;
+#pragma unroll
+      for (int it = 0; it < 4; ++it)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p += drt[it][e] * rt[it][e];
+      p += __shfl_xor(p, 16, 64);
+      p += __shfl_xor(p, 32, 64);
+      if (detok && g == 0)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, p), rsrc(detok + c * kB, (T - c * kB) * 4), n * 4, 0, 0);
+#pragma unroll
+      for (int it = 0; it < 4; ++it) drt[it] *= ecur;  // dR = diag(e) dRt
     }
     bf16x8_t drop[2];
 #pragma unroll
@@ -445,6 +490,7 @@ __global__ __launch_bounds__(128) void linear_bwd_mfma_kernel(LinearBwdArgs a, c
 #pragma unroll
         for (int it = 0; it < 4; ++it) gt[kb][hf][it] = mfma(aup, bup[it], gt[kb][hf][it]);
       }
+    ecur = enext;
   }
 
   float* dw0 = a.dw0 + static_cast<size_t>(chain) * kD * kD;
@@ -480,10 +526,18 @@ hipError_t launch_linear_bwd_mfma(const LinearArgs& fwd, const LinearBwdArgs& a,
   if (nchains > 0x7fffffffLL) return hipErrorInvalidValue;
   bf16* whist = static_cast<bf16*>(workspace);
   const dim3 grid(static_cast<unsigned>(nchains)), block(128);  // compute wave + loader wave
-  hipLaunchKernelGGL(linear_fwd_hist_kernel, grid, block, 0, s, fwd, whist);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(linear_bwd_mfma_kernel, grid, block, 0, s, a, static_cast<const bf16*>(whist));
+  if ((fwd.eta_tok != nullptr) != (a.eta_tok != nullptr)) return hipErrorInvalidValue;
+  if (a.eta_tok) {
+    hipLaunchKernelGGL(linear_fwd_hist_kernel<true>, grid, block, 0, s, fwd, whist);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(linear_bwd_mfma_kernel<true>, grid, block, 0, s, a, static_cast<const bf16*>(whist));
+  } else {
+    hipLaunchKernelGGL(linear_fwd_hist_kernel<false>, grid, block, 0, s, fwd, whist);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(linear_bwd_mfma_kernel<false>, grid, block, 0, s, a, static_cast<const bf16*>(whist));
+  }
   return hipGetLastError();
 }
 

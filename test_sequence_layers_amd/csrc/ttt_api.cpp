@@ -255,13 +255,14 @@ int ttt_linear_bwd(const void* q, const void* k, const void* v, const float* w0,
   const bool bf16 = io_dtype == TTT_BF16;
   {
     // matrix-core path: bf16 chunk-start states (8 KB per chunk) in a stream-ordered workspace
-    ttt::LinearBwdArgs g{q, k, v, dz, dw_out, nullptr, dq, dk, dv, dw0, B, H, T, d, chunk, eta};
-    if (!eta_tok && ttt::linear_bwd_mfma_supported(g, bf16)) {
+    ttt::LinearBwdArgs g{q, k, v, dz, dw_out, nullptr, dq, dk, dv, dw0,
+                         B, H, T, d, chunk, eta, eta_tok, deta_tok};
+    if (ttt::linear_bwd_mfma_supported(g, bf16)) {
       StreamBuffer ws;
       rc = get_workspace(ttt::linear_bwd_mfma_workspace_bytes(g), s, &ws);
       if (rc != TTT_OK) return rc;
       ttt::LinearArgs f{q, k, v, w0, w0_batch_stride, nullptr, nullptr, B, H, T, d, chunk, 1, eta,
-                        nullptr, 0, nullptr};
+                        eta_tok, 0, nullptr};
       hipError_t e = ttt::launch_linear_bwd_mfma(f, g, ws.ptr, s);
       if (e != hipSuccess) return hip_fail(e, "ttt_linear_bwd launch");
       return TTT_OK;
