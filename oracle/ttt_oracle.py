@@ -404,7 +404,7 @@ def delta_rule(q, k, v, w0, eta, dtype=np.float64, eta_tok=None):
 # Gradients of the layer (outer-loop backward pass)
 # ----------------------------------------------------------------------------------------
 
-def ttt_linear_vjp(q, k, v, w0, eta, chunk, dz, dw_out=None, eta_tok=None):
+def ttt_linear_vjp(q, k, v, w0, eta, chunk, dz, dw_out=None, eta_tok=None, loss="mse"):
     """Vector-Jacobian product of the causal TTT-Linear layer (reconstruction loss).
 
     The outer loop trains K, V, Q projections and the initial state by backpropagating
@@ -415,7 +415,8 @@ def ttt_linear_vjp(q, k, v, w0, eta, chunk, dz, dw_out=None, eta_tok=None):
     dw0 per chain (not summed over a shared leading dimension).  With per-token rate factors
     eta_tok [..., T] (token t's gradient taken with rate eta * eta_tok[t], as in ttt_linear;
     wmrh.cn summary, section 2.2.3, the learnable rate) it also returns their gradient
-    deta_tok [..., T] (per chain).
+    deta_tok [..., T] (per chain).  loss="dot" takes the negative dot-product loss -v^T W k of
+    ttt_linear (ViT3 news page, section 2), whose gradient row is r = -v.
 
     The definition, written out: the primal recurrence of ttt_linear, in float64 torch
     tensors, differentiated by torch.autograd (reverse mode) -- no hand-derived backward.
@@ -442,7 +443,10 @@ def ttt_linear_vjp(q, k, v, w0, eta, chunk, dz, dw_out=None, eta_tok=None):
         G = torch.zeros_like(Wc)
         Wt = Wc
         for t in range(c0, min(c0 + b, T)):
-            r = torch.einsum("nij,nj->ni", Wc, K[:, t]) - V[:, t]
+            if loss == "dot":
+                r = -V[:, t]
+            else:
+                r = torch.einsum("nij,nj->ni", Wc, K[:, t]) - V[:, t]
             if E is not None:
                 r = r * E[:, t, None]  # token t's gradient with its own rate factor
             G = G + torch.einsum("ni,nj->nij", r, K[:, t])

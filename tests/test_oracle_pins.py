@@ -771,6 +771,48 @@ def test_linear_vjp_token_rates_match_finite_differences(chunk, with_dw):
         assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (which, fd, an)
 
 
+@pytest.mark.parametrize("chunk,with_dw", [(1, True), (4, False), (5, True)])
+def test_linear_vjp_dot_loss_matches_finite_differences(chunk, with_dw):
+    """The negative dot-product loss: every gradient against central differences of the numpy
+    forward with loss="dot"."""
+    rng = _rng(70 + chunk)
+    N, T, d = 2, 9, 4
+    q, k, v = _rand_chains(rng, N, T, d)
+    w0 = 0.3 * rng.standard_normal((N, d, d))
+    dz = rng.standard_normal((N, T, d))
+    dw = rng.standard_normal((N, d, d)) if with_dw else None
+    args = dict(q=q, k=k, v=v, w0=w0)
+
+    def L(a):
+        z, w = O.ttt_linear(a["q"], a["k"], a["v"], a["w0"], 0.2, chunk, loss="dot")
+        return float(np.sum(z * dz) + (np.sum(w * dw) if dw is not None else 0.0))
+    grads = dict(zip(("q", "k", "v", "w0"), O.ttt_linear_vjp(q, k, v, w0, 0.2, chunk, dz, dw, loss="dot")))
+    h = 1e-6
+    for which in ("q", "k", "v", "w0"):
+        direction = rng.standard_normal(args[which].shape)
+        ap, am = dict(args), dict(args)
+        ap[which] = args[which] + h * direction
+        am[which] = args[which] - h * direction
+        fd = (L(ap) - L(am)) / (2 * h)
+        an = float(np.sum(grads[which] * direction))
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (which, fd, an)
+
+
+def test_linear_vjp_dot_loss_closed_form():
+    """Dot loss, one chunk: W_t = W0 + eta sum_{s<=t} v_s k_s^T doesn't depend on W0 beyond the
+    additive term, so dw0 = sum_t dz_t q_t^T (+ dw_out) and dq_t = W_t^T dz_t."""
+    rng = _rng(75)
+    q, k, v = _rand_chains(rng, 1, 6, 3)
+    w0 = rng.standard_normal((1, 3, 3))
+    dz = rng.standard_normal((1, 6, 3))
+    dw = rng.standard_normal((1, 3, 3))
+    dq, dk, dv, dw0 = O.ttt_linear_vjp(q, k, v, w0, 0.3, 6, dz, dw, loss="dot")
+    np.testing.assert_allclose(dw0[0], dz[0].T @ q[0] + dw[0], atol=1e-12)
+    for t in range(6):
+        wt = w0[0] + 0.3 * sum(np.outer(v[0, s], k[0, s]) for s in range(t + 1))
+        np.testing.assert_allclose(dq[0, t], wt.T @ dz[0, t], atol=1e-12)
+
+
 def test_linear_vjp_unit_token_rates_match_no_rates():
     rng = _rng(55)
     q, k, v = _rand_chains(rng, 1, 11, 3)
