@@ -144,11 +144,11 @@ int delta_rule_fwd(const void* q, const void* k, const void* v,
                    int io_dtype, ttt_stream_t stream);
 
 /*
- * Backward pass of the causal TTT-Linear layer (reconstruction loss): the gradients the
- * outer loop needs to train the projections, the initial state and per-token rates through
- * the inner updates (wmrh.cn summary of Sun et al. 2024, sections 2.2 and 2.2.3; "Fast
- * weights" page, opening paragraph).  For the forward call ttt_linear_fwd(q, k, v, w0, ...,
- * chunk, causal = 1, eta, eta_tok, TTT_LOSS_MSE, 1) and upstream gradients dz of z and
+ * Backward pass of the causal TTT-Linear layer: the gradients the outer loop needs to train
+ * the projections, the initial state and per-token rates through the inner updates
+ * (wmrh.cn summary of Sun et al. 2024, sections 2.2 and 2.2.3; "Fast weights" page, opening
+ * paragraph).  For the forward call ttt_linear_fwd(q, k, v, w0, ..., chunk, causal = 1, eta,
+ * eta_tok, loss, 1) (loss TTT_LOSS_MSE or TTT_LOSS_DOT) and upstream gradients dz of z and
  * dw_out of the final state, writes
  *   dq, dk, dv  [B][H][T][d] io_dtype (out)
  *   dw0         [B][H][d][d] float32 (out): per (b, h) sequence; when w0 is shared over the
@@ -166,7 +166,7 @@ int ttt_linear_bwd(const void* q, const void* k, const void* v,
                    const void* dz, const float* dw_out,
                    void* dq, void* dk, void* dv, float* dw0,
                    int B, int H, int T, int d, int chunk, float eta,
-                   const float* eta_tok, float* deta_tok,
+                   const float* eta_tok, float* deta_tok, int loss,
                    int io_dtype, ttt_stream_t stream);
 
 /*

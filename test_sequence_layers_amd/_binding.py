@@ -35,7 +35,7 @@ SIGNATURES = {
                             _i, _i, _i, _i, _i, _i, _i, _f, _vp, _i, _i, _i, _vp]),
     "delta_rule_fwd": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _i, _i, _i, _i, _f, _vp, _i, _vp]),
     "ttt_linear_bwd": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp, _vp, _vp, _vp,
-                            _i, _i, _i, _i, _i, _f, _vp, _vp, _i, _vp]),
+                            _i, _i, _i, _i, _i, _f, _vp, _vp, _i, _i, _vp]),
     "ttt_mlp_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                          _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
     "ttt_last_error": (ctypes.c_char_p, []),
@@ -219,12 +219,13 @@ def ttt_linear_ln_fwd(q, k, v, w0, ln_weight, ln_bias, eta, chunk, causal=True, 
                    epochs, z, w_out, return_state, stream)
 
 
-def ttt_linear_bwd(q, k, v, w0, eta, chunk, dz, dw_out=None, *, eta_tok=None, stream=None):
+def ttt_linear_bwd(q, k, v, w0, eta, chunk, dz, dw_out=None, *, eta_tok=None, loss="mse",
+                   stream=None):
     """Gradients of the causal TTT-Linear layer (reconstruction loss) for the upstream
     gradients dz [B,H,T,d] (dtype of q) and dw_out [B,H,d,d] float32 (or None).  Returns
     (dq, dk, dv, dw0) with dw0 [B,H,d,d] per sequence (sum it over the batch when w0 is
     shared); with per-token rate factors eta_tok [B,H,T] float32 (as in ttt_linear_fwd) also
-    their gradient, (dq, dk, dv, dw0, deta_tok)."""
+    their gradient, (dq, dk, dv, dw0, deta_tok).  loss: "mse" or "dot", as in the forward."""
     torch = _torch()
     lib = load_library()
     B, H, T, d = _tokens(q, k, v)
@@ -245,8 +246,8 @@ def ttt_linear_bwd(q, k, v, w0, eta, chunk, dz, dw_out=None, *, eta_tok=None, st
                                 dz.data_ptr(), dw_out.data_ptr() if dw_out is not None else None,
                                 dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dw0.data_ptr(),
                                 B, H, T, d, int(chunk), float(eta), et,
-                                deta.data_ptr() if deta is not None else None, _io_dtype(q),
-                                _stream(q.device, stream))
+                                deta.data_ptr() if deta is not None else None, _loss(loss),
+                                _io_dtype(q), _stream(q.device, stream))
     _check(rc)
     return (dq, dk, dv, dw0) if deta is None else (dq, dk, dv, dw0, deta)
 

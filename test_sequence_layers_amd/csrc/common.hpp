@@ -104,6 +104,7 @@ struct LinearBwdArgs {
   // [B][H][T] (out) or null
   const float* eta_tok = nullptr;
   float* deta_tok = nullptr;
+  int dot_loss = 0;  // 1: loss -v^T W k (R = -V)
 };
 
 struct MlpArgs {

@@ -19,6 +19,8 @@
 // summary, section 2.2.3) R is replaced by Rt = diag(e) R in Z and in the update; the lines
 // above then give dRt (in place of dR, with Rt in dP and in -eta Rt G), and
 //     dR = diag(e) dRt,   de_t = <dRt_t, R_t>.
+// With the negative dot-product loss -v^T W k (ViT3 news page, section 2) R = -V depends on
+// neither W nor K, and the dR W term of dK and the dR^T K term of dL/dW_c drop out.
 // The chunk-start states W_c come from a forward recomputation that stores them
 // (w_hist); the recursion in G is serial over the chunks, everything else is per chunk.
 #include "common.hpp"
@@ -87,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void linear_bwd_generic_kernel(LinearBwdA
       float acc = 0.0f;
 #pragma unroll 16
       for (int j = 0; j < D; ++j) acc += Ks[t][j] * Wc[i][j];
-      const float r = t < n ? acc - Vs[t][i] : 0.0f;
+      const float r = t < n ? (a.dot_loss ? 0.0f : acc) - Vs[t][i] : 0.0f;
       Rs[t][i] = et[t] * r;
       if (etok) R0[t][i] = r;
     }
@@ -141,6 +143,7 @@ __global__ __launch_bounds__(kThreads) void linear_bwd_generic_kernel(LinearBwdA
         ak += dR[t][i] * Wc[i][j];
         rg += Rs[t][i] * G[i][j];
       }
+      if (a.dot_loss) ak = 0.0f;  // R = -V does not depend on K: no dR W term
       for (int s = 0; s <= t; ++s) aq += dP[t][s] * Ks[s][j];
       for (int s = t; s < n; ++s) ak += dP[s][t] * Qs[s][j];
       const size_t off = static_cast<size_t>(c0 + t) * D + j;
@@ -152,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void linear_bwd_generic_kernel(LinearBwdA
     for (int e = tid; e < D * D; e += kThreads) {
       const int i = e / D, j = e % D;
       float acc = 0.0f;
-      for (int t = 0; t < n; ++t) acc += dZ[t][i] * Qs[t][j] + dR[t][i] * Ks[t][j];
+      for (int t = 0; t < n; ++t) acc += dZ[t][i] * Qs[t][j] + (a.dot_loss ? 0.0f : dR[t][i] * Ks[t][j]);
       G[i][j] += acc;
     }
   }

@@ -10,7 +10,8 @@
 // With per-token rate factors e_t (token t's gradient at rate eta e_t; wmrh.cn summary,
 // section 2.2.3) Rt = diag(e) R replaces R in Z and in the update; the lines above then hold
 // for Rt (Rt in dP and in -eta Rt G, the dR line giving dRt), and dR = diag(e) dRt,
-// de_t = <dRt_t, R_t>.
+// de_t = <dRt_t, R_t>.  With the negative dot-product loss -v^T W k (ViT3 news page,
+// section 2) R = -V, and the dR W term of dK and the dR^T K term of dL/dW_c drop out.
 // Two kernels:
 //   * linear_fwd_hist_kernel recomputes the forward chain (R and the update only) and stores
 //     every chunk-start state W_c as bf16 rows [64][64] (the precision the forward products
@@ -152,7 +153,7 @@ __device__ __forceinline__ int src_off(int h, int lane) {
 constexpr int kRingF = 8;
 constexpr int kSlotFK = 0, kSlotFV = kTileBytes, kSlotFBytes = 2 * kTileBytes;
 
-template <bool kTok>
+template <bool kTok, bool kDot>
 __global__ __launch_bounds__(128) void linear_fwd_hist_kernel(LinearArgs a, bf16* whist) {
   __shared__ __attribute__((aligned(16))) char ring_mem[kRingF * kSlotFBytes];
   lds_char* ring = (lds_char*)(ring_mem);
@@ -231,8 +232,11 @@ __global__ __launch_bounds__(128) void linear_fwd_hist_kernel(LinearArgs a, bf16
     bf16x8_t rb[4];
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      float4_t r = mfma(kop[0], wop[0][it], zero);
-      r = mfma(kop[1], wop[1][it], r);
+      float4_t r = zero;
+      if constexpr (!kDot) {
+        r = mfma(kop[0], wop[0][it], zero);
+        r = mfma(kop[1], wop[1][it], r);
+      }
       // V in the C layout: tokens 4 g + e of column 16 it + n (a transposing read)
       r -= unpack4(tr(sl + kSlotFV, 4 * g + (n >> 2), 16 * it + 4 * (n & 3)));
       rb[it] = pad_op(r * (ecur * -eta));
@@ -256,7 +260,7 @@ constexpr int kSlotQ = 0, kSlotK = kTileBytes, kSlotV = 2 * kTileBytes, kSlotZ =
 constexpr int kSlotW = 4 * kTileBytes;
 constexpr int kSlotBBytes = kSlotW + kStateBytes;
 
-template <bool kTok>
+template <bool kTok, bool kDot>
 __global__ __launch_bounds__(128) void linear_bwd_mfma_kernel(LinearBwdArgs a, const bf16* whist) {
   __shared__ __attribute__((aligned(16))) char ring_mem[kRingB * kSlotBBytes];
   __shared__ __attribute__((aligned(16))) char gcopy_mem[kStateBytes];  // bf16 G rows [i][j]
@@ -379,8 +383,11 @@ __global__ __launch_bounds__(128) void linear_bwd_mfma_kernel(LinearBwdArgs a, c
     float4_t rt[4];
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      rt[it] = mfma(wop[0][it], kr[0], zero);
-      rt[it] = mfma(wop[1][it], kr[1], rt[it]);
+      rt[it] = zero;
+      if constexpr (!kDot) {
+        rt[it] = mfma(wop[0][it], kr[0], zero);
+        rt[it] = mfma(wop[1][it], kr[1], rt[it]);
+      }
       rt[it] -= unpack4(lds_ld<u32x2>(sv + sw(n, 16 * it + 4 * g)));
     }
     bf16x8_t rtop[2], zcat[2];  // over outputs: tiles 2 h, 2 h + 1 side by side (Rt^T)
@@ -463,7 +470,7 @@ __global__ __launch_bounds__(128) void linear_bwd_mfma_kernel(LinearBwdArgs a, c
           const bf16x8_t gtr = join2(tr(gcp, 32 * h + 4 * g + (n >> 2), 16 * jt + 4 * (n & 3)),
                                      tr(gcp, 32 * h + 16 + 4 * g + (n >> 2), 16 * jt + 4 * (n & 3)));
           xq = mfma(wtr, zcat[h], xq);
-          xk = mfma(wtr, drop[h], xk);
+          if constexpr (!kDot) xk = mfma(wtr, drop[h], xk);
           xg = mfma(gtr, rtop[h], xg);
         }
         const bf16x8_t ktr = pad2(tr(sk, 4 * g + (n >> 2), 16 * jt + 4 * (n & 3)));
@@ -480,7 +487,7 @@ __global__ __launch_bounds__(128) void linear_bwd_mfma_kernel(LinearBwdArgs a, c
     bf16x8_t bup[4];
 #pragma unroll
     for (int it = 0; it < 4; ++it)
-      bup[it] = join2(ztr[it], tr(drs, 4 * g + (n >> 2), 16 * it + 4 * (n & 3)));
+      bup[it] = join2(ztr[it], kDot ? u32x2{0u, 0u} : tr(drs, 4 * g + (n >> 2), 16 * it + 4 * (n & 3)));
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -526,19 +533,21 @@ hipError_t launch_linear_bwd_mfma(const LinearArgs& fwd, const LinearBwdArgs& a,
   if (nchains > 0x7fffffffLL) return hipErrorInvalidValue;
   bf16* whist = static_cast<bf16*>(workspace);
   const dim3 grid(static_cast<unsigned>(nchains)), block(128);  // compute wave + loader wave
-  if ((fwd.eta_tok != nullptr) != (a.eta_tok != nullptr)) return hipErrorInvalidValue;
-  if (a.eta_tok) {
-    hipLaunchKernelGGL(linear_fwd_hist_kernel<true>, grid, block, 0, s, fwd, whist);
+  if ((fwd.eta_tok != nullptr) != (a.eta_tok != nullptr) || fwd.dot_loss != a.dot_loss)
+    return hipErrorInvalidValue;
+  const bf16* wc = static_cast<const bf16*>(whist);
+  auto run = [&](auto fk, auto bk) {
+    hipLaunchKernelGGL(fk, grid, block, 0, s, fwd, whist);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(linear_bwd_mfma_kernel<true>, grid, block, 0, s, a, static_cast<const bf16*>(whist));
-  } else {
-    hipLaunchKernelGGL(linear_fwd_hist_kernel<false>, grid, block, 0, s, fwd, whist);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(linear_bwd_mfma_kernel<false>, grid, block, 0, s, a, static_cast<const bf16*>(whist));
-  }
-  return hipGetLastError();
+    hipLaunchKernelGGL(bk, grid, block, 0, s, a, wc);
+    return hipGetLastError();
+  };
+  if (a.eta_tok && a.dot_loss)
+    return run(linear_fwd_hist_kernel<true, true>, linear_bwd_mfma_kernel<true, true>);
+  if (a.eta_tok) return run(linear_fwd_hist_kernel<true, false>, linear_bwd_mfma_kernel<true, false>);
+  if (a.dot_loss) return run(linear_fwd_hist_kernel<false, true>, linear_bwd_mfma_kernel<false, true>);
+  return run(linear_fwd_hist_kernel<false, false>, linear_bwd_mfma_kernel<false, false>);
 }
 
 }  // namespace ttt

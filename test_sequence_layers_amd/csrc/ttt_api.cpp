@@ -195,7 +195,7 @@ int mlp_fwd(const char* fn, const void* q, const void* k, const void* v, const f
 
 extern "C" {
 
-int ttt_abi_version(void) { return 7; }
+int ttt_abi_version(void) { return 8; }
 
 const char* ttt_last_error(void) { return g_last_error.c_str(); }
 
@@ -230,11 +230,14 @@ int delta_rule_fwd(const void* q, const void* k, const void* v, const float* w0,
 int ttt_linear_bwd(const void* q, const void* k, const void* v, const float* w0,
                    long long w0_batch_stride, const void* dz, const float* dw_out, void* dq,
                    void* dk, void* dv, float* dw0, int B, int H, int T, int d, int chunk,
-                   float eta, const float* eta_tok, float* deta_tok, int io_dtype,
+                   float eta, const float* eta_tok, float* deta_tok, int loss, int io_dtype,
                    ttt_stream_t stream) {
   g_last_error.clear();
   int rc = check_common("ttt_linear_bwd", q, k, v, dz, B, H, T, d, eta, eta_tok, io_dtype);
   if (rc != TTT_OK) return rc;
+  if (loss != TTT_LOSS_MSE && loss != TTT_LOSS_DOT)
+    return fail(TTT_E_INVALID, "ttt_linear_bwd: unknown loss %d", loss);
+  const int dot = loss == TTT_LOSS_DOT ? 1 : 0;
   if (deta_tok && !eta_tok)
     return fail(TTT_E_INVALID, "ttt_linear_bwd: deta_tok needs eta_tok");
   if (deta_tok && (reinterpret_cast<uintptr_t>(deta_tok) & 3) != 0)
@@ -256,13 +259,13 @@ int ttt_linear_bwd(const void* q, const void* k, const void* v, const float* w0,
   {
     // matrix-core path: bf16 chunk-start states (8 KB per chunk) in a stream-ordered workspace
     ttt::LinearBwdArgs g{q, k, v, dz, dw_out, nullptr, dq, dk, dv, dw0,
-                         B, H, T, d, chunk, eta, eta_tok, deta_tok};
+                         B, H, T, d, chunk, eta, eta_tok, deta_tok, dot};
     if (ttt::linear_bwd_mfma_supported(g, bf16)) {
       StreamBuffer ws;
       rc = get_workspace(ttt::linear_bwd_mfma_workspace_bytes(g), s, &ws);
       if (rc != TTT_OK) return rc;
       ttt::LinearArgs f{q, k, v, w0, w0_batch_stride, nullptr, nullptr, B, H, T, d, chunk, 1, eta,
-                        eta_tok, 0, nullptr};
+                        eta_tok, dot, nullptr};
       hipError_t e = ttt::launch_linear_bwd_mfma(f, g, ws.ptr, s);
       if (e != hipSuccess) return hip_fail(e, "ttt_linear_bwd launch");
       return TTT_OK;
@@ -277,11 +280,11 @@ int ttt_linear_bwd(const void* q, const void* k, const void* v, const float* w0,
   rc = get_workspace(static_cast<size_t>(B) * H * nchunks * dd * sizeof(float), s, &ws);
   if (rc != TTT_OK) return rc;
   ttt::LinearArgs f{q, k, v, w0, w0_batch_stride, nullptr, nullptr, B, H, T, d, chunk, 1, eta,
-                    eta_tok, 0, static_cast<float*>(ws.ptr)};
+                    eta_tok, dot, static_cast<float*>(ws.ptr)};
   hipError_t e = ttt::launch_linear_generic(f, bf16, s);
   if (e != hipSuccess) return hip_fail(e, "ttt_linear_bwd state launch");
   ttt::LinearBwdArgs g{q, k, v, dz, dw_out, static_cast<const float*>(ws.ptr), dq, dk, dv, dw0,
-                       B, H, T, d, chunk, eta, eta_tok, deta_tok};
+                       B, H, T, d, chunk, eta, eta_tok, deta_tok, dot};
   e = ttt::launch_linear_bwd_generic(g, bf16, s);
   if (e != hipSuccess) return hip_fail(e, "ttt_linear_bwd launch");
   return TTT_OK;

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ttt_abi_version() == 7
+    assert lib.ttt_abi_version() == 8
 
 
 FAKE = 0x1000  # never dereferenced: validation fails before any HIP call
@@ -136,12 +136,12 @@ def test_delta_rejects(lib, kw, code, msg):
 def _bwd(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, w0=FAKE, stride=0, dz=FAKE, dw_out=None, dq=FAKE, dk=FAKE,
              dv=FAKE, dw0=FAKE, B=1, H=1, T=16, d=16, chunk=16, eta=0.1, eta_tok=None,
-             deta_tok=None, io=0)
+             deta_tok=None, loss=0, io=0)
     a.update(kw)
     return lib.ttt_linear_bwd(a["q"], a["k"], a["v"], a["w0"], a["stride"], a["dz"], a["dw_out"],
                               a["dq"], a["dk"], a["dv"], a["dw0"], a["B"], a["H"], a["T"],
-                              a["d"], a["chunk"], a["eta"], a["eta_tok"], a["deta_tok"], a["io"],
-                              None)
+                              a["d"], a["chunk"], a["eta"], a["eta_tok"], a["deta_tok"],
+                              a["loss"], a["io"], None)
 
 
 @pytest.mark.parametrize("kw,code,msg", [
@@ -157,6 +157,7 @@ def _bwd(lib, **kw):
     (dict(deta_tok=FAKE), ttt.TTT_E_INVALID, "needs eta_tok"),
     (dict(eta_tok=FAKE, deta_tok=FAKE + 2), ttt.TTT_E_INVALID, "deta_tok"),
     (dict(eta_tok=FAKE + 1), ttt.TTT_E_INVALID, "eta_tok"),
+    (dict(loss=2), ttt.TTT_E_INVALID, "loss"),
 ])
 def test_linear_bwd_rejects(lib, kw, code, msg):
     assert _bwd(lib, **kw) == code

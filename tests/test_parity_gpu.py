@@ -398,12 +398,12 @@ def test_paper_mlp_config_full_size_sampled():
 # ttt_linear_bwd against the oracle's vector-Jacobian product (autograd of the primal
 # recurrence in float64, pinned to finite differences)
 
-def _check_bwd(w, inp, with_dw, sel=None, seed=0, rates=False):
+def _check_bwd(w, inp, with_dw, sel=None, seed=0, rates=False, loss="mse"):
     import torch
     import test_sequence_layers_amd as ttt
     from oracle import ttt_oracle as O
     _note(f"[parity] linear_bwd B={w.B} H={w.H} T={w.T} d={w.d} chunk={w.chunk} io={w.io} "
-          f"dw_out={with_dw} rates={rates} seed={w.seed}")
+          f"dw_out={with_dw} rates={rates} loss={loss} seed={w.seed}")
     rng = np.random.default_rng(20_000 + seed)
     dz = rng.standard_normal((w.B, w.H, w.T, w.d)).astype(np.float32)
     if w.io == "bf16":
@@ -416,7 +416,7 @@ def _check_bwd(w, inp, with_dw, sel=None, seed=0, rates=False):
     et = make_token_rates(w, seed) if rates else None
     etd = torch.from_numpy(et).to("cuda").contiguous() if rates else None
     out = ttt.ttt_linear_bwd(dev["q"], dev["k"], dev["v"], dev["w0"], w.eta, w.chunk, dzd, dwd,
-                             eta_tok=etd)
+                             eta_tok=etd, loss=loss)
     torch.cuda.synchronize()
     got = [to_np(t) for t in out]
     q, k, v, dzz = inp["q"], inp["k"], inp["v"], dz
@@ -429,7 +429,7 @@ def _check_bwd(w, inp, with_dw, sel=None, seed=0, rates=False):
         dww = dw[bs, hs][None] if dw is not None else None
         et = et[bs, hs][None] if rates else None
         got = [g[bs, hs][None] for g in got]
-    ref = O.ttt_linear_vjp(q, k, v, w0, w.eta, w.chunk, dzz, dww, eta_tok=et)
+    ref = O.ttt_linear_vjp(q, k, v, w0, w.eta, w.chunk, dzz, dww, eta_tok=et, loss=loss)
     tol = tol_for(w.io)
     for name, g, r in zip(("dq", "dk", "dv", "dw0", "deta_tok"), got, ref):
         assert np.isfinite(g).all(), name
@@ -450,6 +450,20 @@ def test_linear_bwd_token_rates_fp32(d, chunk, with_dw):
 def test_linear_bwd_token_rates_bf16_d64(T, with_dw):
     w = workload(1).replace(B=2, H=3, T=T, seed=240 + T)
     _check_bwd(w, make_inputs(w), with_dw, seed=T, rates=True)
+
+
+@pytest.mark.parametrize("d,chunk,rates", [(16, 4, False), (32, 16, True)])
+def test_linear_bwd_dot_loss_fp32(d, chunk, rates):
+    # the negative dot-product loss (R = -V): linear attention with a trained update
+    w = workload(0).replace(B=2, H=2, T=37, d=d, chunk=chunk, init="normal", eta=0.3,
+                            seed=260 + d + chunk)
+    _check_bwd(w, make_inputs(w), True, seed=d + chunk, rates=rates, loss="dot")
+
+
+@pytest.mark.parametrize("T,with_dw,rates", [(77, True, False), (200, False, True)])
+def test_linear_bwd_dot_loss_bf16_d64(T, with_dw, rates):
+    w = workload(1).replace(B=2, H=3, T=T, seed=270 + T)
+    _check_bwd(w, make_inputs(w), with_dw, seed=T, rates=rates, loss="dot")
 
 
 def test_linear_bwd_token_rates_full_size_sampled():
