@@ -85,18 +85,28 @@ constexpr int kTileBytes = kB * kD * 2;  // one 16 x 64 bf16 chunk of one tensor
 constexpr int kTmBytes = kB * kB * 2;  // one 16 x 16 bf16 Tm matrix of the delta rule
 constexpr int kChainWaves = 2;
 constexpr int kOutWaves = kChainWaves;
-constexpr int kLoaderWave = kChainWaves + kOutWaves;
+// Waves of a workgroup: 0, 1 chain; 2, 3 output (first chunk of each pair); 4, 5 loaders;
+// 6, 7 output (second chunk of each pair).  Waves are placed on the four SIMDs in turn, so
+// each chain wave shares its SIMD with a loader and the four output waves share the other
+// two.  Each output wave forms all of the workgroup's 32 Z columns of its chunk, so that one
+// 16-byte store per lane writes the chunk's rows (a compute unit's memory pipeline pays per
+// row piece touched, and loads and stores share it).  Two loader waves (Q and V; K with the rate factors and Tm^T): one wave issues a
+// direct-to-LDS load only every ~70 cycles, so a compute unit streams about twice as fast
+// from two waves as from one.
+constexpr int kLoaderWave = kChainWaves + kOutWaves;  // first loader wave
+constexpr int kLoaderWaves = 2;
 constexpr int kSplit = 4 / kChainWaves;  // workgroups per chain
-constexpr int kThreads = 64 * (kLoaderWave + 1);
+constexpr int kThreads = 64 * (kLoaderWave + kLoaderWaves + kOutWaves);
 constexpr int kHalfCols = kD / kSplit;  // output rows (= V columns) per workgroup
 
 // LDS ring of kRing slots, published kGroup chunks per barrier.  Slot layout: Q tile at 0
 // and K tile at 2 KB (16 rows of 128 bytes, 16-byte pieces swizzled by row), this
 // workgroup's 32 V columns at 4 KB (16 rows of 64 bytes, swizzled), and for the delta
 // rule the chunk's Tm^T (512 bytes, row-major) after that; with per-token rates, the
-// chunk's 16 rate factors (64 bytes) sit between V and Tm^T.  The
-// loader issues kLoads direct-to-LDS loads per chunk; its waits before barriers are
-// bounded by the 6-bit vmcnt (a smaller count than needed only waits longer).
+// chunk's 16 rate factors (64 bytes) sit between V and Tm^T.  Loader wave p issues
+// loads(p) direct-to-LDS loads of every chunk, so the same chunk counts bound each
+// loader's waits before barriers, times its own loads per chunk and capped by the 6-bit
+// vmcnt (a smaller count than needed only waits longer).
 // Barrier b publishes the chunks that the chain waves read after it (up to kGroup b +
 // kGroup + 1) and frees the slots of the chunks that the output waves finished before it (up
 // to kGroup b - kGroup - 1); the loader then refills up to kRing chunks past that.
@@ -109,19 +119,21 @@ constexpr int kTmOffRates = kEtaOff + kEtaBytes;
 // (Plain constants: a dependent static member passed to the direct-to-LDS load builtin
 // kept the host compiler from emitting the kernel's launch stub.)
 template <bool kDelta, bool kTok> struct Ring {
-  static constexpr int kRing = 24;
-  static constexpr int kLoads = 5 + (kDelta ? 1 : 0) + (kTok ? 1 : 0);
+  static constexpr int kRing = kDelta && kTok ? 20 : 24;  // within 160 KB of LDS
   static constexpr int kSlotBytes = (kTok ? kTmOffRates : kTmOffNoRates) + (kDelta ? kTmBytes : 0);
-  static constexpr int clampw(int nchunks) {
-    return nchunks * kLoads < 64 ? nchunks * kLoads : (63 / kLoads) * kLoads;
+  // loads per chunk of loader wave p: Q tile (2) and V half tile (1); K tile (2), rates, Tm^T
+  static constexpr int loads(int p) { return p == 0 ? 3 : 2 + (kTok ? 1 : 0) + (kDelta ? 1 : 0); }
+  static constexpr int clampw(int nchunks, int per) {
+    return nchunks * per < 64 ? nchunks * per : (63 / per) * per;
   }
-  static constexpr int kWait0 = clampw(kRing - 2 - kGroup);
-  static constexpr int kWait1 = clampw(kRing - 2 - 2 * kGroup);
-  static constexpr int kWaitN = clampw(kRing - 2 - 3 * kGroup);
+  template <int P> static constexpr int kWait0 = clampw(kRing - 2 - kGroup, loads(P));
+  template <int P> static constexpr int kWait1 = clampw(kRing - 2 - 2 * kGroup, loads(P));
+  template <int P> static constexpr int kWaitN = clampw(kRing - 2 - 3 * kGroup, loads(P));
   static_assert(kRing % kGroup == 0 && kRing - 2 - 3 * kGroup >= 0, "ring too small");
 };
 constexpr int kRingMax = 24;
-// Cache policy of the streaming loads: non-temporal (each byte is read once per workgroup).
+// Cache policy of the streaming loads and of the Z stores: non-temporal (each byte is read
+// once per workgroup, and Z is not read back).
 constexpr int kNT = 2;
 
 // Handoff from a chain wave to its output wave, per pair of chunks: the bf16 W^T operands
@@ -135,6 +147,8 @@ constexpr int kHandPair = kHandR1 + 64 * 8;
 constexpr int kHandWave = (kGroup / 2) * kHandPair;
 constexpr int kHandGroup = kChainWaves * kHandWave;
 constexpr int kHandBytes = 2 * kHandGroup;
+// Per output wave, 1 KB that restages its chunk's 16 x 32 Z block row-major for the store.
+constexpr int kStageBytes = 4 * kB * kHalfCols * 2;
 
 // Swizzle of the 128-byte Q/K rows: logical 16-byte piece p of row r sits at piece
 // p ^ sig(r).  sig is a bijection on r mod 8, so the 8 lanes of a 16-byte row read (rows
@@ -361,15 +375,20 @@ __device__ __forceinline__ void lds_barrier() {
   __asm__ __volatile__("" ::: "memory");
 }
 
+template <int P> struct IntTag {
+  static constexpr int value = P;
+};
+
 template <bool kDelta, bool kTok, bool kDot>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) void linear_mfma_kernel(
     LinearArgs a, const bf16* tmat) {
   using RG = Ring<kDelta, kTok>;
   constexpr int kTmOff = kTok ? kTmOffRates : kTmOffNoRates;
   constexpr int kRing = RG::kRing;
-  __shared__ __attribute__((aligned(16))) char lds_mem[kRing * RG::kSlotBytes + kHandBytes];
+  __shared__ __attribute__((aligned(16))) char lds_mem[kRing * RG::kSlotBytes + kHandBytes + kStageBytes];
   lds_char* ring = (lds_char*)(lds_mem);
   lds_char* hand = ring + kRing * RG::kSlotBytes;
+  lds_char* stage = hand + kHandBytes;
 
   // blockIdx = 8 kSplit (chain / 8) + 8 part + chain % 8: the parts of a chain share an XCD
   const int bidx = blockIdx.x;
@@ -391,11 +410,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   // .. + kGroup - 1) between barriers grp and grp + 1 and hand it off; output waves finish it
   // between barriers grp + 1 and grp + 2.
 
-  if (wv == kLoaderWave) {
-    // Loader wave: streams chunk c into ring slot c % kRing with direct-to-LDS loads.  Lane
-    // l of a Q/K half tile fills physical piece l % 8 of row 8 hh + l / 8, i.e. loads that
-    // row's logical piece (l % 8) ^ sig(l / 8); lane l of the V load fills physical piece
-    // l % 4 of row l / 4 from this workgroup's 64-byte half of the V row.
+  if (wv >= kLoaderWave && wv < kLoaderWave + kLoaderWaves) {
+    // Loader waves: stream chunk c into ring slot c % kRing with direct-to-LDS loads, wave
+    // kLoaderWave + p taking part p of every chunk (Q tile and V half tile; K tile with the
+    // rate factors and Tm^T).  Lane l of a Q/K half tile fills physical piece l % 8 of row
+    // 8 hh + l / 8, i.e. loads that row's logical piece (l % 8) ^ sig(l / 8); lane l of the
+    // V load fills physical piece l % 4 of row l / 4 from this workgroup's 64-byte half of
+    // the V row.
     const char* qsrc = reinterpret_cast<const char*>(static_cast<const bf16*>(a.q) + tok0);
     const char* ksrc = reinterpret_cast<const char*>(static_cast<const bf16*>(a.k) + tok0);
     const char* vsrc = reinterpret_cast<const char*>(static_cast<const bf16*>(a.v) + tok0);
@@ -406,47 +427,56 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
     const char* tsrc = reinterpret_cast<const char*>(tmat) +
                        (kDelta ? static_cast<size_t>(chain) * nchunks * kTmBytes : 0);
     const char* esrc = kTok ? reinterpret_cast<const char*>(a.eta_tok + static_cast<size_t>(chain) * T) : nullptr;
-    auto issue = [&](int c) {
-      const int off = c * kTileBytes;
-      lds_char* dst = ring + (c % kRing) * RG::kSlotBytes;
-      const __amdgpu_buffer_rsrc_t rq = chunk_rsrc(qsrc + off, seq_bytes - off);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, dst, 16, lglob, 0, 0, kNT);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, dst + 1024, 16, lglob + 1024, 0, 0, kNT);
-      const __amdgpu_buffer_rsrc_t rk = chunk_rsrc(ksrc + off, seq_bytes - off);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dst + kTileBytes, 16, lglob, 0, 0, kNT);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dst + kTileBytes + 1024, 16, lglob + 1024, 0, 0, kNT);
-      const __amdgpu_buffer_rsrc_t rv = chunk_rsrc(vsrc + off, seq_bytes - off);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst + kVOff, 16, vglob, 0, 0, kNT);
-      if (kTok && lane < kB) {
-        // rate factors of chunk c's tokens: 4 bytes per lane (zeros past the end)
-        const __amdgpu_buffer_rsrc_t re = chunk_rsrc(esrc + c * kEtaBytes, T * 4 - c * kEtaBytes);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(re, dst + kEtaOff, 4, lane * 4, 0, 0, kNT);
-      }
-      if (kDelta && lane < 32) {
-        // Tm^T of chunk c: 512 bytes, 16 per lane (zeros past the last chunk)
-        const __amdgpu_buffer_rsrc_t rs =
-            chunk_rsrc(tsrc + static_cast<size_t>(c) * kTmBytes, c < nchunks ? kTmBytes : 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + kTmOff, 16, lane * 16, 0, 0, kNT);
-      }
-    };
     // Chain waves read chunks 0, 1 after barrier 0 and chunks up to kGroup b + kGroup + 1
     // after barrier b (one pair ahead); output waves read chunks kGroup (b - 1) .. kGroup b - 1 after barrier
     // b.  So barrier b must publish the chunks up to kGroup b + kGroup + 1, and from b = 2 on it
     // frees the slots of the chunks up to kGroup b - kGroup - 1 (barriers 0 and 1 free
-    // nothing), after which the loader refills the ring up to chunk kGroup b - kGroup - 1 +
+    // nothing), after which each loader refills the ring up to chunk kGroup b - kGroup - 1 +
     // kRing.
-    for (int c = 0; c < kRing; ++c) issue(c);
-    wait_vmcnt<RG::kWait0>();
-    lds_barrier();  // barrier 0
-    wait_vmcnt<RG::kWait1>();
-    lds_barrier();  // barrier 1
-    for (int b = 2; b <= ngroups; ++b) {
-      wait_vmcnt<RG::kWaitN>();
-      lds_barrier();  // barrier b
-      if (b < ngroups) {
+    auto stream = [&](auto part_tag) {
+      constexpr int P = decltype(part_tag)::value;
+      auto issue = [&](int c) {
+        const int off = c * kTileBytes;
+        lds_char* dst = ring + (c % kRing) * RG::kSlotBytes;
+        const __amdgpu_buffer_rsrc_t rs = chunk_rsrc((P == 0 ? qsrc : ksrc) + off, seq_bytes - off);
+        lds_char* d = dst + P * kTileBytes;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, lglob, 0, 0, kNT);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d + 1024, 16, lglob + 1024, 0, 0, kNT);
+        if constexpr (P == 0) {
+          const __amdgpu_buffer_rsrc_t rv = chunk_rsrc(vsrc + off, seq_bytes - off);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst + kVOff, 16, vglob, 0, 0, kNT);
+        } else {
+          if (kTok && lane < kB) {
+            // rate factors of chunk c's tokens: 4 bytes per lane (zeros past the end)
+            const __amdgpu_buffer_rsrc_t re = chunk_rsrc(esrc + c * kEtaBytes, T * 4 - c * kEtaBytes);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(re, dst + kEtaOff, 4, lane * 4, 0, 0, kNT);
+          }
+          if (kDelta && lane < 32) {
+            // Tm^T of chunk c: 512 bytes, 16 per lane (zeros past the last chunk)
+            const __amdgpu_buffer_rsrc_t rs =
+                chunk_rsrc(tsrc + static_cast<size_t>(c) * kTmBytes, c < nchunks ? kTmBytes : 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + kTmOff, 16, lane * 16, 0, 0, kNT);
+          }
+        }
+      };
+      for (int c = 0; c < kRing; ++c) issue(c);
+      wait_vmcnt<RG::template kWait0<P>>();
+      lds_barrier();  // barrier 0
+      wait_vmcnt<RG::template kWait1<P>>();
+      lds_barrier();  // barrier 1
+      for (int b = 2; b <= ngroups; ++b) {
+        wait_vmcnt<RG::template kWaitN<P>>();
+        lds_barrier();  // barrier b
+        if (b < ngroups) {
 #pragma unroll
-        for (int x = 0; x < kGroup; ++x) issue(kGroup * b - 2 * kGroup + kRing + x);
+          for (int x = 0; x < kGroup; ++x) issue(kGroup * b - 2 * kGroup + kRing + x);
+        }
       }
+    };
+    if (wv == kLoaderWave) {
+      stream(IntTag<0>{});
+    } else {
+      stream(IntTag<1>{});
     }
     wait_vmcnt<0>();  // no load outlives the wave
     return;
@@ -457,16 +487,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   o.ka1 = swz(n, 4 + g) * 16;
 
   if (wv >= kChainWaves) {
-    // Output wave ow: Z columns i0 .. i0 + 15 of chain wave ow's rows.  Each chunk's store
-    // is 8 bytes per lane (rows past T are dropped by the buffer range); the stores of a
-    // block of kRing chunks share one buffer resource, rebased once per block.
-    const int ow = wv - kChainWaves;
-    const int i0 = kHalfCols * part + 16 * ow;
+    // Output wave (pr, hf): chunk hf of pair pr of every group, Z columns 32 part .. + 31 (the
+    // row blocks of both chain waves).  Lane (g, n) holds token n, columns 16 ow + 4 g .. + 3
+    // of block ow; the wave restages the two blocks row-major in its own 1 KB of LDS and
+    // stores 16 bytes per lane, 64 bytes of each of the chunk's 16 rows, non-temporal like
+    // the loads (rows past T are dropped by the buffer range).  The stores of a block of kRing chunks share one buffer
+    // resource, rebased once per block.
+    const int pr = wv & 1;
+    const bool hf = wv >= kLoaderWave + kLoaderWaves;
+    lds_char* zst = stage + (pr + (hf ? 2 : 0)) * (kStageBytes / 4);
     char* z = reinterpret_cast<char*>(static_cast<bf16*>(a.z) + tok0);
     const uint32_t pmask0 = (4 * g + 0 <= n ? 0x0000FFFFu : 0u) | (4 * g + 1 <= n ? 0xFFFF0000u : 0u);
     const uint32_t pmask1 = (4 * g + 2 <= n ? 0x0000FFFFu : 0u) | (4 * g + 3 <= n ? 0xFFFF0000u : 0u);
-    const int zoff = n * 128 + 2 * (i0 + 4 * g);
-    lds_char* hw = hand + ow * kHandWave;
+    const int zw = n * (kHalfCols * 2) + 8 * g;  // restage offset of block 0 (block 1: + 32)
+    const int zoff = (lane >> 2) * 128 + part * (kHalfCols * 2) + (lane & 3) * 16 + (hf ? kTileBytes : 0);
     lds_barrier();  // barrier 0
     for (int gbase = 0; gbase < ngroups; gbase += kRing / kGroup) {
       const int boff = gbase * kGroup * kTileBytes;
@@ -476,17 +510,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
         const int grp = gbase + gg;
         if (grp >= ngroups) break;
         lds_barrier();  // barrier grp + 1: group grp's handoffs are complete
-        const lds_char* hg = hw + (grp & 1) * kHandGroup;
-#pragma unroll
-        for (int x = 0; x < kGroup; x += 2) {
-          const int slot = gg * kGroup + x;  // chunk kGroup grp + x, mod kRing
-          const lds_char* s0 = ring + slot * RG::kSlotBytes;
-          const lds_char* hp = hg + (x / 2) * kHandPair;
-          const u32x2 z0 = out_step<false>(s0, s0, hp, o.ka0, o.ka1, lw, lr, pmask0, pmask1);
-          const u32x2 z1 = out_step<true>(s0 + RG::kSlotBytes, s0, hp, o.ka0, o.ka1, lw, lr, pmask0, pmask1);
-          __builtin_amdgcn_raw_buffer_store_b64(z0, zrs, zoff + slot * kTileBytes, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b64(z1, zrs, zoff + (slot + 1) * kTileBytes, 0, 0);
+        const int slot = gg * kGroup + 2 * pr;  // chunk kGroup grp + 2 pr, mod kRing
+        const lds_char* s0 = ring + slot * RG::kSlotBytes;
+        const lds_char* hp0 = hand + (grp & 1) * kHandGroup + pr * kHandPair;
+        const lds_char* hp1 = hp0 + kHandWave;
+        u32x2 za, zb;
+        if (!hf) {
+          za = out_step<false>(s0, s0, hp0, o.ka0, o.ka1, lw, lr, pmask0, pmask1);
+          zb = out_step<false>(s0, s0, hp1, o.ka0, o.ka1, lw, lr, pmask0, pmask1);
+        } else {
+          za = out_step<true>(s0 + RG::kSlotBytes, s0, hp0, o.ka0, o.ka1, lw, lr, pmask0, pmask1);
+          zb = out_step<true>(s0 + RG::kSlotBytes, s0, hp1, o.ka0, o.ka1, lw, lr, pmask0, pmask1);
         }
+        lds_store<u32x2>(zst + zw, za);
+        lds_store<u32x2>(zst + zw + 32, zb);
+        __asm__ __volatile__("" ::: "memory");  // the wave's LDS accesses execute in order
+        const u32x4 zr = lds_load<u32x4>(zst + 16 * lane);
+        __builtin_amdgcn_raw_buffer_store_b128(zr, zrs, zoff + slot * kTileBytes, 0, kNT);
       }
     }
     return;
