@@ -471,9 +471,11 @@ def ttt_linear_vjp(q, k, v, w0, eta, chunk, dz, dw_out=None, eta_tok=None, loss=
     return res
 
 
-def ttt_mlp_vjp(q, k, v, w1, w2, eta, chunk, dz, dw1_out=None, dw2_out=None):
+def ttt_mlp_vjp(q, k, v, w1, w2, eta, chunk, dz, dw1_out=None, dw2_out=None, loss="mse"):
     """Vector-Jacobian product of the causal TTT-MLP layer (2-layer SiLU inner MLP,
-    reconstruction loss), the MLP counterpart of ttt_linear_vjp.
+    reconstruction loss), the MLP counterpart of ttt_linear_vjp.  loss="dot" takes the
+    negative dot-product loss -v^T f(k) of ttt_mlp (ViT3 news page, section 2), whose error
+    term is r = -v whatever the weights are.
 
     For upstream gradients dz [..., T, d] of z and dw1_out [..., h, d], dw2_out [..., d, h]
     of the final states (or None), returns (dq, dk, dv [..., T, d], dw1 [..., h, d],
@@ -513,7 +515,12 @@ def ttt_mlp_vjp(q, k, v, w1, w2, eta, chunk, dz, dw1_out=None, dw2_out=None):
         for t in range(c0, min(c0 + b, T)):
             u = torch.einsum("nhj,nj->nh", W1c, K[:, t])
             a = silu_t(u)
-            r = torch.einsum("nih,nh->ni", W2c, a) - V[:, t]
+            if loss == "mse":
+                r = torch.einsum("nih,nh->ni", W2c, a) - V[:, t]
+            elif loss == "dot":
+                r = -V[:, t]
+            else:
+                raise ValueError(loss)
             du = torch.einsum("nih,ni->nh", W2c, r) * dsilu_t(u)
             G1 = G1 + torch.einsum("nh,nj->nhj", du, K[:, t])
             G2 = G2 + torch.einsum("ni,nh->nih", r, a)

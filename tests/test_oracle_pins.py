@@ -838,11 +838,11 @@ def test_linear_vjp_zero_rate_is_the_fixed_map():
     np.testing.assert_array_equal(dv, 0.0)
 
 
-def _fd_mlp_vjp(args, eta, chunk, dz, dw1, dw2, which, direction, h=1e-6):
+def _fd_mlp_vjp(args, eta, chunk, dz, dw1, dw2, which, direction, h=1e-6, loss="mse"):
     def L(x):
         a = dict(args)
         a[which] = x
-        z, w1, w2 = O.ttt_mlp(a["q"], a["k"], a["v"], a["w1"], a["w2"], eta, chunk)
+        z, w1, w2 = O.ttt_mlp(a["q"], a["k"], a["v"], a["w1"], a["w2"], eta, chunk, loss=loss)
         out = float(np.sum(z * dz))
         if dw1 is not None:
             out += float(np.sum(w1 * dw1) + np.sum(w2 * dw2))
@@ -869,6 +869,39 @@ def test_mlp_vjp_matches_finite_differences(chunk, with_dw):
             fd = _fd_mlp_vjp(args, 0.2, chunk, dz, dw1, dw2, which, direction)
             an = float(np.sum(grads[which] * direction))
             assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (which, fd, an)
+
+
+@pytest.mark.parametrize("chunk,with_dw", [(1, False), (4, True), (9, True)])
+def test_mlp_vjp_dot_loss_matches_finite_differences(chunk, with_dw):
+    """Negative dot-product loss (ViT3 news page, section 2): the VJP against central
+    differences of the forward recurrence with loss="dot", for every input."""
+    rng = _rng(70 + chunk)
+    N, T, d, hdim = 2, 9, 3, 5
+    q, k, v = _rand_chains(rng, N, T, d)
+    args = dict(q=q, k=k, v=v, w1=0.5 * rng.standard_normal((N, hdim, d)),
+                w2=0.5 * rng.standard_normal((N, d, hdim)))
+    dz = rng.standard_normal((N, T, d))
+    dw1 = rng.standard_normal((N, hdim, d)) if with_dw else None
+    dw2 = rng.standard_normal((N, d, hdim)) if with_dw else None
+    grads = dict(zip(("q", "k", "v", "w1", "w2"),
+                     O.ttt_mlp_vjp(q, k, v, args["w1"], args["w2"], 0.2, chunk, dz, dw1, dw2, loss="dot")))
+    for which in ("q", "k", "v", "w1", "w2"):
+        for _ in range(2):
+            direction = rng.standard_normal(args[which].shape)
+            fd = _fd_mlp_vjp(args, 0.2, chunk, dz, dw1, dw2, which, direction, loss="dot")
+            an = float(np.sum(grads[which] * direction))
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (which, fd, an)
+
+
+def test_mlp_vjp_dot_loss_differs_from_reconstruction():
+    """The two losses give different gradients (the dot loss is not silently ignored)."""
+    rng = _rng(75)
+    q, k, v = _rand_chains(rng, 1, 6, 3)
+    w1, w2 = rng.standard_normal((1, 4, 3)), rng.standard_normal((1, 3, 4))
+    dz = rng.standard_normal((1, 6, 3))
+    a = O.ttt_mlp_vjp(q, k, v, w1, w2, 0.3, 3, dz)
+    b = O.ttt_mlp_vjp(q, k, v, w1, w2, 0.3, 3, dz, loss="dot")
+    assert np.abs(a[1] - b[1]).max() > 1e-3
 
 
 def test_mlp_vjp_zero_rate_is_the_fixed_map():
