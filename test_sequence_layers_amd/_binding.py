@@ -37,7 +37,7 @@ SIGNATURES = {
     "ttt_linear_bwd": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp, _vp, _vp, _vp,
                             _i, _i, _i, _i, _i, _f, _vp, _vp, _i, _i, _vp]),
     "ttt_mlp_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                         _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
+                         _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "ttt_last_error": (ctypes.c_char_p, []),
     "ttt_abi_version": (_i, []),
 }
@@ -252,8 +252,9 @@ def ttt_linear_bwd(q, k, v, w0, eta, chunk, dz, dw_out=None, *, eta_tok=None, lo
     return (dq, dk, dv, dw0) if deta is None else (dq, dk, dv, dw0, deta)
 
 
-def ttt_mlp_bwd(q, k, v, w1, w2, eta, chunk, dz, dw1_out=None, dw2_out=None, *, stream=None):
-    """Gradients of the causal TTT-MLP layer (SiLU, reconstruction loss, scalar eta) for the
+def ttt_mlp_bwd(q, k, v, w1, w2, eta, chunk, dz, dw1_out=None, dw2_out=None, *, loss="mse",
+                stream=None):
+    """Gradients of the causal TTT-MLP layer (SiLU, scalar eta; loss "mse" or "dot") for the
     upstream gradients dz [B,H,T,d] (dtype of q) and dw1_out [B,H,dh,d], dw2_out [B,H,d,dh]
     float32 (or None).  Returns (dq, dk, dv, dw1, dw2) with the state gradients per sequence
     (sum them over the batch when the states are shared)."""
@@ -283,7 +284,7 @@ def ttt_mlp_bwd(q, k, v, w1, w2, eta, chunk, dz, dw1_out=None, dw2_out=None, *, 
         rc = lib.ttt_mlp_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), w1.data_ptr(), w2.data_ptr(),
                              s1, dz.data_ptr(), ptr(dw1_out), ptr(dw2_out), dq.data_ptr(),
                              dk.data_ptr(), dv.data_ptr(), dw1.data_ptr(), dw2.data_ptr(),
-                             B, H, T, d, dh, int(chunk), float(eta), _io_dtype(q),
+                             B, H, T, d, dh, int(chunk), float(eta), _loss(loss), _io_dtype(q),
                              _stream(q.device, stream))
     _check(rc)
     return dq, dk, dv, dw1, dw2

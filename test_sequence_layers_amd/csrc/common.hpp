@@ -147,6 +147,7 @@ struct MlpBwdArgs {
   float* dw2;            // [B][H][d][h]
   int B, H, T, d, dh, chunk;
   float eta;
+  int dot_loss = 0;      // 1: loss -v^T f(k), error term -v (vector-ALU path only)
 };
 
 // Host-side launchers (return a hipError_t; argument checks are done by the caller).

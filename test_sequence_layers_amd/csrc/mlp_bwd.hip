@@ -1,5 +1,5 @@
 // Backward pass of the causal TTT-MLP layer on the vector ALUs: f(k) = W2 SiLU(W1 k),
-// reconstruction loss, scalar rate, chunk <= 16, hidden width <= 256, d in {16, 32, 64},
+// reconstruction loss or the negative dot-product loss (ViT3 news page, section 2), scalar rate, chunk <= 16, hidden width <= 256, d in {16, 32, 64},
 // fp32 or bf16 I/O.  One workgroup of 1024 threads per (batch, head) chain walks the chunks
 // from last to first.
 //
@@ -18,6 +18,8 @@
 //   dUk = dA * phi'(U) + ddU * Dm * phi''(U),
 //   dQ = dUq W1 + Mb K,  dK = Mb^T Q - eta dU G1 + dUk W1,  dV = -dR,
 //   dL/dW1 = G1 + dUq^T Q + dUk^T K,  dL/dW2 = G2 + dZ^T Aq + R^T (ddU * phi'(U)) + dR^T A.
+// With the dot-product loss R = -V depends on neither A nor W2, so the dR W2 term of dUk and
+// the dR^T A term of dL/dW2 drop out (dV = -dR still holds).
 // G1 and G2 accumulate in the dw1 / dw2 outputs (read and written by the owning threads);
 // the chunk-start states come from a forward recomputation that stores them (w_hist).
 #include "common.hpp"
@@ -123,7 +125,8 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_generic_kernel(MlpBwdArgs a)
     for (int e = tid; e < kMaxB * D; e += kThreads) {
       const int t = e / D, i = e % D;
       float o = 0.0f;
-      for (int cc = 0; cc < h; ++cc) o += Ha[t * h + cc] * W2[static_cast<size_t>(i) * h + cc];
+      if (!a.dot_loss)
+        for (int cc = 0; cc < h; ++cc) o += Ha[t * h + cc] * W2[static_cast<size_t>(i) * h + cc];
       Rs[e] = t < n ? o - Vs[e] : 0.0f;
     }
     __syncthreads();
@@ -207,7 +210,7 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_generic_kernel(MlpBwdArgs a)
       if (t < n) dv[static_cast<size_t>(c0 + t) * D + i] = from_f32<IO>(-r);
     }
     __syncthreads();
-    // dUk = (dA + dR W2) * phi'(U) + ddU * (R W2) * phi''(U)
+    // dUk = (dA + dR W2) * phi'(U) + ddU * (R W2) * phi''(U)  (no dR W2 with the dot loss)
     for (int e = tid; e < kMaxB * h; e += kThreads) {
       const int t = e / h, cc = e % h;
       float rw = 0.0f, dm = 0.0f;
@@ -217,6 +220,7 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_generic_kernel(MlpBwdArgs a)
         dm += Rs[t * D + i] * w;
       }
       const float u = Hu[e];
+      if (a.dot_loss) rw = 0.0f;
       Hda[e] = (Hda[e] + rw) * dsilu_(u) + Hdd[e] * dm * d2silu_(u);
     }
     __syncthreads();
@@ -238,7 +242,9 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_generic_kernel(MlpBwdArgs a)
       dk[static_cast<size_t>(c0 + t) * D + j] = from_f32<IO>(ak);
     }
     __syncthreads();  // every read of G1, G2 of this chunk is done
-    // G1 += dUq^T Q + dUk^T K;  G2 += dZ^T Aq + R^T (ddU * phi'(U)) + dR^T A
+    // G1 += dUq^T Q + dUk^T K;  G2 += dZ^T Aq + R^T (ddU * phi'(U)) + dR^T A (no dR^T A with
+    // the dot loss)
+    const float rterm = a.dot_loss ? 0.0f : 1.0f;
     for (size_t e = tid; e < hd; e += kThreads) {
       const int cc = static_cast<int>(e / D), j = static_cast<int>(e % D);
       float acc = 0.0f;
@@ -250,7 +256,7 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_generic_kernel(MlpBwdArgs a)
       float acc = 0.0f;
       for (int t = 0; t < n; ++t)
         acc += Zb[t * D + i] * Haq[t * h + cc] + Rs[t * D + i] * Hdd[t * h + cc] * dsilu_(Hu[t * h + cc]) +
-               Rb[t * D + i] * Ha[t * h + cc];
+               rterm * Rb[t * D + i] * Ha[t * h + cc];
       G2[e] += acc;
     }
   }

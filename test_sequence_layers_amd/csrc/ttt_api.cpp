@@ -195,7 +195,7 @@ int mlp_fwd(const char* fn, const void* q, const void* k, const void* v, const f
 
 extern "C" {
 
-int ttt_abi_version(void) { return 8; }
+int ttt_abi_version(void) { return 9; }
 
 const char* ttt_last_error(void) { return g_last_error.c_str(); }
 
@@ -293,11 +293,13 @@ int ttt_linear_bwd(const void* q, const void* k, const void* v, const float* w0,
 int ttt_mlp_bwd(const void* q, const void* k, const void* v, const float* w1, const float* w2,
                 long long w_batch_stride, const void* dz, const float* dw1_out,
                 const float* dw2_out, void* dq, void* dk, void* dv, float* dw1, float* dw2, int B,
-                int H, int T, int d, int dh, int chunk, float eta, int io_dtype,
+                int H, int T, int d, int dh, int chunk, float eta, int loss, int io_dtype,
                 ttt_stream_t stream) {
   g_last_error.clear();
   int rc = check_common("ttt_mlp_bwd", q, k, v, dz, B, H, T, d, eta, nullptr, io_dtype);
   if (rc != TTT_OK) return rc;
+  if (loss != TTT_LOSS_MSE && loss != TTT_LOSS_DOT)
+    return fail(TTT_E_INVALID, "ttt_mlp_bwd: unknown loss %d", loss);
   if (!w1 || !w2 || !dw1 || !dw2)
     return fail(TTT_E_INVALID, "ttt_mlp_bwd: w1, w2, dw1 and dw2 must be non-null");
   if (T > 0 && (!dq || !dk || !dv))
@@ -323,12 +325,13 @@ int ttt_mlp_bwd(const void* q, const void* k, const void* v, const float* w1, co
   if (!fits_int64(B, H, nchunks, 2LL * static_cast<long long>(per)))
     return fail(TTT_E_INVALID, "ttt_mlp_bwd: state history overflows");
   const bool bf16 = io_dtype == TTT_BF16;
+  const int dot = loss == TTT_LOSS_DOT ? 1 : 0;
   ttt::MlpBwdArgs g{q, k, v, dz, dw1_out, dw2_out, nullptr, dq, dk, dv,
-                    dw1, dw2, B, H, T, d, dh, chunk, eta};
+                    dw1, dw2, B, H, T, d, dh, chunk, eta, dot};
   ttt::MlpArgs f{q, k, v, w1, w2, w_batch_stride, nullptr, nullptr, nullptr,
-                 B, H, T, d, dh, chunk, 1, eta, nullptr, 0};
+                 B, H, T, d, dh, chunk, 1, eta, nullptr, dot};
   hipError_t e;
-  if (ttt::mlp_bwd_mfma_supported(g, bf16) && ttt::mlp_fast_supported(f, bf16)) {
+  if (!dot && ttt::mlp_bwd_mfma_supported(g, bf16) && ttt::mlp_fast_supported(f, bf16)) {
     // matrix cores: the forward pass stores its bf16 chunk-start states, the backward pass
     // reads them
     StreamBuffer hist;

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ttt_abi_version() == 8
+    assert lib.ttt_abi_version() == 9
 
 
 FAKE = 0x1000  # never dereferenced: validation fails before any HIP call
@@ -206,11 +206,11 @@ def test_paper_models_reject(lib, fn, kw, code, msg):
 
 def _mlp_bwd(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, w1=FAKE, w2=FAKE, stride=0, dz=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
-             dw1=FAKE, dw2=FAKE, B=1, H=1, T=16, d=16, dh=32, chunk=16, eta=0.1, io=0)
+             dw1=FAKE, dw2=FAKE, B=1, H=1, T=16, d=16, dh=32, chunk=16, eta=0.1, loss=0, io=0)
     a.update(kw)
     return lib.ttt_mlp_bwd(a["q"], a["k"], a["v"], a["w1"], a["w2"], a["stride"], a["dz"], None,
                            None, a["dq"], a["dk"], a["dv"], a["dw1"], a["dw2"], a["B"], a["H"],
-                           a["T"], a["d"], a["dh"], a["chunk"], a["eta"], a["io"], None)
+                           a["T"], a["d"], a["dh"], a["chunk"], a["eta"], a["loss"], a["io"], None)
 
 
 @pytest.mark.parametrize("kw,code,msg", [
@@ -224,6 +224,7 @@ def _mlp_bwd(lib, **kw):
     (dict(chunk=32, T=64), ttt.TTT_E_UNSUPPORTED, "16 tokens"),
     (dict(eta=float("inf")), ttt.TTT_E_INVALID, "finite"),
     (dict(d=24), ttt.TTT_E_UNSUPPORTED, "d=24"),
+    (dict(loss=7), ttt.TTT_E_INVALID, "unknown loss"),
 ])
 def test_mlp_bwd_rejects(lib, kw, code, msg):
     assert _mlp_bwd(lib, **kw) == code

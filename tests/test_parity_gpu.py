@@ -503,12 +503,12 @@ def test_linear_bwd_config_full_size_sampled():
     _check_bwd(w, make_inputs(w), True, sel=[(6, 4)], seed=1)
 
 
-def _check_mlp_bwd(w, inp, with_dw, sel=None, seed=0):
+def _check_mlp_bwd(w, inp, with_dw, sel=None, seed=0, loss="mse"):
     import torch
     import test_sequence_layers_amd as ttt
     from oracle import ttt_oracle as O
     _note(f"[parity] mlp_bwd B={w.B} H={w.H} T={w.T} d={w.d} h={w.h} chunk={w.chunk} io={w.io} "
-          f"dw_out={with_dw} seed={w.seed}")
+          f"dw_out={with_dw} loss={loss} seed={w.seed}")
     rng = np.random.default_rng(30_000 + seed)
     dz = rng.standard_normal((w.B, w.H, w.T, w.d)).astype(np.float32)
     if w.io == "bf16":
@@ -520,7 +520,7 @@ def _check_mlp_bwd(w, inp, with_dw, sel=None, seed=0):
     dd1 = torch.from_numpy(dw1).to("cuda").contiguous() if with_dw else None
     dd2 = torch.from_numpy(dw2).to("cuda").contiguous() if with_dw else None
     out = ttt.ttt_mlp_bwd(dev["q"], dev["k"], dev["v"], dev["w1"], dev["w2"], w.eta, w.chunk, dzd,
-                          dd1, dd2)
+                          dd1, dd2, loss=loss)
     torch.cuda.synchronize()
     got = [to_np(t) for t in out]
     bc = lambda x, sh: np.broadcast_to(x, (w.B, w.H) + sh) if x.ndim == 3 else x
@@ -532,7 +532,7 @@ def _check_mlp_bwd(w, inp, with_dw, sel=None, seed=0):
         pick = lambda x: x[bs, hs][None] if x is not None else None
         q, k, v, dzz, w1, w2, dw1, dw2 = map(pick, (q, k, v, dzz, w1, w2, dw1, dw2))
         got = [g[bs, hs][None] for g in got]
-    ref = O.ttt_mlp_vjp(q, k, v, w1, w2, w.eta, w.chunk, dzz, dw1, dw2)
+    ref = O.ttt_mlp_vjp(q, k, v, w1, w2, w.eta, w.chunk, dzz, dw1, dw2, loss=loss)
     tol = tol_for(w.io)
     for name, g, r in zip(("dq", "dk", "dv", "dw1", "dw2"), got, ref):
         assert np.isfinite(g).all(), name
@@ -568,6 +568,22 @@ def test_mlp_bwd_bf16_matrix_core_cases(T, with_dw, per_batch, eta):
         inp["w1"] = (0.02 * rng.standard_normal((w.B, w.H, w.h, w.d))).astype(np.float32)
         inp["w2"] = (0.02 * rng.standard_normal((w.B, w.H, w.d, w.h))).astype(np.float32)
     _check_mlp_bwd(w, inp, with_dw, seed=T + 3)
+
+
+@pytest.mark.parametrize("d,h,chunk,with_dw", [(16, 32, 4, True), (32, 64, 16, False),
+                                               (16, 24, 5, True)])
+def test_mlp_bwd_dot_loss_fp32(d, h, chunk, with_dw):
+    # negative dot-product loss: error term -v (vector-ALU backward)
+    w = workload(3).replace(B=2, H=2, T=37, d=d, h=h, chunk=chunk, io="f32", eta=0.2,
+                            seed=560 + d + h + chunk)
+    _check_mlp_bwd(w, make_inputs(w), with_dw, seed=d + chunk + 7, loss="dot")
+
+
+@pytest.mark.parametrize("T,with_dw", [(16, True), (45, False)])
+def test_mlp_bwd_dot_loss_bf16_h256(T, with_dw):
+    # the causal MLP workload's shape (d 64, hidden 256, chunk 16) in bf16 with the dot loss
+    w = workload(3).replace(B=2, H=2, T=T, seed=580 + T)
+    _check_mlp_bwd(w, make_inputs(w), with_dw, seed=T + 9, loss="dot")
 
 
 def test_mlp_bwd_config_full_size_sampled():
