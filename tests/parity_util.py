@@ -6,9 +6,25 @@ from oracle import ttt_oracle as O
 from test_sequence_layers_amd.workloads import (make_inputs, make_ln_params, make_token_rates,
                                                 workload)
 
-FP32_TOL = 1e-4   # relative Frobenius error per slab, float32 I/O
+# Bounds per slab (one (batch, head) sequence), each applied to two measures:
+#   Frobenius:    ||z - ref||_F / ||ref||_F
+#   element-wise: max |z - ref| / max |ref|
+# float32 I/O: 1e-4.  bfloat16 I/O with float32 state: 2e-2, which is five times the bf16
+# unit roundoff u = 2^-8: the output's own rounding costs up to u max|ref| per element, the
+# bf16 operands of each product (state, residual and activation copies, u each) cost up to
+# about 2u of that product's sum of |terms|, roughly 1.3 u max|ref| for sums of 64 terms of
+# random sign, and the oracle's own float32-vs-float64 gap at these sizes is below 1e-6.
+# The paper's inner models with layer norm (x + LN(f_res(x))) are worse conditioned at the
+# first tokens of a sequence: from the N(0, 0.02^2) initial state the LN input is small, LN
+# divides by its spread, and the first updates are large, so the bf16 operands of the first
+# chunk move those outputs by up to a few percent of max|ref| (a numpy emulation of the first
+# chunk's dual form with bf16 operands at the kernel's rounding points lands as far from the
+# float64 oracle as the kernel does).  Their element-wise bound is 0.1 (25 u); the
+# Frobenius bound stays 2e-2.
+FP32_TOL = 1e-4
+BF16_TOL = 2e-2
+BF16_LN_ELEM_TOL = 0.1
 LN_EPS = 1e-6     # layer-norm epsilon of the paper's inner models in the parity cases
-BF16_TOL = 2e-2   # relative Frobenius error per slab, bfloat16 I/O, float32 state
 
 
 def tol_for(io):
@@ -17,15 +33,45 @@ def tol_for(io):
 
 def slab_rel(z, ref):
     """max over (b, h) of ||z - ref||_F / ||ref||_F (ref all-zero slabs use the abs error)."""
+    return slab_errors(z, ref)[0][:2]
+
+
+def slab_errors(z, ref):
+    """Per-slab errors of z against ref over the last two axes (one slab per (b, h)):
+    ((max Frobenius rel, per-slab array), (max element-wise rel, per-slab array)), the
+    element-wise measure being max |z - ref| / max |ref| (absolute for all-zero slabs)."""
     z = np.asarray(z, np.float64)
     ref = np.asarray(ref, np.float64)
+    if z.shape != ref.shape:
+        raise ValueError(f"shape {z.shape} against {ref.shape}")
     lead = ref.shape[:-2]
     zz = z.reshape((-1,) + ref.shape[-2:])
     rr = ref.reshape((-1,) + ref.shape[-2:])
-    num = np.sqrt(((zz - rr) ** 2).sum(axis=(-2, -1)))
+    diff = zz - rr
+    num = np.sqrt((diff ** 2).sum(axis=(-2, -1)))
     den = np.sqrt((rr ** 2).sum(axis=(-2, -1)))
     rel = np.where(den > 0, num / np.maximum(den, 1e-300), num)
-    return float(rel.max()) if rel.size else 0.0, rel.reshape(lead)
+    emax = np.abs(diff).max(axis=(-2, -1)) if diff.size else np.zeros(zz.shape[0])
+    rmax = np.abs(rr).max(axis=(-2, -1)) if rr.size else np.zeros(zz.shape[0])
+    erel = np.where(rmax > 0, emax / np.maximum(rmax, 1e-300), emax)
+    fmax = float(rel.max()) if rel.size else 0.0
+    elmax = float(erel.max()) if erel.size else 0.0
+    return (fmax, rel.reshape(lead), int(rel.argmax()) if rel.size else -1), \
+           (elmax, erel.reshape(lead), int(erel.argmax()) if erel.size else -1)
+
+
+def check_close(name, got, ref, tol, note=print, elem_tol=None):
+    """Assert both per-slab measures of got against ref (Frobenius within tol, element-wise
+    within elem_tol, default tol); print them first."""
+    elem_tol = tol if elem_tol is None else elem_tol
+    (f, _, fi), (e, _, ei) = slab_errors(got, ref)
+    note(f"[parity]   {name}: frob rel {f:.3e} (slab {fi}), elem rel {e:.3e} (slab {ei}), "
+         f"{int(np.prod(np.shape(ref)[:-2]))} slabs, tol {tol}"
+         + (f" / elem {elem_tol}" if elem_tol != tol else ""))
+    assert np.isfinite(np.asarray(got, np.float64)).all(), name
+    assert f <= tol, (name, "frobenius", f)
+    assert e <= elem_tol, (name, "element-wise", e)
+    return f, e
 
 
 def to_device(inp, io):
@@ -62,6 +108,29 @@ def run_gpu(kind, dev, eta, chunk, causal, return_state=True, loss="mse", epochs
                                   return_state=return_state)
     return ttt.ttt_mlp_fwd(dev["q"], dev["k"], dev["v"], dev["w1"], dev["w2"], eta, chunk,
                            causal, eta_tok=et, loss=loss, epochs=epochs, return_state=return_state)
+
+
+def run_oracle_all(kind, inp, eta, chunk, causal, loss="mse", epochs=1):
+    """The oracle on every (b, h) sequence of inp, in parallel worker processes."""
+    from tests.oracle_pool import run_chains
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    B, H = q.shape[:2]
+    kw = {"loss": loss, "eta_tok": inp.get("eta_tok")}
+    shared = {3: 3}
+    if "ln_w" in inp:
+        kw["ln"] = (inp["ln_w"], inp["ln_b"], LN_EPS)
+        shared["ln"] = 2
+    if kind == "linear":
+        kw["epochs"] = epochs
+        return run_chains("ttt_linear", B, H, (q, k, v, inp["w0"], eta, chunk, causal), kw, shared)
+    if kind == "delta":
+        return run_chains("delta_rule", B, H, (q, k, v, inp["w0"], eta), {"eta_tok": kw["eta_tok"]},
+                          shared)
+    kw["epochs"] = epochs
+    kw["act"] = "gelu" if "ln_w" in inp else "silu"
+    shared[4] = 3
+    return run_chains("ttt_mlp", B, H, (q, k, v, inp["w1"], inp["w2"], eta, chunk, causal), kw,
+                      shared)
 
 
 def run_oracle(kind, inp, eta, chunk, causal, sel=None, loss="mse", epochs=1):
