@@ -111,7 +111,9 @@ int ttt_mlp_fwd(const void* q, const void* k, const void* v,
  * ttt_mlp_fwd; only W (W1, W2) is trained, the layer norm's parameters are fixed.
  *   ln_weight, ln_bias  float32 [H][d] device pointers (one gain and bias per head, shared
  *                       over the batch), owned by the caller;  ln_eps > 0 and finite.
- * Supported: as ttt_linear_fwd / ttt_mlp_fwd (these run on the vector-ALU kernels).
+ * Supported: as ttt_linear_fwd / ttt_mlp_fwd.  The causal d = 64, chunk 16, bf16 shape runs on
+ * matrix-core kernels (and, for the MLP, hidden width 256), every other shape on the
+ * vector-ALU kernels.
  * TTT_E_INVALID additionally for a null ln_weight / ln_bias or a bad ln_eps.
  */
 int ttt_linear_ln_fwd(const void* q, const void* k, const void* v,
@@ -158,8 +160,10 @@ int delta_rule_fwd(const void* q, const void* k, const void* v,
  *   dz          [B][H][T][d] io_dtype;  dw_out [B][H][d][d] float32 or NULL (zero).
  * Supported: d in {16, 32, 64}, chunks of at most 16 tokens (min(chunk, T) <= 16), both
  * dtypes.  The call recomputes the forward pass and keeps its chunk-start states in a
- * stream-ordered workspace of B*H*ceil(T/chunk)*d*d*4 bytes.  T = 0 copies dw_out to dw0
- * (zeros without it).
+ * stream-ordered workspace: bf16 on the matrix cores (d = 64, chunk 16, bf16, with q, k, v,
+ * dz, dq, dk, dv, dw0, dw_out and w0 16-byte aligned and w0_batch_stride a multiple of 4;
+ * B*H*ceil(T/16)*8 KB), else float32 (B*H*ceil(T/chunk)*d*d*4 bytes).  T = 0 copies dw_out
+ * to dw0 (zeros without it).
  */
 int ttt_linear_bwd(const void* q, const void* k, const void* v,
                    const float* w0, long long w0_batch_stride,

@@ -179,7 +179,8 @@ size_t mlp_bwd_mfma_workspace_bytes(const MlpBwdArgs& a);
 hipError_t launch_mlp_bwd_mfma(const MlpBwdArgs& a, const void* ws, hipStream_t s);
 // matrix-core backward (bf16, d = 64, chunk 16): the forward recomputation (fwd: q, k, v, w0,
 // w0_batch_stride, B, H, T, eta) stores the bf16 chunk-start states in the workspace
-bool linear_bwd_mfma_supported(const LinearBwdArgs& a, bool bf16_io);
+// fwd: the forward arguments (its initial state is read with 16-byte loads)
+bool linear_bwd_mfma_supported(const LinearArgs& fwd, const LinearBwdArgs& a, bool bf16_io);
 size_t linear_bwd_mfma_workspace_bytes(const LinearBwdArgs& a);
 hipError_t launch_linear_bwd_mfma(const LinearArgs& fwd, const LinearBwdArgs& a, void* workspace,
                                   hipStream_t s);

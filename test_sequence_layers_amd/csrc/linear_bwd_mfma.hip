@@ -1,5 +1,6 @@
 // Backward pass of the causal TTT-Linear layer on the gfx950 matrix cores: d = 64, mini-batch
-// b = 16, bf16 Q/K/V/dZ/dQ/dK/dV, fp32 dL/dW, reconstruction loss, scalar rate.
+// b = 16, bf16 Q/K/V/dZ/dQ/dK/dV, fp32 dL/dW; reconstruction or negative dot-product loss,
+// scalar rate or per-token rate factors (with their gradient).
 //
 // The outer loop trains the projections and the initial state through the inner updates
 // (wmrh.cn summary of Sun et al. 2024, section 2.2; "Fast weights" page, opening
@@ -513,11 +514,13 @@ __global__ __launch_bounds__(128) void linear_bwd_mfma_kernel(LinearBwdArgs a, c
 
 }  // namespace
 
-bool linear_bwd_mfma_supported(const LinearBwdArgs& a, bool bf16_io) {
+bool linear_bwd_mfma_supported(const LinearArgs& fwd, const LinearBwdArgs& a, bool bf16_io) {
   auto al = [](const void* p, uintptr_t m) { return (reinterpret_cast<uintptr_t>(p) & (m - 1)) == 0; };
+  // 16-byte vector accesses: token rows, dw0 / dw_out rows and the initial state's rows
   const bool aligned = al(a.q, 16) && al(a.k, 16) && al(a.v, 16) && al(a.dz, 16) && al(a.dq, 16) &&
                        al(a.dk, 16) && al(a.dv, 16) && al(a.dw0, 16) &&
-                       (a.dw_out == nullptr || al(a.dw_out, 16));
+                       (a.dw_out == nullptr || al(a.dw_out, 16)) && al(fwd.w0, 16) &&
+                       (fwd.w0_batch_stride % 4) == 0;
   const bool fits = static_cast<long long>(a.T) * kRowBytes + 2LL * kTileBytes < 0x7fffffffLL;
   return bf16_io && a.d == kD && a.chunk == kB && a.T > 0 && aligned && fits;
 }

@@ -256,20 +256,18 @@ int ttt_linear_bwd(const void* q, const void* k, const void* v, const float* w0,
   if (T == 0) return copy_state(dw0, dw_out, static_cast<long long>(H) * dd, B, H, dd, s);
 
   const bool bf16 = io_dtype == TTT_BF16;
-  {
+  ttt::LinearArgs f{q, k, v, w0, w0_batch_stride, nullptr, nullptr, B, H, T, d, chunk, 1, eta,
+                    eta_tok, dot, nullptr};
+  ttt::LinearBwdArgs g{q, k, v, dz, dw_out, nullptr, dq, dk, dv, dw0,
+                       B, H, T, d, chunk, eta, eta_tok, deta_tok, dot};
+  if (ttt::linear_bwd_mfma_supported(f, g, bf16)) {
     // matrix-core path: bf16 chunk-start states (8 KB per chunk) in a stream-ordered workspace
-    ttt::LinearBwdArgs g{q, k, v, dz, dw_out, nullptr, dq, dk, dv, dw0,
-                         B, H, T, d, chunk, eta, eta_tok, deta_tok, dot};
-    if (ttt::linear_bwd_mfma_supported(g, bf16)) {
-      StreamBuffer ws;
-      rc = get_workspace(ttt::linear_bwd_mfma_workspace_bytes(g), s, &ws);
-      if (rc != TTT_OK) return rc;
-      ttt::LinearArgs f{q, k, v, w0, w0_batch_stride, nullptr, nullptr, B, H, T, d, chunk, 1, eta,
-                        eta_tok, dot, nullptr};
-      hipError_t e = ttt::launch_linear_bwd_mfma(f, g, ws.ptr, s);
-      if (e != hipSuccess) return hip_fail(e, "ttt_linear_bwd launch");
-      return TTT_OK;
-    }
+    StreamBuffer ws;
+    rc = get_workspace(ttt::linear_bwd_mfma_workspace_bytes(g), s, &ws);
+    if (rc != TTT_OK) return rc;
+    hipError_t e = ttt::launch_linear_bwd_mfma(f, g, ws.ptr, s);
+    if (e != hipSuccess) return hip_fail(e, "ttt_linear_bwd launch");
+    return TTT_OK;
   }
   // chunk-start states of the forward pass, recomputed into a stream-ordered workspace
   const int b = chunk < T ? chunk : T;
@@ -279,12 +277,10 @@ int ttt_linear_bwd(const void* q, const void* k, const void* v, const float* w0,
   StreamBuffer ws;
   rc = get_workspace(static_cast<size_t>(B) * H * nchunks * dd * sizeof(float), s, &ws);
   if (rc != TTT_OK) return rc;
-  ttt::LinearArgs f{q, k, v, w0, w0_batch_stride, nullptr, nullptr, B, H, T, d, chunk, 1, eta,
-                    eta_tok, dot, static_cast<float*>(ws.ptr)};
+  f.w_hist = static_cast<float*>(ws.ptr);
   hipError_t e = ttt::launch_linear_generic(f, bf16, s);
   if (e != hipSuccess) return hip_fail(e, "ttt_linear_bwd state launch");
-  ttt::LinearBwdArgs g{q, k, v, dz, dw_out, static_cast<const float*>(ws.ptr), dq, dk, dv, dw0,
-                       B, H, T, d, chunk, eta, eta_tok, deta_tok, dot};
+  g.w_hist = static_cast<const float*>(ws.ptr);
   e = ttt::launch_linear_bwd_generic(g, bf16, s);
   if (e != hipSuccess) return hip_fail(e, "ttt_linear_bwd launch");
   return TTT_OK;

@@ -510,6 +510,31 @@ def test_linear_bwd_bf16_matrix_core_cases(T, with_dw, per_batch, eta):
     _check_bwd(w, inp, with_dw, seed=T + 1)
 
 
+def test_linear_bwd_bf16_w0_offset_by_one_float():
+    # w0 starting 4 bytes past a 16-byte boundary: the matrix-core backward reads w0 rows with
+    # 16-byte loads, so this call must take the vector-ALU path (and still match the oracle)
+    import torch
+    import test_sequence_layers_amd as ttt
+    from oracle import ttt_oracle as O
+    w = workload(1).replace(B=2, H=3, T=45, seed=290)
+    inp = make_inputs(w)
+    dev = to_device(inp, w.io)
+    buf = torch.zeros(1 + w.H * w.d * w.d, dtype=torch.float32, device="cuda")
+    w0 = buf[1:].view(w.H, w.d, w.d)
+    w0.copy_(dev["w0"])
+    assert w0.data_ptr() % 16 == 4
+    rng = np.random.default_rng(291)
+    dz = to_np(torch.from_numpy(rng.standard_normal((w.B, w.H, w.T, w.d)).astype(np.float32))
+               .to(torch.bfloat16))
+    dzd = torch.from_numpy(dz).to("cuda").to(torch.bfloat16).contiguous()
+    out = ttt.ttt_linear_bwd(dev["q"], dev["k"], dev["v"], w0, w.eta, w.chunk, dzd)
+    torch.cuda.synchronize()
+    got = [to_np(t) for t in out]
+    ref = O.ttt_linear_vjp(inp["q"], inp["k"], inp["v"], inp["w0"], w.eta, w.chunk, dz)
+    for name, g, r in zip(("dq", "dk", "dv", "dw0"), got, ref):
+        check_close(name, g, r, BF16_TOL, _note)
+
+
 def test_linear_bwd_config_full_size():
     w = workload(1)
     _check_bwd(w, make_inputs(w), True, seed=1, full=True)
