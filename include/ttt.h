@@ -174,6 +174,25 @@ int ttt_linear_bwd(const void* q, const void* k, const void* v,
                    int io_dtype, ttt_stream_t stream);
 
 /*
+ * ttt_linear_bwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving or training loops, harnesses that forbid hipMalloc): the same
+ * arguments, results and supported shapes, but the chunk-start state history lives in a
+ * fixed scratch array of the library (64 MiB, one per GPU, held until the process ends)
+ * instead of a stream-ordered workspace, and the call allocates nothing.  A call whose
+ * history would exceed it (matrix-core path: B*H*ceil(T/16)*8 KB; vector-ALU path:
+ * B*H*ceil(T/chunk)*d*d*4 bytes) returns TTT_E_UNSUPPORTED.  Every call on one GPU shares the
+ * array: calls that overlap on one GPU (on different streams) race and must be ordered by the
+ * caller.
+ */
+int ttt_linear_bwd_noalloc(const void* q, const void* k, const void* v,
+                           const float* w0, long long w0_batch_stride,
+                           const void* dz, const float* dw_out,
+                           void* dq, void* dk, void* dv, float* dw0,
+                           int B, int H, int T, int d, int chunk, float eta,
+                           const float* eta_tok, float* deta_tok, int loss,
+                           int io_dtype, ttt_stream_t stream);
+
+/*
  * Backward pass of the causal TTT-MLP layer (f(k) = W2 SiLU(W1 k), scalar eta), the MLP
  * counterpart of ttt_linear_bwd.  For the forward call ttt_mlp_fwd(q, k, v, w1, w2, ...,
  * chunk, causal = 1, eta, NULL, loss, 1) (loss TTT_LOSS_MSE or TTT_LOSS_DOT; any other value

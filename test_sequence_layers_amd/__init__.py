@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     last_error,
     load_library,
     ttt_linear_bwd,
+    ttt_linear_bwd_noalloc,
     ttt_linear_fwd,
     ttt_linear_ln_fwd,
     ttt_mlp_bwd,

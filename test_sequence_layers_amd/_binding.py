@@ -36,6 +36,8 @@ SIGNATURES = {
     "delta_rule_fwd": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _i, _i, _i, _i, _f, _vp, _i, _vp]),
     "ttt_linear_bwd": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp, _vp, _vp, _vp,
                             _i, _i, _i, _i, _i, _f, _vp, _vp, _i, _i, _vp]),
+    "ttt_linear_bwd_noalloc": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp, _vp, _vp, _vp,
+                                    _i, _i, _i, _i, _i, _f, _vp, _vp, _i, _i, _vp]),
     "ttt_mlp_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                          _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "ttt_last_error": (ctypes.c_char_p, []),
@@ -226,6 +228,20 @@ def ttt_linear_bwd(q, k, v, w0, eta, chunk, dz, dw_out=None, *, eta_tok=None, lo
     (dq, dk, dv, dw0) with dw0 [B,H,d,d] per sequence (sum it over the batch when w0 is
     shared); with per-token rate factors eta_tok [B,H,T] float32 (as in ttt_linear_fwd) also
     their gradient, (dq, dk, dv, dw0, deta_tok).  loss: "mse" or "dot", as in the forward."""
+    return _linear_bwd("ttt_linear_bwd", q, k, v, w0, eta, chunk, dz, dw_out, eta_tok, loss,
+                       stream, None)
+
+
+def ttt_linear_bwd_noalloc(q, k, v, w0, eta, chunk, dz, dw_out=None, *, eta_tok=None,
+                           loss="mse", stream=None, out=None):
+    """ttt_linear_bwd through the library's allocation-free entry point: the state history
+    lives in the library's fixed 64 MiB scratch array (calls that need more raise).  out:
+    optional preallocated (dq, dk, dv, dw0[, deta_tok]) to write into."""
+    return _linear_bwd("ttt_linear_bwd_noalloc", q, k, v, w0, eta, chunk, dz, dw_out, eta_tok,
+                       loss, stream, out)
+
+
+def _linear_bwd(fn, q, k, v, w0, eta, chunk, dz, dw_out, eta_tok, loss, stream, out):
     torch = _torch()
     lib = load_library()
     B, H, T, d = _tokens(q, k, v)
@@ -235,19 +251,27 @@ def ttt_linear_bwd(q, k, v, w0, eta, chunk, dz, dw_out=None, *, eta_tok=None, lo
         raise ValueError(f"dz must be a contiguous {q.dtype} tensor of shape {(B, H, T, d)}")
     if dw_out is not None:
         dw_out = _out(dw_out, (B, H, d, d), torch.float32, q.device, "dw_out")
-    dq = torch.empty_like(q)
-    dk = torch.empty_like(q)
-    dv = torch.empty_like(q)
-    dw0 = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
     et = _rates(eta_tok, B, H, T, q.device)
-    deta = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if et is not None else None
+    if out is not None:
+        dq = _out(out[0], (B, H, T, d), q.dtype, q.device, "dq")
+        dk = _out(out[1], (B, H, T, d), q.dtype, q.device, "dk")
+        dv = _out(out[2], (B, H, T, d), q.dtype, q.device, "dv")
+        dw0 = _out(out[3], (B, H, d, d), torch.float32, q.device, "dw0")
+        deta = (_out(out[4], (B, H, T), torch.float32, q.device, "deta_tok")
+                if et is not None else None)
+    else:
+        dq = torch.empty_like(q)
+        dk = torch.empty_like(q)
+        dv = torch.empty_like(q)
+        dw0 = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
+        deta = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if et is not None else None
     with torch.cuda.device(q.device):
-        rc = lib.ttt_linear_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), w0.data_ptr(), stride,
-                                dz.data_ptr(), dw_out.data_ptr() if dw_out is not None else None,
-                                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dw0.data_ptr(),
-                                B, H, T, d, int(chunk), float(eta), et,
-                                deta.data_ptr() if deta is not None else None, _loss(loss),
-                                _io_dtype(q), _stream(q.device, stream))
+        rc = getattr(lib, fn)(q.data_ptr(), k.data_ptr(), v.data_ptr(), w0.data_ptr(), stride,
+                              dz.data_ptr(), dw_out.data_ptr() if dw_out is not None else None,
+                              dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dw0.data_ptr(),
+                              B, H, T, d, int(chunk), float(eta), et,
+                              deta.data_ptr() if deta is not None else None, _loss(loss),
+                              _io_dtype(q), _stream(q.device, stream))
     _check(rc)
     return (dq, dk, dv, dw0) if deta is None else (dq, dk, dv, dw0, deta)
 

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/ttt.h"
@@ -92,6 +93,34 @@ int copy_state(float* dst, const float* src, long long batch_stride, int B, int 
   if (!dst) return TTT_OK;
   hipError_t e = ttt::launch_copy_state(dst, src, batch_stride, B, H, per_head, s);
   if (e != hipSuccess) return hip_fail(e, "state copy launch");
+  return TTT_OK;
+}
+
+// Fixed scratch memory of the entry points that allocate nothing (ttt_linear_bwd_noalloc):
+// a device array that every GPU the library runs on holds until the process ends.  Host
+// code never passes the array's name to a kernel (on the host it is only a stand-in for
+// the symbol): it takes the device address once per device, with that device current, from
+// hipGetSymbolAddress, and passes that.  Every call on one GPU shares the array, so calls
+// that overlap on one GPU (different streams) race; a call writes every byte it reads.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+int scratch_ptr(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(TTT_E_UNSUPPORTED, "%s: device %d", fn, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
   return TTT_OK;
 }
 
@@ -191,11 +220,81 @@ int mlp_fwd(const char* fn, const void* q, const void* k, const void* v, const f
   return TTT_OK;
 }
 
+// Shared by ttt_linear_bwd (stream-ordered workspace) and ttt_linear_bwd_noalloc (the
+// library's fixed scratch array; no allocation).
+int linear_bwd(const char* fn, const void* q, const void* k, const void* v, const float* w0,
+               long long w0_batch_stride, const void* dz, const float* dw_out, void* dq, void* dk,
+               void* dv, float* dw0, int B, int H, int T, int d, int chunk, float eta,
+               const float* eta_tok, float* deta_tok, int loss, int io_dtype, ttt_stream_t stream,
+               bool noalloc) {
+  int rc = check_common(fn, q, k, v, dz, B, H, T, d, eta, eta_tok, io_dtype);
+  if (rc != TTT_OK) return rc;
+  if (loss != TTT_LOSS_MSE && loss != TTT_LOSS_DOT)
+    return fail(TTT_E_INVALID, "%s: unknown loss %d", fn, loss);
+  const int dot = loss == TTT_LOSS_DOT ? 1 : 0;
+  if (deta_tok && !eta_tok) return fail(TTT_E_INVALID, "%s: deta_tok needs eta_tok", fn);
+  if (deta_tok && (reinterpret_cast<uintptr_t>(deta_tok) & 3) != 0)
+    return fail(TTT_E_INVALID, "%s: deta_tok must be 4-byte aligned", fn);
+  if (!w0 || !dw0) return fail(TTT_E_INVALID, "%s: w0 and dw0 must be non-null", fn);
+  if (T > 0 && (!dq || !dk || !dv))
+    return fail(TTT_E_INVALID, "%s: dq, dk and dv must be non-null", fn);
+  if (chunk < 1) return fail(TTT_E_INVALID, "%s: chunk must be >= 1 (got %d)", fn, chunk);
+  if (w0_batch_stride < 0) return fail(TTT_E_INVALID, "%s: negative w0_batch_stride", fn);
+  if (d != 16 && d != 32 && d != 64)
+    return fail(TTT_E_UNSUPPORTED, "%s: d=%d not supported (16, 32, 64)", fn, d);
+  if (T > 0 && (chunk < T ? chunk : T) > 16)
+    return fail(TTT_E_UNSUPPORTED, "%s: chunks of more than 16 tokens not supported", fn);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t dd = static_cast<size_t>(d) * d;
+  if (T == 0) return copy_state(dw0, dw_out, static_cast<long long>(H) * dd, B, H, dd, s);
+
+  const bool bf16 = io_dtype == TTT_BF16;
+  ttt::LinearArgs f{q, k, v, w0, w0_batch_stride, nullptr, nullptr, B, H, T, d, chunk, 1, eta,
+                    eta_tok, dot, nullptr};
+  ttt::LinearBwdArgs g{q, k, v, dz, dw_out, nullptr, dq, dk, dv, dw0,
+                       B, H, T, d, chunk, eta, eta_tok, deta_tok, dot};
+  // chunk-start states of the forward pass: bf16 on the matrix-core path (8 KB per chunk),
+  // float32 on the vector-ALU path
+  const bool mfma = ttt::linear_bwd_mfma_supported(f, g, bf16);
+  const int b = chunk < T ? chunk : T;
+  const long long nchunks = (T + b - 1) / b;
+  if (!fits_int64(B, H, nchunks, static_cast<long long>(dd) * 4))
+    return fail(TTT_E_INVALID, "%s: state history overflows", fn);
+  const size_t need = mfma ? ttt::linear_bwd_mfma_workspace_bytes(g)
+                           : static_cast<size_t>(B) * H * nchunks * dd * sizeof(float);
+  StreamBuffer owned;
+  void* ws = nullptr;
+  if (noalloc) {
+    if (need > kScratchBytes)
+      return fail(TTT_E_UNSUPPORTED,
+                  "%s: the state history needs %zu bytes, more than the %zu-byte scratch array",
+                  fn, need, kScratchBytes);
+    rc = scratch_ptr(fn, &ws);
+    if (rc != TTT_OK) return rc;
+  } else {
+    rc = get_workspace(need, s, &owned);
+    if (rc != TTT_OK) return rc;
+    ws = owned.ptr;
+  }
+  if (mfma) {
+    hipError_t e = ttt::launch_linear_bwd_mfma(f, g, ws, s);
+    if (e != hipSuccess) return hip_fail(e, "linear backward launch");
+    return TTT_OK;
+  }
+  f.w_hist = static_cast<float*>(ws);
+  hipError_t e = ttt::launch_linear_generic(f, bf16, s);
+  if (e != hipSuccess) return hip_fail(e, "linear backward state launch");
+  g.w_hist = static_cast<const float*>(ws);
+  e = ttt::launch_linear_bwd_generic(g, bf16, s);
+  if (e != hipSuccess) return hip_fail(e, "linear backward launch");
+  return TTT_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int ttt_abi_version(void) { return 9; }
+int ttt_abi_version(void) { return 10; }
 
 const char* ttt_last_error(void) { return g_last_error.c_str(); }
 
@@ -233,57 +332,18 @@ int ttt_linear_bwd(const void* q, const void* k, const void* v, const float* w0,
                    float eta, const float* eta_tok, float* deta_tok, int loss, int io_dtype,
                    ttt_stream_t stream) {
   g_last_error.clear();
-  int rc = check_common("ttt_linear_bwd", q, k, v, dz, B, H, T, d, eta, eta_tok, io_dtype);
-  if (rc != TTT_OK) return rc;
-  if (loss != TTT_LOSS_MSE && loss != TTT_LOSS_DOT)
-    return fail(TTT_E_INVALID, "ttt_linear_bwd: unknown loss %d", loss);
-  const int dot = loss == TTT_LOSS_DOT ? 1 : 0;
-  if (deta_tok && !eta_tok)
-    return fail(TTT_E_INVALID, "ttt_linear_bwd: deta_tok needs eta_tok");
-  if (deta_tok && (reinterpret_cast<uintptr_t>(deta_tok) & 3) != 0)
-    return fail(TTT_E_INVALID, "ttt_linear_bwd: deta_tok must be 4-byte aligned");
-  if (!w0 || !dw0) return fail(TTT_E_INVALID, "ttt_linear_bwd: w0 and dw0 must be non-null");
-  if (T > 0 && (!dq || !dk || !dv))
-    return fail(TTT_E_INVALID, "ttt_linear_bwd: dq, dk and dv must be non-null");
-  if (chunk < 1) return fail(TTT_E_INVALID, "ttt_linear_bwd: chunk must be >= 1 (got %d)", chunk);
-  if (w0_batch_stride < 0) return fail(TTT_E_INVALID, "ttt_linear_bwd: negative w0_batch_stride");
-  if (d != 16 && d != 32 && d != 64)
-    return fail(TTT_E_UNSUPPORTED, "ttt_linear_bwd: d=%d not supported (16, 32, 64)", d);
-  if (T > 0 && (chunk < T ? chunk : T) > 16)
-    return fail(TTT_E_UNSUPPORTED, "ttt_linear_bwd: chunks of more than 16 tokens not supported");
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const size_t dd = static_cast<size_t>(d) * d;
-  if (T == 0) return copy_state(dw0, dw_out, static_cast<long long>(H) * dd, B, H, dd, s);
+  return linear_bwd("ttt_linear_bwd", q, k, v, w0, w0_batch_stride, dz, dw_out, dq, dk, dv, dw0, B,
+                    H, T, d, chunk, eta, eta_tok, deta_tok, loss, io_dtype, stream, false);
+}
 
-  const bool bf16 = io_dtype == TTT_BF16;
-  ttt::LinearArgs f{q, k, v, w0, w0_batch_stride, nullptr, nullptr, B, H, T, d, chunk, 1, eta,
-                    eta_tok, dot, nullptr};
-  ttt::LinearBwdArgs g{q, k, v, dz, dw_out, nullptr, dq, dk, dv, dw0,
-                       B, H, T, d, chunk, eta, eta_tok, deta_tok, dot};
-  if (ttt::linear_bwd_mfma_supported(f, g, bf16)) {
-    // matrix-core path: bf16 chunk-start states (8 KB per chunk) in a stream-ordered workspace
-    StreamBuffer ws;
-    rc = get_workspace(ttt::linear_bwd_mfma_workspace_bytes(g), s, &ws);
-    if (rc != TTT_OK) return rc;
-    hipError_t e = ttt::launch_linear_bwd_mfma(f, g, ws.ptr, s);
-    if (e != hipSuccess) return hip_fail(e, "ttt_linear_bwd launch");
-    return TTT_OK;
-  }
-  // chunk-start states of the forward pass, recomputed into a stream-ordered workspace
-  const int b = chunk < T ? chunk : T;
-  const long long nchunks = (T + b - 1) / b;
-  if (!fits_int64(B, H, nchunks, static_cast<long long>(dd)))
-    return fail(TTT_E_INVALID, "ttt_linear_bwd: state history overflows");
-  StreamBuffer ws;
-  rc = get_workspace(static_cast<size_t>(B) * H * nchunks * dd * sizeof(float), s, &ws);
-  if (rc != TTT_OK) return rc;
-  f.w_hist = static_cast<float*>(ws.ptr);
-  hipError_t e = ttt::launch_linear_generic(f, bf16, s);
-  if (e != hipSuccess) return hip_fail(e, "ttt_linear_bwd state launch");
-  g.w_hist = static_cast<const float*>(ws.ptr);
-  e = ttt::launch_linear_bwd_generic(g, bf16, s);
-  if (e != hipSuccess) return hip_fail(e, "ttt_linear_bwd launch");
-  return TTT_OK;
+int ttt_linear_bwd_noalloc(const void* q, const void* k, const void* v, const float* w0,
+                           long long w0_batch_stride, const void* dz, const float* dw_out,
+                           void* dq, void* dk, void* dv, float* dw0, int B, int H, int T, int d,
+                           int chunk, float eta, const float* eta_tok, float* deta_tok, int loss,
+                           int io_dtype, ttt_stream_t stream) {
+  g_last_error.clear();
+  return linear_bwd("ttt_linear_bwd_noalloc", q, k, v, w0, w0_batch_stride, dz, dw_out, dq, dk, dv,
+                    dw0, B, H, T, d, chunk, eta, eta_tok, deta_tok, loss, io_dtype, stream, true);
 }
 
 int ttt_mlp_bwd(const void* q, const void* k, const void* v, const float* w1, const float* w2,

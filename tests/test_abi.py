@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ttt_abi_version() == 9
+    assert lib.ttt_abi_version() == 10
 
 
 FAKE = 0x1000  # never dereferenced: validation fails before any HIP call
@@ -251,3 +251,12 @@ def _load_missing(tmp_path):
         _binding.load_library(str(tmp_path / "nope.so"))
     finally:
         _binding._lib = saved
+
+
+def test_linear_bwd_noalloc_rejects_a_history_beyond_its_scratch(lib):
+    # 64 x 16 sequences of 8192 tokens: a 4 GiB state history against the 64 MiB scratch
+    # array; the check precedes any HIP call
+    rc = lib.ttt_linear_bwd_noalloc(FAKE, FAKE, FAKE, FAKE, 0, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                                    64, 16, 8192, 64, 16, 0.1, None, None, 0, 1, None)
+    assert rc == ttt.TTT_E_UNSUPPORTED
+    assert "scratch" in ttt.last_error()
