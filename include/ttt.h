@@ -136,8 +136,7 @@ int ttt_mlp_ln_fwd(const void* q, const void* k, const void* v,
  * Delta rule (mini-batch of one token, causal): W_t = W_{t-1} + eta_t (v_t - W_{t-1} k_t) k_t^T,
  * z_t = W_t q_t ("Fast weights" page, section 1), eta_t = eta or eta * eta_tok[t].  Same
  * arguments as ttt_linear_fwd without chunk / causal.  Supported: d in {16, 32, 64}, both
- * dtypes.  The d = 64 bf16 path uses a stream-ordered device workspace of
- * B*H*ceil(T/16)*512 bytes (as ttt_mlp_fwd).
+ * dtypes.  No workspace: the call allocates nothing.
  */
 int delta_rule_fwd(const void* q, const void* k, const void* v,
                    const float* w0, long long w0_batch_stride,

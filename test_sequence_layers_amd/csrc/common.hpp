@@ -162,8 +162,7 @@ hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s);
 bool linear_ln_mfma_supported(const LinearArgs& a, bool bf16_io);
 hipError_t launch_linear_ln_mfma(const LinearArgs& a, hipStream_t s);
 bool delta_fast_supported(const LinearArgs& a, bool bf16_io);
-size_t delta_workspace_bytes(const LinearArgs& a);
-hipError_t launch_delta_fast(const LinearArgs& a, void* workspace, hipStream_t s);
+hipError_t launch_delta_fast(const LinearArgs& a, hipStream_t s);
 bool mlp_fast_supported(const MlpArgs& a, bool bf16_io);
 hipError_t launch_mlp_fast(const MlpArgs& a, hipStream_t s);
 bool mlp_nc_supported(const MlpArgs& a, bool bf16_io);

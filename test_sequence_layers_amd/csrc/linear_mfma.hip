@@ -17,7 +17,11 @@
 // i.e. (I + eta stril(K K^T)) U = -(K W^T - V).  With Tm = (I + eta stril(K K^T))^-1 and
 // R = Tm (K W^T - V) = -U, the chunk's outputs and update are the mini-batch formulas
 // above with this R (z_t = W q_t + eta sum_{s<=t} (q_t . k_s) u_s; W <- W + eta U^T K).
-// Tm depends only on K; delta_tmat_kernel computes it for every chunk beforehand.
+// The same holds for a pair of chunks taken as one block of 32 tokens: the kernel applies
+// the pair's 32 x 32 Tm = I + N at once, R = X + N X (X = K W^T - V of both chunks, exact
+// in fp32, plus a correction with bf16 operands).  N depends only on K (and the rates), so
+// a Tm wave of the workgroup computes it one group of chunks ahead, from the K tiles in the
+// ring (tm_group below); nothing is read from or written to global memory for it.
 //
 // Mapping.  The linear model is separable by output row (row i of W only needs v[i]), so a
 // (batch, head) chain is split over kSplit = 2 workgroups of 32 output rows each; within a
@@ -82,17 +86,16 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr int kD = 64;
 constexpr int kB = 16;                 // tokens per chunk
 constexpr int kTileBytes = kB * kD * 2;  // one 16 x 64 bf16 chunk of one tensor
-constexpr int kTmBytes = kB * kB * 2;  // one 16 x 16 bf16 Tm matrix of the delta rule
 constexpr int kChainWaves = 2;
 constexpr int kOutWaves = kChainWaves;
-// Waves of a workgroup: 0, 1 chain; 2, 3 output (first chunk of each pair); 4, 5 loaders;
-// 6, 7 output (second chunk of each pair).  Waves are placed on the four SIMDs in turn, so
-// each chain wave shares its SIMD with a loader and the four output waves share the other
-// two.  Each output wave forms all of the workgroup's 32 Z columns of its chunk, so that one
+// Waves of a workgroup (Waves<> below): two chain waves, four output waves (two for the first
+// chunk of each pair, two for the second), two loaders, and for the delta rule a Tm wave.
+// Waves are placed on the four SIMDs in turn; each chain wave shares its SIMD with a loader.
+// Each output wave forms all of the workgroup's 32 Z columns of its chunk, so that one
 // 16-byte store per lane writes the chunk's rows (a compute unit's memory pipeline pays per
-// row piece touched, and loads and stores share it).  Two loader waves (Q and V; K with the rate factors and Tm^T): one wave issues a
-// direct-to-LDS load only every ~70 cycles, so a compute unit streams about twice as fast
-// from two waves as from one.
+// row piece touched, and loads and stores share it).  Two loader waves (Q and V; K with the
+// rate factors): one wave issues a direct-to-LDS load only every ~70 cycles, so a compute
+// unit streams about twice as fast from two waves as from one.
 constexpr int kLoaderWave = kChainWaves + kOutWaves;  // first loader wave
 constexpr int kLoaderWaves = 2;
 constexpr int kSplit = 4 / kChainWaves;  // workgroups per chain
@@ -101,35 +104,36 @@ constexpr int kHalfCols = kD / kSplit;  // output rows (= V columns) per workgro
 
 // LDS ring of kRing slots, published kGroup chunks per barrier.  Slot layout: Q tile at 0
 // and K tile at 2 KB (16 rows of 128 bytes, 16-byte pieces swizzled by row), this
-// workgroup's 32 V columns at 4 KB (16 rows of 64 bytes, swizzled), and for the delta
-// rule the chunk's Tm^T (512 bytes, row-major) after that; with per-token rates, the
-// chunk's 16 rate factors (64 bytes) sit between V and Tm^T.  Loader wave p issues
-// loads(p) direct-to-LDS loads of every chunk, so the same chunk counts bound each
-// loader's waits before barriers, times its own loads per chunk and capped by the 6-bit
-// vmcnt (a smaller count than needed only waits longer).
+// workgroup's 32 V columns at 4 KB (16 rows of 64 bytes, swizzled); with per-token rates,
+// the chunk's 16 rate factors (64 bytes) after V.  Loader wave p issues loads(p)
+// direct-to-LDS loads of every chunk, so the same chunk counts bound each loader's waits
+// before barriers, times its own loads per chunk and capped by the 6-bit vmcnt (a smaller
+// count than needed only waits longer).
 // Barrier b publishes the chunks that the chain waves read after it (up to kGroup b +
-// kGroup + 1) and frees the slots of the chunks that the output waves finished before it (up
-// to kGroup b - kGroup - 1); the loader then refills up to kRing chunks past that.
+// kGroup + 1; for the delta rule kAhead = 2 more, the next group that the Tm wave works on)
+// and frees the slots of the chunks that the output waves finished before it (up to
+// kGroup b - kGroup - 1); the loader then refills up to kRing chunks past that.
 constexpr int kGroup = 4;
 constexpr int kVOff = 2 * kTileBytes;
 constexpr int kEtaOff = kVOff + kB * kHalfCols * 2;  // per-token rate factors (64 bytes)
 constexpr int kEtaBytes = kB * 4;
-constexpr int kTmOffNoRates = kEtaOff;
-constexpr int kTmOffRates = kEtaOff + kEtaBytes;
+constexpr int kSlotPlain = kEtaOff;
+constexpr int kSlotRates = kEtaOff + kEtaBytes;
 // (Plain constants: a dependent static member passed to the direct-to-LDS load builtin
 // kept the host compiler from emitting the kernel's launch stub.)
 template <bool kDelta, bool kTok> struct Ring {
-  static constexpr int kRing = kDelta && kTok ? 20 : 24;  // within 160 KB of LDS
-  static constexpr int kSlotBytes = (kTok ? kTmOffRates : kTmOffNoRates) + (kDelta ? kTmBytes : 0);
-  // loads per chunk of loader wave p: Q tile (2) and V half tile (1); K tile (2), rates, Tm^T
-  static constexpr int loads(int p) { return p == 0 ? 3 : 2 + (kTok ? 1 : 0) + (kDelta ? 1 : 0); }
+  static constexpr int kRing = 24;  // within 160 KB of LDS
+  static constexpr int kSlotBytes = kTok ? kSlotRates : kSlotPlain;
+  static constexpr int kAhead = kDelta ? 2 : 0;
+  // loads per chunk of loader wave p: Q tile (2) and V half tile (1); K tile (2) and rates
+  static constexpr int loads(int p) { return p == 0 ? 3 : 2 + (kTok ? 1 : 0); }
   static constexpr int clampw(int nchunks, int per) {
     return nchunks * per < 64 ? nchunks * per : (63 / per) * per;
   }
-  template <int P> static constexpr int kWait0 = clampw(kRing - 2 - kGroup, loads(P));
-  template <int P> static constexpr int kWait1 = clampw(kRing - 2 - 2 * kGroup, loads(P));
-  template <int P> static constexpr int kWaitN = clampw(kRing - 2 - 3 * kGroup, loads(P));
-  static_assert(kRing % kGroup == 0 && kRing - 2 - 3 * kGroup >= 0, "ring too small");
+  template <int P> static constexpr int kWait0 = clampw(kRing - 2 - kGroup - kAhead, loads(P));
+  template <int P> static constexpr int kWait1 = clampw(kRing - 2 - 2 * kGroup - kAhead, loads(P));
+  template <int P> static constexpr int kWaitN = clampw(kRing - 2 - 3 * kGroup - kAhead, loads(P));
+  static_assert(kRing % kGroup == 0 && kRing - 2 - 3 * kGroup - kAhead >= 0, "ring too small");
 };
 constexpr int kRingMax = 24;
 // Cache policy of the streaming loads and of the Z stores: non-temporal (each byte is read
@@ -149,6 +153,13 @@ constexpr int kHandGroup = kChainWaves * kHandWave;
 constexpr int kHandBytes = 2 * kHandGroup;
 // Per output wave, 1 KB that restages its chunk's 16 x 32 Z block row-major for the store.
 constexpr int kStageBytes = 4 * kB * kHalfCols * 2;
+// Delta rule: the pair correction operands N (per pair: N00 over the first chunk's tokens, 8
+// bytes per lane, then [N10 | N11] over both chunks' tokens, 16 bytes per lane), two groups
+// by group parity (the Tm waves fill one while the chain waves read the other).
+constexpr int kNPair = 64 * 8 + 64 * 16;
+constexpr int kNGroup = (kGroup / 2) * kNPair;
+constexpr int kNBytes = 2 * kNGroup;
+constexpr int kTmScratch = 0;
 
 // Swizzle of the 128-byte Q/K rows: logical 16-byte piece p of row r sits at piece
 // p ^ sig(r).  sig is a bijection on r mod 8, so the 8 lanes of a 16-byte row read (rows
@@ -184,7 +195,6 @@ struct PairRegs {
   u32x4 k[2][2];   // chunk e: K[n][8 g + 0..7], K[n][32 + 8 g + 0..7]
   u32x2 v[2];      // chunk e: V[n][i0 + 4 g .. + 3]
   u32x2 kt[2][4];  // chunk e, tile t: K[4 g + s][j_t(n)], s = 0..3
-  u32x2 tm[2];     // delta rule: chunk e's Tm[n][4 g .. 4 g + 3] (from the stored Tm^T)
   float4_t et[2];  // per-token rates: chunk e's factors of tokens 4 g .. 4 g + 3
 };
 
@@ -193,15 +203,13 @@ struct LaneOffsets {
   int ka0, ka1;  // row n, pieces g and 4 + g
   int kt0, kt1;  // transposing reads: row 4 g + n / 4, pieces n % 4 and 4 + n % 4
   int vv;        // V row n, columns i0 - 32 part + 4 g
-  int tm;        // Tm row n, columns 4 g
   int et;        // rate factors of tokens 4 g .. 4 g + 3
 };
 
 // Ring reads of the chain waves.  Only chain waves run this, and their code path issues no
 // direct-to-LDS loads, so the compiler's own lgkmcnt waits order the reads.
-template <bool kDelta, bool kTok>
+template <bool kTok>
 __device__ __forceinline__ void read_pair(PairRegs& r, const lds_char* s0, const lds_char* s1, const LaneOffsets& o) {
-  constexpr int kTmOff = kTok ? kTmOffRates : kTmOffNoRates;
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const lds_char* slot = e ? s1 : s0;
@@ -213,7 +221,6 @@ __device__ __forceinline__ void read_pair(PairRegs& r, const lds_char* s0, const
     r.kt[e][1] = lds_load_tr(k + o.kt0 + 8);
     r.kt[e][2] = lds_load_tr(k + o.kt1);
     r.kt[e][3] = lds_load_tr(k + o.kt1 + 8);
-    if (kDelta) r.tm[e] = lds_load_tr(slot + kTmOff + o.tm);
     if (kTok) r.et[e] = lds_load<float4_t>(slot + kEtaOff + o.et);
   }
 }
@@ -239,13 +246,6 @@ __device__ __forceinline__ float4_t kw_minus_v(const u32x4& k0, const u32x4& k1,
   acc = MFMA32(bf8(k0), wb0, acc, 0, 0, 0);
   return MFMA32(bf8(k1), wb1, acc, 0, 0, 0);
 }
-// Delta rule: R = Tm X, with X in bf16 as the B operand and Tm in the padded A layout.
-__device__ __forceinline__ float4_t tm_apply(const u32x2& tm, const float4_t& x) {
-  const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-  const u32x4 xb = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), 0u, 0u};
-  const u32x4 tma = {tm.x, tm.y, 0u, 0u};
-  return MFMA32(bf8(tma), bf8(xb), zero, 0, 0, 0);
-}
 __device__ __forceinline__ u32x2 neg_eta_bf16(const float4_t& r, float neta) {
   const u32x2 x = {pack_bf16(neta * r[0], neta * r[1]), pack_bf16(neta * r[2], neta * r[3])};
   return x;
@@ -262,12 +262,15 @@ __device__ __forceinline__ u32x2 neg_eta_bf16(const float4_t& r, float neta, con
 //   R_{c+1} = K_{c+1} W_{c+1}^T - V_{c+1} = (K_{c+1} W^T - V_{c+1}) + M (-eta R_c),
 //             M = K_{c+1} K_c^T, because W_{c+1} = W - eta R_c^T K_c
 //   W_{c+2} = W - eta [R_c; R_{c+1}]^T [K_c; K_{c+1}]   (one K = 32 MFMA per state tile)
-// (delta rule: each R is Tm times the bracket).  Only the second R waits for the first; the
-// state update and its bf16 copy happen once per pair.  Hands off the bf16 W_c and
-// -eta R_c, -eta R_{c+1} to the output wave (pair area h; lw = 16 lane, lr = 8 lane).
+// Only the second R waits for the first; the state update and its bf16 copy happen once per
+// pair.  Delta rule: with X_e = K_e W^T - V_e of both chunks, the pair's R = X + N X in one
+// step (N = Tm - I of the pair's 32 tokens, from the Tm wave: n00 over chunk c's tokens,
+// n1 over both chunks'): R_c = X_c + N00 X_c, R_{c+1} = X_{c+1} + N10 X_c + N11 X_{c+1}.
+// Hands off the bf16 W_c and -eta R_c, -eta R_{c+1} to the output wave (pair area h;
+// lw = 16 lane, lr = 8 lane).
 template <bool kDelta, bool kTok, bool kDot>
 __device__ __forceinline__ void pair_step(WState& w, const PairRegs& r, const LaneConst& lc, lds_char* h, int lw,
-                                          int lr) {
+                                          int lr, const lds_char* nb) {
   const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
   const u32x4 wb0u = {pack_bf16(w.t0[0], w.t0[1]), pack_bf16(w.t0[2], w.t0[3]),
                       pack_bf16(w.t1[0], w.t1[1]), pack_bf16(w.t1[2], w.t1[3])};
@@ -283,18 +286,29 @@ __device__ __forceinline__ void pair_step(WState& w, const PairRegs& r, const La
     r1 = MFMA32(bf8(vpad1), lc.neg_eye, zero, 0, 0, 0);
     rn0 = kTok ? neg_eta_bf16(r0, lc.neta, r.et[0]) : neg_eta_bf16(r0, lc.neta);
     rn1 = kTok ? neg_eta_bf16(r1, lc.neta, r.et[1]) : neg_eta_bf16(r1, lc.neta);
+  } else if (kDelta) {
+    const u32x2 n00 = lds_load<u32x2>(nb + 8 * (lr >> 3));
+    const u32x4 n1 = lds_load<u32x4>(nb + 512 + 16 * (lr >> 3));
+    const float4_t x0 = kw_minus_v(r.k[0][0], r.k[0][1], r.v[0], wb0, wb1, lc);
+    const float4_t x1 = kw_minus_v(r.k[1][0], r.k[1][1], r.v[1], wb0, wb1, lc);
+    const uint32_t xa = pack_bf16(x0[0], x0[1]), xb = pack_bf16(x0[2], x0[3]);
+    const u32x4 b0 = {xa, xb, 0u, 0u};
+    const u32x4 b1 = {xa, xb, pack_bf16(x1[0], x1[1]), pack_bf16(x1[2], x1[3])};
+    const u32x4 a0 = {n00.x, n00.y, 0u, 0u};
+    r0 = MFMA32(bf8(a0), bf8(b0), x0, 0, 0, 0);
+    r1 = MFMA32(bf8(n1), bf8(b1), x1, 0, 0, 0);
+    rn0 = kTok ? neg_eta_bf16(r0, lc.neta, r.et[0]) : neg_eta_bf16(r0, lc.neta);
+    rn1 = kTok ? neg_eta_bf16(r1, lc.neta, r.et[1]) : neg_eta_bf16(r1, lc.neta);
   } else {
     r0 = kw_minus_v(r.k[0][0], r.k[0][1], r.v[0], wb0, wb1, lc);
     const float4_t a1 = kw_minus_v(r.k[1][0], r.k[1][1], r.v[1], wb0, wb1, lc);
     // M^T = K_c K_{c+1}^T in the C layout is M as the A operand: lane (g, n) = M[n][4 g + s]
     float4_t mt = MFMA32(bf8(r.k[0][0]), bf8(r.k[1][0]), zero, 0, 0, 0);
     mt = MFMA32(bf8(r.k[0][1]), bf8(r.k[1][1]), mt, 0, 0, 0);
-    if (kDelta) r0 = tm_apply(r.tm[0], r0);
     rn0 = kTok ? neg_eta_bf16(r0, lc.neta, r.et[0]) : neg_eta_bf16(r0, lc.neta);
     const u32x4 mpad = {pack_bf16(mt[0], mt[1]), pack_bf16(mt[2], mt[3]), 0u, 0u};
     const u32x4 rpad0 = {rn0.x, rn0.y, 0u, 0u};
     r1 = MFMA32(bf8(mpad), bf8(rpad0), a1, 0, 0, 0);
-    if (kDelta) r1 = tm_apply(r.tm[1], r1);
     rn1 = kTok ? neg_eta_bf16(r1, lc.neta, r.et[1]) : neg_eta_bf16(r1, lc.neta);
   }
   lds_store<u32x4>(h + lw, wb0u);
@@ -349,6 +363,93 @@ __device__ __forceinline__ u32x2 out_step(const lds_char* slot, const lds_char* 
   return out;
 }
 
+// Delta rule, a Tm wave's work for one pair of chunks (a group has two pairs, one per Tm
+// wave).  The pair's 32 tokens form one block (our derivation from the per-token write,
+// exact algebra): with L = eta stril(K K^T) diag(rates) over the 32 tokens, Tm = (I + L)^-1
+// is block lower triangular, its diagonal blocks T00, T11 are unit lower triangular (the
+// inverses of the chunks' own I + L_qq) and T10 = -T11 L10 T00.  It writes N = Tm - I as the
+// chain waves' A operands, lane-major: N00 over the first chunk's tokens (8 bytes per lane,
+// row n, columns 4 g .. 4 g + 3) and [N10 | N11] over both chunks' tokens (16 bytes).
+// A chunk's L is strictly lower triangular, so L^16 = 0 and
+//     (I + L)^-1 = (I - L)(I + L^2)(I + L^4)(I + L^8)
+// (each factor (I + L^(2^i)) times (I - L^(2^i)) leaves I - L^(2^(i+1))): three squarings and
+// three products, all bf16 MFMAs with fp32 accumulation, entirely in registers.  Every
+// matrix M is kept as two C-layout tiles, M (lane (g, n): M[4 g + e][n]) and M^T (lane (g, n):
+// M[n][4 g + e]); the C layout of M is the B operand of a product over M's rows and the C
+// layout of M^T the A operand over its columns, so (XY) = mfma(X^T, Y) and
+// (XY)^T = mfma(Y, X^T).  L and L^T come from one Gram tile (K K^T is symmetric).
+struct TmIn {
+  u32x4 k[2][2];   // chunk q's K rows for lane (g, n): K[n][8 g .. + 7], K[n][32 + 8 g .. + 7]
+  float4_t r4[2];  // chunk q's rates of tokens 4 g .. 4 g + 3 (ones without rates)
+  float rn[2];     // chunk q's rate of token n
+};
+__device__ __forceinline__ u32x4 pk4(const float4_t& x) {
+  const u32x4 u = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), 0u, 0u};
+  return u;
+}
+// T_q = (I + L_q)^-1 as the tiles T_q and T_q^T
+__device__ __forceinline__ void tm_block(const u32x4& k0, const u32x4& k1, const float4_t& r4, float rn, float eta,
+                                         int g, int n, float4_t& tC, float4_t& tT) {
+  const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  float4_t gq = MFMA32(bf8(k0), bf8(k0), zero, 0, 0, 0);
+  gq = MFMA32(bf8(k1), bf8(k1), gq, 0, 0, 0);
+  float4_t aC, aT, iC;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int row = 4 * g + e;
+    aC[e] = (n < row) ? (eta * rn) * gq[e] : 0.0f;     // L[row][n], column rate r_n
+    aT[e] = (row < n) ? (eta * r4[e]) * gq[e] : 0.0f;  // L[n][row] = eta r_row G[n][row]
+    iC[e] = (row == n) ? 1.0f : 0.0f;
+  }
+  const u32x4 aCb = pk4(aC), aTb = pk4(aT);
+  const float4_t a2C = MFMA32(bf8(aTb), bf8(aCb), zero, 0, 0, 0);
+  const float4_t a2T = MFMA32(bf8(aCb), bf8(aTb), zero, 0, 0, 0);
+  const u32x4 a2Cb = pk4(a2C), a2Tb = pk4(a2T);
+  const float4_t a4C = MFMA32(bf8(a2Tb), bf8(a2Cb), zero, 0, 0, 0);
+  const float4_t a4T = MFMA32(bf8(a2Cb), bf8(a2Tb), zero, 0, 0, 0);
+  const u32x4 a4Cb = pk4(a4C), a4Tb = pk4(a4T);
+  const float4_t a8C = MFMA32(bf8(a4Tb), bf8(a4Cb), zero, 0, 0, 0);
+  const float4_t imaC = iC - aC, imaT = iC - aT;  // I - L and its transpose
+  const u32x4 imaTb = pk4(imaT);
+  const float4_t p1C = MFMA32(bf8(imaTb), bf8(a2Cb), imaC, 0, 0, 0);  // (I - L)(I + L^2)
+  const float4_t p1T = MFMA32(bf8(a2Cb), bf8(imaTb), imaT, 0, 0, 0);
+  const u32x4 p1Tb = pk4(p1T);
+  const float4_t p2C = MFMA32(bf8(p1Tb), bf8(a4Cb), p1C, 0, 0, 0);  // ... (I + L^4)
+  const float4_t p2T = MFMA32(bf8(a4Cb), bf8(p1Tb), p1T, 0, 0, 0);
+  const u32x4 p2Tb = pk4(p2T), a8Cb = pk4(a8C);
+  tC = MFMA32(bf8(p2Tb), bf8(a8Cb), p2C, 0, 0, 0);  // ... (I + L^8)
+  tT = MFMA32(bf8(a8Cb), bf8(p2Tb), p2T, 0, 0, 0);
+}
+__device__ __forceinline__ void tm_pair(const TmIn& in, lds_char* nbuf, float eta, int lane) {
+  const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  const int g = lane >> 4;
+  const int n = lane & 15;
+  float4_t t0C, t0T, t1C, t1T;
+  tm_block(in.k[0][0], in.k[0][1], in.r4[0], in.rn[0], eta, g, n, t0C, t0T);
+  tm_block(in.k[1][0], in.k[1][1], in.r4[1], in.rn[1], eta, g, n, t1C, t1T);
+  (void)t1C;
+  // K_0 K_1^T in the C layout: lane (g, n) = G10[n][4 g + e], G10 = K_1 K_0^T, so the A
+  // operand of L10 = eta G10 diag(rates of chunk 0) over chunk 0's tokens
+  float4_t gt = MFMA32(bf8(in.k[0][0]), bf8(in.k[1][0]), zero, 0, 0, 0);
+  gt = MFMA32(bf8(in.k[0][1]), bf8(in.k[1][1]), gt, 0, 0, 0);
+  const float4_t r0 = in.r4[0];
+  const u32x4 l10 = {pack_bf16(eta * r0[0] * gt[0], eta * r0[1] * gt[1]),
+                     pack_bf16(eta * r0[2] * gt[2], eta * r0[3] * gt[3]), 0u, 0u};
+  // P = L10 T00; T10^T = -(P^T)(T11^T), whose C layout is T10 as the A operand
+  const float4_t pp = MFMA32(bf8(l10), bf8(pk4(t0C)), zero, 0, 0, 0);
+  const u32x4 pa = {pack_bf16(-pp[0], -pp[1]), pack_bf16(-pp[2], -pp[3]), 0u, 0u};
+  const u32x4 t11r = pk4(t1T);  // T11[n][4 g + e]
+  const float4_t t10 = MFMA32(bf8(pa), bf8(t11r), zero, 0, 0, 0);
+  // N = T - I over rows n, columns 4 g + e: T is unit lower triangular, so keep 4 g + e < n
+  const uint32_t sm0 = (4 * g + 0 < n ? 0x0000FFFFu : 0u) | (4 * g + 1 < n ? 0xFFFF0000u : 0u);
+  const uint32_t sm1 = (4 * g + 2 < n ? 0x0000FFFFu : 0u) | (4 * g + 3 < n ? 0xFFFF0000u : 0u);
+  const u32x4 t00r = pk4(t0T);
+  const u32x2 n00 = {t00r.x & sm0, t00r.y & sm1};
+  const u32x4 n1 = {pack_bf16(t10[0], t10[1]), pack_bf16(t10[2], t10[3]), t11r.x & sm0, t11r.y & sm1};
+  lds_store<u32x2>(nbuf + 8 * lane, n00);
+  lds_store<u32x4>(nbuf + 512 + 16 * lane, n1);
+}
+
 // Buffer resource over the rest of a sequence: base at a chunk, range = bytes left, so rows
 // past the end read as zero and stores to them are dropped.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void* base, int left) {
@@ -379,16 +480,36 @@ template <int P> struct IntTag {
   static constexpr int value = P;
 };
 
+// Roles of the waves (wave w runs on SIMD w % 4).  Plain: chain waves 0, 1; output waves
+// 2, 3, 6, 7; loaders 4, 5.  The delta rule adds two Tm waves (one per pair of a group) and
+// keeps them off the chain waves' SIMDs: chain waves 1, 2, each with a loader (5, 6) and an
+// idle wave (9, 10: barriers only); Tm waves 0, 3, each with two output waves (4, 8 and 7, 11).
+template <bool kDelta> struct Waves {
+  static constexpr int kCount = kDelta ? 12 : kThreads / 64;
+  static constexpr int kPerSimdMax = (kCount + 3) / 4;
+  static constexpr int chain(int w) { return kDelta ? (w == 1 ? 0 : w == 2 ? 1 : -1) : (w < 2 ? w : -1); }
+  static constexpr int loader(int w) { return kDelta ? (w == 5 ? 0 : w == 6 ? 1 : -1) : (w == 4 ? 0 : w == 5 ? 1 : -1); }
+  // output wave (pr, hf) as pr + 2 hf
+  static constexpr int output(int w) {
+    return kDelta ? (w == 4 ? 0 : w == 7 ? 1 : w == 8 ? 2 : w == 11 ? 3 : -1)
+                  : (w == 2 ? 0 : w == 3 ? 1 : w == 6 ? 2 : w == 7 ? 3 : -1);
+  }
+  // Tm wave for pair p of each group
+  static constexpr int tm(int w) { return kDelta ? (w == 0 ? 0 : w == 3 ? 1 : -1) : -1; }
+  static constexpr bool idle(int w) { return kDelta && (w == 9 || w == 10); }
+};
+
 template <bool kDelta, bool kTok, bool kDot>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) void linear_mfma_kernel(
-    LinearArgs a, const bf16* tmat) {
+__global__ __launch_bounds__(64 * Waves<kDelta>::kCount) __attribute__((amdgpu_waves_per_eu(
+    Waves<kDelta>::kPerSimdMax - 1, Waves<kDelta>::kPerSimdMax))) void linear_mfma_kernel(LinearArgs a) {
   using RG = Ring<kDelta, kTok>;
-  constexpr int kTmOff = kTok ? kTmOffRates : kTmOffNoRates;
   constexpr int kRing = RG::kRing;
-  __shared__ __attribute__((aligned(16))) char lds_mem[kRing * RG::kSlotBytes + kHandBytes + kStageBytes];
+  constexpr int kExtra = kDelta ? kNBytes + kTmScratch : 0;
+  __shared__ __attribute__((aligned(16))) char lds_mem[kRing * RG::kSlotBytes + kHandBytes + kStageBytes + kExtra];
   lds_char* ring = (lds_char*)(lds_mem);
   lds_char* hand = ring + kRing * RG::kSlotBytes;
   lds_char* stage = hand + kHandBytes;
+  lds_char* nring = stage + kStageBytes;  // delta rule: N operands, then the Tm wave's scratch
 
   // blockIdx = 8 kSplit (chain / 8) + 8 part + chain % 8: the parts of a chain share an XCD
   const int bidx = blockIdx.x;
@@ -410,10 +531,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   // .. + kGroup - 1) between barriers grp and grp + 1 and hand it off; output waves finish it
   // between barriers grp + 1 and grp + 2.
 
-  if (wv >= kLoaderWave && wv < kLoaderWave + kLoaderWaves) {
+  using WR = Waves<kDelta>;
+  if (WR::loader(wv) >= 0) {
     // Loader waves: stream chunk c into ring slot c % kRing with direct-to-LDS loads, wave
-    // kLoaderWave + p taking part p of every chunk (Q tile and V half tile; K tile with the
-    // rate factors and Tm^T).  Lane l of a Q/K half tile fills physical piece l % 8 of row
+    // loader wave p taking part p of every chunk (Q tile and V half tile; K tile with the
+    // rate factors).  Lane l of a Q/K half tile fills physical piece l % 8 of row
     // 8 hh + l / 8, i.e. loads that row's logical piece (l % 8) ^ sig(l / 8); lane l of the
     // V load fills physical piece l % 4 of row l / 4 from this workgroup's 64-byte half of
     // the V row.
@@ -424,15 +546,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
     const int lglob = lrow * 128 + (((lane & 7) ^ sig(lrow)) * 16);
     const int vrow = lane >> 2;
     const int vglob = vrow * 128 + part * (kHalfCols * 2) + (((lane & 3) ^ ((vrow >> 1) & 3)) * 16);
-    const char* tsrc = reinterpret_cast<const char*>(tmat) +
-                       (kDelta ? static_cast<size_t>(chain) * nchunks * kTmBytes : 0);
     const char* esrc = kTok ? reinterpret_cast<const char*>(a.eta_tok + static_cast<size_t>(chain) * T) : nullptr;
     // Chain waves read chunks 0, 1 after barrier 0 and chunks up to kGroup b + kGroup + 1
-    // after barrier b (one pair ahead); output waves read chunks kGroup (b - 1) .. kGroup b - 1 after barrier
-    // b.  So barrier b must publish the chunks up to kGroup b + kGroup + 1, and from b = 2 on it
-    // frees the slots of the chunks up to kGroup b - kGroup - 1 (barriers 0 and 1 free
-    // nothing), after which each loader refills the ring up to chunk kGroup b - kGroup - 1 +
-    // kRing.
+    // after barrier b (one pair ahead); the delta rule's Tm wave reads chunks kGroup (b + 1) ..
+    // kGroup b + 2 kGroup - 1 after barrier b; output waves read chunks kGroup (b - 1) .. kGroup b - 1
+    // after barrier b.  So barrier b must publish the chunks up to kGroup b + kGroup + 1 + kAhead,
+    // and from b = 2 on it frees the slots of the chunks up to kGroup b - kGroup - 1 (barriers 0
+    // and 1 free nothing), after which each loader refills the ring up to chunk
+    // kGroup b - kGroup - 1 + kRing.
     auto stream = [&](auto part_tag) {
       constexpr int P = decltype(part_tag)::value;
       auto issue = [&](int c) {
@@ -451,12 +572,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
             const __amdgpu_buffer_rsrc_t re = chunk_rsrc(esrc + c * kEtaBytes, T * 4 - c * kEtaBytes);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(re, dst + kEtaOff, 4, lane * 4, 0, 0, kNT);
           }
-          if (kDelta && lane < 32) {
-            // Tm^T of chunk c: 512 bytes, 16 per lane (zeros past the last chunk)
-            const __amdgpu_buffer_rsrc_t rs =
-                chunk_rsrc(tsrc + static_cast<size_t>(c) * kTmBytes, c < nchunks ? kTmBytes : 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + kTmOff, 16, lane * 16, 0, 0, kNT);
-          }
         }
       };
       for (int c = 0; c < kRing; ++c) issue(c);
@@ -473,7 +588,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
         }
       }
     };
-    if (wv == kLoaderWave) {
+    if (WR::loader(wv) == 0) {
       stream(IntTag<0>{});
     } else {
       stream(IntTag<1>{});
@@ -486,15 +601,67 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   o.ka0 = swz(n, g) * 16;
   o.ka1 = swz(n, 4 + g) * 16;
 
-  if (wv >= kChainWaves) {
+  if (WR::idle(wv)) {
+    for (int b = 0; b <= ngroups; ++b) lds_barrier();  // barriers 0 .. ngroups
+    return;
+  }
+  if (WR::tm(wv) >= 0) {
+    // Tm wave for pair tp of every group: the pair corrections N of group 0 from global memory
+    // before barrier 0, then of group grp + 1 from the ring between barriers grp and grp + 1
+    // (published at barrier grp), into N buffer (grp + 1) & 1, which the chain waves read
+    // after barrier grp + 1.
+    const int tp = WR::tm(wv);
+    const float eta = a.eta;
+    const float* etok = kTok ? a.eta_tok + static_cast<size_t>(chain) * T : nullptr;
+    {
+      const char* ksrc = reinterpret_cast<const char*>(static_cast<const bf16*>(a.k) + tok0);
+      TmIn in;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int c = 2 * tp + q;
+        const int off = c * kTileBytes;
+        const __amdgpu_buffer_rsrc_t rk = chunk_rsrc(ksrc + off, seq_bytes - off);
+        in.k[q][0] = __builtin_amdgcn_raw_buffer_load_b128(rk, n * 128 + 16 * g, 0, 0);
+        in.k[q][1] = __builtin_amdgcn_raw_buffer_load_b128(rk, n * 128 + 64 + 16 * g, 0, 0);
+        in.r4[q] = float4_t{1.0f, 1.0f, 1.0f, 1.0f};
+        in.rn[q] = 1.0f;
+        if (kTok) {
+          const __amdgpu_buffer_rsrc_t re = chunk_rsrc(etok + c * kB, (T - c * kB) * 4);
+          in.r4[q] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(re, 16 * g, 0, 0));
+          in.rn[q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(re, 4 * n, 0, 0));
+        }
+      }
+      tm_pair(in, nring + tp * kNPair, eta, lane);
+    }
+    lds_barrier();  // barrier 0
+    for (int grp = 0; grp < ngroups; ++grp) {
+      if (grp + 1 < ngroups) {
+        const int c0 = kGroup * (grp + 1) + 2 * tp;
+        TmIn in;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const lds_char* slot = ring + ((c0 + q) % kRing) * RG::kSlotBytes;
+          in.k[q][0] = lds_load<u32x4>(slot + kTileBytes + o.ka0);
+          in.k[q][1] = lds_load<u32x4>(slot + kTileBytes + o.ka1);
+          in.r4[q] = kTok ? lds_load<float4_t>(slot + kEtaOff + 16 * g) : float4_t{1.0f, 1.0f, 1.0f, 1.0f};
+          in.rn[q] = kTok ? lds_load<float>(slot + kEtaOff + 4 * n) : 1.0f;
+        }
+        tm_pair(in, nring + ((grp + 1) & 1) * kNGroup + tp * kNPair, eta, lane);
+      }
+      lds_barrier();  // barrier grp + 1
+    }
+    return;
+  }
+
+  if (WR::chain(wv) < 0) {
     // Output wave (pr, hf): chunk hf of pair pr of every group, Z columns 32 part .. + 31 (the
     // row blocks of both chain waves).  Lane (g, n) holds token n, columns 16 ow + 4 g .. + 3
     // of block ow; the wave restages the two blocks row-major in its own 1 KB of LDS and
     // stores 16 bytes per lane, 64 bytes of each of the chunk's 16 rows, non-temporal like
     // the loads (rows past T are dropped by the buffer range).  The stores of a block of kRing chunks share one buffer
     // resource, rebased once per block.
-    const int pr = wv & 1;
-    const bool hf = wv >= kLoaderWave + kLoaderWaves;
+    const int pr = WR::output(wv) & 1;
+    const bool hf = WR::output(wv) >= 2;
     lds_char* zst = stage + (pr + (hf ? 2 : 0)) * (kStageBytes / 4);
     char* z = reinterpret_cast<char*>(static_cast<bf16*>(a.z) + tok0);
     const uint32_t pmask0 = (4 * g + 0 <= n ? 0x0000FFFFu : 0u) | (4 * g + 1 <= n ? 0xFFFF0000u : 0u);
@@ -533,7 +700,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   }
 
   // Chain waves: wave w of part p owns output rows i0 .. i0 + 15, i0 = 32 p + 16 w.
-  const int i0 = kHalfCols * part + 16 * wv;
+  const int cw = WR::chain(wv);
+  const int i0 = kHalfCols * part + 16 * cw;
   const int bi = chain / a.H;
   const int hi = chain - bi * a.H;
   const float* w0 = a.w0 + bi * a.w0_batch_stride + static_cast<long long>(hi) * kD * kD;
@@ -557,16 +725,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   }
   o.kt0 = swz(4 * g + (n >> 2), n & 3) * 16;
   o.kt1 = swz(4 * g + (n >> 2), 4 + (n & 3)) * 16;
-  o.vv = vswz(n, 2 * wv + (g >> 1)) * 16 + 8 * (g & 1);
-  o.tm = (4 * g + (n >> 2)) * 32 + 8 * (n & 3);
+  o.vv = vswz(n, 2 * cw + (g >> 1)) * 16 + 8 * (g & 1);
   o.et = 16 * g;
 
   // Pair step p computes chunks 2p, 2p + 1 from registers read in step p - 1 while reading
   // chunks 2p + 2, 2p + 3.  Chunks past the end read as zeros and leave the state unchanged.
-  lds_char* hw = hand + wv * kHandWave;
+  lds_char* hw = hand + cw * kHandWave;
   lds_barrier();  // barrier 0: chunks 0 .. kGroup + 1 published
   PairRegs ra, rb;
-  read_pair<kDelta, kTok>(ra, ring, ring + RG::kSlotBytes, o);
+  read_pair<kTok>(ra, ring, ring + RG::kSlotBytes, o);
   for (int gbase = 0; gbase < ngroups; gbase += kRing / kGroup) {
 #pragma unroll
     for (int gg = 0; gg < kRing / kGroup; ++gg) {
@@ -581,8 +748,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
         const PairRegs& cur = (x & 2) ? rb : ra;
         PairRegs& nxt = (x & 2) ? ra : rb;
         __builtin_amdgcn_sched_barrier(0);  // keep steps apart (register pressure)
-        read_pair<kDelta, kTok>(nxt, ring + s2 * RG::kSlotBytes, ring + s3 * RG::kSlotBytes, o);
-        pair_step<kDelta, kTok, kDot>(wacc, cur, lc, hg + (x / 2) * kHandPair, lw, lr);
+        read_pair<kTok>(nxt, ring + s2 * RG::kSlotBytes, ring + s3 * RG::kSlotBytes, o);
+        pair_step<kDelta, kTok, kDot>(wacc, cur, lc, hg + (x / 2) * kHandPair, lw, lr,
+                                      nring + (grp & 1) * kNGroup + (x / 2) * kNPair);
       }
     }
   }
@@ -624,134 +792,34 @@ hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s) {
   const long long nblocks = mfma_grid(a);
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(nblocks)), block(kThreads);
-  const bf16* none = nullptr;
   if (a.dot_loss) {
     if (a.eta_tok)
-      hipLaunchKernelGGL((linear_mfma_kernel<false, true, true>), grid, block, 0, s, a, none);
+      hipLaunchKernelGGL((linear_mfma_kernel<false, true, true>), grid, block, 0, s, a);
     else
-      hipLaunchKernelGGL((linear_mfma_kernel<false, false, true>), grid, block, 0, s, a, none);
+      hipLaunchKernelGGL((linear_mfma_kernel<false, false, true>), grid, block, 0, s, a);
   } else {
     if (a.eta_tok)
-      hipLaunchKernelGGL((linear_mfma_kernel<false, true, false>), grid, block, 0, s, a, none);
+      hipLaunchKernelGGL((linear_mfma_kernel<false, true, false>), grid, block, 0, s, a);
     else
-      hipLaunchKernelGGL((linear_mfma_kernel<false, false, false>), grid, block, 0, s, a, none);
+      hipLaunchKernelGGL((linear_mfma_kernel<false, false, false>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------------------------ delta rule
 
-// Tm = (I + eta stril(K K^T) diag(eta_tok))^-1 for every chunk of every chain (diag(eta_tok)
-// = I without per-token rates: the write of token s carries its own rate, so column s of
-// the strict lower triangle is scaled by it), stored transposed in bf16:
-// [chain][chunk][j][t] = Tm[t][j] (row j of the stored tile is column j of Tm).  One wave
-// per 4 chunks: the wave forms the Gram matrix G = K K^T of each chunk with two MFMAs (K
-// rows loaded straight into the operand layout; the A and B operands of K K^T are the same
-// registers), stages L = eta stril(G) in LDS, and then lane (q, j) solves column j of chunk
-// q by forward substitution in fp32, Tm[t][j] = [t == j] - sum_{s<t} L[t][s] Tm[s][j]
-// (the 16 lanes of a chunk read the same L row, a broadcast).  Rows past the end of the
-// sequence have zero keys, so their rows of Tm are unit rows.
-constexpr int kTmWaves = 4;
-constexpr int kTmChunksPerWave = 4;
-__global__ __launch_bounds__(64 * kTmWaves) void delta_tmat_kernel(const bf16* __restrict__ k, bf16* __restrict__ tmt,
-                                                                 int T, int nchunks, long long total, float eta,
-                                                                 const float* __restrict__ etok) {
-  __shared__ float ls[kTmWaves][kTmChunksPerWave][kB][kB];
-  const int wv = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int g = lane >> 4;
-  const int n = lane & 15;
-  const long long id0 = (static_cast<long long>(blockIdx.x) * kTmWaves + wv) * kTmChunksPerWave;
-  const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int q = 0; q < kTmChunksPerWave; ++q) {
-    const long long id = id0 + q;  // uniform in the wave
-    float4_t gacc = zero;
-    float rate = eta;
-    if (id < total) {
-      const long long chain = id / nchunks;
-      const int c = static_cast<int>(id - chain * nchunks);
-      if (etok) {  // uniform: rate factor of token n of the chunk (zero past T)
-        const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<float*>(etok + static_cast<size_t>(chain) * T + static_cast<size_t>(c) * kB), 0,
-            (T - c * kB) * 4, 0x00020000);
-        rate = eta * __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(re, n * 4, 0, 0));
-      }
-      const bf16* kc = k + (static_cast<size_t>(chain) * T + static_cast<size_t>(c) * kB) * kD;
-      const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(kc), 0, (T - c * kB) * kD * 2, 0x00020000);
-      // lane (g, n): K[n][8 g .. 8 g + 7] and K[n][32 + 8 g ..]; rows past T read as zero
-      const u32x4 k0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, n * 128 + 16 * g, 0, 0));
-      const u32x4 k1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, n * 128 + 64 + 16 * g, 0, 0));
-      gacc = MFMA32(bf8(k0), bf8(k0), zero, 0, 0, 0);
-      gacc = MFMA32(bf8(k1), bf8(k1), gacc, 0, 0, 0);
-    }
-    // lane (g, n) holds G[4 g + e][n]; keep the strict lower triangle, scaled by the rate of
-    // token n (column)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) ls[wv][q][4 * g + e][n] = (n < 4 * g + e) ? rate * gacc[e] : 0.0f;
-  }
-  __syncthreads();
-  // lane (q, j): column j of chunk q
-  const int q = g;
-  const int j = n;
-  const float* lq = &ls[wv][q][0][0];
-  float x[kB];
-#pragma unroll
-  for (int t = 0; t < kB; ++t) {
-    float acc = (t == j) ? 1.0f : 0.0f;
-#pragma unroll
-    for (int s4 = 0; s4 < t; s4 += 4) {
-      const float4_t l4 = *reinterpret_cast<const float4_t*>(lq + t * kB + s4);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (s4 + u < t) acc -= l4[u] * x[s4 + u];
-    }
-    x[t] = acc;
-  }
-  const long long id = id0 + q;
-  if (id < total) {
-    u32x4 lo, hi;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      lo[u] = pack_bf16(x[2 * u], x[2 * u + 1]);
-      hi[u] = pack_bf16(x[8 + 2 * u], x[8 + 2 * u + 1]);
-    }
-    u32x4* out = reinterpret_cast<u32x4*>(tmt + static_cast<size_t>(id) * kB * kB + j * kB);
-    out[0] = lo;
-    out[1] = hi;
-  }
-}
-
 bool delta_fast_supported(const LinearArgs& a, bool bf16_io) {
   return bf16_io && mfma_shape_ok(a);
 }
 
-size_t delta_workspace_bytes(const LinearArgs& a) {
-  const long long nchunks = (a.T + kB - 1) / kB;
-  return static_cast<size_t>(a.B) * a.H * nchunks * kTmBytes;
-}
-
-hipError_t launch_delta_fast(const LinearArgs& a, void* workspace, hipStream_t s) {
-  const long long nchains = static_cast<long long>(a.B) * a.H;
-  const int nchunks = (a.T + kB - 1) / kB;
-  const long long total = nchains * nchunks;
-  constexpr int kPerBlock = kTmWaves * kTmChunksPerWave;
-  const long long nblocks = (total + kPerBlock - 1) / kPerBlock;
-  if (nchains > 0x7fffffffLL || nblocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  bf16* tm = static_cast<bf16*>(workspace);
-  hipLaunchKernelGGL(delta_tmat_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(64 * kTmWaves), 0, s,
-                     static_cast<const bf16*>(a.k), tm, a.T, nchunks, total, a.eta, a.eta_tok);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+hipError_t launch_delta_fast(const LinearArgs& a, hipStream_t s) {
   const long long nmain = mfma_grid(a);
   if (nmain > 0x7fffffffLL) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(nmain)), block(64 * Waves<true>::kCount);
   if (a.eta_tok)
-    hipLaunchKernelGGL((linear_mfma_kernel<true, true, false>), dim3(static_cast<unsigned>(nmain)), dim3(kThreads),
-                       0, s, a, static_cast<const bf16*>(tm));
+    hipLaunchKernelGGL((linear_mfma_kernel<true, true, false>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((linear_mfma_kernel<true, false, false>), dim3(static_cast<unsigned>(nmain)), dim3(kThreads),
-                       0, s, a, static_cast<const bf16*>(tm));
+    hipLaunchKernelGGL((linear_mfma_kernel<true, false, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 

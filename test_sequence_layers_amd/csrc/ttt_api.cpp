@@ -314,11 +314,8 @@ int delta_rule_fwd(const void* q, const void* k, const void* v, const float* w0,
   ttt::LinearArgs a{q, k, v, w0, w0_batch_stride, z, w_out, B, H, T, d, 1, 1, eta, eta_tok, 0};
   const bool bf16 = io_dtype == TTT_BF16;
   hipError_t e;
-  StreamBuffer ws;
   if (ttt::delta_fast_supported(a, bf16)) {
-    rc = get_workspace(ttt::delta_workspace_bytes(a), s, &ws);
-    if (rc != TTT_OK) return rc;
-    e = ttt::launch_delta_fast(a, ws.ptr, s);
+    e = ttt::launch_delta_fast(a, s);
   } else {
     e = ttt::launch_linear_generic(a, bf16, s);
   }
