@@ -178,10 +178,24 @@ def time_backward(w, steps, warmup, torch, ttt, rates=False):
     return {"ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3)}
 
 
-def cpu_baseline(w, budget_s=15.0):
-    """Time the CPU oracle (float64, as it stands) on a bounded sample of the workload:
-    full-length sequences of a few (batch, head) chains.  Returns tokens/s scaled to the
-    metric's unit (a token counts once across its H heads)."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(w, budget_s=1.5, repeats=3):
+    """Time the CPU oracle (the NumPy recurrence as it stands) on a bounded sample of the
+    workload: full-length sequences of up to B*H (batch, head) chains, repeated in passes so
+    one run takes about budget_s.  Median of `repeats` runs each in float32 with every host
+    core, float32 with one thread and float64 with every core (about 15 s of CPU work in
+    all); tokens/s scaled to the metric's unit (a token counts once across its H heads)."""
     import numpy as np
     try:
         from threadpoolctl import threadpool_limits
@@ -190,35 +204,63 @@ def cpu_baseline(w, budget_s=15.0):
     from oracle import ttt_oracle as O
     from test_sequence_layers_amd.workloads import make_inputs
 
-    def run(n_chains):
+    def run(n_chains, dtype, passes=1):
         x = make_inputs(w, B=1, H=n_chains)
         t0 = time.perf_counter()
-        if w.kind == "linear":
-            O.ttt_linear(x["q"], x["k"], x["v"], x["w0"], w.eta, w.chunk, w.causal)
-        elif w.kind == "delta":
-            O.delta_rule(x["q"], x["k"], x["v"], x["w0"], w.eta)
-        else:
-            O.ttt_mlp(x["q"], x["k"], x["v"], x["w1"], x["w2"], w.eta, w.chunk, w.causal)
+        for _ in range(passes):
+            if w.kind == "linear":
+                O.ttt_linear(x["q"], x["k"], x["v"], x["w0"], w.eta, w.chunk, w.causal, dtype=dtype)
+            elif w.kind == "delta":
+                O.delta_rule(x["q"], x["k"], x["v"], x["w0"], w.eta, dtype=dtype)
+            else:
+                O.ttt_mlp(x["q"], x["k"], x["v"], x["w1"], x["w2"], w.eta, w.chunk, w.causal,
+                          dtype=dtype)
         return time.perf_counter() - t0
 
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    if ctx:
-        ctx.__enter__()
     try:
-        t1 = run(1)
-        n = int(max(1, min(w.B * w.H, budget_s / max(t1, 1e-6))))
-        tn = run(n) if n > 1 else t1
-    finally:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count() or 1
+
+    def timed(threads, dtype):
+        """(sequences, passes, median seconds, tokens/s): passes over up to B*H sequences,
+        enough for one run to take about budget_s."""
+        ctx = threadpool_limits(limits=threads) if threadpool_limits else None
         if ctx:
-            ctx.__exit__(None, None, None)
-    head_tokens = n * w.T
+            ctx.__enter__()
+        try:
+            t1 = run(1, dtype)
+            n = int(max(1, min(w.B * w.H, budget_s / max(t1, 1e-6))))
+            tn = run(n, dtype)
+            passes = int(max(1, round(budget_s / max(tn, 1e-6))))
+            ts = sorted(run(n, dtype, passes) for _ in range(repeats))
+        finally:
+            if ctx:
+                ctx.__exit__(None, None, None)
+        tm = ts[len(ts) // 2]
+        return n, passes, tm, n * passes * w.T / w.H / tm
+
+    n_all, p_all, t_all, v_all = timed(cores, np.float32)
+    n_one, p_one, t_one, v_one = timed(1, np.float32)
+    n_64, p_64, t_64, v_64 = timed(cores, np.float64)
     return {
-        "value": head_tokens / w.H / tn,
+        "value": v_all,
         "unit": "tokens/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
-        "sample": f"{n} of {w.B * w.H} (batch, head) sequences at full length T={w.T}, "
-                  f"float64 NumPy, one thread, {tn:.1f} s",
+        "sample": f"{n_all} of the {w.B * w.H} (batch, head) sequences at full length T={w.T}, "
+                  f"{p_all} pass(es) per run, float32 NumPy, median of {repeats} runs "
+                  f"({t_all:.2f} s each) with {cores} threads allowed",
+        "one_thread": {"value": v_one, "unit": "tokens/s", "cores": 1,
+                       "sample": f"{n_one} sequences x {p_one} pass(es), median of {repeats} "
+                                 f"runs ({t_one:.2f} s each)"},
+        "float64": {"value": v_64, "unit": "tokens/s", "cores": cores,
+                    "sample": f"{n_64} sequences x {p_64} pass(es), median of {repeats} runs "
+                              f"({t_64:.2f} s each)"},
+        "cpu_model": _cpu_model(),
+        "note": "the oracle steps through the tokens in Python, each step a few NumPy calls "
+                "on small matrices batched over the sampled sequences, so the thread count "
+                "barely changes it",
     }
 
 
@@ -240,7 +282,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "bench.py measures one GPU only (every GPU would run its own "
+                                   "share of the independent sequences); --gpus must be 1"}))
         sys.exit(2)
     for key in ("RANK", "WORLD_SIZE"):
         if int(os.environ.get(key, "0" if key == "RANK" else "1")) not in (0, 1):
@@ -267,32 +310,38 @@ def main():
     w = workload(args.workload)
     res = time_workload(w, args.steps, args.warmup, torch, ttt, rotate=args.rotate,
                         rates=args.token_rates)
-    if w.kind == "mlp":
-        # dense bf16 contractions: priced against the matrix-core peak
-        kern = "mlp_mfma_kernel" if w.causal else "mlp_nc_mfma_kernel"
-        roofline = {
-            "bound": "mfma",
-            "achieved": round(res["tflops"], 2),
-            "peak": BF16_MFMA_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(res["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4),
-            "traffic": None if args.token_rates else measured_traffic(w.name),
-            "kernel": f"{kern} (per launch: the method's flops, tril products at half)",
-            "flops_per_launch": res["flops"],
-        }
-    else:
-        kern = ("linear_mfma_kernel" if w.kind == "linear"
-                else "delta_tmat_kernel + linear_mfma_kernel (whole call)")
-        roofline = {
+
+    def roofline_of(wl, r, rates=False):
+        if wl.kind == "mlp":
+            # dense bf16 contractions: priced against the matrix-core peak
+            kern = "mlp_mfma_kernel" if wl.causal else "mlp_nc_kernel"
+            return {
+                "bound": "mfma",
+                "achieved": round(r["tflops"], 2),
+                "peak": BF16_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s",
+                "frac": round(r["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4),
+                "traffic": None if rates else measured_traffic(wl.name),
+                "kernel": f"{kern} (per launch: the method's flops, tril products at half)",
+                "flops_per_launch": r["flops"],
+            }
+        kern = "linear_mfma_kernel" if wl.kind == "linear" else "linear_mfma_kernel (delta rule)"
+        return {
             "bound": "hbm",
-            "achieved": round(res["hbm_gbs"], 1),
+            "achieved": round(r["hbm_gbs"], 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(res["hbm_gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": None if args.token_rates else measured_traffic(w.name),
+            "frac": round(r["hbm_gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": None if rates else measured_traffic(wl.name),
             "kernel": f"{kern} (per launch: Q,K,V read + Z written + W0 read)",
-            "bytes_per_launch": res["bytes"],
+            "bytes_per_launch": r["bytes"],
         }
+
+    roofline = roofline_of(w, res, args.token_rates)
+    # the MFMA half of the metric: the matrix-core-bound d = 64, T = 2048 workload (the causal
+    # TTT-MLP, hidden 256), timed here as a first-class figure next to the headline
+    mw = workload("mlp_h256_T2048")
+    mres = res if w.name == mw.name else time_workload(mw, max(10, args.steps // 2), 5, torch, ttt)
     line = {
         "metric": "TTT-layer fwd tokens/sec at d=64,T=2048 + MFMA util % (1 MI355X)",
         "value": round(res["tokens_per_s"], 1),
@@ -310,16 +359,22 @@ def main():
                    "chunk": w.chunk, "causal": w.causal, "eta": w.eta, "state": "f32",
                    "per_token_rates": bool(args.token_rates),
                    "rotated_input_sets": res["rotated_sets"]},
-        "mfma_util_pct": round(100 * res["tflops"] / BF16_MFMA_PEAK_TFLOPS, 3),
-        "mfma_util_rocprof_pct": None if args.token_rates else measured_mfma_util(w.name),
+        "mfma_util_pct": round(100 * mres["tflops"] / BF16_MFMA_PEAK_TFLOPS, 3),
+        "mfma_util_workload": mw.name,
+        "mfma_util_rocprof_pct": measured_mfma_util(mw.name),
         "roofline": roofline,
+        "roofline_mfma": dict(roofline_of(mw, mres), workload=mw.name,
+                              tokens_per_s=round(mres["tokens_per_s"], 1),
+                              ms_per_step=round(mres["ms_per_step"], 5)),
+        "headline_mfma_util_pct": round(100 * res["tflops"] / BF16_MFMA_PEAK_TFLOPS, 3),
+        "headline_mfma_util_rocprof_pct": None if args.token_rates else measured_mfma_util(w.name),
     }
     if not args.no_others:
         others = {}
         for o in WORKLOADS:
             if o.name == w.name:
                 continue
-            r = time_workload(o, max(10, args.steps // 2), 5, torch, ttt)
+            r = mres if o.name == mw.name else time_workload(o, max(10, args.steps // 2), 5, torch, ttt)
             others[o.name] = {
                 "tokens_per_s": round(r["tokens_per_s"], 1),
                 "ms_per_step": round(r["ms_per_step"], 5),

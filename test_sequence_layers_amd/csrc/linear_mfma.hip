@@ -20,23 +20,24 @@
 // The same holds for a pair of chunks taken as one block of 32 tokens: the kernel applies
 // the pair's 32 x 32 Tm = I + N at once, R = X + N X (X = K W^T - V of both chunks, exact
 // in fp32, plus a correction with bf16 operands).  N depends only on K (and the rates), so
-// a Tm wave of the workgroup computes it one group of chunks ahead, from the K tiles in the
-// ring (tm_group below); nothing is read from or written to global memory for it.
+// two Tm waves of the workgroup compute it one group of chunks ahead, from the K tiles in
+// the ring (tm_pair below), and hand it to the chain waves through LDS; nothing is read
+// from or written to global memory for it.
 //
 // Mapping.  The linear model is separable by output row (row i of W only needs v[i]), so a
 // (batch, head) chain is split over kSplit = 2 workgroups of 32 output rows each; within a
 // workgroup, chain wave w owns 16 rows and never exchanges state with the other chain wave.
 // The two workgroups of a chain get block indices that are equal mod 8, which places them
 // on the same XCD, so their reads of the chain's Q and K meet in one L2.
-// Work per workgroup, each on its own SIMD:
+// Work per workgroup (the wave roles are listed in Waves<> below):
 //   * two chain waves run the state recursion only, two chunks per step (below), and hand
-//     each pair's bf16 start state and -eta R to an output wave through LDS;
-//   * two output waves form each chunk's Z one group of chunks later and store it;
-//   * a loader wave streams chunks into an LDS ring with direct-to-LDS buffer loads (no
-//     registers are spent on data in flight).  What bounds the kernel is this stream: a
-//     compute unit takes in at most about 38 GB/s (one 128-byte line per ~7 cycles, with
-//     the non-temporal policy), and a chunk costs a workgroup 48 lines (Q, K and V; the V
-//     half-rows cost whole lines).
+//     each pair's bf16 start state and -eta R to the output waves through LDS;
+//   * four output waves form each chunk's Z one group of chunks later and store it;
+//   * two loader waves stream chunks into an LDS ring with direct-to-LDS buffer loads (no
+//     registers are spent on data in flight).  A compute unit takes in about 38 GB/s from
+//     one loader wave (one 128-byte line per ~7 cycles, with the non-temporal policy), and
+//     a chunk costs a workgroup 48 lines (Q, K and V; the V half-rows cost whole lines);
+//   * for the delta rule, two Tm waves form the pair inverses of the next group of chunks.
 // One barrier per group of 4 chunks publishes chunks and handoffs and recycles ring slots and
 // handoff buffers.  The chain waves read a pair's operands one step ahead.  Loops are
 // unrolled over the whole ring, so every LDS address is a per-lane base plus an immediate.
@@ -89,8 +90,10 @@ constexpr int kTileBytes = kB * kD * 2;  // one 16 x 64 bf16 chunk of one tensor
 constexpr int kChainWaves = 2;
 constexpr int kOutWaves = kChainWaves;
 // Waves of a workgroup (Waves<> below): two chain waves, four output waves (two for the first
-// chunk of each pair, two for the second), two loaders, and for the delta rule a Tm wave.
-// Waves are placed on the four SIMDs in turn; each chain wave shares its SIMD with a loader.
+// chunk of each pair, two for the second), two loaders, and for the delta rule two Tm waves
+// and two idle ones.  Waves are placed on the four SIMDs in turn (wave w on SIMD w % 4); each
+// chain wave shares its SIMD only with a loader (and, for the delta rule, an idle wave), and
+// each delta Tm wave shares its SIMD with two output waves.
 // Each output wave forms all of the workgroup's 32 Z columns of its chunk, so that one
 // 16-byte store per lane writes the chunk's rows (a compute unit's memory pipeline pays per
 // row piece touched, and loads and stores share it).  Two loader waves (Q and V; K with the
@@ -159,7 +162,6 @@ constexpr int kStageBytes = 4 * kB * kHalfCols * 2;
 constexpr int kNPair = 64 * 8 + 64 * 16;
 constexpr int kNGroup = (kGroup / 2) * kNPair;
 constexpr int kNBytes = 2 * kNGroup;
-constexpr int kTmScratch = 0;
 
 // Swizzle of the 128-byte Q/K rows: logical 16-byte piece p of row r sits at piece
 // p ^ sig(r).  sig is a bijection on r mod 8, so the 8 lanes of a 16-byte row read (rows
@@ -504,7 +506,7 @@ __global__ __launch_bounds__(64 * Waves<kDelta>::kCount) __attribute__((amdgpu_w
     Waves<kDelta>::kPerSimdMax - 1, Waves<kDelta>::kPerSimdMax))) void linear_mfma_kernel(LinearArgs a) {
   using RG = Ring<kDelta, kTok>;
   constexpr int kRing = RG::kRing;
-  constexpr int kExtra = kDelta ? kNBytes + kTmScratch : 0;
+  constexpr int kExtra = kDelta ? kNBytes : 0;
   __shared__ __attribute__((aligned(16))) char lds_mem[kRing * RG::kSlotBytes + kHandBytes + kStageBytes + kExtra];
   lds_char* ring = (lds_char*)(lds_mem);
   lds_char* hand = ring + kRing * RG::kSlotBytes;
