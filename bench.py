@@ -36,7 +36,7 @@ def algorithmic_cost(w, epochs=1):
         b = 1 if w.kind == "delta" else min(w.chunk, w.T)
         # R = K W^T - V, Q W^T, W update: 3 x 2 d^2 per head-token; tril(QK^T) and P R:
         # 2 x (b/2) x 2d ... counted as 2 b d per head-token.
-        fl = w.B * w.H * w.T * ((4 * epochs + 2) * w.d * w.d + (2 * b * w.d if b > 1 else 0))
+        fl = w.B * w.H * w.T * ((4 * epochs + 2) * w.d * w.d + (2 * b * w.d if b > 1 and w.causal else 0))
     else:
         state = 2 * w.H * w.d * w.h * 4
         b = min(w.chunk, w.T)
@@ -44,6 +44,16 @@ def algorithmic_cost(w, epochs=1):
         per = (10 * epochs + 4) * w.d * w.h + (2 * b * (w.d + w.h) if w.causal else 0)
         fl = w.B * w.H * w.T * per
     return 4 * tok + state, fl
+
+
+def named_workload(name):
+    """A workload of the method by name: the five measured workloads, and the non-causal
+    TTT-Linear layer at the vision workload's shape (B 64, H 6, N 196, d 64; one full-batch
+    step at eta 1, raw keys), the linear inner model of the same setting."""
+    from test_sequence_layers_amd.workloads import workload
+    if name == "linear_nc_N196":
+        return workload("mlp_vision_N196").replace(name=name, kind="linear", h=0)
+    return workload(name)
 
 
 def _profile_record(workload_name, kind):
@@ -307,7 +317,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
 
-    w = workload(args.workload)
+    w = named_workload(args.workload)
     res = time_workload(w, args.steps, args.warmup, torch, ttt, rotate=args.rotate,
                         rates=args.token_rates)
 
@@ -325,7 +335,8 @@ def main():
                 "kernel": f"{kern} (per launch: the method's flops, tril products at half)",
                 "flops_per_launch": r["flops"],
             }
-        kern = "linear_mfma_kernel" if wl.kind == "linear" else "linear_mfma_kernel (delta rule)"
+        kern = ("linear_mfma_kernel (delta rule)" if wl.kind == "delta"
+                else "linear_mfma_kernel" if wl.causal else "linear_nc_kernel")
         return {
             "bound": "hbm",
             "achieved": round(r["hbm_gbs"], 1),
@@ -393,6 +404,12 @@ def main():
         variants.append((w, "+dot_loss", dict(loss="dot")))
         variants += [(o, "+dot_loss", dict(loss="dot")) for o in WORKLOADS
                      if o.name == "mlp_vision_N196"]
+        # the non-causal TTT-Linear layer at the vision shape (one full-batch step), with the
+        # reconstruction and the dot-product loss
+        lnc = named_workload("linear_nc_N196")
+        if w.name != lnc.name:
+            variants.append((lnc, "", {}))
+        variants.append((lnc, "+dot_loss", dict(loss="dot")))
         # the vision workload in four consecutive mini-batches of 49 pairs, two epochs
         # (eta 0.01: at eta 1 several steps diverge)
         variants += [(o.replace(chunk=49, eta=0.01), "+chunk49_epochs2", dict(epochs=2))

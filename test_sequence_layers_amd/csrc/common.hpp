@@ -165,6 +165,8 @@ bool delta_fast_supported(const LinearArgs& a, bool bf16_io);
 hipError_t launch_delta_fast(const LinearArgs& a, hipStream_t s);
 bool mlp_fast_supported(const MlpArgs& a, bool bf16_io);
 hipError_t launch_mlp_fast(const MlpArgs& a, hipStream_t s);
+bool linear_nc_supported(const LinearArgs& a, bool bf16_io);
+hipError_t launch_linear_nc(const LinearArgs& a, hipStream_t s);
 bool mlp_nc_supported(const MlpArgs& a, bool bf16_io);
 hipError_t launch_mlp_nc(const MlpArgs& a, hipStream_t s);
 

@@ -156,6 +156,8 @@ int linear_fwd(const char* fn, const void* q, const void* k, const void* v, cons
   hipError_t e;
   if (ttt::linear_mfma_supported(a, bf16))
     e = ttt::launch_linear_mfma(a, s);
+  else if (ttt::linear_nc_supported(a, bf16))
+    e = ttt::launch_linear_nc(a, s);
   else if (ttt::linear_ln_mfma_supported(a, bf16))
     e = ttt::launch_linear_ln_mfma(a, s);
   else

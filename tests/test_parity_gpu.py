@@ -320,6 +320,56 @@ def test_epochs_linear(d, chunk, epochs, io):
     _check("linear", w, make_inputs(w), epochs=epochs)
 
 
+# ------------------------------------------------------------------ non-causal TTT-Linear
+# The linear layer trained first on all pairs, then read by every query (ViT3 news page,
+# section 1; wmrh.cn summary, section 2.1.1), at the vision shape on the matrix cores
+# (d = 64, bf16): one full-batch step, or mini-batches and epochs.
+
+def _linear_nc(**kw):
+    base = dict(kind="linear", h=0, chunk=196, causal=False, name="linear_nc_N196")
+    base.update(kw)
+    return workload(4).replace(**base)
+
+
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 100, 196, 333])
+def test_linear_nc_full_batch(T):
+    w = _linear_nc(B=2, H=3, T=T, chunk=T, seed=300 + T)
+    _check("linear", w, make_inputs(w))
+
+
+@pytest.mark.parametrize("chunk,epochs", [(98, 1), (66, 2), (49, 3), (16, 1), (5, 2), (300, 2)])
+def test_linear_nc_minibatches_and_epochs(chunk, epochs):
+    w = _linear_nc(B=2, H=3, chunk=chunk, unit_keys=True, eta=0.1, seed=310 + chunk)
+    _check("linear", w, make_inputs(w), epochs=epochs)
+
+
+@pytest.mark.parametrize("loss,rates,chunk,epochs", [("mse", True, 196, 1), ("dot", False, 196, 1),
+                                                     ("dot", True, 49, 2), ("mse", True, 66, 2)])
+def test_linear_nc_loss_and_rates(loss, rates, chunk, epochs):
+    w = _linear_nc(B=2, H=3, chunk=chunk, unit_keys=True, eta=0.1, seed=320 + chunk)
+    _check("linear", w, _with_rates(w, 13) if rates else make_inputs(w), loss=loss, epochs=epochs)
+
+
+def test_linear_nc_per_batch_state_and_chain_count():
+    w = _linear_nc(B=13, H=1, T=150, chunk=150, seed=330)
+    inp = make_inputs(w)
+    rng = np.random.default_rng(1)
+    inp["w0"] = (0.05 * rng.standard_normal((13, 1, 64, 64))).astype(np.float32)
+    _check("linear", w, inp)
+
+
+def test_linear_nc_vision_shape_full_size():
+    w = _linear_nc()
+    _check("linear", w, make_inputs(w), full=True)
+
+
+def test_linear_nc_vision_shape_dot_loss_full_size():
+    # with the dot-product loss one full-batch step from W0 is W0 + eta V^T K: non-causal
+    # linear attention (the blog page, section TTT / 如何理解)
+    w = _linear_nc()
+    _check("linear", w, make_inputs(w), loss="dot", full=True)
+
+
 # ------------------------------------------------------------------ the paper's inner models
 # f(x) = x + LN(f_res(x)), f_res = W x or W2 GELU(W1 x) (wmrh.cn summary, section 2.2.1):
 # ttt_linear_ln_fwd / ttt_mlp_ln_fwd against the oracle's ln / act="gelu"
