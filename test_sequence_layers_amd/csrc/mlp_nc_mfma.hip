@@ -107,6 +107,7 @@ struct KvTile {
   u32x2 vv[4];        // V[t = n][16 it + 4 g .. + 3]
   float et;           // rate factor of token n (1 without per-token rates)
 };
+template <bool kTok>
 __device__ __forceinline__ void load_kv(KvTile& r, const char* k, const char* v, const float* etok, int tt,
                                         int seq_bytes, int row, const int (&kto)[4], int g, int n) {
   const int off = tt * kTileBytes;
@@ -123,7 +124,7 @@ __device__ __forceinline__ void load_kv(KvTile& r, const char* k, const char* v,
   for (int it = 0; it < 4; ++it)
     r.vv[it] = __builtin_amdgcn_raw_buffer_load_b64(rv, n * 128 + 2 * (16 * it + 4 * g), 0, 0);
   r.et = 1.0f;
-  if (etok) {  // uniform: 4 bytes per token, zero past T
+  if (kTok) {  // 4 bytes per token, zero past the end
     const __amdgpu_buffer_rsrc_t re = tile_rsrc(etok + tt * kTile, (seq_bytes >> 5) - tt * kTile * 4);
     r.et = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(re, n * 4, 0, 0));
   }
@@ -132,7 +133,12 @@ __device__ __forceinline__ void load_kv(KvTile& r, const char* k, const char* v,
 // fp32 weight rows staged in LDS, padded to 68 floats so that the 16-byte reads of 16
 // lanes in 16 consecutive rows spread over the banks
 constexpr int kWRow = kD + 4;
-template <bool kDot>
+// The tiles stream through register rings that are unrolled, with every load issued
+// unconditionally (past the end of a step a tile reads zero and adds nothing) and scheduling
+// barriers between the ring slots: a register copy of a tile still in flight, a load issued
+// on one path only, or a product hoisted above another slot's loads would each make the
+// wave wait for more loads than the tile it needs.
+template <bool kDot, bool kTok>
 __global__ __launch_bounds__(64 * kNcWaves) __attribute__((amdgpu_waves_per_eu(1, 1))) void mlp_nc_kernel(MlpArgs a) {
   // partial gradient tiles [wave][tile f][lane], then the trained tiles in [0][f][lane]
   __shared__ float4_t red[kNcWaves][16][64];
@@ -156,7 +162,7 @@ __global__ __launch_bounds__(64 * kNcWaves) __attribute__((amdgpu_waves_per_eu(1
   const char* k = reinterpret_cast<const char*>(static_cast<const bf16*>(a.k) + tok0);
   const char* v = reinterpret_cast<const char*>(static_cast<const bf16*>(a.v) + tok0);
   char* z = reinterpret_cast<char*>(static_cast<bf16*>(a.z) + tok0);
-  const float* etok = a.eta_tok ? a.eta_tok + static_cast<size_t>(chain) * T : nullptr;
+  const float* etok = kTok ? a.eta_tok + static_cast<size_t>(chain) * T : nullptr;
   const size_t hd = static_cast<size_t>(kH) * kD;
   const float* w1g = a.w1 + bi * a.w_batch_stride + static_cast<long long>(hi) * hd;
   const float* w2g = a.w2 + bi * a.w_batch_stride + static_cast<long long>(hi) * hd;
@@ -183,29 +189,44 @@ __global__ __launch_bounds__(64 * kNcWaves) __attribute__((amdgpu_waves_per_eu(1
   int ns = mb;                               // its tokens
   int ntl = (ns + kTile - 1) / kTile;        // its tiles
 
-  // K/V tiles are prefetched two tiles ahead (the wave's tiles i and i + 1 are in flight
-  // while it computes tile i - 1)
-  KvTile cur, nx1, nx2;
-  auto prefetch = [&](int start, int len, int tiles) {  // this wave's first two tiles of a step
+  // ring of four K/V tiles: slot x holds this wave's tile tt + x kNcWaves of the step
+  constexpr int kRing = 4;
+  KvTile ring[kRing];
+  auto prefetch = [&](int start, int len) {  // this wave's first tiles of a step
     const char* ks = k + start * kRowBytes;
     const char* vs = v + start * kRowBytes;
-    const float* es = etok ? etok + start : nullptr;
-    if (wv < tiles) load_kv(cur, ks, vs, es, wv, len * kRowBytes, row, kto, g, n);
-    if (wv + kNcWaves < tiles) load_kv(nx1, ks, vs, es, wv + kNcWaves, len * kRowBytes, row, kto, g, n);
+    const float* es = kTok ? etok + start : nullptr;
+#pragma unroll
+    for (int x = 0; x < kRing; ++x) {
+      load_kv<kTok>(ring[x], ks, vs, es, wv + x * kNcWaves, len * kRowBytes, row, kto, g, n);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
-  prefetch(m0, ns, ntl);
   {
     // W1 and W2 (64 x 64 fp32 each) into LDS: thread x copies 16-byte pieces x, x + 128, ...
+    // The global loads are issued before the first K/V tiles, so that the wait for them
+    // leaves the tiles in flight.
+    constexpr int kPer = kH * kD / 4 / (64 * kNcWaves);
     const int tid = threadIdx.x;
+    float4_t wv4[2][kPer];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const float* src = m ? w2g : w1g;
 #pragma unroll
-      for (int x = tid; x < kH * kD / 4; x += 64 * kNcWaves) {
-        const int r = x >> 4, c = (x & 15) * 4;
-        *reinterpret_cast<float4_t*>(&wsh[m][r][c]) = *reinterpret_cast<const float4_t*>(src + r * kD + c);
+      for (int i = 0; i < kPer; ++i) {
+        const int x = tid + i * 64 * kNcWaves;
+        wv4[m][i] = *reinterpret_cast<const float4_t*>(src + (x >> 4) * kD + (x & 15) * 4);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    prefetch(m0, ns);
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int x = tid + i * 64 * kNcWaves;
+        *reinterpret_cast<float4_t*>(&wsh[m][x >> 4][(x & 15) * 4]) = wv4[m][i];
+      }
   }
   __syncthreads();
   float* w1l = &wsh[0][0][0];
@@ -217,7 +238,14 @@ __global__ __launch_bounds__(64 * kNcWaves) __attribute__((amdgpu_waves_per_eu(1
   // this wave's half of the W tiles, for W' = W - eta G after pass 1 (tile f = 4 x + y of
   // the [x][y] tile arrays, f in 8 w .. 8 w + 7)
   float4_t w1own[2][4], w2own[2][4];
-  u32x4 qn0 = {0u, 0u, 0u, 0u}, qn1 = {0u, 0u, 0u, 0u};
+  // ring of four query tiles for pass 2 (loaded while the last step's sums are reduced)
+  u32x4 qa[kRing][2];
+  auto load_q = [&](u32x4 (&dst)[2], int tt) {
+    const int off = tt * kTileBytes;
+    const __amdgpu_buffer_rsrc_t rq = tile_rsrc(q + off, seq_bytes - off);
+    dst[0] = __builtin_amdgcn_raw_buffer_load_b128(rq, row, 0, 0);
+    dst[1] = __builtin_amdgcn_raw_buffer_load_b128(rq, row + 16, 0, 0);
+  };
   for (int step = 0;; ++step) {
     // ---- bf16 operands of the current weights (the LDS copy) ----
     {
@@ -260,9 +288,12 @@ __global__ __launch_bounds__(64 * kNcWaves) __attribute__((amdgpu_waves_per_eu(1
       }
     const char* ks = k + m0 * kRowBytes;
     const char* vs = v + m0 * kRowBytes;
-    const float* es = etok ? etok + m0 : nullptr;
-    for (int tt = wv; tt < ntl; tt += kNcWaves) {
-      if (tt + 2 * kNcWaves < ntl) load_kv(nx2, ks, vs, es, tt + 2 * kNcWaves, ns * kRowBytes, row, kto, g, n);
+    const float* es = kTok ? etok + m0 : nullptr;
+    for (int tt0 = wv; tt0 < ntl; tt0 += kRing * kNcWaves) {
+#pragma unroll
+    for (int x = 0; x < kRing; ++x) {
+    if (tt0 + x * kNcWaves < ntl) {
+      const KvTile& cur = ring[x];
       const bf16x8_t ka0 = bf(cur.ka0), ka1 = bf(cur.ka1);
       // U = K W1^T (rows t); A = SiLU(U), S = SiLU'(U)
       float4_t act[4], sd[4];
@@ -327,25 +358,26 @@ __global__ __launch_bounds__(64 * kNcWaves) __attribute__((amdgpu_waves_per_eu(1
 #pragma unroll
         for (int it = 0; it < 4; ++it) g2t[aa][it] = mfma(ab, rb[it], g2t[aa][it]);
       }
-      cur = nx1;
-      nx1 = nx2;
+    }
+    load_kv<kTok>(ring[x], ks, vs, es, tt0 + (x + kRing) * kNcWaves, ns * kRowBytes, row, kto, g, n);
+    __builtin_amdgcn_sched_barrier(0);
+    }
     }
 
     const bool last = step + 1 == nsteps;
     if (last) {
-      // queries of this wave's first tile, loaded while the sums are reduced
-      if (wv < ntiles) {
-        const int off = wv * kTileBytes;
-        const __amdgpu_buffer_rsrc_t rq = tile_rsrc(q + off, seq_bytes - off);
-        qn0 = __builtin_amdgcn_raw_buffer_load_b128(rq, row, 0, 0);
-        qn1 = __builtin_amdgcn_raw_buffer_load_b128(rq, row + 16, 0, 0);
+      // the queries of this wave's first tiles, loaded while the sums are reduced
+#pragma unroll
+      for (int x = 0; x < kRing; ++x) {
+        load_q(qa[x], wv + x * kNcWaves);
+        __builtin_amdgcn_sched_barrier(0);
       }
     } else {
       // the next step's first tiles, loaded while the sums are reduced
       m0 = ((step + 1) % nmb) * mb;
       ns = min(mb, T - m0);
       ntl = (ns + kTile - 1) / kTile;
-      prefetch(m0, ns, ntl);
+      prefetch(m0, ns);
     }
 
     // ---- W -= eta G: the partial sums meet in LDS; wave w reduces tiles 8 w .. 8 w + 7 ----
@@ -451,32 +483,34 @@ __global__ __launch_bounds__(64 * kNcWaves) __attribute__((amdgpu_waves_per_eu(1
   }
 
   // ---- pass 2: Z^T = W2' SiLU(W1' Q^T) over this wave's tiles ----
-  for (int tt = wv; tt < ntiles; tt += kNcWaves) {
-    const bf16x8_t qb0 = bf(qn0), qb1 = bf(qn1);
-    if (tt + kNcWaves < ntiles) {
-      const int offn = (tt + kNcWaves) * kTileBytes;
-      const __amdgpu_buffer_rsrc_t rqn = tile_rsrc(q + offn, seq_bytes - offn);
-      qn0 = __builtin_amdgcn_raw_buffer_load_b128(rqn, row, 0, 0);
-      qn1 = __builtin_amdgcn_raw_buffer_load_b128(rqn, row + 16, 0, 0);
-    }
-    float4_t aq[4];
+  for (int tt0 = wv; tt0 < ntiles; tt0 += kRing * kNcWaves) {
 #pragma unroll
-    for (int aa = 0; aa < 4; ++aa) {
-      float4_t u = mfma(w1nb[0][aa], qb0, zero);
-      u = mfma(w1nb[1][aa], qb1, u);
+    for (int x = 0; x < kRing; ++x) {
+      const int tt = tt0 + x * kNcWaves;
+      if (tt < ntiles) {
+        const bf16x8_t qb0 = bf(qa[x][0]), qb1 = bf(qa[x][1]);
+        float4_t aq[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) u[e] = u[e] * sigmoid_f(u[e]);
-      aq[aa] = u;
-    }
-    const bf16x8_t aqb0 = pair_op(aq[0], aq[1]), aqb1 = pair_op(aq[2], aq[3]);
-    const int off = tt * kTileBytes;
-    const __amdgpu_buffer_rsrc_t rz = tile_rsrc(z + off, seq_bytes - off);
+        for (int aa = 0; aa < 4; ++aa) {
+          float4_t u = mfma(w1nb[0][aa], qb0, zero);
+          u = mfma(w1nb[1][aa], qb1, u);
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      float4_t zt = mfma(w2nb[0][it], aqb0, zero);
-      zt = mfma(w2nb[1][it], aqb1, zt);
-      const u32x2 out = {pack_bf16(zt[0], zt[1]), pack_bf16(zt[2], zt[3])};
-      __builtin_amdgcn_raw_buffer_store_b64(out, rz, n * 128 + 2 * (16 * it + 4 * g), 0, 0);
+          for (int e = 0; e < 4; ++e) u[e] = u[e] * sigmoid_f(u[e]);
+          aq[aa] = u;
+        }
+        const bf16x8_t aqb0 = pair_op(aq[0], aq[1]), aqb1 = pair_op(aq[2], aq[3]);
+        const int off = tt * kTileBytes;
+        const __amdgpu_buffer_rsrc_t rz = tile_rsrc(z + off, seq_bytes - off);
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          float4_t zt = mfma(w2nb[0][it], aqb0, zero);
+          zt = mfma(w2nb[1][it], aqb1, zt);
+          const u32x2 out = {pack_bf16(zt[0], zt[1]), pack_bf16(zt[2], zt[3])};
+          __builtin_amdgcn_raw_buffer_store_b64(out, rz, n * 128 + 2 * (16 * it + 4 * g), 0, 0);
+        }
+      }
+      load_q(qa[x], tt + kRing * kNcWaves);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -497,10 +531,18 @@ bool mlp_nc_supported(const MlpArgs& a, bool bf16_io) {
 hipError_t launch_mlp_nc(const MlpArgs& a, hipStream_t s) {
   const long long nchains = static_cast<long long>(a.B) * a.H;
   if (nchains > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (a.dot_loss)
-    hipLaunchKernelGGL(mlp_nc_kernel<true>, dim3(static_cast<unsigned>(nchains)), dim3(64 * kNcWaves), 0, s, a);
-  else
-    hipLaunchKernelGGL(mlp_nc_kernel<false>, dim3(static_cast<unsigned>(nchains)), dim3(64 * kNcWaves), 0, s, a);
+  const dim3 grid(static_cast<unsigned>(nchains)), block(64 * kNcWaves);
+  if (a.dot_loss) {
+    if (a.eta_tok)
+      hipLaunchKernelGGL((mlp_nc_kernel<true, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((mlp_nc_kernel<true, false>), grid, block, 0, s, a);
+  } else {
+    if (a.eta_tok)
+      hipLaunchKernelGGL((mlp_nc_kernel<false, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((mlp_nc_kernel<false, false>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 
