@@ -74,6 +74,7 @@ __all__ = [
     "delta_rule",
     "ttt_linear_vjp",
     "ttt_mlp_vjp",
+    "ttt_layer_vjp",
 ]
 
 LOSSES = ("mse", "dot")
@@ -541,3 +542,122 @@ def ttt_mlp_vjp(q, k, v, w1, w2, eta, chunk, dz, dw1_out=None, dw2_out=None, los
     tok = lambda t: (np.zeros((N, T, d)) if t is None else t.numpy()).reshape(shape)
     st = lambda t, like, sh: (np.zeros(like.shape) if t is None else t.numpy()).reshape(tuple(lead) + sh)
     return (tok(res[0]), tok(res[1]), tok(res[2]), st(res[3], W1i, (h, d)), st(res[4], W2i, (d, h)))
+
+
+def ttt_layer_vjp(kind, q, k, v, state, eta, chunk, dz, dstate=None, *, causal=True, epochs=1,
+                  eta_tok=None, loss="mse", act="silu", ln=None):
+    """Vector-Jacobian product of every TTT layer variant of ttt_linear / ttt_mlp: causal or
+    not, mini-batches and epochs, per-token rate factors, either loss, SiLU or GELU, with or
+    without the paper's layer norm and residual.
+
+    The outer loop trains the projections that make q, k, v, the initial state, the rates
+    and the layer-norm parameters through the inner updates (wmrh.cn summary, section 2.2,
+    the outer loop and its "gradient of the gradient"; section 2.2.3, the learnable rate;
+    "Fast weights" page, opening paragraph and section 2: the outer gradient runs through
+    the whole update trajectory; ViT3 news page, section 1: K and V are learned end to end).
+
+    kind: "linear" (state = (w0,)) or "mlp" (state = (w1, w2)); every other argument as in
+    ttt_linear / ttt_mlp, ln = (gamma, beta, eps).  dz [..., T, d]: upstream gradient of z;
+    dstate: upstream gradients of the final states (a tuple like state) or None.
+    Returns (dq, dk, dv, dstate..., deta_tok, dgamma, dbeta), per chain; deta_tok is None
+    without rates, dgamma and dbeta are None without ln.
+
+    The definition, written out: the recurrence of ttt_linear / ttt_mlp in float64 torch
+    tensors, where each token's inner gradient is itself taken by torch.autograd (with
+    create_graph, at the chunk-start weights) rather than written out, and the whole
+    trajectory is differentiated by torch.autograd in reverse mode.
+    """
+    import torch
+    if kind not in ("linear", "mlp"):
+        raise ValueError(kind)
+    if loss not in LOSSES:
+        raise ValueError(loss)
+    q2, lead = _flatten_tokens(q, np.float64)
+    k2, _ = _flatten_tokens(k, np.float64)
+    v2, _ = _flatten_tokens(v, np.float64)
+    N, T, d = q2.shape
+    b = _check_chunk(T, chunk)
+    epochs = _check_epochs(epochs, causal)
+    Q = torch.tensor(q2, requires_grad=True)
+    K = torch.tensor(k2, requires_grad=True)
+    V = torch.tensor(v2, requires_grad=True)
+    W0 = [torch.tensor(_broadcast_state(s, lead, np.float64), requires_grad=True) for s in state]
+    E = None
+    if eta_tok is not None:
+        E = torch.tensor(np.broadcast_to(np.asarray(eta_tok, np.float64), tuple(lead) + (T,))
+                         .reshape(N, T).copy(), requires_grad=True)
+    G_, B_, eps = None, None, None
+    if ln is not None:
+        G_ = torch.tensor(np.broadcast_to(np.asarray(ln[0], np.float64), tuple(lead) + (d,))
+                          .reshape(N, d).copy(), requires_grad=True)
+        B_ = torch.tensor(np.broadcast_to(np.asarray(ln[1], np.float64), tuple(lead) + (d,))
+                          .reshape(N, d).copy(), requires_grad=True)
+        eps = float(ln[2])
+
+    def activation(u):
+        if act == "silu":
+            return u * torch.sigmoid(u)
+        if act == "gelu":
+            return 0.5 * u * (1.0 + torch.erf(u / np.sqrt(2.0)))
+        raise ValueError(act)
+
+    def f(x, W):
+        if kind == "linear":
+            y = torch.einsum("nij,nj->ni", W[0], x)
+        else:
+            y = torch.einsum("nih,nh->ni", W[1], activation(torch.einsum("nhj,nj->nh", W[0], x)))
+        if G_ is None:
+            return y
+        mu = y.mean(dim=-1, keepdim=True)
+        var = ((y - mu) ** 2).mean(dim=-1, keepdim=True)
+        return x + G_ * (y - mu) / torch.sqrt(var + eps) + B_
+
+    def inner_loss(fx, vt):
+        if loss == "mse":
+            return 0.5 * ((fx - vt) ** 2).sum()
+        return -(vt * fx).sum()
+
+    W = W0
+    zs = [None] * T
+    for c0 in [c for _ in range(epochs) for c in range(0, T, b)]:
+        Wc = W
+        G = [torch.zeros_like(w) for w in Wc]
+        Wt = Wc
+        for t in range(c0, min(c0 + b, T)):
+            g = torch.autograd.grad(inner_loss(f(K[:, t], Wc), V[:, t]), Wc, create_graph=True,
+                                    allow_unused=True)
+            g = [torch.zeros_like(w) if gi is None else gi for gi, w in zip(g, Wc)]
+            G = [Gi + (gi if E is None else E[:, t].reshape((N,) + (1,) * (gi.dim() - 1)) * gi)
+                 for Gi, gi in zip(G, g)]
+            Wt = [w - eta * Gi for w, Gi in zip(Wc, G)]
+            if causal:
+                zs[t] = f(Q[:, t], Wt)
+        W = Wt
+    if not causal:
+        for t in range(T):
+            zs[t] = f(Q[:, t], W)
+    Z = torch.stack(zs, dim=1) if T else torch.zeros((N, 0, d), dtype=torch.float64)
+    outs, grads = [Z], [torch.tensor(_flatten_tokens(dz, np.float64)[0])]
+    if dstate is not None:
+        for w, ds in zip(W, dstate):
+            if ds is not None:
+                outs.append(w)
+                grads.append(torch.tensor(_broadcast_state(ds, lead, np.float64)))
+    wrt = [Q, K, V] + W0 + [x for x in (E, G_, B_) if x is not None]
+    got = list(torch.autograd.grad(outs, wrt, grads, allow_unused=True))
+    zero_like = lambda t, ref: np.zeros(ref.shape) if t is None else t.numpy()
+    res = [zero_like(got[i], x).reshape(tuple(lead) + (T, d)) for i, x in enumerate((Q, K, V))]
+    for j, w in enumerate(W0):
+        res.append(zero_like(got[3 + j], w).reshape(tuple(lead) + tuple(w.shape[1:])))
+    i = 3 + len(W0)
+    if E is not None:
+        res.append(zero_like(got[i], E).reshape(tuple(lead) + (T,)))
+        i += 1
+    else:
+        res.append(None)
+    if G_ is not None:
+        res.append(zero_like(got[i], G_).reshape(tuple(lead) + (d,)))
+        res.append(zero_like(got[i + 1], B_).reshape(tuple(lead) + (d,)))
+    else:
+        res += [None, None]
+    return tuple(res)

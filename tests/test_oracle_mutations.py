@@ -97,6 +97,22 @@ MUTATIONS = {
         "return 0.5 * (1.0 + erf(u / np.sqrt(2.0))) + u * np.exp(-0.5 * u * u) / np.sqrt(2.0 * np.pi)",
         "return 0.5 * (1.0 + erf(u / np.sqrt(2.0)))"),
     "gelu_is_silu": ('"gelu": (gelu, dgelu)', '"gelu": (silu, dsilu)'),
+    "layer_vjp_inner_gradient_at_current_weights": (
+        "g = torch.autograd.grad(inner_loss(f(K[:, t], Wc), V[:, t]), Wc,",
+        "g = torch.autograd.grad(inner_loss(f(K[:, t], Wt), V[:, t]), Wt,"),
+    "layer_vjp_rate_dropped": (
+        "G = [Gi + (gi if E is None else", "G = [Gi + (gi if True else"),
+    "layer_vjp_noncausal_reads_initial_weights": (
+        "            zs[t] = f(Q[:, t], W)\n", "            zs[t] = f(Q[:, t], W0)\n"),
+    "layer_vjp_ln_residual_dropped": (
+        "return x + G_ * (y - mu) / torch.sqrt(var + eps) + B_",
+        "return G_ * (y - mu) / torch.sqrt(var + eps) + B_"),
+    "layer_vjp_epochs_ignored": (
+        "for c0 in [c for _ in range(epochs) for c in range(0, T, b)]:",
+        "for c0 in [c for _ in range(1) for c in range(0, T, b)]:"),
+    "layer_vjp_gelu_is_silu": (
+        "            return 0.5 * u * (1.0 + torch.erf(u / np.sqrt(2.0)))",
+        "            return u * torch.sigmoid(u)"),
     "noncausal_reads_initial_weights": (
         "    if not causal:\n        for t in range(T):\n            z[:, t] = linear_f(W, q2[:, t], lnp)",
         "    if not causal:\n        W = _broadcast_state(w0, lead, dtype)\n"

@@ -952,3 +952,127 @@ def test_ragged_last_chunk():
     zb, wb = O.ttt_linear(q[:, 8:], k[:, 8:], v[:, 8:], wa, 0.1, 2)
     np.testing.assert_allclose(z, np.concatenate([za, zb], 1), atol=1e-13)
     np.testing.assert_allclose(w, wb, atol=1e-13)
+
+
+# ---------------------------------------------------------------- gradients of every variant
+# ttt_layer_vjp (each token's inner gradient by autograd, the trajectory by autograd) against
+# central finite differences of the numpy forward, for the variants the written-out VJPs do
+# not cover: the non-causal layer with mini-batches and epochs, the MLP with per-token rates,
+# the paper's layer norm + residual models (GELU MLP), and the gradients of the rates and of
+# the layer-norm gain and bias.  On the options both cover it must equal the written-out VJPs.
+
+_LAYER_CASES = [
+    # kind, causal, chunk, epochs, rates, loss, act, ln
+    ("linear", False, 3, 2, False, "mse", "silu", False),
+    ("linear", False, 10, 1, True, "dot", "silu", False),
+    ("linear", True, 4, 1, False, "mse", "silu", True),
+    ("linear", False, 4, 2, True, "mse", "silu", True),
+    ("mlp", True, 3, 1, True, "mse", "silu", False),
+    ("mlp", False, 4, 2, True, "mse", "silu", False),
+    ("mlp", False, 10, 1, False, "mse", "silu", False),
+    ("mlp", True, 3, 1, False, "mse", "gelu", True),
+    ("mlp", False, 5, 2, True, "dot", "gelu", True),
+]
+
+
+def _layer_forward(kind, a, eta, chunk, causal, epochs, loss, act, ln_eps):
+    ln = (a["gamma"], a["beta"], ln_eps) if "gamma" in a else None
+    et = a.get("et")
+    if kind == "linear":
+        return O.ttt_linear(a["q"], a["k"], a["v"], a["w0"], eta, chunk, causal, loss=loss,
+                            eta_tok=et, epochs=epochs, ln=ln)
+    return O.ttt_mlp(a["q"], a["k"], a["v"], a["w1"], a["w2"], eta, chunk, causal, loss=loss,
+                     eta_tok=et, epochs=epochs, act=act, ln=ln)
+
+
+@pytest.mark.parametrize("kind,causal,chunk,epochs,rates,loss,act,ln", _LAYER_CASES)
+def test_layer_vjp_matches_finite_differences(kind, causal, chunk, epochs, rates, loss, act, ln):
+    rng = _rng(hash((kind, causal, chunk, epochs, rates, loss, act, ln)) % 1000)
+    N, T, d, h = 2, 10, 4, 5
+    q, k, v = _rand_chains(rng, N, T, d)
+    a = dict(q=q, k=k, v=v)
+    if kind == "linear":
+        a["w0"] = 0.3 * rng.standard_normal((N, d, d))
+        names = ("w0",)
+    else:
+        a["w1"] = 0.3 * rng.standard_normal((N, h, d))
+        a["w2"] = 0.3 * rng.standard_normal((N, d, h))
+        names = ("w1", "w2")
+    if rates:
+        a["et"] = rng.uniform(0.2, 1.5, (N, T))
+    eps = 0.05  # large enough that the layer norm's own curvature matters
+    if ln:
+        a["gamma"] = 1.0 + 0.3 * rng.standard_normal((N, d))
+        a["beta"] = 0.3 * rng.standard_normal((N, d))
+    eta = 0.15
+    dz = rng.standard_normal((N, T, d))
+    dst = tuple(rng.standard_normal(a[n].shape) for n in names)
+    out = O.ttt_layer_vjp(kind, q, k, v, tuple(a[n] for n in names), eta, chunk, dz, dst,
+                          causal=causal, epochs=epochs, eta_tok=a.get("et"), loss=loss, act=act,
+                          ln=(a["gamma"], a["beta"], eps) if ln else None)
+    grads = dict(zip(("q", "k", "v") + names + ("et", "gamma", "beta"), out))
+
+    def L(x):
+        z, *ws = _layer_forward(kind, x, eta, chunk, causal, epochs, loss, act, eps)
+        return float(np.sum(z * dz) + sum(np.sum(w * g) for w, g in zip(ws, dst)))
+    for which in [w for w in ("q", "k", "v") + names + ("et", "gamma", "beta") if w in a]:
+        assert grads[which] is not None, which
+        direction = rng.standard_normal(a[which].shape)
+        hh = 1e-6
+        ap, am = dict(a), dict(a)
+        ap[which] = a[which] + hh * direction
+        am[which] = a[which] - hh * direction
+        fd = (L(ap) - L(am)) / (2 * hh)
+        an = float(np.sum(grads[which] * direction))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (which, fd, an)
+    if not rates:
+        assert grads["et"] is None
+    if not ln:
+        assert grads["gamma"] is None and grads["beta"] is None
+
+
+def test_layer_vjp_equals_the_written_out_vjps():
+    rng = _rng(91)
+    N, T, d, h = 2, 9, 4, 5
+    q, k, v = _rand_chains(rng, N, T, d)
+    w0 = 0.3 * rng.standard_normal((N, d, d))
+    w1 = 0.3 * rng.standard_normal((N, h, d))
+    w2 = 0.3 * rng.standard_normal((N, d, h))
+    dz = rng.standard_normal((N, T, d))
+    dw0 = rng.standard_normal((N, d, d))
+    dw1 = rng.standard_normal((N, h, d))
+    dw2 = rng.standard_normal((N, d, h))
+    et = rng.uniform(0.2, 1.5, (N, T))
+    a = O.ttt_linear_vjp(q, k, v, w0, 0.2, 4, dz, dw0, eta_tok=et)
+    b = O.ttt_layer_vjp("linear", q, k, v, (w0,), 0.2, 4, dz, (dw0,), eta_tok=et)
+    for x, y in zip(a, b[:5]):
+        np.testing.assert_allclose(x, y, rtol=0, atol=1e-12)
+    for loss in ("mse", "dot"):
+        a = O.ttt_mlp_vjp(q, k, v, w1, w2, 0.2, 3, dz, dw1, dw2, loss=loss)
+        b = O.ttt_layer_vjp("mlp", q, k, v, (w1, w2), 0.2, 3, dz, (dw1, dw2), loss=loss)
+        for x, y in zip(a, b[:5]):
+            np.testing.assert_allclose(x, y, rtol=0, atol=1e-12)
+
+
+def test_noncausal_full_batch_linear_vjp_closed_form():
+    """One full-batch step (chunk = T, causal = 0): W' = W0 - eta (W0 K^T - V^T) K and
+    Z = Q W'^T, so dQ = dZ W', dW' = dZ^T Q, dV = eta K dW'^T, and
+    dW0 = dW' (I - eta K^T K) and, per key, dk_t = -eta (W0^T dW' k_t + dW'^T r_t) with
+    r_t = W0 k_t - v_t."""
+    rng = _rng(92)
+    N, T, d = 2, 7, 3
+    q, k, v = _rand_chains(rng, N, T, d)
+    w0 = 0.3 * rng.standard_normal((N, d, d))
+    dz = rng.standard_normal((N, T, d))
+    eta = 0.1
+    dq, dk, dv, dw0, *_ = O.ttt_layer_vjp("linear", q, k, v, (w0,), eta, T, dz, None, causal=False)
+    R = np.einsum("ntj,nij->nti", k, w0) - v
+    W1 = w0 - eta * np.einsum("nti,ntj->nij", R, k)
+    D = np.einsum("nti,ntj->nij", dz, q)       # dW'
+    np.testing.assert_allclose(dq, np.einsum("nti,nij->ntj", dz, W1), atol=1e-12)
+    np.testing.assert_allclose(dv, eta * np.einsum("ntj,nij->nti", k, D), atol=1e-12)
+    I = np.eye(d)[None]
+    np.testing.assert_allclose(dw0, np.einsum("nij,njk->nik", D, I - eta * np.einsum("ntj,ntk->njk", k, k)),
+                               atol=1e-12)
+    dk_ref = -eta * (np.einsum("nij,nim,ntm->ntj", w0, D, k) + np.einsum("nti,nij->ntj", R, D))
+    np.testing.assert_allclose(dk, dk_ref, atol=1e-12)
