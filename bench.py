@@ -161,13 +161,21 @@ def time_workload(w, steps, warmup, torch, ttt, rotate=None, rates=False, loss="
 
 
 def time_backward(w, steps, warmup, torch, ttt, rates=False):
-    """Event-timed ttt_linear_bwd / ttt_mlp_bwd calls on the workload (inputs resident in
+    """Event-timed ttt_linear_bwd / ttt_mlp_bwd calls (ttt_linear_nc_bwd / ttt_mlp_nc_bwd for
+    the non-causal workloads) on the workload (inputs resident in
     HBM; seeded dZ ~ N(0, 1), no upstream state gradient; rates: TTT-Linear with per-token
     rate factors, their gradient included)."""
     dev = make_device_inputs(w, w.seed, torch, rates=rates)
     g = torch.Generator(device="cuda").manual_seed(w.seed)
     dz = torch.randn(dev["q"].shape, generator=g, device="cuda").to(dev["q"].dtype)
-    if w.kind == "linear":
+    if not w.causal:  # the non-causal layers
+        if w.kind == "linear":
+            call = lambda: ttt.ttt_linear_nc_bwd(dev["q"], dev["k"], dev["v"], dev["w0"], w.eta, w.chunk,
+                                                 dz, eta_tok=dev.get("eta_tok"))
+        else:
+            call = lambda: ttt.ttt_mlp_nc_bwd(dev["q"], dev["k"], dev["v"], dev["w1"], dev["w2"], w.eta,
+                                              w.chunk, dz, eta_tok=dev.get("eta_tok"))
+    elif w.kind == "linear":
         call = lambda: ttt.ttt_linear_bwd(dev["q"], dev["k"], dev["v"], dev["w0"], w.eta, w.chunk, dz,
                                           eta_tok=dev.get("eta_tok"))
     else:
@@ -421,7 +429,7 @@ def main():
         # backward passes of the headline linear workload and of the causal MLP workload
         # (dz ~ N(0, 1), no upstream state gradient)
         bwd = [w] if w.kind == "linear" else []
-        bwd += [o for o in WORKLOADS if o.name == "mlp_h256_T2048"]
+        bwd += [o for o in WORKLOADS if o.name in ("mlp_h256_T2048", "mlp_vision_N196")]
         for o in bwd:
             r = time_backward(o, max(10, args.steps // 2) if o.kind == "linear" else 3,
                               3 if o.kind == "linear" else 1, torch, ttt)

@@ -216,6 +216,43 @@ int ttt_mlp_bwd(const void* q, const void* k, const void* v,
                 int B, int H, int T, int d, int dh, int chunk, float eta,
                 int loss, int io_dtype, ttt_stream_t stream);
 
+/*
+ * Backward pass of the non-causal TTT layers: the layer trains on every pair first (steps of
+ * mini-batch GD over the chunks, `epochs` passes) and then every query reads the final
+ * weights (ViT3 news page, section 1, observation 2); the outer loop trains the projections,
+ * the initial state and the rates through those steps (wmrh.cn summary of Sun et al. 2024,
+ * sections 2.2 and 2.2.3; "Fast weights" page, section 2).  For the forward call
+ * ttt_linear_fwd(q, k, v, w0, ..., chunk, causal = 0, eta, eta_tok, loss, epochs), resp.
+ * ttt_mlp_fwd(q, k, v, w1, w2, ..., chunk, causal = 0, eta, eta_tok, loss, epochs), and the
+ * upstream gradients dz of z and dw_out (dw1_out, dw2_out) of the final states, writes
+ *   dq, dk, dv  [B][H][T][d] io_dtype (out)
+ *   dw0 [B][H][d][d] (linear) or dw1 [B][H][dh][d], dw2 [B][H][d][dh] (MLP), float32 (out),
+ *               per (b, h) sequence (sum over b for a state shared over the batch)
+ *   deta_tok    [B][H][T] float32 (out) or NULL: the gradient of the per-token rate factors
+ *               eta_tok (needs eta_tok)
+ *   dz [B][H][T][d] io_dtype;  dw_out / dw1_out, dw2_out float32 or NULL (zero).
+ * Supported: d in {16, 32, 64}, 1 <= dh <= 256 (MLP, SiLU), any chunk >= 1 and epochs >= 1,
+ * TTT_LOSS_MSE or TTT_LOSS_DOT, both dtypes, on the vector ALUs (one workgroup per sequence).
+ * The call keeps every step-start state and fp32 accumulators of dk, dv and deta_tok in a
+ * stream-ordered workspace of B*H*((S+1)*state + 2*T*d + T)*4 bytes, S = ceil(T/chunk)*epochs
+ * steps and state = d*d (linear) or 2*d*dh (MLP) floats.  T = 0 copies the upstream state
+ * gradients (zeros without them).
+ */
+int ttt_linear_nc_bwd(const void* q, const void* k, const void* v,
+                      const float* w0, long long w0_batch_stride,
+                      const void* dz, const float* dw_out,
+                      void* dq, void* dk, void* dv, float* dw0,
+                      int B, int H, int T, int d, int chunk, int epochs, float eta,
+                      const float* eta_tok, float* deta_tok, int loss,
+                      int io_dtype, ttt_stream_t stream);
+int ttt_mlp_nc_bwd(const void* q, const void* k, const void* v,
+                   const float* w1, const float* w2, long long w_batch_stride,
+                   const void* dz, const float* dw1_out, const float* dw2_out,
+                   void* dq, void* dk, void* dv, float* dw1, float* dw2,
+                   int B, int H, int T, int d, int dh, int chunk, int epochs, float eta,
+                   const float* eta_tok, float* deta_tok, int loss,
+                   int io_dtype, ttt_stream_t stream);
+
 /* Message for the calling thread's last non-OK status ("" if none).  Owned by the library;
    valid until the thread's next call into it. */
 const char* ttt_last_error(void);

@@ -2,7 +2,8 @@
 
 The compute runs in libttt.so (C ABI, include/ttt.h): hand-written HIP kernels for the
 TTT-Linear, TTT-MLP and delta-rule forward passes (plain inner models, and the paper's with
-layer norm and residual) and the TTT-Linear and TTT-MLP backward passes.  This package holds the ctypes
+layer norm and residual) and the TTT-Linear and TTT-MLP backward passes (causal and
+non-causal).  This package holds the ctypes
 binding (argument marshalling only), the in-tree build script and the seeded synthetic
 workloads.
 """
@@ -23,7 +24,9 @@ from ._binding import (  # noqa: F401
     ttt_linear_bwd_noalloc,
     ttt_linear_fwd,
     ttt_linear_ln_fwd,
+    ttt_linear_nc_bwd,
     ttt_mlp_bwd,
     ttt_mlp_fwd,
     ttt_mlp_ln_fwd,
+    ttt_mlp_nc_bwd,
 )

@@ -40,6 +40,10 @@ SIGNATURES = {
                                     _i, _i, _i, _i, _i, _f, _vp, _vp, _i, _i, _vp]),
     "ttt_mlp_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                          _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
+    "ttt_linear_nc_bwd": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp, _vp, _vp, _vp,
+                               _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _i, _i, _vp]),
+    "ttt_mlp_nc_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                            _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _i, _i, _vp]),
     "ttt_last_error": (ctypes.c_char_p, []),
     "ttt_abi_version": (_i, []),
 }
@@ -312,6 +316,81 @@ def ttt_mlp_bwd(q, k, v, w1, w2, eta, chunk, dz, dw1_out=None, dw2_out=None, *, 
                              _stream(q.device, stream))
     _check(rc)
     return dq, dk, dv, dw1, dw2
+
+
+def _dz(dz, q, B, H, T, d):
+    torch = _torch()
+    if (not isinstance(dz, torch.Tensor) or tuple(dz.shape) != (B, H, T, d) or dz.dtype != q.dtype
+            or dz.device != q.device or not dz.is_contiguous()):
+        raise ValueError(f"dz must be a contiguous {q.dtype} tensor of shape {(B, H, T, d)}")
+    return dz
+
+
+def ttt_linear_nc_bwd(q, k, v, w0, eta, chunk, dz, dw_out=None, *, epochs=1, eta_tok=None,
+                      loss="mse", stream=None):
+    """Gradients of the non-causal TTT-Linear layer (ttt_linear_fwd with causal=False, the
+    same chunk, epochs, eta_tok and loss) for the upstream gradients dz [B,H,T,d] (dtype of q)
+    and dw_out [B,H,d,d] float32 (or None).  Returns (dq, dk, dv, dw0), plus deta_tok
+    [B,H,T] with eta_tok; dw0 per sequence."""
+    torch = _torch()
+    lib = load_library()
+    B, H, T, d = _tokens(q, k, v)
+    w0, stride = _state(w0, B, H, (d, d), "w0", q.device)
+    dz = _dz(dz, q, B, H, T, d)
+    if dw_out is not None:
+        dw_out = _out(dw_out, (B, H, d, d), torch.float32, q.device, "dw_out")
+    et = _rates(eta_tok, B, H, T, q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dw0 = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
+    deta = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if et is not None else None
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    with torch.cuda.device(q.device):
+        rc = lib.ttt_linear_nc_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), w0.data_ptr(), stride,
+                                   dz.data_ptr(), ptr(dw_out), dq.data_ptr(), dk.data_ptr(),
+                                   dv.data_ptr(), dw0.data_ptr(), B, H, T, d, int(chunk),
+                                   int(epochs), float(eta), et, ptr(deta), _loss(loss),
+                                   _io_dtype(q), _stream(q.device, stream))
+    _check(rc)
+    return (dq, dk, dv, dw0) if deta is None else (dq, dk, dv, dw0, deta)
+
+
+def ttt_mlp_nc_bwd(q, k, v, w1, w2, eta, chunk, dz, dw1_out=None, dw2_out=None, *, epochs=1,
+                   eta_tok=None, loss="mse", stream=None):
+    """Gradients of the non-causal TTT-MLP layer (ttt_mlp_fwd with causal=False; SiLU) for
+    the upstream gradients dz and dw1_out [B,H,dh,d], dw2_out [B,H,d,dh] (or None).  Returns
+    (dq, dk, dv, dw1, dw2), plus deta_tok [B,H,T] with eta_tok; state gradients per
+    sequence."""
+    torch = _torch()
+    lib = load_library()
+    B, H, T, d = _tokens(q, k, v)
+    if w1.dim() < 2:
+        raise ValueError("w1 must be [H, dh, d] or [B, H, dh, d]")
+    dh = int(w1.shape[-2])
+    w1, s1 = _state(w1, B, H, (dh, d), "w1", q.device)
+    w2, s2 = _state(w2, B, H, (d, dh), "w2", q.device)
+    if s1 != s2:
+        raise ValueError("w1 and w2 must both be shared over the batch or both per batch")
+    dz = _dz(dz, q, B, H, T, d)
+    if (dw1_out is None) != (dw2_out is None):
+        raise ValueError("give both dw1_out and dw2_out, or neither")
+    if dw1_out is not None:
+        dw1_out = _out(dw1_out, (B, H, dh, d), torch.float32, q.device, "dw1_out")
+        dw2_out = _out(dw2_out, (B, H, d, dh), torch.float32, q.device, "dw2_out")
+    et = _rates(eta_tok, B, H, T, q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dw1 = torch.empty((B, H, dh, d), dtype=torch.float32, device=q.device)
+    dw2 = torch.empty((B, H, d, dh), dtype=torch.float32, device=q.device)
+    deta = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if et is not None else None
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    with torch.cuda.device(q.device):
+        rc = lib.ttt_mlp_nc_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), w1.data_ptr(),
+                                w2.data_ptr(), s1, dz.data_ptr(), ptr(dw1_out), ptr(dw2_out),
+                                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dw1.data_ptr(),
+                                dw2.data_ptr(), B, H, T, d, dh, int(chunk), int(epochs),
+                                float(eta), et, ptr(deta), _loss(loss), _io_dtype(q),
+                                _stream(q.device, stream))
+    _check(rc)
+    return (dq, dk, dv, dw1, dw2) if deta is None else (dq, dk, dv, dw1, dw2, deta)
 
 
 def delta_rule_fwd(q, k, v, w0, eta, *, eta_tok=None, z=None, w_out=None, return_state=False,

@@ -186,6 +186,15 @@ size_t linear_bwd_mfma_workspace_bytes(const LinearBwdArgs& a);
 hipError_t launch_linear_bwd_mfma(const LinearArgs& fwd, const LinearBwdArgs& a, void* workspace,
                                   hipStream_t s);
 
+// backward of the non-causal layers (vector ALUs; linear or SiLU MLP, any chunk / epochs)
+size_t nc_bwd_workspace_floats(bool mlp, int B, int H, int T, int d, int h, int chunk, int epochs);
+hipError_t launch_nc_bwd(bool mlp, const void* q, const void* k, const void* v, const void* dz,
+                         const float* w1, const float* w2, long long w_batch_stride,
+                         const float* dw1_out, const float* dw2_out, const float* eta_tok,
+                         void* dq, void* dk, void* dv, float* dw1, float* dw2, float* deta_tok,
+                         float* ws, int B, int H, int T, int d, int h, int chunk, int epochs,
+                         float eta, int dot_loss, bool bf16_io, hipStream_t s);
+
 // dst[b][h][:] = src + b * batch_stride + h * per_head (the state when T = 0); zeros when
 // src is null.
 hipError_t launch_copy_state(float* dst, const float* src, long long batch_stride, int B, int H,

@@ -296,7 +296,7 @@ int linear_bwd(const char* fn, const void* q, const void* k, const void* v, cons
 
 extern "C" {
 
-int ttt_abi_version(void) { return 10; }
+int ttt_abi_version(void) { return 11; }
 
 const char* ttt_last_error(void) { return g_last_error.c_str(); }
 
@@ -343,6 +343,79 @@ int ttt_linear_bwd_noalloc(const void* q, const void* k, const void* v, const fl
   g_last_error.clear();
   return linear_bwd("ttt_linear_bwd_noalloc", q, k, v, w0, w0_batch_stride, dz, dw_out, dq, dk, dv,
                     dw0, B, H, T, d, chunk, eta, eta_tok, deta_tok, loss, io_dtype, stream, true);
+}
+
+// Shared by ttt_linear_nc_bwd (mlp false: w1 = w0, dw1 = dw0) and ttt_mlp_nc_bwd.
+int nc_bwd(const char* fn, bool mlp, const void* q, const void* k, const void* v, const float* w1,
+           const float* w2, long long w_batch_stride, const void* dz, const float* dw1_out,
+           const float* dw2_out, void* dq, void* dk, void* dv, float* dw1, float* dw2, int B,
+           int H, int T, int d, int dh, int chunk, int epochs, float eta, const float* eta_tok,
+           float* deta_tok, int loss, int io_dtype, ttt_stream_t stream) {
+  int rc = check_common(fn, q, k, v, dz, B, H, T, d, eta, eta_tok, io_dtype);
+  if (rc != TTT_OK) return rc;
+  if (loss != TTT_LOSS_MSE && loss != TTT_LOSS_DOT)
+    return fail(TTT_E_INVALID, "%s: unknown loss %d", fn, loss);
+  rc = check_epochs(fn, epochs, 0);
+  if (rc != TTT_OK) return rc;
+  if (deta_tok && !eta_tok) return fail(TTT_E_INVALID, "%s: deta_tok needs eta_tok", fn);
+  if (deta_tok && (reinterpret_cast<uintptr_t>(deta_tok) & 3) != 0)
+    return fail(TTT_E_INVALID, "%s: deta_tok must be 4-byte aligned", fn);
+  if (!w1 || !dw1 || (mlp && (!w2 || !dw2)))
+    return fail(TTT_E_INVALID, "%s: the states and their gradients must be non-null", fn);
+  if (T > 0 && (!dq || !dk || !dv))
+    return fail(TTT_E_INVALID, "%s: dq, dk and dv must be non-null", fn);
+  if (chunk < 1) return fail(TTT_E_INVALID, "%s: chunk must be >= 1 (got %d)", fn, chunk);
+  if (w_batch_stride < 0) return fail(TTT_E_INVALID, "%s: negative state batch stride", fn);
+  if (mlp && dh <= 0) return fail(TTT_E_INVALID, "%s: dh must be positive (got %d)", fn, dh);
+  if (d != 16 && d != 32 && d != 64)
+    return fail(TTT_E_UNSUPPORTED, "%s: d=%d not supported (16, 32, 64)", fn, d);
+  if (mlp && dh > 256) return fail(TTT_E_UNSUPPORTED, "%s: dh=%d not supported (<= 256)", fn, dh);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t n1 = mlp ? static_cast<size_t>(dh) * d : static_cast<size_t>(d) * d;
+  if (T == 0) {
+    const long long st = static_cast<long long>(H) * static_cast<long long>(n1);
+    rc = copy_state(dw1, dw1_out, st, B, H, n1, s);
+    if (rc != TTT_OK || !mlp) return rc;
+    return copy_state(dw2, dw2_out, st, B, H, n1, s);
+  }
+  const int b = chunk < T ? chunk : T;
+  const long long steps = static_cast<long long>((T + b - 1) / b) * epochs;
+  if (!fits_int64(B, H, steps + 2, 2LL * static_cast<long long>(n1) + 2LL * T * d + T) ||
+      steps > 0x7fffffffLL)
+    return fail(TTT_E_INVALID, "%s: workspace size overflows", fn);
+  StreamBuffer ws;
+  rc = get_workspace(ttt::nc_bwd_workspace_floats(mlp, B, H, T, d, dh, chunk, epochs) * sizeof(float),
+                     s, &ws);
+  if (rc != TTT_OK) return rc;
+  hipError_t e = ttt::launch_nc_bwd(mlp, q, k, v, dz, w1, w2, w_batch_stride, dw1_out, dw2_out,
+                                    eta_tok, dq, dk, dv, dw1, dw2, deta_tok,
+                                    static_cast<float*>(ws.ptr), B, H, T, d, dh, chunk, epochs, eta,
+                                    loss == TTT_LOSS_DOT ? 1 : 0, io_dtype == TTT_BF16, s);
+  if (e != hipSuccess) return hip_fail(e, "non-causal backward launch");
+  return TTT_OK;
+}
+
+int ttt_linear_nc_bwd(const void* q, const void* k, const void* v, const float* w0,
+                      long long w0_batch_stride, const void* dz, const float* dw_out, void* dq,
+                      void* dk, void* dv, float* dw0, int B, int H, int T, int d, int chunk,
+                      int epochs, float eta, const float* eta_tok, float* deta_tok, int loss,
+                      int io_dtype, ttt_stream_t stream) {
+  g_last_error.clear();
+  return nc_bwd("ttt_linear_nc_bwd", false, q, k, v, w0, nullptr, w0_batch_stride, dz, dw_out,
+                nullptr, dq, dk, dv, dw0, nullptr, B, H, T, d, 0, chunk, epochs, eta, eta_tok,
+                deta_tok, loss, io_dtype, stream);
+}
+
+int ttt_mlp_nc_bwd(const void* q, const void* k, const void* v, const float* w1, const float* w2,
+                   long long w_batch_stride, const void* dz, const float* dw1_out,
+                   const float* dw2_out, void* dq, void* dk, void* dv, float* dw1, float* dw2,
+                   int B, int H, int T, int d, int dh, int chunk, int epochs, float eta,
+                   const float* eta_tok, float* deta_tok, int loss, int io_dtype,
+                   ttt_stream_t stream) {
+  g_last_error.clear();
+  return nc_bwd("ttt_mlp_nc_bwd", true, q, k, v, w1, w2, w_batch_stride, dz, dw1_out, dw2_out, dq,
+                dk, dv, dw1, dw2, B, H, T, d, dh, chunk, epochs, eta, eta_tok, deta_tok, loss,
+                io_dtype, stream);
 }
 
 int ttt_mlp_bwd(const void* q, const void* k, const void* v, const float* w1, const float* w2,

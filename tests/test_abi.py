@@ -29,7 +29,8 @@ def lib():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("ttt_linear_fwd", "ttt_mlp_fwd", "delta_rule_fwd", "ttt_linear_bwd", "ttt_mlp_bwd",
-              "ttt_linear_ln_fwd", "ttt_mlp_ln_fwd", "ttt_last_error", "ttt_abi_version"):
+              "ttt_linear_ln_fwd", "ttt_mlp_ln_fwd", "ttt_last_error", "ttt_abi_version",
+              "ttt_linear_nc_bwd", "ttt_mlp_nc_bwd", "ttt_linear_bwd_noalloc"):
         assert n in names
 
 
@@ -40,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ttt_abi_version() == 10
+    assert lib.ttt_abi_version() == 11
 
 
 FAKE = 0x1000  # never dereferenced: validation fails before any HIP call
@@ -260,3 +261,48 @@ def test_linear_bwd_noalloc_rejects_a_history_beyond_its_scratch(lib):
                                     64, 16, 8192, 64, 16, 0.1, None, None, 0, 1, None)
     assert rc == ttt.TTT_E_UNSUPPORTED
     assert "scratch" in ttt.last_error()
+
+
+def _nc_bwd(lib, fn, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, w1=FAKE, w2=FAKE, stride=0, dz=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+             dw1=FAKE, dw2=FAKE, B=1, H=1, T=16, d=16, dh=32, chunk=4, epochs=2, eta=0.1,
+             eta_tok=None, deta=None, loss=0, io=0)
+    a.update(kw)
+    if fn == "linear":
+        return lib.ttt_linear_nc_bwd(a["q"], a["k"], a["v"], a["w1"], a["stride"], a["dz"], None,
+                                     a["dq"], a["dk"], a["dv"], a["dw1"], a["B"], a["H"], a["T"],
+                                     a["d"], a["chunk"], a["epochs"], a["eta"], a["eta_tok"],
+                                     a["deta"], a["loss"], a["io"], None)
+    return lib.ttt_mlp_nc_bwd(a["q"], a["k"], a["v"], a["w1"], a["w2"], a["stride"], a["dz"], None,
+                              None, a["dq"], a["dk"], a["dv"], a["dw1"], a["dw2"], a["B"], a["H"],
+                              a["T"], a["d"], a["dh"], a["chunk"], a["epochs"], a["eta"],
+                              a["eta_tok"], a["deta"], a["loss"], a["io"], None)
+
+
+@pytest.mark.parametrize("fn", ["linear", "mlp"])
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(epochs=0), ttt.TTT_E_INVALID, "epochs"),
+    (dict(chunk=0), ttt.TTT_E_INVALID, "chunk"),
+    (dict(dz=None), ttt.TTT_E_INVALID, "non-null"),
+    (dict(dk=None), ttt.TTT_E_INVALID, "dk"),
+    (dict(dw1=None), ttt.TTT_E_INVALID, "non-null"),
+    (dict(deta=FAKE), ttt.TTT_E_INVALID, "deta_tok needs eta_tok"),
+    (dict(eta_tok=FAKE + 2), ttt.TTT_E_INVALID, "aligned"),
+    (dict(loss=7), ttt.TTT_E_INVALID, "loss"),
+    (dict(d=48), ttt.TTT_E_UNSUPPORTED, "d=48"),
+    (dict(stride=-1), ttt.TTT_E_INVALID, "stride"),
+    (dict(io=5), ttt.TTT_E_INVALID, "io_dtype"),
+])
+def test_nc_bwd_rejects(lib, fn, kw, code, msg):
+    rc = _nc_bwd(lib, fn, **kw)
+    assert rc == code and msg in ttt.last_error(), (rc, ttt.last_error())
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(dh=0), ttt.TTT_E_INVALID, "dh"),
+    (dict(dh=300), ttt.TTT_E_UNSUPPORTED, "dh=300"),
+    (dict(w2=None), ttt.TTT_E_INVALID, "non-null"),
+])
+def test_mlp_nc_bwd_rejects(lib, kw, code, msg):
+    rc = _nc_bwd(lib, "mlp", **kw)
+    assert rc == code and msg in ttt.last_error(), (rc, ttt.last_error())

@@ -705,3 +705,124 @@ def test_linear_bwd_empty_sequence_copies_dw_out():
     _, _, _, dw0 = ttt.ttt_linear_bwd(q, q, q, w0, 0.1, 16, q)
     torch.cuda.synchronize()
     assert torch.count_nonzero(dw0).item() == 0
+
+
+# ------------------------------------------------------------------ backward of the non-causal layers
+# ttt_linear_nc_bwd / ttt_mlp_nc_bwd against the oracle's ttt_layer_vjp (torch.autograd
+# through the recurrence, pinned by central differences of the numpy forward): one
+# full-batch step at the vision shape, and mini-batches, epochs, rates and both losses.
+
+def _check_nc_bwd(kind, w, inp, with_dw, seed=0, rates=False, loss="mse", epochs=1, full=False):
+    import torch
+    import test_sequence_layers_amd as ttt
+    from oracle import ttt_oracle as O
+    from tests.oracle_pool import run_chains
+    _note(f"[parity] {kind}_nc_bwd B={w.B} H={w.H} T={w.T} d={w.d} h={w.h} chunk={w.chunk} "
+          f"epochs={epochs} io={w.io} dw_out={with_dw} rates={rates} loss={loss} seed={w.seed} "
+          f"full={full}")
+    rng = np.random.default_rng(40_000 + seed)
+    dz = rng.standard_normal((w.B, w.H, w.T, w.d)).astype(np.float32)
+    if w.io == "bf16":
+        dz = to_np(torch.from_numpy(dz).to(torch.bfloat16))
+    names = ("w0",) if kind == "linear" else ("w1", "w2")
+    shapes = {"w0": (w.d, w.d), "w1": (w.h, w.d), "w2": (w.d, w.h)}
+    dst = tuple(rng.standard_normal((w.B, w.H) + shapes[n]).astype(np.float32) for n in names) \
+        if with_dw else None
+    dev = to_device(inp, w.io)
+    dzd = torch.from_numpy(dz).to("cuda").to(dev["q"].dtype).contiguous()
+    dsd = tuple(torch.from_numpy(x).to("cuda").contiguous() for x in dst) if with_dw else None
+    et = make_token_rates(w, seed) if rates else None
+    etd = torch.from_numpy(et).to("cuda").contiguous() if rates else None
+    if kind == "linear":
+        out = ttt.ttt_linear_nc_bwd(dev["q"], dev["k"], dev["v"], dev["w0"], w.eta, w.chunk, dzd,
+                                    dsd[0] if with_dw else None, epochs=epochs, eta_tok=etd,
+                                    loss=loss)
+    else:
+        out = ttt.ttt_mlp_nc_bwd(dev["q"], dev["k"], dev["v"], dev["w1"], dev["w2"], w.eta, w.chunk,
+                                 dzd, *(dsd if with_dw else (None, None)), epochs=epochs,
+                                 eta_tok=etd, loss=loss)
+    torch.cuda.synchronize()
+    got = [to_np(t) for t in out]
+    del out, dev
+    state = tuple(inp[n] for n in names)
+    kw = dict(causal=False, epochs=epochs, eta_tok=et, loss=loss)
+    args = (kind, inp["q"], inp["k"], inp["v"], state, w.eta, w.chunk, dz, dst)
+    if full:
+        _note("[parity]   oracle over every sequence (worker processes)")
+        ref = run_chains("ttt_layer_vjp", w.B, w.H, args, kw, {4: 3})
+    else:
+        ref = O.ttt_layer_vjp(*args, **kw)
+    ref = [r for r in ref if r is not None]
+    tol = tol_for(w.io)
+    labels = ("dq", "dk", "dv") + tuple("d" + n for n in names) + (("deta_tok",) if rates else ())
+    assert len(got) == len(ref) == len(labels)
+    for name, g, r in zip(labels, got, ref):
+        if name == "deta_tok":  # [.., T]: one row per sequence
+            g, r = g[..., None, :], r[..., None, :]
+        check_close(name, g, r, tol, _note)
+
+
+@pytest.mark.parametrize("d,T,chunk,epochs,with_dw,rates,loss", [
+    (16, 30, 4, 2, True, False, "mse"), (16, 40, 40, 1, False, True, "mse"),
+    (32, 33, 7, 3, True, True, "dot"), (64, 50, 16, 1, False, False, "mse")])
+def test_linear_nc_bwd_fp32(d, T, chunk, epochs, with_dw, rates, loss):
+    w = workload(0).replace(B=2, H=3, T=T, d=d, chunk=chunk, causal=False, init="normal",
+                            eta=0.1, seed=400 + d + chunk)
+    _check_nc_bwd("linear", w, make_inputs(w), with_dw, seed=d, rates=rates, loss=loss,
+                  epochs=epochs)
+
+
+@pytest.mark.parametrize("d,h,T,chunk,epochs,with_dw,rates,loss", [
+    (16, 32, 30, 5, 2, True, True, "mse"), (16, 24, 37, 37, 1, False, False, "dot"),
+    (32, 64, 41, 9, 2, True, False, "mse"), (16, 256, 20, 8, 1, True, True, "mse"),
+    (64, 128, 20, 20, 1, False, False, "mse")])
+def test_mlp_nc_bwd_fp32(d, h, T, chunk, epochs, with_dw, rates, loss):
+    w = workload(3).replace(B=2, H=2, T=T, d=d, h=h, chunk=chunk, causal=False, io="f32",
+                            eta=0.05, seed=410 + h + chunk)
+    _check_nc_bwd("mlp", w, make_inputs(w), with_dw, seed=h, rates=rates, loss=loss,
+                  epochs=epochs)
+
+
+@pytest.mark.parametrize("kind,rates,loss,epochs,chunk", [
+    ("linear", False, "mse", 1, 196), ("linear", True, "dot", 2, 66),
+    ("mlp", False, "mse", 1, 196), ("mlp", True, "mse", 2, 49), ("mlp", False, "dot", 1, 196)])
+def test_nc_bwd_bf16_vision_shape(kind, rates, loss, epochs, chunk):
+    w = workload(4).replace(B=2, H=3, chunk=chunk, seed=420 + chunk)
+    if kind == "linear":
+        w = w.replace(kind="linear", h=0)
+    if epochs > 1:
+        w = w.replace(unit_keys=True, eta=0.1)
+    _check_nc_bwd(kind, w, make_inputs(w), with_dw=True, seed=7, rates=rates, loss=loss,
+                  epochs=epochs)
+
+
+def test_nc_bwd_per_batch_states():
+    w = workload(4).replace(B=3, H=2, T=50, chunk=20, unit_keys=True, eta=0.1, seed=430)
+    inp = make_inputs(w)
+    rng = np.random.default_rng(5)
+    inp["w1"] = (0.05 * rng.standard_normal((3, 2, 64, 64))).astype(np.float32)
+    inp["w2"] = (0.05 * rng.standard_normal((3, 2, 64, 64))).astype(np.float32)
+    _check_nc_bwd("mlp", w, inp, with_dw=False, epochs=2)
+
+
+def test_mlp_nc_bwd_vision_config_full_size():
+    w = workload(4)
+    _check_nc_bwd("mlp", w, make_inputs(w), with_dw=False, full=True)
+
+
+def test_linear_nc_bwd_vision_shape_full_size():
+    w = workload(4).replace(kind="linear", h=0)
+    _check_nc_bwd("linear", w, make_inputs(w), with_dw=False, full=True)
+
+
+def test_nc_bwd_empty_sequence_copies_state_gradients():
+    import torch
+    import test_sequence_layers_amd as ttt
+    z = torch.zeros((2, 3, 0, 16), dtype=torch.float32, device="cuda")
+    w1 = torch.zeros((3, 24, 16), device="cuda")
+    w2 = torch.zeros((3, 16, 24), device="cuda")
+    d1 = torch.randn((2, 3, 24, 16), device="cuda")
+    d2 = torch.randn((2, 3, 16, 24), device="cuda")
+    out = ttt.ttt_mlp_nc_bwd(z, z, z, w1, w2, 0.1, 4, z, d1, d2, epochs=2)
+    torch.cuda.synchronize()
+    assert torch.equal(out[3], d1) and torch.equal(out[4], d2)
