@@ -192,20 +192,22 @@ int ttt_linear_bwd_noalloc(const void* q, const void* k, const void* v,
                            int io_dtype, ttt_stream_t stream);
 
 /*
- * Backward pass of the causal TTT-MLP layer (f(k) = W2 SiLU(W1 k), scalar eta), the MLP
- * counterpart of ttt_linear_bwd.  For the forward call ttt_mlp_fwd(q, k, v, w1, w2, ...,
- * chunk, causal = 1, eta, NULL, loss, 1) (loss TTT_LOSS_MSE or TTT_LOSS_DOT; any other value
- * is TTT_E_INVALID) and upstream gradients dz of z and dw1_out, dw2_out of the final states,
+ * Backward pass of the causal TTT-MLP layer (f(k) = W2 SiLU(W1 k)), the MLP counterpart of
+ * ttt_linear_bwd.  For the forward call ttt_mlp_fwd(q, k, v, w1, w2, ..., chunk, causal = 1,
+ * eta, eta_tok, loss, 1) (loss TTT_LOSS_MSE or TTT_LOSS_DOT; any other value is
+ * TTT_E_INVALID) and upstream gradients dz of z and dw1_out, dw2_out of the final states,
  * writes
  *   dq, dk, dv  [B][H][T][d] io_dtype (out)
  *   dw1 [B][H][dh][d], dw2 [B][H][d][dh] float32 (out), per (b, h) sequence (sum over b for a
  *               state shared over the batch).
+ *   deta_tok    [B][H][T] float32 (out) or NULL: the gradient of the per-token rate factors
+ *               eta_tok [B][H][T] (or NULL: the scalar rate); needs eta_tok.
  *   dz [B][H][T][d] io_dtype;  dw1_out, dw2_out float32 of the same shapes as dw1, dw2, or
  *   NULL (zero).
  * Supported: d in {16, 32, 64}, 1 <= dh <= 256, chunks of at most 16 tokens, both dtypes.  The
  * call recomputes the forward pass and keeps its chunk-start states in a stream-ordered
- * workspace: bf16 with d = 64, dh = 256, chunk = 16, TTT_LOSS_MSE and 16-byte aligned buffers
- * (matrix cores; B*H*ceil(T/16)*64 KB), else float32 (B*H*ceil(T/chunk)*2*d*dh*4 bytes, plus the
+ * workspace: bf16 with d = 64, dh = 256, chunk = 16, TTT_LOSS_MSE, no eta_tok and 16-byte
+ * aligned buffers (matrix cores; B*H*ceil(T/16)*64 KB), else float32 (B*H*ceil(T/chunk)*2*d*dh*4 bytes, plus the
  * forward's 4*d*dh*4 bytes per sequence).  T = 0 copies dw1_out, dw2_out to dw1, dw2 (zeros
  * without them).
  */
@@ -214,6 +216,7 @@ int ttt_mlp_bwd(const void* q, const void* k, const void* v,
                 const void* dz, const float* dw1_out, const float* dw2_out,
                 void* dq, void* dk, void* dv, float* dw1, float* dw2,
                 int B, int H, int T, int d, int dh, int chunk, float eta,
+                const float* eta_tok, float* deta_tok,
                 int loss, int io_dtype, ttt_stream_t stream);
 
 /*

@@ -39,7 +39,7 @@ SIGNATURES = {
     "ttt_linear_bwd_noalloc": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp, _vp, _vp, _vp,
                                     _i, _i, _i, _i, _i, _f, _vp, _vp, _i, _i, _vp]),
     "ttt_mlp_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                         _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
+                         _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _i, _i, _vp]),
     "ttt_linear_nc_bwd": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp, _vp, _vp, _vp,
                                _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _i, _i, _vp]),
     "ttt_mlp_nc_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -280,12 +280,13 @@ def _linear_bwd(fn, q, k, v, w0, eta, chunk, dz, dw_out, eta_tok, loss, stream, 
     return (dq, dk, dv, dw0) if deta is None else (dq, dk, dv, dw0, deta)
 
 
-def ttt_mlp_bwd(q, k, v, w1, w2, eta, chunk, dz, dw1_out=None, dw2_out=None, *, loss="mse",
-                stream=None):
-    """Gradients of the causal TTT-MLP layer (SiLU, scalar eta; loss "mse" or "dot") for the
-    upstream gradients dz [B,H,T,d] (dtype of q) and dw1_out [B,H,dh,d], dw2_out [B,H,d,dh]
-    float32 (or None).  Returns (dq, dk, dv, dw1, dw2) with the state gradients per sequence
-    (sum them over the batch when the states are shared)."""
+def ttt_mlp_bwd(q, k, v, w1, w2, eta, chunk, dz, dw1_out=None, dw2_out=None, *, eta_tok=None,
+                loss="mse", stream=None):
+    """Gradients of the causal TTT-MLP layer (SiLU; loss "mse" or "dot") for the upstream
+    gradients dz [B,H,T,d] (dtype of q) and dw1_out [B,H,dh,d], dw2_out [B,H,d,dh] float32 (or
+    None).  Returns (dq, dk, dv, dw1, dw2) with the state gradients per sequence (sum them over
+    the batch when the states are shared); with per-token rate factors eta_tok [B,H,T] (as in
+    ttt_mlp_fwd) also their gradient, (dq, dk, dv, dw1, dw2, deta_tok)."""
     torch = _torch()
     lib = load_library()
     B, H, T, d = _tokens(q, k, v)
@@ -304,18 +305,20 @@ def ttt_mlp_bwd(q, k, v, w1, w2, eta, chunk, dz, dw1_out=None, dw2_out=None, *, 
     if dw1_out is not None:
         dw1_out = _out(dw1_out, (B, H, dh, d), torch.float32, q.device, "dw1_out")
         dw2_out = _out(dw2_out, (B, H, d, dh), torch.float32, q.device, "dw2_out")
+    et = _rates(eta_tok, B, H, T, q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     dw1 = torch.empty((B, H, dh, d), dtype=torch.float32, device=q.device)
     dw2 = torch.empty((B, H, d, dh), dtype=torch.float32, device=q.device)
+    deta = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if et is not None else None
     ptr = lambda t: t.data_ptr() if t is not None else None
     with torch.cuda.device(q.device):
         rc = lib.ttt_mlp_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), w1.data_ptr(), w2.data_ptr(),
                              s1, dz.data_ptr(), ptr(dw1_out), ptr(dw2_out), dq.data_ptr(),
                              dk.data_ptr(), dv.data_ptr(), dw1.data_ptr(), dw2.data_ptr(),
-                             B, H, T, d, dh, int(chunk), float(eta), _loss(loss), _io_dtype(q),
-                             _stream(q.device, stream))
+                             B, H, T, d, dh, int(chunk), float(eta), et, ptr(deta), _loss(loss),
+                             _io_dtype(q), _stream(q.device, stream))
     _check(rc)
-    return dq, dk, dv, dw1, dw2
+    return (dq, dk, dv, dw1, dw2) if deta is None else (dq, dk, dv, dw1, dw2, deta)
 
 
 def _dz(dz, q, B, H, T, d):

@@ -148,6 +148,10 @@ struct MlpBwdArgs {
   int B, H, T, d, dh, chunk;
   float eta;
   int dot_loss = 0;      // 1: loss -v^T f(k), error term -v (vector-ALU path only)
+  // per-token rate factors [B][H][T] (rate eta * eta_tok[t]) or null; their gradient
+  // [B][H][T] (out) or null (vector-ALU path only)
+  const float* eta_tok = nullptr;
+  float* deta_tok = nullptr;
 };
 
 // Host-side launchers (return a hipError_t; argument checks are done by the caller).

@@ -1,6 +1,6 @@
 // Backward pass of the causal TTT-MLP layer on the vector ALUs: f(k) = W2 SiLU(W1 k),
 // reconstruction loss or the negative dot-product loss (ViT3 news page, section 2), scalar
-// rate, chunk <= 16, hidden width <= 256, d in {16, 32, 64}, fp32 or bf16 I/O.  One workgroup of 1024 threads per (batch, head) chain walks the chunks
+// rate or per-token rate factors, chunk <= 16, hidden width <= 256, d in {16, 32, 64}, fp32 or bf16 I/O.  One workgroup of 1024 threads per (batch, head) chain walks the chunks
 // from last to first.
 //
 // The outer loop trains the projections and the initial states through the inner updates
@@ -20,6 +20,10 @@
 //   dL/dW1 = G1 + dUq^T Q + dUk^T K,  dL/dW2 = G2 + dZ^T Aq + R^T (ddU * phi'(U)) + dR^T A.
 // With the dot-product loss R = -V depends on neither A nor W2, so the dR W2 term of dUk and
 // the dR^T A term of dL/dW2 drop out (dV = -dR still holds).
+// With per-token rate factors e (token t learns at eta e_t; wmrh.cn summary, section 2.2.3)
+// every line above holds with Rt = diag(e) R in place of R, where R enters the update, the
+// outputs and Dm (our derivation): the lines give dRt, and then dR = diag(e) dRt (the path
+// through R = A W2^T - V: dV, dR W2, dR^T A) and de_t = <dRt_t, R_t>.
 // G1 and G2 accumulate in the dw1 / dw2 outputs (read and written by the owning threads);
 // the chunk-start states come from a forward recomputation that stores them (w_hist).
 #include "common.hpp"
@@ -38,8 +42,8 @@ __device__ __forceinline__ float d2silu_(float u) {  // SiLU''(u) = s (1 - s) (2
 
 template <int D>
 struct BwdLds {  // float offsets in the dynamic LDS block for hidden width h (row stride h)
-  static __host__ __device__ size_t tok(int i) { return static_cast<size_t>(i) * kMaxB * D; }  // 6 [b][D]
-  static __host__ __device__ size_t sq(int i) { return tok(6) + static_cast<size_t>(i) * kMaxB * kMaxB; }  // 4 [b][b]
+  static __host__ __device__ size_t tok(int i) { return static_cast<size_t>(i) * kMaxB * D; }  // 7 [b][D] + rates
+  static __host__ __device__ size_t sq(int i) { return tok(8) + static_cast<size_t>(i) * kMaxB * kMaxB; }  // 4 [b][b]
   static __host__ __device__ size_t hid(int i, int h) { return sq(4) + static_cast<size_t>(i) * kMaxB * h; }  // 7 [b][h]
   static __host__ __device__ size_t total(int h) { return hid(7, h); }
 };
@@ -52,8 +56,10 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_generic_kernel(MlpBwdArgs a)
   float* Qs = lds + BwdLds<D>::tok(1);
   float* Vs = lds + BwdLds<D>::tok(2);
   float* Zb = lds + BwdLds<D>::tok(3);   // dZ
-  float* Rs = lds + BwdLds<D>::tok(4);   // R
-  float* Rb = lds + BwdLds<D>::tok(5);   // dR
+  float* Rs = lds + BwdLds<D>::tok(4);   // Rt = diag(e) R
+  float* Rb = lds + BwdLds<D>::tok(5);   // dRt, then dR
+  float* Rr = lds + BwdLds<D>::tok(6);   // R (with per-token rates)
+  float* Es = lds + BwdLds<D>::tok(7);   // rate factors [kMaxB] (1 without)
   float* Mm = lds + BwdLds<D>::sq(0);    // tril(Q K^T)
   float* Nn = lds + BwdLds<D>::sq(1);    // tril(Aq A^T)
   float* Nb = lds + BwdLds<D>::sq(2);
@@ -84,6 +90,7 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_generic_kernel(MlpBwdArgs a)
   float* G1 = a.dw1 + static_cast<size_t>(chain) * hd;  // [h][D]
   float* G2 = a.dw2 + static_cast<size_t>(chain) * hd;  // [D][h]
 
+  const float* etok = a.eta_tok ? a.eta_tok + static_cast<size_t>(chain) * T : nullptr;
   for (size_t e = tid; e < hd; e += kThreads) {
     G1[e] = a.dw1_out ? a.dw1_out[static_cast<size_t>(chain) * hd + e] : 0.0f;
     G2[e] = a.dw2_out ? a.dw2_out[static_cast<size_t>(chain) * hd + e] : 0.0f;
@@ -104,6 +111,7 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_generic_kernel(MlpBwdArgs a)
       Vs[e] = in ? to_f32(v[off]) : 0.0f;
       Zb[e] = in ? to_f32(dz[off]) : 0.0f;
     }
+    for (int t = tid; t < kMaxB; t += kThreads) Es[t] = (etok && t < n) ? etok[c0 + t] : 1.0f;
     __syncthreads();
     // U = K W1^T, A = phi(U);  M = tril(Q K^T)
     for (int e = tid; e < kMaxB * h; e += kThreads) {
@@ -127,7 +135,9 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_generic_kernel(MlpBwdArgs a)
       float o = 0.0f;
       if (!a.dot_loss)
         for (int cc = 0; cc < h; ++cc) o += Ha[t * h + cc] * W2[static_cast<size_t>(i) * h + cc];
-      Rs[e] = t < n ? o - Vs[e] : 0.0f;
+      const float r = t < n ? o - Vs[e] : 0.0f;
+      Rr[e] = r;
+      Rs[e] = Es[t] * r;
     }
     __syncthreads();
     // dU = (R W2) * phi'(U)
@@ -205,7 +215,20 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_generic_kernel(MlpBwdArgs a)
       float acc = 0.0f;
       for (int cc = 0; cc < h; ++cc)
         acc += Hdd[t * h + cc] * dsilu_(Hu[t * h + cc]) * W2[static_cast<size_t>(i) * h + cc];
-      const float r = Rb[e] + acc;
+      Rb[e] += acc;  // dRt complete
+    }
+    __syncthreads();
+    // de_t = <dRt_t, R_t>; dR = diag(e) dRt; dV = -dR
+    if (a.deta_tok)
+      for (int t = tid; t < n; t += kThreads) {
+        float x = 0.0f;
+        for (int i = 0; i < D; ++i) x += Rb[t * D + i] * Rr[t * D + i];
+        a.deta_tok[static_cast<size_t>(chain) * T + c0 + t] = x;
+      }
+    __syncthreads();
+    for (int e = tid; e < kMaxB * D; e += kThreads) {
+      const int t = e / D, i = e % D;
+      const float r = Es[t] * Rb[e];
       Rb[e] = r;
       if (t < n) dv[static_cast<size_t>(c0 + t) * D + i] = from_f32<IO>(-r);
     }

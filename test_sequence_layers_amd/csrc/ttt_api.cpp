@@ -421,11 +421,14 @@ int ttt_mlp_nc_bwd(const void* q, const void* k, const void* v, const float* w1,
 int ttt_mlp_bwd(const void* q, const void* k, const void* v, const float* w1, const float* w2,
                 long long w_batch_stride, const void* dz, const float* dw1_out,
                 const float* dw2_out, void* dq, void* dk, void* dv, float* dw1, float* dw2, int B,
-                int H, int T, int d, int dh, int chunk, float eta, int loss, int io_dtype,
-                ttt_stream_t stream) {
+                int H, int T, int d, int dh, int chunk, float eta, const float* eta_tok,
+                float* deta_tok, int loss, int io_dtype, ttt_stream_t stream) {
   g_last_error.clear();
-  int rc = check_common("ttt_mlp_bwd", q, k, v, dz, B, H, T, d, eta, nullptr, io_dtype);
+  int rc = check_common("ttt_mlp_bwd", q, k, v, dz, B, H, T, d, eta, eta_tok, io_dtype);
   if (rc != TTT_OK) return rc;
+  if (deta_tok && !eta_tok) return fail(TTT_E_INVALID, "ttt_mlp_bwd: deta_tok needs eta_tok");
+  if (deta_tok && (reinterpret_cast<uintptr_t>(deta_tok) & 3) != 0)
+    return fail(TTT_E_INVALID, "ttt_mlp_bwd: deta_tok must be 4-byte aligned");
   if (loss != TTT_LOSS_MSE && loss != TTT_LOSS_DOT)
     return fail(TTT_E_INVALID, "ttt_mlp_bwd: unknown loss %d", loss);
   if (!w1 || !w2 || !dw1 || !dw2)
@@ -455,11 +458,11 @@ int ttt_mlp_bwd(const void* q, const void* k, const void* v, const float* w1, co
   const bool bf16 = io_dtype == TTT_BF16;
   const int dot = loss == TTT_LOSS_DOT ? 1 : 0;
   ttt::MlpBwdArgs g{q, k, v, dz, dw1_out, dw2_out, nullptr, dq, dk, dv,
-                    dw1, dw2, B, H, T, d, dh, chunk, eta, dot};
+                    dw1, dw2, B, H, T, d, dh, chunk, eta, dot, eta_tok, deta_tok};
   ttt::MlpArgs f{q, k, v, w1, w2, w_batch_stride, nullptr, nullptr, nullptr,
-                 B, H, T, d, dh, chunk, 1, eta, nullptr, dot};
+                 B, H, T, d, dh, chunk, 1, eta, eta_tok, dot};
   hipError_t e;
-  if (!dot && ttt::mlp_bwd_mfma_supported(g, bf16) && ttt::mlp_fast_supported(f, bf16)) {
+  if (!dot && !eta_tok && ttt::mlp_bwd_mfma_supported(g, bf16) && ttt::mlp_fast_supported(f, bf16)) {
     // matrix cores: the forward pass stores its bf16 chunk-start states, the backward pass
     // reads them
     StreamBuffer hist;

@@ -211,7 +211,8 @@ def _mlp_bwd(lib, **kw):
     a.update(kw)
     return lib.ttt_mlp_bwd(a["q"], a["k"], a["v"], a["w1"], a["w2"], a["stride"], a["dz"], None,
                            None, a["dq"], a["dk"], a["dv"], a["dw1"], a["dw2"], a["B"], a["H"],
-                           a["T"], a["d"], a["dh"], a["chunk"], a["eta"], a["loss"], a["io"], None)
+                           a["T"], a["d"], a["dh"], a["chunk"], a["eta"], a.get("eta_tok"),
+                           a.get("deta"), a["loss"], a["io"], None)
 
 
 @pytest.mark.parametrize("kw,code,msg", [
@@ -226,6 +227,8 @@ def _mlp_bwd(lib, **kw):
     (dict(eta=float("inf")), ttt.TTT_E_INVALID, "finite"),
     (dict(d=24), ttt.TTT_E_UNSUPPORTED, "d=24"),
     (dict(loss=7), ttt.TTT_E_INVALID, "unknown loss"),
+    (dict(deta=FAKE), ttt.TTT_E_INVALID, "deta_tok needs eta_tok"),
+    (dict(eta_tok=FAKE, deta=FAKE + 1), ttt.TTT_E_INVALID, "aligned"),
 ])
 def test_mlp_bwd_rejects(lib, kw, code, msg):
     assert _mlp_bwd(lib, **kw) == code

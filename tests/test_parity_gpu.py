@@ -590,13 +590,13 @@ def test_linear_bwd_config_full_size():
     _check_bwd(w, make_inputs(w), True, seed=1, full=True)
 
 
-def _check_mlp_bwd(w, inp, with_dw, sel=None, seed=0, loss="mse", full=False):
+def _check_mlp_bwd(w, inp, with_dw, sel=None, seed=0, loss="mse", full=False, rates=False):
     import torch
     import test_sequence_layers_amd as ttt
     from oracle import ttt_oracle as O
     from tests.oracle_pool import run_chains
     _note(f"[parity] mlp_bwd B={w.B} H={w.H} T={w.T} d={w.d} h={w.h} chunk={w.chunk} io={w.io} "
-          f"dw_out={with_dw} loss={loss} seed={w.seed} full={full}")
+          f"dw_out={with_dw} loss={loss} rates={rates} seed={w.seed} full={full}")
     rng = np.random.default_rng(30_000 + seed)
     dz = rng.standard_normal((w.B, w.H, w.T, w.d)).astype(np.float32)
     if w.io == "bf16":
@@ -607,14 +607,30 @@ def _check_mlp_bwd(w, inp, with_dw, sel=None, seed=0, loss="mse", full=False):
     dzd = torch.from_numpy(dz).to("cuda").to(dev["q"].dtype).contiguous()
     dd1 = torch.from_numpy(dw1).to("cuda").contiguous() if with_dw else None
     dd2 = torch.from_numpy(dw2).to("cuda").contiguous() if with_dw else None
+    et = make_token_rates(w, seed) if rates else None
+    etd = torch.from_numpy(et).to("cuda").contiguous() if rates else None
     out = ttt.ttt_mlp_bwd(dev["q"], dev["k"], dev["v"], dev["w1"], dev["w2"], w.eta, w.chunk, dzd,
-                          dd1, dd2, loss=loss)
+                          dd1, dd2, eta_tok=etd, loss=loss)
     torch.cuda.synchronize()
     got = [to_np(t) for t in out]
     del out, dev
     bc = lambda x, sh: np.broadcast_to(x, (w.B, w.H) + sh) if x.ndim == 3 else x
     q, k, v, dzz = inp["q"], inp["k"], inp["v"], dz
     w1, w2 = bc(inp["w1"], (w.h, w.d)), bc(inp["w2"], (w.d, w.h))
+    if rates:  # the general VJP (per-token rates), returning (..., deta_tok, None, None)
+        dst = (dw1, dw2) if with_dw else None
+        args = ("mlp", q, k, v, (w1, w2), w.eta, w.chunk, dzz, dst)
+        kw = dict(eta_tok=et, loss=loss)
+        if full:
+            _note("[parity]   oracle over every sequence (worker processes)")
+            ref = run_chains("ttt_layer_vjp", w.B, w.H, args, kw, {})
+        else:
+            ref = O.ttt_layer_vjp(*args, **kw)
+        for name, g, r in zip(("dq", "dk", "dv", "dw1", "dw2", "deta_tok"), got, ref):
+            if name == "deta_tok":
+                g, r = g[..., None, :], r[..., None, :]
+            check_close(name, g, r, tol_for(w.io), _note)
+        return
     if full:
         _note("[parity]   oracle over every sequence (worker processes)")
         ref = run_chains("ttt_mlp_vjp", w.B, w.H, (q, k, v, w1, w2, w.eta, w.chunk, dzz, dw1, dw2),
@@ -826,3 +842,26 @@ def test_nc_bwd_empty_sequence_copies_state_gradients():
     out = ttt.ttt_mlp_nc_bwd(z, z, z, w1, w2, 0.1, 4, z, d1, d2, epochs=2)
     torch.cuda.synchronize()
     assert torch.equal(out[3], d1) and torch.equal(out[4], d2)
+
+
+# ------------------------------------------------------------------ MLP backward with per-token rates
+# ttt_mlp_bwd with eta_tok (the learnable rate of the wmrh.cn summary, section 2.2.3) and its
+# gradient deta_tok, against the oracle's ttt_layer_vjp (pinned by central differences).
+
+@pytest.mark.parametrize("d,h,chunk,with_dw,loss", [(16, 32, 4, True, "mse"), (32, 64, 16, False, "mse"),
+                                                    (16, 24, 5, True, "dot"), (16, 32, 1, False, "mse")])
+def test_mlp_bwd_token_rates_fp32(d, h, chunk, with_dw, loss):
+    w = workload(3).replace(B=2, H=2, T=37, d=d, h=h, chunk=chunk, io="f32", eta=0.1,
+                            seed=500 + h + chunk)
+    _check_mlp_bwd(w, make_inputs(w), with_dw, seed=chunk, loss=loss, rates=True)
+
+
+@pytest.mark.parametrize("T,with_dw", [(16, True), (70, False)])
+def test_mlp_bwd_token_rates_bf16_h256(T, with_dw):
+    w = workload(3).replace(B=1, H=2, T=T, seed=510 + T)
+    _check_mlp_bwd(w, make_inputs(w), with_dw, seed=T, rates=True)
+
+
+def test_mlp_bwd_token_rates_config_full_size():
+    w = workload(3)
+    _check_mlp_bwd(w, make_inputs(w), False, seed=3, rates=True, full=True)
