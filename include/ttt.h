@@ -220,6 +220,28 @@ int ttt_mlp_bwd(const void* q, const void* k, const void* v,
                 int loss, int io_dtype, ttt_stream_t stream);
 
 /*
+ * Backward pass of the paper's causal TTT-Linear layer, f(x) = x + LN(W x) (wmrh.cn summary
+ * of Sun et al. 2024, section 2.2.1), the counterpart of ttt_linear_bwd for the forward call
+ * ttt_linear_ln_fwd(q, k, v, w0, ..., ln_weight, ln_bias, ln_eps, ..., chunk, causal = 1,
+ * eta, eta_tok, loss, 1).  Besides dq, dk, dv, dw0 and deta_tok (as ttt_linear_bwd) writes
+ *   dln_weight, dln_bias  [B][H][d] float32 (out): the gradients of the layer norm's gain and
+ *               bias, per (b, h) sequence (sum over b for the per-head parameters).
+ * Supported: d in {16, 32, 64}, chunks of at most 16 tokens, either loss, both dtypes, on the
+ * vector ALUs; the call recomputes the forward pass and keeps its float32 chunk-start states
+ * in a stream-ordered workspace (B*H*ceil(T/chunk)*d*d*4 bytes).  T = 0 copies dw_out to dw0
+ * and zeroes dln_weight, dln_bias.
+ */
+int ttt_linear_ln_bwd(const void* q, const void* k, const void* v,
+                      const float* w0, long long w0_batch_stride,
+                      const float* ln_weight, const float* ln_bias, float ln_eps,
+                      const void* dz, const float* dw_out,
+                      void* dq, void* dk, void* dv, float* dw0,
+                      float* dln_weight, float* dln_bias,
+                      int B, int H, int T, int d, int chunk, float eta,
+                      const float* eta_tok, float* deta_tok, int loss,
+                      int io_dtype, ttt_stream_t stream);
+
+/*
  * Backward pass of the non-causal TTT layers: the layer trains on every pair first (steps of
  * mini-batch GD over the chunks, `epochs` passes) and then every query reads the final
  * weights (ViT3 news page, section 1, observation 2); the outer loop trains the projections,

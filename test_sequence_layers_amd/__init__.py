@@ -23,6 +23,7 @@ from ._binding import (  # noqa: F401
     ttt_linear_bwd,
     ttt_linear_bwd_noalloc,
     ttt_linear_fwd,
+    ttt_linear_ln_bwd,
     ttt_linear_ln_fwd,
     ttt_linear_nc_bwd,
     ttt_mlp_bwd,

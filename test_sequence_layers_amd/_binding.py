@@ -40,6 +40,8 @@ SIGNATURES = {
                                     _i, _i, _i, _i, _i, _f, _vp, _vp, _i, _i, _vp]),
     "ttt_mlp_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                          _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _i, _i, _vp]),
+    "ttt_linear_ln_bwd": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _f, _vp, _vp, _vp, _vp, _vp, _vp,
+                               _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _vp, _i, _i, _vp]),
     "ttt_linear_nc_bwd": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp, _vp, _vp, _vp,
                                _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _i, _i, _vp]),
     "ttt_mlp_nc_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -327,6 +329,39 @@ def _dz(dz, q, B, H, T, d):
             or dz.device != q.device or not dz.is_contiguous()):
         raise ValueError(f"dz must be a contiguous {q.dtype} tensor of shape {(B, H, T, d)}")
     return dz
+
+
+def ttt_linear_ln_bwd(q, k, v, w0, ln_weight, ln_bias, eta, chunk, dz, dw_out=None, *,
+                      ln_eps=1e-6, eta_tok=None, loss="mse", stream=None):
+    """Gradients of the paper's causal TTT-Linear layer x + LN(W x) (ttt_linear_ln_fwd with
+    the same arguments) for the upstream gradients dz and dw_out.  Returns (dq, dk, dv, dw0,
+    dln_weight, dln_bias), plus deta_tok [B,H,T] with eta_tok; dw0 [B,H,d,d] and the layer-norm
+    gradients [B,H,d] per sequence."""
+    torch = _torch()
+    lib = load_library()
+    B, H, T, d = _tokens(q, k, v)
+    w0, stride = _state(w0, B, H, (d, d), "w0", q.device)
+    lw, lb, eps = _ln(ln_weight, ln_bias, ln_eps, H, d, q.device)
+    dz = _dz(dz, q, B, H, T, d)
+    if dw_out is not None:
+        dw_out = _out(dw_out, (B, H, d, d), torch.float32, q.device, "dw_out")
+    et = _rates(eta_tok, B, H, T, q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dw0 = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
+    dlw = torch.empty((B, H, d), dtype=torch.float32, device=q.device)
+    dlb = torch.empty((B, H, d), dtype=torch.float32, device=q.device)
+    deta = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if et is not None else None
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    with torch.cuda.device(q.device):
+        rc = lib.ttt_linear_ln_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), w0.data_ptr(), stride,
+                                   lw, lb, eps, dz.data_ptr(),
+                                   ptr(dw_out), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                   dw0.data_ptr(), dlw.data_ptr(), dlb.data_ptr(), B, H, T, d,
+                                   int(chunk), float(eta), et, ptr(deta), _loss(loss), _io_dtype(q),
+                                   _stream(q.device, stream))
+    _check(rc)
+    res = (dq, dk, dv, dw0, dlw, dlb)
+    return res if deta is None else res + (deta,)
 
 
 def ttt_linear_nc_bwd(q, k, v, w0, eta, chunk, dz, dw_out=None, *, epochs=1, eta_tok=None,

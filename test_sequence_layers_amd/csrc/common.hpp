@@ -105,6 +105,13 @@ struct LinearBwdArgs {
   const float* eta_tok = nullptr;
   float* deta_tok = nullptr;
   int dot_loss = 0;  // 1: loss -v^T W k (R = -V)
+  // the paper's inner model f(x) = x + LN(W x): per-head gamma, beta [H][d], eps, and their
+  // gradients per sequence [B][H][d] (out)
+  const float* ln_w = nullptr;
+  const float* ln_b = nullptr;
+  float ln_eps = 0.0f;
+  float* dln_w = nullptr;
+  float* dln_b = nullptr;
 };
 
 struct MlpArgs {
@@ -175,6 +182,9 @@ bool mlp_nc_supported(const MlpArgs& a, bool bf16_io);
 hipError_t launch_mlp_nc(const MlpArgs& a, hipStream_t s);
 
 hipError_t launch_linear_bwd_generic(const LinearBwdArgs& a, bool bf16_io, hipStream_t s);
+// backward of the paper's TTT-Linear x + LN(W x) (vector ALUs; reads the chunk-start states
+// in a.w_hist)
+hipError_t launch_linear_ln_bwd(const LinearBwdArgs& a, bool bf16_io, hipStream_t s);
 hipError_t launch_mlp_bwd_generic(const MlpBwdArgs& a, bool bf16_io, hipStream_t s);
 // matrix-core forward pass that stores the bf16 chunk-start states (64 KB per chunk), and
 // the matrix-core backward pass reading them (d = 64, hidden 256, chunk 16, bf16)

@@ -345,6 +345,71 @@ int ttt_linear_bwd_noalloc(const void* q, const void* k, const void* v, const fl
                     dw0, B, H, T, d, chunk, eta, eta_tok, deta_tok, loss, io_dtype, stream, true);
 }
 
+int ttt_linear_ln_bwd(const void* q, const void* k, const void* v, const float* w0,
+                      long long w0_batch_stride, const float* ln_weight, const float* ln_bias,
+                      float ln_eps, const void* dz, const float* dw_out, void* dq, void* dk,
+                      void* dv, float* dw0, float* dln_weight, float* dln_bias, int B, int H,
+                      int T, int d, int chunk, float eta, const float* eta_tok, float* deta_tok,
+                      int loss, int io_dtype, ttt_stream_t stream) {
+  g_last_error.clear();
+  const char* fn = "ttt_linear_ln_bwd";
+  int rc = check_ln(fn, ln_weight, ln_bias, ln_eps);
+  if (rc != TTT_OK) return rc;
+  rc = check_common(fn, q, k, v, dz, B, H, T, d, eta, eta_tok, io_dtype);
+  if (rc != TTT_OK) return rc;
+  if (loss != TTT_LOSS_MSE && loss != TTT_LOSS_DOT)
+    return fail(TTT_E_INVALID, "%s: unknown loss %d", fn, loss);
+  if (deta_tok && !eta_tok) return fail(TTT_E_INVALID, "%s: deta_tok needs eta_tok", fn);
+  if (deta_tok && (reinterpret_cast<uintptr_t>(deta_tok) & 3) != 0)
+    return fail(TTT_E_INVALID, "%s: deta_tok must be 4-byte aligned", fn);
+  if (!w0 || !dw0 || !dln_weight || !dln_bias)
+    return fail(TTT_E_INVALID, "%s: w0, dw0, dln_weight and dln_bias must be non-null", fn);
+  if (T > 0 && (!dq || !dk || !dv))
+    return fail(TTT_E_INVALID, "%s: dq, dk and dv must be non-null", fn);
+  if (chunk < 1) return fail(TTT_E_INVALID, "%s: chunk must be >= 1 (got %d)", fn, chunk);
+  if (w0_batch_stride < 0) return fail(TTT_E_INVALID, "%s: negative w0_batch_stride", fn);
+  if (d != 16 && d != 32 && d != 64)
+    return fail(TTT_E_UNSUPPORTED, "%s: d=%d not supported (16, 32, 64)", fn, d);
+  if (T > 0 && (chunk < T ? chunk : T) > 16)
+    return fail(TTT_E_UNSUPPORTED, "%s: chunks of more than 16 tokens not supported", fn);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t dd = static_cast<size_t>(d) * d;
+  if (T == 0) {
+    rc = copy_state(dw0, dw_out, static_cast<long long>(H) * dd, B, H, dd, s);
+    if (rc != TTT_OK) return rc;
+    rc = copy_state(dln_weight, nullptr, 0, B, H, static_cast<size_t>(d), s);
+    if (rc != TTT_OK) return rc;
+    return copy_state(dln_bias, nullptr, 0, B, H, static_cast<size_t>(d), s);
+  }
+  const int b = chunk < T ? chunk : T;
+  const long long nchunks = (T + b - 1) / b;
+  if (!fits_int64(B, H, nchunks, static_cast<long long>(dd) * 4))
+    return fail(TTT_E_INVALID, "%s: state history overflows", fn);
+  const bool bf16 = io_dtype == TTT_BF16;
+  const int dot = loss == TTT_LOSS_DOT ? 1 : 0;
+  StreamBuffer hist;
+  rc = get_workspace(static_cast<size_t>(B) * H * nchunks * dd * sizeof(float), s, &hist);
+  if (rc != TTT_OK) return rc;
+  // the forward recomputation on the generic kernel, storing the chunk-start states
+  ttt::LinearArgs f{q, k, v, w0, w0_batch_stride, nullptr, nullptr, B, H, T, d, chunk, 1, eta,
+                    eta_tok, dot, static_cast<float*>(hist.ptr)};
+  f.ln_w = ln_weight;
+  f.ln_b = ln_bias;
+  f.ln_eps = ln_eps;
+  hipError_t e = ttt::launch_linear_generic(f, bf16, s);
+  if (e != hipSuccess) return hip_fail(e, "ttt_linear_ln_bwd state launch");
+  ttt::LinearBwdArgs g{q, k, v, dz, dw_out, static_cast<const float*>(hist.ptr), dq, dk, dv, dw0,
+                       B, H, T, d, chunk, eta, eta_tok, deta_tok, dot};
+  g.ln_w = ln_weight;
+  g.ln_b = ln_bias;
+  g.ln_eps = ln_eps;
+  g.dln_w = dln_weight;
+  g.dln_b = dln_bias;
+  e = ttt::launch_linear_ln_bwd(g, bf16, s);
+  if (e != hipSuccess) return hip_fail(e, "ttt_linear_ln_bwd launch");
+  return TTT_OK;
+}
+
 // Shared by ttt_linear_nc_bwd (mlp false: w1 = w0, dw1 = dw0) and ttt_mlp_nc_bwd.
 int nc_bwd(const char* fn, bool mlp, const void* q, const void* k, const void* v, const float* w1,
            const float* w2, long long w_batch_stride, const void* dz, const float* dw1_out,

@@ -309,3 +309,28 @@ def test_nc_bwd_rejects(lib, fn, kw, code, msg):
 def test_mlp_nc_bwd_rejects(lib, kw, code, msg):
     rc = _nc_bwd(lib, "mlp", **kw)
     assert rc == code and msg in ttt.last_error(), (rc, ttt.last_error())
+
+
+def _ln_bwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, w0=FAKE, stride=0, lw=FAKE, lb=FAKE, eps=1e-6, dz=FAKE,
+             dq=FAKE, dk=FAKE, dv=FAKE, dw0=FAKE, dlw=FAKE, dlb=FAKE, B=1, H=1, T=16, d=16,
+             chunk=16, eta=0.1, eta_tok=None, deta=None, loss=0, io=0)
+    a.update(kw)
+    return lib.ttt_linear_ln_bwd(a["q"], a["k"], a["v"], a["w0"], a["stride"], a["lw"], a["lb"],
+                                 a["eps"], a["dz"], None, a["dq"], a["dk"], a["dv"], a["dw0"],
+                                 a["dlw"], a["dlb"], a["B"], a["H"], a["T"], a["d"], a["chunk"],
+                                 a["eta"], a["eta_tok"], a["deta"], a["loss"], a["io"], None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(eps=0.0), ttt.TTT_E_INVALID, "ln_eps"),
+    (dict(lw=None), ttt.TTT_E_INVALID, "ln_bias must be non-null"),
+    (dict(dlb=None), ttt.TTT_E_INVALID, "dln_bias"),
+    (dict(chunk=32, T=64), ttt.TTT_E_UNSUPPORTED, "16 tokens"),
+    (dict(d=48), ttt.TTT_E_UNSUPPORTED, "d=48"),
+    (dict(deta=FAKE), ttt.TTT_E_INVALID, "deta_tok needs eta_tok"),
+    (dict(loss=3), ttt.TTT_E_INVALID, "loss"),
+])
+def test_linear_ln_bwd_rejects(lib, kw, code, msg):
+    rc = _ln_bwd(lib, **kw)
+    assert rc == code and msg in ttt.last_error(), (rc, ttt.last_error())

@@ -865,3 +865,87 @@ def test_mlp_bwd_token_rates_bf16_h256(T, with_dw):
 def test_mlp_bwd_token_rates_config_full_size():
     w = workload(3)
     _check_mlp_bwd(w, make_inputs(w), False, seed=3, rates=True, full=True)
+
+
+# ------------------------------------------------------------------ backward of the paper's TTT-Linear
+# ttt_linear_ln_bwd (f(x) = x + LN(W x); wmrh.cn summary, section 2.2.1) against the oracle's
+# ttt_layer_vjp with ln, including the layer norm's gain and bias gradients.
+
+def _check_ln_bwd(w, inp, with_dw, seed=0, rates=False, loss="mse", full=False, w_scale=None):
+    import torch
+    import test_sequence_layers_amd as ttt
+    from oracle import ttt_oracle as O
+    from tests.oracle_pool import run_chains
+    from tests.parity_util import LN_EPS
+    _note(f"[parity] linear_ln_bwd B={w.B} H={w.H} T={w.T} d={w.d} chunk={w.chunk} io={w.io} "
+          f"dw_out={with_dw} rates={rates} loss={loss} seed={w.seed} full={full}")
+    if w_scale is not None:
+        inp["w0"] = (inp["w0"] * w_scale).astype(np.float32)
+    rng = np.random.default_rng(50_000 + seed)
+    dz = rng.standard_normal((w.B, w.H, w.T, w.d)).astype(np.float32)
+    if w.io == "bf16":
+        dz = to_np(torch.from_numpy(dz).to(torch.bfloat16))
+    dw = rng.standard_normal((w.B, w.H, w.d, w.d)).astype(np.float32) if with_dw else None
+    lw, lb = make_ln_params(w, seed)
+    et = make_token_rates(w, seed) if rates else None
+    dev = to_device(inp, w.io)
+    out = ttt.ttt_linear_ln_bwd(
+        dev["q"], dev["k"], dev["v"], dev["w0"], torch.from_numpy(lw).cuda(),
+        torch.from_numpy(lb).cuda(), w.eta, w.chunk,
+        torch.from_numpy(dz).to("cuda").to(dev["q"].dtype).contiguous(),
+        torch.from_numpy(dw).cuda() if with_dw else None, ln_eps=LN_EPS,
+        eta_tok=torch.from_numpy(et).cuda() if rates else None, loss=loss)
+    torch.cuda.synchronize()
+    got = [to_np(t) for t in out]
+    del out, dev
+    args = ("linear", inp["q"], inp["k"], inp["v"], (inp["w0"],), w.eta, w.chunk, dz,
+            (dw,) if with_dw else None)
+    kw = dict(eta_tok=et, loss=loss, ln=(lw, lb, LN_EPS))
+    if full:
+        _note("[parity]   oracle over every sequence (worker processes)")
+        ref = run_chains("ttt_layer_vjp", w.B, w.H, args, kw, {4: 3, "ln": 2})
+    else:
+        ref = O.ttt_layer_vjp(*args, **kw)
+    dq, dk, dv, dw0, de, dg, db = ref
+    refs = [dq, dk, dv, dw0, dg, db] + ([de] if rates else [])
+    tol = tol_for(w.io)
+    for name, g, r in zip(("dq", "dk", "dv", "dw0", "dln_weight", "dln_bias", "deta_tok"), got, refs):
+        if name in ("deta_tok", "dln_weight", "dln_bias"):  # one row per sequence
+            g, r = g[..., None, :], r[..., None, :]
+        check_close(name, g, r, tol, _note)
+
+
+@pytest.mark.parametrize("d,chunk,with_dw,rates,loss", [
+    (16, 4, True, True, "mse"), (32, 16, False, False, "dot"), (64, 5, True, False, "mse"),
+    (16, 1, False, True, "mse")])
+def test_linear_ln_bwd_fp32(d, chunk, with_dw, rates, loss):
+    w = workload(0).replace(B=2, H=3, T=37, d=d, chunk=chunk, init="normal", eta=0.2,
+                            seed=600 + d + chunk)
+    # chunk 1: larger initial weights, so that the first tokens' layer-norm inputs are not of
+    # the order of sqrt(eps) (where the recurrence itself is ill-conditioned)
+    _check_ln_bwd(w, make_inputs(w), with_dw, seed=d, rates=rates, loss=loss,
+                  w_scale=10.0 if chunk == 1 else None)
+
+
+@pytest.mark.parametrize("T,with_dw,rates,loss", [(16, True, False, "mse"), (77, False, True, "mse"),
+                                                  (200, True, False, "dot")])
+def test_linear_ln_bwd_bf16_d64_chunk16(T, with_dw, rates, loss):
+    w = workload(1).replace(B=2, H=3, T=T, seed=610 + T)
+    _check_ln_bwd(w, make_inputs(w), with_dw, seed=T, rates=rates, loss=loss)
+
+
+def test_linear_ln_bwd_config_full_size():
+    w = workload(1)
+    _check_ln_bwd(w, make_inputs(w), False, seed=1, full=True)
+
+
+def test_linear_ln_bwd_empty_sequence():
+    import torch
+    import test_sequence_layers_amd as ttt
+    z = torch.zeros((2, 3, 0, 16), device="cuda")
+    w0 = torch.zeros((3, 16, 16), device="cuda")
+    lw, lb = torch.ones((3, 16), device="cuda"), torch.zeros((3, 16), device="cuda")
+    d0 = torch.randn((2, 3, 16, 16), device="cuda")
+    out = ttt.ttt_linear_ln_bwd(z, z, z, w0, lw, lb, 0.1, 4, z, d0)
+    torch.cuda.synchronize()
+    assert torch.equal(out[3], d0) and not out[4].any() and not out[5].any()
