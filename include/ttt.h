@@ -242,6 +242,27 @@ int ttt_linear_ln_bwd(const void* q, const void* k, const void* v,
                       int io_dtype, ttt_stream_t stream);
 
 /*
+ * Backward pass of the paper's causal TTT-MLP layer, f(x) = x + LN(W2 GELU(W1 x)), the
+ * counterpart of ttt_mlp_bwd for the forward call ttt_mlp_ln_fwd(q, k, v, w1, w2, ...,
+ * ln_weight, ln_bias, ln_eps, ..., chunk, causal = 1, eta, eta_tok, loss, 1).  Besides dq,
+ * dk, dv, dw1, dw2 and deta_tok (as ttt_mlp_bwd) writes dln_weight, dln_bias [B][H][d]
+ * float32 (out), per (b, h) sequence.  Supported: d in {16, 32, 64}, 1 <= dh <= 256, chunks
+ * of at most 16 tokens, either loss, both dtypes, on the vector ALUs; the call recomputes the
+ * forward pass and keeps its float32 chunk-start states in a stream-ordered workspace
+ * (B*H*ceil(T/chunk)*2*d*dh*4 bytes, plus the forward's 4*d*dh*4 bytes per sequence).
+ * T = 0 copies dw1_out, dw2_out and zeroes dln_weight, dln_bias.
+ */
+int ttt_mlp_ln_bwd(const void* q, const void* k, const void* v,
+                   const float* w1, const float* w2, long long w_batch_stride,
+                   const float* ln_weight, const float* ln_bias, float ln_eps,
+                   const void* dz, const float* dw1_out, const float* dw2_out,
+                   void* dq, void* dk, void* dv, float* dw1, float* dw2,
+                   float* dln_weight, float* dln_bias,
+                   int B, int H, int T, int d, int dh, int chunk, float eta,
+                   const float* eta_tok, float* deta_tok, int loss,
+                   int io_dtype, ttt_stream_t stream);
+
+/*
  * Backward pass of the non-causal TTT layers: the layer trains on every pair first (steps of
  * mini-batch GD over the chunks, `epochs` passes) and then every query reads the final
  * weights (ViT3 news page, section 1, observation 2); the outer loop trains the projections,

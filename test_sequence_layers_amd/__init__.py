@@ -28,6 +28,7 @@ from ._binding import (  # noqa: F401
     ttt_linear_nc_bwd,
     ttt_mlp_bwd,
     ttt_mlp_fwd,
+    ttt_mlp_ln_bwd,
     ttt_mlp_ln_fwd,
     ttt_mlp_nc_bwd,
 )

@@ -42,6 +42,8 @@ SIGNATURES = {
                          _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _i, _i, _vp]),
     "ttt_linear_ln_bwd": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _f, _vp, _vp, _vp, _vp, _vp, _vp,
                                _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _vp, _i, _i, _vp]),
+    "ttt_mlp_ln_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _ll, _vp, _vp, _f, _vp, _vp, _vp, _vp, _vp, _vp,
+                            _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _i, _i, _vp]),
     "ttt_linear_nc_bwd": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp, _vp, _vp, _vp,
                                _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _i, _i, _vp]),
     "ttt_mlp_nc_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -361,6 +363,48 @@ def ttt_linear_ln_bwd(q, k, v, w0, ln_weight, ln_bias, eta, chunk, dz, dw_out=No
                                    _stream(q.device, stream))
     _check(rc)
     res = (dq, dk, dv, dw0, dlw, dlb)
+    return res if deta is None else res + (deta,)
+
+
+def ttt_mlp_ln_bwd(q, k, v, w1, w2, ln_weight, ln_bias, eta, chunk, dz, dw1_out=None,
+                   dw2_out=None, *, ln_eps=1e-6, eta_tok=None, loss="mse", stream=None):
+    """Gradients of the paper's causal TTT-MLP layer x + LN(W2 GELU(W1 x)) (ttt_mlp_ln_fwd
+    with the same arguments).  Returns (dq, dk, dv, dw1, dw2, dln_weight, dln_bias), plus
+    deta_tok [B,H,T] with eta_tok; state and layer-norm gradients per sequence."""
+    torch = _torch()
+    lib = load_library()
+    B, H, T, d = _tokens(q, k, v)
+    if w1.dim() < 2:
+        raise ValueError("w1 must be [H, dh, d] or [B, H, dh, d]")
+    dh = int(w1.shape[-2])
+    w1, s1 = _state(w1, B, H, (dh, d), "w1", q.device)
+    w2, s2 = _state(w2, B, H, (d, dh), "w2", q.device)
+    if s1 != s2:
+        raise ValueError("w1 and w2 must both be shared over the batch or both per batch")
+    lw, lb, eps = _ln(ln_weight, ln_bias, ln_eps, H, d, q.device)
+    dz = _dz(dz, q, B, H, T, d)
+    if (dw1_out is None) != (dw2_out is None):
+        raise ValueError("give both dw1_out and dw2_out, or neither")
+    if dw1_out is not None:
+        dw1_out = _out(dw1_out, (B, H, dh, d), torch.float32, q.device, "dw1_out")
+        dw2_out = _out(dw2_out, (B, H, d, dh), torch.float32, q.device, "dw2_out")
+    et = _rates(eta_tok, B, H, T, q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dw1 = torch.empty((B, H, dh, d), dtype=torch.float32, device=q.device)
+    dw2 = torch.empty((B, H, d, dh), dtype=torch.float32, device=q.device)
+    dlw = torch.empty((B, H, d), dtype=torch.float32, device=q.device)
+    dlb = torch.empty((B, H, d), dtype=torch.float32, device=q.device)
+    deta = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if et is not None else None
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    with torch.cuda.device(q.device):
+        rc = lib.ttt_mlp_ln_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), w1.data_ptr(),
+                                w2.data_ptr(), s1, lw, lb, eps, dz.data_ptr(), ptr(dw1_out),
+                                ptr(dw2_out), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                dw1.data_ptr(), dw2.data_ptr(), dlw.data_ptr(), dlb.data_ptr(),
+                                B, H, T, d, dh, int(chunk), float(eta), et, ptr(deta), _loss(loss),
+                                _io_dtype(q), _stream(q.device, stream))
+    _check(rc)
+    res = (dq, dk, dv, dw1, dw2, dlw, dlb)
     return res if deta is None else res + (deta,)
 
 

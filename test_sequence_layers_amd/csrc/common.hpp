@@ -159,6 +159,13 @@ struct MlpBwdArgs {
   // [B][H][T] (out) or null (vector-ALU path only)
   const float* eta_tok = nullptr;
   float* deta_tok = nullptr;
+  // the paper's TTT-MLP x + LN(W2 GELU(W1 x)): per-head gamma, beta [H][d], eps, and their
+  // gradients per sequence [B][H][d] (out)
+  const float* ln_w = nullptr;
+  const float* ln_b = nullptr;
+  float ln_eps = 0.0f;
+  float* dln_w = nullptr;
+  float* dln_b = nullptr;
 };
 
 // Host-side launchers (return a hipError_t; argument checks are done by the caller).
@@ -186,6 +193,9 @@ hipError_t launch_linear_bwd_generic(const LinearBwdArgs& a, bool bf16_io, hipSt
 // in a.w_hist)
 hipError_t launch_linear_ln_bwd(const LinearBwdArgs& a, bool bf16_io, hipStream_t s);
 hipError_t launch_mlp_bwd_generic(const MlpBwdArgs& a, bool bf16_io, hipStream_t s);
+// backward of the paper's TTT-MLP x + LN(W2 GELU(W1 x)) (vector ALUs; reads w_hist)
+size_t mlp_ln_bwd_lds_bytes(int d, int dh);
+hipError_t launch_mlp_ln_bwd(const MlpBwdArgs& a, bool bf16_io, hipStream_t s);
 // matrix-core forward pass that stores the bf16 chunk-start states (64 KB per chunk), and
 // the matrix-core backward pass reading them (d = 64, hidden 256, chunk 16, bf16)
 hipError_t launch_mlp_fwd_hist(const MlpArgs& a, void* hist, hipStream_t s);

@@ -410,6 +410,78 @@ int ttt_linear_ln_bwd(const void* q, const void* k, const void* v, const float* 
   return TTT_OK;
 }
 
+int ttt_mlp_ln_bwd(const void* q, const void* k, const void* v, const float* w1, const float* w2,
+                   long long w_batch_stride, const float* ln_weight, const float* ln_bias,
+                   float ln_eps, const void* dz, const float* dw1_out, const float* dw2_out,
+                   void* dq, void* dk, void* dv, float* dw1, float* dw2, float* dln_weight,
+                   float* dln_bias, int B, int H, int T, int d, int dh, int chunk, float eta,
+                   const float* eta_tok, float* deta_tok, int loss, int io_dtype,
+                   ttt_stream_t stream) {
+  g_last_error.clear();
+  const char* fn = "ttt_mlp_ln_bwd";
+  int rc = check_ln(fn, ln_weight, ln_bias, ln_eps);
+  if (rc != TTT_OK) return rc;
+  rc = check_common(fn, q, k, v, dz, B, H, T, d, eta, eta_tok, io_dtype);
+  if (rc != TTT_OK) return rc;
+  if (loss != TTT_LOSS_MSE && loss != TTT_LOSS_DOT)
+    return fail(TTT_E_INVALID, "%s: unknown loss %d", fn, loss);
+  if (deta_tok && !eta_tok) return fail(TTT_E_INVALID, "%s: deta_tok needs eta_tok", fn);
+  if (deta_tok && (reinterpret_cast<uintptr_t>(deta_tok) & 3) != 0)
+    return fail(TTT_E_INVALID, "%s: deta_tok must be 4-byte aligned", fn);
+  if (!w1 || !w2 || !dw1 || !dw2 || !dln_weight || !dln_bias)
+    return fail(TTT_E_INVALID, "%s: w1, w2, dw1, dw2, dln_weight and dln_bias must be non-null", fn);
+  if (T > 0 && (!dq || !dk || !dv))
+    return fail(TTT_E_INVALID, "%s: dq, dk and dv must be non-null", fn);
+  if (dh <= 0) return fail(TTT_E_INVALID, "%s: dh must be positive (got %d)", fn, dh);
+  if (chunk < 1) return fail(TTT_E_INVALID, "%s: chunk must be >= 1 (got %d)", fn, chunk);
+  if (w_batch_stride < 0) return fail(TTT_E_INVALID, "%s: negative w_batch_stride", fn);
+  if (d != 16 && d != 32 && d != 64)
+    return fail(TTT_E_UNSUPPORTED, "%s: d=%d not supported (16, 32, 64)", fn, d);
+  if (dh > 256) return fail(TTT_E_UNSUPPORTED, "%s: dh=%d not supported (<= 256)", fn, dh);
+  if (T > 0 && (chunk < T ? chunk : T) > 16)
+    return fail(TTT_E_UNSUPPORTED, "%s: chunks of more than 16 tokens not supported", fn);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t per = static_cast<size_t>(d) * dh;
+  if (T == 0) {
+    const long long st = static_cast<long long>(H) * static_cast<long long>(per);
+    rc = copy_state(dw1, dw1_out, st, B, H, per, s);
+    if (rc == TTT_OK) rc = copy_state(dw2, dw2_out, st, B, H, per, s);
+    if (rc == TTT_OK) rc = copy_state(dln_weight, nullptr, 0, B, H, static_cast<size_t>(d), s);
+    if (rc == TTT_OK) rc = copy_state(dln_bias, nullptr, 0, B, H, static_cast<size_t>(d), s);
+    return rc;
+  }
+  const int b = chunk < T ? chunk : T;
+  const long long nchunks = (T + b - 1) / b;
+  if (!fits_int64(B, H, nchunks, 2LL * static_cast<long long>(per)))
+    return fail(TTT_E_INVALID, "%s: state history overflows", fn);
+  const bool bf16 = io_dtype == TTT_BF16;
+  const int dot = loss == TTT_LOSS_DOT ? 1 : 0;
+  // forward recomputation on the generic kernel, storing the chunk-start states
+  ttt::MlpArgs f{q, k, v, w1, w2, w_batch_stride, nullptr, nullptr, nullptr,
+                 B, H, T, d, dh, chunk, 1, eta, eta_tok, dot};
+  f.ln_w = ln_weight;
+  f.ln_b = ln_bias;
+  f.ln_eps = ln_eps;
+  StreamBuffer hist, fws;
+  rc = get_workspace(static_cast<size_t>(B) * H * nchunks * 2 * per * sizeof(float), s, &hist);
+  if (rc != TTT_OK) return rc;
+  f.w_hist = static_cast<float*>(hist.ptr);
+  rc = get_workspace(ttt::mlp_generic_workspace_floats(f) * sizeof(float), s, &fws);
+  if (rc != TTT_OK) return rc;
+  hipError_t e = ttt::launch_mlp_generic(f, bf16, static_cast<float*>(fws.ptr), s);
+  if (e != hipSuccess) return hip_fail(e, "ttt_mlp_ln_bwd state launch");
+  ttt::MlpBwdArgs g{q, k, v, dz, dw1_out, dw2_out, static_cast<const float*>(hist.ptr), dq, dk, dv,
+                    dw1, dw2, B, H, T, d, dh, chunk, eta, dot, eta_tok, deta_tok};
+  g.ln_w = ln_weight;
+  g.ln_b = ln_bias;
+  g.ln_eps = ln_eps;
+  g.dln_w = dln_weight;
+  g.dln_b = dln_bias;
+  e = ttt::launch_mlp_ln_bwd(g, bf16, s);
+  if (e != hipSuccess) return hip_fail(e, "ttt_mlp_ln_bwd launch");
+  return TTT_OK;
+}
+
 // Shared by ttt_linear_nc_bwd (mlp false: w1 = w0, dw1 = dw0) and ttt_mlp_nc_bwd.
 int nc_bwd(const char* fn, bool mlp, const void* q, const void* k, const void* v, const float* w1,
            const float* w2, long long w_batch_stride, const void* dz, const float* dw1_out,

@@ -334,3 +334,11 @@ def _ln_bwd(lib, **kw):
 def test_linear_ln_bwd_rejects(lib, kw, code, msg):
     rc = _ln_bwd(lib, **kw)
     assert rc == code and msg in ttt.last_error(), (rc, ttt.last_error())
+
+
+def test_mlp_ln_bwd_rejects_oversized_hidden_and_bad_eps(lib):
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, 1e-6, FAKE, None, None, FAKE, FAKE, FAKE,
+            FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 16, 300, 16, 0.1, None, None, 0, 0, None]
+    assert lib.ttt_mlp_ln_bwd(*args) == ttt.TTT_E_UNSUPPORTED and "dh=300" in ttt.last_error()
+    args[8] = -1.0
+    assert lib.ttt_mlp_ln_bwd(*args) == ttt.TTT_E_INVALID and "ln_eps" in ttt.last_error()

@@ -949,3 +949,77 @@ def test_linear_ln_bwd_empty_sequence():
     out = ttt.ttt_linear_ln_bwd(z, z, z, w0, lw, lb, 0.1, 4, z, d0)
     torch.cuda.synchronize()
     assert torch.equal(out[3], d0) and not out[4].any() and not out[5].any()
+
+
+# ------------------------------------------------------------------ backward of the paper's TTT-MLP
+# ttt_mlp_ln_bwd (f(x) = x + LN(W2 GELU(W1 x)); wmrh.cn summary, section 2.2.1) against the
+# oracle's ttt_layer_vjp with act="gelu" and ln.
+
+def _check_mlp_ln_bwd(w, inp, with_dw, seed=0, rates=False, loss="mse", full=False, w_scale=None):
+    import torch
+    import test_sequence_layers_amd as ttt
+    from oracle import ttt_oracle as O
+    from tests.oracle_pool import run_chains
+    from tests.parity_util import LN_EPS
+    _note(f"[parity] mlp_ln_bwd B={w.B} H={w.H} T={w.T} d={w.d} h={w.h} chunk={w.chunk} "
+          f"io={w.io} dw_out={with_dw} rates={rates} loss={loss} seed={w.seed} full={full}")
+    if w_scale is not None:
+        inp["w1"] = (inp["w1"] * w_scale).astype(np.float32)
+        inp["w2"] = (inp["w2"] * w_scale).astype(np.float32)
+    rng = np.random.default_rng(60_000 + seed)
+    dz = rng.standard_normal((w.B, w.H, w.T, w.d)).astype(np.float32)
+    if w.io == "bf16":
+        dz = to_np(torch.from_numpy(dz).to(torch.bfloat16))
+    dw1 = rng.standard_normal((w.B, w.H, w.h, w.d)).astype(np.float32) if with_dw else None
+    dw2 = rng.standard_normal((w.B, w.H, w.d, w.h)).astype(np.float32) if with_dw else None
+    lw, lb = make_ln_params(w, seed)
+    et = make_token_rates(w, seed) if rates else None
+    dev = to_device(inp, w.io)
+    out = ttt.ttt_mlp_ln_bwd(
+        dev["q"], dev["k"], dev["v"], dev["w1"], dev["w2"], torch.from_numpy(lw).cuda(),
+        torch.from_numpy(lb).cuda(), w.eta, w.chunk,
+        torch.from_numpy(dz).to("cuda").to(dev["q"].dtype).contiguous(),
+        torch.from_numpy(dw1).cuda() if with_dw else None,
+        torch.from_numpy(dw2).cuda() if with_dw else None, ln_eps=LN_EPS,
+        eta_tok=torch.from_numpy(et).cuda() if rates else None, loss=loss)
+    torch.cuda.synchronize()
+    got = [to_np(t) for t in out]
+    del out, dev
+    args = ("mlp", inp["q"], inp["k"], inp["v"], (inp["w1"], inp["w2"]), w.eta, w.chunk, dz,
+            (dw1, dw2) if with_dw else None)
+    kw = dict(eta_tok=et, loss=loss, act="gelu", ln=(lw, lb, LN_EPS))
+    if full:
+        _note("[parity]   oracle over every sequence (worker processes)")
+        ref = run_chains("ttt_layer_vjp", w.B, w.H, args, kw, {4: 3, "ln": 2})
+    else:
+        ref = O.ttt_layer_vjp(*args, **kw)
+    dq, dk, dv, d1, d2, de, dg, db = ref
+    refs = [dq, dk, dv, d1, d2, dg, db] + ([de] if rates else [])
+    tol = tol_for(w.io)
+    names = ("dq", "dk", "dv", "dw1", "dw2", "dln_weight", "dln_bias", "deta_tok")
+    for name, g, r in zip(names, got, refs):
+        if name in ("deta_tok", "dln_weight", "dln_bias"):  # one row per sequence
+            g, r = g[..., None, :], r[..., None, :]
+        check_close(name, g, r, tol, _note)
+
+
+@pytest.mark.parametrize("d,h,chunk,with_dw,rates,loss", [
+    (16, 32, 4, True, True, "mse"), (32, 64, 16, False, False, "dot"), (16, 24, 5, True, False, "mse"),
+    (16, 32, 1, False, True, "mse")])
+def test_mlp_ln_bwd_fp32(d, h, chunk, with_dw, rates, loss):
+    w = workload(3).replace(B=2, H=2, T=37, d=d, h=h, chunk=chunk, io="f32", eta=0.1,
+                            seed=700 + h + chunk)
+    _check_mlp_ln_bwd(w, make_inputs(w), with_dw, seed=h, rates=rates, loss=loss,
+                      w_scale=10.0 if chunk == 1 else None)
+
+
+@pytest.mark.parametrize("T,with_dw,rates,loss", [(16, True, False, "mse"), (70, False, True, "mse"),
+                                                  (45, True, False, "dot")])
+def test_mlp_ln_bwd_bf16_h256(T, with_dw, rates, loss):
+    w = workload(3).replace(B=1, H=2, T=T, seed=710 + T)
+    _check_mlp_ln_bwd(w, make_inputs(w), with_dw, seed=T, rates=rates, loss=loss)
+
+
+def test_mlp_ln_bwd_config_full_size():
+    w = workload(3)
+    _check_mlp_ln_bwd(w, make_inputs(w), False, seed=2, full=True)
