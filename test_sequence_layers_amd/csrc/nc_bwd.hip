@@ -77,9 +77,28 @@ __host__ __device__ inline size_t ws_floats(int d, int h, int T, int steps) {
   return (steps + 1) * state_floats<kMlp>(d, h) + 2 * static_cast<size_t>(T) * d + T;
 }
 __host__ __device__ inline int tile_tokens(int h) { return h <= 128 ? 16 : 8; }
+// LDS floats of the token and hidden tiles, and of the padded copies of the step's state and
+// of P (rows padded by one float against bank conflicts)
+__host__ __device__ inline size_t tile_lds_floats(int d, int h) {
+  const int tb = tile_tokens(h);
+  return static_cast<size_t>(tb) * (7 * d + 1) + static_cast<size_t>(tb) * h * 10;
+}
+__host__ __device__ inline size_t mat_lds_floats(bool mlp, int d, int h) {
+  return mlp ? 2 * (static_cast<size_t>(h) * (d + 1) + static_cast<size_t>(d) * (h + 1))
+             : 2 * static_cast<size_t>(d) * (d + 1);
+}
 
-// kOwn: state entries per thread per matrix (4 for states of up to 4096 entries, else 16)
-template <typename IO, int D, bool kMlp, int kOwn>
+// A row-major matrix in global memory or a padded copy in LDS.
+struct Mat {
+  const float* p;
+  int ld;
+  __device__ __forceinline__ float operator()(int r, int c) const { return p[r * ld + c]; }
+};
+
+// kOwn: state entries per thread per matrix (4 for states of up to 4096 entries, else 16);
+// kLds: the step's state and P are read from padded LDS copies (when they fit), else from
+// global memory through the caches
+template <typename IO, int D, bool kMlp, int kOwn, bool kLds>
 __global__ __launch_bounds__(kThreads) void nc_bwd_kernel(NcBwdArgs a) {
   extern __shared__ float lds[];
   const int h = kMlp ? a.h : 0;
@@ -104,6 +123,14 @@ __global__ __launch_bounds__(kThreads) void nc_bwd_kernel(NcBwdArgs a) {
   float* Hdda = Hddu + TB * h;  // dda0
   float* Hds = Hdda + TB * h;   // ds
   float* Hdu = Hds + TB * h;    // du
+  // padded copies: state 1 [rows1][D + 1] (W1 [h][D] or W [D][D]), state 2 [D][h + 1] (MLP),
+  // then P1, P2 likewise
+  const int rows1 = kMlp ? h : D;
+  float* Ml = Hdu + TB * h;
+  float* Wl1 = Ml;
+  float* Wl2 = Wl1 + rows1 * (D + 1);
+  float* Pl1 = Wl2 + (kMlp ? D * (h + 1) : 0);
+  float* Pl2 = Pl1 + rows1 * (D + 1);
 
   const int tid = threadIdx.x;
   const int chain = blockIdx.x;
@@ -149,17 +176,30 @@ __global__ __launch_bounds__(kThreads) void nc_bwd_kernel(NcBwdArgs a) {
   auto load_rates = [&](int t0, int n) {
     for (int t = tid; t < TB; t += kThreads) Es[t] = t < n ? (etok ? etok[t0 + t] : 1.0f) : 0.0f;
   };
+  // the state at `src` (state 1 then state 2) as Mats, copied into LDS with kLds; ends
+  // synchronised when it copies
+  auto state_mats = [&](const float* src, float* l1, float* l2, Mat& m1, Mat& m2) {
+    if (kLds) {
+      for (size_t e = tid; e < n1; e += kThreads) l1[(e / D) * (D + 1) + e % D] = src[e];
+      if (kMlp)
+        for (size_t e = tid; e < n2; e += kThreads) l2[(e / h) * (h + 1) + e % h] = src[n1 + e];
+      __syncthreads();
+      m1 = Mat{l1, D + 1};
+      m2 = Mat{l2, h + 1};
+    } else {
+      m1 = Mat{src, D};
+      m2 = Mat{src + n1, h};
+    }
+  };
 
   // Shared per-tile forward of a training step from state W (W1 = W, W2 = W + n1):
   // Hu, Ha, Hs; Rr, Rt; Hda0, Hdu0 (MLP).  Ends synchronised.
-  auto tile_forward = [&](const float* W) {
-    const float* W1 = W;
-    const float* W2 = W + n1;
+  auto tile_forward = [&](const Mat& W1, const Mat& W2) {
     if (kMlp) {
       for (int e = tid; e < TB * h; e += kThreads) {
         const int t = e / h, j = e % h;
         float u = 0.0f;
-        for (int i = 0; i < D; ++i) u += W1[static_cast<size_t>(j) * D + i] * Ks[t * D + i];
+        for (int i = 0; i < D; ++i) u += W1(j, i) * Ks[t * D + i];
         Hu[e] = u;
         Ha[e] = silu_(u);
         Hs[e] = dsilu_(u);
@@ -171,9 +211,9 @@ __global__ __launch_bounds__(kThreads) void nc_bwd_kernel(NcBwdArgs a) {
       float o = 0.0f;
       if (!a.dot_loss) {
         if (kMlp)
-          for (int j = 0; j < h; ++j) o += W2[static_cast<size_t>(i) * h + j] * Ha[t * h + j];
+          for (int j = 0; j < h; ++j) o += W2(i, j) * Ha[t * h + j];
         else
-          for (int j = 0; j < D; ++j) o += W1[static_cast<size_t>(i) * D + j] * Ks[t * D + j];
+          for (int j = 0; j < D; ++j) o += W1(i, j) * Ks[t * D + j];
       }
       const float r = o - Vs[e];
       Rr[e] = r;
@@ -184,7 +224,7 @@ __global__ __launch_bounds__(kThreads) void nc_bwd_kernel(NcBwdArgs a) {
       for (int e = tid; e < TB * h; e += kThreads) {
         const int t = e / h, j = e % h;
         float da0 = 0.0f;
-        for (int i = 0; i < D; ++i) da0 += W2[static_cast<size_t>(i) * h + j] * Rt[t * D + i];
+        for (int i = 0; i < D; ++i) da0 += W2(i, j) * Rt[t * D + i];
         Hda0[e] = da0;
         Hdu0[e] = da0 * Hs[e];
       }
@@ -198,6 +238,8 @@ __global__ __launch_bounds__(kThreads) void nc_bwd_kernel(NcBwdArgs a) {
   for (int s = 0; s < S; ++s) {
     const int m0 = (s % nmb) * mb, ns = min(mb, T - m0);
     const float* W = hist + static_cast<size_t>(s) * sf;
+    Mat Wm1, Wm2;
+    state_mats(W, Wl1, Wl2, Wm1, Wm2);
 #pragma unroll
     for (int m = 0; m < kOwn; ++m) acc1[m] = acc2[m] = 0.0f;
     for (int t0 = 0; t0 < ns; t0 += TB) {
@@ -206,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void nc_bwd_kernel(NcBwdArgs a) {
       load_rows(Vs, v, m0 + t0, n);
       load_rates(m0 + t0, n);
       __syncthreads();
-      tile_forward(W);
+      tile_forward(Wm1, Wm2);
       // G1 += du0 k^T (MLP) or G += rt k^T (linear); G2 += rt a^T
 #pragma unroll
       for (int m = 0; m < kOwn; ++m) {
@@ -238,8 +280,8 @@ __global__ __launch_bounds__(kThreads) void nc_bwd_kernel(NcBwdArgs a) {
 
   // ---- queries: dq and P = dL/dW_S ----
   {
-    const float* W1 = hist + static_cast<size_t>(S) * sf;
-    const float* W2 = W1 + n1;
+    Mat W1, W2;
+    state_mats(hist + static_cast<size_t>(S) * sf, Wl1, Wl2, W1, W2);
 #pragma unroll
     for (int m = 0; m < kOwn; ++m) {
       const size_t e = tid + static_cast<size_t>(m) * kThreads;
@@ -257,8 +299,8 @@ __global__ __launch_bounds__(kThreads) void nc_bwd_kernel(NcBwdArgs a) {
           const int t = e / h, j = e % h;
           float u = 0.0f, da = 0.0f;
           for (int i = 0; i < D; ++i) {
-            u += W1[static_cast<size_t>(j) * D + i] * Xs[t * D + i];
-            da += W2[static_cast<size_t>(i) * h + j] * Vs[t * D + i];
+            u += W1(j, i) * Xs[t * D + i];
+            da += W2(i, j) * Vs[t * D + i];
           }
           Ha[e] = silu_(u);
           Hdu[e] = da * dsilu_(u);
@@ -270,9 +312,9 @@ __global__ __launch_bounds__(kThreads) void nc_bwd_kernel(NcBwdArgs a) {
         if (t >= n) continue;
         float x = 0.0f;
         if (kMlp)
-          for (int r = 0; r < h; ++r) x += W1[static_cast<size_t>(r) * D + j] * Hdu[t * h + r];
+          for (int r = 0; r < h; ++r) x += W1(r, j) * Hdu[t * h + r];
         else
-          for (int i = 0; i < D; ++i) x += W1[static_cast<size_t>(i) * D + j] * Vs[t * D + i];
+          for (int i = 0; i < D; ++i) x += W1(i, j) * Vs[t * D + i];
         dq[static_cast<size_t>(t0 + t) * D + j] = from_f32<IO>(x);
       }
 #pragma unroll
@@ -305,9 +347,19 @@ __global__ __launch_bounds__(kThreads) void nc_bwd_kernel(NcBwdArgs a) {
   // ---- steps in reverse ----
   for (int s = S - 1; s >= 0; --s) {
     const int m0 = (s % nmb) * mb, ns = min(mb, T - m0);
-    const float* W = hist + static_cast<size_t>(s) * sf;
-    const float* W1 = W;
-    const float* W2 = W + n1;
+    Mat W1, W2, Pm1, Pm2;
+    state_mats(hist + static_cast<size_t>(s) * sf, Wl1, Wl2, W1, W2);
+    if (kLds) {
+      for (size_t e = tid; e < n1; e += kThreads) Pl1[(e / D) * (D + 1) + e % D] = P1[e];
+      if (kMlp)
+        for (size_t e = tid; e < n2; e += kThreads) Pl2[(e / h) * (h + 1) + e % h] = P2[e];
+      __syncthreads();
+      Pm1 = Mat{Pl1, D + 1};
+      Pm2 = Mat{Pl2, h + 1};
+    } else {
+      Pm1 = Mat{P1, D};
+      Pm2 = Mat{P2, h};
+    }
 #pragma unroll
     for (int m = 0; m < kOwn; ++m) acc1[m] = acc2[m] = 0.0f;
     for (int t0 = 0; t0 < ns; t0 += TB) {
@@ -316,15 +368,15 @@ __global__ __launch_bounds__(kThreads) void nc_bwd_kernel(NcBwdArgs a) {
       load_rows(Vs, v, m0 + t0, n);
       load_rates(m0 + t0, n);
       __syncthreads();
-      tile_forward(W);
+      tile_forward(W1, W2);
       if (kMlp) {
         // da = c P2^T rt,  ddu0 = c P1 k,  dda0 = ddu0 s,  ds = ddu0 da0
         for (int e = tid; e < TB * h; e += kThreads) {
           const int t = e / h, j = e % h;
           float da = 0.0f, ddu = 0.0f;
           for (int i = 0; i < D; ++i) {
-            da += P2[static_cast<size_t>(i) * h + j] * Rt[t * D + i];
-            ddu += P1[static_cast<size_t>(j) * D + i] * Ks[t * D + i];
+            da += Pm2(i, j) * Rt[t * D + i];
+            ddu += Pm1(j, i) * Ks[t * D + i];
           }
           Hda[e] = c * da;
           Hddu[e] = c * ddu;
@@ -337,9 +389,9 @@ __global__ __launch_bounds__(kThreads) void nc_bwd_kernel(NcBwdArgs a) {
           const int t = e / D, i = e % D;
           float x = 0.0f, y = 0.0f, z = 0.0f;
           for (int j = 0; j < h; ++j) {
-            x += P2[static_cast<size_t>(i) * h + j] * Ha[t * h + j];
-            y += W2[static_cast<size_t>(i) * h + j] * Hdda[t * h + j];
-            z += P1[static_cast<size_t>(j) * D + i] * Hdu0[t * h + j];
+            x += Pm2(i, j) * Ha[t * h + j];
+            y += W2(i, j) * Hdda[t * h + j];
+            z += Pm1(j, i) * Hdu0[t * h + j];
           }
           Dr[e] = c * x + y;
           Dk[e] = c * z;
@@ -350,8 +402,8 @@ __global__ __launch_bounds__(kThreads) void nc_bwd_kernel(NcBwdArgs a) {
           const int t = e / D, i = e % D;
           float x = 0.0f, z = 0.0f;
           for (int j = 0; j < D; ++j) {
-            x += P1[static_cast<size_t>(i) * D + j] * Ks[t * D + j];
-            z += P1[static_cast<size_t>(j) * D + i] * Rt[t * D + j];
+            x += Pm1(i, j) * Ks[t * D + j];
+            z += Pm1(j, i) * Rt[t * D + j];
           }
           Dr[e] = c * x;
           Dk[e] = c * z;
@@ -373,7 +425,7 @@ __global__ __launch_bounds__(kThreads) void nc_bwd_kernel(NcBwdArgs a) {
           const int t = e / h, j = e % h;
           float x = Hda[e];
           if (!a.dot_loss)
-            for (int i = 0; i < D; ++i) x += W2[static_cast<size_t>(i) * h + j] * Dr[t * D + i];
+            for (int i = 0; i < D; ++i) x += W2(i, j) * Dr[t * D + i];
           Hdu[e] = x * Hs[e] + Hds[e] * d2silu(Hu[e]);
         }
         __syncthreads();
@@ -384,9 +436,9 @@ __global__ __launch_bounds__(kThreads) void nc_bwd_kernel(NcBwdArgs a) {
         if (t >= n) continue;
         float x = Dk[e];
         if (kMlp)
-          for (int r = 0; r < h; ++r) x += W1[static_cast<size_t>(r) * D + j] * Hdu[t * h + r];
+          for (int r = 0; r < h; ++r) x += W1(r, j) * Hdu[t * h + r];
         else if (!a.dot_loss)
-          for (int i = 0; i < D; ++i) x += W1[static_cast<size_t>(i) * D + j] * Dr[t * D + i];
+          for (int i = 0; i < D; ++i) x += W1(i, j) * Dr[t * D + i];
         const size_t o = static_cast<size_t>(m0 + t0 + t) * D + j;
         dkacc[o] += x;
         dvacc[o] -= Dr[e];
@@ -433,16 +485,23 @@ __global__ __launch_bounds__(kThreads) void nc_bwd_kernel(NcBwdArgs a) {
     for (int t = tid; t < T; t += kThreads) a.deta_tok[static_cast<size_t>(chain) * T + t] = deacc[t];
 }
 
+template <typename IO, int D, bool kMlp, int kOwn, bool kLds>
+hipError_t launch_lds(const NcBwdArgs& a, hipStream_t s) {
+  const int h = kMlp ? a.h : 0;
+  const size_t lds = (tile_lds_floats(D, h) + (kLds ? mat_lds_floats(kMlp, D, h) : 0)) * sizeof(float);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nc_bwd_kernel<IO, D, kMlp, kOwn, kLds>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((nc_bwd_kernel<IO, D, kMlp, kOwn, kLds>), dim3(a.B * a.H), dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
 template <typename IO, int D, bool kMlp, int kOwn>
 hipError_t launch_own(const NcBwdArgs& a, hipStream_t s) {
   const int h = kMlp ? a.h : 0;
-  const int tb = tile_tokens(h);
-  const size_t lds = (static_cast<size_t>(tb) * (7 * D + 1) + static_cast<size_t>(tb) * h * 10) * sizeof(float);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nc_bwd_kernel<IO, D, kMlp, kOwn>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((nc_bwd_kernel<IO, D, kMlp, kOwn>), dim3(a.B * a.H), dim3(kThreads), lds, s, a);
-  return hipGetLastError();
+  if ((tile_lds_floats(D, h) + mat_lds_floats(kMlp, D, h)) * sizeof(float) <= 160 * 1024)
+    return launch_lds<IO, D, kMlp, kOwn, true>(a, s);
+  return launch_lds<IO, D, kMlp, kOwn, false>(a, s);
 }
 
 template <typename IO, int D, bool kMlp>
