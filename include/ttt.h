@@ -161,8 +161,10 @@ int delta_rule_fwd(const void* q, const void* k, const void* v,
  * dtypes.  The call recomputes the forward pass and keeps its chunk-start states in a
  * stream-ordered workspace: bf16 on the matrix cores (d = 64, chunk 16, bf16, with q, k, v,
  * dz, dq, dk, dv, dw0, dw_out and w0 16-byte aligned and w0_batch_stride a multiple of 4;
- * B*H*ceil(T/16)*8 KB), else float32 (B*H*ceil(T/chunk)*d*d*4 bytes).  T = 0 copies dw_out
- * to dw0 (zeros without it).
+ * B*H*ceil(T/16)*8 KB), else float32 (B*H*ceil(T/chunk)*d*d*4 bytes).  chunk = 1 (the delta
+ * rule) runs the exact chunked form 16 tokens at a time on the vector ALUs, with float32
+ * states every 16 tokens (B*H*ceil(T/16)*d*d*4 bytes).  T = 0 copies dw_out to dw0 (zeros
+ * without it).
  */
 int ttt_linear_bwd(const void* q, const void* k, const void* v,
                    const float* w0, long long w0_batch_stride,

@@ -189,6 +189,11 @@ bool mlp_nc_supported(const MlpArgs& a, bool bf16_io);
 hipError_t launch_mlp_nc(const MlpArgs& a, hipStream_t s);
 
 hipError_t launch_linear_bwd_generic(const LinearBwdArgs& a, bool bf16_io, hipStream_t s);
+// backward of the delta rule (chunk 1), in the exact form 16 tokens at a time (vector ALUs;
+// the kernel recomputes its own chunk-start states into the workspace)
+size_t delta_bwd_workspace_bytes(const LinearBwdArgs& a);
+hipError_t launch_delta_bwd(const LinearBwdArgs& a, const float* w0, long long w0_batch_stride, void* ws,
+                            bool bf16_io, hipStream_t s);
 // backward of the paper's TTT-Linear x + LN(W x) (vector ALUs; reads the chunk-start states
 // in a.w_hist)
 hipError_t launch_linear_ln_bwd(const LinearBwdArgs& a, bool bf16_io, hipStream_t s);

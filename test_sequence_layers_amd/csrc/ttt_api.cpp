@@ -255,10 +255,32 @@ int linear_bwd(const char* fn, const void* q, const void* k, const void* v, cons
                     eta_tok, dot, nullptr};
   ttt::LinearBwdArgs g{q, k, v, dz, dw_out, nullptr, dq, dk, dv, dw0,
                        B, H, T, d, chunk, eta, eta_tok, deta_tok, dot};
+  const int b = chunk < T ? chunk : T;
+  if (b == 1) {
+    // the delta rule: its exact chunked form, 16 tokens per step, with float32 chunk-start
+    // states every 16 tokens
+    const size_t dneed = ttt::delta_bwd_workspace_bytes(g);
+    StreamBuffer downed;
+    void* dws = nullptr;
+    if (noalloc) {
+      if (dneed > kScratchBytes)
+        return fail(TTT_E_UNSUPPORTED,
+                    "%s: the state history needs %zu bytes, more than the %zu-byte scratch array",
+                    fn, dneed, kScratchBytes);
+      rc = scratch_ptr(fn, &dws);
+      if (rc != TTT_OK) return rc;
+    } else {
+      rc = get_workspace(dneed, s, &downed);
+      if (rc != TTT_OK) return rc;
+      dws = downed.ptr;
+    }
+    hipError_t e = ttt::launch_delta_bwd(g, w0, w0_batch_stride, dws, bf16, s);
+    if (e != hipSuccess) return hip_fail(e, "delta-rule backward launch");
+    return TTT_OK;
+  }
   // chunk-start states of the forward pass: bf16 on the matrix-core path (8 KB per chunk),
   // float32 on the vector-ALU path
   const bool mfma = ttt::linear_bwd_mfma_supported(f, g, bf16);
-  const int b = chunk < T ? chunk : T;
   const long long nchunks = (T + b - 1) / b;
   if (!fits_int64(B, H, nchunks, static_cast<long long>(dd) * 4))
     return fail(TTT_E_INVALID, "%s: state history overflows", fn);

@@ -1023,3 +1023,26 @@ def test_mlp_ln_bwd_bf16_h256(T, with_dw, rates, loss):
 def test_mlp_ln_bwd_config_full_size():
     w = workload(3)
     _check_mlp_ln_bwd(w, make_inputs(w), False, seed=2, full=True)
+
+
+# ------------------------------------------------------------------ backward of the delta rule
+# ttt_linear_bwd with chunk 1 runs the exact chunked form 16 tokens at a time; the oracle's
+# ttt_linear_vjp walks the tokens one by one.
+
+@pytest.mark.parametrize("d,T,with_dw,rates,loss", [
+    (16, 37, True, False, "mse"), (32, 50, False, True, "mse"), (64, 33, True, True, "mse"),
+    (16, 21, True, False, "dot"), (64, 1, True, True, "mse")])
+def test_delta_bwd_fp32(d, T, with_dw, rates, loss):
+    w = workload(2).replace(B=2, H=3, T=T, d=d, io="f32", eta=0.3, seed=800 + d + T)
+    _check_bwd(w, make_inputs(w), with_dw, seed=d, rates=rates, loss=loss)
+
+
+@pytest.mark.parametrize("T,rates", [(200, False), (333, True)])
+def test_delta_bwd_bf16_d64(T, rates):
+    w = workload(2).replace(B=2, H=3, T=T, seed=810 + T)
+    _check_bwd(w, make_inputs(w), True, seed=T, rates=rates)
+
+
+def test_delta_bwd_config_full_size():
+    w = workload(2)
+    _check_bwd(w, make_inputs(w), False, seed=2, full=True)
