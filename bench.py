@@ -161,8 +161,8 @@ def time_workload(w, steps, warmup, torch, ttt, rotate=None, rates=False, loss="
 
 
 def time_backward(w, steps, warmup, torch, ttt, rates=False):
-    """Event-timed ttt_linear_bwd / ttt_mlp_bwd calls (ttt_linear_nc_bwd / ttt_mlp_nc_bwd for
-    the non-causal workloads) on the workload (inputs resident in
+    """Event-timed ttt_linear_bwd / ttt_mlp_bwd calls (ttt_linear_bwd with chunk 1 for the
+    delta rule, ttt_linear_nc_bwd / ttt_mlp_nc_bwd for the non-causal workloads) on the workload (inputs resident in
     HBM; seeded dZ ~ N(0, 1), no upstream state gradient; rates: TTT-Linear with per-token
     rate factors, their gradient included)."""
     dev = make_device_inputs(w, w.seed, torch, rates=rates)
@@ -175,7 +175,7 @@ def time_backward(w, steps, warmup, torch, ttt, rates=False):
         else:
             call = lambda: ttt.ttt_mlp_nc_bwd(dev["q"], dev["k"], dev["v"], dev["w1"], dev["w2"], w.eta,
                                               w.chunk, dz, eta_tok=dev.get("eta_tok"))
-    elif w.kind == "linear":
+    elif w.kind in ("linear", "delta"):  # the delta rule is TTT-Linear with chunk 1
         call = lambda: ttt.ttt_linear_bwd(dev["q"], dev["k"], dev["v"], dev["w0"], w.eta, w.chunk, dz,
                                           eta_tok=dev.get("eta_tok"))
     else:
@@ -426,13 +426,15 @@ def main():
         # and the causal MLP workloads
         variants += [(o, "+paper_ln", dict(paper=True)) for o in WORKLOADS
                      if o.name in ("linear_d64_T2048", "mlp_h256_T2048")]
-        # backward passes of the headline linear workload and of the causal MLP workload
-        # (dz ~ N(0, 1), no upstream state gradient)
+        # backward passes of the headline linear workload, the delta rule, the causal MLP
+        # workload and the vision workload (dz ~ N(0, 1), no upstream state gradient)
         bwd = [w] if w.kind == "linear" else []
-        bwd += [o for o in WORKLOADS if o.name in ("mlp_h256_T2048", "mlp_vision_N196")]
+        bwd += [o for o in WORKLOADS
+                if o.name in ("delta_d64_T8192", "mlp_h256_T2048", "mlp_vision_N196")]
         for o in bwd:
-            r = time_backward(o, max(10, args.steps // 2) if o.kind == "linear" else 3,
-                              3 if o.kind == "linear" else 1, torch, ttt)
+            quick = o.kind == "linear" and o.chunk > 1
+            r = time_backward(o, max(10, args.steps // 2) if quick else 3, 3 if quick else 1,
+                              torch, ttt)
             others[o.name + "+backward"] = {
                 "tokens_per_s": round(r["tokens_per_s"], 1),
                 "ms_per_step": round(r["ms_per_step"], 5),
