@@ -141,6 +141,20 @@ def test_mlp_vision_small():
     _check("mlp", w, make_inputs(w))
 
 
+# One full-batch step at the vision shape runs the kernel that splits the hidden units over two
+# waves and the tiles over two token groups: one token, a partial tile, one and two whole tiles,
+# odd and even tile counts (the second token group's last round is then empty), both losses,
+# rates, and an odd chain count.
+@pytest.mark.parametrize("T,B,H,loss,rates", [
+    (1, 1, 3, "mse", False), (5, 2, 1, "mse", True), (16, 1, 2, "mse", False),
+    (17, 1, 3, "dot", False), (33, 3, 1, "mse", True), (48, 1, 1, "dot", True),
+    (100, 1, 3, "mse", False)])
+def test_mlp_vision_single_step_shapes(T, B, H, loss, rates):
+    w = workload(4).replace(B=B, H=H, T=T, chunk=T, eta=0.5, seed=60 + T)
+    inp = _with_rates(w, 13) if rates else make_inputs(w)
+    _check("mlp", w, inp, loss=loss)
+
+
 def test_mlp_config_full_size():
     w = workload(3)
     _check("mlp", w, make_inputs(w), full=True)
