@@ -162,9 +162,9 @@ int delta_rule_fwd(const void* q, const void* k, const void* v,
  * stream-ordered workspace: bf16 on the matrix cores (d = 64, chunk 16, bf16, with q, k, v,
  * dz, dq, dk, dv, dw0, dw_out and w0 16-byte aligned and w0_batch_stride a multiple of 4;
  * B*H*ceil(T/16)*8 KB), else float32 (B*H*ceil(T/chunk)*d*d*4 bytes).  chunk = 1 (the delta
- * rule) runs the exact chunked form 16 tokens at a time on the vector ALUs, with float32
- * states every 16 tokens (B*H*ceil(T/16)*d*d*4 bytes).  T = 0 copies dw_out to dw0 (zeros
- * without it).
+ * rule) runs the exact chunked form 16 tokens at a time on the matrix cores in fp32, keeping
+ * per 16 tokens the float32 state and the chunk's two 16 x 16 matrices (B*H*ceil(T/16)*
+ * (d*d + 512)*4 bytes).  T = 0 copies dw_out to dw0 (zeros without it).
  */
 int ttt_linear_bwd(const void* q, const void* k, const void* v,
                    const float* w0, long long w0_batch_stride,
@@ -181,7 +181,8 @@ int ttt_linear_bwd(const void* q, const void* k, const void* v,
  * fixed scratch array of the library (64 MiB, one per GPU, held until the process ends)
  * instead of a stream-ordered workspace, and the call allocates nothing.  A call whose
  * history would exceed it (matrix-core path: B*H*ceil(T/16)*8 KB; vector-ALU path:
- * B*H*ceil(T/chunk)*d*d*4 bytes) returns TTT_E_UNSUPPORTED.  Every call on one GPU shares the
+ * B*H*ceil(T/chunk)*d*d*4 bytes; chunk 1: B*H*ceil(T/16)*(d*d + 512)*4 bytes) returns
+ * TTT_E_UNSUPPORTED.  Every call on one GPU shares the
  * array: calls that overlap on one GPU (on different streams) race and must be ordered by the
  * caller.
  */

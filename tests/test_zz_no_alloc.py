@@ -61,6 +61,13 @@ def test_no_alloc_vector_alu_path_two_calls():
     _case(w.replace(B=1, H=2, T=21, seed=612), 613, rates=True, with_dw=False)
 
 
+def test_no_alloc_delta_rule_two_calls():
+    # chunk 1: the chunked delta-rule backward keeps its states and 16 x 16 matrices there
+    w = workload(2).replace(B=2, H=3, T=90, d=32, io="f32", eta=0.3, seed=620)
+    _case(w, 621, rates=True, with_dw=True)
+    _case(w.replace(B=1, H=2, T=37, io="bf16", d=64, seed=622), 623, rates=False, with_dw=False)
+
+
 def test_no_alloc_rejects_a_history_beyond_the_scratch_array():
     import torch
     import test_sequence_layers_amd as ttt
