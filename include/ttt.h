@@ -43,7 +43,10 @@
  *     pass would let a causal output see later tokens.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream).  Calls are
  *     asynchronous, never synchronise, keep no pointer after returning and are thread-safe;
- *     any workspace a call needs is allocated and released in stream order on `stream`.
+ *     any workspace a call needs is allocated and released in stream order on `stream`,
+ *     from a memory pool of the library's own per device that keeps the blocks it has
+ *     handed out (so repeated calls map no new pages); that memory, at most the largest
+ *     workspace in use at once, stays with the process until it ends.
  *   - Arguments are validated on the host before any HIP call.  Return values:
  *       TTT_OK             work enqueued;
  *       TTT_E_INVALID      a null required pointer, a non-positive size, chunk < 1, a
@@ -91,7 +94,8 @@ int ttt_linear_fwd(const void* q, const void* k, const void* v,
  *   w1_out [B][H][dh][d], w2_out [B][H][d][dh] float32 (out) or NULL.
  * Supported: d in {16, 32, 64}, 1 <= dh <= 512, any chunk, both dtypes, causal 0/1.
  * Some shapes use a device workspace that the call allocates and frees in stream order on
- * `stream` (hipMallocAsync / hipFreeAsync; TTT_E_HIP if the allocation fails).
+ * `stream` (hipMallocFromPoolAsync on the library's pool / hipFreeAsync; TTT_E_HIP if the
+ * allocation fails).
  */
 int ttt_mlp_fwd(const void* q, const void* k, const void* v,
                 const float* w1, const float* w2, long long w_batch_stride,

@@ -38,6 +38,8 @@
 //     consecutive features of one token.
 //   * The update of G^T puts both of its token sums into one K = 32 product: slots 0..3 hold
 //     the dZ^T Q term's tokens, slots 4..7 the dR^T K term's.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace ttt {
@@ -124,10 +126,12 @@ __device__ __forceinline__ void lds_barrier() {
   __asm__ __volatile__("" ::: "memory");
 }
 
-// Loader protocol shared by both kernels: step k reads slot k % R; barrier k publishes the
-// chunk of step k and frees the slot of step k - 1, which the loader then refills with the
-// chunk of step k - 1 + R.  Before barrier k the loads of step k are complete once at most
-// R - 2 later steps (R - 1 before barrier 0) of kLoads loads each are outstanding.
+// Loader protocols.  Every loader wave issues kLoads loads per step, whatever the step (a step
+// past the data loads zeros), so the vector-memory counter bounds the loads still in flight.
+// Lag 1: step k reads slot k % R; barrier k publishes the chunk of step k and frees the slot
+// of step k - 1, which the loader then refills with the chunk of step k - 1 + R.  Before
+// barrier k the loads of step k are complete once at most R - 2 later steps (R - 1 before
+// barrier 0) are outstanding.
 template <int R, int kLoads, typename Issue>
 __device__ __forceinline__ void loader_loop(int nsteps, Issue&& issue) {
   static_assert((R - 1) * kLoads < 64, "vmcnt is 6 bits");
@@ -142,6 +146,26 @@ __device__ __forceinline__ void loader_loop(int nsteps, Issue&& issue) {
   }
   wait_vmcnt<0>();  // no load into LDS outlives the wave
 }
+// Lag 2 (a slot is read during two steps): nsteps + 1 barriers; barrier k publishes step k
+// and frees the slot of step k - 2, refilled with step k - 2 + R.  Before barrier k, steps
+// 0 .. R - 1 + max(0, k - 2) have been issued, so step k is complete once at most R - 1,
+// R - 2, then R - 3 later steps are outstanding.
+template <int R, int kLoads, typename Issue>
+__device__ __forceinline__ void loader_loop_lag2(int nsteps, Issue&& issue) {
+  static_assert(R >= 3 && (R - 1) * kLoads < 64, "ring depth / vmcnt");
+  for (int k = 0; k < R; ++k) issue(k);
+  for (int k = 0; k <= nsteps; ++k) {
+    if (k == 0)
+      wait_vmcnt<(R - 1) * kLoads>();
+    else if (k == 1)
+      wait_vmcnt<(R - 2) * kLoads>();
+    else
+      wait_vmcnt<(R - 3) * kLoads>();
+    lds_barrier();
+    if (k >= 2 && k < nsteps) issue(k - 2 + R);
+  }
+  wait_vmcnt<0>();
+}
 
 // the lane's 1024-byte share of a tile of 8 rows: row 8 h + l / 8, physical piece l % 8 holds
 // logical piece (l % 8) ^ (row % 8)
@@ -149,16 +173,76 @@ __device__ __forceinline__ int src_off(int h, int lane) {
   const int r = 8 * h + (lane >> 3);
   return r * kRowBytes + 16 * ((lane & 7) ^ (r & 7));
 }
+__device__ __forceinline__ void load_lds(__amdgpu_buffer_rsrc_t r, lds_char* dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+}
+// 16 rate factors (4 bytes a lane; lanes past the range, and past T, read zero)
+__device__ __forceinline__ void load_lds_e(const float* etok, int c, int T, lds_char* dst, int lane) {
+  const bool live = c >= 0 && c * kB < T;
+  const int cnt = live ? (T - c * kB < kB ? T - c * kB : kB) : 0;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(etok + (live ? c * kB : 0), 4 * cnt), dst, 4, 4 * lane, 0, 0, 0);
+}
+// the byte range of token tile c of a [T][64] bf16 sequence (empty outside 0 .. nchunks - 1)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* seq, int c, int nchunks, int seq_bytes) {
+  const bool live = c >= 0 && c < nchunks;
+  const int off = live ? c * kTileBytes : 0;
+  return rsrc(seq + off, live ? seq_bytes - off : 0);
+}
+
+// Both kernels run four compute waves per chain: wave w owns the state rows (outputs)
+// i = 16 w .. 16 w + 15.  The recursions W_{c+1} = W_c - eta Rt^T K and
+// G_c = G_{c+1} + dZ^T Q + dR^T K act on each row of the state separately (R[:, i] needs
+// only row i of W; dR[:, i] only row i of G), so the waves never exchange state.
 
 // ---------------------------------------------------------------- forward recompute
-constexpr int kRingF = 8;
-constexpr int kSlotFK = 0, kSlotFV = kTileBytes, kSlotFBytes = 2 * kTileBytes;
+// Each compute wave reads a step's operands from LDS one step ahead (into registers), so its
+// recursion (state -> R -> update -> state) never waits on an LDS read.  Loader protocol for
+// that: nsteps + 1 barriers; barrier k publishes steps 0 .. k + 1; the slot of step s is read
+// before barrier max(s, 1), and after barrier k >= 1 the loader refills the slot of step
+// k - 1 with step k - 1 + R.  Before barrier 0, steps 0 .. R - 1 have been issued, so steps
+// 0 and 1 are complete once at most R - 2 later steps are outstanding; before barrier k >= 1,
+// steps 0 .. R + k - 2, so steps up to k + 1 are complete once at most R - 3 are.
+template <int R, int kLoads, typename Issue>
+__device__ __forceinline__ void loader_loop_ahead1(int nsteps, Issue&& issue) {
+  static_assert(R >= 4 && (R - 2) * kLoads < 64, "ring depth / vmcnt");
+  for (int k = 0; k < R; ++k) issue(k);
+  for (int k = 0; k <= nsteps; ++k) {
+    if (k == 0)
+      wait_vmcnt<(R - 2) * kLoads>();
+    else
+      wait_vmcnt<(R - 3) * kLoads>();
+    lds_barrier();
+    if (k >= 1) issue(k - 1 + R);
+  }
+  wait_vmcnt<0>();  // no load into LDS outlives the wave
+}
+
+template <int N>
+using IC = std::integral_constant<int, N>;
+constexpr int kWavesC = 4;
+// The history pass is bound by its stores (8 KB of W_c per chunk and chain; one compute unit
+// writes about 30 GB/s whatever the number of waves storing), so a chain's rows are split
+// over kSplitF workgroups, each with kWavesC / kSplitF compute waves.
+constexpr int kSplitF = 2;
+constexpr int kWavesF = kWavesC / kSplitF;
+constexpr int kRowsF = kD / kSplitF;     // state rows per workgroup
+constexpr int kLoadWavesF = 2;           // one streams K, the other V
+constexpr int kStoreWavesF = 2;          // each stores half of the workgroup's rows of W_c
+constexpr int kRingF = 8;       // the compute loop unrolls by it
+constexpr int kSlotFK = 0, kSlotFV = kTileBytes, kSlotFE = 2 * kTileBytes;
+constexpr int kSlotFBytes = kSlotFE + 256;
 
 template <bool kTok, bool kDot>
-__global__ __launch_bounds__(128) void linear_fwd_hist_kernel(LinearArgs a, bf16* whist) {
+__global__ __launch_bounds__(64 * (kWavesF + kLoadWavesF + kStoreWavesF)) void linear_fwd_hist_kernel(LinearArgs a, bf16* whist) {
   __shared__ __attribute__((aligned(16))) char ring_mem[kRingF * kSlotFBytes];
+  __shared__ __attribute__((aligned(16))) char stage_mem[2 * kStateBytes];  // bf16 W_c rows, by step parity
   lds_char* ring = (lds_char*)(ring_mem);
-  const int chain = blockIdx.x;
+  lds_char* stage = (lds_char*)(stage_mem);
+  // the kSplitF workgroups of a chain are b, b + 8, ...: the same XCD (workgroup id mod 8),
+  // so its L2 serves the chain's K and V to all of them
+  const int grp = blockIdx.x / (8 * kSplitF), within = blockIdx.x % (8 * kSplitF);
+  const int chain = 8 * grp + within % 8, part = within / 8;
+  if (chain >= a.B * a.H) return;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, n = lane & 15;
@@ -167,108 +251,151 @@ __global__ __launch_bounds__(128) void linear_fwd_hist_kernel(LinearArgs a, bf16
   const int nchunks = (T + kB - 1) / kB;
   const int seq_bytes = T * kRowBytes;
   const size_t tok0 = static_cast<size_t>(chain) * static_cast<size_t>(T) * kD;
-  const char* k = reinterpret_cast<const char*>(static_cast<const bf16*>(a.k) + tok0);
-  const char* v = reinterpret_cast<const char*>(static_cast<const bf16*>(a.v) + tok0);
 
-  if (wv == 1) {
+  char* wh = reinterpret_cast<char*>(whist + static_cast<size_t>(chain) * nchunks * (kD * kD));
+  if (wv >= kWavesF + kLoadWavesF) {
+    // store waves: after barrier c + 1, the workgroup's rows of W_c from the staging buffer
+    // to HBM, 8 whole 128-byte rows per store (the compute waves' stores would stall their
+    // recursion)
+    const int sw_ = wv - kWavesF - kLoadWavesF;
+    lds_barrier();  // barrier 0
+    for (int c = 0; c < nchunks; ++c) {
+      lds_barrier();  // barrier c + 1: W_c is in stage (c & 1)
+      const lds_char* st = stage + (c & 1) * kStateBytes;
+      const __amdgpu_buffer_rsrc_t rw = rsrc(wh + static_cast<size_t>(c) * kStateBytes, kStateBytes);
+#pragma unroll
+      for (int i = 0; i < kRowsF / (8 * kStoreWavesF); ++i) {
+        const int row = kRowsF * part + (kRowsF / kStoreWavesF) * sw_ + 8 * i + (lane >> 3), piece = lane & 7;
+        const u32x4 x = lds_ld<u32x4>(st + sw(row, 8 * piece));
+        __builtin_amdgcn_raw_buffer_store_b128(x, rw, row * kRowBytes + 16 * piece, 0, 0);
+      }
+    }
+    return;
+  }
+  if (wv >= kWavesF) {
+    const int lw = wv - kWavesF;
+    const char* src = reinterpret_cast<const char*>(static_cast<const bf16*>(lw == 0 ? a.k : a.v) + tok0);
+    const int slot = lw == 0 ? kSlotFK : kSlotFV;
+    const float* etok = kTok ? a.eta_tok + static_cast<size_t>(chain) * T : nullptr;
     const int s0 = src_off(0, lane), s1 = src_off(1, lane);
-    loader_loop<kRingF, 4>(nchunks, [&](int c) {
-      const int off = c * kTileBytes;
+    loader_loop_ahead1<kRingF, kTok ? 3 : 2>(nchunks, [&](int c) {
       lds_char* dst = ring + (c % kRingF) * kSlotFBytes;
-      const __amdgpu_buffer_rsrc_t rk = rsrc(k + off, seq_bytes - off);
-      const __amdgpu_buffer_rsrc_t rv = rsrc(v + off, seq_bytes - off);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dst + kSlotFK, 16, s0, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dst + kSlotFK + 1024, 16, s1, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst + kSlotFV, 16, s0, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst + kSlotFV + 1024, 16, s1, 0, 0, 0);
+      const __amdgpu_buffer_rsrc_t r = tile_rsrc(src, c, nchunks, seq_bytes);
+      load_lds(r, dst + slot, s0);
+      load_lds(r, dst + slot + 1024, s1);
+      if constexpr (kTok) load_lds_e(etok, c, T, dst + kSlotFE, lane);  // both waves, same bytes
     });
     return;
   }
 
+  const int w = kWavesF * part + wv;  // this wave's state rows: 16 w .. 16 w + 15
   const float eta = a.eta;
   const float* w0 = a.w0 + bi * a.w0_batch_stride + static_cast<long long>(hi) * kD * kD;
-  float4_t wt[2][2][4];
+  // W^T tiles of this wave's outputs i = 16 w + n: [kb][hf], rows j = 32 kb + 8 g + 4 hf + e
+  float4_t wt[2][2];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const float* wr = w0 + (16 * it + n) * kD + 32 * kb + 8 * g;
-      wt[kb][0][it] = *reinterpret_cast<const float4_t*>(wr);
-      wt[kb][1][it] = *reinterpret_cast<const float4_t*>(wr + 4);
-    }
-  bf16* wh = whist + static_cast<size_t>(chain) * nchunks * (kD * kD);
+  for (int kb = 0; kb < 2; ++kb) {
+    const float* wr = w0 + (16 * w + n) * kD + 32 * kb + 8 * g;
+    wt[kb][0] = *reinterpret_cast<const float4_t*>(wr);
+    wt[kb][1] = *reinterpret_cast<const float4_t*>(wr + 4);
+  }
   const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-  // rate factors of tokens 4 g + 0..3 of chunk c (zero past T), loaded a chunk ahead
-  const float* etok = kTok ? a.eta_tok + static_cast<size_t>(chain) * T : nullptr;
-  auto load_e = [&](int c) {
-    float4_t e = {1.0f, 1.0f, 1.0f, 1.0f};
-    if constexpr (kTok) {
-      const __amdgpu_buffer_rsrc_t re = rsrc(etok + c * kB, (T - c * kB) * 4);
-#pragma unroll
-      for (int x = 0; x < 4; ++x) e[x] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(re, (4 * g + x) * 4, 0, 0));
-    }
-    return e;
-  };
-  float4_t ecur = load_e(0);
 
-  for (int c = 0; c < nchunks; ++c) {
-    const float4_t enext = (kTok && c + 1 < nchunks) ? load_e(c + 1) : ecur;
-    lds_barrier();
-    const lds_char* sl = ring + (c % kRingF) * kSlotFBytes;
-    // bf16 chunk-start state: the operand, and the stored copy (row 16 it + n, 8 inputs)
-    bf16x8_t wop[2][4];
-    char* out = reinterpret_cast<char*>(wh + static_cast<size_t>(c) * (kD * kD));
+  struct Ops {
+    bf16x8_t kop[2];  // K rows: K[n][32 kb + 8 g ..]
+    u32x2 vt;         // V in the C layout: V[4 g + s][16 w + n]
+    u32x2 kt[2][2];   // K^T rows j in the tile order, tokens 4 g + s
+    float4_t sc;      // -eta e_t of tokens 4 g + 0..3
+  };
+  auto load = [&](auto slot_c) __attribute__((always_inline)) {
+    const lds_char* sl = ring + static_cast<int>(slot_c) * kSlotFBytes;
+    Ops o;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      if constexpr (!kDot) o.kop[kb] = bf(lds_ld<u32x4>(sl + kSlotFK + sw(n, 32 * kb + 8 * g)));
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const u32x4 u = cat_u(wt[kb][0][it], wt[kb][1][it]);
-        wop[kb][it] = bf(u);
-        *reinterpret_cast<u32x4*>(out + (16 * it + n) * kRowBytes + (32 * kb + 8 * g) * 2) = u;
-      }
-    // R (rows: tokens 4 g + e; columns: outputs 16 it + n) = K W^T - V, times -eta
-    bf16x8_t kop[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) kop[kb] = bf(lds_ld<u32x4>(sl + kSlotFK + sw(n, 32 * kb + 8 * g)));
-    bf16x8_t rb[4];
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      float4_t r = zero;
-      if constexpr (!kDot) {
-        r = mfma(kop[0], wop[0][it], zero);
-        r = mfma(kop[1], wop[1][it], r);
-      }
-      // V in the C layout: tokens 4 g + e of column 16 it + n (a transposing read)
-      r -= unpack4(tr(sl + kSlotFV, 4 * g + (n >> 2), 16 * it + 4 * (n & 3)));
-      rb[it] = pad_op(r * (ecur * -eta));
+      for (int hf = 0; hf < 2; ++hf) o.kt[kb][hf] = tr(sl + kSlotFK, 4 * g + (n >> 2), 32 * kb + 8 * (n & 3) + 4 * hf);
     }
-    // W^T += K^T (-eta R): K^T rows j in the tile order, tokens 4 g + s (transposing reads)
+    o.vt = tr(sl + kSlotFV, 4 * g + (n >> 2), 16 * w + 4 * (n & 3));
+    o.sc = float4_t{-eta, -eta, -eta, -eta};
+    if constexpr (kTok) o.sc *= lds_ld<float4_t>(sl + kSlotFE + 16 * g);
+    return o;
+  };
+  // the work of step c; par = c & 1
+  auto work = [&](const Ops& o, auto par_c) __attribute__((always_inline)) {
+    // bf16 chunk-start rows: the operand (row 16 w + n, inputs 32 kb + 8 g ..), and the copy
+    // for the store waves
+    bf16x8_t wop[2];
+    lds_char* st = stage + static_cast<int>(par_c) * kStateBytes;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const u32x4 u = cat_u(wt[kb][0], wt[kb][1]);
+      wop[kb] = bf(u);
+      lds_st<u32x4>(st + sw(16 * w + n, 32 * kb + 8 * g), u);
+    }
+    // R (rows: tokens 4 g + e; columns: outputs 16 w + n) = K W^T - V, times -eta e_t
+    float4_t r = zero;
+    if constexpr (!kDot) {
+      r = mfma(o.kop[0], wop[0], zero);
+      r = mfma(o.kop[1], wop[1], r);
+    }
+    r -= unpack4(o.vt);
+    const bf16x8_t rb = pad_op(r * o.sc);
+    // W^T += K^T (-eta Rt)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const bf16x8_t ktb = pad2(tr(sl + kSlotFK, 4 * g + (n >> 2), 32 * kb + 8 * (n & 3) + 4 * hf));
-#pragma unroll
-        for (int it = 0; it < 4; ++it) wt[kb][hf][it] = mfma(ktb, rb[it], wt[kb][hf][it]);
-      }
-    ecur = enext;
+      for (int hf = 0; hf < 2; ++hf) wt[kb][hf] = mfma(pad2(o.kt[kb][hf]), rb, wt[kb][hf]);
+  };
+  lds_barrier();  // barrier 0: steps 0 and 1 are in the ring
+  Ops oa = load(IC<0>{});
+  // step c: load step c + 1's operands, work on step c, barrier c + 1
+  int c = 0;
+  for (; c + kRingF <= nchunks; c += kRingF) {
+    Ops ob = load(IC<1>{}); work(oa, IC<0>{}); lds_barrier();
+    oa = load(IC<2>{}); work(ob, IC<1>{}); lds_barrier();
+    ob = load(IC<3>{}); work(oa, IC<0>{}); lds_barrier();
+    oa = load(IC<4>{}); work(ob, IC<1>{}); lds_barrier();
+    ob = load(IC<5>{}); work(oa, IC<0>{}); lds_barrier();
+    oa = load(IC<6>{}); work(ob, IC<1>{}); lds_barrier();
+    ob = load(IC<7>{}); work(oa, IC<0>{}); lds_barrier();
+    oa = load(IC<0>{}); work(ob, IC<1>{}); lds_barrier();
+  }
+  for (; c < nchunks; ++c) {
+    const Ops ob = load((c + 1) % kRingF);
+    work(oa, c & 1);
+    lds_barrier();
+    oa = ob;
   }
 }
 
 // ---------------------------------------------------------------- reverse pass
-constexpr int kRingB = 4;
+// Twelve waves per chain.  Between barriers k and k + 1:
+//   recursion wave w (0..3), chunk c = nchunks - 1 - k, state rows 16 w .. 16 w + 15:
+//     Rt^T and dR^T of those rows, dV, the update of G^T, and the rows' Rt, dR and G (bf16)
+//     into LDS;
+//   gradient wave w (4..7), chunk c + 1 (the previous step's), features j = 16 (w - 4) ..:
+//     dP over all outputs, dQ^T and dK^T of those features, from the Rt, dR and G rows all
+//     four recursion waves wrote during the previous step;
+//   loader waves (8..11): the chunk of step k + 1 .. into the ring.
+// Each SIMD runs one recursion and one gradient wave, so the gradient work fills the
+// recursion's stalls.  The Rt / dR / G buffers alternate between steps; the ring slot of a
+// step is read during two steps (lag-2 loader).
+constexpr int kLoadWavesB = 4;
+constexpr int kRingB = 6;  // even (buffer parity = slot parity); the loops unroll by it
 constexpr int kSlotQ = 0, kSlotK = kTileBytes, kSlotV = 2 * kTileBytes, kSlotZ = 3 * kTileBytes;
 constexpr int kSlotW = 4 * kTileBytes;
-constexpr int kSlotBBytes = kSlotW + kStateBytes;
+constexpr int kSlotE = kSlotW + kStateBytes;
+constexpr int kSlotBBytes = kSlotE + 256;
 
 template <bool kTok, bool kDot>
-__global__ __launch_bounds__(128) void linear_bwd_mfma_kernel(LinearBwdArgs a, const bf16* whist) {
+__global__ __launch_bounds__(64 * (2 * kWavesC + kLoadWavesB)) void linear_bwd_mfma_kernel(LinearBwdArgs a, const bf16* whist) {
   __shared__ __attribute__((aligned(16))) char ring_mem[kRingB * kSlotBBytes];
-  __shared__ __attribute__((aligned(16))) char gcopy_mem[kStateBytes];  // bf16 G rows [i][j]
-  __shared__ __attribute__((aligned(16))) char drs_mem[kTileBytes];     // bf16 dR rows [s][i]
+  __shared__ __attribute__((aligned(16))) char rt_mem[2 * kTileBytes];   // bf16 Rt rows [s][i]
+  __shared__ __attribute__((aligned(16))) char dr_mem[2 * kTileBytes];   // bf16 dR rows [s][i]
+  __shared__ __attribute__((aligned(16))) char g_mem[2 * kStateBytes];   // bf16 G rows [i][j]
+  __shared__ __attribute__((aligned(16))) float de_mem[2 * kWavesC * kB];  // per-wave <dRt, R>
   lds_char* ring = (lds_char*)(ring_mem);
-  lds_char* gcp = (lds_char*)(gcopy_mem);
-  lds_char* drs = (lds_char*)(drs_mem);
   const int chain = blockIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -281,53 +408,42 @@ __global__ __launch_bounds__(128) void linear_bwd_mfma_kernel(LinearBwdArgs a, c
   const char* k = reinterpret_cast<const char*>(static_cast<const bf16*>(a.k) + tok0);
   const char* v = reinterpret_cast<const char*>(static_cast<const bf16*>(a.v) + tok0);
   const char* dz = reinterpret_cast<const char*>(static_cast<const bf16*>(a.dz) + tok0);
-  const char* wh = reinterpret_cast<const char*>(whist + static_cast<size_t>(chain) * nchunks * (kD * kD));
+  const float* etok = kTok ? a.eta_tok + static_cast<size_t>(chain) * T : nullptr;
 
-  if (wv == 1) {
+  if (wv >= 2 * kWavesC) {
+    // loader waves: 0 streams Q and K, 1 V and dZ, 2 and 3 half of W_c each; step k holds
+    // chunk nchunks - 1 - k
+    const int lw = wv - 2 * kWavesC;
+    const char* wh = reinterpret_cast<const char*>(whist + static_cast<size_t>(chain) * nchunks * (kD * kD));
+    const char* b0 = lw == 0 ? q : v;
+    const char* b1 = lw == 0 ? k : dz;
+    const int d0 = lw == 0 ? kSlotQ : kSlotV, d1 = lw == 0 ? kSlotK : kSlotZ;
+    const int h0 = lw == 3 ? 4 : 0;
     const int s0 = src_off(0, lane), s1 = src_off(1, lane);
-    // step k handles chunk nchunks - 1 - k (steps past the first chunk load zeros)
-    loader_loop<kRingB, 16>(nchunks, [&](int kk) {
+    loader_loop_lag2<kRingB, kTok ? 5 : 4>(nchunks, [&](int kk) {
       const int c = nchunks - 1 - kk;
-      const int off = c * kTileBytes;
-      const int left = c >= 0 ? seq_bytes - off : 0;
       lds_char* dst = ring + (kk % kRingB) * kSlotBBytes;
-      const __amdgpu_buffer_rsrc_t rq = rsrc(q + (c >= 0 ? off : 0), left);
-      const __amdgpu_buffer_rsrc_t rk = rsrc(k + (c >= 0 ? off : 0), left);
-      const __amdgpu_buffer_rsrc_t rv = rsrc(v + (c >= 0 ? off : 0), left);
-      const __amdgpu_buffer_rsrc_t rz = rsrc(dz + (c >= 0 ? off : 0), left);
-      const __amdgpu_buffer_rsrc_t rw =
-          rsrc(wh + (c >= 0 ? static_cast<size_t>(c) * kStateBytes : 0), c >= 0 ? kStateBytes : 0);
+      if (lw < 2) {
+        const __amdgpu_buffer_rsrc_t r0 = tile_rsrc(b0, c, nchunks, seq_bytes);
+        const __amdgpu_buffer_rsrc_t r1 = tile_rsrc(b1, c, nchunks, seq_bytes);
+        load_lds(r0, dst + d0, s0);
+        load_lds(r0, dst + d0 + 1024, s1);
+        load_lds(r1, dst + d1, s0);
+        load_lds(r1, dst + d1 + 1024, s1);
+      } else {
+        const bool live = c >= 0;
+        const __amdgpu_buffer_rsrc_t rw =
+            rsrc(wh + (live ? static_cast<size_t>(c) * kStateBytes : 0), live ? kStateBytes : 0);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int so = h ? s1 : s0;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, dst + kSlotQ + 1024 * h, 16, so, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dst + kSlotK + 1024 * h, 16, so, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst + kSlotV + 1024 * h, 16, so, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, dst + kSlotZ + 1024 * h, 16, so, 0, 0, 0);
+        for (int h = 0; h < 4; ++h) load_lds(rw, dst + kSlotW + 1024 * (h0 + h), src_off(h0 + h, lane));
       }
-#pragma unroll
-      for (int h = 0; h < 8; ++h)  // the 64 rows of W_c, 8 per load
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, dst + kSlotW + 1024 * h, 16, src_off(h, lane), 0, 0, 0);
+      if constexpr (kTok) load_lds_e(etok, c, T, dst + kSlotE, lane);  // every loader, same bytes
     });
     return;
   }
 
   const float eta = a.eta;
-  // G^T tiles, from dL/dW_final (zeros without it)
-  float4_t gt[2][2][4];
-  const float* dwo = a.dw_out ? a.dw_out + static_cast<size_t>(chain) * kD * kD : nullptr;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const float4_t zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
-      const float* wr = dwo ? dwo + (16 * it + n) * kD + 32 * kb + 8 * g : nullptr;
-      gt[kb][0][it] = dwo ? *reinterpret_cast<const float4_t*>(wr) : zero4;
-      gt[kb][1][it] = dwo ? *reinterpret_cast<const float4_t*>(wr + 4) : zero4;
-    }
-  char* dq = reinterpret_cast<char*>(static_cast<bf16*>(a.dq) + tok0);
-  char* dk = reinterpret_cast<char*>(static_cast<bf16*>(a.dk) + tok0);
-  char* dv = reinterpret_cast<char*>(static_cast<bf16*>(a.dv) + tok0);
+  const char* dv = reinterpret_cast<const char*>(static_cast<bf16*>(a.dv) + tok0);
   const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
   // causal masks: P (rows t = 4 g + e, cols s = n) keeps s <= t; P^T (rows s, cols t) keeps s <= t
   bool keep_p[4], keep_t[4];
@@ -337,179 +453,203 @@ __global__ __launch_bounds__(128) void linear_bwd_mfma_kernel(LinearBwdArgs a, c
     keep_t[e] = 4 * g + e <= n;
   }
 
-  // the rate factor of token n of chunk c (zero past T), loaded a chunk ahead
-  const float* etok = kTok ? a.eta_tok + static_cast<size_t>(chain) * T : nullptr;
-  float* detok = kTok && a.deta_tok ? a.deta_tok + static_cast<size_t>(chain) * T : nullptr;
-  auto load_e = [&](int c) {
-    if constexpr (kTok)
-      return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc(etok + c * kB, (T - c * kB) * 4), n * 4, 0, 0));
-    return 1.0f;
-  };
-  float ecur = load_e(nchunks - 1);
-
-  for (int kk = 0; kk < nchunks; ++kk) {
-    const int c = nchunks - 1 - kk;
-    const float enext = (kTok && c > 0) ? load_e(c - 1) : ecur;
-    lds_barrier();  // barrier kk: this step's chunk is in its slot
-    const lds_char* sl = ring + (kk % kRingB) * kSlotBBytes;
-    const lds_char* sq = sl + kSlotQ;
-    const lds_char* sk = sl + kSlotK;
-    const lds_char* sv = sl + kSlotV;
-    const lds_char* sz = sl + kSlotZ;
-    const lds_char* sw_ = sl + kSlotW;
-
-    // ---- operands ----
-    bf16x8_t kr[2], qr[2], zr[2];  // rows: X[n][32 kb + 8 g ..]
+  if (wv < kWavesC) {
+    // ---------------- recursion wave: G^T tiles of the outputs i = 16 w + n, from
+    // dL/dW_final (zeros without it)
+    const int w = wv;
+    float4_t gt[2][2];
+    const float* dwo = a.dw_out ? a.dw_out + static_cast<size_t>(chain) * kD * kD : nullptr;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      kr[kb] = bf(lds_ld<u32x4>(sk + sw(n, 32 * kb + 8 * g)));
-      qr[kb] = bf(lds_ld<u32x4>(sq + sw(n, 32 * kb + 8 * g)));
-      zr[kb] = bf(lds_ld<u32x4>(sz + sw(n, 32 * kb + 8 * g)));
+      const float4_t zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+      const float* wr = dwo ? dwo + (16 * w + n) * kD + 32 * kb + 8 * g : nullptr;
+      gt[kb][0] = dwo ? *reinterpret_cast<const float4_t*>(wr) : zero4;
+      gt[kb][1] = dwo ? *reinterpret_cast<const float4_t*>(wr + 4) : zero4;
     }
-    bf16x8_t wop[2][4], gop[2][4];  // rows i = 16 it + n, inputs 32 kb + 8 g ..
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        wop[kb][it] = bf(lds_ld<u32x4>(sw_ + sw(16 * it + n, 32 * kb + 8 * g)));
-        const u32x4 gu = cat_u(gt[kb][0][it], gt[kb][1][it]);
-        gop[kb][it] = bf(gu);
-        lds_st<u32x4>(gcp + sw(16 * it + n, 32 * kb + 8 * g), gu);  // G rows for the G^T reads
-      }
-    u32x2 zq[4];  // dZ[n][16 it + 4 g .. + 3]
-#pragma unroll
-    for (int it = 0; it < 4; ++it) zq[it] = lds_ld<u32x2>(sz + sw(n, 16 * it + 4 * g));
+    // step kk (slot = kk % kRingB, passed as a constant in the unrolled loop so that every
+    // LDS address is a loop-invariant register plus an immediate)
+    auto step = [&](int kk, auto slot_c) __attribute__((always_inline)) {
+      const int slot = slot_c;
+      const int par = slot & 1;  // kRingB is even: the parity of kk
+      lds_barrier();  // barrier kk: step kk's chunk is in its slot
+      {
+        const int c = nchunks - 1 - kk;
+        const lds_char* sl = ring + slot * kSlotBBytes;
+        const lds_char* sq = sl + kSlotQ;
+        const lds_char* sk = sl + kSlotK;
+        const lds_char* sz = sl + kSlotZ;
+        lds_char* rtw = (lds_char*)(rt_mem) + par * kTileBytes;
+        lds_char* drw = (lds_char*)(dr_mem) + par * kTileBytes;
+        lds_char* gw = (lds_char*)(g_mem) + par * kStateBytes;
 
-    // ---- R^T (rows i = 16 it + 4 g + e, cols s = n) = W K^T - V^T ----
-    float4_t rt[4];
+        bf16x8_t kr[2], qr[2], wop[2], gop[2];  // rows: K[n][..], Q[n][..], W[16 w + n][..], G[16 w + n][..]
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      rt[it] = zero;
-      if constexpr (!kDot) {
-        rt[it] = mfma(wop[0][it], kr[0], zero);
-        rt[it] = mfma(wop[1][it], kr[1], rt[it]);
-      }
-      rt[it] -= unpack4(lds_ld<u32x2>(sv + sw(n, 16 * it + 4 * g)));
-    }
-    bf16x8_t rtop[2], zcat[2];  // over outputs: tiles 2 h, 2 h + 1 side by side (Rt^T)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      rtop[h] = kTok ? cat_op(rt[2 * h] * ecur, rt[2 * h + 1] * ecur) : cat_op(rt[2 * h], rt[2 * h + 1]);
-      zcat[h] = join2(zq[2 * h], zq[2 * h + 1]);
-    }
-
-    // ---- P, P^T (masked), dP = -eta tril(dZ R^T) (rows t), dP^T (rows s) ----
-    float4_t pm = mfma(qr[0], kr[0], zero);
-    pm = mfma(qr[1], kr[1], pm);
-    float4_t dp = mfma(zcat[0], rtop[0], zero);
-    dp = mfma(zcat[1], rtop[1], dp);
-    float4_t dpt = mfma(rtop[0], zcat[0], zero);
-    dpt = mfma(rtop[1], zcat[1], dpt);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      pm[e] = keep_p[e] ? pm[e] : 0.0f;
-      dp[e] = keep_p[e] ? -eta * dp[e] : 0.0f;
-      dpt[e] = keep_t[e] ? -eta * dpt[e] : 0.0f;
-    }
-    const bf16x8_t pmb = pad_op(pm), dpb = pad_op(dp), dptb = pad_op(dpt);
-
-    // ---- dR^T (rows i, cols s) = -eta (G K^T + dZ^T P) ----
-    u32x2 ztr[4];  // dZ[4 g + s][16 it + n]: dZ^T rows i, tokens
-#pragma unroll
-    for (int it = 0; it < 4; ++it) ztr[it] = tr(sz, 4 * g + (n >> 2), 16 * it + 4 * (n & 3));
-    float4_t drt[4];
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      float4_t x = mfma(gop[0][it], kr[0], zero);
-      x = mfma(gop[1][it], kr[1], x);
-      x = mfma(pad2(ztr[it]), pmb, x);
-      drt[it] = x * -eta;
-    }
-    if constexpr (kTok) {
-      // de_n = <dRt_n, R_n>: this lane's 16 outputs, then the other three lane groups'
-      float p = 0.0f;
-#pragma unroll
-      for (int it = 0; it < 4; ++it)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) p += drt[it][e] * rt[it][e];
-      p += __shfl_xor(p, 16, 64);
-      p += __shfl_xor(p, 32, 64);
-      if (detok && g == 0)
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, p), rsrc(detok + c * kB, (T - c * kB) * 4), n * 4, 0, 0);
-#pragma unroll
-      for (int it = 0; it < 4; ++it) drt[it] *= ecur;  // dR = diag(e) dRt
-    }
-    bf16x8_t drop[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) drop[h] = cat_op(drt[2 * h], drt[2 * h + 1]);
-
-    // dV = -dR (lane: token n, outputs 16 it + 4 g ..), and dR rows [s][i] to LDS
-    {
-      const int off = c * kTileBytes;
-      const __amdgpu_buffer_rsrc_t rdv = rsrc(dv + off, seq_bytes - off);
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        __builtin_amdgcn_raw_buffer_store_b64(pack4(-drt[it]), rdv, n * kRowBytes + 32 * it + 8 * g, 0, 0);
-        lds_st<u32x2>(drs + sw(n, 16 * it + 4 * g), pack4(drt[it]));
-      }
-    }
-
-    // ---- dQ^T (rows j = 16 jt + 4 g + e, cols t) = W^T dZ^T + K^T dP^T;
-    //      dK^T (rows j, cols s) = -eta G^T R^T + Q^T dP + W^T dR^T ----
-    {
-      const int off = c * kTileBytes;
-      const __amdgpu_buffer_rsrc_t rdq = rsrc(dq + off, seq_bytes - off);
-      const __amdgpu_buffer_rsrc_t rdk = rsrc(dk + off, seq_bytes - off);
-#pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        float4_t xq = zero, xk = zero, xg = zero;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          // W^T and G^T rows j = 16 jt + n, outputs i of tiles 2 h, 2 h + 1 (rows 4 g + s)
-          const bf16x8_t wtr = join2(tr(sw_, 32 * h + 4 * g + (n >> 2), 16 * jt + 4 * (n & 3)),
-                                     tr(sw_, 32 * h + 16 + 4 * g + (n >> 2), 16 * jt + 4 * (n & 3)));
-          const bf16x8_t gtr = join2(tr(gcp, 32 * h + 4 * g + (n >> 2), 16 * jt + 4 * (n & 3)),
-                                     tr(gcp, 32 * h + 16 + 4 * g + (n >> 2), 16 * jt + 4 * (n & 3)));
-          xq = mfma(wtr, zcat[h], xq);
-          if constexpr (!kDot) xk = mfma(wtr, drop[h], xk);
-          xg = mfma(gtr, rtop[h], xg);
+        for (int kb = 0; kb < 2; ++kb) {
+          kr[kb] = bf(lds_ld<u32x4>(sk + sw(n, 32 * kb + 8 * g)));
+          qr[kb] = bf(lds_ld<u32x4>(sq + sw(n, 32 * kb + 8 * g)));
+          wop[kb] = bf(lds_ld<u32x4>(sl + kSlotW + sw(16 * w + n, 32 * kb + 8 * g)));
+          const u32x4 gu = cat_u(gt[kb][0], gt[kb][1]);
+          gop[kb] = bf(gu);
+          lds_st<u32x4>(gw + sw(16 * w + n, 32 * kb + 8 * g), gu);  // G rows for the G^T reads
         }
-        const bf16x8_t ktr = pad2(tr(sk, 4 * g + (n >> 2), 16 * jt + 4 * (n & 3)));
-        const bf16x8_t qtr = pad2(tr(sq, 4 * g + (n >> 2), 16 * jt + 4 * (n & 3)));
-        xq = mfma(ktr, dptb, xq);
-        xk = mfma(qtr, dpb, xk);
-        xk += -eta * xg;
-        __builtin_amdgcn_raw_buffer_store_b64(pack4(xq), rdq, n * kRowBytes + 32 * jt + 8 * g, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b64(pack4(xk), rdk, n * kRowBytes + 32 * jt + 8 * g, 0, 0);
+        // R^T (rows i = 16 w + 4 g + e, cols s = n) = W K^T - V^T
+        float4_t rt = zero;
+        if constexpr (!kDot) {
+          rt = mfma(wop[0], kr[0], zero);
+          rt = mfma(wop[1], kr[1], rt);
+        }
+        rt -= unpack4(lds_ld<u32x2>(sl + kSlotV + sw(n, 16 * w + 4 * g)));
+        const float ecur = kTok ? lds_ld<float>(sl + kSlotE + 4 * n) : 1.0f;
+        lds_st<u32x2>(rtw + sw(n, 16 * w + 4 * g), pack4(kTok ? rt * ecur : rt));
+        // P = tril(Q K^T) (rows t = 4 g + e, cols s = n)
+        float4_t pm = mfma(qr[0], kr[0], zero);
+        pm = mfma(qr[1], kr[1], pm);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pm[e] = keep_p[e] ? pm[e] : 0.0f;
+        // dR^T (rows i, cols s) = -eta (G K^T + dZ^T P)
+        const u32x2 ztr = tr(sz, 4 * g + (n >> 2), 16 * w + 4 * (n & 3));  // dZ[4 g + s][16 w + n]
+        float4_t drt = mfma(gop[0], kr[0], zero);
+        drt = mfma(gop[1], kr[1], drt);
+        drt = mfma(pad2(ztr), pad_op(pm), drt);
+        drt *= -eta;
+        if constexpr (kTok) {
+          // this wave's share of de_s = <dRt_s, R_s>: its 16 outputs, over the four lane groups
+          float p = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p += drt[e] * rt[e];
+          p += __shfl_xor(p, 16, 64);
+          p += __shfl_xor(p, 32, 64);
+          lds_st<float>((lds_char*)(de_mem) + 4 * (par * kWavesC * kB + kB * w + n), p);
+          drt *= ecur;  // dR = diag(e) dRt
+        }
+        // dV = -dR (token n, outputs 16 w + 4 g ..), dR rows to LDS
+        __builtin_amdgcn_raw_buffer_store_b64(pack4(-drt), tile_rsrc(dv, c, nchunks, seq_bytes),
+                                              n * kRowBytes + 32 * w + 8 * g, 0, 0);
+        lds_st<u32x2>(drw + sw(n, 16 * w + 4 * g), pack4(drt));
+        // G^T += Q^T dZ + K^T dR: slots 0..3 the dZ^T Q tokens, 4..7 the dR^T K tokens (dR
+        // read back transposed from this wave's own rows)
+        const bf16x8_t bup =
+            join2(ztr, kDot ? u32x2{0u, 0u} : tr(drw, 4 * g + (n >> 2), 16 * w + 4 * (n & 3)));
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const int col = 32 * kb + 8 * (n & 3) + 4 * hf;
+            const bf16x8_t aup = join2(tr(sq, 4 * g + (n >> 2), col), tr(sk, 4 * g + (n >> 2), col));
+            gt[kb][hf] = mfma(aup, bup, gt[kb][hf]);
+          }
       }
+    };
+    int kk = 0;
+    for (; kk + kRingB <= nchunks; kk += kRingB) {
+      step(kk, IC<0>{});
+      step(kk + 1, IC<1>{});
+      step(kk + 2, IC<2>{});
+      step(kk + 3, IC<3>{});
+      step(kk + 4, IC<4>{});
+      step(kk + 5, IC<5>{});
     }
-
-    // ---- G^T += Q^T dZ + K^T dR: slots 0..3 the dZ^T Q tokens, 4..7 the dR^T K tokens ----
-    bf16x8_t bup[4];
+    for (; kk < nchunks; ++kk) step(kk, kk % kRingB);
+    // the last step's G is dL/dW_0
+    float* dw0 = a.dw0 + static_cast<size_t>(chain) * kD * kD;
 #pragma unroll
-    for (int it = 0; it < 4; ++it)
-      bup[it] = join2(ztr[it], kDot ? u32x2{0u, 0u} : tr(drs, 4 * g + (n >> 2), 16 * it + 4 * (n & 3)));
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int col = 32 * kb + 8 * (n & 3) + 4 * hf;
-        const bf16x8_t aup = join2(tr(sq, 4 * g + (n >> 2), col), tr(sk, 4 * g + (n >> 2), col));
-#pragma unroll
-        for (int it = 0; it < 4; ++it) gt[kb][hf][it] = mfma(aup, bup[it], gt[kb][hf][it]);
-      }
-    ecur = enext;
+    for (int kb = 0; kb < 2; ++kb) {
+      float* wr = dw0 + (16 * w + n) * kD + 32 * kb + 8 * g;
+      *reinterpret_cast<float4_t*>(wr) = gt[kb][0];
+      *reinterpret_cast<float4_t*>(wr + 4) = gt[kb][1];
+    }
+    lds_barrier();  // barrier nchunks, for the gradient waves' last step
+    return;
   }
 
-  float* dw0 = a.dw0 + static_cast<size_t>(chain) * kD * kD;
+  // ---------------- gradient wave: features j = 16 w + 4 g + e of the previous step's chunk
+  const int w = wv - kWavesC;
+  const char* dq = reinterpret_cast<const char*>(static_cast<bf16*>(a.dq) + tok0);
+  const char* dk = reinterpret_cast<const char*>(static_cast<bf16*>(a.dk) + tok0);
+  float* detok = kTok ? a.deta_tok : nullptr;
+  if (detok) detok += static_cast<size_t>(chain) * T;
+  // barrier kk (kk >= 1): step kk - 1's rows are in LDS; slot = (kk - 1) % kRingB, whose
+  // parity is that of the buffers step kk - 1 wrote
+  auto step = [&](int kk, auto slot_c) __attribute__((always_inline)) {
+    const int slot = slot_c;
+    const int par1 = slot & 1;
+    lds_barrier();
+    {
+      const int c2 = nchunks - kk;  // the chunk of step kk - 1
+      const lds_char* sl = ring + slot * kSlotBBytes;
+      const lds_char* sq = sl + kSlotQ;
+      const lds_char* sk = sl + kSlotK;
+      const lds_char* sz = sl + kSlotZ;
+      const lds_char* sw_ = sl + kSlotW;
+      const lds_char* rtr = (lds_char*)(rt_mem) + par1 * kTileBytes;
+      const lds_char* drr = (lds_char*)(dr_mem) + par1 * kTileBytes;
+      const lds_char* gr = (lds_char*)(g_mem) + par1 * kStateBytes;
+      // operands over outputs (tiles 2 h, 2 h + 1 side by side: k = 8 g + s' <->
+      // i = 16 (2 h + s' / 4) + 4 g + s' % 4): dZ rows, Rt rows, dR rows of token n
+      bf16x8_t zcat[2], rtop[2], drop[2];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+      for (int h = 0; h < 2; ++h) {
+        zcat[h] = join2(lds_ld<u32x2>(sz + sw(n, 32 * h + 4 * g)), lds_ld<u32x2>(sz + sw(n, 32 * h + 16 + 4 * g)));
+        rtop[h] = join2(lds_ld<u32x2>(rtr + sw(n, 32 * h + 4 * g)), lds_ld<u32x2>(rtr + sw(n, 32 * h + 16 + 4 * g)));
+        if constexpr (!kDot)
+          drop[h] = join2(lds_ld<u32x2>(drr + sw(n, 32 * h + 4 * g)), lds_ld<u32x2>(drr + sw(n, 32 * h + 16 + 4 * g)));
+      }
+      // dP = -eta tril(dZ Rt^T) (rows t), dP^T (rows s)
+      float4_t dp = mfma(zcat[0], rtop[0], zero);
+      dp = mfma(zcat[1], rtop[1], dp);
+      float4_t dpt = mfma(rtop[0], zcat[0], zero);
+      dpt = mfma(rtop[1], zcat[1], dpt);
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      float* wr = dw0 + (16 * it + n) * kD + 32 * kb + 8 * g;
-      *reinterpret_cast<float4_t*>(wr) = gt[kb][0][it];
-      *reinterpret_cast<float4_t*>(wr + 4) = gt[kb][1][it];
+      for (int e = 0; e < 4; ++e) {
+        dp[e] = keep_p[e] ? -eta * dp[e] : 0.0f;
+        dpt[e] = keep_t[e] ? -eta * dpt[e] : 0.0f;
+      }
+      // dQ^T (rows j, cols t) = W^T dZ^T + K^T dP^T;  dK^T (rows j, cols s) = -eta G^T Rt^T +
+      // Q^T dP + W^T dR^T.  W^T and G^T rows j = 16 w + n over outputs i (transposing reads).
+      float4_t xq = zero, xk = zero, xg = zero;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bf16x8_t wtr = join2(tr(sw_, 32 * h + 4 * g + (n >> 2), 16 * w + 4 * (n & 3)),
+                                   tr(sw_, 32 * h + 16 + 4 * g + (n >> 2), 16 * w + 4 * (n & 3)));
+        const bf16x8_t gtr = join2(tr(gr, 32 * h + 4 * g + (n >> 2), 16 * w + 4 * (n & 3)),
+                                   tr(gr, 32 * h + 16 + 4 * g + (n >> 2), 16 * w + 4 * (n & 3)));
+        xq = mfma(wtr, zcat[h], xq);
+        if constexpr (!kDot) xk = mfma(wtr, drop[h], xk);
+        xg = mfma(gtr, rtop[h], xg);
+      }
+      const bf16x8_t ktr = pad2(tr(sk, 4 * g + (n >> 2), 16 * w + 4 * (n & 3)));
+      const bf16x8_t qtr = pad2(tr(sq, 4 * g + (n >> 2), 16 * w + 4 * (n & 3)));
+      xq = mfma(ktr, pad_op(dpt), xq);
+      xk = mfma(qtr, pad_op(dp), xk);
+      xk += -eta * xg;
+      __builtin_amdgcn_raw_buffer_store_b64(pack4(xq), tile_rsrc(dq, c2, nchunks, seq_bytes),
+                                            n * kRowBytes + 32 * w + 8 * g, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(pack4(xk), tile_rsrc(dk, c2, nchunks, seq_bytes),
+                                            n * kRowBytes + 32 * w + 8 * g, 0, 0);
+      if constexpr (kTok) {
+        // de of this chunk: the four recursion waves' shares, stored by gradient wave 0 (its
+        // four lane groups write the same value)
+        const lds_char* dsh = (lds_char*)(de_mem) + 4 * (par1 * kWavesC * kB + n);
+        const float d = lds_ld<float>(dsh) + lds_ld<float>(dsh + 4 * kB) + lds_ld<float>(dsh + 8 * kB) +
+                        lds_ld<float>(dsh + 12 * kB);
+        const bool live = detok && w == 0;
+        const int cnt = live ? (T - c2 * kB < kB ? T - c2 * kB : kB) : 0;
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, d),
+                                              rsrc(live ? detok + c2 * kB : detok, 4 * cnt), 4 * n, 0, 0);
+      }
     }
+  };
+  lds_barrier();  // barrier 0
+  int kk = 1;
+  for (; kk + kRingB <= nchunks + 1; kk += kRingB) {
+    step(kk, IC<0>{});
+    step(kk + 1, IC<1>{});
+    step(kk + 2, IC<2>{});
+    step(kk + 3, IC<3>{});
+    step(kk + 4, IC<4>{});
+    step(kk + 5, IC<5>{});
+  }
+  for (; kk <= nchunks; ++kk) step(kk, (kk - 1) % kRingB);
 }
 
 }  // namespace
@@ -533,17 +673,19 @@ size_t linear_bwd_mfma_workspace_bytes(const LinearBwdArgs& a) {
 hipError_t launch_linear_bwd_mfma(const LinearArgs& fwd, const LinearBwdArgs& a, void* workspace,
                                   hipStream_t s) {
   const long long nchains = static_cast<long long>(a.B) * a.H;
-  if (nchains > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (nchains > (1LL << 27)) return hipErrorInvalidValue;  // grids of at most 2^30 workgroups
   bf16* whist = static_cast<bf16*>(workspace);
-  const dim3 grid(static_cast<unsigned>(nchains)), block(128);  // compute wave + loader wave
+  const dim3 grid(static_cast<unsigned>(nchains));
+  const dim3 fgrid(static_cast<unsigned>((nchains + 7) / 8 * 8 * kSplitF));
+  const dim3 fblock(64 * (kWavesF + kLoadWavesF + kStoreWavesF)), bblock(64 * (2 * kWavesC + kLoadWavesB));
   if ((fwd.eta_tok != nullptr) != (a.eta_tok != nullptr) || fwd.dot_loss != a.dot_loss)
     return hipErrorInvalidValue;
   const bf16* wc = static_cast<const bf16*>(whist);
   auto run = [&](auto fk, auto bk) {
-    hipLaunchKernelGGL(fk, grid, block, 0, s, fwd, whist);
+    hipLaunchKernelGGL(fk, fgrid, fblock, 0, s, fwd, whist);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bk, grid, block, 0, s, a, wc);
+    hipLaunchKernelGGL(bk, grid, bblock, 0, s, a, wc);
     return hipGetLastError();
   };
   if (a.eta_tok && a.dot_loss)

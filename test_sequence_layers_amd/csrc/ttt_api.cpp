@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <mutex>
 #include <string>
@@ -66,10 +67,43 @@ int check_epochs(const char* fn, int epochs, int causal) {
   return TTT_OK;
 }
 
-// Per-call device workspace, allocated and released in stream order (hipMallocAsync /
+// Per-call device workspace, allocated and released in stream order (hipMallocFromPoolAsync /
 // hipFreeAsync on the caller's stream): the release is queued behind the kernels that use
 // it, so concurrent calls on different streams never share a workspace and the host never
-// waits.
+// waits.  The memory comes from a stream-ordered pool of the library's own, one per device,
+// that keeps what it has allocated (no release threshold): the next call reuses those blocks
+// instead of mapping fresh pages (a 100 MB workspace mapped per call cost more than the
+// kernels using it).  The pool holds its largest working set until the process ends.
+constexpr int kMaxDevices = 64;
+std::mutex g_pool_mu;
+hipMemPool_t g_pool[kMaxDevices] = {};
+
+int workspace_pool(hipMemPool_t* out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(TTT_E_UNSUPPORTED, "workspace pool: device %d", dev);
+  std::lock_guard<std::mutex> lock(g_pool_mu);
+  if (!g_pool[dev]) {
+    hipMemPoolProps props = {};
+    props.allocType = hipMemAllocationTypePinned;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t p = nullptr;
+    e = hipMemPoolCreate(&p, &props);
+    if (e != hipSuccess) return hip_fail(e, "hipMemPoolCreate(workspace)");
+    uint64_t keep = UINT64_MAX;
+    e = hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep);
+    if (e != hipSuccess) {
+      (void)hipMemPoolDestroy(p);
+      return hip_fail(e, "hipMemPoolSetAttribute(workspace)");
+    }
+    g_pool[dev] = p;
+  }
+  *out = g_pool[dev];
+  return TTT_OK;
+}
+
 struct StreamBuffer {
   void* ptr = nullptr;
   hipStream_t stream = nullptr;
@@ -80,10 +114,13 @@ struct StreamBuffer {
 
 int get_workspace(size_t bytes, hipStream_t s, StreamBuffer* out) {
   out->stream = s;
-  hipError_t e = hipMallocAsync(&out->ptr, bytes > 0 ? bytes : 1, s);
+  hipMemPool_t pool = nullptr;
+  int rc = workspace_pool(&pool);
+  if (rc != TTT_OK) return rc;
+  hipError_t e = hipMallocFromPoolAsync(&out->ptr, bytes > 0 ? bytes : 1, pool, s);
   if (e != hipSuccess) {
     out->ptr = nullptr;
-    return hip_fail(e, "hipMallocAsync(workspace)");
+    return hip_fail(e, "hipMallocFromPoolAsync(workspace)");
   }
   return TTT_OK;
 }
@@ -104,7 +141,6 @@ int copy_state(float* dst, const float* src, long long batch_stride, int B, int 
 // that overlap on one GPU (different streams) race; a call writes every byte it reads.
 constexpr size_t kScratchBytes = size_t(64) << 20;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
-constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_dev[kMaxDevices] = {};
 
