@@ -826,6 +826,25 @@ def test_nc_bwd_bf16_vision_shape(kind, rates, loss, epochs, chunk):
                   epochs=epochs)
 
 
+@pytest.mark.parametrize("T,rates,loss,with_dw", [
+    (1, False, "mse", True), (16, True, "mse", False), (37, False, "dot", True),
+    (100, True, "dot", True), (196, True, "mse", True), (256, False, "mse", False)])
+def test_mlp_nc_bwd_matrix_core_cases(T, rates, loss, with_dw):
+    # one full-batch step at d = hidden = 64, bf16: the matrix-core backward for 16 <= T <= 256
+    # (T = 1 checks that shorter sequences go to the fp32 kernel)
+    w = workload(4).replace(B=2, H=3, T=T, chunk=T, seed=440 + T)
+    _check_nc_bwd("mlp", w, make_inputs(w), with_dw, seed=T, rates=rates, loss=loss)
+
+
+def test_mlp_nc_bwd_matrix_core_per_batch_states():
+    w = workload(4).replace(B=3, H=2, T=70, chunk=70, seed=450)
+    inp = make_inputs(w)
+    rng = np.random.default_rng(6)
+    inp["w1"] = (0.05 * rng.standard_normal((3, 2, 64, 64))).astype(np.float32)
+    inp["w2"] = (0.05 * rng.standard_normal((3, 2, 64, 64))).astype(np.float32)
+    _check_nc_bwd("mlp", w, inp, with_dw=True, rates=True)
+
+
 def test_nc_bwd_per_batch_states():
     w = workload(4).replace(B=3, H=2, T=50, chunk=20, unit_keys=True, eta=0.1, seed=430)
     inp = make_inputs(w)
