@@ -28,7 +28,7 @@
 // S1, S2).  The products with W1, W2 in pass 1 and with W1', W2' in pass 2 take each state as
 // a sum of two bf16 parts (hi + lo): dq passes through the roundings of both, and with one
 // part each its element-wise error reached 2.2e-2 of max|dq| over the 384 vision sequences
-// (1.6e-2 with two; a numpy emulation of this kernel's rounding points reproduces both).
+// (1.6e-2 with two; a numpy emulation of this kernel's rounding points reproduced both).
 // Below 16 tokens the sums are too short to average the roundings out and the vector-ALU
 // kernel serves.  Every per-tile quantity is
 // formed transposed (rows: hidden or feature index, columns: tokens), so each lane holds
