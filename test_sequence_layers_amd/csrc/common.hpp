@@ -217,6 +217,17 @@ hipError_t launch_linear_bwd_mfma(const LinearArgs& fwd, const LinearBwdArgs& a,
 
 // backward of the non-causal layers (vector ALUs; linear or SiLU MLP, any chunk / epochs)
 size_t nc_bwd_workspace_floats(bool mlp, int B, int H, int T, int d, int h, int chunk, int epochs);
+// matrix-core backward of the non-causal linear layer for one full-batch step (d = 64,
+// 16 <= T <= 256, bf16 I/O); no workspace
+bool linear_nc_bwd_mfma_supported(const void* q, const void* k, const void* v, const void* dz,
+                                  const float* w0, long long w_batch_stride, const float* dw_out,
+                                  const void* dq, const void* dk, const void* dv, const float* dw0,
+                                  int T, int d, int chunk, int epochs, bool bf16_io);
+hipError_t launch_linear_nc_bwd_mfma(const void* q, const void* k, const void* v, const void* dz,
+                                     const float* w0, long long w_batch_stride, const float* dw_out,
+                                     const float* eta_tok, void* dq, void* dk, void* dv, float* dw0,
+                                     float* deta_tok, int B, int H, int T, float eta, int dot_loss,
+                                     hipStream_t s);
 // matrix-core backward of the non-causal MLP for one full-batch step (d = hidden = 64, T <= 256,
 // bf16 I/O); no workspace
 bool mlp_nc_bwd_mfma_supported(const void* q, const void* k, const void* v, const void* dz,

@@ -1,5 +1,6 @@
-// Backward pass of the non-causal TTT-MLP layer on the gfx950 matrix cores, for one
-// full-batch step: f(k) = W2 SiLU(W1 k), d = 64, hidden 64, at most 256 tokens, bf16
+// Backward pass of the non-causal TTT layers on the gfx950 matrix cores, for one full-batch
+// step (the linear inner model at the end of this file): f(k) = W2 SiLU(W1 k), d = 64,
+// hidden 64, 16 to 256 tokens, bf16
 // Q/K/V/dZ/dQ/dK/dV, fp32 states and state gradients, reconstruction or negative
 // dot-product loss, scalar rate or per-token rate factors (with their gradient).
 //
@@ -608,6 +609,288 @@ __global__ __launch_bounds__(64 * kWaves) void mlp_nc_bwd_mfma_kernel(NcBwdMfmaA
   }
 }
 
+
+// ---------------------------------------------------------------- linear inner model
+// f(k) = W k, W [i][j] (64 x 64): with R = K W^T - V (or -V), Rt = diag(e) R, G = Rt^T K,
+// W' = W - eta G and Z = Q W'^T, the reverse mode (the same per-token formulas as the
+// vector-ALU kernel) is
+//   queries:  dQ = dZ W',  P = dW_out + dZ^T Q,  S = -eta P;
+//   keys:     dRt = K S^T, dR = diag(e) dRt, de_t = <dRt_t, R_t>, dV = -dR,
+//             dK = Rt S (+ dR W),  dW = P (+ dR^T K)  (the terms in brackets: reconstruction
+//             loss only).
+// Same mapping as the MLP kernel: four waves, three passes over the tiles, W and W' as
+// bf16 hi + lo parts in the products that form W' and dQ.
+constexpr int kLW = 0, kLWlo = kMatB, kLX = 2 * kMatB, kLXlo = 3 * kMatB, kLMatsB = 4 * kMatB;
+
+template <bool kTok, bool kDot>
+__global__ __launch_bounds__(64 * kWaves) void linear_nc_bwd_mfma_kernel(NcBwdMfmaArgs a) {
+  __shared__ __attribute__((aligned(16))) char mats_mem[kLMatsB];
+  __shared__ __attribute__((aligned(16))) char tiles_mem[kWaves * kWaveB];
+  __shared__ __attribute__((aligned(16))) float acc_mem[kD * kAccRow];
+  lds_char* mats = (lds_char*)(mats_mem);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  lds_char* my = (lds_char*)(tiles_mem) + wv * kWaveB;
+  lds_float* acc = (lds_float*)(acc_mem);  // G, then P (+ dW), rows i, cols j
+  const int chain = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int g = lane >> 4, x = lane & 15;
+  const int bi = chain / a.H, hi = chain - bi * a.H;
+  const int T = a.T;
+  const int ntiles = (T + kT - 1) / kT;
+  const float eta = a.eta;
+  const size_t tok0 = static_cast<size_t>(chain) * static_cast<size_t>(T) * kD;
+  const char* q = reinterpret_cast<const char*>(static_cast<const bf16*>(a.q) + tok0);
+  const char* k = reinterpret_cast<const char*>(static_cast<const bf16*>(a.k) + tok0);
+  const char* v = reinterpret_cast<const char*>(static_cast<const bf16*>(a.v) + tok0);
+  const char* dz = reinterpret_cast<const char*>(static_cast<const bf16*>(a.dz) + tok0);
+  const char* dq = reinterpret_cast<const char*>(static_cast<bf16*>(a.dq) + tok0);
+  const char* dk = reinterpret_cast<const char*>(static_cast<bf16*>(a.dk) + tok0);
+  const char* dv = reinterpret_cast<const char*>(static_cast<bf16*>(a.dv) + tok0);
+  const float* etok = kTok ? a.eta_tok + static_cast<size_t>(chain) * T : nullptr;
+  float* detok = kTok && a.deta_tok ? a.deta_tok + static_cast<size_t>(chain) * T : nullptr;
+  const size_t dd = static_cast<size_t>(kD) * kD;
+  const float* wg = a.w1 + bi * a.w_batch_stride + static_cast<long long>(hi) * dd;
+  const float* up = a.dw1_out ? a.dw1_out + static_cast<size_t>(chain) * dd : nullptr;
+  const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  constexpr int kPer = kD * kD / 4 / (64 * kWaves);
+  typedef __attribute__((address_space(3))) float4_t lds_f4;
+
+  // ---- W as bf16 hi + lo; zero the accumulator ----
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int p = tid + i * 64 * kWaves, r = p >> 4, c = 4 * (p & 15);
+    u32x2 h, l;
+    split4(*reinterpret_cast<const float4_t*>(wg + r * kD + c), h, l);
+    lds_st<u32x2>(mats + kLW + sw(r, c), h);
+    lds_st<u32x2>(mats + kLWlo + sw(r, c), l);
+    *reinterpret_cast<lds_f4*>(acc + r * kAccRow + c) = zero;
+  }
+  __syncthreads();
+  const lds_char* mW = mats + kLW;
+  const lds_char* mWlo = mats + kLWlo;
+
+  // acc += the four waves' tiles (rows 16 rt + 4 g + e, cols 16 ct + x); see the MLP kernel
+  auto reduce = [&](const float4_t (&t)[4][4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int f = 0; f < 16; ++f) reinterpret_cast<lds_f4*>(my)[f * 64 + lane] = t[f >> 2][f & 3];
+    __syncthreads();
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const int f = 4 * wv + ct;
+      float4_t sum = zero;
+#pragma unroll
+      for (int w2 = 0; w2 < kWaves; ++w2)
+        sum += reinterpret_cast<const lds_f4*>((lds_char*)(tiles_mem) + w2 * kWaveB)[f * 64 + lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[(16 * wv + 4 * g + e) * kAccRow + 16 * ct + x] += sum[e];
+    }
+    __syncthreads();
+  };
+  // R^T (rows i, cols t) = W K^T - V^T (or -V^T); Rt rows to my + kRt
+  auto fwd_r = [&](float4_t (&r)[4], float et, auto split_c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      r[it] = zero;
+      if constexpr (!kDot) {
+        r[it] = mm(mW, 16 * it, my + kIn1, 0, g, x, zero);
+        if constexpr (decltype(split_c)::value) r[it] = mm(mWlo, 16 * it, my + kIn1, 0, g, x, r[it]);
+      }
+      r[it] -= unpack4(lds_ld<u32x2>(my + kIn2 + sw(x, 16 * it + 4 * g)));
+      lds_st<u32x2>(my + kRt + sw(x, 16 * it + 4 * g), pack4(r[it] * et));
+    }
+  };
+
+  // ================= pass 1 (keys): G = Rt^T K
+  {
+    float4_t gs[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) gs[i][j] = zero;
+    In cur = load_in<kTok>(k, v, etok, wv, T, lane);
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int tt = wv + kWaves * i;
+      put_in(cur, my + kIn1, my + kIn2, lane);
+      const In nxt = load_in<kTok>(k, v, etok, tt + kWaves, T, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      if (tt < ntiles) {
+        float4_t r[4];
+        fwd_r(r, cur.e, std::true_type{});
+        bf16x8_t kop[4];
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) kop[jt] = tokop(my + kIn1, 16 * jt, g, x);
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const bf16x8_t rop = tokop(my + kRt, 16 * it, g, x);
+#pragma unroll
+          for (int jt = 0; jt < 4; ++jt) gs[it][jt] = mfma(rop, kop[jt], gs[it][jt]);
+        }
+      }
+      cur = nxt;
+    }
+    reduce(gs);
+  }
+  // ---- W' = W - eta G (bf16 hi + lo); the accumulator restarts from the upstream gradient ----
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int p = tid + i * 64 * kWaves, r = p >> 4, c = 4 * (p & 15);
+    auto* a1 = reinterpret_cast<lds_f4*>(acc + r * kAccRow + c);
+    u32x2 h, l;
+    split4(*reinterpret_cast<const float4_t*>(wg + r * kD + c) - eta * *a1, h, l);
+    lds_st<u32x2>(mats + kLX + sw(r, c), h);
+    lds_st<u32x2>(mats + kLXlo + sw(r, c), l);
+    *a1 = up ? *reinterpret_cast<const float4_t*>(up + r * kD + c) : zero;
+  }
+  __syncthreads();
+
+  // ================= pass 2 (queries): dQ = dZ W', P += dZ^T Q
+  {
+    const lds_char* mWp = mats + kLX;
+    const lds_char* mWplo = mats + kLXlo;
+    float4_t ps[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ps[i][j] = zero;
+    In cur = load_in<false>(q, dz, nullptr, wv, T, lane);
+    u32x2 dqv[4];
+    int pend = -1;
+    auto store_dq = [&](int tt) __attribute__((always_inline)) {
+      const __amdgpu_buffer_rsrc_t rd = rsrc(dq + tt * kTileB, T * kRow - tt * kTileB);
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)
+        __builtin_amdgcn_raw_buffer_store_b64(dqv[jt], rd, x * kRow + 2 * (16 * jt + 4 * g), 0, 0);
+    };
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int tt = wv + kWaves * i;
+      put_in(cur, my + kIn1, my + kIn2, lane);  // Q, dZ
+      if (pend >= 0) store_dq(pend);
+      pend = -1;
+      const In nxt = load_in<false>(q, dz, nullptr, tt + kWaves, T, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      if (tt < ntiles) {
+        // dQ^T (rows j, cols t) = sum_i W'[i][j] dZ[t][i]
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt)
+          dqv[jt] = pack4(mm_t(mWplo, 16 * jt, my + kIn2, 0, g, x, mm_t(mWp, 16 * jt, my + kIn2, 0, g, x, zero)));
+        pend = tt;
+        // P (rows i, cols j) += dZ^T Q
+        bf16x8_t qop[4];
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) qop[jt] = tokop(my + kIn1, 16 * jt, g, x);
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const bf16x8_t zop = tokop(my + kIn2, 16 * it, g, x);
+#pragma unroll
+          for (int jt = 0; jt < 4; ++jt) ps[it][jt] = mfma(zop, qop[jt], ps[it][jt]);
+        }
+      }
+      cur = nxt;
+    }
+    if (pend >= 0) store_dq(pend);
+    reduce(ps);
+  }
+  // ---- S = -eta P (bf16); the accumulator keeps P ----
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int p = tid + i * 64 * kWaves, r = p >> 4, c = 4 * (p & 15);
+    lds_st<u32x2>(mats + kLX + sw(r, c), pack4(-eta * *reinterpret_cast<lds_f4*>(acc + r * kAccRow + c)));
+  }
+  __syncthreads();
+
+  // ================= pass 3 (keys): dK, dV, de, dW += dR^T K
+  {
+    const lds_char* mS = mats + kLX;
+    float4_t hs[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) hs[i][j] = zero;
+    In cur = load_in<kTok>(k, v, etok, wv, T, lane);
+    u32x2 dkv[4], dvv[4];
+    float dev = 0.0f;
+    int pend = -1;
+    auto store_out = [&](int tt) __attribute__((always_inline)) {
+      const int off = tt * kTileB, left = T * kRow - off;
+      const __amdgpu_buffer_rsrc_t rk = rsrc(dk + off, left), rv = rsrc(dv + off, left);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        __builtin_amdgcn_raw_buffer_store_b64(dkv[c], rk, x * kRow + 2 * (16 * c + 4 * g), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(dvv[c], rv, x * kRow + 2 * (16 * c + 4 * g), 0, 0);
+      }
+      if (kTok && detok) {  // the four lane groups store the same value
+        const __amdgpu_buffer_rsrc_t re = rsrc(detok + tt * kT, 4 * (T - tt * kT));
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, dev), re, 4 * x, 0, 0);
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int tt = wv + kWaves * i;
+      put_in(cur, my + kIn1, my + kIn2, lane);  // K, V
+      if (pend >= 0) store_out(pend);
+      pend = -1;
+      const In nxt = load_in<kTok>(k, v, etok, tt + kWaves, T, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      if (tt < ntiles) {
+        const float et = cur.e;
+        float4_t r[4];
+        fwd_r(r, et, std::false_type{});
+        // dRt^T (rows i, cols t) = sum_j S[i][j] K[t][j]; de; dR = e dRt; dV = -dR
+        float dpart = 0.0f;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const float4_t drt = mm(mS, 16 * it, my + kIn1, 0, g, x, zero);
+          if constexpr (kTok) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dpart += drt[e] * r[it][e];
+          }
+          const float4_t dr = drt * et;
+          dvv[it] = pack4(-dr);
+          if constexpr (!kDot) lds_st<u32x2>(my + kDR + sw(x, 16 * it + 4 * g), pack4(dr));
+        }
+        if constexpr (kTok) {
+          dpart += __shfl_xor(dpart, 16, 64);
+          dpart += __shfl_xor(dpart, 32, 64);
+          dev = dpart;
+        }
+        // dK^T (rows j, cols t) = sum_i S[i][j] Rt[t][i] (+ sum_i W[i][j] dR[t][i])
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          float4_t dkt = mm_t(mS, 16 * jt, my + kRt, 0, g, x, zero);
+          if constexpr (!kDot) dkt = mm_t(mW, 16 * jt, my + kDR, 0, g, x, dkt);
+          dkv[jt] = pack4(dkt);
+        }
+        pend = tt;
+        // dW (rows i, cols j) += dR^T K
+        if constexpr (!kDot) {
+          bf16x8_t kop[4];
+#pragma unroll
+          for (int jt = 0; jt < 4; ++jt) kop[jt] = tokop(my + kIn1, 16 * jt, g, x);
+#pragma unroll
+          for (int it = 0; it < 4; ++it) {
+            const bf16x8_t dop = tokop(my + kDR, 16 * it, g, x);
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt) hs[it][jt] = mfma(dop, kop[jt], hs[it][jt]);
+          }
+        }
+      }
+      cur = nxt;
+    }
+    if (pend >= 0) store_out(pend);
+    reduce(hs);
+  }
+  // ---- dW0 = P + dR^T K ----
+  float* dw0 = a.dw1 + static_cast<size_t>(chain) * dd;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int p = tid + i * 64 * kWaves, r = p >> 4, c = 4 * (p & 15);
+    *reinterpret_cast<float4_t*>(dw0 + r * kD + c) = *reinterpret_cast<lds_f4*>(acc + r * kAccRow + c);
+  }
+}
+
 }  // namespace
 
 bool mlp_nc_bwd_mfma_supported(const void* q, const void* k, const void* v, const void* dz,
@@ -623,6 +906,36 @@ bool mlp_nc_bwd_mfma_supported(const void* q, const void* k, const void* v, cons
   // roundings (a single token's rank-1 update passes them on whole); the fp32 path serves those
   return bf16_io && d == kD && h == kD && T >= kT && T <= kMaxTokens && chunk >= T && epochs == 1 &&
          aligned;
+}
+
+bool linear_nc_bwd_mfma_supported(const void* q, const void* k, const void* v, const void* dz,
+                                  const float* w0, long long w_batch_stride, const float* dw_out,
+                                  const void* dq, const void* dk, const void* dv, const float* dw0,
+                                  int T, int d, int chunk, int epochs, bool bf16_io) {
+  auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  const bool aligned = al(q) && al(k) && al(v) && al(dz) && al(dq) && al(dk) && al(dv) && al(w0) &&
+                       al(dw0) && (!dw_out || al(dw_out)) && (w_batch_stride % 4) == 0;
+  return bf16_io && d == kD && T >= kT && T <= kMaxTokens && chunk >= T && epochs == 1 && aligned;
+}
+
+hipError_t launch_linear_nc_bwd_mfma(const void* q, const void* k, const void* v, const void* dz,
+                                     const float* w0, long long w_batch_stride, const float* dw_out,
+                                     const float* eta_tok, void* dq, void* dk, void* dv, float* dw0,
+                                     float* deta_tok, int B, int H, int T, float eta, int dot_loss,
+                                     hipStream_t s) {
+  const long long nchains = static_cast<long long>(B) * H;
+  if (nchains > 0x7fffffffLL || T <= 0 || T > kMaxTokens) return hipErrorInvalidValue;
+  NcBwdMfmaArgs a{q, k, v, dz, w0, nullptr, w_batch_stride, dw_out, nullptr, eta_tok, dq, dk, dv,
+                  dw0, nullptr, deta_tok, B, H, T, eta};
+  const dim3 grid(static_cast<unsigned>(nchains)), block(64 * kWaves);
+  auto run = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, block, 0, s, a);
+    return hipGetLastError();
+  };
+  if (eta_tok && dot_loss) return run(linear_nc_bwd_mfma_kernel<true, true>);
+  if (eta_tok) return run(linear_nc_bwd_mfma_kernel<true, false>);
+  if (dot_loss) return run(linear_nc_bwd_mfma_kernel<false, true>);
+  return run(linear_nc_bwd_mfma_kernel<false, false>);
 }
 
 hipError_t launch_mlp_nc_bwd_mfma(const void* q, const void* k, const void* v, const void* dz,

@@ -573,6 +573,14 @@ int nc_bwd(const char* fn, bool mlp, const void* q, const void* k, const void* v
     if (rc != TTT_OK || !mlp) return rc;
     return copy_state(dw2, dw2_out, st, B, H, n1, s);
   }
+  if (!mlp && ttt::linear_nc_bwd_mfma_supported(q, k, v, dz, w1, w_batch_stride, dw1_out, dq, dk, dv,
+                                                dw1, T, d, chunk, epochs, io_dtype == TTT_BF16)) {
+    hipError_t e = ttt::launch_linear_nc_bwd_mfma(q, k, v, dz, w1, w_batch_stride, dw1_out, eta_tok,
+                                                 dq, dk, dv, dw1, deta_tok, B, H, T, eta,
+                                                 loss == TTT_LOSS_DOT ? 1 : 0, s);
+    if (e != hipSuccess) return hip_fail(e, "non-causal backward launch");
+    return TTT_OK;
+  }
   if (mlp && ttt::mlp_nc_bwd_mfma_supported(q, k, v, dz, w1, w2, w_batch_stride, dw1_out, dw2_out, dq,
                                              dk, dv, dw1, dw2, T, d, dh, chunk, epochs,
                                              io_dtype == TTT_BF16)) {

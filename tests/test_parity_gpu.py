@@ -836,6 +836,23 @@ def test_mlp_nc_bwd_matrix_core_cases(T, rates, loss, with_dw):
     _check_nc_bwd("mlp", w, make_inputs(w), with_dw, seed=T, rates=rates, loss=loss)
 
 
+@pytest.mark.parametrize("T,rates,loss,with_dw", [
+    (1, True, "mse", True), (16, False, "dot", True), (45, True, "mse", False),
+    (128, True, "dot", False), (256, False, "mse", True)])
+def test_linear_nc_bwd_matrix_core_cases(T, rates, loss, with_dw):
+    # one full-batch step at d = 64, bf16: the matrix-core backward for 16 <= T <= 256
+    # (T = 1 checks that shorter sequences go to the fp32 kernel)
+    w = workload(4).replace(kind="linear", h=0, B=2, H=3, T=T, chunk=T, seed=460 + T)
+    _check_nc_bwd("linear", w, make_inputs(w), with_dw, seed=T, rates=rates, loss=loss)
+
+
+def test_linear_nc_bwd_matrix_core_per_batch_state():
+    w = workload(4).replace(kind="linear", h=0, B=3, H=2, T=70, chunk=70, seed=470)
+    inp = make_inputs(w)
+    inp["w0"] = (0.05 * np.random.default_rng(8).standard_normal((3, 2, 64, 64))).astype(np.float32)
+    _check_nc_bwd("linear", w, inp, with_dw=True, rates=True)
+
+
 def test_mlp_nc_bwd_matrix_core_per_batch_states():
     w = workload(4).replace(B=3, H=2, T=70, chunk=70, seed=450)
     inp = make_inputs(w)
