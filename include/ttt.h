@@ -288,9 +288,9 @@ int ttt_mlp_ln_bwd(const void* q, const void* k, const void* v,
  * TTT_LOSS_MSE or TTT_LOSS_DOT, both dtypes, on the vector ALUs (one workgroup per sequence).
  * The call keeps every step-start state and fp32 accumulators of dk, dv and deta_tok in a
  * stream-ordered workspace of B*H*((S+1)*state + 2*T*d + T)*4 bytes, S = ceil(T/chunk)*epochs
- * steps and state = d*d (linear) or 2*d*dh (MLP) floats.  One exception: the MLP with
- * d = dh = 64, bf16, one full-batch step (chunk >= T, epochs = 1), 16 <= T <= 256 and
- * 16-byte aligned q, k, v, dz, dq, dk, dv, states and state gradients (w_batch_stride a
+ * steps and state = d*d (linear) or 2*d*dh (MLP) floats.  One exception: d = 64 (and dh = 64
+ * for the MLP), bf16, one full-batch step (chunk >= T, epochs = 1), 16 <= T <= 256 and
+ * 16-byte aligned q, k, v, dz, dq, dk, dv, states and state gradients (batch stride a
  * multiple of 4) runs on the matrix cores with no workspace.  T = 0 copies the upstream state
  * gradients (zeros without them).
  */
