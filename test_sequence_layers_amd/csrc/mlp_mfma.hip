@@ -31,8 +31,11 @@
 // directly; the backward pass contracts it over outputs, so each chunk the wave also
 // writes its chunk-start W2 in bf16 to LDS (rows: outputs) and reads the operand back with
 // the transposing LDS read.  The only cross-wave sums, O = A W2^T and Z, go through LDS.
-// Every product is one v_mfma_f32_16x16x32_bf16 per 16 x 16 x 32 block; products over the
-// 16 tokens of a chunk use the same instruction with the upper half of one operand zero.
+// Every product is one v_mfma_f32_16x16x32_bf16 per 16 x 16 x 32 block.  Products over the
+// 16 tokens of a chunk use the same instruction with the upper half of one operand zero where
+// they share an accumulator with K = 32 products, and v_mfma_f32_16x16x16_bf16 where the
+// accumulator is theirs alone (the state updates, the transposes by I): an accumulator is
+// only ever written by one of the two opcodes.
 
 // Layout conventions (C layout of a 16 x 16 tile: lane (g, n) = (lane / 16, lane % 16)
 // holds rows 4g + e, e = 0..3, of column n):
@@ -90,6 +93,18 @@ __device__ __forceinline__ bf16x8_t pad_op(const float4_t& x, float s = 1.0f) {
 __device__ __forceinline__ float4_t mfma(const bf16x8_t& a, const bf16x8_t& b, const float4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+// Products over the 16 tokens of a chunk whose accumulator no K = 32 product touches (the
+// state updates, the transposes by I): one 16x16x16 MFMA on the K = 16 operand itself (the
+// first two dwords of its padded form, same contraction index 4 g + s).
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4_t mfma16(const u32x2& a, const u32x2& b, const float4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, a),
+                                                    __builtin_bit_cast(bf16x4_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ u32x2 k16(const float4_t& x) {
+  return u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
+}
+__device__ __forceinline__ bf16x8_t pad2(const u32x2& x) { return op4(x.x, x.y, 0u, 0u); }
 
 __device__ __forceinline__ float sigmoid_f(float u) { return sigmoidf_(u); }
 
@@ -346,8 +361,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   // ---- constants ----
   const uint32_t one = 0x3F80u;  // bf16 1.0
-  const bf16x8_t eye = op4((4 * g + 0 == n ? one : 0u) | (4 * g + 1 == n ? one << 16 : 0u),
-                           (4 * g + 2 == n ? one : 0u) | (4 * g + 3 == n ? one << 16 : 0u), 0u, 0u);
+  const u32x2 eye = {(4 * g + 0 == n ? one : 0u) | (4 * g + 1 == n ? one << 16 : 0u),
+                     (4 * g + 2 == n ? one : 0u) | (4 * g + 3 == n ? one << 16 : 0u)};
   const bool keep[4] = {4 * g + 0 <= n, 4 * g + 1 <= n, 4 * g + 2 <= n, 4 * g + 3 <= n};
   Offsets o;
   o.row = n * 128 + 32 * g;
@@ -418,13 +433,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         sd[aa][e] = dv;
       }
     }
-    // A as padded K = 16 operands (rows t); A^T (rows hidden) by an MFMA with I
-    bf16x8_t ab[kHT];
+    // A as K = 16 operands (rows t); A^T (rows hidden) by an MFMA with I
+    u32x2 ab[kHT];
     float4_t actT[kHT];
 #pragma unroll
     for (int aa = 0; aa < kHT; ++aa) {
-      ab[aa] = pad_op(act[aa]);
-      actT[aa] = mfma(ab[aa], eye, zero);
+      ab[aa] = k16(act[aa]);
+      actT[aa] = mfma16(ab[aa], eye, zero);
     }
 
     // bf16 chunk-start W2 as A operands over the wave's hidden units (rows output
@@ -491,12 +506,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     // -eta R tiles as padded K = 16 operands in the C layout (rows t = 4 g + 0..3 of column
     // 16 it + n), and as row operands over outputs (m = t, k = outputs 32 h + 8 g + 0..7)
-    bf16x8_t rb[4];
+    u32x2 rb[4];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const u32x2 x = lds_load<u32x2>(rtb, ((16 * it + n) * kTRow + 4 * g) * 2);
-      rb[it] = op4(x.x, x.y, 0u, 0u);
-    }
+    for (int it = 0; it < 4; ++it) rb[it] = lds_load<u32x2>(rtb, ((16 * it + n) * kTRow + 4 * g) * 2);
     bf16x8_t rrow[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) rrow[h] = bf(lds_load<u32x4>(rrb, (n * kRRow + 32 * h + 8 * g) * 2));
@@ -504,7 +516,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // operand W2[32 h + 8 g + s][h0 + 16 aa + n] comes from two transposing reads of the LDS
     // copy: lane 4 s' + q of group g fetches row 32 h + 8 g + 4 half + s', hidden
     // 16 aa + 4 q .. + 3 of the wave's slice.
-    bf16x8_t dub[kHT];
+    u32x2 dub[kHT];
 #pragma unroll
     for (int aa = 0; aa < kHT; ++aa) {
       float4_t da = zero;
@@ -515,7 +527,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const u32x4 w2k = {lo.x, lo.y, hi2.x, hi2.y};
         da = mfma(rrow[h], bf(w2k), da);
       }
-      dub[aa] = pad_op(da * sd[aa]);
+      dub[aa] = k16(da * sd[aa]);
     }
 
     // ---- outputs (use the chunk-start state) ----
@@ -532,7 +544,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       for (int aa = 0; aa < kHT; ++aa) {
         float4_t u = mfma(w1b[0][aa], qb0, zero);
         u = mfma(w1b[1][aa], qb1, u);
-        u = mfma(dub[aa], ptb, u);
+        u = mfma(pad2(dub[aa]), ptb, u);
 #pragma unroll
         for (int e = 0; e < 4; ++e) u[e] = act_only<kPaper>(u[e]);
         aqT[aa] = u;
@@ -547,7 +559,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
         float4_t zt = mfma(bf(w2op[it]), aqb, zero);
-        zt = mfma(rb[it], gtb, zt);
+        zt = mfma(pad2(rb[it]), gtb, zt);
         lds_store<float4_t>(zpart, ((wv * kB + n) * kRow + 16 * it + 4 * g) * 4, zt);
       }
     }
@@ -558,25 +570,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int jb = 0; jb < 4; ++jb) {
       const int h = jb >> 1;
       const uint32_t sel = (jb & 1) ? kHi : kLo;
-      const bf16x8_t kt = op4(__builtin_amdgcn_perm(cur.kt[1][h], cur.kt[0][h], sel),
-                              __builtin_amdgcn_perm(cur.kt[3][h], cur.kt[2][h], sel), 0u, 0u);
+      const u32x2 kt = {__builtin_amdgcn_perm(cur.kt[1][h], cur.kt[0][h], sel),
+                        __builtin_amdgcn_perm(cur.kt[3][h], cur.kt[2][h], sel)};
 #pragma unroll
-      for (int aa = 0; aa < kHT; ++aa) st.w1t[jb][aa] = mfma(kt, dub[aa], st.w1t[jb][aa]);
+      for (int aa = 0; aa < kHT; ++aa) st.w1t[jb][aa] = mfma16(kt, dub[aa], st.w1t[jb][aa]);
     }
     // W2^T += A^T (-eta R): A-operand = A tile aa (rows t), B = -eta R tile it
 #pragma unroll
     for (int aa = 0; aa < kHT; ++aa)
 #pragma unroll
-      for (int it = 0; it < 4; ++it) st.w2t[aa][it] = mfma(ab[aa], rb[it], st.w2t[aa][it]);
+      for (int it = 0; it < 4; ++it) st.w2t[aa][it] = mfma16(ab[aa], rb[it], st.w2t[aa][it]);
     qv_prev = cur.qv;
   };
 
+  // two operand buffers in turn (a copy of a buffer whose loads are in flight would wait
+  // for them)
   ChunkIn ca, cb;
   load_chunk<kPaper>(ca, q, k, v, etok, 0, seq_bytes, o);
-  for (int c = 0; c < nchunks; ++c) {
+  int c = 0;
+  for (; c + 1 < nchunks; c += 2) {
     step(ca, cb, c);
-    ca = cb;
+    step(cb, ca, c + 1);
   }
+  if (c < nchunks) step(ca, cb, c);
   barrier();
   if (!kHist && nchunks > 0) reduce_store_z(nchunks - 1);
 
