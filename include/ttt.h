@@ -53,7 +53,9 @@
  *                          non-finite eta, a misaligned eta_tok, an unknown dtype or loss,
  *                          epochs < 1 (or > 1 with causal = 1), or a size overflow;
  *       TTT_E_UNSUPPORTED  a valid combination with no kernel (see each function);
- *       TTT_E_HIP          a HIP runtime error (launch failure, workspace allocation).
+ *       TTT_E_HIP          a HIP runtime error (launch failure, workspace allocation);
+ *       TTT_E_NONFINITE    only with the finite check on (ttt_set_check_finite below): the
+ *                          call ran and one of its outputs holds a NaN or an infinity.
  *     ttt_last_error() returns the calling thread's message for the last non-OK status.
  */
 #ifndef TTT_H_
@@ -65,7 +67,7 @@ extern "C" {
 
 typedef struct ihipStream_t* ttt_stream_t; /* identical to hipStream_t */
 
-enum { TTT_OK = 0, TTT_E_INVALID = -1, TTT_E_UNSUPPORTED = -2, TTT_E_HIP = -3 };
+enum { TTT_OK = 0, TTT_E_INVALID = -1, TTT_E_UNSUPPORTED = -2, TTT_E_HIP = -3, TTT_E_NONFINITE = -4 };
 enum { TTT_F32 = 0, TTT_BF16 = 1 };
 enum { TTT_LOSS_MSE = 0, TTT_LOSS_DOT = 1 };
 
@@ -312,6 +314,22 @@ int ttt_mlp_nc_bwd(const void* q, const void* k, const void* v,
 /* Message for the calling thread's last non-OK status ("" if none).  Owned by the library;
    valid until the thread's next call into it. */
 const char* ttt_last_error(void);
+
+/*
+ * Finite check of the outputs, for debugging (no page describes it; a layer whose inner
+ * updates diverge, as the raw-key MLP workloads do at large rates, fills its outputs with
+ * NaN or infinities, and this names where).  When it is on, every call that would return
+ * TTT_OK then scans each of its outputs on its stream (z, final states, gradients; token
+ * outputs only when T > 0), waits for the stream, and returns TTT_E_NONFINITE with the
+ * first output holding a NaN or an infinity named in ttt_last_error().  Calls with the
+ * check on are therefore synchronous, and calls with it on that overlap on one GPU share
+ * that GPU's flags and can report each other's outputs.  Off by default; a non-empty
+ * environment variable TTT_CHECK_FINITE other than "0" turns it on for the process.
+ * ttt_set_check_finite(on) sets it for the process (nonzero = on) and returns the previous
+ * setting; ttt_get_check_finite() returns the current one (1 or 0).  Neither touches the GPU.
+ */
+int ttt_set_check_finite(int on);
+int ttt_get_check_finite(void);
 
 /* ABI version of this header (incremented on any incompatible change). */
 int ttt_abi_version(void);

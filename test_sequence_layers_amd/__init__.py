@@ -13,13 +13,16 @@ from ._binding import (  # noqa: F401
     TTT_BF16,
     TTT_E_HIP,
     TTT_E_INVALID,
+    TTT_E_NONFINITE,
     TTT_E_UNSUPPORTED,
     TTT_F32,
     TTT_OK,
     TTTError,
     delta_rule_fwd,
+    get_check_finite,
     last_error,
     load_library,
+    set_check_finite,
     ttt_linear_bwd,
     ttt_linear_bwd_noalloc,
     ttt_linear_fwd,

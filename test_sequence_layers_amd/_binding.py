@@ -12,7 +12,7 @@ import threading
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libttt.so")
 
-TTT_OK, TTT_E_INVALID, TTT_E_UNSUPPORTED, TTT_E_HIP = 0, -1, -2, -3
+TTT_OK, TTT_E_INVALID, TTT_E_UNSUPPORTED, TTT_E_HIP, TTT_E_NONFINITE = 0, -1, -2, -3, -4
 TTT_F32, TTT_BF16 = 0, 1
 
 _lib = None
@@ -50,6 +50,8 @@ SIGNATURES = {
                             _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _i, _i, _vp]),
     "ttt_last_error": (ctypes.c_char_p, []),
     "ttt_abi_version": (_i, []),
+    "ttt_set_check_finite": (_i, [_i]),
+    "ttt_get_check_finite": (_i, []),
 }
 
 
@@ -79,6 +81,17 @@ def load_library(path: str = LIB_PATH):
 
 def last_error() -> str:
     return load_library().ttt_last_error().decode()
+
+
+def set_check_finite(on: bool) -> bool:
+    """Switch the library's finite check of every call's outputs on or off (debugging; calls
+    then wait for their stream and fail with TTT_E_NONFINITE on a NaN or an infinity).
+    Returns the previous setting."""
+    return bool(load_library().ttt_set_check_finite(1 if on else 0))
+
+
+def get_check_finite() -> bool:
+    return bool(load_library().ttt_get_check_finite())
 
 
 def _check(rc):

@@ -253,4 +253,17 @@ hipError_t launch_nc_bwd(bool mlp, const void* q, const void* k, const void* v, 
 hipError_t launch_copy_state(float* dst, const float* src, long long batch_stride, int B, int H,
                              size_t per_head, hipStream_t s);
 
+// Debug check for non-finite outputs: one entry per output buffer (null or empty entries are
+// skipped); host_flags[i] (kMaxCheckedOutputs entries) receives 1 if buffer i holds a NaN or
+// an infinity.  Enqueues on s and then waits for s.
+constexpr int kMaxCheckedOutputs = 8;
+struct CheckedOutput {
+  const char* name;
+  const void* ptr;
+  long long count;     // elements
+  int bytes_per_elem;  // 2 (bf16) or 4 (float32)
+};
+hipError_t check_finite_outputs(const CheckedOutput* outs, int nouts, hipStream_t s,
+                                unsigned int* host_flags);
+
 }  // namespace ttt

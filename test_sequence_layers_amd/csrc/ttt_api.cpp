@@ -6,6 +6,10 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <atomic>
+#include <initializer_list>
 #include <mutex>
 #include <string>
 
@@ -350,17 +354,53 @@ int linear_bwd(const char* fn, const void* q, const void* k, const void* v, cons
   return TTT_OK;
 }
 
+// ---- finite check of the outputs (debugging) ----
+// -1: not yet read from the environment (TTT_CHECK_FINITE), else 0 / 1
+std::atomic<int> g_check_finite{-1};
+
+bool check_finite_on() {
+  int v = g_check_finite.load(std::memory_order_relaxed);
+  if (v < 0) {
+    const char* env = std::getenv("TTT_CHECK_FINITE");
+    const int want = (env != nullptr && env[0] != '\0' && std::strcmp(env, "0") != 0) ? 1 : 0;
+    g_check_finite.compare_exchange_strong(v, want, std::memory_order_relaxed);
+    v = g_check_finite.load(std::memory_order_relaxed);
+  }
+  return v == 1;
+}
+
+using Out = ttt::CheckedOutput;
+
+// rc of the call; when it is TTT_OK and the check is on, the call's outputs are scanned on
+// its stream (which is then waited for) and TTT_E_NONFINITE names the first output holding
+// a NaN or an infinity.
+int finite_outputs(int rc, const char* fn, ttt_stream_t stream, std::initializer_list<Out> outs) {
+  if (rc != TTT_OK || !check_finite_on()) return rc;
+  unsigned int flags[ttt::kMaxCheckedOutputs] = {};
+  const int n = static_cast<int>(outs.size());
+  const hipError_t e = ttt::check_finite_outputs(outs.begin(), n, reinterpret_cast<hipStream_t>(stream), flags);
+  if (e != hipSuccess) return fail(TTT_E_HIP, "%s finite check: %s", fn, hipGetErrorString(e));
+  for (int i = 0; i < n; ++i)
+    if (flags[i]) return fail(TTT_E_NONFINITE, "%s: non-finite values in %s", fn, outs.begin()[i].name);
+  return TTT_OK;
+}
+
+// element counts: token tensors (none when T = 0, where they are left untouched) and states
+long long tok(int B, int H, int T, int d) { return static_cast<long long>(B) * H * T * d; }
+long long per_seq(int B, int H, long long n) { return static_cast<long long>(B) * H * n; }
+int io_bytes(int io_dtype) { return io_dtype == TTT_BF16 ? 2 : 4; }
+
 }  // namespace
 
 extern "C" {
 
-int ttt_abi_version(void) { return 11; }
+int ttt_abi_version(void) { return 12; }
 
 const char* ttt_last_error(void) { return g_last_error.c_str(); }
 
-int delta_rule_fwd(const void* q, const void* k, const void* v, const float* w0,
-                   long long w0_batch_stride, void* z, float* w_out, int B, int H, int T,
-                   int d, float eta, const float* eta_tok, int io_dtype, ttt_stream_t stream) {
+static int impl_delta_rule_fwd(const void* q, const void* k, const void* v, const float* w0,
+                               long long w0_batch_stride, void* z, float* w_out, int B, int H, int T,
+                               int d, float eta, const float* eta_tok, int io_dtype, ttt_stream_t stream) {
   g_last_error.clear();
   int rc = check_common("delta_rule_fwd", q, k, v, z, B, H, T, d, eta, eta_tok, io_dtype);
   if (rc != TTT_OK) return rc;
@@ -383,32 +423,32 @@ int delta_rule_fwd(const void* q, const void* k, const void* v, const float* w0,
   return TTT_OK;
 }
 
-int ttt_linear_bwd(const void* q, const void* k, const void* v, const float* w0,
-                   long long w0_batch_stride, const void* dz, const float* dw_out, void* dq,
-                   void* dk, void* dv, float* dw0, int B, int H, int T, int d, int chunk,
-                   float eta, const float* eta_tok, float* deta_tok, int loss, int io_dtype,
-                   ttt_stream_t stream) {
+static int impl_ttt_linear_bwd(const void* q, const void* k, const void* v, const float* w0,
+                               long long w0_batch_stride, const void* dz, const float* dw_out, void* dq,
+                               void* dk, void* dv, float* dw0, int B, int H, int T, int d, int chunk,
+                               float eta, const float* eta_tok, float* deta_tok, int loss, int io_dtype,
+                               ttt_stream_t stream) {
   g_last_error.clear();
   return linear_bwd("ttt_linear_bwd", q, k, v, w0, w0_batch_stride, dz, dw_out, dq, dk, dv, dw0, B,
                     H, T, d, chunk, eta, eta_tok, deta_tok, loss, io_dtype, stream, false);
 }
 
-int ttt_linear_bwd_noalloc(const void* q, const void* k, const void* v, const float* w0,
-                           long long w0_batch_stride, const void* dz, const float* dw_out,
-                           void* dq, void* dk, void* dv, float* dw0, int B, int H, int T, int d,
-                           int chunk, float eta, const float* eta_tok, float* deta_tok, int loss,
-                           int io_dtype, ttt_stream_t stream) {
+static int impl_ttt_linear_bwd_noalloc(const void* q, const void* k, const void* v, const float* w0,
+                                       long long w0_batch_stride, const void* dz, const float* dw_out,
+                                       void* dq, void* dk, void* dv, float* dw0, int B, int H, int T, int d,
+                                       int chunk, float eta, const float* eta_tok, float* deta_tok, int loss,
+                                       int io_dtype, ttt_stream_t stream) {
   g_last_error.clear();
   return linear_bwd("ttt_linear_bwd_noalloc", q, k, v, w0, w0_batch_stride, dz, dw_out, dq, dk, dv,
                     dw0, B, H, T, d, chunk, eta, eta_tok, deta_tok, loss, io_dtype, stream, true);
 }
 
-int ttt_linear_ln_bwd(const void* q, const void* k, const void* v, const float* w0,
-                      long long w0_batch_stride, const float* ln_weight, const float* ln_bias,
-                      float ln_eps, const void* dz, const float* dw_out, void* dq, void* dk,
-                      void* dv, float* dw0, float* dln_weight, float* dln_bias, int B, int H,
-                      int T, int d, int chunk, float eta, const float* eta_tok, float* deta_tok,
-                      int loss, int io_dtype, ttt_stream_t stream) {
+static int impl_ttt_linear_ln_bwd(const void* q, const void* k, const void* v, const float* w0,
+                                  long long w0_batch_stride, const float* ln_weight, const float* ln_bias,
+                                  float ln_eps, const void* dz, const float* dw_out, void* dq, void* dk,
+                                  void* dv, float* dw0, float* dln_weight, float* dln_bias, int B, int H,
+                                  int T, int d, int chunk, float eta, const float* eta_tok, float* deta_tok,
+                                  int loss, int io_dtype, ttt_stream_t stream) {
   g_last_error.clear();
   const char* fn = "ttt_linear_ln_bwd";
   int rc = check_ln(fn, ln_weight, ln_bias, ln_eps);
@@ -468,13 +508,13 @@ int ttt_linear_ln_bwd(const void* q, const void* k, const void* v, const float* 
   return TTT_OK;
 }
 
-int ttt_mlp_ln_bwd(const void* q, const void* k, const void* v, const float* w1, const float* w2,
-                   long long w_batch_stride, const float* ln_weight, const float* ln_bias,
-                   float ln_eps, const void* dz, const float* dw1_out, const float* dw2_out,
-                   void* dq, void* dk, void* dv, float* dw1, float* dw2, float* dln_weight,
-                   float* dln_bias, int B, int H, int T, int d, int dh, int chunk, float eta,
-                   const float* eta_tok, float* deta_tok, int loss, int io_dtype,
-                   ttt_stream_t stream) {
+static int impl_ttt_mlp_ln_bwd(const void* q, const void* k, const void* v, const float* w1, const float* w2,
+                               long long w_batch_stride, const float* ln_weight, const float* ln_bias,
+                               float ln_eps, const void* dz, const float* dw1_out, const float* dw2_out,
+                               void* dq, void* dk, void* dv, float* dw1, float* dw2, float* dln_weight,
+                               float* dln_bias, int B, int H, int T, int d, int dh, int chunk, float eta,
+                               const float* eta_tok, float* deta_tok, int loss, int io_dtype,
+                               ttt_stream_t stream) {
   g_last_error.clear();
   const char* fn = "ttt_mlp_ln_bwd";
   int rc = check_ln(fn, ln_weight, ln_bias, ln_eps);
@@ -541,11 +581,11 @@ int ttt_mlp_ln_bwd(const void* q, const void* k, const void* v, const float* w1,
 }
 
 // Shared by ttt_linear_nc_bwd (mlp false: w1 = w0, dw1 = dw0) and ttt_mlp_nc_bwd.
-int nc_bwd(const char* fn, bool mlp, const void* q, const void* k, const void* v, const float* w1,
-           const float* w2, long long w_batch_stride, const void* dz, const float* dw1_out,
-           const float* dw2_out, void* dq, void* dk, void* dv, float* dw1, float* dw2, int B,
-           int H, int T, int d, int dh, int chunk, int epochs, float eta, const float* eta_tok,
-           float* deta_tok, int loss, int io_dtype, ttt_stream_t stream) {
+static int nc_bwd(const char* fn, bool mlp, const void* q, const void* k, const void* v, const float* w1,
+                  const float* w2, long long w_batch_stride, const void* dz, const float* dw1_out,
+                  const float* dw2_out, void* dq, void* dk, void* dv, float* dw1, float* dw2, int B,
+                  int H, int T, int d, int dh, int chunk, int epochs, float eta, const float* eta_tok,
+                  float* deta_tok, int loss, int io_dtype, ttt_stream_t stream) {
   int rc = check_common(fn, q, k, v, dz, B, H, T, d, eta, eta_tok, io_dtype);
   if (rc != TTT_OK) return rc;
   if (loss != TTT_LOSS_MSE && loss != TTT_LOSS_DOT)
@@ -607,34 +647,34 @@ int nc_bwd(const char* fn, bool mlp, const void* q, const void* k, const void* v
   return TTT_OK;
 }
 
-int ttt_linear_nc_bwd(const void* q, const void* k, const void* v, const float* w0,
-                      long long w0_batch_stride, const void* dz, const float* dw_out, void* dq,
-                      void* dk, void* dv, float* dw0, int B, int H, int T, int d, int chunk,
-                      int epochs, float eta, const float* eta_tok, float* deta_tok, int loss,
-                      int io_dtype, ttt_stream_t stream) {
+static int impl_ttt_linear_nc_bwd(const void* q, const void* k, const void* v, const float* w0,
+                                  long long w0_batch_stride, const void* dz, const float* dw_out, void* dq,
+                                  void* dk, void* dv, float* dw0, int B, int H, int T, int d, int chunk,
+                                  int epochs, float eta, const float* eta_tok, float* deta_tok, int loss,
+                                  int io_dtype, ttt_stream_t stream) {
   g_last_error.clear();
   return nc_bwd("ttt_linear_nc_bwd", false, q, k, v, w0, nullptr, w0_batch_stride, dz, dw_out,
                 nullptr, dq, dk, dv, dw0, nullptr, B, H, T, d, 0, chunk, epochs, eta, eta_tok,
                 deta_tok, loss, io_dtype, stream);
 }
 
-int ttt_mlp_nc_bwd(const void* q, const void* k, const void* v, const float* w1, const float* w2,
-                   long long w_batch_stride, const void* dz, const float* dw1_out,
-                   const float* dw2_out, void* dq, void* dk, void* dv, float* dw1, float* dw2,
-                   int B, int H, int T, int d, int dh, int chunk, int epochs, float eta,
-                   const float* eta_tok, float* deta_tok, int loss, int io_dtype,
-                   ttt_stream_t stream) {
+static int impl_ttt_mlp_nc_bwd(const void* q, const void* k, const void* v, const float* w1, const float* w2,
+                               long long w_batch_stride, const void* dz, const float* dw1_out,
+                               const float* dw2_out, void* dq, void* dk, void* dv, float* dw1, float* dw2,
+                               int B, int H, int T, int d, int dh, int chunk, int epochs, float eta,
+                               const float* eta_tok, float* deta_tok, int loss, int io_dtype,
+                               ttt_stream_t stream) {
   g_last_error.clear();
   return nc_bwd("ttt_mlp_nc_bwd", true, q, k, v, w1, w2, w_batch_stride, dz, dw1_out, dw2_out, dq,
                 dk, dv, dw1, dw2, B, H, T, d, dh, chunk, epochs, eta, eta_tok, deta_tok, loss,
                 io_dtype, stream);
 }
 
-int ttt_mlp_bwd(const void* q, const void* k, const void* v, const float* w1, const float* w2,
-                long long w_batch_stride, const void* dz, const float* dw1_out,
-                const float* dw2_out, void* dq, void* dk, void* dv, float* dw1, float* dw2, int B,
-                int H, int T, int d, int dh, int chunk, float eta, const float* eta_tok,
-                float* deta_tok, int loss, int io_dtype, ttt_stream_t stream) {
+static int impl_ttt_mlp_bwd(const void* q, const void* k, const void* v, const float* w1, const float* w2,
+                            long long w_batch_stride, const void* dz, const float* dw1_out,
+                            const float* dw2_out, void* dq, void* dk, void* dv, float* dw1, float* dw2, int B,
+                            int H, int T, int d, int dh, int chunk, float eta, const float* eta_tok,
+                            float* deta_tok, int loss, int io_dtype, ttt_stream_t stream) {
   g_last_error.clear();
   int rc = check_common("ttt_mlp_bwd", q, k, v, dz, B, H, T, d, eta, eta_tok, io_dtype);
   if (rc != TTT_OK) return rc;
@@ -701,20 +741,20 @@ int ttt_mlp_bwd(const void* q, const void* k, const void* v, const float* w1, co
   return TTT_OK;
 }
 
-int ttt_linear_fwd(const void* q, const void* k, const void* v, const float* w0,
-                   long long w0_batch_stride, void* z, float* w_out, int B, int H, int T,
-                   int d, int chunk, int causal, float eta, const float* eta_tok, int loss,
-                   int epochs, int io_dtype, ttt_stream_t stream) {
+static int impl_ttt_linear_fwd(const void* q, const void* k, const void* v, const float* w0,
+                               long long w0_batch_stride, void* z, float* w_out, int B, int H, int T,
+                               int d, int chunk, int causal, float eta, const float* eta_tok, int loss,
+                               int epochs, int io_dtype, ttt_stream_t stream) {
   g_last_error.clear();
   return linear_fwd("ttt_linear_fwd", q, k, v, w0, w0_batch_stride, nullptr, nullptr, 0.0f, z,
                     w_out, B, H, T, d, chunk, causal, eta, eta_tok, loss, epochs, io_dtype, stream);
 }
 
-int ttt_linear_ln_fwd(const void* q, const void* k, const void* v, const float* w0,
-                      long long w0_batch_stride, const float* ln_weight, const float* ln_bias,
-                      float ln_eps, void* z, float* w_out, int B, int H, int T, int d, int chunk,
-                      int causal, float eta, const float* eta_tok, int loss, int epochs,
-                      int io_dtype, ttt_stream_t stream) {
+static int impl_ttt_linear_ln_fwd(const void* q, const void* k, const void* v, const float* w0,
+                                  long long w0_batch_stride, const float* ln_weight, const float* ln_bias,
+                                  float ln_eps, void* z, float* w_out, int B, int H, int T, int d, int chunk,
+                                  int causal, float eta, const float* eta_tok, int loss, int epochs,
+                                  int io_dtype, ttt_stream_t stream) {
   g_last_error.clear();
   const int rc = check_ln("ttt_linear_ln_fwd", ln_weight, ln_bias, ln_eps);
   if (rc != TTT_OK) return rc;
@@ -723,14 +763,73 @@ int ttt_linear_ln_fwd(const void* q, const void* k, const void* v, const float* 
                     stream);
 }
 
-int ttt_mlp_fwd(const void* q, const void* k, const void* v, const float* w1, const float* w2,
-                long long w_batch_stride, void* z, float* w1_out, float* w2_out, int B, int H,
-                int T, int d, int dh, int chunk, int causal, float eta, const float* eta_tok,
-                int loss, int epochs, int io_dtype, ttt_stream_t stream) {
+static int impl_ttt_mlp_fwd(const void* q, const void* k, const void* v, const float* w1, const float* w2,
+                            long long w_batch_stride, void* z, float* w1_out, float* w2_out, int B, int H,
+                            int T, int d, int dh, int chunk, int causal, float eta, const float* eta_tok,
+                            int loss, int epochs, int io_dtype, ttt_stream_t stream) {
   g_last_error.clear();
   return mlp_fwd("ttt_mlp_fwd", q, k, v, w1, w2, w_batch_stride, nullptr, nullptr, 0.0f, z,
                  w1_out, w2_out, B, H, T, d, dh, chunk, causal, eta, eta_tok, loss, epochs,
                  io_dtype, stream);
+}
+
+static int impl_ttt_mlp_ln_fwd(const void* q, const void* k, const void* v, const float* w1, const float* w2,
+                               long long w_batch_stride, const float* ln_weight, const float* ln_bias,
+                               float ln_eps, void* z, float* w1_out, float* w2_out, int B, int H, int T,
+                               int d, int dh, int chunk, int causal, float eta, const float* eta_tok,
+                               int loss, int epochs, int io_dtype, ttt_stream_t stream) {
+  g_last_error.clear();
+  const int rc = check_ln("ttt_mlp_ln_fwd", ln_weight, ln_bias, ln_eps);
+  if (rc != TTT_OK) return rc;
+  return mlp_fwd("ttt_mlp_ln_fwd", q, k, v, w1, w2, w_batch_stride, ln_weight, ln_bias, ln_eps,
+                 z, w1_out, w2_out, B, H, T, d, dh, chunk, causal, eta, eta_tok, loss, epochs,
+                 io_dtype, stream);
+}
+
+// ---- public entry points: the calls above, then the optional finite check ----
+
+int ttt_set_check_finite(int on) {
+  const int prev = check_finite_on() ? 1 : 0;
+  g_check_finite.store(on ? 1 : 0, std::memory_order_relaxed);
+  return prev;
+}
+
+int ttt_get_check_finite(void) { return check_finite_on() ? 1 : 0; }
+
+int ttt_linear_fwd(const void* q, const void* k, const void* v, const float* w0,
+                   long long w0_batch_stride, void* z, float* w_out, int B, int H, int T, int d,
+                   int chunk, int causal, float eta, const float* eta_tok, int loss, int epochs,
+                   int io_dtype, ttt_stream_t stream) {
+  const int rc = impl_ttt_linear_fwd(q, k, v, w0, w0_batch_stride, z, w_out, B, H, T, d, chunk,
+                                     causal, eta, eta_tok, loss, epochs, io_dtype, stream);
+  return finite_outputs(rc, "ttt_linear_fwd", stream,
+                        {{"z", z, tok(B, H, T, d), io_bytes(io_dtype)},
+                         {"w_out", w_out, per_seq(B, H, 1LL * d * d), 4}});
+}
+
+int ttt_linear_ln_fwd(const void* q, const void* k, const void* v, const float* w0,
+                      long long w0_batch_stride, const float* ln_weight, const float* ln_bias,
+                      float ln_eps, void* z, float* w_out, int B, int H, int T, int d, int chunk,
+                      int causal, float eta, const float* eta_tok, int loss, int epochs,
+                      int io_dtype, ttt_stream_t stream) {
+  const int rc = impl_ttt_linear_ln_fwd(q, k, v, w0, w0_batch_stride, ln_weight, ln_bias, ln_eps,
+                                        z, w_out, B, H, T, d, chunk, causal, eta, eta_tok, loss,
+                                        epochs, io_dtype, stream);
+  return finite_outputs(rc, "ttt_linear_ln_fwd", stream,
+                        {{"z", z, tok(B, H, T, d), io_bytes(io_dtype)},
+                         {"w_out", w_out, per_seq(B, H, 1LL * d * d), 4}});
+}
+
+int ttt_mlp_fwd(const void* q, const void* k, const void* v, const float* w1, const float* w2,
+                long long w_batch_stride, void* z, float* w1_out, float* w2_out, int B, int H,
+                int T, int d, int dh, int chunk, int causal, float eta, const float* eta_tok,
+                int loss, int epochs, int io_dtype, ttt_stream_t stream) {
+  const int rc = impl_ttt_mlp_fwd(q, k, v, w1, w2, w_batch_stride, z, w1_out, w2_out, B, H, T, d,
+                                  dh, chunk, causal, eta, eta_tok, loss, epochs, io_dtype, stream);
+  return finite_outputs(rc, "ttt_mlp_fwd", stream,
+                        {{"z", z, tok(B, H, T, d), io_bytes(io_dtype)},
+                         {"w1_out", w1_out, per_seq(B, H, 1LL * dh * d), 4},
+                         {"w2_out", w2_out, per_seq(B, H, 1LL * d * dh), 4}});
 }
 
 int ttt_mlp_ln_fwd(const void* q, const void* k, const void* v, const float* w1, const float* w2,
@@ -738,12 +837,139 @@ int ttt_mlp_ln_fwd(const void* q, const void* k, const void* v, const float* w1,
                    float ln_eps, void* z, float* w1_out, float* w2_out, int B, int H, int T,
                    int d, int dh, int chunk, int causal, float eta, const float* eta_tok,
                    int loss, int epochs, int io_dtype, ttt_stream_t stream) {
-  g_last_error.clear();
-  const int rc = check_ln("ttt_mlp_ln_fwd", ln_weight, ln_bias, ln_eps);
-  if (rc != TTT_OK) return rc;
-  return mlp_fwd("ttt_mlp_ln_fwd", q, k, v, w1, w2, w_batch_stride, ln_weight, ln_bias, ln_eps,
-                 z, w1_out, w2_out, B, H, T, d, dh, chunk, causal, eta, eta_tok, loss, epochs,
-                 io_dtype, stream);
+  const int rc = impl_ttt_mlp_ln_fwd(q, k, v, w1, w2, w_batch_stride, ln_weight, ln_bias, ln_eps,
+                                     z, w1_out, w2_out, B, H, T, d, dh, chunk, causal, eta,
+                                     eta_tok, loss, epochs, io_dtype, stream);
+  return finite_outputs(rc, "ttt_mlp_ln_fwd", stream,
+                        {{"z", z, tok(B, H, T, d), io_bytes(io_dtype)},
+                         {"w1_out", w1_out, per_seq(B, H, 1LL * dh * d), 4},
+                         {"w2_out", w2_out, per_seq(B, H, 1LL * d * dh), 4}});
+}
+
+int delta_rule_fwd(const void* q, const void* k, const void* v, const float* w0,
+                   long long w0_batch_stride, void* z, float* w_out, int B, int H, int T,
+                   int d, float eta, const float* eta_tok, int io_dtype, ttt_stream_t stream) {
+  const int rc = impl_delta_rule_fwd(q, k, v, w0, w0_batch_stride, z, w_out, B, H, T, d, eta,
+                                     eta_tok, io_dtype, stream);
+  return finite_outputs(rc, "delta_rule_fwd", stream,
+                        {{"z", z, tok(B, H, T, d), io_bytes(io_dtype)},
+                         {"w_out", w_out, per_seq(B, H, 1LL * d * d), 4}});
+}
+
+int ttt_linear_bwd(const void* q, const void* k, const void* v, const float* w0,
+                   long long w0_batch_stride, const void* dz, const float* dw_out, void* dq,
+                   void* dk, void* dv, float* dw0, int B, int H, int T, int d, int chunk,
+                   float eta, const float* eta_tok, float* deta_tok, int loss, int io_dtype,
+                   ttt_stream_t stream) {
+  const int rc = impl_ttt_linear_bwd(q, k, v, w0, w0_batch_stride, dz, dw_out, dq, dk, dv, dw0, B,
+                                     H, T, d, chunk, eta, eta_tok, deta_tok, loss, io_dtype, stream);
+  const int ib = io_bytes(io_dtype);
+  return finite_outputs(rc, "ttt_linear_bwd", stream,
+                        {{"dq", dq, tok(B, H, T, d), ib}, {"dk", dk, tok(B, H, T, d), ib},
+                         {"dv", dv, tok(B, H, T, d), ib}, {"dw0", dw0, per_seq(B, H, 1LL * d * d), 4},
+                         {"deta_tok", deta_tok, tok(B, H, T, 1), 4}});
+}
+
+int ttt_linear_bwd_noalloc(const void* q, const void* k, const void* v, const float* w0,
+                           long long w0_batch_stride, const void* dz, const float* dw_out,
+                           void* dq, void* dk, void* dv, float* dw0, int B, int H, int T, int d,
+                           int chunk, float eta, const float* eta_tok, float* deta_tok, int loss,
+                           int io_dtype, ttt_stream_t stream) {
+  const int rc = impl_ttt_linear_bwd_noalloc(q, k, v, w0, w0_batch_stride, dz, dw_out, dq, dk, dv,
+                                             dw0, B, H, T, d, chunk, eta, eta_tok, deta_tok, loss,
+                                             io_dtype, stream);
+  const int ib = io_bytes(io_dtype);
+  return finite_outputs(rc, "ttt_linear_bwd_noalloc", stream,
+                        {{"dq", dq, tok(B, H, T, d), ib}, {"dk", dk, tok(B, H, T, d), ib},
+                         {"dv", dv, tok(B, H, T, d), ib}, {"dw0", dw0, per_seq(B, H, 1LL * d * d), 4},
+                         {"deta_tok", deta_tok, tok(B, H, T, 1), 4}});
+}
+
+int ttt_mlp_bwd(const void* q, const void* k, const void* v, const float* w1, const float* w2,
+                long long w_batch_stride, const void* dz, const float* dw1_out,
+                const float* dw2_out, void* dq, void* dk, void* dv, float* dw1, float* dw2, int B,
+                int H, int T, int d, int dh, int chunk, float eta, const float* eta_tok,
+                float* deta_tok, int loss, int io_dtype, ttt_stream_t stream) {
+  const int rc = impl_ttt_mlp_bwd(q, k, v, w1, w2, w_batch_stride, dz, dw1_out, dw2_out, dq, dk,
+                                  dv, dw1, dw2, B, H, T, d, dh, chunk, eta, eta_tok, deta_tok, loss,
+                                  io_dtype, stream);
+  const int ib = io_bytes(io_dtype);
+  return finite_outputs(rc, "ttt_mlp_bwd", stream,
+                        {{"dq", dq, tok(B, H, T, d), ib}, {"dk", dk, tok(B, H, T, d), ib},
+                         {"dv", dv, tok(B, H, T, d), ib}, {"dw1", dw1, per_seq(B, H, 1LL * dh * d), 4},
+                         {"dw2", dw2, per_seq(B, H, 1LL * d * dh), 4},
+                         {"deta_tok", deta_tok, tok(B, H, T, 1), 4}});
+}
+
+int ttt_linear_ln_bwd(const void* q, const void* k, const void* v, const float* w0,
+                      long long w0_batch_stride, const float* ln_weight, const float* ln_bias,
+                      float ln_eps, const void* dz, const float* dw_out, void* dq, void* dk,
+                      void* dv, float* dw0, float* dln_weight, float* dln_bias, int B, int H,
+                      int T, int d, int chunk, float eta, const float* eta_tok, float* deta_tok,
+                      int loss, int io_dtype, ttt_stream_t stream) {
+  const int rc = impl_ttt_linear_ln_bwd(q, k, v, w0, w0_batch_stride, ln_weight, ln_bias, ln_eps,
+                                        dz, dw_out, dq, dk, dv, dw0, dln_weight, dln_bias, B, H, T,
+                                        d, chunk, eta, eta_tok, deta_tok, loss, io_dtype, stream);
+  const int ib = io_bytes(io_dtype);
+  return finite_outputs(rc, "ttt_linear_ln_bwd", stream,
+                        {{"dq", dq, tok(B, H, T, d), ib}, {"dk", dk, tok(B, H, T, d), ib},
+                         {"dv", dv, tok(B, H, T, d), ib}, {"dw0", dw0, per_seq(B, H, 1LL * d * d), 4},
+                         {"dln_weight", dln_weight, per_seq(B, H, d), 4},
+                         {"dln_bias", dln_bias, per_seq(B, H, d), 4},
+                         {"deta_tok", deta_tok, tok(B, H, T, 1), 4}});
+}
+
+int ttt_mlp_ln_bwd(const void* q, const void* k, const void* v, const float* w1, const float* w2,
+                   long long w_batch_stride, const float* ln_weight, const float* ln_bias,
+                   float ln_eps, const void* dz, const float* dw1_out, const float* dw2_out,
+                   void* dq, void* dk, void* dv, float* dw1, float* dw2, float* dln_weight,
+                   float* dln_bias, int B, int H, int T, int d, int dh, int chunk, float eta,
+                   const float* eta_tok, float* deta_tok, int loss, int io_dtype,
+                   ttt_stream_t stream) {
+  const int rc = impl_ttt_mlp_ln_bwd(q, k, v, w1, w2, w_batch_stride, ln_weight, ln_bias, ln_eps,
+                                     dz, dw1_out, dw2_out, dq, dk, dv, dw1, dw2, dln_weight,
+                                     dln_bias, B, H, T, d, dh, chunk, eta, eta_tok, deta_tok, loss,
+                                     io_dtype, stream);
+  const int ib = io_bytes(io_dtype);
+  return finite_outputs(rc, "ttt_mlp_ln_bwd", stream,
+                        {{"dq", dq, tok(B, H, T, d), ib}, {"dk", dk, tok(B, H, T, d), ib},
+                         {"dv", dv, tok(B, H, T, d), ib}, {"dw1", dw1, per_seq(B, H, 1LL * dh * d), 4},
+                         {"dw2", dw2, per_seq(B, H, 1LL * d * dh), 4},
+                         {"dln_weight", dln_weight, per_seq(B, H, d), 4},
+                         {"dln_bias", dln_bias, per_seq(B, H, d), 4},
+                         {"deta_tok", deta_tok, tok(B, H, T, 1), 4}});
+}
+
+int ttt_linear_nc_bwd(const void* q, const void* k, const void* v, const float* w0,
+                      long long w0_batch_stride, const void* dz, const float* dw_out, void* dq,
+                      void* dk, void* dv, float* dw0, int B, int H, int T, int d, int chunk,
+                      int epochs, float eta, const float* eta_tok, float* deta_tok, int loss,
+                      int io_dtype, ttt_stream_t stream) {
+  const int rc = impl_ttt_linear_nc_bwd(q, k, v, w0, w0_batch_stride, dz, dw_out, dq, dk, dv, dw0,
+                                        B, H, T, d, chunk, epochs, eta, eta_tok, deta_tok, loss,
+                                        io_dtype, stream);
+  const int ib = io_bytes(io_dtype);
+  return finite_outputs(rc, "ttt_linear_nc_bwd", stream,
+                        {{"dq", dq, tok(B, H, T, d), ib}, {"dk", dk, tok(B, H, T, d), ib},
+                         {"dv", dv, tok(B, H, T, d), ib}, {"dw0", dw0, per_seq(B, H, 1LL * d * d), 4},
+                         {"deta_tok", deta_tok, tok(B, H, T, 1), 4}});
+}
+
+int ttt_mlp_nc_bwd(const void* q, const void* k, const void* v, const float* w1, const float* w2,
+                   long long w_batch_stride, const void* dz, const float* dw1_out,
+                   const float* dw2_out, void* dq, void* dk, void* dv, float* dw1, float* dw2,
+                   int B, int H, int T, int d, int dh, int chunk, int epochs, float eta,
+                   const float* eta_tok, float* deta_tok, int loss, int io_dtype,
+                   ttt_stream_t stream) {
+  const int rc = impl_ttt_mlp_nc_bwd(q, k, v, w1, w2, w_batch_stride, dz, dw1_out, dw2_out, dq, dk,
+                                     dv, dw1, dw2, B, H, T, d, dh, chunk, epochs, eta, eta_tok,
+                                     deta_tok, loss, io_dtype, stream);
+  const int ib = io_bytes(io_dtype);
+  return finite_outputs(rc, "ttt_mlp_nc_bwd", stream,
+                        {{"dq", dq, tok(B, H, T, d), ib}, {"dk", dk, tok(B, H, T, d), ib},
+                         {"dv", dv, tok(B, H, T, d), ib}, {"dw1", dw1, per_seq(B, H, 1LL * dh * d), 4},
+                         {"dw2", dw2, per_seq(B, H, 1LL * d * dh), 4},
+                         {"deta_tok", deta_tok, tok(B, H, T, 1), 4}});
 }
 
 }  // extern "C"

@@ -84,6 +84,17 @@ int main() {
     return 1;
   }
   run_all();
+  // the finite-check switch: invalid calls are still rejected before any GPU work
+  const int prev = ttt_set_check_finite(1);
+  if (ttt_get_check_finite() != 1) {
+    std::printf("FAIL ttt_get_check_finite after ttt_set_check_finite(1)\n");
+    ++failures;
+  }
+  run_all();
+  if (ttt_set_check_finite(prev) != 1) {
+    std::printf("FAIL ttt_set_check_finite did not return the previous setting\n");
+    ++failures;
+  }
   std::vector<std::thread> pool;
   for (int t = 0; t < 4; ++t) pool.emplace_back(run_all);
   for (auto& th : pool) th.join();

@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("ttt_linear_fwd", "ttt_mlp_fwd", "delta_rule_fwd", "ttt_linear_bwd", "ttt_mlp_bwd",
               "ttt_linear_ln_fwd", "ttt_mlp_ln_fwd", "ttt_last_error", "ttt_abi_version",
-              "ttt_linear_nc_bwd", "ttt_mlp_nc_bwd", "ttt_linear_bwd_noalloc"):
+              "ttt_linear_nc_bwd", "ttt_mlp_nc_bwd", "ttt_linear_bwd_noalloc",
+              "ttt_set_check_finite", "ttt_get_check_finite"):
         assert n in names
 
 
@@ -41,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ttt_abi_version() == 11
+    assert lib.ttt_abi_version() == 12
 
 
 FAKE = 0x1000  # never dereferenced: validation fails before any HIP call
@@ -342,3 +343,36 @@ def test_mlp_ln_bwd_rejects_oversized_hidden_and_bad_eps(lib):
     assert lib.ttt_mlp_ln_bwd(*args) == ttt.TTT_E_UNSUPPORTED and "dh=300" in ttt.last_error()
     args[8] = -1.0
     assert lib.ttt_mlp_ln_bwd(*args) == ttt.TTT_E_INVALID and "ln_eps" in ttt.last_error()
+
+
+def test_finite_check_switch(lib):
+    """The debug switch is process-wide, off by default and reports its previous value; it
+    does not change argument validation."""
+    prev = ttt.set_check_finite(False)
+    try:
+        assert ttt.get_check_finite() is False
+        assert ttt.set_check_finite(True) is False
+        assert ttt.get_check_finite() is True
+        assert lib.ttt_set_check_finite(7) == 1  # any nonzero value is on
+        assert lib.ttt_get_check_finite() == 1
+        # an invalid call still fails validation first (no GPU call, no check)
+        assert _linear(lib, q=None) == ttt.TTT_E_INVALID
+        assert "non-null" in ttt.last_error()
+        assert ttt.set_check_finite(False) is True
+        assert ttt.get_check_finite() is False
+    finally:
+        ttt.set_check_finite(prev)
+
+
+@pytest.mark.parametrize("value,on", [("1", True), ("yes", True), ("0", False), ("", False)])
+def test_finite_check_environment(value, on):
+    """TTT_CHECK_FINITE sets the switch for a fresh process."""
+    import subprocess
+    import sys
+    code = ("import test_sequence_layers_amd as t; print(int(t.get_check_finite()))")
+    env = dict(os.environ, TTT_CHECK_FINITE=value)
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, cwd=root,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip() == ("1" if on else "0")
