@@ -1,7 +1,8 @@
 // Backward pass of the causal TTT-MLP layer on the vector ALUs: f(k) = W2 SiLU(W1 k),
 // reconstruction loss or the negative dot-product loss (ViT3 news page, section 2), scalar
-// rate or per-token rate factors, chunk <= 16, hidden width <= 256, d in {16, 32, 64}, fp32 or bf16 I/O.  One workgroup of 1024 threads per (batch, head) chain walks the chunks
-// from last to first.
+// rate or per-token rate factors, chunk <= 16, hidden width <= 256, d in {16, 32, 64}, fp32 or
+// bf16 I/O.  One workgroup of 1024 threads per (batch, head) chain walks the chunks from last
+// to first.
 //
 // The outer loop trains the projections and the initial states through the inner updates
 // (wmrh.cn summary of Sun et al. 2024, section 2.2; "Fast weights" page, opening
