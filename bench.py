@@ -56,15 +56,18 @@ def named_workload(name):
     return workload(name)
 
 
-def _profile_record(workload_name, kind):
+def _profile_record(workload_name, kind, kernel=None):
     """A committed rocprofv3 counter record (profiles/<workload>_<kind>.json), or None when
-    none exists or the kernel source has changed since it was taken."""
+    none exists, it was taken on another kernel than `kernel` (a name prefix), or the kernel
+    source has changed since it was taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"{workload_name}_{kind}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
+    if kernel is not None and not rec.get("kernel", "").startswith(kernel):
+        return None
     src = os.path.join(ROOT, rec["source"])
     if not os.path.exists(src):
         return None
@@ -74,17 +77,17 @@ def _profile_record(workload_name, kind):
     return rec
 
 
-def measured_traffic(workload_name):
+def measured_traffic(workload_name, kernel=None):
     """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE for the kernel of
     this workload, or None when no record exists or the kernel source has changed since."""
-    rec = _profile_record(workload_name, "traffic")
+    rec = _profile_record(workload_name, "traffic", kernel)
     return None if rec is None else rec["fetch_bytes"] + rec["write_bytes"]
 
 
-def measured_mfma_util(workload_name):
+def measured_mfma_util(workload_name, kernel=None):
     """MFMA utilisation (%) of this workload's kernel from the rocprofv3 derived counter
     MfmaUtil (matrix-core busy cycles over active cycles of all SIMDs), or None."""
-    rec = _profile_record(workload_name, "mfma")
+    rec = _profile_record(workload_name, "mfma", kernel)
     return None if rec is None else rec["mfma_util_pct"]
 
 
@@ -107,16 +110,26 @@ def make_device_inputs(w, seed, torch, rates=False, paper=False):
     return dev
 
 
-def launch(w, dev, ttt, loss="mse", epochs=1):
+def launch(w, dev, ttt, loss="mse", epochs=1, ws=None):
+    """One forward call.  ws: a workspace for the MLP entry points that take one
+    (ttt_mlp_fwd_ws / ttt_mlp_ln_fwd_ws: two workgroups per sequence)."""
     et = dev.get("eta_tok")
     if "ln_w" in dev:  # the paper's inner models: x + LN(f_res(x)), GELU in the MLP
         ln = (dev["ln_w"], dev["ln_b"])
         if w.kind == "linear":
             ttt.ttt_linear_ln_fwd(dev["q"], dev["k"], dev["v"], dev["w0"], *ln, w.eta, w.chunk,
                                   w.causal, eta_tok=et, loss=loss, epochs=epochs, z=dev["z"])
+        elif ws is not None:
+            ttt.ttt_mlp_ln_fwd_ws(dev["q"], dev["k"], dev["v"], dev["w1"], dev["w2"], *ln, w.eta,
+                                  w.chunk, w.causal, workspace=ws, eta_tok=et, loss=loss,
+                                  epochs=epochs, z=dev["z"])
         else:
             ttt.ttt_mlp_ln_fwd(dev["q"], dev["k"], dev["v"], dev["w1"], dev["w2"], *ln, w.eta,
                                w.chunk, w.causal, eta_tok=et, loss=loss, epochs=epochs, z=dev["z"])
+        return
+    if ws is not None and w.kind == "mlp":
+        ttt.ttt_mlp_fwd_ws(dev["q"], dev["k"], dev["v"], dev["w1"], dev["w2"], w.eta, w.chunk,
+                           w.causal, workspace=ws, eta_tok=et, loss=loss, epochs=epochs, z=dev["z"])
         return
     if w.kind == "linear":
         ttt.ttt_linear_fwd(dev["q"], dev["k"], dev["v"], dev["w0"], w.eta, w.chunk, w.causal,
@@ -128,8 +141,21 @@ def launch(w, dev, ttt, loss="mse", epochs=1):
                         w.causal, eta_tok=et, loss=loss, epochs=epochs, z=dev["z"])
 
 
+def split_workspace(w, torch, ttt):
+    """A workspace for the two-workgroup MLP kernel when the workload has its shape (allocated
+    once, outside the timed region), else None."""
+    if w.kind != "mlp":
+        return None
+    n = ttt.ttt_mlp_fwd_workspace_size(w.B, w.H, w.T, w.d, w.h, w.chunk, w.causal, w.io)
+    return torch.empty(n, dtype=torch.uint8, device="cuda") if n > 0 else None
+
+
 def time_workload(w, steps, warmup, torch, ttt, rotate=None, rates=False, loss="mse", epochs=1,
-                  paper=False):
+                  paper=False, split=True):
+    """Event-timed forward calls.  split: the MLP through ttt_mlp_fwd_ws / ttt_mlp_ln_fwd_ws
+    (two workgroups per sequence, a workspace allocated here beforehand) where the shape has
+    that kernel; False: the one-workgroup entry points."""
+    ws = split_workspace(w, torch, ttt) if split else None
     bytes_, flops = algorithmic_cost(w, epochs)
     if rates:
         bytes_ += w.B * w.H * w.T * 4  # the rate factors, read once
@@ -138,13 +164,13 @@ def time_workload(w, steps, warmup, torch, ttt, rotate=None, rates=False, loss="
     sets = [make_device_inputs(w, w.seed + i, torch, rates, paper) for i in range(rotate)]
     stream = torch.cuda.current_stream()
     for i in range(warmup):
-        launch(w, sets[i % rotate], ttt, loss, epochs)
+        launch(w, sets[i % rotate], ttt, loss, epochs, ws)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(steps):
-        launch(w, sets[i % rotate], ttt, loss, epochs)
+        launch(w, sets[i % rotate], ttt, loss, epochs, ws)
     stop.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / steps
@@ -157,6 +183,8 @@ def time_workload(w, steps, warmup, torch, ttt, rotate=None, rates=False, loss="
         "bytes": bytes_,
         "flops": flops,
         "rotated_sets": rotate,
+        "kernel": ("mlp_split_kernel" if ws is not None else
+                   "mlp_mfma_kernel" if w.kind == "mlp" and w.causal else None),
     }
 
 
@@ -332,14 +360,14 @@ def main():
     def roofline_of(wl, r, rates=False):
         if wl.kind == "mlp":
             # dense bf16 contractions: priced against the matrix-core peak
-            kern = "mlp_mfma_kernel" if wl.causal else "mlp_nc_kernel"
+            kern = r.get("kernel") or ("mlp_mfma_kernel" if wl.causal else "mlp_nc_kernel")
             return {
                 "bound": "mfma",
                 "achieved": round(r["tflops"], 2),
                 "peak": BF16_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s",
                 "frac": round(r["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4),
-                "traffic": None if rates else measured_traffic(wl.name),
+                "traffic": None if rates else measured_traffic(wl.name, kern),
                 "kernel": f"{kern} (per launch: the method's flops, tril products at half)",
                 "flops_per_launch": r["flops"],
             }
@@ -380,7 +408,8 @@ def main():
                    "rotated_input_sets": res["rotated_sets"]},
         "mfma_util_pct": round(100 * mres["tflops"] / BF16_MFMA_PEAK_TFLOPS, 3),
         "mfma_util_workload": mw.name,
-        "mfma_util_rocprof_pct": measured_mfma_util(mw.name),
+        "mfma_util_rocprof_pct": measured_mfma_util(mw.name, mres.get("kernel")),
+        "mfma_util_kernel": mres.get("kernel"),
         "roofline": roofline,
         "roofline_mfma": dict(roofline_of(mw, mres), workload=mw.name,
                               tokens_per_s=round(mres["tokens_per_s"], 1),
@@ -401,8 +430,11 @@ def main():
                 "tflops": round(r["tflops"], 3),
                 "mfma_util_pct": round(100 * r["tflops"] / BF16_MFMA_PEAK_TFLOPS, 3),
             }
-            if measured_mfma_util(o.name) is not None:
-                others[o.name]["mfma_util_rocprof_pct"] = measured_mfma_util(o.name)
+            mu = measured_mfma_util(o.name, r.get("kernel"))
+            if mu is not None:
+                others[o.name]["mfma_util_rocprof_pct"] = mu
+            if r.get("kernel"):
+                others[o.name]["kernel"] = r["kernel"]
         # variants: the headline workload with per-token rate factors (uniform in [0, 1)),
         # the dot-product loss on the headline and the vision workloads, mini-batches with
         # epochs on the vision workload
@@ -426,6 +458,12 @@ def main():
         # and the causal MLP workloads
         variants += [(o, "+paper_ln", dict(paper=True)) for o in WORKLOADS
                      if o.name in ("linear_d64_T2048", "mlp_h256_T2048")]
+        # the causal MLP workloads on the one-workgroup kernel (ttt_mlp_fwd / ttt_mlp_ln_fwd,
+        # no workspace)
+        variants += [(o, "+one_workgroup", dict(split=False)) for o in WORKLOADS
+                     if o.name == "mlp_h256_T2048"]
+        variants += [(o, "+paper_ln+one_workgroup", dict(paper=True, split=False))
+                     for o in WORKLOADS if o.name == "mlp_h256_T2048"]
         # backward passes of the headline linear workload, the delta rule, the causal MLP
         # workload and the vision workload (dz ~ N(0, 1), no upstream state gradient)
         bwd = [w] if w.kind == "linear" else []

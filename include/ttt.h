@@ -61,6 +61,8 @@
 #ifndef TTT_H_
 #define TTT_H_
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -137,6 +139,42 @@ int ttt_mlp_ln_fwd(const void* q, const void* k, const void* v,
                    int B, int H, int T, int d, int dh, int chunk, int causal, float eta,
                    const float* eta_tok, int loss, int epochs, int io_dtype,
                    ttt_stream_t stream);
+
+/*
+ * ttt_mlp_fwd / ttt_mlp_ln_fwd with a workspace owned by the caller, for the causal
+ * d = 64, dh = 256, chunk 16, bf16 shape.  The layer's recursion (the gradients of the keys
+ * and the state updates, wmrh.cn summary of Sun et al. 2024, section 1.2.2) does not depend
+ * on the queries, so a kernel with two workgroups per (b, h) runs it on one compute unit and
+ * forms the outputs on a second, which replays the same state updates from the operands the
+ * first hands over through the workspace (18 KB per chunk of 16 tokens).  Results are
+ * bit-identical to ttt_mlp_fwd / ttt_mlp_ln_fwd.
+ *   workspace        device memory of at least ttt_mlp_fwd_workspace_size(...) bytes,
+ *                    256-byte aligned, owned by the caller; its contents need no
+ *                    initialisation and are left undefined.  One workspace serves one call
+ *                    at a time: calls that may overlap (different streams) need their own.
+ *   workspace_bytes  its size.
+ * With workspace == NULL, or for any other shape (for which ttt_mlp_fwd_workspace_size
+ * returns 0), the call is ttt_mlp_fwd / ttt_mlp_ln_fwd.  The call allocates nothing on the
+ * two-workgroup path.  TTT_E_INVALID additionally for a workspace that is too small or
+ * misaligned.  Should the outputs' workgroup of a sequence ever wait past a bound (about a
+ * second) for the operands, it fills that sequence's remaining outputs with NaN instead of
+ * hanging (never observed: the recursion's workgroups are dispatched first and never wait).
+ */
+size_t ttt_mlp_fwd_workspace_size(int B, int H, int T, int d, int dh, int chunk, int causal,
+                                  int io_dtype);
+int ttt_mlp_fwd_ws(const void* q, const void* k, const void* v,
+                   const float* w1, const float* w2, long long w_batch_stride,
+                   void* z, float* w1_out, float* w2_out,
+                   int B, int H, int T, int d, int dh, int chunk, int causal, float eta,
+                   const float* eta_tok, int loss, int epochs, int io_dtype,
+                   void* workspace, size_t workspace_bytes, ttt_stream_t stream);
+int ttt_mlp_ln_fwd_ws(const void* q, const void* k, const void* v,
+                      const float* w1, const float* w2, long long w_batch_stride,
+                      const float* ln_weight, const float* ln_bias, float ln_eps,
+                      void* z, float* w1_out, float* w2_out,
+                      int B, int H, int T, int d, int dh, int chunk, int causal, float eta,
+                      const float* eta_tok, int loss, int epochs, int io_dtype,
+                      void* workspace, size_t workspace_bytes, ttt_stream_t stream);
 
 /*
  * Delta rule (mini-batch of one token, causal): W_t = W_{t-1} + eta_t (v_t - W_{t-1} k_t) k_t^T,

@@ -31,7 +31,10 @@ from ._binding import (  # noqa: F401
     ttt_linear_nc_bwd,
     ttt_mlp_bwd,
     ttt_mlp_fwd,
+    ttt_mlp_fwd_workspace_size,
+    ttt_mlp_fwd_ws,
     ttt_mlp_ln_bwd,
     ttt_mlp_ln_fwd,
+    ttt_mlp_ln_fwd_ws,
     ttt_mlp_nc_bwd,
 )

@@ -33,6 +33,13 @@ SIGNATURES = {
                                _i, _f, _vp, _i, _i, _i, _vp]),
     "ttt_mlp_ln_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _ll, _vp, _vp, _f, _vp, _vp, _vp,
                             _i, _i, _i, _i, _i, _i, _i, _f, _vp, _i, _i, _i, _vp]),
+    "ttt_mlp_fwd_workspace_size": (ctypes.c_size_t, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "ttt_mlp_fwd_ws": (_i, [_vp, _vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp,
+                            _i, _i, _i, _i, _i, _i, _i, _f, _vp, _i, _i, _i,
+                            _vp, ctypes.c_size_t, _vp]),
+    "ttt_mlp_ln_fwd_ws": (_i, [_vp, _vp, _vp, _vp, _vp, _ll, _vp, _vp, _f, _vp, _vp, _vp,
+                               _i, _i, _i, _i, _i, _i, _i, _f, _vp, _i, _i, _i,
+                               _vp, ctypes.c_size_t, _vp]),
     "delta_rule_fwd": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _i, _i, _i, _i, _f, _vp, _i, _vp]),
     "ttt_linear_bwd": (_i, [_vp, _vp, _vp, _vp, _ll, _vp, _vp, _vp, _vp, _vp, _vp,
                             _i, _i, _i, _i, _i, _f, _vp, _vp, _i, _i, _vp]),
@@ -508,7 +515,7 @@ def delta_rule_fwd(q, k, v, w0, eta, *, eta_tok=None, z=None, w_out=None, return
 
 
 def _mlp(q, k, v, w1, w2, eta, chunk, causal, ln, eta_tok, loss, epochs, z, w1_out, w2_out,
-         return_state, stream):
+         return_state, stream, workspace=False):
     torch = _torch()
     lib = load_library()
     B, H, T, d = _tokens(q, k, v)
@@ -529,7 +536,23 @@ def _mlp(q, k, v, w1, w2, eta, chunk, causal, ln, eta_tok, loss, epochs, z, w1_o
             _rates(eta_tok, B, H, T, q.device), _loss(loss), int(epochs),
             _io_dtype(q), _stream(q.device, stream))
     with torch.cuda.device(q.device):
-        if ln is None:
+        if workspace is not False:
+            # the _ws entry points: tail without the stream, then workspace, size, stream
+            need = lib.ttt_mlp_fwd_workspace_size(B, H, T, d, dh, int(chunk), int(bool(causal)),
+                                                  _io_dtype(q))
+            if workspace is None:
+                workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+            if not (workspace.is_cuda and workspace.device == q.device and workspace.is_contiguous()):
+                raise ValueError("workspace must be a contiguous tensor on the device of q")
+            ws = (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+            if ln is None:
+                rc = lib.ttt_mlp_fwd_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), w1.data_ptr(),
+                                        w2.data_ptr(), s1, *tail[:-1], *ws, tail[-1])
+            else:
+                rc = lib.ttt_mlp_ln_fwd_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                           w1.data_ptr(), w2.data_ptr(), s1,
+                                           *_ln(*ln, H, d, q.device), *tail[:-1], *ws, tail[-1])
+        elif ln is None:
             rc = lib.ttt_mlp_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), w1.data_ptr(),
                                  w2.data_ptr(), s1, *tail)
         else:
@@ -547,6 +570,33 @@ def ttt_mlp_fwd(q, k, v, w1, w2, eta, chunk, causal=True, *, eta_tok=None, loss=
     Returns z (and the final states when return_state or an output state is given)."""
     return _mlp(q, k, v, w1, w2, eta, chunk, causal, None, eta_tok, loss, epochs, z, w1_out,
                 w2_out, return_state, stream)
+
+
+def ttt_mlp_fwd_workspace_size(B, H, T, d, dh, chunk, causal=True, io_dtype="bf16"):
+    """Bytes of workspace ttt_mlp_fwd_ws / ttt_mlp_ln_fwd_ws need for this shape (0: none,
+    the call then runs as ttt_mlp_fwd / ttt_mlp_ln_fwd)."""
+    lib = load_library()
+    code = {"bf16": 1, "f32": 0, "float32": 0, "bfloat16": 1}[str(io_dtype).replace("torch.", "")]
+    return int(lib.ttt_mlp_fwd_workspace_size(int(B), int(H), int(T), int(d), int(dh), int(chunk),
+                                              int(bool(causal)), code))
+
+
+def ttt_mlp_fwd_ws(q, k, v, w1, w2, eta, chunk, causal=True, *, workspace=None, eta_tok=None,
+                   loss="mse", epochs=1, z=None, w1_out=None, w2_out=None, return_state=False,
+                   stream=None):
+    """ttt_mlp_fwd on the two-workgroup kernel, with a caller workspace: a contiguous device
+    tensor of at least ttt_mlp_fwd_workspace_size(...) bytes (None: one is allocated with
+    torch for this call)."""
+    return _mlp(q, k, v, w1, w2, eta, chunk, causal, None, eta_tok, loss, epochs, z, w1_out,
+                w2_out, return_state, stream, workspace)
+
+
+def ttt_mlp_ln_fwd_ws(q, k, v, w1, w2, ln_weight, ln_bias, eta, chunk, causal=True, *,
+                      workspace=None, ln_eps=1e-6, eta_tok=None, loss="mse", epochs=1, z=None,
+                      w1_out=None, w2_out=None, return_state=False, stream=None):
+    """ttt_mlp_ln_fwd on the two-workgroup kernel; workspace as in ttt_mlp_fwd_ws."""
+    return _mlp(q, k, v, w1, w2, eta, chunk, causal, (ln_weight, ln_bias, ln_eps), eta_tok, loss,
+                epochs, z, w1_out, w2_out, return_state, stream, workspace)
 
 
 def ttt_mlp_ln_fwd(q, k, v, w1, w2, ln_weight, ln_bias, eta, chunk, causal=True, *, ln_eps=1e-6,

@@ -623,6 +623,617 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 }
 
+
+// ---------------------------------------------------------------------------------------
+// Two workgroups per chain.  The recursion (U, A, R, dU and the state updates) does not
+// depend on the queries, so a chain's outputs can be formed on a second compute unit that
+// replays the same state updates on a copy of its own:
+//   * the recursion workgroup (blocks 0 .. npad-1) runs the chunk loop above without the
+//     query products and hands each chunk's update operands to its partner: -eta dU and A
+//     of every wave (bf16, in the lanes' operand layout) and -eta R, 18 KB per chunk, into
+//     the caller's workspace;
+//   * the output workgroup (block npad + chain, the same residue mod 8, so the same XCD)
+//     waits for them, forms U_q, A_q and Z, and applies the same rank-16 updates with the
+//     same MFMAs in the same order, so its state, and hence Z, is bit-identical to that of
+//     the one-workgroup kernel.
+// Hand-off protocol.  Each chain has three 64-bit words in its own 128-byte line, each
+// (call tag << 32 | value): the recursion's progress (chunks whose operands are stored), and
+// the compute-unit cluster (XCC) of each of the two workgroups.  The tag changes on every
+// call, so a word left by an earlier call is never taken for this one.
+//   * Both workgroups first post their XCC id with an agent-scope release.  The output
+//     workgroup waits for the recursion's (the recursion has the lower block index, so it
+//     is dispatched first and posts at once); the recursion never waits for its partner and
+//     only looks, once per chunk, whether the partner's id has arrived.
+//   * Operands of chunk c are stored at the top of chunk c + 1, before that chunk's
+//     prefetch loads.  Every wave waits for its older vector-memory operations before the
+//     first barrier of chunk c + 2 (vector memory operations complete in issue order), so
+//     after that barrier wave 0 publishes "c + 1 chunks complete".
+//   * On one XCC the two workgroups share its L2, so the progress word is written and read,
+//     and the operands are read, at device scope past the per-CU cache (sc1), with no cache
+//     write-back or invalidation.  Until the recursion has seen that its partner sits on the
+//     same XCC, and whenever the two sit on different ones, it publishes with an agent-scope
+//     release (L2 write-back) and the output workgroup reads with an agent-scope acquire.
+//     Blocks with equal residues mod 8 land on one XCC under round-robin dispatch, which the
+//     grid arranges; the check keeps the results right if that ever fails.
+//   * The output workgroup loads a chunk's operands one chunk ahead, once the progress word
+//     covers it; wave 0 reads the word one chunk early (without waiting) and spins only when
+//     that reading falls short.  The spin is bounded: past the bound it fills the chain's
+//     remaining outputs with NaN and leaves.
+constexpr int kSlotBytes = kWaves * 2048 + 2048;  // one chunk's hand-off
+constexpr int kFlagStride = 128;
+constexpr int kSpinLimit = 1 << 20;
+__device__ __forceinline__ unsigned long long xcc_id() {
+  return static_cast<unsigned long long>(__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 15);  // HW_REG_XCC_ID
+}
+// vector-memory operations issued at the top of a chunk before its first barrier: at least
+// 2 operand stores and 11 prefetch loads (K rows, K^T gathers, V)
+constexpr int kTopOps = 13;
+__host__ __device__ __forceinline__ size_t split_flag_bytes(int nchains) {
+  return (static_cast<size_t>(nchains) * kFlagStride + 255) & ~static_cast<size_t>(255);
+}
+
+struct Hand {
+  u32x4 du;  // -eta dU tiles 0, 1 of the wave (u32x2 each)
+  u32x4 ab;  // A tiles 0, 1 of the wave
+  u32x4 r0;  // -eta R tiles 0, 1
+  u32x4 r1;  // -eta R tiles 2, 3
+};
+
+struct SplitLds {
+  Lds base;
+  int abort_flag;
+  int same_xcc;
+};
+
+__device__ __forceinline__ void init_state(State& st, const float* w1g, const float* w2g, int h0, int g, int n) {
+#pragma unroll
+  for (int aa = 0; aa < kHT; ++aa) {
+    const float* wr = w1g + static_cast<size_t>(h0 + 16 * aa + n) * kD + 16 * g;
+    const float4_t f0 = *reinterpret_cast<const float4_t*>(wr);
+    const float4_t f1 = *reinterpret_cast<const float4_t*>(wr + 4);
+    const float4_t f2 = *reinterpret_cast<const float4_t*>(wr + 8);
+    const float4_t f3 = *reinterpret_cast<const float4_t*>(wr + 12);
+    st.w1t[0][aa] = float4_t{f0[0], f0[2], f1[0], f1[2]};
+    st.w1t[1][aa] = float4_t{f0[1], f0[3], f1[1], f1[3]};
+    st.w1t[2][aa] = float4_t{f2[0], f2[2], f3[0], f3[2]};
+    st.w1t[3][aa] = float4_t{f2[1], f2[3], f3[1], f3[3]};
+  }
+#pragma unroll
+  for (int aa = 0; aa < kHT; ++aa)
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+      st.w2t[aa][it] = *reinterpret_cast<const float4_t*>(w2g + static_cast<size_t>(16 * it + n) * kH + h0 +
+                                                          16 * aa + 4 * g);
+}
+
+// the state update of one chunk (shared by both workgroups: same operands, same order)
+__device__ __forceinline__ void update_state(State& st, const uint32_t (&kt4)[4][2], const u32x2 (&dub)[kHT],
+                                             const u32x2 (&ab)[kHT], const u32x2 (&rb)[4]) {
+  constexpr uint32_t kLo = 0x05040100u, kHi = 0x07060302u;
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) {
+    const int h = jb >> 1;
+    const uint32_t sel = (jb & 1) ? kHi : kLo;
+    const u32x2 kt = {__builtin_amdgcn_perm(kt4[1][h], kt4[0][h], sel), __builtin_amdgcn_perm(kt4[3][h], kt4[2][h], sel)};
+#pragma unroll
+    for (int aa = 0; aa < kHT; ++aa) st.w1t[jb][aa] = mfma16(kt, dub[aa], st.w1t[jb][aa]);
+  }
+#pragma unroll
+  for (int aa = 0; aa < kHT; ++aa)
+#pragma unroll
+    for (int it = 0; it < 4; ++it) st.w2t[aa][it] = mfma16(ab[aa], rb[it], st.w2t[aa][it]);
+}
+
+__device__ __forceinline__ void store_state(const State& st, float* o1, float* o2, int h0, int g, int n) {
+  if (o1) {
+#pragma unroll
+    for (int aa = 0; aa < kHT; ++aa) {
+      float* wr = o1 + static_cast<size_t>(h0 + 16 * aa + n) * kD + 16 * g;
+      *reinterpret_cast<float4_t*>(wr) =
+          float4_t{st.w1t[0][aa][0], st.w1t[1][aa][0], st.w1t[0][aa][1], st.w1t[1][aa][1]};
+      *reinterpret_cast<float4_t*>(wr + 4) =
+          float4_t{st.w1t[0][aa][2], st.w1t[1][aa][2], st.w1t[0][aa][3], st.w1t[1][aa][3]};
+      *reinterpret_cast<float4_t*>(wr + 8) =
+          float4_t{st.w1t[2][aa][0], st.w1t[3][aa][0], st.w1t[2][aa][1], st.w1t[3][aa][1]};
+      *reinterpret_cast<float4_t*>(wr + 12) =
+          float4_t{st.w1t[2][aa][2], st.w1t[3][aa][2], st.w1t[2][aa][3], st.w1t[3][aa][3]};
+    }
+  }
+  if (o2) {
+#pragma unroll
+    for (int aa = 0; aa < kHT; ++aa)
+#pragma unroll
+      for (int it = 0; it < 4; ++it)
+        *reinterpret_cast<float4_t*>(o2 + static_cast<size_t>(16 * it + n) * kH + h0 + 16 * aa + 4 * g) =
+            st.w2t[aa][it];
+  }
+}
+
+// K, V of one chunk for the recursion workgroup (the layout of ChunkIn, without Q)
+struct MainIn {
+  u32x4 ka0, ka1;
+  uint32_t kt[4][2];
+  uint32_t vv, kv;
+  float et;
+};
+template <bool kPaper>
+__device__ __forceinline__ void load_main(MainIn& r, const char* k, const char* v, const float* etok, int c,
+                                          int seq_bytes, const Offsets& o) {
+  const int off = c * kTileBytes;
+  const __amdgpu_buffer_rsrc_t rk = chunk_rsrc(k + off, seq_bytes - off);
+  const __amdgpu_buffer_rsrc_t rv = chunk_rsrc(v + off, seq_bytes - off);
+  r.ka0 = __builtin_amdgcn_raw_buffer_load_b128(rk, o.row, 0, 0);
+  r.ka1 = __builtin_amdgcn_raw_buffer_load_b128(rk, o.row + 16, 0, 0);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r.kt[e][0] = __builtin_amdgcn_raw_buffer_load_b32(rk, o.kt[e], 0, 0);
+    r.kt[e][1] = __builtin_amdgcn_raw_buffer_load_b32(rk, o.kt[e] + 16, 0, 0);
+  }
+  r.vv = __builtin_amdgcn_raw_buffer_load_b32(rv, o.vv, 0, 0);
+  r.kv = kPaper ? __builtin_amdgcn_raw_buffer_load_b32(rk, o.vv, 0, 0) : 0u;
+  r.et = 1.0f;
+  if (etok) {
+    const int eoff = c * kB * 4;
+    const __amdgpu_buffer_rsrc_t re = chunk_rsrc(etok + c * kB, (seq_bytes >> 5) - eoff);
+    r.et = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(re, o.et, 0, 0));
+  }
+}
+
+// Q, K of one chunk for the output workgroup
+struct PartIn {
+  u32x4 ka0, ka1, qb0, qb1;
+  uint32_t kt[4][2];
+  uint32_t qv;
+};
+template <bool kPaper>
+__device__ __forceinline__ void load_part(PartIn& r, const char* q, const char* k, int c, int seq_bytes,
+                                          const Offsets& o) {
+  const int off = c * kTileBytes;
+  const __amdgpu_buffer_rsrc_t rq = chunk_rsrc(q + off, seq_bytes - off);
+  const __amdgpu_buffer_rsrc_t rk = chunk_rsrc(k + off, seq_bytes - off);
+  r.ka0 = __builtin_amdgcn_raw_buffer_load_b128(rk, o.row, 0, 0);
+  r.ka1 = __builtin_amdgcn_raw_buffer_load_b128(rk, o.row + 16, 0, 0);
+  r.qb0 = __builtin_amdgcn_raw_buffer_load_b128(rq, o.row, 0, 0);
+  r.qb1 = __builtin_amdgcn_raw_buffer_load_b128(rq, o.row + 16, 0, 0);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r.kt[e][0] = __builtin_amdgcn_raw_buffer_load_b32(rk, o.kt[e], 0, 0);
+    r.kt[e][1] = __builtin_amdgcn_raw_buffer_load_b32(rk, o.kt[e] + 16, 0, 0);
+  }
+  r.qv = kPaper ? __builtin_amdgcn_raw_buffer_load_b32(rq, o.vv, 0, 0) : 0u;
+}
+
+__device__ __forceinline__ u32x2 lo2(const u32x4& x) { return u32x2{x.x, x.y}; }
+__device__ __forceinline__ u32x2 hi2(const u32x4& x) { return u32x2{x.z, x.w}; }
+
+template <bool kDot, bool kPaper>
+__device__ __forceinline__ void split_recursion(const MlpArgs& a, SplitLds& sl, int chain, char* slots,
+                                                unsigned long long* flag, unsigned long long tag) {
+  Lds& sh = sl.base;
+  lds_char* opart = (lds_char*)(&sh.opart[0][0][0]);
+  lds_char* rrb = (lds_char*)(&sh.rr[0][0]);
+  lds_char* rtb = (lds_char*)(&sh.rt[0][0]);
+  lds_char* w2lds = (lds_char*)(&sh.w2b[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)][0][0]);
+
+  const int tid = threadIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 4;
+  const int n = lane & 15;
+  const int bi = chain / a.H;
+  const int hi = chain - bi * a.H;
+  const int T = a.T;
+  const int nchunks = (T + kB - 1) / kB;
+  const int seq_bytes = T * kD * 2;
+  const float eta = a.eta;
+  const size_t tok0 = static_cast<size_t>(chain) * static_cast<size_t>(T) * kD;
+  const char* k = reinterpret_cast<const char*>(static_cast<const bf16*>(a.k) + tok0);
+  const char* v = reinterpret_cast<const char*>(static_cast<const bf16*>(a.v) + tok0);
+  const float* etok = a.eta_tok ? a.eta_tok + static_cast<size_t>(chain) * T : nullptr;
+  const size_t hd = static_cast<size_t>(kH) * kD;
+  const float* w1g = a.w1 + bi * a.w_batch_stride + static_cast<long long>(hi) * hd;
+  const float* w2g = a.w2 + bi * a.w_batch_stride + static_cast<long long>(hi) * hd;
+  const int h0 = 16 * kHT * wv;
+  if (kPaper && tid < 2 * kD) sh.lnp[tid / kD][tid % kD] = (tid < kD ? a.ln_w : a.ln_b)[hi * kD + tid % kD];
+
+  State st;
+  init_state(st, w1g, w2g, h0, g, n);
+  const uint32_t one = 0x3F80u;
+  const u32x2 eye = {(4 * g + 0 == n ? one : 0u) | (4 * g + 1 == n ? one << 16 : 0u),
+                     (4 * g + 2 == n ? one : 0u) | (4 * g + 3 == n ? one << 16 : 0u)};
+  Offsets o;
+  o.row = n * 128 + 32 * g;
+  const int c0 = 16 * (n >> 2) + 2 * (n & 3);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o.kt[e] = (4 * g + e) * 128 + 2 * c0;
+  const int rt = tid >> 5;
+  const int ri = 2 * (tid & 31);
+  o.vv = rt * 128 + 2 * ri;
+  o.et = rt * 4;
+  const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  const float2_t zero2 = {0.0f, 0.0f};
+
+  // update operands of the previous chunk, stored at the top of the next one
+  u32x2 pdub[kHT], pab[kHT], prb[4];
+  unsigned long long* hello_own = flag + 1;
+  const unsigned long long* hello_other = flag + 2;
+  const unsigned long long xm = xcc_id();
+  if (wv == 0 && lane == 0) __hip_atomic_store(hello_own, (tag << 32) | xm, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  // wave 0: 0 = partner's XCC not seen yet, 1 = same XCC, 2 = another XCC; the partner's word
+  // is read one chunk before it is looked at
+  int mode = 0;
+  unsigned long long other = 0;
+  auto progress = [&](int count) {  // wave 0, after a barrier
+    if (lane == 0) {
+      const unsigned long long f = (tag << 32) | static_cast<unsigned long long>(count);
+      if (mode == 1)
+        __hip_atomic_store(flag, f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        __hip_atomic_store(flag, f, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+  auto publish = [&](int c) {
+    if (c >= 1) {
+      char* slot = slots + static_cast<size_t>(c - 1) * kSlotBytes;
+      *reinterpret_cast<u32x4*>(slot + wv * 2048 + lane * 16) = u32x4{pdub[0].x, pdub[0].y, pdub[1].x, pdub[1].y};
+      *reinterpret_cast<u32x4*>(slot + wv * 2048 + 1024 + lane * 16) = u32x4{pab[0].x, pab[0].y, pab[1].x, pab[1].y};
+      if (wv == 0) {
+        *reinterpret_cast<u32x4*>(slot + kWaves * 2048 + lane * 16) = u32x4{prb[0].x, prb[0].y, prb[1].x, prb[1].y};
+        *reinterpret_cast<u32x4*>(slot + kWaves * 2048 + 1024 + lane * 16) =
+            u32x4{prb[2].x, prb[2].y, prb[3].x, prb[3].y};
+      }
+    }
+  };
+
+  auto step = [&](const MainIn& cur, MainIn& nxt, int c) {
+    publish(c);
+    load_main<kPaper>(nxt, k, v, etok, c + 1, seq_bytes, o);
+    const bf16x8_t ka0 = bf(cur.ka0), ka1 = bf(cur.ka1);
+    bf16x8_t w1b[2][kHT];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int aa = 0; aa < kHT; ++aa) w1b[h][aa] = pair_op(st.w1t[2 * h][aa], st.w1t[2 * h + 1][aa]);
+    float4_t act[kHT], sd[kHT];
+#pragma unroll
+    for (int aa = 0; aa < kHT; ++aa) {
+      float4_t u = mfma(ka0, w1b[0][aa], zero);
+      u = mfma(ka1, w1b[1][aa], u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float av, dv;
+        act_grad<kPaper>(u[e], av, dv);
+        act[aa][e] = av;
+        sd[aa][e] = dv;
+      }
+    }
+    u32x2 ab[kHT];
+    float4_t actT[kHT];
+#pragma unroll
+    for (int aa = 0; aa < kHT; ++aa) {
+      ab[aa] = k16(act[aa]);
+      actT[aa] = mfma16(ab[aa], eye, zero);
+    }
+    u32x4 w2op[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      w2op[it] = cat_u(st.w2t[0][it], st.w2t[1][it]);
+      const int row = 16 * it + n;
+      lds_store<u32x2>(w2lds, w2off(row, g), u32x2{w2op[it].x, w2op[it].y});
+      lds_store<u32x2>(w2lds, w2off(row, 4 + g), u32x2{w2op[it].z, w2op[it].w});
+    }
+    const bf16x8_t atb = cat_op(actT[0], actT[1]);
+    if (!kDot || kPaper) {
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const float4_t ot = mfma(bf(w2op[it]), atb, zero);
+        lds_store<float4_t>(opart, ((wv * kB + n) * kRow + 16 * it + 4 * g) * 4, ot);
+      }
+    }
+    // every operation older than this chunk's top (the operands of chunk c - 2) is complete
+    __builtin_amdgcn_s_waitcnt(0x0F70 | kTopOps);
+    barrier();
+    if (wv == 0) {
+      if (mode == 0) {  // lane 0 read the partner's word one chunk ago (0 before that)
+        const uint32_t oh = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(other >> 32));
+        const uint32_t ol = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(other));
+        if (oh == static_cast<uint32_t>(tag)) mode = (ol == static_cast<uint32_t>(xm)) ? 1 : 2;
+        if (mode == 0 && lane == 0) other = __hip_atomic_load(hello_other, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (c >= 2) progress(c - 1);
+    }
+    {
+      float2_t s2 = zero2;
+      if (!kDot || kPaper) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) s2 += lds_load<float2_t>(opart, ((w * kB + rt) * kRow + ri) * 4);
+      }
+      const uint32_t vb = cur.vv;
+      const float2_t vr = {__builtin_bit_cast(float, vb << 16), __builtin_bit_cast(float, vb & 0xFFFF0000u)};
+      float2_t r2;
+      if constexpr (kPaper) {
+        const float2_t lng = *reinterpret_cast<const float2_t*>(&sh.lnp[0][ri]);
+        const float2_t lnb = *reinterpret_cast<const float2_t*>(&sh.lnp[1][ri]);
+        const Ln2 st2 = ln2_row(s2, a.ln_eps);
+        const float2_t kr = {__builtin_bit_cast(float, cur.kv << 16), __builtin_bit_cast(float, cur.kv & 0xFFFF0000u)};
+        const float2_t err = kDot ? -vr : kr + lng * st2.xh + lnb - vr;
+        const float2_t gg = lng * err;
+        const float2_t m = sum32x2(float2_t{gg[0] + gg[1], gg[0] * st2.xh[0] + gg[1] * st2.xh[1]}) * (1.0f / kD);
+        r2 = st2.rstd * (gg - m[0] - st2.xh * m[1]);
+      } else {
+        r2 = s2 - vr;
+      }
+      const float nrate = -eta * cur.et;
+      const uint32_t rp = pack_bf16(r2[0] * nrate, r2[1] * nrate);
+      lds_store<uint32_t>(rrb, (rt * kRRow + ri) * 2, rp);
+      lds_store<uint16_t>(rtb, (ri * kTRow + rt) * 2, static_cast<uint16_t>(rp));
+      lds_store<uint16_t>(rtb, ((ri + 1) * kTRow + rt) * 2, static_cast<uint16_t>(rp >> 16));
+    }
+    barrier();
+    u32x2 rb[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) rb[it] = lds_load<u32x2>(rtb, ((16 * it + n) * kTRow + 4 * g) * 2);
+    bf16x8_t rrow[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) rrow[h] = bf(lds_load<u32x4>(rrb, (n * kRRow + 32 * h + 8 * g) * 2));
+    u32x2 dub[kHT];
+#pragma unroll
+    for (int aa = 0; aa < kHT; ++aa) {
+      float4_t da = zero;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const u32x2 lo = lds_load_tr(w2lds, w2off(32 * h + 8 * g + (n >> 2), 4 * aa + (n & 3)));
+        const u32x2 hi2v = lds_load_tr(w2lds, w2off(32 * h + 8 * g + 4 + (n >> 2), 4 * aa + (n & 3)));
+        const u32x4 w2k = {lo.x, lo.y, hi2v.x, hi2v.y};
+        da = mfma(rrow[h], bf(w2k), da);
+      }
+      dub[aa] = k16(da * sd[aa]);
+    }
+    update_state(st, cur.kt, dub, ab, rb);
+#pragma unroll
+    for (int aa = 0; aa < kHT; ++aa) {
+      pdub[aa] = dub[aa];
+      pab[aa] = ab[aa];
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) prb[it] = rb[it];
+  };
+
+  MainIn ca, cb;
+  load_main<kPaper>(ca, k, v, etok, 0, seq_bytes, o);
+  int c = 0;
+  for (; c + 1 < nchunks; c += 2) {
+    step(ca, cb, c);
+    step(cb, ca, c + 1);
+  }
+  if (c < nchunks) step(ca, cb, c);
+  publish(nchunks);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): every operand store of this wave is complete
+  barrier();
+  if (wv == 0) progress(nchunks);
+  // final state (the output workgroup holds the same values; the recursion writes it)
+  store_state(st, a.w1_out ? a.w1_out + static_cast<size_t>(chain) * hd : nullptr,
+              a.w2_out ? a.w2_out + static_cast<size_t>(chain) * hd : nullptr, h0, g, n);
+}
+
+template <bool kPaper>
+__device__ __forceinline__ void load_hand(Hand& hd, __amdgpu_buffer_rsrc_t rs, int c, int wv, int lane) {
+  const int off = c * kSlotBytes;
+  constexpr int kSc1 = 16;  // device scope: read at the XCC's L2, past the CU's cache
+  hd.du = __builtin_amdgcn_raw_buffer_load_b128(rs, off + wv * 2048 + lane * 16, 0, kSc1);
+  hd.ab = __builtin_amdgcn_raw_buffer_load_b128(rs, off + wv * 2048 + 1024 + lane * 16, 0, kSc1);
+  hd.r0 = __builtin_amdgcn_raw_buffer_load_b128(rs, off + kWaves * 2048 + lane * 16, 0, kSc1);
+  hd.r1 = __builtin_amdgcn_raw_buffer_load_b128(rs, off + kWaves * 2048 + 1024 + lane * 16, 0, kSc1);
+}
+
+template <bool kDot, bool kPaper>
+__device__ __forceinline__ void split_outputs(const MlpArgs& a, SplitLds& sl, int chain, const char* slots,
+                                              unsigned long long* flag, unsigned long long tag) {
+  Lds& sh = sl.base;
+  lds_char* zpart = (lds_char*)(&sh.zpart[0][0][0]);
+  const int tid = threadIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 4;
+  const int n = lane & 15;
+  const int bi = chain / a.H;
+  const int hi = chain - bi * a.H;
+  const int T = a.T;
+  const int nchunks = (T + kB - 1) / kB;
+  const int seq_bytes = T * kD * 2;
+  const size_t tok0 = static_cast<size_t>(chain) * static_cast<size_t>(T) * kD;
+  const char* q = reinterpret_cast<const char*>(static_cast<const bf16*>(a.q) + tok0);
+  const char* k = reinterpret_cast<const char*>(static_cast<const bf16*>(a.k) + tok0);
+  char* z = reinterpret_cast<char*>(static_cast<bf16*>(a.z) + tok0);
+  const size_t hd = static_cast<size_t>(kH) * kD;
+  const float* w1g = a.w1 + bi * a.w_batch_stride + static_cast<long long>(hi) * hd;
+  const float* w2g = a.w2 + bi * a.w_batch_stride + static_cast<long long>(hi) * hd;
+  const int h0 = 16 * kHT * wv;
+  if (kPaper && tid < 2 * kD) sh.lnp[tid / kD][tid % kD] = (tid < kD ? a.ln_w : a.ln_b)[hi * kD + tid % kD];
+  if (tid == 0) sl.abort_flag = 0;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(slots), 0, nchunks * kSlotBytes, 0x00020000);
+
+  State st;
+  init_state(st, w1g, w2g, h0, g, n);
+  const uint32_t one = 0x3F80u;
+  const u32x2 eye = {(4 * g + 0 == n ? one : 0u) | (4 * g + 1 == n ? one << 16 : 0u),
+                     (4 * g + 2 == n ? one : 0u) | (4 * g + 3 == n ? one << 16 : 0u)};
+  const bool keep[4] = {4 * g + 0 <= n, 4 * g + 1 <= n, 4 * g + 2 <= n, 4 * g + 3 <= n};
+  Offsets o;
+  o.row = n * 128 + 32 * g;
+  const int c0 = 16 * (n >> 2) + 2 * (n & 3);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o.kt[e] = (4 * g + e) * 128 + 2 * c0;
+  const int rt = tid >> 5;
+  const int ri = 2 * (tid & 31);
+  o.vv = rt * 128 + 2 * ri;
+  o.et = rt * 4;
+  const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  const float2_t zero2 = {0.0f, 0.0f};
+
+  // XCC ids: post this workgroup's, wait for the recursion's
+  const unsigned long long xp = xcc_id();
+  if (wv == 0 && lane == 0) {
+    __hip_atomic_store(flag + 2, (tag << 32) | xp, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    int spins = 0;
+    unsigned long long h = 0;
+    for (;;) {
+      h = __hip_atomic_load(flag + 1, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+      if ((h >> 32) == tag) break;
+      if (++spins > kSpinLimit) {
+        sl.abort_flag = 1;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    sl.same_xcc = ((h >> 32) == tag && (h & 0xffffffffull) == xp) ? 1 : 0;
+  }
+  // chunks known complete (wave 0 only); wait until at least `need` are.  `ahead` holds the
+  // progress word as read one chunk earlier.
+  int pub = 0;
+  bool same = false;  // wave 0: set after the first barrier
+  unsigned long long ahead = 0;
+  auto wait_for = [&](int need) {
+    if (wv == 0) {
+      if (pub < need) {
+        int got = pub;
+        if (lane == 0) {
+          unsigned long long f = ahead;
+          int spins = 0;
+          while (!((f >> 32) == tag && static_cast<int>(f & 0xffffffffu) >= need)) {
+            if (++spins > kSpinLimit) {
+              sl.abort_flag = 1;
+              break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+            f = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+          got = spins > kSpinLimit ? nchunks : static_cast<int>(f & 0xffffffffu);
+          // across XCCs the progress word came with an agent-scope release: acquire it
+          if (!same) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
+        pub = __builtin_amdgcn_readfirstlane(got);
+      }
+      if (lane == 0) ahead = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+
+  uint32_t qv_prev = 0u;
+  auto reduce_store_z = [&](int c) {
+    float2_t s2 = zero2;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) s2 += lds_load<float2_t>(zpart, ((w * kB + rt) * kRow + ri) * 4);
+    if constexpr (kPaper) {
+      const float2_t lng = *reinterpret_cast<const float2_t*>(&sh.lnp[0][ri]);
+      const float2_t lnb = *reinterpret_cast<const float2_t*>(&sh.lnp[1][ri]);
+      const Ln2 st2 = ln2_row(s2, a.ln_eps);
+      s2 = float2_t{__builtin_bit_cast(float, qv_prev << 16), __builtin_bit_cast(float, qv_prev & 0xFFFF0000u)} +
+           lng * st2.xh + lnb;
+    }
+    const int off = c * kTileBytes;
+    __builtin_amdgcn_raw_buffer_store_b32(pack_bf16(s2[0], s2[1]), chunk_rsrc(z + off, seq_bytes - off), o.vv, 0,
+                                          0);
+  };
+
+  int cdone = 0;  // chunks whose outputs are stored
+  auto step = [&](const PartIn& cur, PartIn& nxt, const Hand& hc, Hand& hn, int c) -> bool {
+    wait_for(c + 2 < nchunks ? c + 2 : nchunks);
+    barrier();
+    if (sl.abort_flag) return false;
+    load_part<kPaper>(nxt, q, k, c + 1, seq_bytes, o);
+    load_hand<kPaper>(hn, rs, c + 1, wv, lane);
+    const bf16x8_t ka0 = bf(cur.ka0), ka1 = bf(cur.ka1), qb0 = bf(cur.qb0), qb1 = bf(cur.qb1);
+    const u32x2 dub[kHT] = {lo2(hc.du), hi2(hc.du)};
+    const u32x2 ab[kHT] = {lo2(hc.ab), hi2(hc.ab)};
+    const u32x2 rb[4] = {lo2(hc.r0), hi2(hc.r0), lo2(hc.r1), hi2(hc.r1)};
+    bf16x8_t w1b[2][kHT];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int aa = 0; aa < kHT; ++aa) w1b[h][aa] = pair_op(st.w1t[2 * h][aa], st.w1t[2 * h + 1][aa]);
+    float4_t actT[kHT];
+#pragma unroll
+    for (int aa = 0; aa < kHT; ++aa) actT[aa] = mfma16(ab[aa], eye, zero);
+    const bf16x8_t atb = cat_op(actT[0], actT[1]);
+    float4_t pt = mfma(ka0, qb0, zero);
+    pt = mfma(ka1, qb1, pt);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pt[e] = keep[e] ? pt[e] : 0.0f;
+    const bf16x8_t ptb = pad_op(pt);
+    float4_t aqT[kHT];
+#pragma unroll
+    for (int aa = 0; aa < kHT; ++aa) {
+      float4_t u = mfma(w1b[0][aa], qb0, zero);
+      u = mfma(w1b[1][aa], qb1, u);
+      u = mfma(pad2(dub[aa]), ptb, u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[e] = act_only<kPaper>(u[e]);
+      aqT[aa] = u;
+    }
+    const bf16x8_t aqb = cat_op(aqT[0], aqT[1]);
+    float4_t gt = mfma(atb, aqb, zero);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) gt[e] = keep[e] ? gt[e] : 0.0f;
+    const bf16x8_t gtb = pad_op(gt);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const bf16x8_t w2o = bf(cat_u(st.w2t[0][it], st.w2t[1][it]));
+      float4_t zt = mfma(w2o, aqb, zero);
+      zt = mfma(pad2(rb[it]), gtb, zt);
+      lds_store<float4_t>(zpart, ((wv * kB + n) * kRow + 16 * it + 4 * g) * 4, zt);
+    }
+    barrier();
+    qv_prev = cur.qv;
+    reduce_store_z(c);
+    cdone = c + 1;
+    update_state(st, cur.kt, dub, ab, rb);
+    return true;
+  };
+
+  PartIn ca, cb;
+  Hand ha, hb;
+  barrier();
+  same = sl.same_xcc != 0;
+  wait_for(nchunks > 0 ? 1 : 0);
+  barrier();
+  bool ok = sl.abort_flag == 0;
+  if (ok) {
+    load_part<kPaper>(ca, q, k, 0, seq_bytes, o);
+    load_hand<kPaper>(ha, rs, 0, wv, lane);
+    int c = 0;
+    for (; ok && c + 1 < nchunks; c += 2) {
+      ok = step(ca, cb, ha, hb, c);
+      if (ok) ok = step(cb, ca, hb, ha, c + 1);
+    }
+    if (ok && c < nchunks) ok = step(ca, cb, ha, hb, c);
+  }
+  if (!ok) {  // the recursion never published: no outputs from here on
+    const uint32_t nan2 = 0x7FC07FC0u;
+    for (int c = cdone; c < nchunks; ++c) {
+      const int off = c * kTileBytes;
+      __builtin_amdgcn_raw_buffer_store_b32(nan2, chunk_rsrc(z + off, seq_bytes - off), o.vv, 0, 0);
+    }
+  }
+}
+
+template <bool kDot, bool kPaper>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void mlp_split_kernel(
+    MlpArgs a, char* ws, unsigned long long tag, int npad) {
+  __shared__ __attribute__((aligned(16))) SplitLds sl;
+  const int nchains = a.B * a.H;
+  const bool outputs = static_cast<int>(blockIdx.x) >= npad;
+  const int chain = outputs ? static_cast<int>(blockIdx.x) - npad : static_cast<int>(blockIdx.x);
+  if (chain >= nchains) return;
+  const int nchunks = (a.T + kB - 1) / kB;
+  unsigned long long* flag = reinterpret_cast<unsigned long long*>(ws + static_cast<size_t>(chain) * kFlagStride);
+  char* slots = ws + split_flag_bytes(nchains) + static_cast<size_t>(chain) * nchunks * kSlotBytes;
+  if (outputs)
+    split_outputs<kDot, kPaper>(a, sl, chain, slots, flag, tag);
+  else
+    split_recursion<kDot, kPaper>(a, sl, chain, slots, flag, tag);
+}
+
 }  // namespace
 
 bool mlp_fast_supported(const MlpArgs& a, bool bf16_io) {
@@ -649,6 +1260,36 @@ hipError_t launch_mlp_fast(const MlpArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((mlp_mfma_kernel<true, false, false>), grid, block, 0, s, a, nullptr);
   else
     hipLaunchKernelGGL((mlp_mfma_kernel<false, false, false>), grid, block, 0, s, a, nullptr);
+  return hipGetLastError();
+}
+
+size_t mlp_split_workspace_bytes(const MlpArgs& a) {
+  const long long nchains = static_cast<long long>(a.B) * a.H;
+  const long long nchunks = (a.T + kB - 1) / kB;
+  return split_flag_bytes(static_cast<int>(nchains)) + static_cast<size_t>(nchains * nchunks) * kSlotBytes;
+}
+
+bool mlp_split_supported(const MlpArgs& a, bool bf16_io) {
+  const long long nchunks = (a.T + kB - 1) / kB;
+  return mlp_fast_supported(a, bf16_io) && nchunks * kSlotBytes < 0x7fffffffLL &&
+         static_cast<long long>(a.B) * a.H <= (0x7fffffffLL - 8) / 2;
+}
+
+hipError_t launch_mlp_split(const MlpArgs& a, void* ws, uint32_t tag, hipStream_t s) {
+  const int nchains = a.B * a.H;
+  const int npad = (nchains + 7) & ~7;  // a chain's two workgroups share a residue mod 8
+  const dim3 grid(static_cast<unsigned>(2 * npad)), block(kThreads);
+  char* w = static_cast<char*>(ws);
+  const unsigned long long t = tag;
+  const bool paper = a.ln_w != nullptr;
+  if (paper && a.dot_loss)
+    hipLaunchKernelGGL((mlp_split_kernel<true, true>), grid, block, 0, s, a, w, t, npad);
+  else if (paper)
+    hipLaunchKernelGGL((mlp_split_kernel<false, true>), grid, block, 0, s, a, w, t, npad);
+  else if (a.dot_loss)
+    hipLaunchKernelGGL((mlp_split_kernel<true, false>), grid, block, 0, s, a, w, t, npad);
+  else
+    hipLaunchKernelGGL((mlp_split_kernel<false, false>), grid, block, 0, s, a, w, t, npad);
   return hipGetLastError();
 }
 

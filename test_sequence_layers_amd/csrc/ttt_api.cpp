@@ -11,6 +11,7 @@
 #include <atomic>
 #include <initializer_list>
 #include <mutex>
+#include <random>
 #include <string>
 
 #include "../../include/ttt.h"
@@ -213,12 +214,26 @@ int check_ln(const char* fn, const float* ln_w, const float* ln_b, float ln_eps)
   return TTT_OK;
 }
 
-// Shared by ttt_mlp_fwd (W2 SiLU(W1 x), ln_w null) and ttt_mlp_ln_fwd (x + LN(W2 GELU(W1 x))).
+// Tag of one two-workgroup MLP call: its hand-off flags carry it, so that a flag left in a
+// reused workspace by an earlier call (of this process or, through the random start, of
+// another) is not taken for this call's.  Never 0.
+uint32_t next_split_tag() {
+  static std::atomic<uint32_t> counter{[] {
+    std::random_device rd;
+    return static_cast<uint32_t>(rd());
+  }()};
+  uint32_t t = 0;
+  while (t == 0) t = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+  return t;
+}
+
+// Shared by ttt_mlp_fwd (W2 SiLU(W1 x), ln_w null) and ttt_mlp_ln_fwd (x + LN(W2 GELU(W1 x)));
+// the _ws forms pass a workspace for the two-workgroup kernel.
 int mlp_fwd(const char* fn, const void* q, const void* k, const void* v, const float* w1,
             const float* w2, long long w_batch_stride, const float* ln_w, const float* ln_b,
             float ln_eps, void* z, float* w1_out, float* w2_out, int B, int H, int T, int d,
             int dh, int chunk, int causal, float eta, const float* eta_tok, int loss, int epochs,
-            int io_dtype, ttt_stream_t stream) {
+            int io_dtype, ttt_stream_t stream, void* split_ws = nullptr, size_t split_ws_bytes = 0) {
   int rc = check_common(fn, q, k, v, z, B, H, T, d, eta, eta_tok, io_dtype);
   if (rc != TTT_OK) return rc;
   if (loss != TTT_LOSS_MSE && loss != TTT_LOSS_DOT)
@@ -249,7 +264,14 @@ int mlp_fwd(const char* fn, const void* q, const void* k, const void* v, const f
   const bool bf16 = io_dtype == TTT_BF16;
   hipError_t e;
   StreamBuffer ws;
-  if (ttt::mlp_fast_supported(a, bf16)) {
+  if (split_ws && ttt::mlp_split_supported(a, bf16)) {
+    const size_t need = ttt::mlp_split_workspace_bytes(a);
+    if (split_ws_bytes < need)
+      return fail(TTT_E_INVALID, "%s: workspace of %zu bytes, this call needs %zu", fn, split_ws_bytes, need);
+    if ((reinterpret_cast<uintptr_t>(split_ws) & 255) != 0)
+      return fail(TTT_E_INVALID, "%s: workspace must be 256-byte aligned", fn);
+    e = ttt::launch_mlp_split(a, split_ws, next_split_tag(), s);
+  } else if (ttt::mlp_fast_supported(a, bf16)) {
     e = ttt::launch_mlp_fast(a, s);
   } else if (ttt::mlp_nc_supported(a, bf16)) {
     e = ttt::launch_mlp_nc(a, s);
@@ -394,7 +416,7 @@ int io_bytes(int io_dtype) { return io_dtype == TTT_BF16 ? 2 : 4; }
 
 extern "C" {
 
-int ttt_abi_version(void) { return 12; }
+int ttt_abi_version(void) { return 13; }
 
 const char* ttt_last_error(void) { return g_last_error.c_str(); }
 
@@ -766,24 +788,26 @@ static int impl_ttt_linear_ln_fwd(const void* q, const void* k, const void* v, c
 static int impl_ttt_mlp_fwd(const void* q, const void* k, const void* v, const float* w1, const float* w2,
                             long long w_batch_stride, void* z, float* w1_out, float* w2_out, int B, int H,
                             int T, int d, int dh, int chunk, int causal, float eta, const float* eta_tok,
-                            int loss, int epochs, int io_dtype, ttt_stream_t stream) {
+                            int loss, int epochs, int io_dtype, ttt_stream_t stream,
+                            const char* fn = "ttt_mlp_fwd", void* ws = nullptr, size_t ws_bytes = 0) {
   g_last_error.clear();
-  return mlp_fwd("ttt_mlp_fwd", q, k, v, w1, w2, w_batch_stride, nullptr, nullptr, 0.0f, z,
+  return mlp_fwd(fn, q, k, v, w1, w2, w_batch_stride, nullptr, nullptr, 0.0f, z,
                  w1_out, w2_out, B, H, T, d, dh, chunk, causal, eta, eta_tok, loss, epochs,
-                 io_dtype, stream);
+                 io_dtype, stream, ws, ws_bytes);
 }
 
 static int impl_ttt_mlp_ln_fwd(const void* q, const void* k, const void* v, const float* w1, const float* w2,
                                long long w_batch_stride, const float* ln_weight, const float* ln_bias,
                                float ln_eps, void* z, float* w1_out, float* w2_out, int B, int H, int T,
                                int d, int dh, int chunk, int causal, float eta, const float* eta_tok,
-                               int loss, int epochs, int io_dtype, ttt_stream_t stream) {
+                               int loss, int epochs, int io_dtype, ttt_stream_t stream,
+                               const char* fn = "ttt_mlp_ln_fwd", void* ws = nullptr, size_t ws_bytes = 0) {
   g_last_error.clear();
-  const int rc = check_ln("ttt_mlp_ln_fwd", ln_weight, ln_bias, ln_eps);
+  const int rc = check_ln(fn, ln_weight, ln_bias, ln_eps);
   if (rc != TTT_OK) return rc;
-  return mlp_fwd("ttt_mlp_ln_fwd", q, k, v, w1, w2, w_batch_stride, ln_weight, ln_bias, ln_eps,
+  return mlp_fwd(fn, q, k, v, w1, w2, w_batch_stride, ln_weight, ln_bias, ln_eps,
                  z, w1_out, w2_out, B, H, T, d, dh, chunk, causal, eta, eta_tok, loss, epochs,
-                 io_dtype, stream);
+                 io_dtype, stream, ws, ws_bytes);
 }
 
 // ---- public entry points: the calls above, then the optional finite check ----
@@ -841,6 +865,56 @@ int ttt_mlp_ln_fwd(const void* q, const void* k, const void* v, const float* w1,
                                      z, w1_out, w2_out, B, H, T, d, dh, chunk, causal, eta,
                                      eta_tok, loss, epochs, io_dtype, stream);
   return finite_outputs(rc, "ttt_mlp_ln_fwd", stream,
+                        {{"z", z, tok(B, H, T, d), io_bytes(io_dtype)},
+                         {"w1_out", w1_out, per_seq(B, H, 1LL * dh * d), 4},
+                         {"w2_out", w2_out, per_seq(B, H, 1LL * d * dh), 4}});
+}
+
+size_t ttt_mlp_fwd_workspace_size(int B, int H, int T, int d, int dh, int chunk, int causal,
+                                  int io_dtype) {
+  if (B <= 0 || H <= 0 || T <= 0 || static_cast<long long>(B) * H > 0x7fffffffLL) return 0;
+  ttt::MlpArgs a{};
+  // shape-only query: aligned stand-in pointers, so that only the shape decides
+  const void* p = reinterpret_cast<const void*>(uintptr_t(256));
+  a.q = a.k = a.v = p;
+  a.z = const_cast<void*>(p);
+  a.w1 = a.w2 = static_cast<const float*>(p);
+  a.B = B;
+  a.H = H;
+  a.T = T;
+  a.d = d;
+  a.dh = dh;
+  a.chunk = chunk;
+  a.causal = causal;
+  if (!ttt::mlp_split_supported(a, io_dtype == TTT_BF16)) return 0;
+  return ttt::mlp_split_workspace_bytes(a);
+}
+
+int ttt_mlp_fwd_ws(const void* q, const void* k, const void* v, const float* w1, const float* w2,
+                   long long w_batch_stride, void* z, float* w1_out, float* w2_out, int B, int H,
+                   int T, int d, int dh, int chunk, int causal, float eta, const float* eta_tok,
+                   int loss, int epochs, int io_dtype, void* workspace, size_t workspace_bytes,
+                   ttt_stream_t stream) {
+  const int rc = impl_ttt_mlp_fwd(q, k, v, w1, w2, w_batch_stride, z, w1_out, w2_out, B, H, T, d,
+                                  dh, chunk, causal, eta, eta_tok, loss, epochs, io_dtype, stream,
+                                  "ttt_mlp_fwd_ws", workspace, workspace_bytes);
+  return finite_outputs(rc, "ttt_mlp_fwd_ws", stream,
+                        {{"z", z, tok(B, H, T, d), io_bytes(io_dtype)},
+                         {"w1_out", w1_out, per_seq(B, H, 1LL * dh * d), 4},
+                         {"w2_out", w2_out, per_seq(B, H, 1LL * d * dh), 4}});
+}
+
+int ttt_mlp_ln_fwd_ws(const void* q, const void* k, const void* v, const float* w1,
+                      const float* w2, long long w_batch_stride, const float* ln_weight,
+                      const float* ln_bias, float ln_eps, void* z, float* w1_out, float* w2_out,
+                      int B, int H, int T, int d, int dh, int chunk, int causal, float eta,
+                      const float* eta_tok, int loss, int epochs, int io_dtype, void* workspace,
+                      size_t workspace_bytes, ttt_stream_t stream) {
+  const int rc = impl_ttt_mlp_ln_fwd(q, k, v, w1, w2, w_batch_stride, ln_weight, ln_bias, ln_eps,
+                                     z, w1_out, w2_out, B, H, T, d, dh, chunk, causal, eta,
+                                     eta_tok, loss, epochs, io_dtype, stream, "ttt_mlp_ln_fwd_ws",
+                                     workspace, workspace_bytes);
+  return finite_outputs(rc, "ttt_mlp_ln_fwd_ws", stream,
                         {{"z", z, tok(B, H, T, d), io_bytes(io_dtype)},
                          {"w1_out", w1_out, per_seq(B, H, 1LL * dh * d), 4},
                          {"w2_out", w2_out, per_seq(B, H, 1LL * d * dh), 4}});

@@ -91,6 +91,15 @@ def run_gpu(kind, dev, eta, chunk, causal, return_state=True, loss="mse", epochs
     in the MLP)."""
     import test_sequence_layers_amd as ttt
     et = dev.get("eta_tok")
+    if kind == "mlp_ws":  # the two-workgroup MLP kernel (a workspace from the binding)
+        if "ln_w" in dev:
+            return ttt.ttt_mlp_ln_fwd_ws(dev["q"], dev["k"], dev["v"], dev["w1"], dev["w2"],
+                                         dev["ln_w"], dev["ln_b"], eta, chunk, causal,
+                                         ln_eps=LN_EPS, eta_tok=et, loss=loss, epochs=epochs,
+                                         return_state=return_state)
+        return ttt.ttt_mlp_fwd_ws(dev["q"], dev["k"], dev["v"], dev["w1"], dev["w2"], eta, chunk,
+                                  causal, eta_tok=et, loss=loss, epochs=epochs,
+                                  return_state=return_state)
     if "ln_w" in dev:
         ln = (dev["ln_w"], dev["ln_b"])
         if kind == "linear":

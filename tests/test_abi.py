@@ -31,7 +31,8 @@ def test_header_declares_the_entry_points():
     for n in ("ttt_linear_fwd", "ttt_mlp_fwd", "delta_rule_fwd", "ttt_linear_bwd", "ttt_mlp_bwd",
               "ttt_linear_ln_fwd", "ttt_mlp_ln_fwd", "ttt_last_error", "ttt_abi_version",
               "ttt_linear_nc_bwd", "ttt_mlp_nc_bwd", "ttt_linear_bwd_noalloc",
-              "ttt_set_check_finite", "ttt_get_check_finite"):
+              "ttt_set_check_finite", "ttt_get_check_finite", "ttt_mlp_fwd_workspace_size",
+              "ttt_mlp_fwd_ws", "ttt_mlp_ln_fwd_ws"):
         assert n in names
 
 
@@ -42,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ttt_abi_version() == 12
+    assert lib.ttt_abi_version() == 13
 
 
 FAKE = 0x1000  # never dereferenced: validation fails before any HIP call
@@ -234,6 +235,42 @@ def _mlp_bwd(lib, **kw):
 def test_mlp_bwd_rejects(lib, kw, code, msg):
     assert _mlp_bwd(lib, **kw) == code
     assert msg in ttt.last_error()
+
+
+def test_mlp_workspace_size(lib):
+    # causal d 64, hidden 256, chunk 16, bf16: 128-byte flags per sequence (rounded up to
+    # 256 bytes) and 18 KB of hand-off per chunk of 16 tokens
+    B, H, T = 8, 12, 2048
+    flags = (B * H * 128 + 255) // 256 * 256
+    assert lib.ttt_mlp_fwd_workspace_size(B, H, T, 64, 256, 16, 1, 1) == flags + B * H * (T // 16) * 18432
+    assert lib.ttt_mlp_fwd_workspace_size(1, 1, 17, 64, 256, 16, 1, 1) == 256 + 2 * 18432
+    # every other shape needs none (the _ws call is then the plain one)
+    for args in [(8, 12, 2048, 64, 256, 16, 0, 1), (8, 12, 2048, 64, 256, 16, 1, 0),
+                 (8, 12, 2048, 64, 128, 16, 1, 1), (8, 12, 2048, 32, 256, 16, 1, 1),
+                 (8, 12, 2048, 64, 256, 8, 1, 1), (8, 12, 0, 64, 256, 16, 1, 1),
+                 (0, 12, 2048, 64, 256, 16, 1, 1)]:
+        assert lib.ttt_mlp_fwd_workspace_size(*args) == 0, args
+
+
+def _mlp_ws(lib, ws, ws_bytes, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, w1=FAKE, w2=FAKE, stride=0, z=FAKE, B=2, H=3, T=40, d=64,
+             dh=256, chunk=16, causal=1, eta=0.1, eta_tok=None, loss=0, epochs=1, io=1)
+    a.update(kw)
+    return lib.ttt_mlp_fwd_ws(a["q"], a["k"], a["v"], a["w1"], a["w2"], a["stride"], a["z"], None,
+                              None, a["B"], a["H"], a["T"], a["d"], a["dh"], a["chunk"],
+                              a["causal"], a["eta"], a["eta_tok"], a["loss"], a["epochs"],
+                              a["io"], ws, ws_bytes, None)
+
+
+def test_mlp_ws_rejects_a_small_or_misaligned_workspace(lib):
+    need = lib.ttt_mlp_fwd_workspace_size(2, 3, 40, 64, 256, 16, 1, 1)
+    assert _mlp_ws(lib, 0x10000, need - 1) == ttt.TTT_E_INVALID
+    assert "workspace of" in ttt.last_error() and "ttt_mlp_fwd_ws" in ttt.last_error()
+    assert _mlp_ws(lib, 0x10010, need) == ttt.TTT_E_INVALID
+    assert "256-byte aligned" in ttt.last_error()
+    # the usual argument checks come first
+    assert _mlp_ws(lib, 0x10000, need, q=None) == ttt.TTT_E_INVALID
+    assert "non-null" in ttt.last_error()
 
 
 def test_error_text_is_per_call(lib):

@@ -165,6 +165,88 @@ def test_mlp_vision_config_full_size():
     _check("mlp", w, make_inputs(w), full=True)
 
 
+# ------------------------------------------------------------------ two workgroups per chain
+# ttt_mlp_fwd_ws / ttt_mlp_ln_fwd_ws: the recursion on one compute unit, the outputs on a
+# second that replays the same updates.  Same operands and products in the same order as the
+# one-workgroup kernel, so z and the final states must match it bit for bit; and the oracle.
+
+def _ws_same_as_one_workgroup(w, inp, loss="mse"):
+    import torch
+    import test_sequence_layers_amd as ttt
+    dev = to_device(inp, w.io)
+    one = run_gpu("mlp", dev, w.eta, w.chunk, w.causal, loss=loss)
+    ws_bytes = ttt.ttt_mlp_fwd_workspace_size(w.B, w.H, w.T, w.d, w.h, w.chunk, w.causal, w.io)
+    assert ws_bytes > 0
+    # a workspace that holds garbage (and, on the second call, the first call's flags)
+    ws = torch.full((ws_bytes,), 0xA5, dtype=torch.uint8, device=dev["q"].device)
+    et = dev.get("eta_tok")
+    for rep in range(2):
+        if "ln_w" in dev:
+            two = ttt.ttt_mlp_ln_fwd_ws(dev["q"], dev["k"], dev["v"], dev["w1"], dev["w2"],
+                                        dev["ln_w"], dev["ln_b"], w.eta, w.chunk, w.causal,
+                                        workspace=ws, ln_eps=1e-6, eta_tok=et, loss=loss,
+                                        return_state=True)
+        else:
+            two = ttt.ttt_mlp_fwd_ws(dev["q"], dev["k"], dev["v"], dev["w1"], dev["w2"], w.eta,
+                                     w.chunk, w.causal, workspace=ws, eta_tok=et, loss=loss,
+                                     return_state=True)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("z", "w1_out", "w2_out"), one, two):
+            same = torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+            _note(f"[parity]   call {rep}: {name} bit-identical to the one-workgroup kernel: {same}")
+            assert same, name
+
+
+@pytest.mark.parametrize("T,B,H", [(16, 1, 1), (17, 1, 3), (100, 2, 3), (333, 3, 3), (2048, 1, 2)])
+def test_mlp_ws_matches_one_workgroup_kernel(T, B, H):
+    w = workload(3).replace(B=B, H=H, T=T, seed=70 + T)
+    _note(f"[parity] mlp_ws bit-identity B={B} H={H} T={T}")
+    _ws_same_as_one_workgroup(w, make_inputs(w))
+
+
+@pytest.mark.parametrize("loss,rates,paper", [("dot", False, False), ("mse", True, False),
+                                              ("mse", False, True), ("dot", True, True)])
+def test_mlp_ws_variants_match_one_workgroup_kernel(loss, rates, paper):
+    w = workload(3).replace(B=2, H=3, T=150, seed=80)
+    inp = _with_rates(w, 15) if rates else make_inputs(w)
+    if paper:
+        inp["ln_w"], inp["ln_b"] = make_ln_params(w, 10)
+    _note(f"[parity] mlp_ws variant loss={loss} rates={rates} paper={paper}")
+    _ws_same_as_one_workgroup(w, inp, loss=loss)
+
+
+@pytest.mark.parametrize("T", [16, 77, 200])
+def test_mlp_ws_small(T):
+    w = workload(3).replace(B=2, H=3, T=T, seed=90 + T)
+    _check("mlp_ws", w, make_inputs(w))
+
+
+def test_mlp_ws_config_full_size():
+    w = workload(3)
+    _check("mlp_ws", w, make_inputs(w), full=True)
+
+
+def test_mlp_ws_config_full_size_same_as_one_workgroup():
+    w = workload(3)
+    _ws_same_as_one_workgroup(w, make_inputs(w))
+
+
+def test_mlp_ws_paper_config_full_size():
+    w = workload(3)
+    inp = make_inputs(w)
+    inp["ln_w"], inp["ln_b"] = make_ln_params(w, 8)
+    _check("mlp_ws", w, inp, full=True)
+
+
+def test_mlp_ws_other_shapes_run_the_plain_call():
+    # no workspace is needed (size 0) for any other shape; the _ws call is then ttt_mlp_fwd
+    import test_sequence_layers_amd as ttt
+    w = workload(3).replace(B=1, H=2, T=37, d=16, h=32, io="f32", seed=99)
+    assert ttt.ttt_mlp_fwd_workspace_size(w.B, w.H, w.T, w.d, w.h, w.chunk, w.causal, w.io) == 0
+    _check("mlp_ws", w, make_inputs(w))
+
+
 # ------------------------------------------------------------------ edge cases
 
 def test_zero_length_sequence_returns_initial_state():
