@@ -4,6 +4,7 @@
 // rejection must return the documented status and leave a message naming the function; the
 // calls also run on several threads at once, since the message buffer is per thread.
 #include <cmath>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 #include <thread>
@@ -52,6 +53,25 @@ void run_all() {
          TTT_E_INVALID, "ttt_mlp_fwd", "dh = 0");
   expect(ttt_mlp_fwd(P, P, P, F, F, 0, P, nullptr, nullptr, 1, 1, 16, 64, 4096, 16, 1, 0.1f, nullptr, 0, 1, TTT_BF16, nullptr),
          TTT_E_UNSUPPORTED, "ttt_mlp_fwd", "dh = 4096");
+  {
+    // the two-workgroup MLP entry points: a workspace one byte short, then a misaligned one
+    const size_t need = ttt_mlp_fwd_workspace_size(2, 3, 40, 64, 256, 16, 1, TTT_BF16);
+    if (need == 0) {
+      std::printf("FAIL ttt_mlp_fwd_workspace_size: 0 for the d 64 shape\n");
+      ++failures;
+    }
+    void* ws = reinterpret_cast<void*>(uintptr_t(0x10000));
+    void* ws_mis = reinterpret_cast<void*>(uintptr_t(0x10010));
+    expect(ttt_mlp_fwd_ws(P, P, P, F, F, 0, P, nullptr, nullptr, 2, 3, 40, 64, 256, 16, 1, 0.1f, nullptr, 0, 1,
+                          TTT_BF16, ws, need - 1, nullptr),
+           TTT_E_INVALID, "ttt_mlp_fwd_ws", "small workspace");
+    expect(ttt_mlp_fwd_ws(P, P, P, F, F, 0, P, nullptr, nullptr, 2, 3, 40, 64, 256, 16, 1, 0.1f, nullptr, 0, 1,
+                          TTT_BF16, ws_mis, need, nullptr),
+           TTT_E_INVALID, "ttt_mlp_fwd_ws", "misaligned workspace");
+    expect(ttt_mlp_ln_fwd_ws(P, P, P, F, F, 0, F, F, 0.0f, P, nullptr, nullptr, 2, 3, 40, 64, 256, 16, 1, 0.1f,
+                             nullptr, 0, 1, TTT_BF16, ws, need, nullptr),
+           TTT_E_INVALID, "ttt_mlp_ln_fwd_ws", "ln_eps 0");
+  }
   expect(ttt_linear_ln_fwd(P, P, P, F, 0, nullptr, F, 1e-6f, P, nullptr, 1, 1, 16, 64, 16, 1, 0.1f, nullptr, 0, 1, TTT_BF16, nullptr),
          TTT_E_INVALID, "ttt_linear_ln_fwd", "null ln weight");
   expect(ttt_mlp_ln_fwd(P, P, P, F, F, 0, F, F, 1e-6f, P, nullptr, nullptr, -1, 1, 16, 64, 256, 16, 1, 0.1f, nullptr, 0, 1, TTT_BF16, nullptr),
