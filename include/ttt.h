@@ -369,6 +369,19 @@ const char* ttt_last_error(void);
 int ttt_set_check_finite(int on);
 int ttt_get_check_finite(void);
 
+/*
+ * Debug switches of the two-workgroup MLP kernel (ttt_mlp_fwd_ws, ttt_mlp_ln_fwd_ws), for
+ * tests of its paths that a normal run does not take; set for the process, read at each
+ * call.  TTT_SPLIT_FORMAL: hand off with agent-scope release and acquire on every chunk, the
+ * path taken when the two workgroups of a sequence sit on different XCCs (results are
+ * identical, the call is slower).  TTT_SPLIT_TEST_ABORT: the output workgroups wait for a
+ * tag the recursion never writes, with a bound of 64 polls, so that they take the failure
+ * path at once: every z of the call is NaN, the final states are right, and the call returns
+ * TTT_OK.  Returns the previous flags; 0 turns both off.
+ */
+enum { TTT_SPLIT_FORMAL = 1, TTT_SPLIT_TEST_ABORT = 2 };
+int ttt_set_split_debug(int flags);
+
 /* ABI version of this header (incremented on any incompatible change). */
 int ttt_abi_version(void);
 

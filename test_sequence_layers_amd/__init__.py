@@ -23,6 +23,7 @@ from ._binding import (  # noqa: F401
     last_error,
     load_library,
     set_check_finite,
+    set_split_debug,
     ttt_linear_bwd,
     ttt_linear_bwd_noalloc,
     ttt_linear_fwd,

@@ -59,6 +59,7 @@ SIGNATURES = {
     "ttt_abi_version": (_i, []),
     "ttt_set_check_finite": (_i, [_i]),
     "ttt_get_check_finite": (_i, []),
+    "ttt_set_split_debug": (_i, [_i]),
 }
 
 
@@ -95,6 +96,12 @@ def set_check_finite(on: bool) -> bool:
     then wait for their stream and fail with TTT_E_NONFINITE on a NaN or an infinity).
     Returns the previous setting."""
     return bool(load_library().ttt_set_check_finite(1 if on else 0))
+
+
+def set_split_debug(flags: int) -> int:
+    """Debug switches of the two-workgroup MLP kernel (TTT_SPLIT_FORMAL = 1,
+    TTT_SPLIT_TEST_ABORT = 2); returns the previous flags."""
+    return int(load_library().ttt_set_split_debug(int(flags)))
 
 
 def get_check_finite() -> bool:

@@ -186,7 +186,7 @@ hipError_t launch_mlp_fast(const MlpArgs& a, hipStream_t s);
 // the same layer on two workgroups per chain (recursion, outputs) with a caller workspace
 bool mlp_split_supported(const MlpArgs& a, bool bf16_io);
 size_t mlp_split_workspace_bytes(const MlpArgs& a);
-hipError_t launch_mlp_split(const MlpArgs& a, void* ws, uint32_t tag, hipStream_t s);
+hipError_t launch_mlp_split(const MlpArgs& a, void* ws, uint32_t tag, int dbg, hipStream_t s);
 bool linear_nc_supported(const LinearArgs& a, bool bf16_io);
 hipError_t launch_linear_nc(const LinearArgs& a, hipStream_t s);
 bool mlp_nc_supported(const MlpArgs& a, bool bf16_io);

@@ -662,6 +662,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 constexpr int kSlotBytes = kWaves * 2048 + 2048;  // one chunk's hand-off
 constexpr int kFlagStride = 128;
 constexpr int kSpinLimit = 1 << 20;
+// debug switches (ttt_set_split_debug): the agent-scope protocol whatever the placement; a
+// forced failure of the output workgroup's first wait with a bound of 64 polls
+constexpr int kSplitFormal = 1;
+constexpr int kSplitTestAbort = 2;
 __device__ __forceinline__ unsigned long long xcc_id() {
   return static_cast<unsigned long long>(__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 15);  // HW_REG_XCC_ID
 }
@@ -808,7 +812,7 @@ __device__ __forceinline__ u32x2 hi2(const u32x4& x) { return u32x2{x.z, x.w}; }
 
 template <bool kDot, bool kPaper>
 __device__ __forceinline__ void split_recursion(const MlpArgs& a, SplitLds& sl, int chain, char* slots,
-                                                unsigned long long* flag, unsigned long long tag) {
+                                                unsigned long long* flag, unsigned long long tag, int dbg) {
   Lds& sh = sl.base;
   lds_char* opart = (lds_char*)(&sh.opart[0][0][0]);
   lds_char* rrb = (lds_char*)(&sh.rr[0][0]);
@@ -861,7 +865,7 @@ __device__ __forceinline__ void split_recursion(const MlpArgs& a, SplitLds& sl, 
   if (wv == 0 && lane == 0) __hip_atomic_store(hello_own, (tag << 32) | xm, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
   // wave 0: 0 = partner's XCC not seen yet, 1 = same XCC, 2 = another XCC; the partner's word
   // is read one chunk before it is looked at
-  int mode = 0;
+  int mode = (dbg & kSplitFormal) ? 2 : 0;
   unsigned long long other = 0;
   auto progress = [&](int count) {  // wave 0, after a barrier
     if (lane == 0) {
@@ -1028,7 +1032,10 @@ __device__ __forceinline__ void load_hand(Hand& hd, __amdgpu_buffer_rsrc_t rs, i
 
 template <bool kDot, bool kPaper>
 __device__ __forceinline__ void split_outputs(const MlpArgs& a, SplitLds& sl, int chain, const char* slots,
-                                              unsigned long long* flag, unsigned long long tag) {
+                                              unsigned long long* flag, unsigned long long tag, int dbg) {
+  // failure-path test: wait for a tag the recursion never writes, with a short bound
+  const unsigned long long want_tag = (dbg & kSplitTestAbort) ? (tag ^ 1ull) : tag;
+  const int spin_limit = (dbg & kSplitTestAbort) ? 64 : kSpinLimit;
   Lds& sh = sl.base;
   lds_char* zpart = (lds_char*)(&sh.zpart[0][0][0]);
   const int tid = threadIdx.x;
@@ -1080,14 +1087,14 @@ __device__ __forceinline__ void split_outputs(const MlpArgs& a, SplitLds& sl, in
     unsigned long long h = 0;
     for (;;) {
       h = __hip_atomic_load(flag + 1, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-      if ((h >> 32) == tag) break;
-      if (++spins > kSpinLimit) {
+      if ((h >> 32) == want_tag) break;
+      if (++spins > spin_limit) {
         sl.abort_flag = 1;
         break;
       }
       __builtin_amdgcn_s_sleep(2);
     }
-    sl.same_xcc = ((h >> 32) == tag && (h & 0xffffffffull) == xp) ? 1 : 0;
+    sl.same_xcc = ((h >> 32) == want_tag && (h & 0xffffffffull) == xp && !(dbg & kSplitFormal)) ? 1 : 0;
   }
   // chunks known complete (wave 0 only); wait until at least `need` are.  `ahead` holds the
   // progress word as read one chunk earlier.
@@ -1102,14 +1109,14 @@ __device__ __forceinline__ void split_outputs(const MlpArgs& a, SplitLds& sl, in
           unsigned long long f = ahead;
           int spins = 0;
           while (!((f >> 32) == tag && static_cast<int>(f & 0xffffffffu) >= need)) {
-            if (++spins > kSpinLimit) {
+            if (++spins > spin_limit) {
               sl.abort_flag = 1;
               break;
             }
             __builtin_amdgcn_s_sleep(2);
             f = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
-          got = spins > kSpinLimit ? nchunks : static_cast<int>(f & 0xffffffffu);
+          got = spins > spin_limit ? nchunks : static_cast<int>(f & 0xffffffffu);
           // across XCCs the progress word came with an agent-scope release: acquire it
           if (!same) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         }
@@ -1219,7 +1226,7 @@ __device__ __forceinline__ void split_outputs(const MlpArgs& a, SplitLds& sl, in
 
 template <bool kDot, bool kPaper>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void mlp_split_kernel(
-    MlpArgs a, char* ws, unsigned long long tag, int npad) {
+    MlpArgs a, char* ws, unsigned long long tag, int npad, int dbg) {
   __shared__ __attribute__((aligned(16))) SplitLds sl;
   const int nchains = a.B * a.H;
   const bool outputs = static_cast<int>(blockIdx.x) >= npad;
@@ -1229,9 +1236,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   unsigned long long* flag = reinterpret_cast<unsigned long long*>(ws + static_cast<size_t>(chain) * kFlagStride);
   char* slots = ws + split_flag_bytes(nchains) + static_cast<size_t>(chain) * nchunks * kSlotBytes;
   if (outputs)
-    split_outputs<kDot, kPaper>(a, sl, chain, slots, flag, tag);
+    split_outputs<kDot, kPaper>(a, sl, chain, slots, flag, tag, dbg);
   else
-    split_recursion<kDot, kPaper>(a, sl, chain, slots, flag, tag);
+    split_recursion<kDot, kPaper>(a, sl, chain, slots, flag, tag, dbg);
 }
 
 }  // namespace
@@ -1275,7 +1282,7 @@ bool mlp_split_supported(const MlpArgs& a, bool bf16_io) {
          static_cast<long long>(a.B) * a.H <= (0x7fffffffLL - 8) / 2;
 }
 
-hipError_t launch_mlp_split(const MlpArgs& a, void* ws, uint32_t tag, hipStream_t s) {
+hipError_t launch_mlp_split(const MlpArgs& a, void* ws, uint32_t tag, int dbg, hipStream_t s) {
   const int nchains = a.B * a.H;
   const int npad = (nchains + 7) & ~7;  // a chain's two workgroups share a residue mod 8
   const dim3 grid(static_cast<unsigned>(2 * npad)), block(kThreads);
@@ -1283,13 +1290,13 @@ hipError_t launch_mlp_split(const MlpArgs& a, void* ws, uint32_t tag, hipStream_
   const unsigned long long t = tag;
   const bool paper = a.ln_w != nullptr;
   if (paper && a.dot_loss)
-    hipLaunchKernelGGL((mlp_split_kernel<true, true>), grid, block, 0, s, a, w, t, npad);
+    hipLaunchKernelGGL((mlp_split_kernel<true, true>), grid, block, 0, s, a, w, t, npad, dbg);
   else if (paper)
-    hipLaunchKernelGGL((mlp_split_kernel<false, true>), grid, block, 0, s, a, w, t, npad);
+    hipLaunchKernelGGL((mlp_split_kernel<false, true>), grid, block, 0, s, a, w, t, npad, dbg);
   else if (a.dot_loss)
-    hipLaunchKernelGGL((mlp_split_kernel<true, false>), grid, block, 0, s, a, w, t, npad);
+    hipLaunchKernelGGL((mlp_split_kernel<true, false>), grid, block, 0, s, a, w, t, npad, dbg);
   else
-    hipLaunchKernelGGL((mlp_split_kernel<false, false>), grid, block, 0, s, a, w, t, npad);
+    hipLaunchKernelGGL((mlp_split_kernel<false, false>), grid, block, 0, s, a, w, t, npad, dbg);
   return hipGetLastError();
 }
 

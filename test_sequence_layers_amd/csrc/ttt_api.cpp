@@ -217,6 +217,9 @@ int check_ln(const char* fn, const float* ln_w, const float* ln_b, float ln_eps)
 // Tag of one two-workgroup MLP call: its hand-off flags carry it, so that a flag left in a
 // reused workspace by an earlier call (of this process or, through the random start, of
 // another) is not taken for this call's.  Never 0.
+// Debug switches of the two-workgroup MLP kernel (ttt_set_split_debug).
+std::atomic<int> g_split_debug{0};
+
 uint32_t next_split_tag() {
   static std::atomic<uint32_t> counter{[] {
     std::random_device rd;
@@ -270,7 +273,7 @@ int mlp_fwd(const char* fn, const void* q, const void* k, const void* v, const f
       return fail(TTT_E_INVALID, "%s: workspace of %zu bytes, this call needs %zu", fn, split_ws_bytes, need);
     if ((reinterpret_cast<uintptr_t>(split_ws) & 255) != 0)
       return fail(TTT_E_INVALID, "%s: workspace must be 256-byte aligned", fn);
-    e = ttt::launch_mlp_split(a, split_ws, next_split_tag(), s);
+    e = ttt::launch_mlp_split(a, split_ws, next_split_tag(), g_split_debug.load(std::memory_order_relaxed), s);
   } else if (ttt::mlp_fast_supported(a, bf16)) {
     e = ttt::launch_mlp_fast(a, s);
   } else if (ttt::mlp_nc_supported(a, bf16)) {
@@ -416,7 +419,7 @@ int io_bytes(int io_dtype) { return io_dtype == TTT_BF16 ? 2 : 4; }
 
 extern "C" {
 
-int ttt_abi_version(void) { return 13; }
+int ttt_abi_version(void) { return 14; }
 
 const char* ttt_last_error(void) { return g_last_error.c_str(); }
 
@@ -819,6 +822,10 @@ int ttt_set_check_finite(int on) {
 }
 
 int ttt_get_check_finite(void) { return check_finite_on() ? 1 : 0; }
+
+int ttt_set_split_debug(int flags) {
+  return g_split_debug.exchange(flags & (TTT_SPLIT_FORMAL | TTT_SPLIT_TEST_ABORT), std::memory_order_relaxed);
+}
 
 int ttt_linear_fwd(const void* q, const void* k, const void* v, const float* w0,
                    long long w0_batch_stride, void* z, float* w_out, int B, int H, int T, int d,

@@ -72,6 +72,10 @@ void run_all() {
                              nullptr, 0, 1, TTT_BF16, ws, need, nullptr),
            TTT_E_INVALID, "ttt_mlp_ln_fwd_ws", "ln_eps 0");
   }
+  if (ttt_set_split_debug(TTT_SPLIT_FORMAL) != 0 || ttt_set_split_debug(0) != TTT_SPLIT_FORMAL) {
+    std::printf("FAIL ttt_set_split_debug: previous flags\n");
+    ++failures;
+  }
   expect(ttt_linear_ln_fwd(P, P, P, F, 0, nullptr, F, 1e-6f, P, nullptr, 1, 1, 16, 64, 16, 1, 0.1f, nullptr, 0, 1, TTT_BF16, nullptr),
          TTT_E_INVALID, "ttt_linear_ln_fwd", "null ln weight");
   expect(ttt_mlp_ln_fwd(P, P, P, F, F, 0, F, F, 1e-6f, P, nullptr, nullptr, -1, 1, 16, 64, 256, 16, 1, 0.1f, nullptr, 0, 1, TTT_BF16, nullptr),

@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
               "ttt_linear_ln_fwd", "ttt_mlp_ln_fwd", "ttt_last_error", "ttt_abi_version",
               "ttt_linear_nc_bwd", "ttt_mlp_nc_bwd", "ttt_linear_bwd_noalloc",
               "ttt_set_check_finite", "ttt_get_check_finite", "ttt_mlp_fwd_workspace_size",
-              "ttt_mlp_fwd_ws", "ttt_mlp_ln_fwd_ws"):
+              "ttt_mlp_fwd_ws", "ttt_mlp_ln_fwd_ws", "ttt_set_split_debug"):
         assert n in names
 
 
@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ttt_abi_version() == 13
+    assert lib.ttt_abi_version() == 14
 
 
 FAKE = 0x1000  # never dereferenced: validation fails before any HIP call
@@ -271,6 +271,16 @@ def test_mlp_ws_rejects_a_small_or_misaligned_workspace(lib):
     # the usual argument checks come first
     assert _mlp_ws(lib, 0x10000, need, q=None) == ttt.TTT_E_INVALID
     assert "non-null" in ttt.last_error()
+
+
+def test_split_debug_switch(lib):
+    prev = lib.ttt_set_split_debug(3)
+    try:
+        assert lib.ttt_set_split_debug(1) == 3
+        assert lib.ttt_set_split_debug(0xFF) == 1
+        assert lib.ttt_set_split_debug(0) == 3      # unknown bits are dropped
+    finally:
+        lib.ttt_set_split_debug(prev)
 
 
 def test_error_text_is_per_call(lib):

@@ -239,6 +239,38 @@ def test_mlp_ws_paper_config_full_size():
     _check("mlp_ws", w, inp, full=True)
 
 
+def test_mlp_ws_formal_protocol_is_bit_identical():
+    # the agent-scope hand-off (the path for workgroups on different XCCs), forced
+    import test_sequence_layers_amd as ttt
+    w = workload(3).replace(B=2, H=3, T=333, seed=95)
+    prev = ttt.set_split_debug(1)
+    try:
+        _note("[parity] mlp_ws with the agent-scope hand-off forced")
+        _ws_same_as_one_workgroup(w, make_inputs(w))
+    finally:
+        ttt.set_split_debug(prev)
+
+
+def test_mlp_ws_forced_failure_fills_nan_and_returns():
+    # the output workgroups' bounded wait, made to fail from the host: z is all NaN, the
+    # recursion's final states are still right, and the next call is normal again
+    import torch
+    import test_sequence_layers_amd as ttt
+    w = workload(3).replace(B=2, H=3, T=100, seed=96)
+    dev = to_device(make_inputs(w), w.io)
+    one = run_gpu("mlp", dev, w.eta, w.chunk, w.causal)
+    prev = ttt.set_split_debug(2)
+    try:
+        _note("[parity] mlp_ws with a forced failure of the output workgroups' wait")
+        two = run_gpu("mlp_ws", dev, w.eta, w.chunk, w.causal)
+        torch.cuda.synchronize()
+    finally:
+        ttt.set_split_debug(prev)
+    assert torch.isnan(two[0].float()).all()
+    assert torch.equal(one[1], two[1]) and torch.equal(one[2], two[2])
+    _ws_same_as_one_workgroup(w, make_inputs(w))
+
+
 def test_mlp_ws_other_shapes_run_the_plain_call():
     # no workspace is needed (size 0) for any other shape; the _ws call is then ttt_mlp_fwd
     import test_sequence_layers_amd as ttt
