@@ -271,6 +271,38 @@ def test_mlp_ws_forced_failure_fills_nan_and_returns():
     _ws_same_as_one_workgroup(w, make_inputs(w))
 
 
+def test_mlp_ws_more_sequences_than_resident_workgroups():
+    # 300 sequences: 600 workgroups of one compute unit each, more than the chip holds at
+    # once; the recursion workgroups (lower block indices) are dispatched first and never
+    # wait, so every output workgroup's wait ends
+    w = workload(3).replace(B=25, H=12, T=128, seed=97)
+    _note("[parity] mlp_ws with 600 workgroups")
+    _ws_same_as_one_workgroup(w, make_inputs(w))
+
+
+def test_mlp_ws_two_calls_on_two_streams():
+    # two calls in flight at once on two streams, each with its own workspace
+    import torch
+    import test_sequence_layers_amd as ttt
+    ws_list, outs, refs = [], [], []
+    cases = [workload(3).replace(B=4, H=12, T=512, seed=98), workload(3).replace(B=3, H=12, T=333, seed=99)]
+    devs = [to_device(make_inputs(w), w.io) for w in cases]
+    for w, dev in zip(cases, devs):
+        refs.append(run_gpu("mlp", dev, w.eta, w.chunk, w.causal)[0])
+        n = ttt.ttt_mlp_fwd_workspace_size(w.B, w.H, w.T, w.d, w.h, w.chunk, w.causal, w.io)
+        ws_list.append(torch.empty(n, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    _note("[parity] mlp_ws on two streams at once")
+    for w, dev, ws, st in zip(cases, devs, ws_list, streams):
+        with torch.cuda.stream(st):
+            outs.append(ttt.ttt_mlp_fwd_ws(dev["q"], dev["k"], dev["v"], dev["w1"], dev["w2"], w.eta,
+                                           w.chunk, w.causal, workspace=ws, stream=st))
+    torch.cuda.synchronize()
+    for a, b in zip(refs, outs):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
 def test_mlp_ws_other_shapes_run_the_plain_call():
     # no workspace is needed (size 0) for any other shape; the _ws call is then ttt_mlp_fwd
     import test_sequence_layers_amd as ttt
