@@ -271,6 +271,18 @@ def test_mlp_ws_forced_failure_fills_nan_and_returns():
     _ws_same_as_one_workgroup(w, make_inputs(w))
 
 
+def test_mlp_ws_per_batch_initial_states():
+    # W1, W2 per (batch, head) ([B, H, ...], w_batch_stride = H h d) and a ragged last chunk
+    w = workload(3).replace(B=3, H=2, T=77, seed=94)
+    inp = make_inputs(w)
+    rng = np.random.default_rng(194)
+    inp["w1"] = (0.02 * rng.standard_normal((w.B, w.H, w.h, w.d))).astype(np.float32)
+    inp["w2"] = (0.02 * rng.standard_normal((w.B, w.H, w.d, w.h))).astype(np.float32)
+    _note("[parity] mlp_ws with per-batch initial states")
+    _ws_same_as_one_workgroup(w, inp)
+    _check("mlp_ws", w, inp)
+
+
 def test_mlp_ws_more_sequences_than_resident_workgroups():
     # 300 sequences: 600 workgroups of one compute unit each, more than the chip holds at
     # once; the recursion workgroups (lower block indices) are dispatched first and never
