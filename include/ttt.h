@@ -153,10 +153,12 @@ int ttt_mlp_ln_fwd(const void* q, const void* k, const void* v,
  *                    initialisation and are left undefined.  One workspace serves one call
  *                    at a time: calls that may overlap (different streams) need their own.
  *   workspace_bytes  its size.
- * With workspace == NULL, or for any other shape (for which ttt_mlp_fwd_workspace_size
- * returns 0), the call is ttt_mlp_fwd / ttt_mlp_ln_fwd.  The call allocates nothing on the
- * two-workgroup path.  TTT_E_INVALID additionally for a workspace that is too small or
- * misaligned.  Should the outputs' workgroup of a sequence ever wait past a bound (about a
+ * With workspace == NULL, for any other shape (for which ttt_mlp_fwd_workspace_size
+ * returns 0), or with pointers the matrix-core kernels cannot take (q, k, v, z, w1, w2 and
+ * the output states 16-byte aligned, w_batch_stride a multiple of 4, eta_tok 4-byte
+ * aligned, as for ttt_mlp_fwd's matrix-core path), the call is ttt_mlp_fwd /
+ * ttt_mlp_ln_fwd.  The call allocates nothing on the two-workgroup path.  TTT_E_INVALID
+ * additionally for a workspace that is too small or misaligned.  Should the outputs' workgroup of a sequence ever wait past a bound (about a
  * second) for the operands, it fills that sequence's remaining outputs with NaN instead of
  * hanging (never observed: the recursion's workgroups are dispatched first and never wait).
  */
