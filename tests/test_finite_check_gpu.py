@@ -95,3 +95,24 @@ def test_infinite_upstream_gradient_is_reported_in_dq(check_on):
     with pytest.raises(ttt.TTTError) as ei:
         ttt.ttt_linear_bwd(q, k, v, w0, 0.1, 16, dz)
     assert ei.value.code == ttt.TTT_E_NONFINITE and "non-finite values in dq" in str(ei.value)
+
+
+def test_two_workgroup_mlp_under_the_check(check_on):
+    # ttt_mlp_fwd_ws with the check on: finite outputs unchanged; a NaN in v reported in z
+    torch = _torch()
+    print("[finite] mlp fwd on two workgroups, bf16 d=64 h=256", flush=True)
+    q, k, v = _tokens(2, 3, 70, 64, torch.bfloat16, 7)
+    g = torch.Generator().manual_seed(8)
+    w1 = (0.02 * torch.randn(3, 256, 64, generator=g)).cuda()
+    w2 = (0.02 * torch.randn(3, 64, 256, generator=g)).cuda()
+    z_on, w1_on, w2_on = ttt.ttt_mlp_fwd_ws(q, k, v, w1, w2, 0.1, 16, return_state=True)
+    ttt.set_check_finite(False)
+    z_off, w1_off, w2_off = ttt.ttt_mlp_fwd_ws(q, k, v, w1, w2, 0.1, 16, return_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(z_on, z_off) and torch.equal(w1_on, w1_off) and torch.equal(w2_on, w2_off)
+    ttt.set_check_finite(True)
+    v[0, 1, 33, 5] = float("nan")
+    with pytest.raises(ttt.TTTError) as ei:
+        ttt.ttt_mlp_fwd_ws(q, k, v, w1, w2, 0.1, 16)
+    assert ei.value.code == ttt.TTT_E_NONFINITE
+    assert "ttt_mlp_fwd_ws" in str(ei.value) and "z" in str(ei.value)
